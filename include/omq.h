@@ -1,0 +1,290 @@
+/*
+ * omq.h -- C ABI of the OmniQuant block-calibration hot path on MI355X (gfx950).
+ *
+ * The method (paper reading "OmniQuant: Omnidirectionally Calibrated Quantization
+ * for Large Language Models", onecrewdev.com/posts/omniquant-paper-reading):
+ * weights are frozen; per LLaMA-shaped decoder block the learnable clipping
+ * strengths gamma/beta of Learnable Weight Clipping (section "LWC", the LWC
+ * equation) and the Learnable Equivalent Transformation parameters s, delta and
+ * s_a (section "LET", the linear-layer and attention-affinity equations) are
+ * trained against the full-precision block output (section "框架", the block-wise
+ * objective) with AdamW (section "实验证据").
+ *
+ * Conventions (every entry point):
+ *  - Tensor pointers are DEVICE pointers unless stated.  The caller owns every
+ *    buffer; the library allocates nothing and keeps no global mutable state.
+ *  - Weights are stored like nn.Linear: W is [c_out x c_in] row-major, Y = X W^T + B.
+ *    The page's s (.) W therefore scales W's input channels (columns).
+ *  - Activations are [T x C] row-major (T tokens).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    asynchronously; a kernel fault surfaces at the caller's next synchronisation.
+ *  - Outputs never alias inputs unless stated.
+ *  - Every function validates its arguments before launching anything and returns
+ *    OMQ_OK (0) or a negative OMQ_E_* status; on error nothing is launched.
+ *  - Row lengths must be multiples of 4 elements (OMQ_E_ALIGN), and of 8 for the
+ *    bf16 operands of omq_gemm; pointers must be 16-byte aligned (OMQ_E_ALIGN).
+ *  - Bit widths: 2..8, or 16 meaning "this quantizer is off".
+ *  - Quantizer arithmetic is IEEE float32, one rounding per operation, no fused
+ *    multiply-add, rint = round half to even, gamma = sigmoid(a) computed in
+ *    double and rounded to float; integer codes are therefore reproducible.
+ */
+#ifndef OMQ_H_
+#define OMQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define OMQ_ABI_VERSION 1
+
+/* status codes */
+#define OMQ_OK 0
+#define OMQ_E_INVALID_ARG -1   /* NULL where required, bit width out of range, bad enum */
+#define OMQ_E_SHAPE -2         /* inconsistent or unsupported sizes */
+#define OMQ_E_DTYPE -3         /* unsupported dtype combination */
+#define OMQ_E_ALIGN -4         /* row length or pointer alignment not supported */
+#define OMQ_E_WORKSPACE -5     /* workspace NULL or smaller than the query says */
+#define OMQ_E_HIP -6           /* a HIP call or kernel launch failed */
+#define OMQ_E_UNIMPLEMENTED -7
+
+/* element types */
+#define OMQ_F32 0
+#define OMQ_BF16 1
+
+/* LET applied to the quantizer input x (section "LET" of the paper reading) */
+#define OMQ_LET_NONE 0  /* x~ = x */
+#define OMQ_LET_DIV 1   /* x~ = (x - delta) / s   (activation side; delta may be NULL = 0) */
+#define OMQ_LET_MUL 2   /* x~ = s * x             (weight side, and K~ = s_a * K) */
+
+/* optimizers */
+#define OMQ_OPT_ADAMW 0
+#define OMQ_OPT_SGD 1
+
+/* compute path of a quantized linear layer */
+#define OMQ_PATH_FP32 0  /* fp32 storage, fp32 GEMM */
+#define OMQ_PATH_BF16 1  /* bf16 weights/activations, dequantized operands in bf16, fp32 accumulate */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* omq_status_str(int status);
+int omq_abi_version(void);
+
+/*
+ * omq_lwc_fakequant -- weight side of one linear layer (LWC + LET-W + bias fold).
+ * Paper reading, section "LWC" (the LWC equation) and section "LET" (W~ = s (.) W,
+ * B~ = B + delta W).  Per output channel o (row of W):
+ *   W~_o = s (.) W_o                       (s NULL: W~ = W)
+ *   M, m = max / min of W~_o (first index on ties) -> arg_max[o], arg_min[o]
+ *   gamma = sigmoid(a_gamma[o]), beta = sigmoid(a_beta[o])
+ *   h[o] = max((gamma M - beta m) / (2^N - 1), 1e-8);  z[o] = -rint(beta m / h)
+ *   codes = clamp(rint(W~ / h) + z, 0, 2^N - 1);  W_hat = (codes - z) h
+ *   B_tilde[o] = B[o] + sum_i delta_i W_oi  (original W; B, delta may be NULL = 0)
+ * W: [c_out x c_in] of w_dt.  W_hat: [c_out x c_in] of what_dt (required).
+ * h, z: float[c_out] (required).  arg_max, arg_min: int32[c_out] (required).
+ * B_tilde: float[c_out] or NULL.  codes: uint8[c_out x c_in] or NULL.
+ * n_bits 2..8.
+ */
+int omq_lwc_fakequant(const void* W, int w_dt, int64_t c_out, int64_t c_in, int n_bits,
+                      const float* a_gamma, const float* a_beta, const float* s,
+                      const float* delta, const float* B, void* W_hat, int what_dt, float* h,
+                      float* z, int32_t* arg_max, int32_t* arg_min, float* B_tilde,
+                      uint8_t* codes, void* stream);
+
+/*
+ * omq_let_apply -- the LET transforms alone (paper reading, section "LET",
+ * linear-layer equation), each group optional:
+ *   activation side (X != NULL): X_tilde = (X - delta) / s, X [T x c_in] of x_dt,
+ *     X_tilde [T x c_in] of xt_dt (delta NULL = 0);
+ *   weight side (W != NULL): W_tilde = s (.) W, [c_out x c_in] of w_dt / wt_dt, and
+ *     B_tilde = B + delta W (float[c_out], NULL to skip; B NULL = 0).
+ * s: float[c_in] (required), delta: float[c_in] or NULL.
+ */
+int omq_let_apply(const void* X, int x_dt, int64_t T, int64_t c_in, const float* s,
+                  const float* delta, void* X_tilde, int xt_dt, const void* W, int w_dt,
+                  int64_t c_out, const float* B, void* W_tilde, int wt_dt, float* B_tilde,
+                  void* stream);
+
+/*
+ * omq_act_quant -- per-token asymmetric MinMax fake quantization (gamma = beta = 1)
+ * with an optional fused LET on its input.  Paper reading, section "实验证据"
+ * (per-token activations) with the LWC equation's quantizer.  Per token t:
+ *   x~ = LET(X_t) per let_mode (s, delta: float[C]);  M, m = max / min of x~
+ *   h[t] = max((M - m) / (2^N - 1), 1e-8); z[t] = -rint(m / h)
+ *   X_hat = (clamp(rint(x~ / h) + z, 0, 2^N - 1) - z) h
+ * n_bits 2..8, or 16: X_hat = x~ and h, z, arg_max, arg_min are not written.
+ * X: [T x C] of x_dt; X_hat: [T x C] of xh_dt; h, z: float[T]; arg_max,
+ * arg_min: int32[T]; codes: uint8[T x C] or NULL.
+ */
+int omq_act_quant(const void* X, int x_dt, int64_t T, int64_t C, int n_bits, int let_mode,
+                  const float* s, const float* delta, void* X_hat, int xh_dt, float* h, float* z,
+                  int32_t* arg_max, int32_t* arg_min, uint8_t* codes, void* stream);
+
+/*
+ * omq_gemm -- the quantized layer's contraction (paper reading, section "LET":
+ * Y = Q_a(X~) Q_w(W~) + B~, and the two products of its backward):
+ *   C[M x N] (float32) = alpha * A[M x K] * B[N x K]^T + bias[N]  (bias NULL = 0)
+ * A and B are both dt (OMQ_BF16 on the matrix cores with float32 accumulation,
+ * or OMQ_F32), row-major with leading dimensions lda, ldb, ldc (elements).
+ * accumulate != 0 adds the result to C's current contents.
+ */
+int omq_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+             int64_t ldb, int dt, const float* bias, float alpha, float* C, int64_t ldc,
+             int accumulate, void* stream);
+
+/*
+ * omq_lwc_backward -- straight-through backward of omq_lwc_fakequant.
+ * Only rint is straight-through (the LWC blog, section 2.2: the gradient bypasses
+ * the rounding); clamp, max/min, h and z are differentiated exactly.  Per row o,
+ * with g = gW_hat[o, :], u = W~/h, in = [0 <= rint(u) + z <= 2^N - 1]:
+ *   g_h = sum g ((q - z) - in u),  g_z = -h sum g (1 - in)
+ *   G = g_h + g_z beta m / h^2 (0 when the h floor is active)
+ *   g_gamma = G M / Q,  g_beta = -(G / Q + g_z / h) m
+ *   g_a_gamma = g_gamma gamma (1 - gamma), likewise beta
+ *   gW~ = g in, plus G gamma / Q at arg_max and -(G / Q + g_z / h) beta at arg_min
+ *   g_s[i] = sum_o gW~_oi W_oi      (if g_s != NULL; s may be NULL = 1)
+ *   g_delta[i] = sum_o dy_colsum[o] W_oi   (the bias fold; if g_delta != NULL,
+ *     dy_colsum: float[c_out] = sum over tokens of dL/dY)
+ * gW_hat: float[c_out x c_in] (dL/dW_hat).  h, z, arg_max, arg_min: the forward's.
+ * g_a_gamma, g_a_beta: float[c_out] (required).  g_s, g_delta: float[c_in] or NULL.
+ * ws: device workspace of at least omq_lwc_backward_workspace_size(c_out, c_in) bytes.
+ */
+size_t omq_lwc_backward_workspace_size(int64_t c_out, int64_t c_in);
+int omq_lwc_backward(const float* gW_hat, const void* W, int w_dt, int64_t c_out, int64_t c_in,
+                     int n_bits, const float* a_gamma, const float* a_beta, const float* s,
+                     const float* h, const float* z, const int32_t* arg_max,
+                     const int32_t* arg_min, const float* dy_colsum, float* g_a_gamma,
+                     float* g_a_beta, float* g_s, float* g_delta, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/*
+ * omq_act_quant_backward -- straight-through backward of omq_act_quant (the same
+ * rule as omq_lwc_backward with gamma = beta = 1) chained through the fused LET:
+ *   gx~ = g in + scatter at arg_max / arg_min
+ *   OMQ_LET_DIV: gX = gx~ / s;  g_s += sum_t gx~ (-x~ / s);  g_delta = sum_t gx~ (-1 / s)
+ *   OMQ_LET_MUL: gX = gx~ s;    g_s = sum_t gx~ X
+ *   OMQ_LET_NONE: gX = gx~
+ * gX_hat: float[T x C]; X, s, delta, let_mode, n_bits and h, z, arg_max, arg_min as
+ * given to / returned by omq_act_quant (n_bits 16: gx~ = gX_hat).
+ * gX: float[T x C] or NULL; g_s, g_delta: float[C] or NULL (written, not accumulated).
+ * ws: at least omq_act_quant_backward_workspace_size(T, C) bytes.
+ */
+size_t omq_act_quant_backward_workspace_size(int64_t T, int64_t C);
+int omq_act_quant_backward(const float* gX_hat, int64_t T, int64_t C, const void* X, int x_dt,
+                           int n_bits, int let_mode, const float* s, const float* delta,
+                           const float* h, const float* z, const int32_t* arg_max,
+                           const int32_t* arg_min, float* gX, float* g_s, float* g_delta,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* A quantized linear layer Y = Q_a(X~) Q_w(W~)^T + B~ (paper reading, section "LET"). */
+typedef struct omq_qlinear_desc {
+  size_t struct_size; /* sizeof(omq_qlinear_desc) */
+  int64_t T, c_in, c_out;
+  int wbits;   /* 2..8, or 16 = weight quantizer off */
+  int abits;   /* 2..8, or 16 = activation quantizer off */
+  int use_let; /* 1: theta carries s, delta (LET on this layer) */
+  int path;    /* OMQ_PATH_FP32: X, W float32;  OMQ_PATH_BF16: X, W bf16 */
+} omq_qlinear_desc;
+
+/*
+ * theta / dtheta layout (float): a_gamma[c_out], a_beta[c_out], then when use_let
+ * s[c_in], delta[c_in].  omq_qlinear_theta_size gives the element count.
+ */
+int64_t omq_qlinear_theta_size(const omq_qlinear_desc* d);
+size_t omq_qlinear_workspace_size(const omq_qlinear_desc* d);
+
+/*
+ * omq_qlinear_fwd -- Y[T x c_out] (float32) = Q_a(X~) Q_w(W~)^T + B~.
+ * X: [T x c_in], W: [c_out x c_in] (path dtype), B: float[c_out] or NULL.
+ * The state the backward needs (dequantized operands, step sizes, indices) is
+ * kept in ws, which must be passed unchanged to omq_qlinear_bwd.
+ */
+int omq_qlinear_fwd(const omq_qlinear_desc* d, const void* X, const void* W, const float* B,
+                    const float* theta, float* Y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * omq_qlinear_bwd -- given dY = dL/dY (float[T x c_out]) after omq_qlinear_fwd with
+ * the same arguments and ws: dtheta (theta layout) and dX = dL/dX (float[T x c_in],
+ * NULL to skip).
+ */
+int omq_qlinear_bwd(const omq_qlinear_desc* d, const void* X, const void* W, const float* theta,
+                    const float* dY, float* dX, float* dtheta, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/*
+ * omq_sgd / omq_adamw -- parameter update over a packed float vector (paper reading,
+ * section "实验证据": AdamW, zero weight decay, lr 5e-3 for LWC logits and 1e-2 for
+ * LET parameters).  Elements [0, n_lwc) use lr_lwc, [n_lwc, n) use lr_let.
+ * adamw: m, v float[n] moments (zero before step 1); step counts from 1;
+ * theta -= lr * (m / (1 - b1^step)) / (sqrt(v / (1 - b2^step)) + eps) after
+ * theta *= (1 - lr * weight_decay).
+ */
+int omq_sgd(float* theta, const float* grad, int64_t n, int64_t n_lwc, float lr_lwc,
+            float lr_let, void* stream);
+int omq_adamw(float* theta, const float* grad, float* m, float* v, int64_t n, int64_t n_lwc,
+              float lr_lwc, float lr_let, float beta1, float beta2, float eps,
+              float weight_decay, int64_t step, void* stream);
+
+/*
+ * A LLaMA-shaped decoder block (or its FFN alone): RMSNorm (unit gain) -> q/k/v ->
+ * RoPE (rotate-half) -> s_a on Q/K -> causal scaled attention with float32
+ * softmax -> o -> residual -> RMSNorm -> SiLU(gate) * up -> down -> residual.
+ * LET sites (paper reading, section "LET"): (s_qkv, delta_qkv) on the q/k/v input,
+ * (s_o, delta_o) on the o input (per KV channel, broadcast over the query heads of
+ * a group), (s_ffn, delta_ffn) on the gate/up input, none on down; s_a per KV
+ * channel on the post-RoPE Q (divided) and K (multiplied), learned only when
+ * abits < 16.  Q~, K~, V and every linear input are quantized per token at abits;
+ * softmax is never quantized.  ffn_only: y = down(SiLU(gate(x~)) * up(x~)) with the
+ * ffn LET site, no norm and no residual.
+ */
+typedef struct omq_block_desc {
+  size_t struct_size; /* sizeof(omq_block_desc) */
+  int64_t T, d, n_q, n_kv, head_dim, F;
+  int wbits, abits;   /* 2..8 / 16 */
+  int ffn_only;
+  float eps;          /* RMSNorm epsilon */
+  float rope_theta;
+  int optimizer;      /* OMQ_OPT_ADAMW or OMQ_OPT_SGD */
+  float lr_lwc, lr_let;
+  float beta1, beta2, adam_eps, weight_decay;
+} omq_block_desc;
+
+/*
+ * Packed theta order: for each linear of (q, k, v, o, gate, up, down) (ffn_only:
+ * gate, up, down) a_gamma[C_out] then a_beta[C_out]; then for each LET site of
+ * (qkv, o, ffn) (ffn_only: ffn) s[C] then delta[C] (C = d, n_kv*head_dim, d);
+ * then s_a[n_kv*head_dim] when abits < 16 and not ffn_only.
+ * offsets: int64[2*n_linears + 2*n_sites + 1] host array or NULL; *total: count.
+ * *n_lwc: number of leading LWC logits (or NULL).
+ */
+int omq_block_theta_layout(const omq_block_desc* d, int64_t* offsets, int64_t* n_entries,
+                           int64_t* n_lwc, int64_t* total);
+size_t omq_block_workspace_size(const omq_block_desc* d);
+
+/*
+ * omq_block_forward -- y[T x d] (float32) of the block.  x: bf16 [T x d];
+ * weights: host array of 7 device pointers (q, k, v, o, gate, up, down; bf16,
+ * [C_out x C_in]; ffn_only: the first four may be NULL).  theta == NULL runs the
+ * full-precision block (no quantizers, no LET): the calibration target.
+ */
+int omq_block_forward(const omq_block_desc* d, const void* x, const void* const* weights,
+                      const float* theta, float* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * omq_block_step -- one calibration step (paper reading, section "框架"): quantized
+ * forward, L = mean((y - y_target)^2) over T x d, straight-through backward into
+ * dtheta (theta layout), and the optimizer update of theta (and m, v for AdamW,
+ * float[total], zero before step 1; step counts from 1).  loss: float device
+ * scalar (the loss before the update), or NULL.  y_target: float32 [T x d].
+ */
+int omq_block_step(const omq_block_desc* d, const void* x, const float* y_target,
+                   const void* const* weights, float* theta, float* dtheta, float* adam_m,
+                   float* adam_v, int64_t step, float* loss, void* ws, size_t ws_bytes,
+                   void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OMQ_H_ */

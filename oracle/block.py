@@ -90,8 +90,11 @@ def silu(x):
     return x / (1.0 + np.exp(-x))
 
 
-def attention(Q, K, V, n_q, n_kv, hd):
-    """Causal scaled attention, float64 softmax.  Q [T, n_q*hd], K/V [T, n_kv*hd]."""
+def attention(Q, K, V, n_q, n_kv, hd, cast=None):
+    """Causal scaled attention, float64 softmax.  Q [T, n_q*hd], K/V [T, n_kv*hd].
+
+    cast: how the probabilities enter the P V product (the bf16 path feeds them to
+    the matrix cores in bf16); the softmax itself is never quantized."""
     T = Q.shape[0]
     grp = n_q // n_kv
     c = 1.0 / np.sqrt(hd)
@@ -108,8 +111,9 @@ def attention(Q, K, V, n_q, n_kv, hd):
         S = S - S.max(axis=1, keepdims=True)
         E = np.exp(S)
         Ph = E / E.sum(axis=1, keepdims=True)
-        O[:, h * hd:(h + 1) * hd] = Ph @ v
-        P.append(Ph)
+        Pop = Ph if cast is None else cast(Ph)
+        O[:, h * hd:(h + 1) * hd] = Pop @ v
+        P.append((Ph, Pop))
     return O, P
 
 
@@ -125,8 +129,8 @@ def attention_bwd(dO, Q, K, V, P, n_q, n_kv, hd):
         sl_q = slice(h * hd, (h + 1) * hd)
         sl_k = slice(g * hd, (g + 1) * hd)
         do = dO[:, sl_q]
-        Ph = P[h]
-        dV[:, sl_k] += Ph.T @ do
+        Ph, Pop = P[h]
+        dV[:, sl_k] += Pop.T @ do
         dP = do @ V[:, sl_k].T
         dS = Ph * (dP - np.sum(dP * Ph, axis=1, keepdims=True))
         dQ[:, sl_q] = c * (dS @ K[:, sl_k])
@@ -259,7 +263,7 @@ def forward(c, x, Wd, th, ops=None):
         aK, Kh = ops.act(Kt, c.abits, "a_k")
         aV, Vh = ops.act(Yv, c.abits, "a_v")
         Qo, Ko, Vo = ops.operand(Qh), ops.operand(Kh), ops.operand(Vh)
-        O, P = attention(Qo, Ko, Vo, n_q, n_kv, hd)
+        O, P = attention(Qo, Ko, Vo, n_q, n_kv, hd, cast=ops.operand)
         s_o = kv_broadcast(th["s_o"], n_q, n_kv, hd)
         d_o = kv_broadcast(th["delta_o"], n_q, n_kv, hd)
         Xt_o = ops.let_act(O, s_o, d_o)

@@ -1,0 +1,318 @@
+"""Python binding of libomq (OmniQuant block calibration on MI355X / gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels behind the C ABI
+declared in include/omq.h.  PyTorch provides device memory and the current
+stream.  Importing this package without the built library raises (build with
+``python -m post_quantization_amd.build``); there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Sequence
+
+import torch
+
+__all__ = [
+    "OmqError", "lib", "status_str", "abi_version", "lwc_fakequant", "let_apply", "act_quant",
+    "gemm", "lwc_backward", "act_quant_backward", "QLinearDesc", "qlinear_theta_size",
+    "qlinear_workspace_size", "qlinear_fwd", "qlinear_bwd", "sgd", "adamw", "BlockDesc",
+    "block_theta_layout", "block_workspace_size", "block_forward", "block_step",
+    "F32", "BF16", "LET_NONE", "LET_DIV", "LET_MUL", "PATH_FP32", "PATH_BF16",
+    "OPT_ADAMW", "OPT_SGD",
+]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libomq.so")
+
+F32, BF16 = 0, 1
+LET_NONE, LET_DIV, LET_MUL = 0, 1, 2
+PATH_FP32, PATH_BF16 = 0, 1
+OPT_ADAMW, OPT_SGD = 0, 1
+
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_vp = ctypes.c_void_p
+_f = ctypes.c_float
+_sz = ctypes.c_size_t
+
+
+class OmqError(RuntimeError):
+    pass
+
+
+class QLinearDesc(ctypes.Structure):
+    _fields_ = [("struct_size", _sz), ("T", _i64), ("c_in", _i64), ("c_out", _i64),
+                ("wbits", _int), ("abits", _int), ("use_let", _int), ("path", _int)]
+
+    def __init__(self, T, c_in, c_out, wbits, abits, use_let, path):
+        super().__init__(ctypes.sizeof(QLinearDesc), T, c_in, c_out, wbits, abits,
+                         int(use_let), path)
+
+
+class BlockDesc(ctypes.Structure):
+    _fields_ = [("struct_size", _sz), ("T", _i64), ("d", _i64), ("n_q", _i64),
+                ("n_kv", _i64), ("head_dim", _i64), ("F", _i64), ("wbits", _int),
+                ("abits", _int), ("ffn_only", _int), ("eps", _f), ("rope_theta", _f),
+                ("optimizer", _int), ("lr_lwc", _f), ("lr_let", _f), ("beta1", _f),
+                ("beta2", _f), ("adam_eps", _f), ("weight_decay", _f)]
+
+    def __init__(self, T, d, n_q, n_kv, head_dim, F, wbits, abits, ffn_only=False, eps=1e-6,
+                 rope_theta=10000.0, optimizer=OPT_ADAMW, lr_lwc=5e-3, lr_let=1e-2,
+                 beta1=0.9, beta2=0.999, adam_eps=1e-8, weight_decay=0.0):
+        super().__init__(ctypes.sizeof(BlockDesc), T, d, n_q, n_kv, head_dim, F, wbits, abits,
+                         int(ffn_only), eps, rope_theta, optimizer, lr_lwc, lr_let, beta1,
+                         beta2, adam_eps, weight_decay)
+
+
+_SIGS = {
+    "omq_status_str": (ctypes.c_char_p, [_int]),
+    "omq_abi_version": (_int, []),
+    "omq_lwc_fakequant": (_int, [_vp, _int, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "omq_let_apply": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _vp, _int, _vp, _int, _i64, _vp,
+                             _vp, _int, _vp, _vp]),
+    "omq_act_quant": (_int, [_vp, _int, _i64, _i64, _int, _int, _vp, _vp, _vp, _int, _vp, _vp,
+                             _vp, _vp, _vp, _vp]),
+    "omq_gemm": (_int, [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _int, _vp, _f, _vp, _i64, _int,
+                        _vp]),
+    "omq_lwc_backward_workspace_size": (_sz, [_i64, _i64]),
+    "omq_lwc_backward": (_int, [_vp, _vp, _int, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp,
+                                _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "omq_act_quant_backward_workspace_size": (_sz, [_i64, _i64]),
+    "omq_act_quant_backward": (_int, [_vp, _i64, _i64, _vp, _int, _int, _int, _vp, _vp, _vp,
+                                      _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "omq_qlinear_theta_size": (_i64, [ctypes.POINTER(QLinearDesc)]),
+    "omq_qlinear_workspace_size": (_sz, [ctypes.POINTER(QLinearDesc)]),
+    "omq_qlinear_fwd": (_int, [ctypes.POINTER(QLinearDesc), _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                               _vp]),
+    "omq_qlinear_bwd": (_int, [ctypes.POINTER(QLinearDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                               _sz, _vp]),
+    "omq_sgd": (_int, [_vp, _vp, _i64, _i64, _f, _f, _vp]),
+    "omq_adamw": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _f, _f, _f, _f, _f, _f, _i64, _vp]),
+    "omq_block_theta_layout": (_int, [ctypes.POINTER(BlockDesc), _vp, _vp, _vp, _vp]),
+    "omq_block_workspace_size": (_sz, [ctypes.POINTER(BlockDesc)]),
+    "omq_block_forward": (_int, [ctypes.POINTER(BlockDesc), _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "omq_block_step": (_int, [ctypes.POINTER(BlockDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                              _i64, _vp, _vp, _sz, _vp]),
+}
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libomq.so; raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise OmqError("libomq.so not built: run `python -m post_quantization_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def status_str(rc: int) -> str:
+    return lib().omq_status_str(rc).decode()
+
+
+def abi_version() -> int:
+    return lib().omq_abi_version()
+
+
+def _check(name: str, rc: int) -> None:
+    if rc != 0:
+        raise OmqError("%s: %s (%d)" % (name, status_str(rc), rc))
+
+
+def _p(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise OmqError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise OmqError("unsupported dtype %s" % t.dtype)
+
+
+def _tdt(code: int):
+    return torch.float32 if code == F32 else torch.bfloat16
+
+
+def lwc_fakequant(W, a_gamma, a_beta, n_bits, s=None, delta=None, B=None, out_dtype=None,
+                  want_bias=False, want_codes=False) -> Dict[str, torch.Tensor]:
+    c_out, c_in = W.shape
+    dev = W.device
+    out_dtype = W.dtype if out_dtype is None else out_dtype
+    r = {"W_hat": torch.empty(c_out, c_in, dtype=out_dtype, device=dev),
+         "h": torch.empty(c_out, dtype=torch.float32, device=dev),
+         "z": torch.empty(c_out, dtype=torch.float32, device=dev),
+         "arg_max": torch.empty(c_out, dtype=torch.int32, device=dev),
+         "arg_min": torch.empty(c_out, dtype=torch.int32, device=dev)}
+    r["B_tilde"] = torch.empty(c_out, dtype=torch.float32, device=dev) if want_bias else None
+    r["codes"] = torch.empty(c_out, c_in, dtype=torch.uint8, device=dev) if want_codes else None
+    _check("omq_lwc_fakequant", lib().omq_lwc_fakequant(
+        _p(W), _dt(W), c_out, c_in, n_bits, _p(a_gamma), _p(a_beta), _p(s), _p(delta), _p(B),
+        _p(r["W_hat"]), _dt(r["W_hat"]), _p(r["h"]), _p(r["z"]), _p(r["arg_max"]),
+        _p(r["arg_min"]), _p(r["B_tilde"]), _p(r["codes"]), _stream()))
+    return r
+
+
+def let_apply(s, delta=None, X=None, W=None, B=None, x_out_dtype=torch.float32,
+              w_out_dtype=torch.float32, want_bias=False):
+    dev = s.device
+    c_in = s.numel()
+    Xt = torch.empty(X.shape, dtype=x_out_dtype, device=dev) if X is not None else None
+    Wt = torch.empty(W.shape, dtype=w_out_dtype, device=dev) if W is not None else None
+    Bt = torch.empty(W.shape[0], dtype=torch.float32, device=dev) if (W is not None and want_bias) else None
+    T = X.shape[0] if X is not None else 0
+    c_out = W.shape[0] if W is not None else 0
+    _check("omq_let_apply", lib().omq_let_apply(
+        _p(X), _dt(X) if X is not None else 0, T, c_in, _p(s), _p(delta), _p(Xt),
+        _dt(Xt) if Xt is not None else 0, _p(W), _dt(W) if W is not None else 0, c_out, _p(B),
+        _p(Wt), _dt(Wt) if Wt is not None else 0, _p(Bt), _stream()))
+    return Xt, Wt, Bt
+
+
+def act_quant(X, n_bits, let_mode=LET_NONE, s=None, delta=None, out_dtype=torch.bfloat16,
+              want_codes=False) -> Dict[str, torch.Tensor]:
+    T, C = X.shape
+    dev = X.device
+    r = {"X_hat": torch.empty(T, C, dtype=out_dtype, device=dev),
+         "h": torch.empty(T, dtype=torch.float32, device=dev),
+         "z": torch.empty(T, dtype=torch.float32, device=dev),
+         "arg_max": torch.empty(T, dtype=torch.int32, device=dev),
+         "arg_min": torch.empty(T, dtype=torch.int32, device=dev)}
+    r["codes"] = torch.empty(T, C, dtype=torch.uint8, device=dev) if want_codes else None
+    _check("omq_act_quant", lib().omq_act_quant(
+        _p(X), _dt(X), T, C, n_bits, let_mode, _p(s), _p(delta), _p(r["X_hat"]),
+        _dt(r["X_hat"]), _p(r["h"]), _p(r["z"]), _p(r["arg_max"]), _p(r["arg_min"]),
+        _p(r["codes"]), _stream()))
+    return r
+
+
+def gemm(A, B, bias=None, alpha=1.0, C=None, accumulate=False):
+    """C = alpha A B^T (+ bias) (+ C);  A [M x K], B [N x K], both bf16 or both float32."""
+    M, K = A.shape
+    N = B.shape[0]
+    if C is None:
+        C = torch.empty(M, N, dtype=torch.float32, device=A.device)
+    _check("omq_gemm", lib().omq_gemm(M, N, K, _p(A), K, _p(B), K, _dt(A), _p(bias), alpha,
+                                      _p(C), N, int(accumulate), _stream()))
+    return C
+
+
+def lwc_backward(gW_hat, W, n_bits, a_gamma, a_beta, h, z, arg_max, arg_min, s=None,
+                 dy_colsum=None, want_s=False, want_delta=False):
+    c_out, c_in = W.shape
+    dev = W.device
+    ga = torch.empty(c_out, dtype=torch.float32, device=dev)
+    gb = torch.empty(c_out, dtype=torch.float32, device=dev)
+    gs = torch.empty(c_in, dtype=torch.float32, device=dev) if want_s else None
+    gd = torch.empty(c_in, dtype=torch.float32, device=dev) if want_delta else None
+    nbytes = lib().omq_lwc_backward_workspace_size(c_out, c_in)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _check("omq_lwc_backward", lib().omq_lwc_backward(
+        _p(gW_hat), _p(W), _dt(W), c_out, c_in, n_bits, _p(a_gamma), _p(a_beta), _p(s), _p(h),
+        _p(z), _p(arg_max), _p(arg_min), _p(dy_colsum), _p(ga), _p(gb), _p(gs), _p(gd), _p(ws),
+        nbytes, _stream()))
+    return ga, gb, gs, gd
+
+
+def act_quant_backward(gX_hat, X, n_bits, h, z, arg_max, arg_min, let_mode=LET_NONE, s=None,
+                       delta=None, want_gx=True, want_s=False, want_delta=False):
+    T, C = X.shape
+    dev = X.device
+    gx = torch.empty(T, C, dtype=torch.float32, device=dev) if want_gx else None
+    gs = torch.empty(C, dtype=torch.float32, device=dev) if want_s else None
+    gd = torch.empty(C, dtype=torch.float32, device=dev) if want_delta else None
+    nbytes = lib().omq_act_quant_backward_workspace_size(T, C)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _check("omq_act_quant_backward", lib().omq_act_quant_backward(
+        _p(gX_hat), T, C, _p(X), _dt(X), n_bits, let_mode, _p(s), _p(delta), _p(h), _p(z),
+        _p(arg_max), _p(arg_min), _p(gx), _p(gs), _p(gd), _p(ws), nbytes, _stream()))
+    return gx, gs, gd
+
+
+def qlinear_theta_size(desc: QLinearDesc) -> int:
+    return lib().omq_qlinear_theta_size(ctypes.byref(desc))
+
+
+def qlinear_workspace_size(desc: QLinearDesc) -> int:
+    return lib().omq_qlinear_workspace_size(ctypes.byref(desc))
+
+
+def qlinear_fwd(desc, X, W, B, theta, Y, ws):
+    _check("omq_qlinear_fwd", lib().omq_qlinear_fwd(
+        ctypes.byref(desc), _p(X), _p(W), _p(B), _p(theta), _p(Y), _p(ws), ws.numel(), _stream()))
+    return Y
+
+
+def qlinear_bwd(desc, X, W, theta, dY, dX, dtheta, ws):
+    _check("omq_qlinear_bwd", lib().omq_qlinear_bwd(
+        ctypes.byref(desc), _p(X), _p(W), _p(theta), _p(dY), _p(dX), _p(dtheta), _p(ws),
+        ws.numel(), _stream()))
+    return dtheta
+
+
+def sgd(theta, grad, n_lwc, lr_lwc, lr_let):
+    _check("omq_sgd", lib().omq_sgd(_p(theta), _p(grad), theta.numel(), n_lwc, lr_lwc, lr_let,
+                                    _stream()))
+
+
+def adamw(theta, grad, m, v, n_lwc, lr_lwc, lr_let, step, beta1=0.9, beta2=0.999, eps=1e-8,
+          weight_decay=0.0):
+    _check("omq_adamw", lib().omq_adamw(_p(theta), _p(grad), _p(m), _p(v), theta.numel(), n_lwc,
+                                        lr_lwc, lr_let, beta1, beta2, eps, weight_decay, step,
+                                        _stream()))
+
+
+def block_theta_layout(desc: BlockDesc):
+    """(offsets of the packed entries, number of leading LWC logits, total size)."""
+    offs = (ctypes.c_int64 * 32)()
+    n = ctypes.c_int64()
+    nl = ctypes.c_int64()
+    tot = ctypes.c_int64()
+    _check("omq_block_theta_layout", lib().omq_block_theta_layout(
+        ctypes.byref(desc), ctypes.addressof(offs), ctypes.addressof(n), ctypes.addressof(nl),
+        ctypes.addressof(tot)))
+    return list(offs[:n.value]), nl.value, tot.value
+
+
+def block_workspace_size(desc: BlockDesc) -> int:
+    return lib().omq_block_workspace_size(ctypes.byref(desc))
+
+
+def _wptrs(weights: Sequence[Optional[torch.Tensor]]):
+    arr = (ctypes.c_void_p * 7)()
+    for i, w in enumerate(weights):
+        arr[i] = _p(w) if w is not None else None
+    return arr
+
+
+def block_forward(desc, x, weights, theta, y, ws):
+    arr = _wptrs(weights)
+    _check("omq_block_forward", lib().omq_block_forward(
+        ctypes.byref(desc), _p(x), ctypes.addressof(arr), _p(theta), _p(y), _p(ws), ws.numel(),
+        _stream()))
+    return y
+
+
+def block_step(desc, x, y_target, weights, theta, dtheta, adam_m, adam_v, step, loss, ws):
+    arr = _wptrs(weights)
+    _check("omq_block_step", lib().omq_block_step(
+        ctypes.byref(desc), _p(x), _p(y_target), ctypes.addressof(arr), _p(theta), _p(dtheta),
+        _p(adam_m), _p(adam_v), step, _p(loss), _p(ws), ws.numel(), _stream()))

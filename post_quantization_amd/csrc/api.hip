@@ -1,0 +1,372 @@
+// C ABI of the OmniQuant calibration hot path: argument validation, workspace
+// layout, and the composition of kernels into the layer-level operations.
+#include "api_util.h"
+
+using namespace omq;
+
+extern "C" {
+
+const char* omq_status_str(int status) {
+  switch (status) {
+    case OMQ_OK: return "ok";
+    case OMQ_E_INVALID_ARG: return "invalid argument";
+    case OMQ_E_SHAPE: return "inconsistent or unsupported shape";
+    case OMQ_E_DTYPE: return "unsupported dtype";
+    case OMQ_E_ALIGN: return "unsupported row length or pointer alignment";
+    case OMQ_E_WORKSPACE: return "workspace missing or too small";
+    case OMQ_E_HIP: return "HIP launch failed";
+    case OMQ_E_UNIMPLEMENTED: return "not implemented";
+    default: return "unknown status";
+  }
+}
+
+int omq_abi_version(void) { return OMQ_ABI_VERSION; }
+
+int omq_lwc_fakequant(const void* W, int w_dt, int64_t c_out, int64_t c_in, int n_bits,
+                      const float* a_gamma, const float* a_beta, const float* s,
+                      const float* delta, const float* B, void* W_hat, int what_dt, float* h,
+                      float* z, int32_t* arg_max, int32_t* arg_min, float* B_tilde,
+                      uint8_t* codes, void* stream) {
+  if (!W || !a_gamma || !a_beta || !W_hat || !h || !z || !arg_max || !arg_min)
+    return OMQ_E_INVALID_ARG;
+  if (n_bits < 2 || n_bits > 8) return OMQ_E_INVALID_ARG;
+  if (!dt_ok(w_dt) || !dt_ok(what_dt)) return OMQ_E_DTYPE;
+  if (c_out < 0 || c_in <= 0) return OMQ_E_SHAPE;
+  if (c_in % 4) return OMQ_E_ALIGN;
+  if (!al16(W) || !al16(W_hat) || !al16(s) || !al16(delta) || !al4(codes)) return OMQ_E_ALIGN;
+  RowQuantFwd a;
+  a.x = W; a.x_dt = w_dt; a.rows = c_out; a.cols = c_in; a.ldx = c_in;
+  a.let_mode = s ? OMQ_LET_MUL : OMQ_LET_NONE; a.s = s;
+  a.nbits = n_bits; a.a_gamma = a_gamma; a.a_beta = a_beta;
+  a.out = W_hat; a.out_dt = what_dt; a.ldo = c_in;
+  a.h = h; a.z = z; a.amax = arg_max; a.amin = arg_min; a.codes = codes;
+  a.fold_delta = delta; a.bias = B; a.bias_out = B_tilde;
+  if (B_tilde && !delta) {
+    // no shift: B~ = B
+    if (B) OMQ_HIP_CHECK(hipMemcpyAsync(B_tilde, B, c_out * 4, hipMemcpyDeviceToDevice, S(stream)));
+    else OMQ_HIP_CHECK(hipMemsetAsync(B_tilde, 0, c_out * 4, S(stream)));
+    a.bias_out = nullptr;
+  }
+  OMQ_HIP_CHECK(launch_rowquant_fwd(a, S(stream)));
+  return OMQ_OK;
+}
+
+int omq_let_apply(const void* X, int x_dt, int64_t T, int64_t c_in, const float* s,
+                  const float* delta, void* X_tilde, int xt_dt, const void* W, int w_dt,
+                  int64_t c_out, const float* B, void* W_tilde, int wt_dt, float* B_tilde,
+                  void* stream) {
+  if (!s) return OMQ_E_INVALID_ARG;
+  if (c_in <= 0) return OMQ_E_SHAPE;
+  if (c_in % 4) return OMQ_E_ALIGN;
+  if (X) {
+    if (!X_tilde) return OMQ_E_INVALID_ARG;
+    if (!dt_ok(x_dt) || !dt_ok(xt_dt)) return OMQ_E_DTYPE;
+    if (T < 0) return OMQ_E_SHAPE;
+    if (!al16(X) || !al16(X_tilde)) return OMQ_E_ALIGN;
+  }
+  if (W) {
+    if (!W_tilde && !B_tilde) return OMQ_E_INVALID_ARG;
+    if (!dt_ok(w_dt) || (W_tilde && !dt_ok(wt_dt))) return OMQ_E_DTYPE;
+    if (c_out < 0) return OMQ_E_SHAPE;
+    if (!al16(W) || !al16(W_tilde)) return OMQ_E_ALIGN;
+  }
+  if (X)
+    OMQ_HIP_CHECK(launch_let_elementwise(X, x_dt, T, c_in, OMQ_LET_DIV, s, delta, X_tilde, xt_dt,
+                                         S(stream)));
+  if (W && W_tilde)
+    OMQ_HIP_CHECK(launch_let_elementwise(W, w_dt, c_out, c_in, OMQ_LET_MUL, s, nullptr, W_tilde,
+                                         wt_dt, S(stream)));
+  if (W && B_tilde) {
+    if (delta)
+      OMQ_HIP_CHECK(launch_bias_fold(W, w_dt, c_out, c_in, delta, B, B_tilde, S(stream)));
+    else if (B)
+      OMQ_HIP_CHECK(hipMemcpyAsync(B_tilde, B, c_out * 4, hipMemcpyDeviceToDevice, S(stream)));
+    else
+      OMQ_HIP_CHECK(hipMemsetAsync(B_tilde, 0, c_out * 4, S(stream)));
+  }
+  return OMQ_OK;
+}
+
+int omq_act_quant(const void* X, int x_dt, int64_t T, int64_t C, int n_bits, int let_mode,
+                  const float* s, const float* delta, void* X_hat, int xh_dt, float* h, float* z,
+                  int32_t* arg_max, int32_t* arg_min, uint8_t* codes, void* stream) {
+  if (!X || !X_hat) return OMQ_E_INVALID_ARG;
+  if (!bits_ok(n_bits)) return OMQ_E_INVALID_ARG;
+  if (n_bits < 16 && (!h || !z || !arg_max || !arg_min)) return OMQ_E_INVALID_ARG;
+  if (let_mode < 0 || let_mode > 2 || (let_mode != OMQ_LET_NONE && !s)) return OMQ_E_INVALID_ARG;
+  if (!dt_ok(x_dt) || !dt_ok(xh_dt)) return OMQ_E_DTYPE;
+  if (T < 0 || C <= 0) return OMQ_E_SHAPE;
+  if (C % 4) return OMQ_E_ALIGN;
+  if (!al16(X) || !al16(X_hat) || !al4(codes)) return OMQ_E_ALIGN;
+  RowQuantFwd a;
+  a.x = X; a.x_dt = x_dt; a.rows = T; a.cols = C; a.ldx = C;
+  a.let_mode = let_mode; a.s = s; a.delta = delta; a.nbits = n_bits;
+  a.out = X_hat; a.out_dt = xh_dt; a.ldo = C;
+  a.h = h; a.z = z; a.amax = arg_max; a.amin = arg_min; a.codes = codes;
+  OMQ_HIP_CHECK(launch_rowquant_fwd(a, S(stream)));
+  return OMQ_OK;
+}
+
+int omq_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+             int64_t ldb, int dt, const float* bias, float alpha, float* C, int64_t ldc,
+             int accumulate, void* stream) {
+  if (!A || !B || !C) return OMQ_E_INVALID_ARG;
+  if (!dt_ok(dt)) return OMQ_E_DTYPE;
+  if (M < 0 || N < 0 || K < 0 || lda < K || ldb < K || ldc < N) return OMQ_E_SHAPE;
+  if (dt == OMQ_BF16 && (K % 8 || lda % 8 || ldb % 8 || !al16(A) || !al16(B)))
+    return OMQ_E_ALIGN;
+  Gemm g;
+  g.A = A; g.lda = lda; g.B = B; g.ldb = ldb; g.C = C; g.ldc = ldc; g.bias = bias;
+  g.M = M; g.N = N; g.K = K; g.alpha = alpha; g.accumulate = accumulate; g.dt = dt;
+  OMQ_HIP_CHECK(launch_gemm(g, S(stream)));
+  return OMQ_OK;
+}
+
+size_t omq_lwc_backward_workspace_size(int64_t c_out, int64_t c_in) {
+  return rowquant_bwd_ws_bytes(c_out, c_in);
+}
+
+int omq_lwc_backward(const float* gW_hat, const void* W, int w_dt, int64_t c_out, int64_t c_in,
+                     int n_bits, const float* a_gamma, const float* a_beta, const float* s,
+                     const float* h, const float* z, const int32_t* arg_max,
+                     const int32_t* arg_min, const float* dy_colsum, float* g_a_gamma,
+                     float* g_a_beta, float* g_s, float* g_delta, void* ws, size_t ws_bytes,
+                     void* stream) {
+  if (!gW_hat || !W || !a_gamma || !a_beta || !h || !z || !arg_max || !arg_min || !g_a_gamma ||
+      !g_a_beta)
+    return OMQ_E_INVALID_ARG;
+  if (g_delta && !dy_colsum) return OMQ_E_INVALID_ARG;
+  if (n_bits < 2 || n_bits > 8) return OMQ_E_INVALID_ARG;
+  if (!dt_ok(w_dt)) return OMQ_E_DTYPE;
+  if (c_out < 0 || c_in <= 0) return OMQ_E_SHAPE;
+  if (c_in % 4) return OMQ_E_ALIGN;
+  if (!al16(gW_hat) || !al16(W)) return OMQ_E_ALIGN;
+  if (!ws || ws_bytes < omq_lwc_backward_workspace_size(c_out, c_in)) return OMQ_E_WORKSPACE;
+  RowQuantBwd a;
+  a.g = gW_hat; a.ldg = c_in; a.x = W; a.x_dt = w_dt; a.rows = c_out; a.cols = c_in;
+  a.ldx = c_in; a.let_mode = s ? OMQ_LET_MUL : OMQ_LET_NONE; a.s = s; a.nbits = n_bits;
+  a.h = h; a.z = z; a.amax = arg_max; a.amin = arg_min; a.a_gamma = a_gamma; a.a_beta = a_beta;
+  a.col_mode = (g_s || g_delta) ? COL_WEIGHT : COL_NONE;
+  a.rowvec = dy_colsum; a.g_agamma = g_a_gamma; a.g_abeta = g_a_beta;
+  a.out0 = g_s; a.out1 = g_delta; a.ws = reinterpret_cast<float*>(ws);
+  OMQ_HIP_CHECK(launch_rowquant_bwd(a, S(stream)));
+  return OMQ_OK;
+}
+
+size_t omq_act_quant_backward_workspace_size(int64_t T, int64_t C) {
+  return rowquant_bwd_ws_bytes(T, C);
+}
+
+int omq_act_quant_backward(const float* gX_hat, int64_t T, int64_t C, const void* X, int x_dt,
+                           int n_bits, int let_mode, const float* s, const float* delta,
+                           const float* h, const float* z, const int32_t* arg_max,
+                           const int32_t* arg_min, float* gX, float* g_s, float* g_delta,
+                           void* ws, size_t ws_bytes, void* stream) {
+  if (!gX_hat || !X) return OMQ_E_INVALID_ARG;
+  if (!bits_ok(n_bits)) return OMQ_E_INVALID_ARG;
+  if (n_bits < 16 && (!h || !z || !arg_max || !arg_min)) return OMQ_E_INVALID_ARG;
+  if (let_mode < 0 || let_mode > 2 || (let_mode != OMQ_LET_NONE && !s)) return OMQ_E_INVALID_ARG;
+  if ((g_s || g_delta) && let_mode == OMQ_LET_NONE) return OMQ_E_INVALID_ARG;
+  if (g_delta && let_mode != OMQ_LET_DIV) return OMQ_E_INVALID_ARG;
+  if (!dt_ok(x_dt)) return OMQ_E_DTYPE;
+  if (T < 0 || C <= 0) return OMQ_E_SHAPE;
+  if (C % 4) return OMQ_E_ALIGN;
+  if (!al16(gX_hat) || !al16(X) || !al16(gX)) return OMQ_E_ALIGN;
+  if (!ws || ws_bytes < omq_act_quant_backward_workspace_size(T, C)) return OMQ_E_WORKSPACE;
+  RowQuantBwd a;
+  a.g = gX_hat; a.ldg = C; a.x = X; a.x_dt = x_dt; a.rows = T; a.cols = C; a.ldx = C;
+  a.let_mode = let_mode; a.s = s; a.delta = delta; a.nbits = n_bits;
+  a.h = h; a.z = z; a.amax = arg_max; a.amin = arg_min;
+  a.col_mode = (g_s || g_delta) ? (let_mode == OMQ_LET_DIV ? COL_ACT_DIV : COL_ACT_MUL) : COL_NONE;
+  a.gx = gX; a.ldgx = C; a.out0 = g_s; a.out1 = g_delta;
+  a.ws = reinterpret_cast<float*>(ws);
+  OMQ_HIP_CHECK(launch_rowquant_bwd(a, S(stream)));
+  return OMQ_OK;
+}
+
+// ---------------------------------------------------------------------------
+// quantized linear layer
+// ---------------------------------------------------------------------------
+
+int64_t omq_qlinear_theta_size(const omq_qlinear_desc* d) {
+  if (!d) return -1;
+  return 2 * d->c_out + (d->use_let ? 2 * d->c_in : 0);
+}
+
+namespace {
+
+struct QLinWs {
+  void* What; float *wh, *wz; int32_t *wamax, *wamin; float* Bt;
+  void* Xhat; float *ah, *az; int32_t *aamax, *aamin;
+  float *gW, *gXh, *colsum;
+  uint16_t *dYb, *dYt, *Xht, *Wht;
+  float *rq, *cs;
+  size_t total;
+};
+
+QLinWs qlin_layout(const omq_qlinear_desc* d, void* base) {
+  Bump b(base);
+  QLinWs w;
+  const bool bf = d->path == OMQ_PATH_BF16;
+  const size_t es = bf ? 2 : 4;
+  const int64_t T = d->T, ci = d->c_in, co = d->c_out;
+  w.What = b.take<char>(co * ci * es);
+  w.wh = b.take<float>(co); w.wz = b.take<float>(co);
+  w.wamax = b.take<int32_t>(co); w.wamin = b.take<int32_t>(co);
+  w.Bt = b.take<float>(co);
+  w.Xhat = b.take<char>(T * ci * es);
+  w.ah = b.take<float>(T); w.az = b.take<float>(T);
+  w.aamax = b.take<int32_t>(T); w.aamin = b.take<int32_t>(T);
+  w.gW = b.take<float>(co * ci);
+  w.gXh = b.take<float>(T * ci);
+  w.colsum = b.take<float>(co);
+  if (bf) {
+    w.dYb = b.take<uint16_t>(T * co); w.dYt = b.take<uint16_t>(co * T);
+    w.Xht = b.take<uint16_t>(ci * T); w.Wht = b.take<uint16_t>(ci * co);
+  } else {
+    w.dYb = w.dYt = w.Xht = w.Wht = nullptr;
+  }
+  w.rq = b.take<float>(std::max(rowquant_bwd_ws_bytes(co, ci), rowquant_bwd_ws_bytes(T, ci)) / 4);
+  w.cs = b.take<float>(colsum_ws_bytes(T, co) / 4);
+  w.total = b.off;
+  return w;
+}
+
+int qlin_check(const omq_qlinear_desc* d) {
+  if (!d || d->struct_size < sizeof(omq_qlinear_desc)) return OMQ_E_INVALID_ARG;
+  if (!bits_ok(d->wbits) || !bits_ok(d->abits)) return OMQ_E_INVALID_ARG;
+  if (d->path != OMQ_PATH_FP32 && d->path != OMQ_PATH_BF16) return OMQ_E_INVALID_ARG;
+  if (d->T < 0 || d->c_in <= 0 || d->c_out <= 0) return OMQ_E_SHAPE;
+  if (d->c_in % 4) return OMQ_E_ALIGN;
+  if (d->path == OMQ_PATH_BF16 && (d->T % 8 || d->c_in % 8 || d->c_out % 8)) return OMQ_E_ALIGN;
+  return OMQ_OK;
+}
+
+}  // namespace
+
+size_t omq_qlinear_workspace_size(const omq_qlinear_desc* d) {
+  if (qlin_check(d) != OMQ_OK) return 0;
+  return qlin_layout(d, nullptr).total;
+}
+
+int omq_qlinear_fwd(const omq_qlinear_desc* d, const void* X, const void* W, const float* B,
+                    const float* theta, float* Y, void* ws, size_t ws_bytes, void* stream) {
+  int rc = qlin_check(d);
+  if (rc) return rc;
+  if (!X || !W || !theta || !Y) return OMQ_E_INVALID_ARG;
+  if (!al16(X) || !al16(W) || !al16(Y)) return OMQ_E_ALIGN;
+  if (!ws || ws_bytes < omq_qlinear_workspace_size(d)) return OMQ_E_WORKSPACE;
+  const QLinWs w = qlin_layout(d, ws);
+  const hipStream_t st = S(stream);
+  const int dt = d->path == OMQ_PATH_BF16 ? OMQ_BF16 : OMQ_F32;
+  const int64_t T = d->T, ci = d->c_in, co = d->c_out;
+  const float* ag = theta;
+  const float* ab = theta + co;
+  const float* s = d->use_let ? theta + 2 * co : nullptr;
+  const float* dl = d->use_let ? theta + 2 * co + ci : nullptr;
+  // weight side: LET-W, LWC, bias fold
+  RowQuantFwd a;
+  a.x = W; a.x_dt = dt; a.rows = co; a.cols = ci; a.ldx = ci;
+  a.let_mode = s ? OMQ_LET_MUL : OMQ_LET_NONE; a.s = s;
+  a.nbits = d->wbits; a.a_gamma = ag; a.a_beta = ab;
+  a.out = w.What; a.out_dt = dt; a.ldo = ci;
+  a.h = w.wh; a.z = w.wz; a.amax = w.wamax; a.amin = w.wamin;
+  a.fold_delta = dl; a.bias = B; a.bias_out = dl ? w.Bt : nullptr;
+  OMQ_HIP_CHECK(launch_rowquant_fwd(a, st));
+  if (dl && d->wbits >= 16) OMQ_HIP_CHECK(launch_bias_fold(W, dt, co, ci, dl, B, w.Bt, st));
+  const float* bias = dl ? w.Bt : B;
+  // activation side: LET-X, per-token quantizer
+  RowQuantFwd x;
+  x.x = X; x.x_dt = dt; x.rows = T; x.cols = ci; x.ldx = ci;
+  x.let_mode = s ? OMQ_LET_DIV : OMQ_LET_NONE; x.s = s; x.delta = dl;
+  x.nbits = d->abits; x.out = w.Xhat; x.out_dt = dt; x.ldo = ci;
+  x.h = w.ah; x.z = w.az; x.amax = w.aamax; x.amin = w.aamin;
+  OMQ_HIP_CHECK(launch_rowquant_fwd(x, st));
+  Gemm g;
+  g.A = w.Xhat; g.lda = ci; g.B = w.What; g.ldb = ci; g.C = Y; g.ldc = co; g.bias = bias;
+  g.M = T; g.N = co; g.K = ci; g.dt = dt;
+  OMQ_HIP_CHECK(launch_gemm(g, st));
+  return OMQ_OK;
+}
+
+int omq_qlinear_bwd(const omq_qlinear_desc* d, const void* X, const void* W, const float* theta,
+                    const float* dY, float* dX, float* dtheta, void* ws, size_t ws_bytes,
+                    void* stream) {
+  int rc = qlin_check(d);
+  if (rc) return rc;
+  if (!X || !W || !theta || !dY || !dtheta) return OMQ_E_INVALID_ARG;
+  if (!al16(X) || !al16(W) || !al16(dY) || !al16(dX)) return OMQ_E_ALIGN;
+  if (!ws || ws_bytes < omq_qlinear_workspace_size(d)) return OMQ_E_WORKSPACE;
+  const QLinWs w = qlin_layout(d, ws);
+  const hipStream_t st = S(stream);
+  const bool bf = d->path == OMQ_PATH_BF16;
+  const int dt = bf ? OMQ_BF16 : OMQ_F32;
+  const int64_t T = d->T, ci = d->c_in, co = d->c_out;
+  const float* s = d->use_let ? theta + 2 * co : nullptr;
+  const float* dl = d->use_let ? theta + 2 * co + ci : nullptr;
+  float* g_ag = dtheta;
+  float* g_ab = dtheta + co;
+  float* g_s = d->use_let ? dtheta + 2 * co : nullptr;
+  float* g_d = d->use_let ? dtheta + 2 * co + ci : nullptr;
+  // the two products of the backward
+  Gemm gw, gx;
+  if (bf) {
+    OMQ_HIP_CHECK(launch_f32_to_bf16(dY, T, co, co, w.dYb, co, w.dYt, T, st));
+    OMQ_HIP_CHECK(launch_transpose_bf16((const uint16_t*)w.Xhat, T, ci, ci, w.Xht, T, 1, 0, 0, st));
+    OMQ_HIP_CHECK(launch_transpose_bf16((const uint16_t*)w.What, co, ci, ci, w.Wht, co, 1, 0, 0, st));
+    gw.A = w.dYt; gw.lda = T; gw.B = w.Xht; gw.ldb = T;
+    gx.A = w.dYb; gx.lda = co; gx.B = w.Wht; gx.ldb = co;
+  } else {
+    gw.A = dY; gw.lda = co; gw.ta = 1; gw.B = w.Xhat; gw.ldb = ci; gw.tb = 1;
+    gx.A = dY; gx.lda = co; gx.B = w.What; gx.ldb = ci; gx.tb = 1;
+  }
+  gw.C = w.gW; gw.ldc = ci; gw.M = co; gw.N = ci; gw.K = T; gw.dt = dt;
+  OMQ_HIP_CHECK(launch_gemm(gw, st));
+  gx.C = w.gXh; gx.ldc = ci; gx.M = T; gx.N = ci; gx.K = co; gx.dt = dt;
+  OMQ_HIP_CHECK(launch_gemm(gx, st));
+  if (dl) OMQ_HIP_CHECK(launch_colsum(dY, T, co, co, w.colsum, w.cs, st));
+  // weight side: LWC straight-through backward, s grad (W side), bias-fold delta grad
+  if (d->wbits >= 16) {
+    OMQ_HIP_CHECK(hipMemsetAsync(dtheta, 0, 2 * co * sizeof(float), st));
+  }
+  RowQuantBwd a;
+  a.g = w.gW; a.ldg = ci; a.x = W; a.x_dt = dt; a.rows = co; a.cols = ci; a.ldx = ci;
+  a.let_mode = s ? OMQ_LET_MUL : OMQ_LET_NONE; a.s = s; a.nbits = d->wbits;
+  a.h = w.wh; a.z = w.wz; a.amax = w.wamax; a.amin = w.wamin;
+  a.a_gamma = theta; a.a_beta = theta + co;
+  a.col_mode = s ? COL_WEIGHT : COL_NONE; a.rowvec = dl ? w.colsum : nullptr;
+  a.g_agamma = g_ag; a.g_abeta = g_ab; a.out0 = g_s; a.out1 = g_d; a.ws = w.rq;
+  OMQ_HIP_CHECK(launch_rowquant_bwd(a, st));
+  // activation side: per-token quantizer backward through LET-X
+  if (dX || s) {
+    RowQuantBwd x;
+    x.g = w.gXh; x.ldg = ci; x.x = X; x.x_dt = dt; x.rows = T; x.cols = ci; x.ldx = ci;
+    x.let_mode = s ? OMQ_LET_DIV : OMQ_LET_NONE; x.s = s; x.delta = dl; x.nbits = d->abits;
+    x.h = w.ah; x.z = w.az; x.amax = w.aamax; x.amin = w.aamin;
+    x.col_mode = s ? COL_ACT_DIV : COL_NONE; x.gx = dX; x.ldgx = ci;
+    x.out0 = g_s; x.out1 = g_d; x.accumulate = 1; x.ws = w.rq;
+    OMQ_HIP_CHECK(launch_rowquant_bwd(x, st));
+  }
+  return OMQ_OK;
+}
+
+int omq_sgd(float* theta, const float* grad, int64_t n, int64_t n_lwc, float lr_lwc,
+            float lr_let, void* stream) {
+  if (!theta || !grad) return OMQ_E_INVALID_ARG;
+  if (n < 0 || n_lwc < 0 || n_lwc > n) return OMQ_E_SHAPE;
+  OMQ_HIP_CHECK(launch_sgd(theta, grad, n, n_lwc, lr_lwc, lr_let, S(stream)));
+  return OMQ_OK;
+}
+
+int omq_adamw(float* theta, const float* grad, float* m, float* v, int64_t n, int64_t n_lwc,
+              float lr_lwc, float lr_let, float beta1, float beta2, float eps,
+              float weight_decay, int64_t step, void* stream) {
+  if (!theta || !grad || !m || !v) return OMQ_E_INVALID_ARG;
+  if (step < 1) return OMQ_E_INVALID_ARG;
+  if (n < 0 || n_lwc < 0 || n_lwc > n) return OMQ_E_SHAPE;
+  OMQ_HIP_CHECK(launch_adamw(theta, grad, m, v, n, n_lwc, lr_lwc, lr_let, beta1, beta2, eps,
+                             weight_decay, step, S(stream)));
+  return OMQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,119 @@
+// Shared device helpers for the OmniQuant calibration kernels (gfx950).
+//
+// Every translation unit is compiled with -ffp-contract=off, so no multiply-add
+// is fused unless written as an explicit fmaf(); float division is IEEE
+// correctly rounded (-fhip-fp32-correctly-rounded-divide-sqrt) and rintf maps to
+// round-half-to-even.  These three properties make the quantizer's integer codes
+// reproducible bit for bit against a float32 reference.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/omq.h"
+
+#define OMQ_DEV __device__ __forceinline__
+
+namespace omq {
+
+constexpr int kWave = 64;
+
+OMQ_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// float32 -> bf16, round to nearest even; NaN stays NaN.
+OMQ_DEV uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u)
+    return (u & 0x007fffffu) ? (uint16_t)((u >> 16) | 0x40u) : (uint16_t)(u >> 16);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Four consecutive elements of a float32 or bf16 row, widened to float32.
+OMQ_DEV void load4(const void* base, int dt, int64_t idx, float v[4]) {
+  if (dt == OMQ_F32) {
+    float4 t = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + idx);
+    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+  } else {
+    uint2 t = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + idx);
+    v[0] = __uint_as_float(t.x << 16);
+    v[1] = __uint_as_float(t.x & 0xffff0000u);
+    v[2] = __uint_as_float(t.y << 16);
+    v[3] = __uint_as_float(t.y & 0xffff0000u);
+  }
+}
+
+OMQ_DEV void store4(void* base, int dt, int64_t idx, const float v[4]) {
+  if (dt == OMQ_F32) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + idx) =
+        make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+    uint2 t;
+    t.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    t.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(base) + idx) = t;
+  }
+}
+
+// gamma = sigmoid(a) evaluated in double and rounded once to float.
+OMQ_DEV float sigmoid_f32(float a) { return (float)(1.0 / (1.0 + exp(-(double)a))); }
+
+template <typename T>
+OMQ_DEV T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// (value, index) reductions; ties go to the lower index.
+OMQ_DEV void argmax_merge(float& v, int& i, float v2, int i2) {
+  if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
+}
+OMQ_DEV void argmin_merge(float& v, int& i, float v2, int i2) {
+  if (v2 < v || (v2 == v && i2 < i)) { v = v2; i = i2; }
+}
+
+OMQ_DEV void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float v2 = __shfl_xor(v, o, kWave);
+    int i2 = __shfl_xor(i, o, kWave);
+    argmax_merge(v, i, v2, i2);
+  }
+}
+OMQ_DEV void wave_argmin(float& v, int& i) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float v2 = __shfl_xor(v, o, kWave);
+    int i2 = __shfl_xor(i, o, kWave);
+    argmin_merge(v, i, v2, i2);
+  }
+}
+
+// The quantization step of one row (the LWC equation), float32 one op at a time:
+// h = (gamma*max - beta*min) / (2^N - 1), floored at 1e-8; z = -rint(beta*min / h).
+struct RowQ {
+  float h, z, Q, t2;
+  bool floor;
+};
+
+OMQ_DEV RowQ row_step(float M, float m, float gamma, float beta, int nbits) {
+  RowQ r;
+  r.Q = (float)((1 << nbits) - 1);
+  float t1 = gamma * M;
+  r.t2 = beta * m;
+  float h = (t1 - r.t2) / r.Q;
+  r.floor = h < 1e-8f;
+  r.h = r.floor ? 1e-8f : h;
+  r.z = -rintf(r.t2 / r.h);
+  return r;
+}
+
+}  // namespace omq
+
+#define OMQ_HIP_CHECK(expr)                                   \
+  do {                                                        \
+    hipError_t e_ = (expr);                                   \
+    if (e_ != hipSuccess) return OMQ_E_HIP;                   \
+  } while (0)

@@ -1,0 +1,406 @@
+// Block glue around the quantized linears: RMSNorm, RoPE, SiLU gating, the MSE
+// objective (paper reading, section "框架": block output reconstruction), the
+// full-precision causal softmax and its backward, and the parameter updates
+// (section "实验证据": AdamW, zero weight decay).
+#include "common.h"
+#include "kernels.h"
+
+#include <float.h>
+#include <math.h>
+
+namespace omq {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+OMQ_DEV float block_sum(float v, float* sh) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) sh[wid] = v;
+  __syncthreads();
+  return (sh[0] + sh[1]) + (sh[2] + sh[3]);
+}
+
+template <int XDT>
+__global__ __launch_bounds__(kThreads) void k_rmsnorm(const void* x, int64_t d, float eps,
+                                                      float* y, float* rstd) {
+  const int64_t r = blockIdx.x;
+  const char* xr = reinterpret_cast<const char*>(x) + r * d * (XDT == OMQ_F32 ? 4 : 2);
+  __shared__ float sh[4];
+  float ss = 0.f;
+  for (int64_t c = (int64_t)threadIdx.x * 4; c < d; c += 4 * kThreads) {
+    float v[4];
+    load4(xr, XDT, c, v);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ss = fmaf(v[j], v[j], ss);
+  }
+  ss = block_sum(ss, sh);
+  const float rs = 1.f / sqrtf(ss / (float)d + eps);
+  if (threadIdx.x == 0 && rstd) rstd[r] = rs;
+  for (int64_t c = (int64_t)threadIdx.x * 4; c < d; c += 4 * kThreads) {
+    float v[4];
+    load4(xr, XDT, c, v);
+    *reinterpret_cast<float4*>(y + r * d + c) =
+        make_float4(v[0] * rs, v[1] * rs, v[2] * rs, v[3] * rs);
+  }
+}
+
+// gx = rstd * gy - x * (rstd^3 * sum(gy * x) / d)  (+ add)
+__global__ __launch_bounds__(kThreads) void k_rmsnorm_bwd(const float* gy, const float* x,
+                                                          const float* rstd, int64_t d,
+                                                          const float* add, float* gx) {
+  const int64_t r = blockIdx.x;
+  __shared__ float sh[4];
+  float dot = 0.f;
+  for (int64_t c = (int64_t)threadIdx.x * 4; c < d; c += 4 * kThreads) {
+    const float4 a = *reinterpret_cast<const float4*>(gy + r * d + c);
+    const float4 b = *reinterpret_cast<const float4*>(x + r * d + c);
+    dot = fmaf(a.x, b.x, dot); dot = fmaf(a.y, b.y, dot);
+    dot = fmaf(a.z, b.z, dot); dot = fmaf(a.w, b.w, dot);
+  }
+  dot = block_sum(dot, sh);
+  const float rs = rstd[r];
+  const float k = rs * rs * rs * dot / (float)d;
+  for (int64_t c = (int64_t)threadIdx.x * 4; c < d; c += 4 * kThreads) {
+    const float4 a = *reinterpret_cast<const float4*>(gy + r * d + c);
+    const float4 b = *reinterpret_cast<const float4*>(x + r * d + c);
+    float4 o = make_float4(rs * a.x - b.x * k, rs * a.y - b.y * k, rs * a.z - b.z * k,
+                           rs * a.w - b.w * k);
+    if (add) {
+      const float4 e = *reinterpret_cast<const float4*>(add + r * d + c);
+      o.x += e.x; o.y += e.y; o.z += e.z; o.w += e.w;
+    }
+    *reinterpret_cast<float4*>(gx + r * d + c) = o;
+  }
+}
+
+__global__ void k_rope_tables(int64_t T, int64_t hd, float theta, float* cos_t, float* sin_t) {
+  const int64_t half = hd / 2;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= T * half) return;
+  const int64_t t = i / half, k = i % half;
+  const double inv = pow((double)theta, -2.0 * (double)k / (double)hd);
+  const double ang = (double)t * inv;
+  cos_t[i] = (float)cos(ang);
+  sin_t[i] = (float)sin(ang);
+}
+
+// rotate-half RoPE per head; inverse applies the transposed rotation
+__global__ __launch_bounds__(kThreads) void k_rope(const float* x, int64_t ldx, int64_t T,
+                                                   int64_t n_heads, int64_t hd,
+                                                   const float* cos_t, const float* sin_t,
+                                                   int inverse, float* y, int64_t ldy) {
+  const int64_t half = hd / 2;
+  const int64_t n = T * n_heads * half;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * kThreads) {
+    const int64_t k = i % half;
+    const int64_t hh = (i / half) % n_heads;
+    const int64_t t = i / (half * n_heads);
+    const float c = cos_t[t * half + k], s = sin_t[t * half + k];
+    const float a = x[t * ldx + hh * hd + k], b = x[t * ldx + hh * hd + k + half];
+    float ya, yb;
+    if (!inverse) { ya = a * c - b * s; yb = b * c + a * s; }
+    else { ya = a * c + b * s; yb = b * c - a * s; }
+    y[t * ldy + hh * hd + k] = ya;
+    y[t * ldy + hh * hd + k + half] = yb;
+  }
+}
+
+OMQ_DEV float sigmoidf_(float x) { return 1.f / (1.f + expf(-x)); }
+
+__global__ __launch_bounds__(kThreads) void k_silu_gate(const float* gu, int64_t T, int64_t F,
+                                                        float* a) {
+  const int64_t n = T * F;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * kThreads) {
+    const int64_t t = i / F, f = i % F;
+    const float g = gu[t * 2 * F + f], u = gu[t * 2 * F + F + f];
+    a[i] = g * sigmoidf_(g) * u;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void k_silu_gate_bwd(const float* gu, const float* ga,
+                                                            int64_t T, int64_t F, float* ggu) {
+  const int64_t n = T * F;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * kThreads) {
+    const int64_t t = i / F, f = i % F;
+    const float g = gu[t * 2 * F + f], u = gu[t * 2 * F + F + f];
+    const float sg = sigmoidf_(g);
+    const float d = ga[i];
+    ggu[t * 2 * F + f] = d * u * sg * (1.f + g * (1.f - sg));
+    ggu[t * 2 * F + F + f] = d * g * sg;
+  }
+}
+
+constexpr int kMseBlocks = 1024;
+
+__global__ __launch_bounds__(kThreads) void k_mse_part(const float* y, const float* t, int64_t n,
+                                                       float* dy, float* part) {
+  __shared__ float sh[4];
+  float s = 0.f;
+  const float sc = 2.f / (float)n;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * kThreads) {
+    const float d = y[i] - t[i];
+    s = fmaf(d, d, s);
+    if (dy) dy[i] = sc * d;
+  }
+  s = block_sum(s, sh);
+  if (threadIdx.x == 0) part[blockIdx.x] = s;
+}
+
+__global__ __launch_bounds__(kThreads) void k_mse_final(const float* part, int np, int64_t n,
+                                                        float* loss) {
+  __shared__ float sh[4];
+  float s = 0.f;
+  for (int i = threadIdx.x; i < np; i += kThreads) s += part[i];
+  s = block_sum(s, sh);
+  if (threadIdx.x == 0) *loss = s / (float)n;
+}
+
+// causal softmax of one row of S (scores already scaled); P is written for the
+// whole row (zeros right of the diagonal) in bf16.
+__global__ __launch_bounds__(kThreads) void k_softmax_causal(const float* S, int64_t T,
+                                                             uint16_t* P) {
+  const int64_t row = blockIdx.x;          // h * T + i
+  const int64_t i = row % T;
+  const float* s = S + row * T;
+  __shared__ float sh[4];
+  float mx = -FLT_MAX;
+  for (int64_t j = threadIdx.x; j <= i; j += kThreads) mx = fmaxf(mx, s[j]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+  float sum = 0.f;
+  for (int64_t j = threadIdx.x; j <= i; j += kThreads) sum += expf(s[j] - mx);
+  sum = block_sum(sum, sh);
+  const float inv = 1.f / sum;
+  for (int64_t j = threadIdx.x; j < T; j += kThreads)
+    P[row * T + j] = j <= i ? f32_to_bf16(expf(s[j] - mx) * inv) : (uint16_t)0;
+}
+
+// dS = P * (dP - D) * scale, D = sum_d dO * O for this (head, row); P recomputed in
+// float32 from S.
+__global__ __launch_bounds__(kThreads) void k_softmax_bwd_causal(
+    const float* S, const float* dP, const float* O, const float* dO, int64_t T, int n_heads,
+    int64_t hd, int64_t ldo, float scale, uint16_t* dS) {
+  const int64_t row = blockIdx.x;
+  const int64_t i = row % T, h = row / T;
+  const float* s = S + row * T;
+  const float* dp = dP + row * T;
+  __shared__ float sh[4];
+  float dd = 0.f;
+  for (int64_t k = threadIdx.x; k < hd; k += kThreads)
+    dd = fmaf(dO[i * ldo + h * hd + k], O[i * ldo + h * hd + k], dd);
+  const float D = block_sum(dd, sh);
+  float mx = -FLT_MAX;
+  for (int64_t j = threadIdx.x; j <= i; j += kThreads) mx = fmaxf(mx, s[j]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+  float sum = 0.f;
+  for (int64_t j = threadIdx.x; j <= i; j += kThreads) sum += expf(s[j] - mx);
+  sum = block_sum(sum, sh);
+  const float inv = 1.f / sum;
+  for (int64_t j = threadIdx.x; j < T; j += kThreads) {
+    float v = 0.f;
+    if (j <= i) v = expf(s[j] - mx) * inv * (dp[j] - D) * scale;
+    dS[row * T + j] = f32_to_bf16(v);
+  }
+}
+
+__global__ void k_kv_expand(const float* v, int64_t n_q, int64_t n_kv, int64_t hd, float* out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_q * hd) return;
+  const int64_t grp = n_q / n_kv;
+  const int64_t h = i / hd, k = i % hd;
+  out[i] = v[(h / grp) * hd + k];
+}
+
+__global__ void k_kv_reduce_add(const float* v, int64_t n_q, int64_t n_kv, int64_t hd,
+                                float* out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_kv * hd) return;
+  const int64_t grp = n_q / n_kv;
+  const int64_t g = i / hd, k = i % hd;
+  float s = 0.f;
+  for (int64_t r = 0; r < grp; ++r) s += v[(g * grp + r) * hd + k];
+  out[i] += s;
+}
+
+__global__ __launch_bounds__(kThreads) void k_adamw(float* th, const float* g, float* m, float* v,
+                                                    int64_t n, int64_t n_lwc, float lr_lwc,
+                                                    float lr_let, float b1, float b2, float eps,
+                                                    float wd, float c1, float c2) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= n) return;
+  const float lr = i < n_lwc ? lr_lwc : lr_let;
+  const float gi = g[i];
+  const float mi = b1 * m[i] + (1.f - b1) * gi;
+  const float vi = b2 * v[i] + (1.f - b2) * gi * gi;
+  m[i] = mi;
+  v[i] = vi;
+  const float mh = mi / c1, vh = vi / c2;
+  th[i] = th[i] * (1.f - lr * wd) - lr * mh / (sqrtf(vh) + eps);
+}
+
+__global__ __launch_bounds__(kThreads) void k_sgd(float* th, const float* g, int64_t n,
+                                                  int64_t n_lwc, float lr_lwc, float lr_let) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= n) return;
+  th[i] -= (i < n_lwc ? lr_lwc : lr_let) * g[i];
+}
+
+__global__ __launch_bounds__(kThreads) void k_axpy(float* y, const float* x, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i < n) y[i] += x[i];
+}
+
+unsigned grid_for(int64_t n) {
+  int64_t b = (n + kThreads - 1) / kThreads;
+  if (b > 65536) b = 65536;
+  if (b < 1) b = 1;
+  return (unsigned)b;
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm(const void* x, int x_dt, int64_t T, int64_t d, float eps, float* y,
+                          float* rstd, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  if (x_dt == OMQ_F32)
+    hipLaunchKernelGGL(k_rmsnorm<OMQ_F32>, dim3((unsigned)T), dim3(kThreads), 0, st, x, d, eps, y,
+                       rstd);
+  else
+    hipLaunchKernelGGL(k_rmsnorm<OMQ_BF16>, dim3((unsigned)T), dim3(kThreads), 0, st, x, d, eps,
+                       y, rstd);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_bwd(const float* gy, const float* x, const float* rstd, int64_t T,
+                              int64_t d, const float* add, float* gx, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rmsnorm_bwd, dim3((unsigned)T), dim3(kThreads), 0, st, gy, x, rstd, d, add,
+                     gx);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_tables(int64_t T, int64_t hd, float theta, float* cos_t, float* sin_t,
+                              hipStream_t st) {
+  const int64_t n = T * (hd / 2);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rope_tables, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, T, hd,
+                     theta, cos_t, sin_t);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope(const float* x, int64_t ldx, int64_t T, int64_t n_heads, int64_t hd,
+                       const float* cos_t, const float* sin_t, int inverse, float* y, int64_t ldy,
+                       hipStream_t st) {
+  const int64_t n = T * n_heads * (hd / 2);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rope, dim3(grid_for(n)), dim3(kThreads), 0, st, x, ldx, T, n_heads, hd,
+                     cos_t, sin_t, inverse, y, ldy);
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_gate(const float* gu, int64_t T, int64_t F, float* a, hipStream_t st) {
+  if (T * F == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_silu_gate, dim3(grid_for(T * F)), dim3(kThreads), 0, st, gu, T, F, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_gate_bwd(const float* gu, const float* ga, int64_t T, int64_t F,
+                                float* ggu, hipStream_t st) {
+  if (T * F == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_silu_gate_bwd, dim3(grid_for(T * F)), dim3(kThreads), 0, st, gu, ga, T, F,
+                     ggu);
+  return hipGetLastError();
+}
+
+hipError_t launch_mse(const float* y, const float* target, int64_t n, float* loss, float* dy,
+                      float* ws, hipStream_t st) {
+  const int nb = (int)std::min<int64_t>(kMseBlocks, (n + kThreads - 1) / kThreads);
+  if (nb == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_mse_part, dim3(nb), dim3(kThreads), 0, st, y, target, n, dy, ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !loss) return e;
+  hipLaunchKernelGGL(k_mse_final, dim3(1), dim3(kThreads), 0, st, ws, nb, n, loss);
+  return hipGetLastError();
+}
+
+hipError_t launch_softmax_causal(const float* S, int64_t T, int n_heads, uint16_t* P,
+                                 uint16_t* Pt, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_softmax_causal, dim3((unsigned)(T * n_heads)), dim3(kThreads), 0, st, S, T,
+                     P);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !Pt) return e;
+  return launch_transpose_bf16(P, T, T, T, Pt, T, n_heads, T * T, T * T, st);
+}
+
+hipError_t launch_softmax_bwd_causal(const float* S, const float* dP, const float* O,
+                                     const float* dO, int64_t T, int n_heads, int64_t hd,
+                                     int64_t ldo, float scale, uint16_t* dS, uint16_t* dSt,
+                                     hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_softmax_bwd_causal, dim3((unsigned)(T * n_heads)), dim3(kThreads), 0, st,
+                     S, dP, O, dO, T, n_heads, hd, ldo, scale, dS);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !dSt) return e;
+  return launch_transpose_bf16(dS, T, T, T, dSt, T, n_heads, T * T, T * T, st);
+}
+
+hipError_t launch_kv_expand(const float* v, int64_t n_q, int64_t n_kv, int64_t hd, float* out,
+                            hipStream_t st) {
+  const int64_t n = n_q * hd;
+  hipLaunchKernelGGL(k_kv_expand, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, v, n_q,
+                     n_kv, hd, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_reduce_add(const float* v, int64_t n_q, int64_t n_kv, int64_t hd,
+                                float* out, hipStream_t st) {
+  const int64_t n = n_kv * hd;
+  hipLaunchKernelGGL(k_kv_reduce_add, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, v, n_q,
+                     n_kv, hd, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_adamw(float* theta, const float* grad, float* m, float* v, int64_t n,
+                        int64_t n_lwc, float lr_lwc, float lr_let, float b1, float b2, float eps,
+                        float wd, int64_t step, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const float c1 = (float)(1.0 - pow((double)b1, (double)step));
+  const float c2 = (float)(1.0 - pow((double)b2, (double)step));
+  hipLaunchKernelGGL(k_adamw, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                     st, theta, grad, m, v, n, n_lwc, lr_lwc, lr_let, b1, b2, eps, wd, c1, c2);
+  return hipGetLastError();
+}
+
+hipError_t launch_sgd(float* theta, const float* grad, int64_t n, int64_t n_lwc, float lr_lwc,
+                      float lr_let, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_sgd, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                     st, theta, grad, n, n_lwc, lr_lwc, lr_let);
+  return hipGetLastError();
+}
+
+hipError_t launch_axpy_bcast(float* y, const float* x, int64_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_axpy, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                     st, y, x, n);
+  return hipGetLastError();
+}
+
+}  // namespace omq

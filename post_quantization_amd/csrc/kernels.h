@@ -1,0 +1,126 @@
+// Internal launchers of the OmniQuant calibration kernels (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace omq {
+
+// ---------------------------------------------------------------------------
+// Row quantizer (LWC equation; rows are weight output channels or tokens)
+// ---------------------------------------------------------------------------
+struct RowQuantFwd {
+  const void* x = nullptr;  int x_dt = 0;  int64_t rows = 0, cols = 0, ldx = 0;
+  int let_mode = 0;  const float* s = nullptr;  const float* delta = nullptr;
+  int nbits = 16;                                   // >= 16: pass-through (x~ only)
+  const float* a_gamma = nullptr;  const float* a_beta = nullptr;  // NULL: 1
+  void* out = nullptr;  int out_dt = 0;  int64_t ldo = 0;
+  float* h = nullptr;  float* z = nullptr;  int32_t* amax = nullptr;  int32_t* amin = nullptr;
+  uint8_t* codes = nullptr;                         // [rows x cols], ld = cols
+  const float* fold_delta = nullptr;                // bias fold: sum_i fold_delta_i x_ri
+  const float* bias = nullptr;  float* bias_out = nullptr;
+};
+hipError_t launch_rowquant_fwd(const RowQuantFwd& a, hipStream_t st);
+
+enum ColMode { COL_NONE = 0, COL_WEIGHT = 1, COL_ACT_DIV = 2, COL_ACT_MUL = 3 };
+
+// Straight-through backward, pass 1: a 2-D tile pass over (g, x) producing per-row
+// partial sums (g_h, sum g (1 - in)) per column slab, per-column partial sums per
+// row block, and (activations) the non-scatter part of the upstream gradient.
+struct RowQuantBwd {
+  const float* g = nullptr;  int64_t ldg = 0;       // dL/dx_hat
+  const void* x = nullptr;  int x_dt = 0;  int64_t rows = 0, cols = 0, ldx = 0;
+  int let_mode = 0;  const float* s = nullptr;  const float* delta = nullptr;
+  int nbits = 16;
+  const float* h = nullptr;  const float* z = nullptr;
+  const int32_t* amax = nullptr;  const int32_t* amin = nullptr;
+  const float* a_gamma = nullptr;  const float* a_beta = nullptr;
+  int col_mode = COL_NONE;
+  const float* rowvec = nullptr;                    // COL_WEIGHT: per-row v for sum_o v_o W_oi
+  float* gx = nullptr;  int64_t ldgx = 0;           // upstream gradient (activations)
+  float* g_agamma = nullptr;  float* g_abeta = nullptr;  // per row (weights)
+  float* out0 = nullptr;  float* out1 = nullptr;    // column results (g_s, g_delta)
+  int accumulate = 0;                               // add into out0/out1
+  float* ws = nullptr;                              // partial buffers
+};
+size_t rowquant_bwd_ws_bytes(int64_t rows, int64_t cols);
+hipError_t launch_rowquant_bwd(const RowQuantBwd& a, hipStream_t st);
+
+// LET alone: y = (x - delta) / s  or  y = s * x, elementwise over [rows x cols].
+hipError_t launch_let_elementwise(const void* x, int x_dt, int64_t rows, int64_t cols,
+                                  int mode, const float* s, const float* delta, void* y,
+                                  int y_dt, hipStream_t st);
+// B~ = B + W delta (float accumulate) for W [rows x cols].
+hipError_t launch_bias_fold(const void* W, int w_dt, int64_t rows, int64_t cols,
+                            const float* delta, const float* B, float* out, hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// GEMM  C = alpha A B^T (+ bias) (+ C) ; A [M x K], B [N x K]
+// ---------------------------------------------------------------------------
+enum Causal { CAUSAL_NONE = 0, CAUSAL_SKIP_UPPER = 1, CAUSAL_K_UPPER = 2, CAUSAL_K_LOWER = 3 };
+
+struct Gemm {
+  const void* A = nullptr;  int64_t lda = 0, strideA = 0;
+  const void* B = nullptr;  int64_t ldb = 0, strideB = 0;  int b_group = 1;
+  float* C = nullptr;  int64_t ldc = 0, strideC = 0;
+  uint16_t* Cb = nullptr;                           // bf16 output instead of C
+  const float* bias = nullptr;
+  const void* resid = nullptr;  int resid_dt = 0;  int64_t ldr = 0;
+  int64_t M = 0, N = 0, K = 0;  int batch = 1;
+  float alpha = 1.f;
+  int accumulate = 0;
+  int causal = CAUSAL_NONE;
+  int dt = 1;                                       // OMQ_BF16 or OMQ_F32 operands
+  int ta = 0, tb = 0;                               // float32 only: A is [K x M] / B is [K x N]
+};
+hipError_t launch_gemm(const Gemm& g, hipStream_t st);
+
+// Transposes: out[c][r] = in[r][c]  (bf16 -> bf16, or float -> bf16 with an
+// optional straight bf16 copy written beside it).
+hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, int64_t ldi,
+                                 uint16_t* out, int64_t ldo, int batch, int64_t stride_in,
+                                 int64_t stride_out, hipStream_t st);
+hipError_t launch_f32_to_bf16(const float* in, int64_t rows, int64_t cols, int64_t ldi,
+                              uint16_t* out, int64_t ldo, uint16_t* out_t, int64_t ldt,
+                              hipStream_t st);
+// out[c] = sum_r in[r][c]   (deterministic two-stage)
+hipError_t launch_colsum(const float* in, int64_t rows, int64_t cols, int64_t ld, float* out,
+                         float* ws, hipStream_t st);
+size_t colsum_ws_bytes(int64_t rows, int64_t cols);
+
+// ---------------------------------------------------------------------------
+// Block glue
+// ---------------------------------------------------------------------------
+hipError_t launch_rmsnorm(const void* x, int x_dt, int64_t T, int64_t d, float eps, float* y,
+                          float* rstd, hipStream_t st);
+hipError_t launch_rmsnorm_bwd(const float* gy, const float* x, const float* rstd, int64_t T,
+                              int64_t d, const float* add, float* gx, hipStream_t st);
+hipError_t launch_rope_tables(int64_t T, int64_t hd, float theta, float* cos_t, float* sin_t,
+                              hipStream_t st);
+hipError_t launch_rope(const float* x, int64_t ldx, int64_t T, int64_t n_heads, int64_t hd,
+                       const float* cos_t, const float* sin_t, int inverse, float* y,
+                       int64_t ldy, hipStream_t st);
+hipError_t launch_silu_gate(const float* gu, int64_t T, int64_t F, float* a, hipStream_t st);
+hipError_t launch_silu_gate_bwd(const float* gu, const float* ga, int64_t T, int64_t F,
+                                float* ggu, hipStream_t st);
+hipError_t launch_mse(const float* y, const float* target, int64_t n, float* loss, float* dy,
+                      float* ws, hipStream_t st);
+hipError_t launch_softmax_causal(const float* S, int64_t T, int n_heads, uint16_t* P,
+                                 uint16_t* Pt, hipStream_t st);
+hipError_t launch_softmax_bwd_causal(const float* S, const float* dP, const float* O,
+                                     const float* dO, int64_t T, int n_heads, int64_t hd,
+                                     int64_t ldo, float scale, uint16_t* dS, uint16_t* dSt,
+                                     hipStream_t st);
+hipError_t launch_axpy_bcast(float* y, const float* x, int64_t n, hipStream_t st);
+hipError_t launch_kv_expand(const float* v, int64_t n_q, int64_t n_kv, int64_t hd, float* out,
+                            hipStream_t st);
+hipError_t launch_kv_reduce_add(const float* v, int64_t n_q, int64_t n_kv, int64_t hd,
+                                float* out, hipStream_t st);
+hipError_t launch_adamw(float* theta, const float* grad, float* m, float* v, int64_t n,
+                        int64_t n_lwc, float lr_lwc, float lr_let, float b1, float b2,
+                        float eps, float wd, int64_t step, hipStream_t st);
+hipError_t launch_sgd(float* theta, const float* grad, int64_t n, int64_t n_lwc, float lr_lwc,
+                      float lr_let, hipStream_t st);
+
+}  // namespace omq

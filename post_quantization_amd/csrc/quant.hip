@@ -1,0 +1,462 @@
+// Row quantizer kernels for OmniQuant calibration on gfx950.
+//
+// Forward: the LWC equation of the paper reading (section "LWC") applied per row,
+// with the LET transform of the row's input fused in (section "LET").  Rows are
+// weight output channels (LWC, gamma/beta from sigmoid logits) or tokens (per-token
+// activation quantizer, gamma = beta = 1).
+//
+// Backward: the straight-through rule (rint is the identity; clamp, max/min, h and
+// z differentiated exactly) as a 2-D tile pass plus two small finalizers, the same
+// decomposition a GEMM epilogue can produce.
+#include "common.h"
+#include "kernels.h"
+
+#include <float.h>
+
+namespace omq {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kSlab = 1024;   // columns per thread block in the tile pass (256 x 4)
+
+OMQ_DEV float let_x(float x, int mode, const float* s, const float* delta, int64_t c) {
+  if (mode == OMQ_LET_DIV) {
+    float dl = delta ? delta[c] : 0.f;
+    return (x - dl) / s[c];
+  }
+  if (mode == OMQ_LET_MUL) return s[c] * x;
+  return x;
+}
+
+// ---------------------------------------------------------------------------
+// forward: one 256-thread block per row
+// ---------------------------------------------------------------------------
+template <int XDT>
+__global__ __launch_bounds__(kThreads) void k_rowquant_fwd(RowQuantFwd a) {
+  const int64_t r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wid = tid >> 6;
+  const char* xr = reinterpret_cast<const char*>(a.x) + r * a.ldx * (XDT == OMQ_F32 ? 4 : 2);
+  const int64_t cols = a.cols;
+
+  if (a.nbits >= 16) {  // pass-through: x~ only
+    for (int64_t c = (int64_t)tid * 4; c < cols; c += 4 * kThreads) {
+      float v[4];
+      load4(xr, XDT, c, v);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = let_x(v[j], a.let_mode, a.s, a.delta, c + j);
+      store4(a.out, a.out_dt, r * a.ldo + c, v);
+    }
+    return;
+  }
+
+  float vmax = -FLT_MAX, vmin = FLT_MAX, dot = 0.f;
+  int imax = 0x7fffffff, imin = 0x7fffffff;
+  for (int64_t c = (int64_t)tid * 4; c < cols; c += 4 * kThreads) {
+    float v[4];
+    load4(xr, XDT, c, v);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float xt = let_x(v[j], a.let_mode, a.s, a.delta, c + j);
+      if (xt > vmax || imax == 0x7fffffff) { vmax = xt; imax = (int)(c + j); }
+      if (xt < vmin || imin == 0x7fffffff) { vmin = xt; imin = (int)(c + j); }
+      if (a.fold_delta) dot = fmaf(a.fold_delta[c + j], v[j], dot);
+    }
+  }
+  wave_argmax(vmax, imax);
+  wave_argmin(vmin, imin);
+  dot = wave_sum(dot);
+  __shared__ float s_max[4], s_min[4], s_dot[4];
+  __shared__ int s_imax[4], s_imin[4];
+  if (lane == 0) {
+    s_max[wid] = vmax; s_imax[wid] = imax;
+    s_min[wid] = vmin; s_imin[wid] = imin;
+    s_dot[wid] = dot;
+  }
+  __syncthreads();
+  float M = s_max[0], m = s_min[0], D = s_dot[0];
+  int iM = s_imax[0], im = s_imin[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) {
+    argmax_merge(M, iM, s_max[w], s_imax[w]);
+    argmin_merge(m, im, s_min[w], s_imin[w]);
+    D += s_dot[w];
+  }
+  const float gamma = a.a_gamma ? sigmoid_f32(a.a_gamma[r]) : 1.f;
+  const float beta = a.a_beta ? sigmoid_f32(a.a_beta[r]) : 1.f;
+  const RowQ q = row_step(M, m, gamma, beta, a.nbits);
+  if (tid == 0) {
+    if (a.h) a.h[r] = q.h;
+    if (a.z) a.z[r] = q.z;
+    if (a.amax) a.amax[r] = iM;
+    if (a.amin) a.amin[r] = im;
+    if (a.bias_out) a.bias_out[r] = (a.bias ? a.bias[r] : 0.f) + D;
+  }
+  for (int64_t c = (int64_t)tid * 4; c < cols; c += 4 * kThreads) {
+    float v[4], o[4];
+    load4(xr, XDT, c, v);
+    uint32_t cw = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float xt = let_x(v[j], a.let_mode, a.s, a.delta, c + j);
+      float u = xt / q.h;
+      float rr = rintf(u) + q.z;
+      float qq = fminf(fmaxf(rr, 0.f), q.Q);
+      o[j] = (qq - q.z) * q.h;
+      cw |= ((uint32_t)qq) << (8 * j);
+    }
+    store4(a.out, a.out_dt, r * a.ldo + c, o);
+    if (a.codes) *reinterpret_cast<uint32_t*>(a.codes + r * cols + c) = cw;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// backward tile pass: grid (col slabs, row tiles); wave w takes rows w, w+4, ...
+// ---------------------------------------------------------------------------
+template <int XDT>
+__global__ __launch_bounds__(kThreads) void k_rowquant_bwd_tile(RowQuantBwd a, int rows_per_tile,
+                                                                float* rowpart, float* colpart) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wid = tid >> 6;
+  const int64_t c0 = (int64_t)blockIdx.x * kSlab;
+  const int64_t r0 = (int64_t)blockIdx.y * rows_per_tile;
+  const int64_t cols = a.cols, rows = a.rows;
+  const bool pass = a.nbits >= 16;
+  const float Q = pass ? 0.f : (float)((1 << a.nbits) - 1);
+  float acc0[16], acc1[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) { acc0[i] = 0.f; acc1[i] = 0.f; }
+
+  for (int rr_ = wid; rr_ < rows_per_tile; rr_ += 4) {
+    const int64_t r = r0 + rr_;
+    if (r >= rows) break;
+    const char* xr = reinterpret_cast<const char*>(a.x) + r * a.ldx * (XDT == OMQ_F32 ? 4 : 2);
+    const float* gr = a.g + r * a.ldg;
+    const float h = pass ? 1.f : a.h[r];
+    const float z = pass ? 0.f : a.z[r];
+    const float vrow = a.rowvec ? a.rowvec[r] : 0.f;
+    float sh = 0.f, sz = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t c = c0 + lane * 4 + 256 * k;
+      if (c >= cols) continue;
+      float v[4];
+      load4(xr, XDT, c, v);
+      const float4 g4 = *reinterpret_cast<const float4*>(gr + c);
+      const float gg[4] = {g4.x, g4.y, g4.z, g4.w};
+      float up[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float xt = let_x(v[j], a.let_mode, a.s, a.delta, c + j);
+        float gns;
+        if (pass) {
+          gns = gg[j];
+        } else {
+          const float u = xt / h;
+          const float rr = rintf(u) + z;
+          const bool in = (rr >= 0.f) && (rr <= Q);
+          const float qmz = fminf(fmaxf(rr, 0.f), Q) - z;
+          sh += gg[j] * (qmz - (in ? u : 0.f));
+          sz += in ? 0.f : gg[j];
+          gns = in ? gg[j] : 0.f;
+        }
+        const int ai = k * 4 + j;
+        switch (a.col_mode) {
+          case COL_WEIGHT:
+            acc0[ai] += gns * v[j];
+            acc1[ai] += vrow * v[j];
+            break;
+          case COL_ACT_DIV: {
+            const float sc = a.s[c + j];
+            acc0[ai] += gns * (-xt / sc);
+            acc1[ai] += gns * (-1.f / sc);
+            break;
+          }
+          case COL_ACT_MUL:
+            acc0[ai] += gns * v[j];
+            break;
+          default:
+            break;
+        }
+        if (a.let_mode == OMQ_LET_DIV) up[j] = gns / a.s[c + j];
+        else if (a.let_mode == OMQ_LET_MUL) up[j] = gns * a.s[c + j];
+        else up[j] = gns;
+      }
+      if (a.gx)
+        *reinterpret_cast<float4*>(a.gx + r * a.ldgx + c) = make_float4(up[0], up[1], up[2], up[3]);
+    }
+    if (!pass) {
+      sh = wave_sum(sh);
+      sz = wave_sum(sz);
+      if (lane == 0) {
+        rowpart[((int64_t)blockIdx.x * rows + r) * 2 + 0] = sh;
+        rowpart[((int64_t)blockIdx.x * rows + r) * 2 + 1] = sz;
+      }
+    }
+  }
+  if (a.col_mode == COL_NONE) return;
+  __shared__ float red[4][2][kSlab];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      red[wid][0][lane * 4 + 256 * k + j] = acc0[k * 4 + j];
+      red[wid][1][lane * 4 + 256 * k + j] = acc1[k * 4 + j];
+    }
+  __syncthreads();
+  for (int cl = tid; cl < kSlab; cl += kThreads) {
+    const int64_t c = c0 + cl;
+    if (c >= cols) continue;
+    float s0 = red[0][0][cl] + red[1][0][cl] + red[2][0][cl] + red[3][0][cl];
+    float s1 = red[0][1][cl] + red[1][1][cl] + red[2][1][cl] + red[3][1][cl];
+    colpart[((int64_t)blockIdx.y * 2 + 0) * cols + c] = s0;
+    colpart[((int64_t)blockIdx.y * 2 + 1) * cols + c] = s1;
+  }
+}
+
+// column finalize: out[c] (+)= sum over row tiles
+__global__ __launch_bounds__(kThreads) void k_colpart_reduce(const float* colpart, int ntiles,
+                                                             int64_t cols, float* out0,
+                                                             float* out1, int accumulate) {
+  const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (c >= cols) return;
+  float s0 = 0.f, s1 = 0.f;
+  for (int t = 0; t < ntiles; ++t) {
+    s0 += colpart[((int64_t)t * 2 + 0) * cols + c];
+    s1 += colpart[((int64_t)t * 2 + 1) * cols + c];
+  }
+  if (out0) out0[c] = (accumulate ? out0[c] : 0.f) + s0;
+  if (out1) out1[c] = (accumulate ? out1[c] : 0.f) + s1;
+}
+
+// row finalize: one thread per row.  LWC-logit gradients and the max/min scatter.
+template <int XDT>
+__global__ __launch_bounds__(kThreads) void k_rowquant_bwd_rows(RowQuantBwd a, int nslabs,
+                                                                const float* rowpart) {
+  const int64_t r = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (r >= a.rows) return;
+  float gh = 0.f, gzs = 0.f;
+  for (int s = 0; s < nslabs; ++s) {
+    gh += rowpart[((int64_t)s * a.rows + r) * 2 + 0];
+    gzs += rowpart[((int64_t)s * a.rows + r) * 2 + 1];
+  }
+  const char* xr = reinterpret_cast<const char*>(a.x) + r * a.ldx * (XDT == OMQ_F32 ? 4 : 2);
+  auto xval = [&](int64_t c) -> float {
+    return XDT == OMQ_F32 ? reinterpret_cast<const float*>(xr)[c]
+                          : bf16_to_f32(reinterpret_cast<const uint16_t*>(xr)[c]);
+  };
+  const int iM = a.amax[r], im = a.amin[r];
+  const float xM = xval(iM), xm = xval(im);
+  const float M = let_x(xM, a.let_mode, a.s, a.delta, iM);
+  const float m = let_x(xm, a.let_mode, a.s, a.delta, im);
+  const float gamma = a.a_gamma ? sigmoid_f32(a.a_gamma[r]) : 1.f;
+  const float beta = a.a_beta ? sigmoid_f32(a.a_beta[r]) : 1.f;
+  const RowQ q = row_step(M, m, gamma, beta, a.nbits);
+  const float h = q.h;
+  const float gz = -h * gzs;
+  const float G = q.floor ? 0.f : gh + gz * q.t2 / (h * h);
+  const float gt1 = G / q.Q;
+  const float gt2 = -G / q.Q - gz / h;
+  const float gM = gt1 * gamma, gm = gt2 * beta;
+  if (a.g_agamma) a.g_agamma[r] = (gt1 * M) * gamma * (1.f - gamma);
+  if (a.g_abeta) a.g_abeta[r] = (gt2 * m) * beta * (1.f - beta);
+  // scatter of dL/dmax and dL/dmin into the gradient of x~ at arg_max / arg_min
+  const int idx[2] = {iM, im};
+  const float gv[2] = {gM, gm};
+  const float xo[2] = {xM, xm};
+  const float xtl[2] = {M, m};
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int c = idx[e];
+    const float gsc = gv[e];
+    if (a.gx) {
+      float up = gsc;
+      if (a.let_mode == OMQ_LET_DIV) up = gsc / a.s[c];
+      else if (a.let_mode == OMQ_LET_MUL) up = gsc * a.s[c];
+      a.gx[r * a.ldgx + c] += up;
+    }
+    switch (a.col_mode) {
+      case COL_WEIGHT:
+        if (a.out0) atomicAdd(a.out0 + c, gsc * xo[e]);
+        break;
+      case COL_ACT_DIV:
+        if (a.out0) atomicAdd(a.out0 + c, gsc * (-xtl[e] / a.s[c]));
+        if (a.out1) atomicAdd(a.out1 + c, gsc * (-1.f / a.s[c]));
+        break;
+      case COL_ACT_MUL:
+        if (a.out0) atomicAdd(a.out0 + c, gsc * xo[e]);
+        break;
+      default:
+        break;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// LET alone, bias fold, column sums
+// ---------------------------------------------------------------------------
+template <int XDT>
+__global__ __launch_bounds__(kThreads) void k_let(const void* x, int64_t rows, int64_t cols,
+                                                  int mode, const float* s, const float* delta,
+                                                  void* y, int y_dt) {
+  const int64_t n4 = rows * cols / 4;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * kThreads) {
+    const int64_t e = i * 4;
+    const int64_t c = e % cols;
+    float v[4];
+    load4(x, XDT, e, v);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = let_x(v[j], mode, s, delta, c + j);
+    store4(y, y_dt, e, v);
+  }
+}
+
+template <int XDT>
+__global__ __launch_bounds__(kThreads) void k_bias_fold(const void* W, int64_t rows, int64_t cols,
+                                                        const float* delta, const float* B,
+                                                        float* out) {
+  const int64_t r = blockIdx.x;
+  const char* wr = reinterpret_cast<const char*>(W) + r * cols * (XDT == OMQ_F32 ? 4 : 2);
+  float dot = 0.f;
+  for (int64_t c = (int64_t)threadIdx.x * 4; c < cols; c += 4 * kThreads) {
+    float v[4];
+    load4(wr, XDT, c, v);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dot = fmaf(delta[c + j], v[j], dot);
+  }
+  dot = wave_sum(dot);
+  __shared__ float sd[4];
+  if ((threadIdx.x & 63) == 0) sd[threadIdx.x >> 6] = dot;
+  __syncthreads();
+  if (threadIdx.x == 0) out[r] = (B ? B[r] : 0.f) + ((sd[0] + sd[1]) + (sd[2] + sd[3]));
+}
+
+constexpr int kColsumRows = 64;
+
+__global__ __launch_bounds__(kThreads) void k_colsum_part(const float* in, int64_t rows,
+                                                          int64_t cols, int64_t ld, float* part) {
+  const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (c >= cols) return;
+  const int64_t r0 = (int64_t)blockIdx.y * kColsumRows;
+  float s = 0.f;
+  for (int64_t r = r0; r < r0 + kColsumRows && r < rows; ++r) s += in[r * ld + c];
+  part[(int64_t)blockIdx.y * cols + c] = s;
+}
+
+__global__ __launch_bounds__(kThreads) void k_colsum_final(const float* part, int nparts,
+                                                           int64_t cols, float* out) {
+  const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (c >= cols) return;
+  float s = 0.f;
+  for (int p = 0; p < nparts; ++p) s += part[(int64_t)p * cols + c];
+  out[c] = s;
+}
+
+int bwd_rows_per_tile(int64_t rows) { return rows >= 8192 ? 32 : 16; }
+
+}  // namespace
+
+hipError_t launch_rowquant_fwd(const RowQuantFwd& a, hipStream_t st) {
+  if (a.rows == 0 || a.cols == 0) return hipSuccess;
+  dim3 grid((unsigned)a.rows);
+  if (a.x_dt == OMQ_F32)
+    hipLaunchKernelGGL(k_rowquant_fwd<OMQ_F32>, grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_rowquant_fwd<OMQ_BF16>, grid, dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+size_t rowquant_bwd_ws_bytes(int64_t rows, int64_t cols) {
+  const int64_t nslabs = (cols + kSlab - 1) / kSlab;
+  const int R = bwd_rows_per_tile(rows);
+  const int64_t ntiles = (rows + R - 1) / R;
+  return (size_t)(nslabs * rows * 2 + ntiles * 2 * cols) * sizeof(float) + 256;
+}
+
+hipError_t launch_rowquant_bwd(const RowQuantBwd& a, hipStream_t st) {
+  if (a.rows == 0 || a.cols == 0) return hipSuccess;
+  const int64_t nslabs = (a.cols + kSlab - 1) / kSlab;
+  const int R = bwd_rows_per_tile(a.rows);
+  const int64_t ntiles = (a.rows + R - 1) / R;
+  float* rowpart = a.ws;
+  float* colpart = a.ws + nslabs * a.rows * 2;
+  dim3 grid((unsigned)nslabs, (unsigned)ntiles);
+  if (a.x_dt == OMQ_F32)
+    hipLaunchKernelGGL(k_rowquant_bwd_tile<OMQ_F32>, grid, dim3(kThreads), 0, st, a, R, rowpart,
+                       colpart);
+  else
+    hipLaunchKernelGGL(k_rowquant_bwd_tile<OMQ_BF16>, grid, dim3(kThreads), 0, st, a, R, rowpart,
+                       colpart);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.col_mode != COL_NONE && (a.out0 || a.out1)) {
+    hipLaunchKernelGGL(k_colpart_reduce, dim3((unsigned)((a.cols + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, st, colpart, (int)ntiles, a.cols, a.out0, a.out1,
+                       a.accumulate);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.nbits < 16) {
+    dim3 g2((unsigned)((a.rows + kThreads - 1) / kThreads));
+    if (a.x_dt == OMQ_F32)
+      hipLaunchKernelGGL(k_rowquant_bwd_rows<OMQ_F32>, g2, dim3(kThreads), 0, st, a,
+                         (int)nslabs, rowpart);
+    else
+      hipLaunchKernelGGL(k_rowquant_bwd_rows<OMQ_BF16>, g2, dim3(kThreads), 0, st, a,
+                         (int)nslabs, rowpart);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+hipError_t launch_let_elementwise(const void* x, int x_dt, int64_t rows, int64_t cols, int mode,
+                                  const float* s, const float* delta, void* y, int y_dt,
+                                  hipStream_t st) {
+  const int64_t n4 = rows * cols / 4;
+  if (n4 == 0) return hipSuccess;
+  unsigned blocks = (unsigned)((n4 + kThreads - 1) / kThreads);
+  if (blocks > 65536u) blocks = 65536u;
+  if (x_dt == OMQ_F32)
+    hipLaunchKernelGGL(k_let<OMQ_F32>, dim3(blocks), dim3(kThreads), 0, st, x, rows, cols, mode,
+                       s, delta, y, y_dt);
+  else
+    hipLaunchKernelGGL(k_let<OMQ_BF16>, dim3(blocks), dim3(kThreads), 0, st, x, rows, cols, mode,
+                       s, delta, y, y_dt);
+  return hipGetLastError();
+}
+
+hipError_t launch_bias_fold(const void* W, int w_dt, int64_t rows, int64_t cols,
+                            const float* delta, const float* B, float* out, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  if (w_dt == OMQ_F32)
+    hipLaunchKernelGGL(k_bias_fold<OMQ_F32>, dim3((unsigned)rows), dim3(kThreads), 0, st, W, rows,
+                       cols, delta, B, out);
+  else
+    hipLaunchKernelGGL(k_bias_fold<OMQ_BF16>, dim3((unsigned)rows), dim3(kThreads), 0, st, W,
+                       rows, cols, delta, B, out);
+  return hipGetLastError();
+}
+
+size_t colsum_ws_bytes(int64_t rows, int64_t cols) {
+  return (size_t)(((rows + kColsumRows - 1) / kColsumRows) * cols) * sizeof(float) + 256;
+}
+
+hipError_t launch_colsum(const float* in, int64_t rows, int64_t cols, int64_t ld, float* out,
+                         float* ws, hipStream_t st) {
+  if (cols == 0) return hipSuccess;
+  const int64_t np = (rows + kColsumRows - 1) / kColsumRows;
+  const unsigned cb = (unsigned)((cols + kThreads - 1) / kThreads);
+  if (np == 0) {
+    return hipMemsetAsync(out, 0, cols * sizeof(float), st);
+  }
+  hipLaunchKernelGGL(k_colsum_part, dim3(cb, (unsigned)np), dim3(kThreads), 0, st, in, rows, cols,
+                     ld, ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_colsum_final, dim3(cb), dim3(kThreads), 0, st, ws, (int)np, cols, out);
+  return hipGetLastError();
+}
+
+}  // namespace omq

@@ -1,0 +1,98 @@
+"""CPU-only checks of the C ABI: the library loads, exports every symbol that
+include/omq.h declares, rejects bad arguments before launching anything, and its
+host-side layouts (packed theta, workspace sizes) agree with the oracle's."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import post_quantization_amd as omq
+from oracle import block as ob
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "omq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(omq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    L = omq.lib()
+    names = _declared()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(L, n), n
+    assert omq.abi_version() == 1
+
+
+def test_status_strings():
+    assert omq.status_str(0) == "ok"
+    for rc in range(-1, -8, -1):
+        assert omq.status_str(rc) not in ("ok", "unknown status")
+    assert omq.status_str(-99) == "unknown status"
+
+
+FAKE = 0x10000  # a 16-byte aligned non-NULL address; never dereferenced (validation fails first)
+
+
+def test_validation_before_launch():
+    L = omq.lib()
+    # missing required pointer
+    assert L.omq_lwc_fakequant(None, 1, 4, 8, 4, FAKE, FAKE, None, None, None, FAKE, 1, FAKE,
+                               FAKE, FAKE, FAKE, None, None, None) == -1
+    # bit width out of range
+    assert L.omq_lwc_fakequant(FAKE, 1, 4, 8, 9, FAKE, FAKE, None, None, None, FAKE, 1, FAKE,
+                               FAKE, FAKE, FAKE, None, None, None) == -1
+    assert L.omq_act_quant(FAKE, 1, 4, 8, 1, 0, None, None, FAKE, 1, FAKE, FAKE, FAKE, FAKE,
+                           None, None) == -1
+    # bad dtype
+    assert L.omq_act_quant(FAKE, 7, 4, 8, 4, 0, None, None, FAKE, 1, FAKE, FAKE, FAKE, FAKE,
+                           None, None) == -3
+    # LET mode without s
+    assert L.omq_act_quant(FAKE, 1, 4, 8, 4, 1, None, None, FAKE, 1, FAKE, FAKE, FAKE, FAKE,
+                           None, None) == -1
+    # row length not a multiple of 4
+    assert L.omq_act_quant(FAKE, 1, 4, 10, 4, 0, None, None, FAKE, 1, FAKE, FAKE, FAKE, FAKE,
+                           None, None) == -4
+    # misaligned pointer
+    assert L.omq_act_quant(FAKE + 2, 1, 4, 8, 4, 0, None, None, FAKE, 1, FAKE, FAKE, FAKE, FAKE,
+                           None, None) == -4
+    # bf16 GEMM needs K % 8 == 0
+    assert L.omq_gemm(4, 4, 12, FAKE, 12, FAKE, 12, 1, None, 1.0, FAKE, 4, 0, None) == -4
+    assert L.omq_gemm(4, 4, 16, FAKE, 8, FAKE, 16, 1, None, 1.0, FAKE, 4, 0, None) == -2
+    # workspace too small
+    assert L.omq_lwc_backward(FAKE, FAKE, 1, 8, 8, 4, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                              None, FAKE, FAKE, None, None, FAKE, 16, None) == -5
+    assert L.omq_adamw(FAKE, FAKE, FAKE, FAKE, 10, 4, 1e-3, 1e-3, 0.9, 0.999, 1e-8, 0.0, 0,
+                       None) == -1
+    d = omq.QLinearDesc(T=12, c_in=16, c_out=8, wbits=4, abits=4, use_let=1, path=omq.PATH_BF16)
+    assert omq.qlinear_workspace_size(d) == 0          # bf16 path needs T % 8 == 0
+    d = omq.QLinearDesc(T=16, c_in=16, c_out=8, wbits=4, abits=4, use_let=1, path=omq.PATH_BF16)
+    assert omq.qlinear_workspace_size(d) > 0
+    assert L.omq_qlinear_fwd(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, 64, None) == -5
+    b = omq.BlockDesc(T=64, d=64, n_q=3, n_kv=2, head_dim=16, F=64, wbits=4, abits=4)
+    assert omq.block_workspace_size(b) == 0            # n_q not a multiple of n_kv
+    b = omq.BlockDesc(T=64, d=64, n_q=4, n_kv=2, head_dim=16, F=64, wbits=4, abits=4,
+                      optimizer=5)
+    assert L.omq_block_step(ctypes.byref(b), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None,
+                            FAKE, 1 << 30, None) == -1
+
+
+@pytest.mark.parametrize("kind", ["mha_w4a4", "gqa_w4a16", "ffn_w2a16"])
+def test_block_theta_layout_matches_oracle(kind):
+    c = {"mha_w4a4": synth.BLOCK_CFG4, "gqa_w4a16": synth.BLOCK_CFG5_W4,
+         "ffn_w2a16": synth.FFN_CFG3_W2}[kind]
+    d = omq.BlockDesc(T=c.T, d=c.d, n_q=c.n_q, n_kv=c.n_kv, head_dim=c.head_dim, F=c.F,
+                      wbits=c.wbits, abits=c.abits, ffn_only=c.ffn_only)
+    offs, n_lwc, total = omq.block_theta_layout(d)
+    lay = ob.theta_layout(c, synth.block_weight_shapes(c))
+    sizes = [n for _, n in lay]
+    assert total == sum(sizes)
+    assert offs == list(np.cumsum([0] + sizes[:-1]))
+    assert n_lwc == sum(n for name, n in lay if name.startswith("a_"))
+    assert omq.block_workspace_size(d) > 0

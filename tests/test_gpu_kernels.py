@@ -1,0 +1,223 @@
+"""GPU parity of the individual kernels against the CPU oracle, through the C ABI.
+
+Integer results (codes, zero points, argmax/argmin) and the float32 code path
+(step h, dequantized values) must match bit for bit: both sides evaluate the
+same float32 operations in the same order with IEEE division and rint.
+Reductions and products (bias fold, GEMM, backward sums) are compared by
+relative Frobenius norm against the oracle's float64 results.
+"""
+import numpy as np
+import pytest
+import torch
+
+import post_quantization_amd as omq
+from oracle import quant
+from oracle.ops import ExactOps
+import synth
+from gpu_util import DEV, bf16_np, dev, host, log, rel
+
+pytestmark = pytest.mark.gpu
+
+F32 = np.float32
+
+
+def _params(rng, c_out, c_in):
+    ag = rng.uniform(0.0, 6.0, c_out).astype(F32)
+    ab = rng.uniform(0.0, 6.0, c_out).astype(F32)
+    s = rng.uniform(0.5, 2.0, c_in).astype(F32)
+    d = (rng.standard_normal(c_in) * 0.1).astype(F32)
+    B = rng.standard_normal(c_out).astype(F32)
+    return ag, ab, s, d, B
+
+
+@pytest.mark.parametrize("c_out,c_in,nbits,let,out", [
+    (77, 200, 4, True, "f32"), (64, 4096, 3, True, "bf16"), (16, 11008, 2, False, "bf16"),
+    (130, 1028, 8, True, "f32"), (4096, 4096, 4, True, "bf16")])
+def test_lwc_fakequant_bitexact(c_out, c_in, nbits, let, out):
+    log("lwc_fakequant", c_out, c_in, nbits, let, out)
+    rng = np.random.default_rng(c_out + c_in)
+    W = synth.normal(90, c_out, (c_out, c_in), synth.WEIGHT_STD)
+    ag, ab, s, d, B = _params(rng, c_out, c_in)
+    if not let:
+        s = d = None
+    ref = quant.lwc_fakequant(W, ag, ab, nbits, s, d, B)
+    od = torch.float32 if out == "f32" else torch.bfloat16
+    r = omq.lwc_fakequant(dev(W, torch.bfloat16), dev(ag), dev(ab), nbits,
+                          dev(s) if let else None, dev(d) if let else None, dev(B),
+                          out_dtype=od, want_bias=True, want_codes=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(r["arg_max"]), ref.st.iM)
+    assert np.array_equal(host(r["arg_min"]), ref.st.im)
+    assert np.array_equal(host(r["h"]), ref.h)
+    assert np.array_equal(host(r["z"]), ref.z)
+    assert np.array_equal(host(r["codes"]), ref.codes)
+    expect = ref.W_hat if out == "f32" else bf16_np(ref.W_hat)
+    assert np.array_equal(host(r["W_hat"]).astype(np.float64), np.asarray(expect, np.float64))
+    assert rel(host(r["B_tilde"]), ref.B_tilde) < 1e-5
+
+
+@pytest.mark.parametrize("T,C,nbits,mode,xdt", [
+    (48, 200, 4, "div", "f32"), (33, 4096, 4, "div", "bf16"), (64, 4096, 8, "mul", "f32"),
+    (40, 11008, 4, "none", "f32"), (2048, 4096, 4, "div", "bf16")])
+def test_act_quant_bitexact(T, C, nbits, mode, xdt):
+    log("act_quant", T, C, nbits, mode, xdt)
+    rng = np.random.default_rng(T * 7 + C)
+    X = synth.outlier_activations(91, T, T, C, max(1, C // 100), 20.0, 100.0, bf16=(xdt == "bf16"))
+    if xdt == "f32":
+        X = (X * rng.uniform(0.5, 1.5, X.shape)).astype(F32)
+    s = rng.uniform(0.5, 2.0, C).astype(F32)
+    d = (rng.standard_normal(C) * 0.3).astype(F32)
+    ops = ExactOps(bf16=False)
+    if mode == "div":
+        Xt, lm = quant.let_act(X, s, d), omq.LET_DIV
+    elif mode == "mul":
+        Xt, lm, d = ops.mul(X, s), omq.LET_MUL, None
+    else:
+        Xt, lm, s, d = X, omq.LET_NONE, None, None
+    st = quant.quantize_rows(Xt, F32(1), F32(1), nbits)
+    r = omq.act_quant(dev(X, torch.float32 if xdt == "f32" else torch.bfloat16), nbits, lm,
+                      dev(s) if s is not None else None, dev(d) if d is not None else None,
+                      out_dtype=torch.float32, want_codes=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(r["codes"]), st.codes)
+    assert np.array_equal(host(r["h"]), st.h)
+    assert np.array_equal(host(r["z"]), st.z)
+    assert np.array_equal(host(r["arg_max"]), st.iM)
+    assert np.array_equal(host(r["X_hat"]), st.xhat)
+    rb = omq.act_quant(dev(X, torch.float32 if xdt == "f32" else torch.bfloat16), nbits, lm,
+                       dev(s) if s is not None else None, dev(d) if d is not None else None,
+                       out_dtype=torch.bfloat16)
+    assert np.array_equal(host(rb["X_hat"]).astype(np.float64), bf16_np(st.xhat))
+
+
+def test_act_quant_passthrough_and_let_apply():
+    rng = np.random.default_rng(3)
+    X = rng.standard_normal((24, 64)).astype(F32)
+    W = synth.normal(92, 1, (40, 64), 0.02)
+    s = rng.uniform(0.5, 2.0, 64).astype(F32)
+    d = rng.standard_normal(64).astype(F32)
+    B = rng.standard_normal(40).astype(F32)
+    r = omq.act_quant(dev(X), 16, omq.LET_DIV, dev(s), dev(d), out_dtype=torch.float32)
+    assert np.array_equal(host(r["X_hat"]), quant.let_act(X, s, d))
+    Xt, Wt, Bt = omq.let_apply(dev(s), dev(d), X=dev(X), W=dev(W, torch.bfloat16), B=dev(B),
+                               want_bias=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(Xt), quant.let_act(X, s, d))
+    assert np.array_equal(host(Wt), quant.let_weight(W, s))
+    assert rel(host(Bt), quant.bias_fold(W, B, d)) < 1e-5
+
+
+@pytest.mark.parametrize("M,N,K,dt", [(200, 136, 328, "bf16"), (128, 256, 64, "bf16"),
+                                      (2048, 4096, 4096, "bf16"), (70, 50, 36, "f32"),
+                                      (2048, 12288, 4096, "bf16")])
+def test_gemm(M, N, K, dt):
+    log("gemm", M, N, K, dt)
+    rng = np.random.default_rng(M + N + K)
+    A = rng.standard_normal((M, K)).astype(F32)
+    B = rng.standard_normal((N, K)).astype(F32)
+    bias = rng.standard_normal(N).astype(F32)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    if dt == "bf16":
+        A, B = synth.to_bf16(A), synth.to_bf16(B)
+    C = omq.gemm(dev(A, tdt), dev(B, tdt), bias=dev(bias))
+    torch.cuda.synchronize()
+    rows = np.arange(M) if M <= 256 else rng.choice(M, 96, replace=False)
+    ref = A[rows].astype(np.float64) @ B.astype(np.float64).T + bias
+    assert rel(host(C)[rows], ref) < 2e-5
+    # accumulate into the previous result
+    C2 = omq.gemm(dev(A, tdt), dev(B, tdt), C=C, accumulate=True, alpha=0.5)
+    torch.cuda.synchronize()
+    assert rel(host(C2)[rows], 1.5 * (A[rows].astype(np.float64) @ B.astype(np.float64).T) + bias) < 2e-5
+
+
+@pytest.mark.parametrize("c_out,c_in,nbits,let", [(77, 200, 4, True), (96, 4096, 2, True),
+                                                  (64, 11008, 3, False), (4096, 4096, 4, True)])
+def test_lwc_backward(c_out, c_in, nbits, let):
+    log("lwc_backward", c_out, c_in, nbits, let)
+    rng = np.random.default_rng(c_out * 3 + c_in)
+    W = synth.normal(93, c_out, (c_out, c_in), synth.WEIGHT_STD)
+    ag, ab, s, d, B = _params(rng, c_out, c_in)
+    if not let:
+        s = None
+    ref = quant.lwc_fakequant(W, ag, ab, nbits, s, None, None)
+    g = (rng.standard_normal((c_out, c_in)) * 1e-3).astype(F32)
+    v = rng.standard_normal(c_out).astype(F32)
+    gWt, gg, gb = quant.quantize_rows_bwd(g, ref.st)
+    gam, bet = ref.st.gamma.astype(np.float64), ref.st.beta.astype(np.float64)
+    r = omq.lwc_fakequant(dev(W, torch.bfloat16), dev(ag), dev(ab), nbits,
+                          dev(s) if let else None, out_dtype=torch.bfloat16)
+    ga, gbb, gs, gd = omq.lwc_backward(dev(g), dev(W, torch.bfloat16), nbits, dev(ag), dev(ab),
+                                       r["h"], r["z"], r["arg_max"], r["arg_min"],
+                                       s=dev(s) if let else None, dy_colsum=dev(v),
+                                       want_s=let, want_delta=True)
+    torch.cuda.synchronize()
+    assert rel(host(ga), gg * gam * (1 - gam)) < 1e-4
+    assert rel(host(gbb), gb * bet * (1 - bet)) < 1e-4
+    if let:
+        assert rel(host(gs), np.sum(gWt * W.astype(np.float64), axis=0)) < 1e-4
+    assert rel(host(gd), W.astype(np.float64).T @ v) < 1e-5
+
+
+@pytest.mark.parametrize("T,C,nbits,mode", [(48, 200, 4, "div"), (64, 4096, 4, "div"),
+                                            (64, 4096, 8, "mul"), (40, 11008, 4, "none"),
+                                            (2048, 4096, 4, "div"), (32, 512, 16, "div")])
+def test_act_quant_backward(T, C, nbits, mode):
+    log("act_quant_backward", T, C, nbits, mode)
+    rng = np.random.default_rng(T + 5 * C)
+    X = (rng.standard_normal((T, C)) * rng.uniform(0.2, 3.0, C)).astype(F32)
+    s = rng.uniform(0.5, 2.0, C).astype(F32)
+    d = (rng.standard_normal(C) * 0.3).astype(F32)
+    ops = ExactOps(bf16=False)
+    lm = {"div": omq.LET_DIV, "mul": omq.LET_MUL, "none": omq.LET_NONE}[mode]
+    if mode == "div":
+        Xt = quant.let_act(X, s, d)
+    elif mode == "mul":
+        Xt, d = ops.mul(X, s), None
+    else:
+        Xt, s, d = X, None, None
+    st, _ = quant.act_quant(Xt, nbits)
+    g = rng.standard_normal((T, C)).astype(F32)
+    gXt = quant.act_quant_bwd(g, st)
+    Xt64 = Xt.astype(np.float64)
+    r = omq.act_quant(dev(X), nbits, lm, dev(s) if s is not None else None,
+                      dev(d) if d is not None else None, out_dtype=torch.float32)
+    gx, gs, gd = omq.act_quant_backward(
+        dev(g), dev(X), nbits, r["h"], r["z"], r["arg_max"], r["arg_min"], lm,
+        dev(s) if s is not None else None, dev(d) if d is not None else None,
+        want_gx=True, want_s=mode != "none", want_delta=mode == "div")
+    torch.cuda.synchronize()
+    if mode == "div":
+        s64 = s.astype(np.float64)
+        assert rel(host(gx), gXt / s64) < 1e-5
+        assert rel(host(gs), np.sum(gXt * (-Xt64 / s64), axis=0)) < 1e-4
+        assert rel(host(gd), np.sum(gXt, axis=0) * (-1 / s64)) < 1e-4
+    elif mode == "mul":
+        assert rel(host(gx), gXt * s.astype(np.float64)) < 1e-5
+        assert rel(host(gs), np.sum(gXt * X.astype(np.float64), axis=0)) < 1e-4
+    else:
+        assert rel(host(gx), gXt) < 1e-5
+
+
+def test_optimizers():
+    from oracle import optim
+    rng = np.random.default_rng(9)
+    n, n_lwc = 1000, 600
+    th = rng.standard_normal(n).astype(F32)
+    g = (rng.standard_normal(n) * 1e-2).astype(F32)
+    m = (rng.standard_normal(n) * 1e-3).astype(F32)
+    v = (rng.uniform(0, 1e-4, n)).astype(F32)
+    tt, tg, tm, tv = dev(th), dev(g), dev(m), dev(v)
+    omq.adamw(tt, tg, tm, tv, n_lwc, 5e-3, 1e-2, 3)
+    torch.cuda.synchronize()
+    e1 = optim.adamw(th[:n_lwc], g[:n_lwc], m[:n_lwc], v[:n_lwc], 3, 5e-3)
+    e2 = optim.adamw(th[n_lwc:], g[n_lwc:], m[n_lwc:], v[n_lwc:], 3, 1e-2)
+    # the update (~lr) is read back through float32 theta (~1): one ulp of theta is
+    # ~2e-5 of the update, so compare updates at 1e-4
+    assert rel(host(tt) - th, np.concatenate([e1[0], e2[0]]) - th) < 1e-4
+    assert rel(host(tm), np.concatenate([e1[1], e2[1]])) < 1e-6
+    assert rel(host(tv), np.concatenate([e1[2], e2[2]])) < 1e-6
+    tt = dev(th)
+    omq.sgd(tt, tg, n_lwc, 5e-3, 1e-2)
+    torch.cuda.synchronize()
+    lr = np.where(np.arange(n) < n_lwc, 5e-3, 1e-2)
+    assert rel(host(tt) - th, -lr * g) < 1e-4
