@@ -1,0 +1,223 @@
+"""Benchmark of the OmniQuant block-calibration step on one MI355X.
+
+One step = quantized forward of a LLaMA-7B-shaped decoder block (LWC + LET,
+W4A4, s_a on Q/K) on one 2048-token sample, the MSE against the full-precision
+block output, the straight-through backward for every learnable parameter, and
+the AdamW update.  The full-precision target is computed once, before timing.
+Inputs are seeded synthetic tensors of the real shapes (random-init weights,
+activations with systematic outlier channels) resident in HBM before timing.
+
+Prints one JSON line.  Other workloads (--workload) are available for
+exploration; the default is the headline one.
+"""
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "LWC+LET block fwd+bwd calib steps/s & TFLOP/s, LLaMA-7B-shaped, W4A4, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0
+
+
+def workloads():
+    import synth
+    return {
+        "llama7b_block_w4a4": synth.BLOCK_CFG4,
+        "llama70b_block_w4a16": synth.BLOCK_CFG5_W4,
+        "llama70b_block_w2a16": synth.BLOCK_CFG5_W2,
+        "llama7b_ffn_w3a16": synth.FFN_CFG3_W3,
+        "llama7b_ffn_w2a16": synth.FFN_CFG3_W2,
+    }
+
+
+def step_flops(c):
+    """Algorithmic FLOPs of one step: GEMMs 6 T sum(W) (forward 2, backward 4);
+    attention counts the causal half, forward 2 T^2 n_q hd, backward twice that."""
+    import synth
+    shapes = synth.block_weight_shapes(c)
+    names = ("gate", "up", "down") if c.ffn_only else synth.WEIGHT_NAMES
+    sw = sum(shapes[n][0] * shapes[n][1] for n in names)
+    f = 6.0 * c.T * sw
+    if not c.ffn_only:
+        f += 3.0 * 2.0 * c.T * c.T * c.n_q * c.head_dim
+    return f
+
+
+def cpu_baseline(c, inp, tokens):
+    """The oracle (never tuned for speed) on a bounded sample of the workload:
+    the same block with only `tokens` of the 2048 tokens, one full step
+    (forward, MSE, backward, AdamW); steps/s scaled linearly to the full token
+    count (the weight-side quantizer work does not shrink with tokens, so this
+    understates the oracle's full-size time per token only mildly)."""
+    import numpy as np
+    import synth
+    from oracle import block as ob
+    from oracle import optim
+    from oracle.ops import ExactOps
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    cs = synth.reduced(c, T=tokens)
+    x = inp["x"][:tokens]
+    Wd = {k: v for k, v in inp.items() if k.startswith("W_")}
+    ystar = ob.reference(cs, x, Wd)
+    shapes = synth.block_weight_shapes(cs)
+    th = ob.init_theta(cs, shapes)
+    t0 = time.perf_counter()
+    loss, g, _, _ = ob.calib_step(cs, x, Wd, ystar, th, ExactOps(bf16=True))
+    vec = ob.pack(cs, shapes, th)
+    gv = ob.pack(cs, shapes, {k: np.asarray(v, np.float32) for k, v in g.items()})
+    z = np.zeros_like(vec)
+    optim.adamw(vec, gv, z, z, 1, c.lr_let)
+    dt = time.perf_counter() - t0
+    sec_full = dt * (c.T / tokens)
+    return {"value": 1.0 / sec_full, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": "one oracle step (fwd+MSE+bwd+AdamW) on %d of %d tokens, all weights "
+                      "full size; %.1f s measured, scaled x%d to the full token count"
+                      % (tokens, c.T, dt, c.T // tokens),
+            "host": platform.processor() or platform.machine()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama7b_block_w4a4", choices=list(workloads()))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=256)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (the block-calibration step does not "
+              "shard across GPUs here); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import post_quantization_amd as omq
+    import synth
+
+    c = workloads()[args.workload]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    inp = synth.block_inputs(c)
+    bf = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)
+    W = [bf(inp["W_" + n]) if ("W_" + n) in inp else None for n in synth.WEIGHT_NAMES]
+    x = bf(inp["x"])
+    n_launch_cap = 64 * (args.steps + 1)
+    timer = omq.GemmTimer(n_launch_cap)
+    d = omq.BlockDesc(T=c.T, d=c.d, n_q=c.n_q, n_kv=c.n_kv, head_dim=c.head_dim, F=c.F,
+                      wbits=c.wbits, abits=c.abits, ffn_only=c.ffn_only, eps=c.eps,
+                      rope_theta=c.rope_theta, lr_lwc=c.lr_lwc, lr_let=c.lr_let)
+    dt_ = omq.BlockDesc(T=c.T, d=c.d, n_q=c.n_q, n_kv=c.n_kv, head_dim=c.head_dim, F=c.F,
+                        wbits=c.wbits, abits=c.abits, ffn_only=c.ffn_only, eps=c.eps,
+                        rope_theta=c.rope_theta, lr_lwc=c.lr_lwc, lr_let=c.lr_let, timer=timer)
+    offs, n_lwc, total = omq.block_theta_layout(d)
+    # initial parameters: clipping logits 4.0, s = 1, delta = 0, s_a = 1
+    th0 = np.ones(total, np.float32)
+    th0[:n_lwc] = 4.0
+    ends = list(offs[1:]) + [total]
+    for j, (a, b) in enumerate(zip(offs, ends)):
+        if a >= n_lwc and (j - offs.index(n_lwc)) % 2 == 1 and b - a > 0:
+            th0[a:b] = 0.0                       # the delta entries
+    if not c.ffn_only and c.abits < 16:
+        th0[offs[-1]:] = 1.0                     # s_a
+    theta = torch.from_numpy(th0).to(dev)
+    dtheta = torch.zeros_like(theta)
+    m = torch.zeros_like(theta)
+    v = torch.zeros_like(theta)
+    loss = torch.zeros(1, dtype=torch.float32, device=dev)
+    ws = torch.empty(omq.block_workspace_size(d), dtype=torch.uint8, device=dev)
+    y_t = torch.empty(c.T, c.d, dtype=torch.float32, device=dev)
+
+    # full-precision target, once
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    omq.block_forward(d, x, W, None, y_t, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    fp_ms = e0.elapsed_time(e1)
+
+    step = 0
+    for _ in range(args.warmup):
+        step += 1
+        omq.block_step(d, x, y_t, W, theta, dtheta, m, v, step, loss, ws)
+    torch.cuda.synchronize()
+    loss_first = float(loss.cpu()[0]) if args.warmup else None
+
+    timer.reset()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step += 1
+        omq.block_step(dt_, x, y_t, W, theta, dtheta, m, v, step, loss, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    loss_last = float(loss.cpu()[0])
+    durs = timer.durations_ms()
+    n_l = len(durs)
+    gemm_ms = sum(durs)
+    gemm_flops = timer.struct.flops
+    avg_dur_s = gemm_ms / n_l / 1e3
+    flops_per_launch = gemm_flops / n_l
+    achieved = flops_per_launch / avg_dur_s / 1e12
+    sps = 1000.0 / ms
+    tflops = step_flops(c) * sps / 1e12
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(c, inp, min(args.cpu_tokens, c.T))
+
+    out = {
+        "metric": METRIC,
+        "value": round(sps, 4),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "T": c.T, "d": c.d, "n_q": c.n_q, "n_kv": c.n_kv,
+                   "head_dim": c.head_dim, "F": c.F, "wbits": c.wbits, "abits": c.abits,
+                   "optimizer": "adamw", "parallelism": "none"},
+        "tflops": round(tflops, 2),
+        "step_tflop": round(step_flops(c) / 1e12, 4),
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "fp_target_ms": round(fp_ms, 3),
+        "loss_first_warmup": loss_first,
+        "loss_last": loss_last,
+        "roofline": {
+            "kernel": "k_gemm_bf16 (all matrix-core GEMM launches of the timed steps)",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "launches": n_l,
+            "avg_launch_us": round(avg_dur_s * 1e6, 2),
+            "gemm_share_of_step": round(gemm_ms / (ms * args.steps), 4),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

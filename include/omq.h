@@ -124,14 +124,17 @@ int omq_act_quant(const void* X, int x_dt, int64_t T, int64_t C, int n_bits, int
 /*
  * omq_gemm -- the quantized layer's contraction (paper reading, section "LET":
  * Y = Q_a(X~) Q_w(W~) + B~, and the two products of its backward):
- *   C[M x N] (float32) = alpha * A[M x K] * B[N x K]^T + bias[N]  (bias NULL = 0)
+ *   C[M x N] (float32) = alpha * op(A) * op(B)^T + bias[N]  (bias NULL = 0)
+ * op(A) is [M x K]: A stored [M x K] row-major (trans_a = 0) or [K x M] (trans_a = 1);
+ * op(B) is [N x K]: B stored [N x K] (trans_b = 0) or [K x N] (trans_b = 1).
  * A and B are both dt (OMQ_BF16 on the matrix cores with float32 accumulation,
- * or OMQ_F32), row-major with leading dimensions lda, ldb, ldc (elements).
+ * or OMQ_F32); lda, ldb, ldc are leading dimensions in elements.
  * accumulate != 0 adds the result to C's current contents.
+ * bf16: the contiguous extent of each operand and lda, ldb must be multiples of 8.
  */
-int omq_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
-             int64_t ldb, int dt, const float* bias, float alpha, float* C, int64_t ldc,
-             int accumulate, void* stream);
+int omq_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int trans_a,
+             const void* B, int64_t ldb, int trans_b, int dt, const float* bias, float alpha,
+             float* C, int64_t ldc, int accumulate, void* stream);
 
 /*
  * omq_lwc_backward -- straight-through backward of omq_lwc_fakequant.
@@ -227,6 +230,21 @@ int omq_adamw(float* theta, const float* grad, float* m, float* v, int64_t n, in
               float weight_decay, int64_t step, void* stream);
 
 /*
+ * Optional timing of the matrix-core contractions of a block step (benchmarks).
+ * The caller creates 2 * capacity hipEvent_t handles in `events`; while
+ * count < capacity the library records events[2*count] before and
+ * events[2*count+1] after each GEMM launch it issues on the call's stream,
+ * increments count, and adds the launch's algorithmic FLOPs to flops (2 M N K per
+ * batch entry; the causal attention products count their causal half).
+ */
+typedef struct omq_timer {
+  void** events;
+  int capacity;
+  int count;
+  double flops;
+} omq_timer;
+
+/*
  * A LLaMA-shaped decoder block (or its FFN alone): RMSNorm (unit gain) -> q/k/v ->
  * RoPE (rotate-half) -> s_a on Q/K -> causal scaled attention with float32
  * softmax -> o -> residual -> RMSNorm -> SiLU(gate) * up -> down -> residual.
@@ -248,6 +266,7 @@ typedef struct omq_block_desc {
   int optimizer;      /* OMQ_OPT_ADAMW or OMQ_OPT_SGD */
   float lr_lwc, lr_let;
   float beta1, beta2, adam_eps, weight_decay;
+  omq_timer* timer;   /* NULL, or per-launch GEMM timing (host struct, caller-owned) */
 } omq_block_desc;
 
 /*

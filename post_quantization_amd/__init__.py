@@ -19,7 +19,7 @@ __all__ = [
     "qlinear_workspace_size", "qlinear_fwd", "qlinear_bwd", "sgd", "adamw", "BlockDesc",
     "block_theta_layout", "block_workspace_size", "block_forward", "block_step",
     "F32", "BF16", "LET_NONE", "LET_DIV", "LET_MUL", "PATH_FP32", "PATH_BF16",
-    "OPT_ADAMW", "OPT_SGD",
+    "OPT_ADAMW", "OPT_SGD", "GemmTimer",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -50,19 +50,66 @@ class QLinearDesc(ctypes.Structure):
                          int(use_let), path)
 
 
+class OmqTimer(ctypes.Structure):
+    _fields_ = [("events", ctypes.POINTER(ctypes.c_void_p)), ("capacity", _int),
+                ("count", _int), ("flops", ctypes.c_double)]
+
+
+def _hip():
+    """The HIP runtime already loaded in this process (torch's)."""
+    path = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+    return ctypes.CDLL(path if os.path.exists(path) else "libamdhip64.so")
+
+
+class GemmTimer:
+    """Event pairs the library records around each matrix-core GEMM of a block step."""
+
+    def __init__(self, capacity: int):
+        hip = _hip()
+        hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), _vp, _vp]
+        self._hip = hip
+        self._ev = (ctypes.c_void_p * (2 * capacity))()
+        for i in range(2 * capacity):
+            e = ctypes.c_void_p()
+            rc = hip.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise OmqError("hipEventCreate failed (%d)" % rc)
+            self._ev[i] = e.value
+        self.struct = OmqTimer(ctypes.cast(self._ev, ctypes.POINTER(ctypes.c_void_p)), capacity,
+                               0, 0.0)
+
+    def reset(self):
+        self.struct.count = 0
+        self.struct.flops = 0.0
+
+    def durations_ms(self):
+        out = []
+        f = ctypes.c_float()
+        for i in range(self.struct.count):
+            rc = self._hip.hipEventElapsedTime(ctypes.byref(f), self._ev[2 * i],
+                                               self._ev[2 * i + 1])
+            if rc != 0:
+                raise OmqError("hipEventElapsedTime failed (%d)" % rc)
+            out.append(f.value)
+        return out
+
+
 class BlockDesc(ctypes.Structure):
     _fields_ = [("struct_size", _sz), ("T", _i64), ("d", _i64), ("n_q", _i64),
                 ("n_kv", _i64), ("head_dim", _i64), ("F", _i64), ("wbits", _int),
                 ("abits", _int), ("ffn_only", _int), ("eps", _f), ("rope_theta", _f),
                 ("optimizer", _int), ("lr_lwc", _f), ("lr_let", _f), ("beta1", _f),
-                ("beta2", _f), ("adam_eps", _f), ("weight_decay", _f)]
+                ("beta2", _f), ("adam_eps", _f), ("weight_decay", _f),
+                ("timer", ctypes.POINTER(OmqTimer))]
 
     def __init__(self, T, d, n_q, n_kv, head_dim, F, wbits, abits, ffn_only=False, eps=1e-6,
                  rope_theta=10000.0, optimizer=OPT_ADAMW, lr_lwc=5e-3, lr_let=1e-2,
-                 beta1=0.9, beta2=0.999, adam_eps=1e-8, weight_decay=0.0):
+                 beta1=0.9, beta2=0.999, adam_eps=1e-8, weight_decay=0.0, timer=None):
         super().__init__(ctypes.sizeof(BlockDesc), T, d, n_q, n_kv, head_dim, F, wbits, abits,
                          int(ffn_only), eps, rope_theta, optimizer, lr_lwc, lr_let, beta1,
-                         beta2, adam_eps, weight_decay)
+                         beta2, adam_eps, weight_decay,
+                         ctypes.pointer(timer.struct) if timer is not None else None)
 
 
 _SIGS = {
@@ -74,8 +121,8 @@ _SIGS = {
                              _vp, _int, _vp, _vp]),
     "omq_act_quant": (_int, [_vp, _int, _i64, _i64, _int, _int, _vp, _vp, _vp, _int, _vp, _vp,
                              _vp, _vp, _vp, _vp]),
-    "omq_gemm": (_int, [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _int, _vp, _f, _vp, _i64, _int,
-                        _vp]),
+    "omq_gemm": (_int, [_i64, _i64, _i64, _vp, _i64, _int, _vp, _i64, _int, _int, _vp, _f, _vp,
+                        _i64, _int, _vp]),
     "omq_lwc_backward_workspace_size": (_sz, [_i64, _i64]),
     "omq_lwc_backward": (_int, [_vp, _vp, _int, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -204,14 +251,16 @@ def act_quant(X, n_bits, let_mode=LET_NONE, s=None, delta=None, out_dtype=torch.
     return r
 
 
-def gemm(A, B, bias=None, alpha=1.0, C=None, accumulate=False):
-    """C = alpha A B^T (+ bias) (+ C);  A [M x K], B [N x K], both bf16 or both float32."""
-    M, K = A.shape
-    N = B.shape[0]
+def gemm(A, B, bias=None, alpha=1.0, C=None, accumulate=False, trans_a=False, trans_b=False):
+    """C = alpha op(A) op(B)^T (+ bias) (+ C).  op(A) [M x K] is A, or A^T when trans_a
+    (A stored [K x M]); op(B) [N x K] is B, or B^T when trans_b.  bf16 or float32."""
+    K, M = A.shape if trans_a else A.shape[::-1]
+    N = B.shape[1] if trans_b else B.shape[0]
     if C is None:
         C = torch.empty(M, N, dtype=torch.float32, device=A.device)
-    _check("omq_gemm", lib().omq_gemm(M, N, K, _p(A), K, _p(B), K, _dt(A), _p(bias), alpha,
-                                      _p(C), N, int(accumulate), _stream()))
+    _check("omq_gemm", lib().omq_gemm(M, N, K, _p(A), A.shape[1], int(trans_a), _p(B),
+                                      B.shape[1], int(trans_b), _dt(A), _p(bias), alpha, _p(C),
+                                      N, int(accumulate), _stream()))
     return C
 
 

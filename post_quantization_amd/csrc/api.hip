@@ -107,17 +107,20 @@ int omq_act_quant(const void* X, int x_dt, int64_t T, int64_t C, int n_bits, int
   return OMQ_OK;
 }
 
-int omq_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
-             int64_t ldb, int dt, const float* bias, float alpha, float* C, int64_t ldc,
-             int accumulate, void* stream) {
+int omq_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int trans_a,
+             const void* B, int64_t ldb, int trans_b, int dt, const float* bias, float alpha,
+             float* C, int64_t ldc, int accumulate, void* stream) {
   if (!A || !B || !C) return OMQ_E_INVALID_ARG;
   if (!dt_ok(dt)) return OMQ_E_DTYPE;
-  if (M < 0 || N < 0 || K < 0 || lda < K || ldb < K || ldc < N) return OMQ_E_SHAPE;
-  if (dt == OMQ_BF16 && (K % 8 || lda % 8 || ldb % 8 || !al16(A) || !al16(B)))
+  if (M < 0 || N < 0 || K < 0 || ldc < N) return OMQ_E_SHAPE;
+  if (lda < (trans_a ? M : K) || ldb < (trans_b ? N : K)) return OMQ_E_SHAPE;
+  if (dt == OMQ_BF16 && ((trans_a ? M : K) % 8 || (trans_b ? N : K) % 8 || lda % 8 ||
+                         ldb % 8 || !al16(A) || !al16(B)))
     return OMQ_E_ALIGN;
   Gemm g;
   g.A = A; g.lda = lda; g.B = B; g.ldb = ldb; g.C = C; g.ldc = ldc; g.bias = bias;
   g.M = M; g.N = N; g.K = K; g.alpha = alpha; g.accumulate = accumulate; g.dt = dt;
+  g.ta = trans_a != 0; g.tb = trans_b != 0;
   OMQ_HIP_CHECK(launch_gemm(g, S(stream)));
   return OMQ_OK;
 }
@@ -199,7 +202,7 @@ struct QLinWs {
   void* What; float *wh, *wz; int32_t *wamax, *wamin; float* Bt;
   void* Xhat; float *ah, *az; int32_t *aamax, *aamin;
   float *gW, *gXh, *colsum;
-  uint16_t *dYb, *dYt, *Xht, *Wht;
+  uint16_t* dYb;
   float *rq, *cs;
   size_t total;
 };
@@ -220,13 +223,13 @@ QLinWs qlin_layout(const omq_qlinear_desc* d, void* base) {
   w.gW = b.take<float>(co * ci);
   w.gXh = b.take<float>(T * ci);
   w.colsum = b.take<float>(co);
-  if (bf) {
-    w.dYb = b.take<uint16_t>(T * co); w.dYt = b.take<uint16_t>(co * T);
-    w.Xht = b.take<uint16_t>(ci * T); w.Wht = b.take<uint16_t>(ci * co);
-  } else {
-    w.dYb = w.dYt = w.Xht = w.Wht = nullptr;
-  }
-  w.rq = b.take<float>(std::max(rowquant_bwd_ws_bytes(co, ci), rowquant_bwd_ws_bytes(T, ci)) / 4);
+  w.dYb = bf ? b.take<uint16_t>(T * co) : nullptr;
+  int64_t n1, t1, n2, t2;
+  gemm_ste_extents(co, ci, &n1, &t1);
+  gemm_ste_extents(T, ci, &n2, &t2);
+  w.rq = b.take<float>(std::max({rowquant_bwd_ws_bytes(co, ci) / 4, rowquant_bwd_ws_bytes(T, ci) / 4,
+                                 ste_partials_floats(co, ci, n1, t1),
+                                 ste_partials_floats(T, ci, n2, t2)}));
   w.cs = b.take<float>(colsum_ws_bytes(T, co) / 4);
   w.total = b.off;
   return w;
@@ -308,27 +311,67 @@ int omq_qlinear_bwd(const omq_qlinear_desc* d, const void* X, const void* W, con
   float* g_ab = dtheta + co;
   float* g_s = d->use_let ? dtheta + 2 * co : nullptr;
   float* g_d = d->use_let ? dtheta + 2 * co + ci : nullptr;
-  // the two products of the backward
-  Gemm gw, gx;
+  // dW = dY^T X_hat and dX_hat = dY W_hat, with dY^T, X_hat and W_hat read K-major
+  if (dl) OMQ_HIP_CHECK(launch_colsum(dY, T, co, co, w.colsum, w.cs, st));
+  if (d->wbits >= 16) OMQ_HIP_CHECK(hipMemsetAsync(dtheta, 0, 2 * co * sizeof(float), st));
   if (bf) {
-    OMQ_HIP_CHECK(launch_f32_to_bf16(dY, T, co, co, w.dYb, co, w.dYt, T, st));
-    OMQ_HIP_CHECK(launch_transpose_bf16((const uint16_t*)w.Xhat, T, ci, ci, w.Xht, T, 1, 0, 0, st));
-    OMQ_HIP_CHECK(launch_transpose_bf16((const uint16_t*)w.What, co, ci, ci, w.Wht, co, 1, 0, 0, st));
-    gw.A = w.dYt; gw.lda = T; gw.B = w.Xht; gw.ldb = T;
-    gx.A = w.dYb; gx.lda = co; gx.B = w.Wht; gx.ldb = co;
-  } else {
-    gw.A = dY; gw.lda = co; gw.ta = 1; gw.B = w.Xhat; gw.ldb = ci; gw.tb = 1;
-    gx.A = dY; gx.lda = co; gx.B = w.What; gx.ldb = ci; gx.tb = 1;
+    // bf16 path: both straight-through passes run in the GEMM epilogues
+    OMQ_HIP_CHECK(launch_f32_to_bf16(dY, T, co, co, w.dYb, co, nullptr, 0, st));
+    int64_t nsl, ntl;
+    if (d->wbits < 16 || s) {
+      gemm_ste_extents(co, ci, &nsl, &ntl);
+      float* rowpart = w.rq;
+      float* colpart = w.rq + nsl * co * 2;
+      Gemm g;
+      g.A = w.dYb; g.lda = co; g.ta = 1; g.B = w.Xhat; g.ldb = ci; g.tb = 1;
+      g.ldc = ci; g.M = co; g.N = ci; g.K = T;
+      SteEpi& se = g.ste;
+      se.mode = 1; se.nseg = 1; se.seg_end[0] = co; se.xseg[0] = W;
+      se.x_dt = OMQ_BF16; se.ldx = ci; se.let_mode = s ? OMQ_LET_MUL : OMQ_LET_NONE; se.s = s;
+      se.h = w.wh; se.z = w.wz; se.nbits = d->wbits; se.rowvec = dl ? w.colsum : nullptr;
+      se.col_mode = s ? COL_WEIGHT : COL_NONE; se.rowpart = rowpart; se.colpart = colpart;
+      OMQ_HIP_CHECK(launch_gemm(g, st));
+      RowQuantBwd a;
+      a.x = W; a.x_dt = OMQ_BF16; a.rows = co; a.cols = ci; a.ldx = ci;
+      a.let_mode = se.let_mode; a.s = s; a.nbits = d->wbits;
+      a.h = w.wh; a.z = w.wz; a.amax = w.wamax; a.amin = w.wamin;
+      a.a_gamma = theta; a.a_beta = theta + co; a.g_agamma = g_ag; a.g_abeta = g_ab;
+      a.col_mode = se.col_mode; a.out0 = g_s; a.out1 = g_d;
+      OMQ_HIP_CHECK(launch_ste_colfinal(a, (int)ntl, colpart, st));
+      OMQ_HIP_CHECK(launch_ste_rowfinal(a, (int)nsl, rowpart, st));
+    }
+    if (dX || s) {
+      gemm_ste_extents(T, ci, &nsl, &ntl);
+      float* rowpart = w.rq;
+      float* colpart = w.rq + nsl * T * 2;
+      Gemm g;
+      g.A = w.dYb; g.lda = co; g.B = w.What; g.ldb = ci; g.tb = 1;
+      g.C = dX ? dX : w.gXh; g.ldc = ci; g.M = T; g.N = ci; g.K = co;
+      SteEpi& se = g.ste;
+      se.mode = 2; se.nseg = 1; se.seg_end[0] = T; se.xseg[0] = X;
+      se.x_dt = OMQ_BF16; se.ldx = ci; se.let_mode = s ? OMQ_LET_DIV : OMQ_LET_NONE;
+      se.s = s; se.delta = dl; se.h = w.ah; se.z = w.az; se.nbits = d->abits;
+      se.col_mode = s ? COL_ACT_DIV : COL_NONE; se.rowpart = rowpart; se.colpart = colpart;
+      OMQ_HIP_CHECK(launch_gemm(g, st));
+      RowQuantBwd x;
+      x.x = X; x.x_dt = OMQ_BF16; x.rows = T; x.cols = ci; x.ldx = ci;
+      x.let_mode = se.let_mode; x.s = s; x.delta = dl; x.nbits = d->abits;
+      x.h = w.ah; x.z = w.az; x.amax = w.aamax; x.amin = w.aamin;
+      x.col_mode = se.col_mode; x.gx = g.C; x.ldgx = ci; x.out0 = g_s; x.out1 = g_d;
+      x.accumulate = 1;
+      OMQ_HIP_CHECK(launch_ste_colfinal(x, (int)ntl, colpart, st));
+      OMQ_HIP_CHECK(launch_ste_rowfinal(x, (int)nsl, rowpart, st));
+    }
+    return OMQ_OK;
   }
+  // fp32 path: the products, then the tile passes
+  Gemm gw, gx;
+  gw.A = dY; gw.lda = co; gw.ta = 1; gw.B = w.Xhat; gw.ldb = ci; gw.tb = 1;
+  gx.A = dY; gx.lda = co; gx.B = w.What; gx.ldb = ci; gx.tb = 1;
   gw.C = w.gW; gw.ldc = ci; gw.M = co; gw.N = ci; gw.K = T; gw.dt = dt;
   OMQ_HIP_CHECK(launch_gemm(gw, st));
   gx.C = w.gXh; gx.ldc = ci; gx.M = T; gx.N = ci; gx.K = co; gx.dt = dt;
   OMQ_HIP_CHECK(launch_gemm(gx, st));
-  if (dl) OMQ_HIP_CHECK(launch_colsum(dY, T, co, co, w.colsum, w.cs, st));
-  // weight side: LWC straight-through backward, s grad (W side), bias-fold delta grad
-  if (d->wbits >= 16) {
-    OMQ_HIP_CHECK(hipMemsetAsync(dtheta, 0, 2 * co * sizeof(float), st));
-  }
   RowQuantBwd a;
   a.g = w.gW; a.ldg = ci; a.x = W; a.x_dt = dt; a.rows = co; a.cols = ci; a.ldx = ci;
   a.let_mode = s ? OMQ_LET_MUL : OMQ_LET_NONE; a.s = s; a.nbits = d->wbits;
@@ -337,7 +380,6 @@ int omq_qlinear_bwd(const omq_qlinear_desc* d, const void* X, const void* W, con
   a.col_mode = s ? COL_WEIGHT : COL_NONE; a.rowvec = dl ? w.colsum : nullptr;
   a.g_agamma = g_ag; a.g_abeta = g_ab; a.out0 = g_s; a.out1 = g_d; a.ws = w.rq;
   OMQ_HIP_CHECK(launch_rowquant_bwd(a, st));
-  // activation side: per-token quantizer backward through LET-X
   if (dX || s) {
     RowQuantBwd x;
     x.g = w.gXh; x.ldg = ci; x.x = X; x.x_dt = dt; x.rows = T; x.cols = ci; x.ldx = ci;

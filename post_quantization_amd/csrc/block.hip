@@ -89,12 +89,11 @@ struct Ws {
   float *Bt_qkv, *Bt_o, *Bt_gu;
   // forward activations
   float *cos_t, *sin_t, *xn, *r1, *Yqkv, *Qr, *Kr, *S, *O, *h1, *r2, *xn2, *GU, *A, *y;
-  uint16_t *Xqkv, *Qh, *Kh, *Vh, *Vt, *P, *Xo, *Xf, *Xd;
+  uint16_t *Xqkv, *Qh, *Kh, *Vh, *P, *Xo, *Xf, *Xd;
   Stats a_qkv, a_q, a_k, a_v, a_o, a_f, a_d;
   // backward
-  float *dy, *gW, *gX, *gA, *gGU, *gxn2, *dh1, *gO, *gQh, *gKh, *gVh, *gQr, *gKr, *gY, *dP;
-  uint16_t *dyb, *dyt, *Wt, *Xt, *gGUb, *gGUt, *dh1b, *dh1t, *gOb, *gOt, *Pt, *dS, *dSt, *Qt,
-      *Kt, *gYb, *gYt;
+  float *dy, *gX, *gA, *gGU, *gxn2, *dh1, *gO, *gQh, *gKh, *gVh, *gQr, *gKr, *gY, *dP;
+  uint16_t *dyb, *gGUb, *dh1b, *gOb, *dS, *gYb;
   float *cs, *gs_full, *gd_full, *gsa_full;
   float *rq, *csws, *msews;
   size_t total;
@@ -105,7 +104,6 @@ Ws layout(const Dims& m, void* base) {
   Ws w{};
   const int64_t T = m.T, d = m.d, F = m.F, dq = m.dq, dk = m.dk, nqkv = m.nqkv;
   const bool att = !m.ffn_only;
-  const int64_t maxw = std::max({att ? nqkv * d : 0, att ? d * dq : 0, 2 * F * d, d * F});
   const int64_t maxc = std::max({d, att ? dq : 0, F});
   if (att) {
     w.s_o_x = b.take<float>(dq); w.d_o_x = b.take<float>(dq); w.sa_q = b.take<float>(dq);
@@ -119,7 +117,7 @@ Ws layout(const Dims& m, void* base) {
     w.h1 = b.take<float>(T * d); w.r2 = b.take<float>(T); w.xn2 = b.take<float>(T * d);
     w.Xqkv = b.take<uint16_t>(T * d); w.Qh = b.take<uint16_t>(T * dq);
     w.Kh = b.take<uint16_t>(T * dk); w.Vh = b.take<uint16_t>(T * dk);
-    w.Vt = b.take<uint16_t>(dk * T); w.P = b.take<uint16_t>(m.nq * T * T);
+    w.P = b.take<uint16_t>(m.nq * T * T);
     w.Xo = b.take<uint16_t>(T * dq);
     w.a_qkv = take_stats(b, T); w.a_q = take_stats(b, T); w.a_k = take_stats(b, T);
     w.a_v = take_stats(b, T); w.a_o = take_stats(b, T);
@@ -132,30 +130,31 @@ Ws layout(const Dims& m, void* base) {
   w.a_f = take_stats(b, T); w.a_d = take_stats(b, T);
   // backward
   w.dy = b.take<float>(T * d);
-  w.gW = b.take<float>(maxw); w.Wt = b.take<uint16_t>(maxw);
-  w.gX = b.take<float>(T * maxc); w.Xt = b.take<uint16_t>(maxc * T);
+  w.gX = b.take<float>(T * maxc);
   w.gA = b.take<float>(T * F); w.gGU = b.take<float>(T * 2 * F);
-  w.dyb = b.take<uint16_t>(T * d); w.dyt = b.take<uint16_t>(d * T);
-  w.gGUb = b.take<uint16_t>(T * 2 * F); w.gGUt = b.take<uint16_t>(2 * F * T);
+  w.dyb = b.take<uint16_t>(T * d);
+  w.gGUb = b.take<uint16_t>(T * 2 * F);
   if (att) {
     w.gxn2 = b.take<float>(T * d); w.dh1 = b.take<float>(T * d);
-    w.dh1b = b.take<uint16_t>(T * d); w.dh1t = b.take<uint16_t>(d * T);
+    w.dh1b = b.take<uint16_t>(T * d);
     w.gO = b.take<float>(T * dq); w.gOb = b.take<uint16_t>(T * dq);
-    w.gOt = b.take<uint16_t>(dq * T);
     w.gQh = b.take<float>(T * dq); w.gKh = b.take<float>(T * dk); w.gVh = b.take<float>(T * dk);
     w.gQr = b.take<float>(T * dq); w.gKr = b.take<float>(T * dk);
     w.gY = b.take<float>(T * nqkv);
-    w.gYb = b.take<uint16_t>(T * nqkv); w.gYt = b.take<uint16_t>(nqkv * T);
+    w.gYb = b.take<uint16_t>(T * nqkv);
     w.dP = b.take<float>(m.nq * T * T);
-    w.Pt = b.take<uint16_t>(m.nq * T * T); w.dS = b.take<uint16_t>(m.nq * T * T);
-    w.dSt = b.take<uint16_t>(m.nq * T * T);
-    w.Qt = b.take<uint16_t>(dq * T); w.Kt = b.take<uint16_t>(dk * T);
+    w.dS = b.take<uint16_t>(m.nq * T * T);
     w.gs_full = b.take<float>(dq); w.gd_full = b.take<float>(dq); w.gsa_full = b.take<float>(dq);
   }
   w.cs = b.take<float>(std::max(nqkv, 2 * F));
   size_t rq = 0;
   const int64_t rshapes[][2] = {{nqkv, d}, {d, dq}, {2 * F, d}, {d, F}, {T, d}, {T, dq}, {T, F}};
-  for (auto& r : rshapes) rq = std::max(rq, rowquant_bwd_ws_bytes(r[0], r[1]));
+  for (auto& r : rshapes) {
+    rq = std::max(rq, rowquant_bwd_ws_bytes(r[0], r[1]));
+    int64_t nsl, ntl;
+    gemm_ste_extents(r[0], r[1], &nsl, &ntl);
+    rq = std::max(rq, ste_partials_floats(r[0], r[1], nsl, ntl) * sizeof(float));
+  }
   w.rq = b.take<float>(rq / 4);
   w.csws = b.take<float>(colsum_ws_bytes(T, std::max(nqkv, 2 * F)) / 4);
   w.msews = b.take<float>(2048);
@@ -206,13 +205,31 @@ hipError_t aq(const void* X, int x_dt, int64_t T, int64_t C, int64_t ldx, int mo
   return launch_rowquant_fwd(a, stream);
 }
 
+// every matrix-core launch of the step goes through here (optional event timing)
+hipError_t run_gemm(const Gemm& g, hipStream_t st, omq_timer* tm) {
+  const bool rec = tm && tm->events && tm->count < tm->capacity;
+  if (rec) {
+    hipError_t e = hipEventRecord(reinterpret_cast<hipEvent_t>(tm->events[2 * tm->count]), st);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = launch_gemm(g, st);
+  if (rec && e == hipSuccess) {
+    e = hipEventRecord(reinterpret_cast<hipEvent_t>(tm->events[2 * tm->count + 1]), st);
+    double f = 2.0 * (double)g.M * (double)g.N * (double)g.K * (double)g.batch;
+    if (g.causal != CAUSAL_NONE) f *= 0.5;
+    tm->flops += f;
+    tm->count += 1;
+  }
+  return e;
+}
+
 hipError_t gemm(const void* A, int64_t lda, const void* B, int64_t ldb, float* C, int64_t ldc,
                 int64_t M, int64_t N, int64_t K, const float* bias, const void* resid,
-                int resid_dt, int64_t ldr, hipStream_t st) {
+                int resid_dt, int64_t ldr, hipStream_t st, omq_timer* tm) {
   Gemm g;
   g.A = A; g.lda = lda; g.B = B; g.ldb = ldb; g.C = C; g.ldc = ldc;
   g.M = M; g.N = N; g.K = K; g.bias = bias; g.resid = resid; g.resid_dt = resid_dt; g.ldr = ldr;
-  return launch_gemm(g, st);
+  return run_gemm(g, st, tm);
 }
 
 #define CK(x)                               \
@@ -224,6 +241,7 @@ hipError_t gemm(const void* A, int64_t lda, const void* B, int64_t ldb, float* C
 // Forward.  fp: the full-precision target (no quantizers, no LET).
 int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w, const void* x,
             const void* const* W, const float* th, bool fp, hipStream_t st) {
+  omq_timer* tm = bd->timer;
   const int64_t T = m.T, d = m.d, F = m.F, dq = m.dq, dk = m.dk, nqkv = m.nqkv;
   const int wb = fp ? 16 : bd->wbits, ab = fp ? 16 : bd->abits;
   const float* s_ffn = fp ? nullptr : th + t.s_ffn;
@@ -251,7 +269,7 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
     CK(launch_rmsnorm(x, OMQ_BF16, T, d, bd->eps, w.xn, w.r1, st));
     CK(aq(w.xn, OMQ_F32, T, d, d, mode_let, s_qkv, d_qkv, ab, w.Xqkv, w.a_qkv, st));
     CK(gemm(w.Xqkv, d, w.Wqkv, d, w.Yqkv, nqkv, T, nqkv, d, fp ? nullptr : w.Bt_qkv, nullptr, 0,
-            0, st));
+            0, st, tm));
     CK(launch_rope(w.Yqkv, nqkv, T, m.nq, m.hd, w.cos_t, w.sin_t, 0, w.Qr, dq, st));
     CK(launch_rope(w.Yqkv + dq, nqkv, T, m.nkv, m.hd, w.cos_t, w.sin_t, 0, w.Kr, dk, st));
     // s_a on the affinity, then Q/K/V quantized per token
@@ -270,21 +288,21 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
       g.C = w.S; g.ldc = T; g.strideC = T * T;
       g.M = T; g.N = T; g.K = m.hd; g.batch = (int)m.nq;
       g.alpha = 1.f / sqrtf((float)m.hd); g.causal = CAUSAL_SKIP_UPPER;
-      CK(launch_gemm(g, st));
+      CK(run_gemm(g, st, tm));
     }
     CK(launch_softmax_causal(w.S, T, (int)m.nq, w.P, nullptr, st));
-    CK(launch_transpose_bf16(w.Vh, T, dk, dk, w.Vt, T, 1, 0, 0, st));
     {
-      Gemm g;
+      Gemm g;  // O = P V, V read K-major
       g.A = w.P; g.lda = T; g.strideA = T * T;
-      g.B = w.Vt; g.ldb = T; g.strideB = m.hd * T; g.b_group = m.grp;
+      g.B = w.Vh; g.ldb = dk; g.tb = 1; g.strideB = m.hd; g.b_group = m.grp;
       g.C = w.O; g.ldc = dq; g.strideC = m.hd;
       g.M = T; g.N = m.hd; g.K = T; g.batch = (int)m.nq; g.causal = CAUSAL_K_UPPER;
-      CK(launch_gemm(g, st));
+      CK(run_gemm(g, st, tm));
     }
     // o_proj with its LET site, residual
     CK(aq(w.O, OMQ_F32, T, dq, dq, mode_let, s_o, d_o, ab, w.Xo, w.a_o, st));
-    CK(gemm(w.Xo, dq, w.Wo, dq, w.h1, d, T, d, dq, fp ? nullptr : w.Bt_o, x, OMQ_BF16, d, st));
+    CK(gemm(w.Xo, dq, w.Wo, dq, w.h1, d, T, d, dq, fp ? nullptr : w.Bt_o, x, OMQ_BF16, d, st,
+            tm));
     CK(launch_rmsnorm(w.h1, OMQ_F32, T, d, bd->eps, w.xn2, w.r2, st));
     xf = w.xn2;
     xf_dt = OMQ_F32;
@@ -297,31 +315,13 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
   CK(wfq(W[LU], F, d, s_ffn, d_ffn, th, t, LU, wb, fp, w.Wgu, w.wq_gu, F, w.Bt_gu, st));
   CK(wfq(W[LD], d, F, nullptr, nullptr, th, t, LD, wb, fp, w.Wd, w.wq_d, 0, nullptr, st));
   CK(aq(xf, xf_dt, T, d, d, mode_let, s_ffn, d_ffn, ab, w.Xf, w.a_f, st));
-  CK(gemm(w.Xf, d, w.Wgu, d, w.GU, 2 * F, T, 2 * F, d, fp ? nullptr : w.Bt_gu, nullptr, 0, 0, st));
+  CK(gemm(w.Xf, d, w.Wgu, d, w.GU, 2 * F, T, 2 * F, d, fp ? nullptr : w.Bt_gu, nullptr, 0, 0, st,
+          tm));
   CK(launch_silu_gate(w.GU, T, F, w.A, st));
   CK(aq(w.A, OMQ_F32, T, F, F, OMQ_LET_NONE, nullptr, nullptr, ab, w.Xd, w.a_d, st));
   CK(gemm(w.Xd, F, w.Wd, F, w.y, d, T, d, F, nullptr, m.ffn_only ? nullptr : w.h1, OMQ_F32, d,
-          st));
+          st, tm));
   return OMQ_OK;
-}
-
-// weight-side straight-through backward of one linear (rows [row0, row0 + rows) of gW)
-hipError_t wbwd(const Ws& w, const void* W, int64_t rows, int64_t cols, const float* s,
-                const float* th, const Theta& t, int l, int wbits, const Stats& st, int64_t row0,
-                const float* gW, const float* cs, float* gs, float* gd, int accumulate,
-                float* dth, hipStream_t stream) {
-  if (wbits >= 16 && !s) return hipSuccess;  // no parameter depends on this weight
-  RowQuantBwd a;
-  a.g = gW + row0 * cols; a.ldg = cols;
-  a.x = W; a.x_dt = OMQ_BF16; a.rows = rows; a.cols = cols; a.ldx = cols;
-  a.let_mode = s ? OMQ_LET_MUL : OMQ_LET_NONE; a.s = s; a.nbits = wbits;
-  a.h = st.h + row0; a.z = st.z + row0; a.amax = st.amax + row0; a.amin = st.amin + row0;
-  a.a_gamma = th + t.ag[l]; a.a_beta = th + t.ab[l];
-  a.col_mode = s ? COL_WEIGHT : COL_NONE;
-  a.rowvec = cs ? cs + row0 : nullptr;
-  a.g_agamma = dth + t.ag[l]; a.g_abeta = dth + t.ab[l];
-  a.out0 = gs; a.out1 = gd; a.accumulate = accumulate; a.ws = w.rq;
-  return launch_rowquant_bwd(a, stream);
 }
 
 // activation-side backward through the per-token quantizer and the fused LET
@@ -338,95 +338,199 @@ hipError_t abwd(const Ws& w, const float* g, int64_t T, int64_t C, const void* X
   return launch_rowquant_bwd(a, stream);
 }
 
-// dX = dY_b Wt^T and dW = dY_t X_t^T for one (possibly concatenated) linear.
-// gY: float [T x N]; Xh: bf16 [T x K]; Wh: bf16 [N x K].
-hipError_t lin_bwd_gemms(const Ws& w, const float* gY, int64_t T, int64_t N, int64_t K,
-                         const uint16_t* Xh, const uint16_t* Wh, uint16_t* gYb, uint16_t* gYt,
-                         float* cs, hipStream_t st) {
+// The backward of one (possibly concatenated) quantized linear with both
+// straight-through passes fused into its GEMM epilogues:
+//   dW = dY^T X_hat with the LWC / LET-W backward of every weight row in the
+//   epilogue (no fp32 dW in HBM), then per-segment row finalizers;
+//   dX_hat = dY W_hat with the per-token quantizer / LET-X backward in the
+//   epilogue, which writes dL/dX (gx_out) directly.
+struct WSeg {
+  const void* W;
+  int64_t rows;
+  int l;
+};
+
+struct LinBwd {
+  // the linear: gY [T x N] float, X_hat [T x K] bf16, W_hat [N x K] bf16
+  const float* gY;
+  int64_t N, K;
+  const uint16_t* Xh;
+  const uint16_t* Wh;
+  uint16_t* gYb;
+  // weight side
+  const WSeg* segs;
+  int nseg;
+  Stats wst;
+  const float* s_w;      // LET scale on W (NULL: none)
+  bool fold;             // bias fold with delta (needs column sums of dY)
+  float* gs_w;
+  float* gd_w;
+  int acc_w;             // accumulate into gs_w / gd_w
+  // activation side
+  const void* X;
+  int x_dt;
+  int a_mode;
+  const float* s_x;
+  const float* d_x;
+  Stats ast;
+  float* gx_out;         // dL/dX [T x K]
+  float* gs_x;
+  float* gd_x;
+};
+
+hipError_t lin_bwd_fused(const Ws& w, const LinBwd& L, int64_t T, int wbits, int abits,
+                         const float* th, const Theta& t, float* dth, hipStream_t st,
+                         omq_timer* tm) {
   hipError_t e;
-  if ((e = launch_f32_to_bf16(gY, T, N, N, gYb, N, gYt, T, st)) != hipSuccess) return e;
-  if ((e = launch_transpose_bf16(Xh, T, K, K, w.Xt, T, 1, 0, 0, st)) != hipSuccess) return e;
-  if ((e = launch_transpose_bf16(Wh, N, K, K, w.Wt, N, 1, 0, 0, st)) != hipSuccess) return e;
-  if ((e = gemm(gYt, T, w.Xt, T, w.gW, K, N, K, T, nullptr, nullptr, 0, 0, st)) != hipSuccess)
-    return e;
-  if ((e = gemm(gYb, N, w.Wt, N, w.gX, K, T, K, N, nullptr, nullptr, 0, 0, st)) != hipSuccess)
-    return e;
-  if (cs) e = launch_colsum(gY, T, N, N, cs, w.csws, st);
-  return e;
+  const int64_t N = L.N, K = L.K;
+  if ((e = launch_f32_to_bf16(L.gY, T, N, N, L.gYb, N, nullptr, 0, st)) != hipSuccess) return e;
+  if (L.fold && (e = launch_colsum(L.gY, T, N, N, w.cs, w.csws, st)) != hipSuccess) return e;
+  int64_t nsl, ntl;
+  // weight side (skipped when no learnable parameter depends on these weights)
+  if (wbits < 16 || L.s_w) {
+    gemm_ste_extents(N, K, &nsl, &ntl);
+    float* rowpart = w.rq;
+    float* colpart = w.rq + nsl * N * 2;
+    Gemm g;
+    g.A = L.gYb; g.lda = N; g.ta = 1; g.B = L.Xh; g.ldb = K; g.tb = 1;
+    g.C = nullptr; g.ldc = K; g.M = N; g.N = K; g.K = T;
+    SteEpi& se = g.ste;
+    se.mode = 1; se.nseg = L.nseg;
+    int64_t r0 = 0;
+    for (int k = 0; k < L.nseg; ++k) {
+      r0 += L.segs[k].rows;
+      se.seg_end[k] = r0;
+      se.xseg[k] = L.segs[k].W;
+    }
+    se.x_dt = OMQ_BF16; se.ldx = K;
+    se.let_mode = L.s_w ? OMQ_LET_MUL : OMQ_LET_NONE; se.s = L.s_w;
+    se.h = L.wst.h; se.z = L.wst.z; se.nbits = wbits;
+    se.rowvec = L.fold ? w.cs : nullptr;
+    se.col_mode = L.s_w ? COL_WEIGHT : COL_NONE;
+    se.rowpart = rowpart; se.colpart = colpart;
+    if ((e = run_gemm(g, st, tm)) != hipSuccess) return e;
+    RowQuantBwd a;
+    a.cols = K; a.col_mode = se.col_mode; a.out0 = L.gs_w; a.out1 = L.fold ? L.gd_w : nullptr;
+    a.accumulate = L.acc_w;
+    if ((e = launch_ste_colfinal(a, (int)ntl, colpart, st)) != hipSuccess) return e;
+    r0 = 0;
+    for (int k = 0; k < L.nseg; ++k) {
+      const WSeg& sg = L.segs[k];
+      RowQuantBwd b;
+      b.x = sg.W; b.x_dt = OMQ_BF16; b.rows = sg.rows; b.cols = K; b.ldx = K;
+      b.let_mode = se.let_mode; b.s = L.s_w; b.nbits = wbits;
+      b.h = L.wst.h + r0; b.z = L.wst.z + r0; b.amax = L.wst.amax + r0; b.amin = L.wst.amin + r0;
+      b.a_gamma = th + t.ag[sg.l]; b.a_beta = th + t.ab[sg.l];
+      b.g_agamma = dth + t.ag[sg.l]; b.g_abeta = dth + t.ab[sg.l];
+      b.col_mode = se.col_mode; b.out0 = L.gs_w;
+      if ((e = launch_ste_rowfinal(b, (int)nsl, rowpart + r0 * nsl * 2, st)) != hipSuccess)
+        return e;
+      r0 += sg.rows;
+    }
+  }
+  // activation side
+  gemm_ste_extents(T, K, &nsl, &ntl);
+  float* rowpart = w.rq;
+  float* colpart = w.rq + nsl * T * 2;
+  Gemm g;
+  g.A = L.gYb; g.lda = N; g.B = L.Wh; g.ldb = K; g.tb = 1;
+  g.C = L.gx_out; g.ldc = K; g.M = T; g.N = K; g.K = N;
+  SteEpi& se = g.ste;
+  const int acol = L.a_mode == OMQ_LET_DIV ? COL_ACT_DIV : COL_NONE;
+  se.mode = 2; se.nseg = 1; se.seg_end[0] = T; se.xseg[0] = L.X;
+  se.x_dt = L.x_dt; se.ldx = K;
+  se.let_mode = L.a_mode; se.s = L.s_x; se.delta = L.d_x;
+  se.h = L.ast.h; se.z = L.ast.z; se.nbits = abits;
+  se.col_mode = acol; se.rowpart = rowpart; se.colpart = colpart;
+  if ((e = run_gemm(g, st, tm)) != hipSuccess) return e;
+  RowQuantBwd a;
+  a.x = L.X; a.x_dt = L.x_dt; a.rows = T; a.cols = K; a.ldx = K;
+  a.let_mode = L.a_mode; a.s = L.s_x; a.delta = L.d_x; a.nbits = abits;
+  a.h = L.ast.h; a.z = L.ast.z; a.amax = L.ast.amax; a.amin = L.ast.amin;
+  a.col_mode = acol; a.gx = L.gx_out; a.ldgx = K;
+  a.out0 = L.gs_x; a.out1 = L.gd_x; a.accumulate = 1;
+  if ((e = launch_ste_colfinal(a, (int)ntl, colpart, st)) != hipSuccess) return e;
+  return launch_ste_rowfinal(a, (int)nsl, rowpart, st);
 }
 
 int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w,
              const void* x, const void* const* W, const float* th, float* dth, hipStream_t st) {
+  omq_timer* tm = bd->timer;
   const int64_t T = m.T, d = m.d, F = m.F, dq = m.dq, dk = m.dk, nqkv = m.nqkv;
   const int wb = bd->wbits, ab = bd->abits;
   CK(hipMemsetAsync(dth, 0, t.total * sizeof(float), st));
-  // FFN second linear (no LET)
-  CK(lin_bwd_gemms(w, w.dy, T, d, F, w.Xd, w.Wd, w.dyb, w.dyt, nullptr, st));
-  CK(wbwd(w, W[LD], d, F, nullptr, th, t, LD, wb, w.wq_d, 0, w.gW, nullptr, nullptr, nullptr, 0,
-          dth, st));
-  CK(abwd(w, w.gX, T, F, w.A, OMQ_F32, F, OMQ_LET_NONE, nullptr, nullptr, ab, w.a_d, w.gA, F,
-          COL_NONE, nullptr, nullptr, 0, st));
+  // FFN second linear (no LET): its input is A = SiLU(G) * U
+  {
+    const WSeg segs[1] = {{W[LD], d, LD}};
+    LinBwd L{};
+    L.gY = w.dy; L.N = d; L.K = F; L.Xh = w.Xd; L.Wh = w.Wd; L.gYb = w.dyb;
+    L.segs = segs; L.nseg = 1; L.wst = w.wq_d;
+    L.X = w.A; L.x_dt = OMQ_F32; L.a_mode = OMQ_LET_NONE; L.ast = w.a_d; L.gx_out = w.gA;
+    CK(lin_bwd_fused(w, L, T, wb, ab, th, t, dth, st, tm));
+  }
   CK(launch_silu_gate_bwd(w.GU, w.gA, T, F, w.gGU, st));
   // gate / up with the shared ffn LET site
-  const float* s_f = th + t.s_ffn;
-  const float* d_f = th + t.d_ffn;
-  float* gs_f = dth + t.s_ffn;
-  float* gd_f = dth + t.d_ffn;
-  CK(lin_bwd_gemms(w, w.gGU, T, 2 * F, d, w.Xf, w.Wgu, w.gGUb, w.gGUt, w.cs, st));
-  CK(wbwd(w, W[LG], F, d, s_f, th, t, LG, wb, w.wq_gu, 0, w.gW, w.cs, gs_f, gd_f, 1, dth, st));
-  CK(wbwd(w, W[LU], F, d, s_f, th, t, LU, wb, w.wq_gu, F, w.gW, w.cs, gs_f, gd_f, 1, dth, st));
-  const void* xf = m.ffn_only ? x : (const void*)w.xn2;
-  const int xf_dt = m.ffn_only ? OMQ_BF16 : OMQ_F32;
-  CK(abwd(w, w.gX, T, d, xf, xf_dt, d, OMQ_LET_DIV, s_f, d_f, ab, w.a_f,
-          m.ffn_only ? nullptr : w.gxn2, d, COL_ACT_DIV, gs_f, gd_f, 1, st));
+  {
+    const WSeg segs[2] = {{W[LG], F, LG}, {W[LU], F, LU}};
+    LinBwd L{};
+    L.gY = w.gGU; L.N = 2 * F; L.K = d; L.Xh = w.Xf; L.Wh = w.Wgu; L.gYb = w.gGUb;
+    L.segs = segs; L.nseg = 2; L.wst = w.wq_gu; L.s_w = th + t.s_ffn; L.fold = true;
+    L.gs_w = dth + t.s_ffn; L.gd_w = dth + t.d_ffn; L.acc_w = 1;
+    L.X = m.ffn_only ? x : (const void*)w.xn2; L.x_dt = m.ffn_only ? OMQ_BF16 : OMQ_F32;
+    L.a_mode = OMQ_LET_DIV; L.s_x = th + t.s_ffn; L.d_x = th + t.d_ffn; L.ast = w.a_f;
+    L.gx_out = m.ffn_only ? w.gX : w.gxn2; L.gs_x = dth + t.s_ffn; L.gd_x = dth + t.d_ffn;
+    CK(lin_bwd_fused(w, L, T, wb, ab, th, t, dth, st, tm));
+  }
   if (m.ffn_only) return OMQ_OK;
 
   // RMSNorm before the FFN, residual
   CK(launch_rmsnorm_bwd(w.gxn2, w.h1, w.r2, T, d, w.dy, w.dh1, st));
   // o_proj with its LET site (per KV channel, broadcast over the query heads)
-  CK(lin_bwd_gemms(w, w.dh1, T, d, dq, w.Xo, w.Wo, w.dh1b, w.dh1t, w.cs, st));
-  CK(wbwd(w, W[LO], d, dq, w.s_o_x, th, t, LO, wb, w.wq_o, 0, w.gW, w.cs, w.gs_full, w.gd_full,
-          0, dth, st));
-  CK(abwd(w, w.gX, T, dq, w.O, OMQ_F32, dq, OMQ_LET_DIV, w.s_o_x, w.d_o_x, ab, w.a_o, w.gO, dq,
-          COL_ACT_DIV, w.gs_full, w.gd_full, 1, st));
+  {
+    const WSeg segs[1] = {{W[LO], d, LO}};
+    LinBwd L{};
+    L.gY = w.dh1; L.N = d; L.K = dq; L.Xh = w.Xo; L.Wh = w.Wo; L.gYb = w.dh1b;
+    L.segs = segs; L.nseg = 1; L.wst = w.wq_o; L.s_w = w.s_o_x; L.fold = true;
+    L.gs_w = w.gs_full; L.gd_w = w.gd_full; L.acc_w = 0;
+    L.X = w.O; L.x_dt = OMQ_F32; L.a_mode = OMQ_LET_DIV; L.s_x = w.s_o_x; L.d_x = w.d_o_x;
+    L.ast = w.a_o; L.gx_out = w.gO; L.gs_x = w.gs_full; L.gd_x = w.gd_full;
+    CK(lin_bwd_fused(w, L, T, wb, ab, th, t, dth, st, tm));
+  }
   CK(launch_kv_reduce_add(w.gs_full, m.nq, m.nkv, m.hd, dth + t.s_o, st));
   CK(launch_kv_reduce_add(w.gd_full, m.nq, m.nkv, m.hd, dth + t.d_o, st));
   // attention backward (softmax in float32, recomputed from S)
-  CK(launch_f32_to_bf16(w.gO, T, dq, dq, w.gOb, dq, w.gOt, T, st));
+  CK(launch_f32_to_bf16(w.gO, T, dq, dq, w.gOb, dq, nullptr, 0, st));
   {
     Gemm g;  // dP = dO V^T
     g.A = w.gOb; g.lda = dq; g.strideA = m.hd;
     g.B = w.Vh; g.ldb = dk; g.strideB = m.hd; g.b_group = m.grp;
     g.C = w.dP; g.ldc = T; g.strideC = T * T;
     g.M = T; g.N = T; g.K = m.hd; g.batch = (int)m.nq; g.causal = CAUSAL_SKIP_UPPER;
-    CK(launch_gemm(g, st));
+    CK(run_gemm(g, st, tm));
   }
   const float scale = 1.f / sqrtf((float)m.hd);
-  CK(launch_softmax_bwd_causal(w.S, w.dP, w.O, w.gO, T, (int)m.nq, m.hd, dq, scale, w.dS, w.dSt,
-                               st));
-  CK(launch_transpose_bf16(w.P, T, T, T, w.Pt, T, (int)m.nq, T * T, T * T, st));
-  CK(launch_transpose_bf16(w.Kh, T, dk, dk, w.Kt, T, 1, 0, 0, st));
-  CK(launch_transpose_bf16(w.Qh, T, dq, dq, w.Qt, T, 1, 0, 0, st));
+  CK(launch_softmax_bwd_causal(w.S, w.dP, w.O, w.gO, T, (int)m.nq, m.hd, dq, scale, w.dS,
+                               nullptr, st));
   {
-    Gemm g;  // dQ = dS K
+    Gemm g;  // dQ = dS K, K read K-major
     g.A = w.dS; g.lda = T; g.strideA = T * T;
-    g.B = w.Kt; g.ldb = T; g.strideB = m.hd * T; g.b_group = m.grp;
+    g.B = w.Kh; g.ldb = dk; g.tb = 1; g.strideB = m.hd; g.b_group = m.grp;
     g.C = w.gQh; g.ldc = dq; g.strideC = m.hd;
     g.M = T; g.N = m.hd; g.K = T; g.batch = (int)m.nq; g.causal = CAUSAL_K_UPPER;
-    CK(launch_gemm(g, st));
+    CK(run_gemm(g, st, tm));
   }
   for (int r = 0; r < m.grp; ++r) {
-    Gemm g;  // dK_g = sum_h dS_h^T Q_h ;  dV_g = sum_h P_h^T dO_h
-    g.A = w.dSt + (int64_t)r * T * T; g.lda = T; g.strideA = (int64_t)m.grp * T * T;
-    g.B = w.Qt + (int64_t)r * m.hd * T; g.ldb = T; g.strideB = (int64_t)m.grp * m.hd * T;
+    Gemm g;  // dK_g = sum_h dS_h^T Q_h ;  dV_g = sum_h P_h^T dO_h  (all operands K-major)
+    g.A = w.dS + (int64_t)r * T * T; g.lda = T; g.ta = 1; g.strideA = (int64_t)m.grp * T * T;
+    g.B = w.Qh + (int64_t)r * m.hd; g.ldb = dq; g.tb = 1; g.strideB = (int64_t)m.grp * m.hd;
     g.C = w.gKh; g.ldc = dk; g.strideC = m.hd;
     g.M = T; g.N = m.hd; g.K = T; g.batch = (int)m.nkv; g.causal = CAUSAL_K_LOWER;
     g.accumulate = r > 0;
-    CK(launch_gemm(g, st));
-    g.A = w.Pt + (int64_t)r * T * T;
-    g.B = w.gOt + (int64_t)r * m.hd * T;
+    CK(run_gemm(g, st, tm));
+    g.A = w.P + (int64_t)r * T * T;
+    g.B = w.gOb + (int64_t)r * m.hd; g.ldb = dq;
     g.C = w.gVh;
-    CK(launch_gemm(g, st));
+    CK(run_gemm(g, st, tm));
   }
   // Q~ / K~ / V quantizers and s_a
   const bool sa = m.use_sa;
@@ -442,17 +546,17 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
   CK(launch_rope(w.gQr, dq, T, m.nq, m.hd, w.cos_t, w.sin_t, 1, w.gY, nqkv, st));
   CK(launch_rope(w.gKr, dk, T, m.nkv, m.hd, w.cos_t, w.sin_t, 1, w.gY + dq, nqkv, st));
   // q / k / v with the shared qkv LET site
-  const float* s_q = th + t.s_qkv;
-  const float* d_q = th + t.d_qkv;
-  float* gs_q = dth + t.s_qkv;
-  float* gd_q = dth + t.d_qkv;
-  CK(lin_bwd_gemms(w, w.gY, T, nqkv, d, w.Xqkv, w.Wqkv, w.gYb, w.gYt, w.cs, st));
-  CK(wbwd(w, W[LQ], dq, d, s_q, th, t, LQ, wb, w.wq_qkv, 0, w.gW, w.cs, gs_q, gd_q, 1, dth, st));
-  CK(wbwd(w, W[LK], dk, d, s_q, th, t, LK, wb, w.wq_qkv, dq, w.gW, w.cs, gs_q, gd_q, 1, dth, st));
-  CK(wbwd(w, W[LV], dk, d, s_q, th, t, LV, wb, w.wq_qkv, dq + dk, w.gW, w.cs, gs_q, gd_q, 1, dth,
-          st));
-  CK(abwd(w, w.gX, T, d, w.xn, OMQ_F32, d, OMQ_LET_DIV, s_q, d_q, ab, w.a_qkv, nullptr, d,
-          COL_ACT_DIV, gs_q, gd_q, 1, st));
+  {
+    const WSeg segs[3] = {{W[LQ], dq, LQ}, {W[LK], dk, LK}, {W[LV], dk, LV}};
+    LinBwd L{};
+    L.gY = w.gY; L.N = nqkv; L.K = d; L.Xh = w.Xqkv; L.Wh = w.Wqkv; L.gYb = w.gYb;
+    L.segs = segs; L.nseg = 3; L.wst = w.wq_qkv; L.s_w = th + t.s_qkv; L.fold = true;
+    L.gs_w = dth + t.s_qkv; L.gd_w = dth + t.d_qkv; L.acc_w = 1;
+    L.X = w.xn; L.x_dt = OMQ_F32; L.a_mode = OMQ_LET_DIV; L.s_x = th + t.s_qkv;
+    L.d_x = th + t.d_qkv; L.ast = w.a_qkv; L.gx_out = w.gX;
+    L.gs_x = dth + t.s_qkv; L.gd_x = dth + t.d_qkv;
+    CK(lin_bwd_fused(w, L, T, wb, ab, th, t, dth, st, tm));
+  }
   return OMQ_OK;
 }
 

@@ -1,18 +1,22 @@
 // Dense contractions of the quantized layer (paper reading, section "LET":
 // Y = Q_a(X~) Q_w(W~) + B~, and the two products of its backward) on gfx950.
 //
-// C[M x N] = alpha * A[M x K] * B[N x K]^T (+ bias[N]) (+ residual) (+ C)
-// Both operands are K-contiguous ("NT"), the layout the matrix cores read without
-// any transposition: a lane of v_mfma_f32_32x32x16_bf16 holds 8 consecutive k of
-// one row of A and 8 consecutive k of one column of B^T.
+// C[M x N] = alpha * op(A)[M x K] * op(B)[N x K]^T (+ bias[N]) (+ residual) (+ C)
+// In LDS both operands are held K-contiguous, the layout the matrix cores read:
+// a lane of v_mfma_f32_32x32x16_bf16 holds 8 consecutive k of one row of A and 8
+// consecutive k of one column of B^T.  An operand stored K-major in HBM ("T",
+// [K x M] with M contiguous) is loaded as 4 k-rows x 8 contiguous elements per
+// thread (coalesced row segments) and transposed in registers with byte
+// permutes on its way into LDS, so no product of the backward needs a
+// transposed copy in HBM.
 //
 // Tile 128 x 128 x 64, 256 threads = 4 waves in a 2 x 2 grid, each wave 64 x 64 as
 // 2 x 2 MFMA 32x32x16 blocks (64 float accumulators per lane).  Global loads are
 // 16-byte vectors staged in registers while the matrix cores consume the other
-// LDS buffer (double buffered, one barrier per K step).  LDS rows are padded by
-// 16 bytes so the 16-byte fragment reads of 8 consecutive rows hit distinct banks.
+// LDS buffer (double buffered, one barrier per K step).
 // Tiles are visited in groups of 8 row-tiles and dealt to the 8 XCDs in
 // contiguous runs, so tiles sharing A rows / B columns share an L2.
+// LDS rows are unpadded and XOR-swizzled (see lds_idx).
 #include "common.h"
 #include "kernels.h"
 
@@ -23,7 +27,15 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
-constexpr int BM = 128, BN = 128, BK = 64, LDP = BK + 8;
+constexpr int BK = 64, LDP = BK;
+
+// LDS tiles are [rows][64] bf16 with the 16-byte k-chunk index XOR-swizzled by
+// (row & 7) ^ ((row >> 3) & 7): the matrix-core fragment reads (8 consecutive rows,
+// one chunk) and the transposed-operand stores (rows 8 apart, one k-quad) both
+// spread over distinct banks.
+OMQ_DEV int lds_idx(int row, int k) {
+  return row * LDP + ((((k >> 3) ^ row ^ (row >> 3)) & 7) << 3) + (k & 7);
+}
 constexpr int kGroupM = 8;
 
 OMQ_DEV void tile_coords(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
@@ -38,12 +50,114 @@ OMQ_DEV void tile_coords(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
   tn = in_g / gsz;
 }
 
-__global__ __launch_bounds__(256, 2) void k_gemm_bf16(Gemm g, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM][LDP];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN][LDP];
+// One operand tile (R rows x 64 k) staged through registers by NT threads.
+//  N layout ([rows x K], K contiguous): 16-byte chunks, 8 per row.
+//  T layout ([K x rows], rows contiguous): 4 k-rows x 8 rows per thread, transposed
+//  in registers (byte permutes) into 8-byte LDS writes of 4 consecutive k.
+template <int TRANS, int R, int NT>
+struct Stage {
+  static constexpr int kUnits = TRANS ? R * 2 : R * 8;          // sub-blocks / chunks
+  static constexpr int kN = (kUnits + NT - 1) / NT;              // per thread
+  uint4 r[TRANS ? 4 * kN : kN];
+
+  // interior tiles (all rows and the whole k-step in range) skip the bounds checks
+  OMQ_DEV void load_full(const uint16_t* P, int64_t ld, int64_t row0, int64_t k0, int tid) {
+    if (!TRANS) {
+#pragma unroll
+      for (int i = 0; i < kN; ++i) {
+        const int id = tid + NT * i;
+        if (kUnits % NT == 0 || id < kUnits)
+          r[i] = *reinterpret_cast<const uint4*>(P + (row0 + (id >> 3)) * ld + k0 + (id & 7) * 8);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kN; ++u) {
+        const int id = tid + NT * u;
+        if (kUnits % NT == 0 || id < kUnits) {
+          const int64_t gr = row0 + (id % (R / 8)) * 8;
+          const int kq = id / (R / 8);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            r[4 * u + i] = *reinterpret_cast<const uint4*>(P + (k0 + kq * 4 + i) * ld + gr);
+        }
+      }
+    }
+  }
+
+  OMQ_DEV void load(const uint16_t* P, int64_t ld, int64_t rows, int64_t row0, int64_t k0,
+                    int64_t ke, int tid) {
+    if (row0 + R <= rows && k0 + BK <= ke) {
+      load_full(P, ld, row0, k0, tid);
+      return;
+    }
+    if (!TRANS) {
+#pragma unroll
+      for (int i = 0; i < kN; ++i) {
+        const int id = tid + NT * i;
+        const int64_t gr = row0 + (id >> 3), gk = k0 + (id & 7) * 8;
+        r[i] = (id < kUnits && gr < rows && gk < ke)
+                   ? *reinterpret_cast<const uint4*>(P + gr * ld + gk)
+                   : make_uint4(0, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kN; ++u) {
+        const int id = tid + NT * u;             // sub-block: (R/8) row blocks x 16 k-quads
+        const int64_t gr = row0 + (id % (R / 8)) * 8;
+        const int kq = id / (R / 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t gk = k0 + kq * 4 + i;
+          r[4 * u + i] = (id < kUnits && gr < rows && gk < ke)
+                             ? *reinterpret_cast<const uint4*>(P + gk * ld + gr)
+                             : make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  OMQ_DEV void store(uint16_t* S, int tid) const {
+    if (!TRANS) {
+#pragma unroll
+      for (int i = 0; i < kN; ++i) {
+        const int id = tid + NT * i;
+        if (id < kUnits) *reinterpret_cast<uint4*>(S + lds_idx(id >> 3, (id & 7) * 8)) = r[i];
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kN; ++u) {
+        const int id = tid + NT * u;
+        if (id >= kUnits) continue;
+        const int rb = (id % (R / 8)) * 8, kc = (id / (R / 8)) * 4;
+        const uint32_t w[4][4] = {{r[4 * u].x, r[4 * u].y, r[4 * u].z, r[4 * u].w},
+                                  {r[4 * u + 1].x, r[4 * u + 1].y, r[4 * u + 1].z, r[4 * u + 1].w},
+                                  {r[4 * u + 2].x, r[4 * u + 2].y, r[4 * u + 2].z, r[4 * u + 2].w},
+                                  {r[4 * u + 3].x, r[4 * u + 3].y, r[4 * u + 3].z, r[4 * u + 3].w}};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int q = j >> 1;
+          const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+          uint2 v;
+          v.x = __builtin_amdgcn_perm(w[1][q], w[0][q], sel);
+          v.y = __builtin_amdgcn_perm(w[3][q], w[2][q], sel);
+          *reinterpret_cast<uint2*>(S + lds_idx(rb + j, kc)) = v;
+        }
+      }
+    }
+  }
+};
+
+// BM x BN tile, WM x WN waves, each wave (BM/WM) x (BN/WN) as 32x32 MFMA blocks.
+template <int BM, int BN, int WM, int WN, int TA, int TB, int EPI>
+__global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m, int tiles_n) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int FM = BM / WM / 32, FN = BN / WN / 32;   // MFMA blocks per wave
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * LDP];
+  uint16_t (*As)[BM * LDP] = reinterpret_cast<uint16_t (*)[BM * LDP]>(smem);
+  uint16_t (*Bs)[BN * LDP] = reinterpret_cast<uint16_t (*)[BN * LDP]>(smem + 2 * BM * LDP);
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
+  const int wm = wid / WN, wn = wid % WN;
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
@@ -57,81 +171,202 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16(Gemm g, int tiles_m, int t
   const uint16_t* B = reinterpret_cast<const uint16_t*>(g.B) + (bz / g.b_group) * g.strideB;
   const int64_t M = g.M, N = g.N;
 
-  uint4 ra[4], rb[4];
-  auto gload = [&](int64_t k0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = tid + 256 * i;
-      const int row = id >> 3;
-      const int kc = (id & 7) * 8;
-      const int64_t gk = k0 + kc;
-      const int64_t gm = m0 + row, gn = n0 + row;
-      ra[i] = (gm < M && gk < ke) ? *reinterpret_cast<const uint4*>(A + gm * g.lda + gk)
-                                  : make_uint4(0, 0, 0, 0);
-      rb[i] = (gn < N && gk < ke) ? *reinterpret_cast<const uint4*>(B + gn * g.ldb + gk)
-                                  : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = tid + 256 * i;
-      const int row = id >> 3;
-      const int kc = (id & 7) * 8;
-      *reinterpret_cast<uint4*>(&As[buf][row][kc]) = ra[i];
-      *reinterpret_cast<uint4*>(&Bs[buf][row][kc]) = rb[i];
-    }
-  };
+  Stage<TA, BM, NT> sa;
+  Stage<TB, BN, NT> sb;
 
-  f32x16 acc[2][2];
+  f32x16 acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // Pipeline per K step: read every fragment of the current LDS buffer, write the
+  // next tile (loaded one step earlier) into the other buffer, issue the global
+  // loads two tiles ahead, then run the MFMAs while those are in flight.
   const int nk = (int)((ke - kb + BK - 1) / BK);
   if (nk > 0) {
-    gload(kb);
-    sstore(0);
+    sa.load(A, g.lda, M, m0, kb, ke, tid);
+    sb.load(B, g.ldb, N, n0, kb, ke, tid);
+    sa.store(As[0], tid);
+    sb.store(Bs[0], tid);
+    if (nk > 1) {
+      sa.load(A, g.lda, M, m0, kb + BK, ke, tid);
+      sb.load(B, g.ldb, N, n0, kb + BK, ke, tid);
+    }
   }
   __syncthreads();
   const int fr = lane & 31, fk = (lane >> 5) * 8;
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kb + (int64_t)(kt + 1) * BK);
+    bf16x8 af[BK / 16][FM], bf[BK / 16][FN];
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8 af[2], bf[2];
+    for (int kk = 0; kk < BK / 16; ++kk) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        af[i] = *reinterpret_cast<const bf16x8*>(&As[buf][wm * 64 + i * 32 + fr][kk + fk]);
-        bf[i] = *reinterpret_cast<const bf16x8*>(&Bs[buf][wn * 64 + i * 32 + fr][kk + fk]);
-      }
+      for (int i = 0; i < FM; ++i)
+        af[kk][i] = *reinterpret_cast<const bf16x8*>(
+            &As[buf][lds_idx(wm * (BM / WM) + i * 32 + fr, kk * 16 + fk)]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < FN; ++j)
+        bf[kk][j] = *reinterpret_cast<const bf16x8*>(
+            &Bs[buf][lds_idx(wn * (BN / WN) + j * 32 + fr, kk * 16 + fk)]);
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
+    if (kt + 1 < nk) {
+      sa.store(As[buf ^ 1], tid);
+      sb.store(Bs[buf ^ 1], tid);
+      if (kt + 2 < nk) {
+        const int64_t k2 = kb + (int64_t)(kt + 2) * BK;
+        sa.load(A, g.lda, M, m0, k2, ke, tid);
+        sb.load(B, g.ldb, N, n0, k2, ke, tid);
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk][i], bf[kk][j], acc[i][j], 0,
+                                                              0, 0);
     __syncthreads();
   }
 
   // epilogue: lane holds column (lane & 31) and rows 8*(r/4) + 4*(lane/32) + r%4
+  if constexpr (EPI != 0) {
+    // Straight-through backward of the row quantizer on the dL/dx_hat tile: the
+    // accumulators are parked in LDS (the K loop ended on a barrier, so the operand
+    // buffers are free), then each wave takes whole rows: it recomputes x~ and the
+    // forward's in-range decision from x and the row's (h, z), reduces the per-row
+    // partials (g_h, sum g (1 - in)) over the tile's 128 columns, accumulates the
+    // per-column partials over its rows, and for token rows writes dL/dx (through
+    // the LET) into C.
+    static_assert(BM == 128 && BN == 128 && WM * WN == 4, "straight-through epilogue tile");
+    float* T = reinterpret_cast<float*>(smem);     // [128][128] fp32 = the whole buffer
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * (BM / WM) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int col = wn * (BN / WN) + j * 32 + (lane & 31);
+          T[row * BN + col] = g.alpha * acc[i][j][r];
+        }
+    __syncthreads();
+    const SteEpi& e = g.ste;
+    const bool pass = e.nbits >= 16;
+    const float Q = pass ? 0.f : (float)((1 << e.nbits) - 1);
+    const int esz = e.x_dt == OMQ_F32 ? 4 : 2;
+    const int64_t gn = n0 + 2 * lane;             // this lane's two columns
+    const bool colv = gn < N;                     // N is a multiple of 8
+    float s_c[2] = {1.f, 1.f}, d_c[2] = {0.f, 0.f};
+    if (colv && e.let_mode != OMQ_LET_NONE) { s_c[0] = e.s[gn]; s_c[1] = e.s[gn + 1]; }
+    if (colv && e.let_mode == OMQ_LET_DIV && e.delta) {
+      d_c[0] = e.delta[gn];
+      d_c[1] = e.delta[gn + 1];
+    }
+    const float r_c[2] = {1.f / s_c[0], 1.f / s_c[1]};
+    float ca0[2] = {0.f, 0.f}, ca1[2] = {0.f, 0.f};
+    float* Cp = g.C + bz * g.strideC;
+    for (int rr = 0; rr < BM / 4; ++rr) {
+      const int row = wid * (BM / 4) + rr;
+      const int64_t gm = m0 + row;
+      if (gm >= M) break;                          // wave-uniform
+      const float2 gv2 = *reinterpret_cast<const float2*>(&T[row * BN + 2 * lane]);
+      const float gvv[2] = {gv2.x, gv2.y};
+      const float hh = pass ? 1.f : e.h[gm];
+      const float zz = pass ? 0.f : e.z[gm];
+      const float vrow = e.rowvec ? e.rowvec[gm] : 0.f;
+      const int sg = (e.nseg > 1 && gm >= e.seg_end[0]) + (e.nseg > 2 && gm >= e.seg_end[1]);
+      const int64_t lr = gm - (sg == 0 ? 0 : e.seg_end[sg - 1]);
+      const char* xr = reinterpret_cast<const char*>(e.xseg[sg]) + lr * e.ldx * esz;
+      float ph = 0.f, pz = 0.f;
+      if (colv) {
+        float xv[2];
+        if (e.x_dt == OMQ_F32) {
+          const float2 t = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(xr) + gn);
+          xv[0] = t.x; xv[1] = t.y;
+        } else {
+          const uint32_t t = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(xr) + gn);
+          xv[0] = __uint_as_float(t << 16);
+          xv[1] = __uint_as_float(t & 0xffff0000u);
+        }
+        float up[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          float xt = xv[q];
+          if (e.let_mode == OMQ_LET_DIV) xt = (xv[q] - d_c[q]) / s_c[q];
+          else if (e.let_mode == OMQ_LET_MUL) xt = s_c[q] * xv[q];
+          const float gv = gvv[q];
+          float gns = gv;
+          if (!pass) {
+            const float u = xt / hh;
+            const float rq = rintf(u) + zz;
+            const bool in = (rq >= 0.f) && (rq <= Q);
+            const float qmz = fminf(fmaxf(rq, 0.f), Q) - zz;
+            ph += gv * (qmz - (in ? u : 0.f));
+            pz += in ? 0.f : gv;
+            gns = in ? gv : 0.f;
+          }
+          if (e.col_mode == COL_WEIGHT) {
+            ca0[q] += gns * xv[q];
+            ca1[q] += vrow * xv[q];
+          } else if (e.col_mode == COL_ACT_DIV) {
+            ca0[q] += gns * (-xt * r_c[q]);
+            ca1[q] += gns * (-r_c[q]);
+          } else if (e.col_mode == COL_ACT_MUL) {
+            ca0[q] += gns * xv[q];
+          }
+          up[q] = e.let_mode == OMQ_LET_DIV ? gns * r_c[q]
+                  : e.let_mode == OMQ_LET_MUL ? gns * s_c[q] : gns;
+        }
+        if (e.mode == 2) *reinterpret_cast<float2*>(&Cp[gm * g.ldc + gn]) = make_float2(up[0], up[1]);
+      }
+      if (!pass) {
+        ph = wave_sum(ph);
+        pz = wave_sum(pz);
+        if (lane == 0) {
+          e.rowpart[(gm * tiles_n + tn) * 2 + 0] = ph;
+          e.rowpart[(gm * tiles_n + tn) * 2 + 1] = pz;
+        }
+      }
+    }
+    if (e.col_mode != COL_NONE) {
+      __syncthreads();                             // every wave is done reading T
+      T[(wid * 2 + 0) * BN + 2 * lane] = ca0[0];
+      T[(wid * 2 + 0) * BN + 2 * lane + 1] = ca0[1];
+      T[(wid * 2 + 1) * BN + 2 * lane] = ca1[0];
+      T[(wid * 2 + 1) * BN + 2 * lane + 1] = ca1[1];
+      __syncthreads();
+      if (tid < BN) {
+        const int64_t c = n0 + tid;
+        if (c < N) {
+          float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            a0 += T[(w * 2 + 0) * BN + tid];
+            a1 += T[(w * 2 + 1) * BN + tid];
+          }
+          e.colpart[((int64_t)tm * 2 + 0) * N + c] = a0;
+          e.colpart[((int64_t)tm * 2 + 1) * N + c] = a1;
+        }
+      }
+    }
+    return;
+  }
   float* C = g.C ? g.C + bz * g.strideC : nullptr;
   uint16_t* Cb = g.Cb ? g.Cb + bz * g.strideC : nullptr;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t gn = n0 + wn * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < FN; ++j) {
+      const int64_t gn = n0 + wn * (BN / WN) + j * 32 + (lane & 31);
       if (gn >= N) continue;
       const float bias = g.bias ? g.bias[gn] : 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t gm = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int64_t gm = m0 + wm * (BM / WM) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (gm >= M) continue;
         float v = g.alpha * acc[i][j][r] + bias;
         if (g.resid) {
@@ -147,6 +382,36 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16(Gemm g, int tiles_m, int t
         }
       }
     }
+}
+
+template <int BM, int BN, int WM, int WN>
+void launch_cfg(const Gemm& g, hipStream_t st) {
+  const int tiles_m = (int)((g.M + BM - 1) / BM), tiles_n = (int)((g.N + BN - 1) / BN);
+  const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)g.batch), block(WM * WN * 64);
+  if (!g.ta && !g.tb)
+    hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, 0, 0, 0>), grid, block, 0, st, g, tiles_m, tiles_n);
+  else if (!g.ta && g.tb)
+    hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, 0, 1, 0>), grid, block, 0, st, g, tiles_m, tiles_n);
+  else if (g.ta && !g.tb)
+    hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, 1, 0, 0>), grid, block, 0, st, g, tiles_m, tiles_n);
+  else
+    hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, 1, 1, 0>), grid, block, 0, st, g, tiles_m, tiles_n);
+}
+
+// the straight-through epilogue runs on 128 x 128 tiles of 4 waves (64-row blocks,
+// 64-column slabs), for the two layouts the backward uses
+constexpr int kSteBM = 128, kSteBN = 128, kSteWM = 2, kSteWN = 2;
+
+void launch_ste(const Gemm& g, hipStream_t st) {
+  const int tiles_m = (int)((g.M + kSteBM - 1) / kSteBM);
+  const int tiles_n = (int)((g.N + kSteBN - 1) / kSteBN);
+  const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)g.batch), block(kSteWM * kSteWN * 64);
+  if (g.ta)
+    hipLaunchKernelGGL((k_gemm_bf16<kSteBM, kSteBN, kSteWM, kSteWN, 1, 1, 1>), grid, block, 0, st,
+                       g, tiles_m, tiles_n);
+  else
+    hipLaunchKernelGGL((k_gemm_bf16<kSteBM, kSteBN, kSteWM, kSteWN, 0, 1, 1>), grid, block, 0, st,
+                       g, tiles_m, tiles_n);
 }
 
 // float32 operands (the fp32 path): 64 x 64 tiles, 4 x 4 outputs per thread.
@@ -248,12 +513,31 @@ __global__ __launch_bounds__(256) void k_f32_to_bf16(const float* in, int64_t ro
 
 }  // namespace
 
+// Tile configuration per problem: 0: 128x128 (4 waves), 1: 256x128 (4 waves),
+// 2: 128x256 (4 waves), 4: 256x128 (8 waves).
+int gemm_config(const Gemm& g) {
+  return 0;
+}
+
+void gemm_ste_extents(int64_t rows, int64_t cols, int64_t* nslabs, int64_t* ntiles) {
+  *nslabs = (cols + kSteBN - 1) / kSteBN;
+  *ntiles = (rows + kSteBM - 1) / kSteBM;
+}
+
 hipError_t launch_gemm(const Gemm& g, hipStream_t st) {
   if (g.M == 0 || g.N == 0 || g.batch == 0) return hipSuccess;
+  if (g.dt == OMQ_BF16 && g.ste.mode != 0) {
+    if (!g.tb) return hipErrorInvalidValue;   // the backward's layouts: (T, T) and (N, T)
+    launch_ste(g, st);
+    return hipGetLastError();
+  }
   if (g.dt == OMQ_BF16) {
-    const int tiles_m = (int)((g.M + BM - 1) / BM), tiles_n = (int)((g.N + BN - 1) / BN);
-    hipLaunchKernelGGL(k_gemm_bf16, dim3((unsigned)(tiles_m * tiles_n), (unsigned)g.batch),
-                       dim3(256), 0, st, g, tiles_m, tiles_n);
+    switch (gemm_config(g)) {
+      case 1: launch_cfg<256, 128, 2, 2>(g, st); break;
+      case 2: launch_cfg<128, 256, 2, 2>(g, st); break;
+      case 4: launch_cfg<256, 128, 4, 2>(g, st); break;
+      default: launch_cfg<128, 128, 2, 2>(g, st); break;
+    }
   } else {
     dim3 grid((unsigned)((g.N + 63) / 64), (unsigned)((g.M + 63) / 64), (unsigned)g.batch);
     hipLaunchKernelGGL(k_gemm_f32, grid, dim3(256), 0, st, g);

@@ -46,6 +46,14 @@ struct RowQuantBwd {
 };
 size_t rowquant_bwd_ws_bytes(int64_t rows, int64_t cols);
 hipError_t launch_rowquant_bwd(const RowQuantBwd& a, hipStream_t st);
+// Finalizers of the straight-through backward, shared by the tile pass and the
+// GEMM-epilogue form.  Partials: rowpart [rows][nslabs][2] (g_h, sum g (1 - in)),
+// colpart [ntiles][2][cols].  colfinal reduces the column partials into out0/out1;
+// rowfinal turns row partials into LWC-logit gradients and adds the max/min scatter.
+size_t ste_partials_floats(int64_t rows, int64_t cols, int64_t nslabs, int64_t ntiles);
+hipError_t launch_ste_colfinal(const RowQuantBwd& a, int ntiles, float* colpart, hipStream_t st);
+hipError_t launch_ste_rowfinal(const RowQuantBwd& a, int nslabs, const float* rowpart,
+                               hipStream_t st);
 
 // LET alone: y = (x - delta) / s  or  y = s * x, elementwise over [rows x cols].
 hipError_t launch_let_elementwise(const void* x, int x_dt, int64_t rows, int64_t cols,
@@ -60,6 +68,22 @@ hipError_t launch_bias_fold(const void* W, int w_dt, int64_t rows, int64_t cols,
 // ---------------------------------------------------------------------------
 enum Causal { CAUSAL_NONE = 0, CAUSAL_SKIP_UPPER = 1, CAUSAL_K_UPPER = 2, CAUSAL_K_LOWER = 3 };
 
+// Straight-through backward fused into a GEMM epilogue (the GEMM's C is dL/dx_hat
+// for rows x cols of x).  Rows may come from up to 3 buffers (concatenated linears).
+struct SteEpi {
+  int mode = 0;                                     // 0 off, 1 weight rows, 2 token rows
+  int nseg = 1;
+  int64_t seg_end[3] = {0, 0, 0};                   // row ends of the segments
+  const void* xseg[3] = {nullptr, nullptr, nullptr};
+  int x_dt = 0;  int64_t ldx = 0;
+  int let_mode = 0;  const float* s = nullptr;  const float* delta = nullptr;
+  const float* h = nullptr;  const float* z = nullptr;  int nbits = 16;
+  const float* rowvec = nullptr;
+  int col_mode = 0;
+  float* rowpart = nullptr;                         // [rows][tiles_n][2]
+  float* colpart = nullptr;                         // [tiles_m][2][cols]
+};
+
 struct Gemm {
   const void* A = nullptr;  int64_t lda = 0, strideA = 0;
   const void* B = nullptr;  int64_t ldb = 0, strideB = 0;  int b_group = 1;
@@ -72,9 +96,12 @@ struct Gemm {
   int accumulate = 0;
   int causal = CAUSAL_NONE;
   int dt = 1;                                       // OMQ_BF16 or OMQ_F32 operands
-  int ta = 0, tb = 0;                               // float32 only: A is [K x M] / B is [K x N]
+  int ta = 0, tb = 0;                               // A is [K x M] / B is [K x N]
+  SteEpi ste;                                       // bf16 only; mode 2 writes dL/dx into C
 };
 hipError_t launch_gemm(const Gemm& g, hipStream_t st);
+// The fused form's partial-buffer extents for a C of rows x cols.
+void gemm_ste_extents(int64_t rows, int64_t cols, int64_t* nslabs, int64_t* ntiles);
 
 // Transposes: out[c][r] = in[r][c]  (bf16 -> bf16, or float -> bf16 with an
 // optional straight bf16 copy written beside it).

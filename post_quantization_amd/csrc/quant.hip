@@ -111,6 +111,188 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd(RowQuantFwd a) {
   }
 }
 
+// Single-pass variant: the row (up to NCH * 1024 elements) stays in registers
+// between the min/max reduction and the quantization, so HBM sees one read of x
+// and one write of x_hat.
+template <int XDT, int NCH>
+__global__ __launch_bounds__(kThreads) void k_rowquant_fwd_reg(RowQuantFwd a) {
+  const int64_t r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wid = tid >> 6;
+  const char* xr = reinterpret_cast<const char*>(a.x) + r * a.ldx * (XDT == OMQ_F32 ? 4 : 2);
+  const int64_t cols = a.cols;
+  float xt[NCH][4];
+  float vmax = -FLT_MAX, vmin = FLT_MAX, dot = 0.f;
+  int imax = 0x7fffffff, imin = 0x7fffffff;
+#pragma unroll
+  for (int k = 0; k < NCH; ++k) {
+    const int64_t c = ((int64_t)k * kThreads + tid) * 4;
+    if (c < cols) {
+      float v[4];
+      load4(xr, XDT, c, v);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        xt[k][j] = let_x(v[j], a.let_mode, a.s, a.delta, c + j);
+        if (a.fold_delta) dot = fmaf(a.fold_delta[c + j], v[j], dot);
+      }
+    }
+  }
+  // per-thread scan in increasing column order keeps the first index on ties
+#pragma unroll
+  for (int k = 0; k < NCH; ++k) {
+    const int64_t c = ((int64_t)k * kThreads + tid) * 4;
+    if (c < cols) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (xt[k][j] > vmax || imax == 0x7fffffff) { vmax = xt[k][j]; imax = (int)(c + j); }
+        if (xt[k][j] < vmin || imin == 0x7fffffff) { vmin = xt[k][j]; imin = (int)(c + j); }
+      }
+    }
+  }
+  wave_argmax(vmax, imax);
+  wave_argmin(vmin, imin);
+  dot = wave_sum(dot);
+  __shared__ float s_max[4], s_min[4], s_dot[4];
+  __shared__ int s_imax[4], s_imin[4];
+  if (lane == 0) {
+    s_max[wid] = vmax; s_imax[wid] = imax;
+    s_min[wid] = vmin; s_imin[wid] = imin;
+    s_dot[wid] = dot;
+  }
+  __syncthreads();
+  float M = s_max[0], m = s_min[0], D = s_dot[0];
+  int iM = s_imax[0], im = s_imin[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) {
+    argmax_merge(M, iM, s_max[w], s_imax[w]);
+    argmin_merge(m, im, s_min[w], s_imin[w]);
+    D += s_dot[w];
+  }
+  const float gamma = a.a_gamma ? sigmoid_f32(a.a_gamma[r]) : 1.f;
+  const float beta = a.a_beta ? sigmoid_f32(a.a_beta[r]) : 1.f;
+  const RowQ q = row_step(M, m, gamma, beta, a.nbits);
+  if (tid == 0) {
+    if (a.h) a.h[r] = q.h;
+    if (a.z) a.z[r] = q.z;
+    if (a.amax) a.amax[r] = iM;
+    if (a.amin) a.amin[r] = im;
+    if (a.bias_out) a.bias_out[r] = (a.bias ? a.bias[r] : 0.f) + D;
+  }
+#pragma unroll
+  for (int k = 0; k < NCH; ++k) {
+    const int64_t c = ((int64_t)k * kThreads + tid) * 4;
+    if (c < cols) {
+      float o[4];
+      uint32_t cw = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float u = xt[k][j] / q.h;
+        const float rr = rintf(u) + q.z;
+        const float qq = fminf(fmaxf(rr, 0.f), q.Q);
+        o[j] = (qq - q.z) * q.h;
+        cw |= ((uint32_t)qq) << (8 * j);
+      }
+      store4(a.out, a.out_dt, r * a.ldo + c, o);
+      if (a.codes) *reinterpret_cast<uint32_t*>(a.codes + r * cols + c) = cw;
+    }
+  }
+}
+
+// One wave per row (rows up to NC * 512 elements): each lane keeps NC chunks of
+// 8 consecutive elements (16-byte bf16 loads, 2 x 16-byte float32 loads) in
+// registers; the row reductions are wave shuffles only, with no barrier.
+OMQ_DEV void load8(const char* xr, int dt, int64_t c, float v[8]) {
+  if (dt == OMQ_F32) {
+    const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(xr) + c);
+    const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(xr) + c + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    const uint4 t = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(xr) + c);
+    const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = __uint_as_float(w[q] << 16);
+      v[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+    }
+  }
+}
+
+template <int XDT, int NC>
+__global__ __launch_bounds__(kThreads) void k_rowquant_fwd_wave(RowQuantFwd a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= a.rows) return;
+  const char* xr = reinterpret_cast<const char*>(a.x) + r * a.ldx * (XDT == OMQ_F32 ? 4 : 2);
+  const int64_t cols = a.cols;
+  float xt[NC][8];
+  float vmax = -FLT_MAX, vmin = FLT_MAX, dot = 0.f;
+  int imax = 0x7fffffff, imin = 0x7fffffff;
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const int64_t c = ((int64_t)k * 64 + lane) * 8;
+    if (c < cols) {
+      float v[8];
+      if (c + 8 <= cols) {
+        load8(xr, XDT, c, v);
+      } else {
+        load4(xr, XDT, c, v);
+        v[4] = v[5] = v[6] = v[7] = 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        xt[k][j] = let_x(v[j], a.let_mode, a.s, a.delta, c + j < cols ? c + j : c);
+        if (a.fold_delta && c + j < cols) dot = fmaf(a.fold_delta[c + j], v[j], dot);
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const int64_t c = ((int64_t)k * 64 + lane) * 8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (c + j < cols) {
+        if (xt[k][j] > vmax || imax == 0x7fffffff) { vmax = xt[k][j]; imax = (int)(c + j); }
+        if (xt[k][j] < vmin || imin == 0x7fffffff) { vmin = xt[k][j]; imin = (int)(c + j); }
+      }
+    }
+  }
+  wave_argmax(vmax, imax);
+  wave_argmin(vmin, imin);
+  dot = wave_sum(dot);
+  const float gamma = a.a_gamma ? sigmoid_f32(a.a_gamma[r]) : 1.f;
+  const float beta = a.a_beta ? sigmoid_f32(a.a_beta[r]) : 1.f;
+  const RowQ q = row_step(vmax, vmin, gamma, beta, a.nbits);
+  if (lane == 0) {
+    if (a.h) a.h[r] = q.h;
+    if (a.z) a.z[r] = q.z;
+    if (a.amax) a.amax[r] = imax;
+    if (a.amin) a.amin[r] = imin;
+    if (a.bias_out) a.bias_out[r] = (a.bias ? a.bias[r] : 0.f) + dot;
+  }
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const int64_t c = ((int64_t)k * 64 + lane) * 8;
+    if (c < cols) {
+      float o[8];
+      uint32_t cw[2] = {0u, 0u};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float u = xt[k][j] / q.h;
+        const float rr = rintf(u) + q.z;
+        const float qq = fminf(fmaxf(rr, 0.f), q.Q);
+        o[j] = (qq - q.z) * q.h;
+        cw[j >> 2] |= ((uint32_t)qq) << (8 * (j & 3));
+      }
+      store4(a.out, a.out_dt, r * a.ldo + c, o);
+      if (a.codes) *reinterpret_cast<uint32_t*>(a.codes + r * cols + c) = cw[0];
+      if (c + 8 <= cols) {
+        store4(a.out, a.out_dt, r * a.ldo + c + 4, o + 4);
+        if (a.codes) *reinterpret_cast<uint32_t*>(a.codes + r * cols + c + 4) = cw[1];
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // backward tile pass: grid (col slabs, row tiles); wave w takes rows w, w+4, ...
 // ---------------------------------------------------------------------------
@@ -190,8 +372,8 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_bwd_tile(RowQuantBwd a, i
       sh = wave_sum(sh);
       sz = wave_sum(sz);
       if (lane == 0) {
-        rowpart[((int64_t)blockIdx.x * rows + r) * 2 + 0] = sh;
-        rowpart[((int64_t)blockIdx.x * rows + r) * 2 + 1] = sz;
+        rowpart[(r * gridDim.x + blockIdx.x) * 2 + 0] = sh;
+        rowpart[(r * gridDim.x + blockIdx.x) * 2 + 1] = sz;
       }
     }
   }
@@ -215,16 +397,35 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_bwd_tile(RowQuantBwd a, i
   }
 }
 
-// column finalize: out[c] (+)= sum over row tiles
-__global__ __launch_bounds__(kThreads) void k_colpart_reduce(const float* colpart, int ntiles,
+// column finalize, level 1: split the row tiles into kColSplit groups so the
+// reduction runs on (cols / 256) x kColSplit blocks; level 2 sums the groups in a
+// fixed order: out[c] (+)= sum over row tiles.
+constexpr int kColSplit = 32;
+
+__global__ __launch_bounds__(kThreads) void k_colpart_split(const float* colpart, int ntiles,
+                                                            int64_t cols, float* part2) {
+  const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (c >= cols) return;
+  const int per = (ntiles + kColSplit - 1) / kColSplit;
+  const int t0 = blockIdx.y * per, t1 = min(ntiles, t0 + per);
+  float s0 = 0.f, s1 = 0.f;
+  for (int t = t0; t < t1; ++t) {
+    s0 += colpart[((int64_t)t * 2 + 0) * cols + c];
+    s1 += colpart[((int64_t)t * 2 + 1) * cols + c];
+  }
+  part2[((int64_t)blockIdx.y * 2 + 0) * cols + c] = s0;
+  part2[((int64_t)blockIdx.y * 2 + 1) * cols + c] = s1;
+}
+
+__global__ __launch_bounds__(kThreads) void k_colpart_reduce(const float* part2, int nsplit,
                                                              int64_t cols, float* out0,
                                                              float* out1, int accumulate) {
   const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (c >= cols) return;
   float s0 = 0.f, s1 = 0.f;
-  for (int t = 0; t < ntiles; ++t) {
-    s0 += colpart[((int64_t)t * 2 + 0) * cols + c];
-    s1 += colpart[((int64_t)t * 2 + 1) * cols + c];
+  for (int t = 0; t < nsplit; ++t) {
+    s0 += part2[((int64_t)t * 2 + 0) * cols + c];
+    s1 += part2[((int64_t)t * 2 + 1) * cols + c];
   }
   if (out0) out0[c] = (accumulate ? out0[c] : 0.f) + s0;
   if (out1) out1[c] = (accumulate ? out1[c] : 0.f) + s1;
@@ -238,8 +439,8 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_bwd_rows(RowQuantBwd a, i
   if (r >= a.rows) return;
   float gh = 0.f, gzs = 0.f;
   for (int s = 0; s < nslabs; ++s) {
-    gh += rowpart[((int64_t)s * a.rows + r) * 2 + 0];
-    gzs += rowpart[((int64_t)s * a.rows + r) * 2 + 1];
+    gh += rowpart[(r * nslabs + s) * 2 + 0];
+    gzs += rowpart[(r * nslabs + s) * 2 + 1];
   }
   const char* xr = reinterpret_cast<const char*>(a.x) + r * a.ldx * (XDT == OMQ_F32 ? 4 : 2);
   auto xval = [&](int64_t c) -> float {
@@ -358,9 +559,47 @@ int bwd_rows_per_tile(int64_t rows) { return rows >= 8192 ? 32 : 16; }
 
 }  // namespace
 
+template <int XDT>
+bool launch_fwd_wave(const RowQuantFwd& a, hipStream_t st) {
+  // 16-byte row loads: bf16 rows must start on 8-element boundaries
+  if (XDT == OMQ_BF16 && (a.ldx % 8)) return false;
+  const int64_t nc = (a.cols + 511) / 512;
+  dim3 grid((unsigned)((a.rows + 3) / 4));
+#define OMQ_FWD_WAVE(N)                                                                   \
+  if (nc <= N) {                                                                          \
+    hipLaunchKernelGGL((k_rowquant_fwd_wave<XDT, N>), grid, dim3(kThreads), 0, st, a);   \
+    return true;                                                                          \
+  }
+  OMQ_FWD_WAVE(1) OMQ_FWD_WAVE(2) OMQ_FWD_WAVE(4) OMQ_FWD_WAVE(8)
+#undef OMQ_FWD_WAVE
+  return false;
+}
+
+template <int XDT>
+bool launch_fwd_reg(const RowQuantFwd& a, hipStream_t st) {
+  const int64_t nch = (a.cols + 4 * kThreads - 1) / (4 * kThreads);
+  dim3 grid((unsigned)a.rows);
+#define OMQ_FWD_REG(N)                                                                   \
+  if (nch <= N) {                                                                        \
+    hipLaunchKernelGGL((k_rowquant_fwd_reg<XDT, N>), grid, dim3(kThreads), 0, st, a);  \
+    return true;                                                                         \
+  }
+  OMQ_FWD_REG(1) OMQ_FWD_REG(2) OMQ_FWD_REG(4) OMQ_FWD_REG(8) OMQ_FWD_REG(12)
+  OMQ_FWD_REG(16) OMQ_FWD_REG(24) OMQ_FWD_REG(32)
+#undef OMQ_FWD_REG
+  return false;
+}
+
 hipError_t launch_rowquant_fwd(const RowQuantFwd& a, hipStream_t st) {
   if (a.rows == 0 || a.cols == 0) return hipSuccess;
   dim3 grid((unsigned)a.rows);
+  if (a.nbits < 16) {
+    bool done = a.x_dt == OMQ_F32 ? launch_fwd_wave<OMQ_F32>(a, st)
+                                  : launch_fwd_wave<OMQ_BF16>(a, st);
+    if (!done)
+      done = a.x_dt == OMQ_F32 ? launch_fwd_reg<OMQ_F32>(a, st) : launch_fwd_reg<OMQ_BF16>(a, st);
+    if (done) return hipGetLastError();
+  }
   if (a.x_dt == OMQ_F32)
     hipLaunchKernelGGL(k_rowquant_fwd<OMQ_F32>, grid, dim3(kThreads), 0, st, a);
   else
@@ -372,7 +611,7 @@ size_t rowquant_bwd_ws_bytes(int64_t rows, int64_t cols) {
   const int64_t nslabs = (cols + kSlab - 1) / kSlab;
   const int R = bwd_rows_per_tile(rows);
   const int64_t ntiles = (rows + R - 1) / R;
-  return (size_t)(nslabs * rows * 2 + ntiles * 2 * cols) * sizeof(float) + 256;
+  return ste_partials_floats(rows, cols, nslabs, ntiles) * sizeof(float);
 }
 
 hipError_t launch_rowquant_bwd(const RowQuantBwd& a, hipStream_t st) {
@@ -391,14 +630,37 @@ hipError_t launch_rowquant_bwd(const RowQuantBwd& a, hipStream_t st) {
                        colpart);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  e = launch_ste_colfinal(a, (int)ntiles, colpart, st);
+  if (e != hipSuccess) return e;
+  return launch_ste_rowfinal(a, (int)nslabs, rowpart, st);
+}
+
+size_t ste_partials_floats(int64_t rows, int64_t cols, int64_t nslabs, int64_t ntiles) {
+  return (size_t)(nslabs * rows * 2 + ntiles * 2 * cols + kColSplit * 2 * cols) + 64;
+}
+
+hipError_t launch_ste_colfinal(const RowQuantBwd& a, int ntiles, float* colpart,
+                               hipStream_t st) {
+  hipError_t e = hipSuccess;
   if (a.col_mode != COL_NONE && (a.out0 || a.out1)) {
-    hipLaunchKernelGGL(k_colpart_reduce, dim3((unsigned)((a.cols + kThreads - 1) / kThreads)),
-                       dim3(kThreads), 0, st, colpart, (int)ntiles, a.cols, a.out0, a.out1,
-                       a.accumulate);
+    float* part2 = colpart + (int64_t)ntiles * 2 * a.cols;
+    const unsigned cb = (unsigned)((a.cols + kThreads - 1) / kThreads);
+    const int nsplit = (int)std::min<int64_t>(kColSplit, ntiles);
+    hipLaunchKernelGGL(k_colpart_split, dim3(cb, (unsigned)nsplit), dim3(kThreads), 0, st,
+                       colpart, (int)ntiles, a.cols, part2);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_colpart_reduce, dim3(cb), dim3(kThreads), 0, st, part2, nsplit, a.cols,
+                       a.out0, a.out1, a.accumulate);
+    e = hipGetLastError();
   }
-  if (a.nbits < 16) {
+  return e;
+}
+
+hipError_t launch_ste_rowfinal(const RowQuantBwd& a, int nslabs, const float* rowpart,
+                               hipStream_t st) {
+  hipError_t e = hipSuccess;
+  if (a.nbits < 16 && a.rows > 0) {
     dim3 g2((unsigned)((a.rows + kThreads - 1) / kThreads));
     if (a.x_dt == OMQ_F32)
       hipLaunchKernelGGL(k_rowquant_bwd_rows<OMQ_F32>, g2, dim3(kThreads), 0, st, a,

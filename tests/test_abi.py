@@ -63,8 +63,10 @@ def test_validation_before_launch():
     assert L.omq_act_quant(FAKE + 2, 1, 4, 8, 4, 0, None, None, FAKE, 1, FAKE, FAKE, FAKE, FAKE,
                            None, None) == -4
     # bf16 GEMM needs K % 8 == 0
-    assert L.omq_gemm(4, 4, 12, FAKE, 12, FAKE, 12, 1, None, 1.0, FAKE, 4, 0, None) == -4
-    assert L.omq_gemm(4, 4, 16, FAKE, 8, FAKE, 16, 1, None, 1.0, FAKE, 4, 0, None) == -2
+    assert L.omq_gemm(4, 4, 12, FAKE, 12, 0, FAKE, 12, 0, 1, None, 1.0, FAKE, 4, 0, None) == -4
+    assert L.omq_gemm(4, 4, 16, FAKE, 8, 0, FAKE, 16, 0, 1, None, 1.0, FAKE, 4, 0, None) == -2
+    # transposed A: its contiguous extent is M (here 12, not a multiple of 8)
+    assert L.omq_gemm(12, 8, 16, FAKE, 12, 1, FAKE, 16, 0, 1, None, 1.0, FAKE, 8, 0, None) == -4
     # workspace too small
     assert L.omq_lwc_backward(FAKE, FAKE, 1, 8, 8, 4, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
                               None, FAKE, FAKE, None, None, FAKE, 16, None) == -5
