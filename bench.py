@@ -95,6 +95,9 @@ def main():
     ap.add_argument("--workload", default="llama7b_block_w4a4", choices=list(workloads()))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=256)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (known bytes) to calibrate the "
+                         "FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (the block-calibration step does not "
@@ -105,6 +108,16 @@ def main():
     import torch
     import post_quantization_amd as omq
     import synth
+
+    if args.copy_calibration:
+        a = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")    # 1 GiB
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": a.numel() * 4, "copy_bytes_written": b.numel() * 4,
+                          "launches": 3}), flush=True)
+        return
 
     c = workloads()[args.workload]
     dev = "cuda:0"

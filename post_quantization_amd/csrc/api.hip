@@ -97,7 +97,7 @@ int omq_act_quant(const void* X, int x_dt, int64_t T, int64_t C, int n_bits, int
   if (!dt_ok(x_dt) || !dt_ok(xh_dt)) return OMQ_E_DTYPE;
   if (T < 0 || C <= 0) return OMQ_E_SHAPE;
   if (C % 4) return OMQ_E_ALIGN;
-  if (!al16(X) || !al16(X_hat) || !al4(codes)) return OMQ_E_ALIGN;
+  if (!al16(X) || !al16(X_hat) || !al4(codes) || !al16(s) || !al16(delta)) return OMQ_E_ALIGN;
   RowQuantFwd a;
   a.x = X; a.x_dt = x_dt; a.rows = T; a.cols = C; a.ldx = C;
   a.let_mode = let_mode; a.s = s; a.delta = delta; a.nbits = n_bits;
@@ -143,7 +143,7 @@ int omq_lwc_backward(const float* gW_hat, const void* W, int w_dt, int64_t c_out
   if (!dt_ok(w_dt)) return OMQ_E_DTYPE;
   if (c_out < 0 || c_in <= 0) return OMQ_E_SHAPE;
   if (c_in % 4) return OMQ_E_ALIGN;
-  if (!al16(gW_hat) || !al16(W)) return OMQ_E_ALIGN;
+  if (!al16(gW_hat) || !al16(W) || !al16(s) || !al16(dy_colsum)) return OMQ_E_ALIGN;
   if (!ws || ws_bytes < omq_lwc_backward_workspace_size(c_out, c_in)) return OMQ_E_WORKSPACE;
   RowQuantBwd a;
   a.g = gW_hat; a.ldg = c_in; a.x = W; a.x_dt = w_dt; a.rows = c_out; a.cols = c_in;
@@ -174,7 +174,7 @@ int omq_act_quant_backward(const float* gX_hat, int64_t T, int64_t C, const void
   if (!dt_ok(x_dt)) return OMQ_E_DTYPE;
   if (T < 0 || C <= 0) return OMQ_E_SHAPE;
   if (C % 4) return OMQ_E_ALIGN;
-  if (!al16(gX_hat) || !al16(X) || !al16(gX)) return OMQ_E_ALIGN;
+  if (!al16(gX_hat) || !al16(X) || !al16(gX) || !al16(s) || !al16(delta)) return OMQ_E_ALIGN;
   if (!ws || ws_bytes < omq_act_quant_backward_workspace_size(T, C)) return OMQ_E_WORKSPACE;
   RowQuantBwd a;
   a.g = gX_hat; a.ldg = C; a.x = X; a.x_dt = x_dt; a.rows = T; a.cols = C; a.ldx = C;

@@ -243,6 +243,51 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
     // the LET) into C.
     static_assert(BM == 128 && BN == 128 && WM * WN == 4, "straight-through epilogue tile");
     float* T = reinterpret_cast<float*>(smem);     // [128][128] fp32 = the whole buffer
+    const SteEpi& e = g.ste;
+    const bool pass = e.nbits >= 16;
+    const float Q = pass ? 0.f : (float)((1 << e.nbits) - 1);
+    const int esz = e.x_dt == OMQ_F32 ? 4 : 2;
+    const int64_t gn = n0 + 2 * lane;             // this lane's two columns
+    const bool colv = gn < N;                     // N is a multiple of 8
+    constexpr int RW = BM / 4;                    // rows per wave
+    const int64_t wr0 = m0 + wid * RW;            // first row of this wave
+    // x is fetched 8 rows at a time, one batch ahead of its use (the first batch
+    // before the accumulators go through LDS); the per-row h, z and bias-fold
+    // scalars come from one lane-indexed load each (lane q holds row q).
+    constexpr int RB = 8;
+    auto fetch = [&](int b, uint32_t (&xa)[RB], uint32_t (&xa2)[RB]) {
+#pragma unroll
+      for (int q = 0; q < RB; ++q) {
+        const int64_t gm = wr0 + b * RB + q;
+        xa[q] = 0u;
+        xa2[q] = 0u;
+        if (gm < M && colv) {
+          const int sg = (e.nseg > 1 && gm >= e.seg_end[0]) + (e.nseg > 2 && gm >= e.seg_end[1]);
+          const int64_t lr = gm - (sg == 0 ? 0 : e.seg_end[sg - 1]);
+          const char* xr = reinterpret_cast<const char*>(e.xseg[sg]) + lr * e.ldx * esz;
+          if (e.x_dt == OMQ_F32) {
+            const uint2 t = *reinterpret_cast<const uint2*>(reinterpret_cast<const float*>(xr) + gn);
+            xa[q] = t.x;
+            xa2[q] = t.y;
+          } else {
+            xa[q] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(xr) + gn);
+          }
+        }
+      }
+    };
+    uint32_t xa[RB], xa2[RB], xn[RB], xn2[RB];
+    fetch(0, xa, xa2);
+    const int64_t rme = wr0 + (lane & (RW - 1));
+    const bool rmv = rme < M;
+    const float h_l = (!pass && rmv) ? e.h[rme] : 1.f;
+    const float z_l = (!pass && rmv) ? e.z[rme] : 0.f;
+    const float v_l = (e.rowvec && rmv) ? e.rowvec[rme] : 0.f;
+    float s_c[2] = {1.f, 1.f}, d_c[2] = {0.f, 0.f};
+    if (colv && e.let_mode != OMQ_LET_NONE) { s_c[0] = e.s[gn]; s_c[1] = e.s[gn + 1]; }
+    if (colv && e.let_mode == OMQ_LET_DIV && e.delta) {
+      d_c[0] = e.delta[gn];
+      d_c[1] = e.delta[gn + 1];
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -254,82 +299,77 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
           T[row * BN + col] = g.alpha * acc[i][j][r];
         }
     __syncthreads();
-    const SteEpi& e = g.ste;
-    const bool pass = e.nbits >= 16;
-    const float Q = pass ? 0.f : (float)((1 << e.nbits) - 1);
-    const int esz = e.x_dt == OMQ_F32 ? 4 : 2;
-    const int64_t gn = n0 + 2 * lane;             // this lane's two columns
-    const bool colv = gn < N;                     // N is a multiple of 8
-    float s_c[2] = {1.f, 1.f}, d_c[2] = {0.f, 0.f};
-    if (colv && e.let_mode != OMQ_LET_NONE) { s_c[0] = e.s[gn]; s_c[1] = e.s[gn + 1]; }
-    if (colv && e.let_mode == OMQ_LET_DIV && e.delta) {
-      d_c[0] = e.delta[gn];
-      d_c[1] = e.delta[gn + 1];
-    }
     const float r_c[2] = {1.f / s_c[0], 1.f / s_c[1]};
     float ca0[2] = {0.f, 0.f}, ca1[2] = {0.f, 0.f};
     float* Cp = g.C + bz * g.strideC;
-    for (int rr = 0; rr < BM / 4; ++rr) {
-      const int row = wid * (BM / 4) + rr;
-      const int64_t gm = m0 + row;
-      if (gm >= M) break;                          // wave-uniform
-      const float2 gv2 = *reinterpret_cast<const float2*>(&T[row * BN + 2 * lane]);
-      const float gvv[2] = {gv2.x, gv2.y};
-      const float hh = pass ? 1.f : e.h[gm];
-      const float zz = pass ? 0.f : e.z[gm];
-      const float vrow = e.rowvec ? e.rowvec[gm] : 0.f;
-      const int sg = (e.nseg > 1 && gm >= e.seg_end[0]) + (e.nseg > 2 && gm >= e.seg_end[1]);
-      const int64_t lr = gm - (sg == 0 ? 0 : e.seg_end[sg - 1]);
-      const char* xr = reinterpret_cast<const char*>(e.xseg[sg]) + lr * e.ldx * esz;
-      float ph = 0.f, pz = 0.f;
-      if (colv) {
+    for (int b = 0; b < RW / RB; ++b) {
+      if (wr0 + b * RB >= M) break;                // wave-uniform
+      if (b + 1 < RW / RB) fetch(b + 1, xn, xn2);
+#pragma unroll
+      for (int q = 0; q < RB; ++q) {
+        const int rw = b * RB + q;
+        const int64_t gm = wr0 + rw;
+        if (gm >= M) break;                        // wave-uniform
+        const float hh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(h_l), rw));
+        const float zz = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z_l), rw));
+        const float vr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v_l), rw));
+        const float2 gv2 = *reinterpret_cast<const float2*>(&T[(wid * RW + rw) * BN + 2 * lane]);
+        const float gvv[2] = {gv2.x, gv2.y};
         float xv[2];
         if (e.x_dt == OMQ_F32) {
-          const float2 t = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(xr) + gn);
-          xv[0] = t.x; xv[1] = t.y;
+          xv[0] = __uint_as_float(xa[q]);
+          xv[1] = __uint_as_float(xa2[q]);
         } else {
-          const uint32_t t = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(xr) + gn);
-          xv[0] = __uint_as_float(t << 16);
-          xv[1] = __uint_as_float(t & 0xffff0000u);
+          xv[0] = __uint_as_float(xa[q] << 16);
+          xv[1] = __uint_as_float(xa[q] & 0xffff0000u);
         }
-        float up[2];
+        float ph = 0.f, pz = 0.f;
+        if (colv) {
+          float up[2];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          float xt = xv[q];
-          if (e.let_mode == OMQ_LET_DIV) xt = (xv[q] - d_c[q]) / s_c[q];
-          else if (e.let_mode == OMQ_LET_MUL) xt = s_c[q] * xv[q];
-          const float gv = gvv[q];
-          float gns = gv;
-          if (!pass) {
-            const float u = xt / hh;
-            const float rq = rintf(u) + zz;
-            const bool in = (rq >= 0.f) && (rq <= Q);
-            const float qmz = fminf(fmaxf(rq, 0.f), Q) - zz;
-            ph += gv * (qmz - (in ? u : 0.f));
-            pz += in ? 0.f : gv;
-            gns = in ? gv : 0.f;
+          for (int c2 = 0; c2 < 2; ++c2) {
+            float xt = xv[c2];
+            if (e.let_mode == OMQ_LET_DIV) xt = (xv[c2] - d_c[c2]) / s_c[c2];
+            else if (e.let_mode == OMQ_LET_MUL) xt = s_c[c2] * xv[c2];
+            const float gv = gvv[c2];
+            float gns = gv;
+            if (!pass) {
+              const float u = xt / hh;
+              const float rq = rintf(u) + zz;
+              const bool in = (rq >= 0.f) && (rq <= Q);
+              const float qmz = fminf(fmaxf(rq, 0.f), Q) - zz;
+              ph += gv * (qmz - (in ? u : 0.f));
+              pz += in ? 0.f : gv;
+              gns = in ? gv : 0.f;
+            }
+            if (e.col_mode == COL_WEIGHT) {
+              ca0[c2] += gns * xv[c2];
+              ca1[c2] += vr * xv[c2];
+            } else if (e.col_mode == COL_ACT_DIV) {
+              ca0[c2] += gns * (-xt * r_c[c2]);
+              ca1[c2] += gns * (-r_c[c2]);
+            } else if (e.col_mode == COL_ACT_MUL) {
+              ca0[c2] += gns * xv[c2];
+            }
+            up[c2] = e.let_mode == OMQ_LET_DIV ? gns * r_c[c2]
+                     : e.let_mode == OMQ_LET_MUL ? gns * s_c[c2] : gns;
           }
-          if (e.col_mode == COL_WEIGHT) {
-            ca0[q] += gns * xv[q];
-            ca1[q] += vrow * xv[q];
-          } else if (e.col_mode == COL_ACT_DIV) {
-            ca0[q] += gns * (-xt * r_c[q]);
-            ca1[q] += gns * (-r_c[q]);
-          } else if (e.col_mode == COL_ACT_MUL) {
-            ca0[q] += gns * xv[q];
-          }
-          up[q] = e.let_mode == OMQ_LET_DIV ? gns * r_c[q]
-                  : e.let_mode == OMQ_LET_MUL ? gns * s_c[q] : gns;
+          if (e.mode == 2)
+            *reinterpret_cast<float2*>(&Cp[gm * g.ldc + gn]) = make_float2(up[0], up[1]);
         }
-        if (e.mode == 2) *reinterpret_cast<float2*>(&Cp[gm * g.ldc + gn]) = make_float2(up[0], up[1]);
+        if (!pass) {
+          ph = wave_sum(ph);
+          pz = wave_sum(pz);
+          if (lane == 0) {
+            e.rowpart[(gm * tiles_n + tn) * 2 + 0] = ph;
+            e.rowpart[(gm * tiles_n + tn) * 2 + 1] = pz;
+          }
+        }
       }
-      if (!pass) {
-        ph = wave_sum(ph);
-        pz = wave_sum(pz);
-        if (lane == 0) {
-          e.rowpart[(gm * tiles_n + tn) * 2 + 0] = ph;
-          e.rowpart[(gm * tiles_n + tn) * 2 + 1] = pz;
-        }
+#pragma unroll
+      for (int q = 0; q < RB; ++q) {
+        xa[q] = xn[q];
+        xa2[q] = xn2[q];
       }
     }
     if (e.col_mode != COL_NONE) {

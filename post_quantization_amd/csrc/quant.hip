@@ -217,6 +217,18 @@ OMQ_DEV void load8(const char* xr, int dt, int64_t c, float v[8]) {
   }
 }
 
+// 8 consecutive float32 parameters (s, delta) starting at c; n = 8 or 4 valid
+OMQ_DEV void load8f(const float* p, int64_t c, int n, float v[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p + c);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  if (n == 8) {
+    const float4 b = *reinterpret_cast<const float4*>(p + c + 4);
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    v[4] = v[5] = v[6] = v[7] = 1.f;
+  }
+}
+
 template <int XDT, int NC>
 __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_wave(RowQuantFwd a) {
   const int lane = threadIdx.x & 63;
@@ -231,17 +243,35 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_wave(RowQuantFwd a) {
   for (int k = 0; k < NC; ++k) {
     const int64_t c = ((int64_t)k * 64 + lane) * 8;
     if (c < cols) {
+      const int n = c + 8 <= cols ? 8 : 4;          // rows are multiples of 4 long
       float v[8];
-      if (c + 8 <= cols) {
+      if (n == 8) {
         load8(xr, XDT, c, v);
       } else {
         load4(xr, XDT, c, v);
         v[4] = v[5] = v[6] = v[7] = 0.f;
       }
+      if (a.let_mode == OMQ_LET_DIV) {
+        float sv[8], dv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        load8f(a.s, c, n, sv);
+        if (a.delta) load8f(a.delta, c, n, dv);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        xt[k][j] = let_x(v[j], a.let_mode, a.s, a.delta, c + j < cols ? c + j : c);
-        if (a.fold_delta && c + j < cols) dot = fmaf(a.fold_delta[c + j], v[j], dot);
+        for (int j = 0; j < 8; ++j) xt[k][j] = (v[j] - dv[j]) / sv[j];
+      } else if (a.let_mode == OMQ_LET_MUL) {
+        float sv[8];
+        load8f(a.s, c, n, sv);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xt[k][j] = sv[j] * v[j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xt[k][j] = v[j];
+      }
+      if (a.fold_delta) {
+        float fv[8];
+        load8f(a.fold_delta, c, n, fv);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (j < n) dot = fmaf(fv[j], v[j], dot);
       }
     }
   }
