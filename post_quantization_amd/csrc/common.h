@@ -98,6 +98,36 @@ struct RowQ {
   bool floor;
 };
 
+// rint(fl32(x / h)) without a division on the common path.  With rh = fl32(1/h),
+// u = fl32(x * rh) lies within 3 ulp of fl32(x / h) (one rounding each in the
+// reciprocal, the product and the true quotient), so the two can round to
+// different integers only when a half-integer lies between them.  Whenever u is
+// within |u| * 2^-20 (8 ulp) of a half-integer, or is not finite, the exact quotient
+// decides.  As |u - rint(u)| <= 1/2, every |u| >= 2^19 takes the exact path.  u
+// returns the quotient used, for sums where a few ulp do not matter.
+OMQ_DEV float rint_quot(float x, float h, float rh, float& u) {
+  u = x * rh;
+  const float r = rintf(u);
+  if (!(fabsf(fabsf(u - r) - 0.5f) > fabsf(u) * 0x1p-20f)) {
+    u = x / h;
+    return rintf(u);
+  }
+  return r;
+}
+
+// The same for a LET-divided input: rint(fl32(fl32(xd / s) / h)) with xd = x - delta
+// already rounded; the product form fl32(fl32(xd * rs) * rh) with rs = fl32(1/s)
+// carries at most 6 ulp against it, inside the same 8-ulp guard.
+OMQ_DEV float rint_quot2(float xd, float s, float rs, float h, float rh, float& u) {
+  u = (xd * rs) * rh;
+  const float r = rintf(u);
+  if (!(fabsf(fabsf(u - r) - 0.5f) > fabsf(u) * 0x1p-20f)) {
+    u = (xd / s) / h;
+    return rintf(u);
+  }
+  return r;
+}
+
 OMQ_DEV RowQ row_step(float M, float m, float gamma, float beta, int nbits) {
   RowQ r;
   r.Q = (float)((1 << nbits) - 1);

@@ -121,13 +121,14 @@ struct Stage {
 #pragma unroll
       for (int i = 0; i < kN; ++i) {
         const int id = tid + NT * i;
-        if (id < kUnits) *reinterpret_cast<uint4*>(S + lds_idx(id >> 3, (id & 7) * 8)) = r[i];
+        if (kUnits % NT == 0 || id < kUnits)
+          *reinterpret_cast<uint4*>(S + lds_idx(id >> 3, (id & 7) * 8)) = r[i];
       }
     } else {
 #pragma unroll
       for (int u = 0; u < kN; ++u) {
         const int id = tid + NT * u;
-        if (id >= kUnits) continue;
+        if (kUnits % NT != 0 && id >= kUnits) continue;
         const int rb = (id % (R / 8)) * 8, kc = (id / (R / 8)) * 4;
         const uint32_t w[4][4] = {{r[4 * u].x, r[4 * u].y, r[4 * u].z, r[4 * u].w},
                                   {r[4 * u + 1].x, r[4 * u + 1].y, r[4 * u + 1].z, r[4 * u + 1].w},
@@ -147,11 +148,41 @@ struct Stage {
   }
 };
 
+// Direct global -> LDS copy of a full R x 64 tile of a K-contiguous operand:
+// one wave instruction fills 8 swizzled LDS rows (1 KB, lane l at byte 16 l), so
+// lane l fetches the k-chunk that the swizzle places at its slot.  Completion is
+// tracked by vmcnt like any vector load.
+template <int R, int NW>
+OMQ_DEV void dma_tile(const uint16_t* P, int64_t ld, int64_t row0, int64_t k0, uint16_t* S,
+                      int wid, int lane) {
+  constexpr int NB = R / 8;
+  static_assert(NB % NW == 0, "8-row blocks must divide over the waves");
+#pragma unroll
+  for (int i = 0; i < NB / NW; ++i) {
+    const int b = wid + NW * i;
+    const int r = b * 8 + (lane >> 3);
+    const int c = ((lane & 7) ^ r ^ (r >> 3)) & 7;
+    __builtin_amdgcn_global_load_lds(
+        (const void*)(P + (row0 + r) * ld + k0 + c * 8),
+        (__attribute__((address_space(3))) void*)(S + b * 8 * LDP), 16, 0, 0);
+  }
+}
+
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+OMQ_DEV void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // BM x BN tile, WM x WN waves, each wave (BM/WM) x (BN/WN) as 32x32 MFMA blocks.
-template <int BM, int BN, int WM, int WN, int TA, int TB, int EPI>
+// DMA: K-contiguous operands are copied straight into LDS (the launcher only sets
+// it when every tile is full and the operands are 16-byte aligned); K-major
+// operands are always staged through registers.
+template <int BM, int BN, int WM, int WN, int TA, int TB, int EPI, int DMA>
 __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m, int tiles_n) {
-  constexpr int NT = WM * WN * 64;
+  constexpr int NT = WM * WN * 64, NW = WM * WN;
   constexpr int FM = BM / WM / 32, FN = BN / WN / 32;   // MFMA blocks per wave
+  constexpr bool kDmaA = DMA && !TA, kDmaB = DMA && !TB;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * LDP];
   uint16_t (*As)[BM * LDP] = reinterpret_cast<uint16_t (*)[BM * LDP]>(smem);
   uint16_t (*Bs)[BN * LDP] = reinterpret_cast<uint16_t (*)[BN * LDP]>(smem + 2 * BM * LDP);
@@ -173,6 +204,13 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
 
   Stage<TA, BM, NT> sa;
   Stage<TB, BN, NT> sb;
+  // register-staged loads a wave issues per K step (they stay in flight across a step)
+  constexpr int kStaged = (kDmaA ? 0 : (TA ? 4 : 1) * Stage<TA, BM, NT>::kN) +
+                          (kDmaB ? 0 : (TB ? 4 : 1) * Stage<TB, BN, NT>::kN);
+  // the vmcnt waits below count on every wave issuing exactly kStaged staged loads
+  static_assert(!DMA || ((kDmaA || Stage<TA, BM, NT>::kUnits % NT == 0) &&
+                         (kDmaB || Stage<TB, BN, NT>::kUnits % NT == 0)),
+                "staged tiles must divide evenly over the threads");
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -182,53 +220,106 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // Pipeline per K step: read every fragment of the current LDS buffer, write the
-  // next tile (loaded one step earlier) into the other buffer, issue the global
-  // loads two tiles ahead, then run the MFMAs while those are in flight.
+  // Pipeline per K step: start the copies of the next tile into the other LDS
+  // buffer (direct for DMA operands, register-staged tiles loaded one step earlier
+  // otherwise), issue the staged loads two tiles ahead, then run the MFMAs with the
+  // fragments of each 16-k slice read one slice ahead; wait for the direct copies
+  // and meet at one barrier.
   const int nk = (int)((ke - kb + BK - 1) / BK);
   if (nk > 0) {
-    sa.load(A, g.lda, M, m0, kb, ke, tid);
-    sb.load(B, g.ldb, N, n0, kb, ke, tid);
-    sa.store(As[0], tid);
-    sb.store(Bs[0], tid);
+    if (kDmaA) dma_tile<BM, NW>(A, g.lda, m0, kb, As[0], wid, lane);
+    else { sa.load(A, g.lda, M, m0, kb, ke, tid); sa.store(As[0], tid); }
+    if (kDmaB) dma_tile<BN, NW>(B, g.ldb, n0, kb, Bs[0], wid, lane);
+    else { sb.load(B, g.ldb, N, n0, kb, ke, tid); sb.store(Bs[0], tid); }
     if (nk > 1) {
-      sa.load(A, g.lda, M, m0, kb + BK, ke, tid);
-      sb.load(B, g.ldb, N, n0, kb + BK, ke, tid);
+      if (!kDmaA) sa.load(A, g.lda, M, m0, kb + BK, ke, tid);
+      if (!kDmaB) sb.load(B, g.ldb, N, n0, kb + BK, ke, tid);
     }
+  }
+  if constexpr (kDmaA || kDmaB) {
+    if (nk > 1) wait_vmem<kStaged>(); else wait_vmem<0>();
   }
   __syncthreads();
   const int fr = lane & 31, fk = (lane >> 5) * 8;
+  const int ar = wm * (BM / WM) + fr, br = wn * (BN / WN) + fr;
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    bf16x8 af[BK / 16][FM], bf[BK / 16][FN];
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
+    const uint16_t* Ab = As[buf];
+    const uint16_t* Bb = Bs[buf];
+    // next tile into the other buffer; staged loads two tiles ahead
+    auto issue_next = [&]() {
+      if (kt + 1 < nk) {
+        const int64_t k1 = kb + (int64_t)(kt + 1) * BK;
+        if (kDmaA) dma_tile<BM, NW>(A, g.lda, m0, k1, As[buf ^ 1], wid, lane);
+        if (kDmaB) dma_tile<BN, NW>(B, g.ldb, n0, k1, Bs[buf ^ 1], wid, lane);
+        if (!kDmaA) sa.store(As[buf ^ 1], tid);
+        if (!kDmaB) sb.store(Bs[buf ^ 1], tid);
+        if (kt + 2 < nk) {
+          const int64_t k2 = kb + (int64_t)(kt + 2) * BK;
+          if (!kDmaA) sa.load(A, g.lda, M, m0, k2, ke, tid);
+          if (!kDmaB) sb.load(B, g.ldb, N, n0, k2, ke, tid);
+        }
+      }
+    };
+    if constexpr (DMA) {
+      // copies first, then the fragments of each 16-k slice read one slice ahead
+      // of their MFMAs
+      issue_next();
+      bf16x8 af[2][FM], bf[2][FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        af[kk][i] = *reinterpret_cast<const bf16x8*>(
-            &As[buf][lds_idx(wm * (BM / WM) + i * 32 + fr, kk * 16 + fk)]);
+        af[0][i] = *reinterpret_cast<const bf16x8*>(&Ab[lds_idx(ar + i * 32, fk)]);
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        bf[kk][j] = *reinterpret_cast<const bf16x8*>(
-            &Bs[buf][lds_idx(wn * (BN / WN) + j * 32 + fr, kk * 16 + fk)]);
-    }
-    if (kt + 1 < nk) {
-      sa.store(As[buf ^ 1], tid);
-      sb.store(Bs[buf ^ 1], tid);
-      if (kt + 2 < nk) {
-        const int64_t k2 = kb + (int64_t)(kt + 2) * BK;
-        sa.load(A, g.lda, M, m0, k2, ke, tid);
-        sb.load(B, g.ldb, N, n0, k2, ke, tid);
+        bf[0][j] = *reinterpret_cast<const bf16x8*>(&Bb[lds_idx(br + j * 32, fk)]);
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        const int cu = kk & 1;
+        if (kk + 1 < BK / 16) {
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+            af[cu ^ 1][i] = *reinterpret_cast<const bf16x8*>(
+                &Ab[lds_idx(ar + i * 32, (kk + 1) * 16 + fk)]);
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            bf[cu ^ 1][j] = *reinterpret_cast<const bf16x8*>(
+                &Bb[lds_idx(br + j * 32, (kk + 1) * 16 + fk)]);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cu][i], bf[cu][j], acc[i][j],
+                                                                0, 0, 0);
       }
-    }
+    } else {
+      // every fragment of this buffer read first, then the next tile's stores and
+      // loads, then the MFMAs while those are in flight
+      bf16x8 af[BK / 16][FM], bf[BK / 16][FN];
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk)
+      for (int kk = 0; kk < BK / 16; ++kk) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < FM; ++i)
+          af[kk][i] = *reinterpret_cast<const bf16x8*>(&Ab[lds_idx(ar + i * 32, kk * 16 + fk)]);
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk][i], bf[kk][j], acc[i][j], 0,
-                                                              0, 0);
+          bf[kk][j] = *reinterpret_cast<const bf16x8*>(&Bb[lds_idx(br + j * 32, kk * 16 + fk)]);
+      }
+      issue_next();
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk][i], bf[kk][j], acc[i][j],
+                                                                0, 0, 0);
+    }
+    // the direct copies into the other buffer must land before the barrier; the
+    // staged loads of the tile after next may stay in flight
+    if constexpr (kDmaA || kDmaB) {
+      if (kt + 2 < nk) wait_vmem<kStaged>(); else wait_vmem<0>();
+    }
     __syncthreads();
   }
 
@@ -300,6 +391,7 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
         }
     __syncthreads();
     const float r_c[2] = {1.f / s_c[0], 1.f / s_c[1]};
+    const float rh_l = 1.f / h_l;
     float ca0[2] = {0.f, 0.f}, ca1[2] = {0.f, 0.f};
     float* Cp = g.C + bz * g.strideC;
     for (int b = 0; b < RW / RB; ++b) {
@@ -311,6 +403,7 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
         const int64_t gm = wr0 + rw;
         if (gm >= M) break;                        // wave-uniform
         const float hh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(h_l), rw));
+        const float rhh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rh_l), rw));
         const float zz = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z_l), rw));
         const float vr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v_l), rw));
         const float2 gv2 = *reinterpret_cast<const float2*>(&T[(wid * RW + rw) * BN + 2 * lane]);
@@ -328,14 +421,19 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
           float up[2];
 #pragma unroll
           for (int c2 = 0; c2 < 2; ++c2) {
+            // x~: exact for MUL / NONE; for DIV within 2 ulp (it only enters sums),
+            // the in-range decision below still follows the exact quotient
+            const float xd = xv[c2] - d_c[c2];
             float xt = xv[c2];
-            if (e.let_mode == OMQ_LET_DIV) xt = (xv[c2] - d_c[c2]) / s_c[c2];
+            if (e.let_mode == OMQ_LET_DIV) xt = xd * r_c[c2];
             else if (e.let_mode == OMQ_LET_MUL) xt = s_c[c2] * xv[c2];
             const float gv = gvv[c2];
             float gns = gv;
             if (!pass) {
-              const float u = xt / hh;
-              const float rq = rintf(u) + zz;
+              float u;
+              const float rq = (e.let_mode == OMQ_LET_DIV
+                                    ? rint_quot2(xd, s_c[c2], r_c[c2], hh, rhh, u)
+                                    : rint_quot(xt, hh, rhh, u)) + zz;
               const bool in = (rq >= 0.f) && (rq <= Q);
               const float qmz = fminf(fmaxf(rq, 0.f), Q) - zz;
               ph += gv * (qmz - (in ? u : 0.f));
@@ -358,18 +456,30 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
             *reinterpret_cast<float2*>(&Cp[gm * g.ldc + gn]) = make_float2(up[0], up[1]);
         }
         if (!pass) {
-          ph = wave_sum(ph);
-          pz = wave_sum(pz);
-          if (lane == 0) {
-            e.rowpart[(gm * tiles_n + tn) * 2 + 0] = ph;
-            e.rowpart[(gm * tiles_n + tn) * 2 + 1] = pz;
-          }
+          // the row's gradients are consumed: its LDS row now holds the lanes'
+          // partials (g_h in columns 0..63, out-of-range sum in 64..127)
+          float* tr = &T[(wid * RW + rw) * BN];
+          tr[lane] = ph;
+          tr[64 + lane] = pz;
         }
       }
 #pragma unroll
       for (int q = 0; q < RB; ++q) {
         xa[q] = xn[q];
         xa2[q] = xn2[q];
+      }
+    }
+    if (!pass) {
+      // lane l sums row (l & 31)'s 64 partials of kind (l >> 5), starting at a
+      // lane-dependent offset so the 64 lanes read 64 different banks
+      const int rw = lane & 31, half = lane >> 5;
+      const int64_t gm = wr0 + rw;
+      if (gm < M) {
+        const float* src = &T[(wid * RW + rw) * BN + half * 64];
+        float sum = 0.f;
+#pragma unroll 16
+        for (int j = 0; j < 64; ++j) sum += src[(j + lane) & 63];
+        e.rowpart[(gm * tiles_n + tn) * 2 + half] = sum;
       }
     }
     if (e.col_mode != COL_NONE) {
@@ -397,6 +507,21 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
   }
   float* C = g.C ? g.C + bz * g.strideC : nullptr;
   uint16_t* Cb = g.Cb ? g.Cb + bz * g.strideC : nullptr;
+  if (m0 + BM <= M && n0 + BN <= N && !g.resid && !g.accumulate && !Cb) {
+    // whole tile, plain fp32 store (+ bias): no per-element conditions
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t gn = n0 + wn * (BN / WN) + j * 32 + (lane & 31);
+      const float bias = g.bias ? g.bias[gn] : 0.f;
+      float* Cc = C + (m0 + wm * (BM / WM) + 4 * (lane >> 5)) * g.ldc + gn;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          Cc[(i * 32 + 8 * (r >> 2) + (r & 3)) * g.ldc] = g.alpha * acc[i][j][r] + bias;
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -429,13 +554,34 @@ void launch_cfg(const Gemm& g, hipStream_t st) {
   const int tiles_m = (int)((g.M + BM - 1) / BM), tiles_n = (int)((g.N + BN - 1) / BN);
   const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)g.batch), block(WM * WN * 64);
   if (!g.ta && !g.tb)
-    hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, 0, 0, 0>), grid, block, 0, st, g, tiles_m, tiles_n);
+    hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, 0, 0, 0, 0>), grid, block, 0, st, g, tiles_m,
+                       tiles_n);
   else if (!g.ta && g.tb)
-    hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, 0, 1, 0>), grid, block, 0, st, g, tiles_m, tiles_n);
+    hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, 0, 1, 0, 0>), grid, block, 0, st, g, tiles_m,
+                       tiles_n);
   else if (g.ta && !g.tb)
-    hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, 1, 0, 0>), grid, block, 0, st, g, tiles_m, tiles_n);
+    hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, 1, 0, 0, 0>), grid, block, 0, st, g, tiles_m,
+                       tiles_n);
   else
-    hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, 1, 1, 0>), grid, block, 0, st, g, tiles_m, tiles_n);
+    hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, 1, 1, 0, 0>), grid, block, 0, st, g, tiles_m,
+                       tiles_n);
+}
+
+// both operands K-contiguous, every tile full: direct-to-LDS operand copies
+template <int BM, int BN, int WM, int WN>
+void launch_nn_dma(const Gemm& g, hipStream_t st) {
+  const int tiles_m = (int)(g.M / BM), tiles_n = (int)(g.N / BN);
+  const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)g.batch), block(WM * WN * 64);
+  hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, 0, 0, 0, 1>), grid, block, 0, st, g, tiles_m,
+                     tiles_n);
+}
+
+// Direct LDS copies need whole tiles (no bounds checks), whole K steps (the causal
+// K ranges start and end on multiples of 64 when K does) and 16-byte aligned rows.
+bool dma_fits(const Gemm& g, int BM, int BN) {
+  auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  return g.M % BM == 0 && g.N % BN == 0 && g.K % BK == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 &&
+         g.strideA % 8 == 0 && g.strideB % 8 == 0 && al16(g.A) && al16(g.B);
 }
 
 // the straight-through epilogue runs on 128 x 128 tiles of 4 waves (64-row blocks,
@@ -447,10 +593,10 @@ void launch_ste(const Gemm& g, hipStream_t st) {
   const int tiles_n = (int)((g.N + kSteBN - 1) / kSteBN);
   const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)g.batch), block(kSteWM * kSteWN * 64);
   if (g.ta)
-    hipLaunchKernelGGL((k_gemm_bf16<kSteBM, kSteBN, kSteWM, kSteWN, 1, 1, 1>), grid, block, 0, st,
+    hipLaunchKernelGGL((k_gemm_bf16<kSteBM, kSteBN, kSteWM, kSteWN, 1, 1, 1, 0>), grid, block, 0, st,
                        g, tiles_m, tiles_n);
   else
-    hipLaunchKernelGGL((k_gemm_bf16<kSteBM, kSteBN, kSteWM, kSteWN, 0, 1, 1>), grid, block, 0, st,
+    hipLaunchKernelGGL((k_gemm_bf16<kSteBM, kSteBN, kSteWM, kSteWN, 0, 1, 1, 0>), grid, block, 0, st,
                        g, tiles_m, tiles_n);
 }
 
@@ -553,12 +699,6 @@ __global__ __launch_bounds__(256) void k_f32_to_bf16(const float* in, int64_t ro
 
 }  // namespace
 
-// Tile configuration per problem: 0: 128x128 (4 waves), 1: 256x128 (4 waves),
-// 2: 128x256 (4 waves), 4: 256x128 (8 waves).
-int gemm_config(const Gemm& g) {
-  return 0;
-}
-
 void gemm_ste_extents(int64_t rows, int64_t cols, int64_t* nslabs, int64_t* ntiles) {
   *nslabs = (cols + kSteBN - 1) / kSteBN;
   *ntiles = (rows + kSteBM - 1) / kSteBM;
@@ -572,12 +712,15 @@ hipError_t launch_gemm(const Gemm& g, hipStream_t st) {
     return hipGetLastError();
   }
   if (g.dt == OMQ_BF16) {
-    switch (gemm_config(g)) {
-      case 1: launch_cfg<256, 128, 2, 2>(g, st); break;
-      case 2: launch_cfg<128, 256, 2, 2>(g, st); break;
-      case 4: launch_cfg<256, 128, 4, 2>(g, st); break;
-      default: launch_cfg<128, 128, 2, 2>(g, st); break;
-    }
+    // 256 x 256 tiles halve the operand traffic per flop; they pay once there are
+    // enough of them to keep every CU busy for two rounds
+    const int64_t big_tiles = (g.M / 256) * (g.N / 256) * g.batch;
+    if (!g.ta && !g.tb && big_tiles >= 512 && dma_fits(g, 256, 256))
+      launch_nn_dma<256, 256, 2, 4>(g, st);
+    else if (!g.ta && !g.tb && dma_fits(g, 128, 128))
+      launch_nn_dma<128, 128, 2, 2>(g, st);
+    else
+      launch_cfg<128, 128, 2, 2>(g, st);
   } else {
     dim3 grid((unsigned)((g.N + 63) / 64), (unsigned)((g.M + 63) / 64), (unsigned)g.batch);
     hipLaunchKernelGGL(k_gemm_f32, grid, dim3(256), 0, st, g);

@@ -93,6 +93,7 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd(RowQuantFwd a) {
     if (a.amin) a.amin[r] = im;
     if (a.bias_out) a.bias_out[r] = (a.bias ? a.bias[r] : 0.f) + D;
   }
+  const float rh = 1.f / q.h;
   for (int64_t c = (int64_t)tid * 4; c < cols; c += 4 * kThreads) {
     float v[4], o[4];
     load4(xr, XDT, c, v);
@@ -100,8 +101,8 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd(RowQuantFwd a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float xt = let_x(v[j], a.let_mode, a.s, a.delta, c + j);
-      float u = xt / q.h;
-      float rr = rintf(u) + q.z;
+      float u;
+      float rr = rint_quot(xt, q.h, rh, u) + q.z;
       float qq = fminf(fmaxf(rr, 0.f), q.Q);
       o[j] = (qq - q.z) * q.h;
       cw |= ((uint32_t)qq) << (8 * j);
@@ -178,6 +179,7 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_reg(RowQuantFwd a) {
     if (a.amin) a.amin[r] = im;
     if (a.bias_out) a.bias_out[r] = (a.bias ? a.bias[r] : 0.f) + D;
   }
+  const float rh = 1.f / q.h;
 #pragma unroll
   for (int k = 0; k < NCH; ++k) {
     const int64_t c = ((int64_t)k * kThreads + tid) * 4;
@@ -186,8 +188,8 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_reg(RowQuantFwd a) {
       uint32_t cw = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float u = xt[k][j] / q.h;
-        const float rr = rintf(u) + q.z;
+        float u;
+        const float rr = rint_quot(xt[k][j], q.h, rh, u) + q.z;
         const float qq = fminf(fmaxf(rr, 0.f), q.Q);
         o[j] = (qq - q.z) * q.h;
         cw |= ((uint32_t)qq) << (8 * j);
@@ -299,6 +301,7 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_wave(RowQuantFwd a) {
     if (a.amin) a.amin[r] = imin;
     if (a.bias_out) a.bias_out[r] = (a.bias ? a.bias[r] : 0.f) + dot;
   }
+  const float rh = 1.f / q.h;
 #pragma unroll
   for (int k = 0; k < NC; ++k) {
     const int64_t c = ((int64_t)k * 64 + lane) * 8;
@@ -307,8 +310,8 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_wave(RowQuantFwd a) {
       uint32_t cw[2] = {0u, 0u};
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float u = xt[k][j] / q.h;
-        const float rr = rintf(u) + q.z;
+        float u;
+        const float rr = rint_quot(xt[k][j], q.h, rh, u) + q.z;
         const float qq = fminf(fmaxf(rr, 0.f), q.Q);
         o[j] = (qq - q.z) * q.h;
         cw[j >> 2] |= ((uint32_t)qq) << (8 * (j & 3));
@@ -339,6 +342,16 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_bwd_tile(RowQuantBwd a, i
   float acc0[16], acc1[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) { acc0[i] = 0.f; acc1[i] = 0.f; }
+  // this lane's 16 columns: LET scale, shift and reciprocal scale, for every row
+  float sc[16], dc[16], rc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t c = c0 + lane * 4 + 256 * (i >> 2) + (i & 3);
+    const bool cv = c < cols && a.let_mode != OMQ_LET_NONE;
+    sc[i] = cv ? a.s[c] : 1.f;
+    dc[i] = (cv && a.let_mode == OMQ_LET_DIV && a.delta) ? a.delta[c] : 0.f;
+    rc[i] = 1.f / sc[i];
+  }
 
   for (int rr_ = wid; rr_ < rows_per_tile; rr_ += 4) {
     const int64_t r = r0 + rr_;
@@ -346,6 +359,7 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_bwd_tile(RowQuantBwd a, i
     const char* xr = reinterpret_cast<const char*>(a.x) + r * a.ldx * (XDT == OMQ_F32 ? 4 : 2);
     const float* gr = a.g + r * a.ldg;
     const float h = pass ? 1.f : a.h[r];
+    const float rh = 1.f / h;
     const float z = pass ? 0.f : a.z[r];
     const float vrow = a.rowvec ? a.rowvec[r] : 0.f;
     float sh = 0.f, sz = 0.f;
@@ -360,39 +374,41 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_bwd_tile(RowQuantBwd a, i
       float up[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float xt = let_x(v[j], a.let_mode, a.s, a.delta, c + j);
+        const int ai = k * 4 + j;
+        // x~ (exact for MUL / NONE; within 2 ulp for DIV, used only in sums)
+        const float xd = v[j] - dc[ai];
+        const float xt = a.let_mode == OMQ_LET_DIV ? xd * rc[ai]
+                         : a.let_mode == OMQ_LET_MUL ? sc[ai] * v[j] : v[j];
         float gns;
         if (pass) {
           gns = gg[j];
         } else {
-          const float u = xt / h;
-          const float rr = rintf(u) + z;
+          float u;
+          const float rr = (a.let_mode == OMQ_LET_DIV ? rint_quot2(xd, sc[ai], rc[ai], h, rh, u)
+                                                      : rint_quot(xt, h, rh, u)) + z;
           const bool in = (rr >= 0.f) && (rr <= Q);
           const float qmz = fminf(fmaxf(rr, 0.f), Q) - z;
           sh += gg[j] * (qmz - (in ? u : 0.f));
           sz += in ? 0.f : gg[j];
           gns = in ? gg[j] : 0.f;
         }
-        const int ai = k * 4 + j;
         switch (a.col_mode) {
           case COL_WEIGHT:
             acc0[ai] += gns * v[j];
             acc1[ai] += vrow * v[j];
             break;
-          case COL_ACT_DIV: {
-            const float sc = a.s[c + j];
-            acc0[ai] += gns * (-xt / sc);
-            acc1[ai] += gns * (-1.f / sc);
+          case COL_ACT_DIV:
+            acc0[ai] += gns * (-xt * rc[ai]);
+            acc1[ai] += gns * (-rc[ai]);
             break;
-          }
           case COL_ACT_MUL:
             acc0[ai] += gns * v[j];
             break;
           default:
             break;
         }
-        if (a.let_mode == OMQ_LET_DIV) up[j] = gns / a.s[c + j];
-        else if (a.let_mode == OMQ_LET_MUL) up[j] = gns * a.s[c + j];
+        if (a.let_mode == OMQ_LET_DIV) up[j] = gns * rc[ai];
+        else if (a.let_mode == OMQ_LET_MUL) up[j] = gns * sc[ai];
         else up[j] = gns;
       }
       if (a.gx)

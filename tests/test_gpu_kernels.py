@@ -90,6 +90,89 @@ def test_act_quant_bitexact(T, C, nbits, mode, xdt):
     assert np.array_equal(host(rb["X_hat"]).astype(np.float64), bf16_np(st.xhat))
 
 
+def _near_tie_rows(rng, rows, cols, nbits):
+    """Rows (in x~ space) whose quotients x~/h sit on, or within 3 ulp of, a
+    half-integer: every element is a rounding decision that a quotient formed
+    as x * (1/h), a few ulp off the true one, could get wrong."""
+    Q = F32(2 ** nbits - 1)
+    out = np.empty((rows, cols), F32)
+    for r in range(rows):
+        m, M = F32(-rng.uniform(0.5, 3.0)), F32(rng.uniform(0.5, 3.0))
+        h = F32(F32(M - m) / Q)
+        lo, hi = float(m / h), float(M / h)
+        ks = np.arange(np.ceil(lo), np.floor(hi)) + 0.5
+        ks = ks[(ks > lo + 0.5) & (ks < hi - 0.5)]
+        y = (rng.choice(ks, cols).astype(F32) * h).astype(F32)
+        steps = rng.integers(-3, 4, cols)
+        for st in range(1, 4):
+            y = np.where(steps >= st, np.nextafter(y, F32(np.inf)), y)
+            y = np.where(steps <= -st, np.nextafter(y, F32(-np.inf)), y)
+        y[0], y[1] = m, M
+        out[r] = y[rng.permutation(cols)]
+    return out
+
+
+@pytest.mark.parametrize("nbits,mode", [(4, "none"), (2, "mul"), (4, "div"), (8, "div")])
+def test_act_quant_near_ties(nbits, mode):
+    log("act_quant_near_ties", nbits, mode)
+    rng = np.random.default_rng(40 + nbits)
+    T, C = 64, 520
+    Xt0 = _near_tie_rows(rng, T, C, nbits)
+    s = rng.uniform(0.5, 2.0, C).astype(F32)
+    d = (rng.standard_normal(C) * 0.3).astype(F32)
+    ops = ExactOps(bf16=False)
+    if mode == "none":
+        X, lm, s, d = Xt0, omq.LET_NONE, None, None
+        Xt = X
+    elif mode == "mul":
+        X, lm, d = (Xt0 / s).astype(F32), omq.LET_MUL, None
+        Xt = ops.mul(X, s)
+    else:
+        X, lm = (Xt0 * s + d).astype(F32), omq.LET_DIV
+        Xt = quant.let_act(X, s, d)
+    st, _ = quant.act_quant(Xt, nbits)
+    r = omq.act_quant(dev(X), nbits, lm, dev(s) if s is not None else None,
+                      dev(d) if d is not None else None, out_dtype=torch.float32, want_codes=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(r["h"]), st.h)
+    assert np.array_equal(host(r["codes"]), st.codes)
+    assert np.array_equal(host(r["X_hat"]), st.xhat)
+    # backward: dL/dx is gated element by element by the in-range decision
+    g = rng.standard_normal((T, C)).astype(F32)
+    gXt = quant.act_quant_bwd(g, st)
+    gx, _, _ = omq.act_quant_backward(dev(g), dev(X), nbits, r["h"], r["z"], r["arg_max"],
+                                      r["arg_min"], lm, dev(s) if s is not None else None,
+                                      dev(d) if d is not None else None, want_gx=True)
+    torch.cuda.synchronize()
+    expect = gXt / s.astype(np.float64) if mode == "div" else (
+        gXt * s.astype(np.float64) if mode == "mul" else gXt)
+    err = np.abs(host(gx) - expect)
+    assert np.all(err <= 1e-5 * (np.abs(expect) + 1.0))
+
+
+@pytest.mark.parametrize("nbits", [2, 3, 4])
+def test_lwc_near_ties(nbits):
+    """Weight side at gamma = beta = 1 (logits 30 give sigmoid exactly 1 in float32),
+    LET scale s on the columns, float32 weights built so that s * W / h lands on
+    or next to half-integers."""
+    log("lwc_near_ties", nbits)
+    rng = np.random.default_rng(50 + nbits)
+    c_out, c_in = 48, 1032
+    Wt0 = _near_tie_rows(rng, c_out, c_in, nbits)
+    s = rng.uniform(0.5, 2.0, c_in).astype(F32)
+    W = (Wt0 / s).astype(F32)
+    ag = np.full(c_out, 30.0, F32)
+    ab = np.full(c_out, 30.0, F32)
+    ref = quant.lwc_fakequant(W, ag, ab, nbits, s, None, None)
+    r = omq.lwc_fakequant(dev(W), dev(ag), dev(ab), nbits, dev(s), out_dtype=torch.float32,
+                          want_codes=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(r["h"]), ref.h)
+    assert np.array_equal(host(r["z"]), ref.z)
+    assert np.array_equal(host(r["codes"]), ref.codes)
+    assert np.array_equal(host(r["W_hat"]), ref.W_hat)
+
+
 def test_act_quant_passthrough_and_let_apply():
     rng = np.random.default_rng(3)
     X = rng.standard_normal((24, 64)).astype(F32)
@@ -110,6 +193,7 @@ def test_act_quant_passthrough_and_let_apply():
 @pytest.mark.parametrize("M,N,K,dt,ta,tb", [
     (200, 136, 328, "bf16", 0, 0), (128, 256, 64, "bf16", 0, 0), (2048, 4096, 4096, "bf16", 0, 0),
     (70, 50, 36, "f32", 0, 0), (2048, 12288, 4096, "bf16", 0, 0),
+    (4096, 8192, 512, "bf16", 0, 0), (256, 256, 4104, "bf16", 0, 0),
     (200, 136, 328, "bf16", 0, 1), (200, 136, 328, "bf16", 1, 0), (200, 136, 328, "bf16", 1, 1),
     (2048, 4096, 2048, "bf16", 1, 1), (2048, 4096, 11008, "bf16", 0, 1),
     (70, 50, 36, "f32", 1, 1)])
