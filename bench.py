@@ -49,6 +49,22 @@ def step_flops(c):
     return f
 
 
+def measured_traffic(workload):
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE scaled by the copy-kernel calibration), or None when
+    there is none for this workload or the GEMM source has changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gemm_traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, "post_quantization_amd", "csrc", "gemm.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("gemm_source_sha256") != sha:
+        return None
+    return rec["traffic_bytes_per_launch"]
+
+
 def cpu_baseline(c, inp, tokens):
     """The oracle (never tuned for speed) on a bounded sample of the workload:
     the same block with only `tokens` of the 2048 tokens, one full step
@@ -94,7 +110,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama7b_block_w4a4", choices=list(workloads()))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=256)
+    ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (known bytes) to calibrate the "
                          "FETCH_SIZE / WRITE_SIZE counters")
@@ -222,7 +238,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(args.workload),
             "launches": n_l,
             "avg_launch_us": round(avg_dur_s * 1e6, 2),
             "gemm_share_of_step": round(gemm_ms / (ms * args.steps), 4),
