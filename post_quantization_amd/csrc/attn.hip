@@ -1,0 +1,569 @@
+// Causal attention of the quantized block, fused on gfx950 (paper reading,
+// section "LET": the affinity Q~ K~^T with s_a folded into the quantized Q^ and K^
+// that arrive here; the softmax output is never quantized and stays float32 up to
+// its bf16 rounding as a matrix-core operand).
+//
+// Head dimension 128, causal mask, grouped K/V heads (query head h reads K/V head
+// h / grp).  Scores never reach HBM: the forward keeps a running max and sum per
+// query (exp2 domain) and writes O and the row's log-sum-exp; the backward
+// recomputes the scores from that log-sum-exp.
+//
+// MFMA 32x32x16 bf16 layouts.  A lane of the instruction supplies 8 consecutive k
+// of one row (A) or one column (B) and receives a column of C: col = lane & 31,
+// rows 8*(r/4) + 4*(lane/32) + (r%4), r = 0..15.  Every product here is arranged
+// so that the C tile of one step is the B operand of the next without moving data
+// between lanes: a C tile whose columns are indexed by lane is re-read as B with
+// its rows as k.  Those rows come in the order 16s + {0..3, 8..11} + 4*(lane/32)
+// within a 16-wide k slice s, so the A operand of that product is read from LDS in
+// the same order (transposed tiles below).
+#include "common.h"
+#include "kernels.h"
+
+namespace omq {
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+// native vectors (HIP's uint4 is a struct whose copies can keep a stack object alive)
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+
+constexpr int HD = 128;             // head dimension
+constexpr int kT = 256;             // threads per block (4 waves)
+
+OMQ_DEV f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row tile [R][128] bf16: the 16-byte chunk c (8 elements) of row r sits at chunk
+// c ^ (r & 7), so 8 lanes reading chunk c of 8 consecutive rows hit 8 bank groups.
+OMQ_DEV int rt_idx(int r, int c) { return r * HD + ((c ^ (r & 7)) << 3); }
+
+// Transposed tile [128][64] bf16 (64 positions per row): the 8-byte chunk q (4
+// positions) of row r sits at q ^ ((r & 15) ^ (r >> 4)); 16 lanes reading chunk q of
+// 16 consecutive rows, and the staging writes (rows 8c + j for c = 0..15), both
+// spread over 16 distinct chunks.
+OMQ_DEV int tt_idx(int r, int q) { return r * 64 + ((q ^ ((r & 15) ^ (r >> 4))) << 2); }
+
+// A-operand fragment of a row tile: row r, k slice s (16 wide), lane half h.
+OMQ_DEV bf16x8 rt_frag(const uint16_t* t, int r, int s, int h) {
+  return *reinterpret_cast<const bf16x8*>(&t[rt_idx(r, 2 * s + h)]);
+}
+
+// A-operand fragment of a transposed tile in C-row order: positions
+// 16s + 4h + {0..3} and 16s + 8 + 4h + {0..3} of row r.
+OMQ_DEV bf16x8 tt_frag(const uint16_t* t, int r, int s, int h) {
+  const u32x2 lo = *reinterpret_cast<const u32x2*>(&t[tt_idx(r, 4 * s + h)]);
+  const u32x2 hi = *reinterpret_cast<const u32x2*>(&t[tt_idx(r, 4 * s + 2 + h)]);
+  const u32x4 v = {lo.x, lo.y, hi.x, hi.y};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+OMQ_DEV uint32_t pack_bf16(float a, float b) {
+  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+// 8 consecutive C values r0..r0+7 of one tile as a B-operand fragment
+OMQ_DEV bf16x8 c_frag(const f32x16& c, int r0) {
+  const u32x4 v = {pack_bf16(c[r0 + 0], c[r0 + 1]), pack_bf16(c[r0 + 2], c[r0 + 3]),
+                   pack_bf16(c[r0 + 4], c[r0 + 5]), pack_bf16(c[r0 + 6], c[r0 + 7])};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// One thread's staging unit of a 64-row block of a [rows x ld] bf16 matrix: rows
+// 4kq .. 4kq+3 (kq = tid >> 4) at 16-byte column chunk c = tid & 15.  Rows past
+// `rows` are clamped to the last one (in bounds; the callers mask their results).
+struct Unit {
+  u32x4 v0, v1, v2, v3;     // rows 4kq + 0..3
+  OMQ_DEV void load(const uint16_t* P, int64_t ld, int64_t col0, int64_t row0, int64_t rows,
+                    int tid) {
+    const int kq = tid >> 4, c = tid & 15;
+    const int64_t r = row0 + 4 * kq;
+    const uint16_t* b = P + col0 + 8 * c;
+    v0 = *reinterpret_cast<const u32x4*>(b + min(r + 0, rows - 1) * ld);
+    v1 = *reinterpret_cast<const u32x4*>(b + min(r + 1, rows - 1) * ld);
+    v2 = *reinterpret_cast<const u32x4*>(b + min(r + 2, rows - 1) * ld);
+    v3 = *reinterpret_cast<const u32x4*>(b + min(r + 3, rows - 1) * ld);
+  }
+  OMQ_DEV void store_rows(uint16_t* t, int tid) const {
+    const int kq = tid >> 4, c = tid & 15;
+    *reinterpret_cast<u32x4*>(&t[rt_idx(4 * kq + 0, c)]) = v0;
+    *reinterpret_cast<u32x4*>(&t[rt_idx(4 * kq + 1, c)]) = v1;
+    *reinterpret_cast<u32x4*>(&t[rt_idx(4 * kq + 2, c)]) = v2;
+    *reinterpret_cast<u32x4*>(&t[rt_idx(4 * kq + 3, c)]) = v3;
+  }
+  // the same 4 x 8 block written transposed: 8 rows (columns 8c + j) of 4 positions
+  OMQ_DEV void store_transposed(uint16_t* t, int tid) const {
+    const int kq = tid >> 4, c = tid & 15;
+    tr2(t, 8 * c + 0, kq, v0.x, v1.x, v2.x, v3.x, 0x05040100u);
+    tr2(t, 8 * c + 1, kq, v0.x, v1.x, v2.x, v3.x, 0x07060302u);
+    tr2(t, 8 * c + 2, kq, v0.y, v1.y, v2.y, v3.y, 0x05040100u);
+    tr2(t, 8 * c + 3, kq, v0.y, v1.y, v2.y, v3.y, 0x07060302u);
+    tr2(t, 8 * c + 4, kq, v0.z, v1.z, v2.z, v3.z, 0x05040100u);
+    tr2(t, 8 * c + 5, kq, v0.z, v1.z, v2.z, v3.z, 0x07060302u);
+    tr2(t, 8 * c + 6, kq, v0.w, v1.w, v2.w, v3.w, 0x05040100u);
+    tr2(t, 8 * c + 7, kq, v0.w, v1.w, v2.w, v3.w, 0x07060302u);
+  }
+  // one bf16 of each of the 4 rows (low or high half of the words, per sel) as the
+  // 4 consecutive positions of transposed row r
+  static OMQ_DEV void tr2(uint16_t* t, int r, int kq, uint32_t a0, uint32_t a1, uint32_t a2,
+                          uint32_t a3, uint32_t sel) {
+    const u32x2 o = {__builtin_amdgcn_perm(a1, a0, sel), __builtin_amdgcn_perm(a3, a2, sel)};
+    *reinterpret_cast<u32x2*>(&t[tt_idx(r, kq)]) = o;
+  }
+};
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// ---------------------------------------------------------------------------
+// forward: block = (query head, 128 queries); wave w owns queries q0 + 32w + 0..31,
+// one per lane (both lane halves hold the same query).  Two passes over the keys
+// in 64-key blocks, S^T = K Q^T each time (A = K rows from LDS, B = Q from
+// registers):
+//   1. running max and sum of exp2 per query -> the log-sum-exp lse2;
+//   2. P = exp2(S c - lse2), already normalized, rounded to bf16 as the P V
+//      operand (the same rounding of the same normalized probabilities as a
+//      two-step softmax, and as the backward's recomputation), O^T += V^T P^T
+//      (A = V^T from LDS, B = P from registers).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kT) void k_flash_fwd(FlashFwd a) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * HD];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][HD * 64];
+  const int64_t T = a.T;
+  const int nqb = (int)((T + 127) / 128);
+  const int hq = blockIdx.x / nqb;
+  const int qb = nqb - 1 - (int)(blockIdx.x % nqb);       // longest rows first
+  const int hk = hq / a.grp;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int64_t q0 = (int64_t)qb * 128;
+  const int64_t q = q0 + 32 * w + l32;
+  const int64_t qc = min(q, T - 1);
+
+  bf16x8 qf[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    qf[s] = *reinterpret_cast<const bf16x8*>(a.Q + qc * a.ldq + hq * HD + 16 * s + 8 * h);
+
+  const int64_t kend = min(q0 + 128, T);
+  const int nkb = (int)((kend + 63) / 64);
+  // scaled, masked scores of key block kb for this lane's query
+  auto scores = [&](const uint16_t* Kb, int kb, f32x16 (&sc)[2]) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[kk][r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) sc[kk] = mfma(rt_frag(Kb, 32 * kk + l32, s, h), qf[s], sc[kk]);
+    }
+    const int64_t k0 = (int64_t)kb * 64;
+    const bool edge = k0 + 63 > q0 + 32 * w || k0 + 64 > T;   // wave-uniform
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float v = sc[kk][r] * a.scale2;
+        if (edge) {
+          const int64_t key = k0 + 32 * kk + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (key > q || key >= T) v = kNegInf;
+        }
+        sc[kk][r] = v;
+      }
+  };
+
+  // pass 1: log-sum-exp
+  Unit uk, uv;
+  uk.load(a.K, a.ldk, hk * HD, 0, T, tid);
+  uk.store_rows(Ks[0], tid);
+  if (nkb > 1) uk.load(a.K, a.ldk, hk * HD, 64, T, tid);
+  __syncthreads();
+  float m2 = kNegInf, l = 0.f;
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int buf = kb & 1;
+    f32x16 sc[2];
+    scores(Ks[buf], kb, sc);
+    if (kb + 1 < nkb) {
+      uk.store_rows(Ks[buf ^ 1], tid);
+      if (kb + 2 < nkb) uk.load(a.K, a.ldk, hk * HD, (int64_t)(kb + 2) * 64, T, tid);
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kk][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mn = fmaxf(m2, mx);
+    const float ms = mn == kNegInf ? 0.f : mn;
+    float add = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) add += exp2f(sc[kk][r] - ms);
+    l = l * exp2f(m2 - ms) + add;
+    m2 = mn;
+    __syncthreads();
+  }
+  l += __shfl_xor(l, 32, 64);
+  const float lse2 = m2 + log2f(l);
+
+  // pass 2: normalized probabilities into O^T += V^T P^T
+  uk.load(a.K, a.ldk, hk * HD, 0, T, tid);
+  uv.load(a.V, a.ldk, hk * HD, 0, T, tid);
+  uk.store_rows(Ks[0], tid);
+  uv.store_transposed(Vt[0], tid);
+  if (nkb > 1) {
+    uk.load(a.K, a.ldk, hk * HD, 64, T, tid);
+    uv.load(a.V, a.ldk, hk * HD, 64, T, tid);
+  }
+  __syncthreads();
+  f32x16 o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int buf = kb & 1;
+    f32x16 sc[2];
+    scores(Ks[buf], kb, sc);
+    if (kb + 1 < nkb) {
+      uk.store_rows(Ks[buf ^ 1], tid);
+      uv.store_transposed(Vt[buf ^ 1], tid);
+      if (kb + 2 < nkb) {
+        uk.load(a.K, a.ldk, hk * HD, (int64_t)(kb + 2) * 64, T, tid);
+        uv.load(a.V, a.ldk, hk * HD, (int64_t)(kb + 2) * 64, T, tid);
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[kk][r] = exp2f(sc[kk][r] - lse2);
+    bf16x8 pf[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) pf[s] = c_frag(sc[s >> 1], 8 * (s & 1));
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) o[hb] = mfma(tt_frag(Vt[buf], 32 * hb + l32, s, h), pf[s], o[hb]);
+    __syncthreads();
+  }
+  if (q < T) {
+    float* orow = a.O + q * a.ldo + hq * HD;
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(orow + 32 * hb + 8 * g + 4 * h) =
+            make_float4(o[hb][4 * g], o[hb][4 * g + 1], o[hb][4 * g + 2], o[hb][4 * g + 3]);
+    if (h == 0) a.lse2[(int64_t)hq * T + q] = lse2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// backward prologue: D = rowsum(dO * O) per (head, query) and dO in bf16
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kT) void k_attn_bwd_prep(const float* gO, const float* O, int64_t ld,
+                                                      int64_t T, int n_q, float* D, uint16_t* gOb,
+                                                      int64_t ldb) {
+  const int64_t q = blockIdx.x;
+  const int n4 = n_q * (HD / 4);
+  for (int base = 0; base < n4; base += kT) {
+    const int idx = base + threadIdx.x;        // n4 is a multiple of 32: whole half-waves
+    float dot = 0.f;
+    if (idx < n4) {
+      const float4 g = *reinterpret_cast<const float4*>(gO + q * ld + 4 * idx);
+      const float4 o = *reinterpret_cast<const float4*>(O + q * ld + 4 * idx);
+      dot = g.x * o.x + g.y * o.y + g.z * o.z + g.w * o.w;
+      *reinterpret_cast<uint2*>(gOb + q * ldb + 4 * idx) =
+          make_uint2(pack_bf16(g.x, g.y), pack_bf16(g.z, g.w));
+    }
+#pragma unroll
+    for (int off = 16; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
+    if (idx < n4 && (idx & 31) == 0) D[(int64_t)(idx >> 5) * T + q] = dot;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// backward, keys stationary: block = (K/V head, 128 keys); wave w owns keys
+// k0 + 32w + 0..31, one per lane.  Over every query head of the group and every
+// 64-query block at or after the keys: S = Q K^T and dP = dO V^T (A = Q / dO rows
+// from LDS, B = K / V from registers), P = exp2(S c - lse2), dS = P (dP - D) / sqrt(hd),
+// dV^T += dO^T P and dK^T += Q^T dS (A = transposed Q / dO from LDS, B = P / dS).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kT) void k_flash_bwd_dkdv(FlashBwd a) {
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][64 * HD];
+  __shared__ __attribute__((aligned(16))) uint16_t Gs[2][64 * HD];
+  __shared__ __attribute__((aligned(16))) uint16_t Qt[2][HD * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t Gt[2][HD * 64];
+  __shared__ __attribute__((aligned(16))) float Ls[2][64];
+  __shared__ __attribute__((aligned(16))) float Ds[2][64];
+  const int64_t T = a.T;
+  const int nkb = (int)((T + 127) / 128);
+  const int g = blockIdx.x / nkb;
+  const int kb = (int)(blockIdx.x % nkb);                 // longest (kb = 0) first
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int64_t k0 = (int64_t)kb * 128;
+  const int64_t key = k0 + 32 * w + l32;
+  const int64_t kc = min(key, T - 1);
+
+  bf16x8 kf[8], vf[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    kf[s] = *reinterpret_cast<const bf16x8*>(a.K + kc * a.ldk + g * HD + 16 * s + 8 * h);
+    vf[s] = *reinterpret_cast<const bf16x8*>(a.V + kc * a.ldk + g * HD + 16 * s + 8 * h);
+  }
+  const int nqb = (int)((T + 63) / 64);
+  const int qb0 = (int)(k0 / 64);
+  const int per = nqb - qb0;                              // query blocks per head
+  const int nit = per * a.grp;
+  auto qbase = [&](int it, int& hq) -> int64_t {
+    hq = g * a.grp + it / per;
+    return (int64_t)(qb0 + it % per) * 64;
+  };
+
+  Unit uq, ug;
+  float lv = 0.f, dv = 0.f;
+  auto load = [&](int it) {
+    int hq;
+    const int64_t q0 = qbase(it, hq);
+    uq.load(a.Q, a.ldq, hq * HD, q0, T, tid);
+    ug.load(a.dO, a.ldq, hq * HD, q0, T, tid);
+    if (tid < 64) {
+      const int64_t qq = min(q0 + tid, T - 1);
+      lv = a.lse2[(int64_t)hq * T + qq];
+      dv = a.D[(int64_t)hq * T + qq];
+    }
+  };
+  auto store = [&](int buf) {
+    uq.store_rows(Qs[buf], tid);
+    uq.store_transposed(Qt[buf], tid);
+    ug.store_rows(Gs[buf], tid);
+    ug.store_transposed(Gt[buf], tid);
+    if (tid < 64) {
+      Ls[buf][tid] = lv;
+      Ds[buf][tid] = dv;
+    }
+  };
+  if (nit > 0) {
+    load(0);
+    store(0);
+    if (nit > 1) load(1);
+  }
+  __syncthreads();
+
+  f32x16 dk[4], dvt[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[i][r] = 0.f;
+      dvt[i][r] = 0.f;
+    }
+  for (int it = 0; it < nit; ++it) {
+    const int buf = it & 1;
+    int hq;
+    const int64_t q0 = qbase(it, hq);
+    f32x16 sc[2], dp[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sc[mb][r] = 0.f;
+        dp[mb][r] = 0.f;
+      }
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        sc[mb] = mfma(rt_frag(Qs[buf], 32 * mb + l32, s, h), kf[s], sc[mb]);
+        dp[mb] = mfma(rt_frag(Gs[buf], 32 * mb + l32, s, h), vf[s], dp[mb]);
+      }
+    }
+    if (it + 1 < nit) {
+      store(buf ^ 1);
+      if (it + 2 < nit) load(it + 2);
+    }
+    const bool edge = q0 < k0 + 127 || q0 + 64 > T;        // block-uniform
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        const int row0 = 32 * mb + 8 * gg + 4 * h;
+        const float4 L4 = *reinterpret_cast<const float4*>(&Ls[buf][row0]);
+        const float4 D4 = *reinterpret_cast<const float4*>(&Ds[buf][row0]);
+        const float Lr[4] = {L4.x, L4.y, L4.z, L4.w};
+        const float Dr[4] = {D4.x, D4.y, D4.z, D4.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int r = 4 * gg + c;
+          float p = exp2f(sc[mb][r] * a.scale2 - Lr[c]);
+          if (edge) {
+            const int64_t qr = q0 + row0 + c;
+            if (key > qr || qr >= T) p = 0.f;
+          }
+          sc[mb][r] = p;
+          dp[mb][r] = p * (dp[mb][r] - Dr[c]) * a.scale;
+        }
+      }
+    bf16x8 pf[4], sf[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      pf[s] = c_frag(sc[s >> 1], 8 * (s & 1));
+      sf[s] = c_frag(dp[s >> 1], 8 * (s & 1));
+    }
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        dvt[hb] = mfma(tt_frag(Gt[buf], 32 * hb + l32, s, h), pf[s], dvt[hb]);
+        dk[hb] = mfma(tt_frag(Qt[buf], 32 * hb + l32, s, h), sf[s], dk[hb]);
+      }
+    __syncthreads();
+  }
+  if (key < T) {
+    float* krow = a.dK + key * a.lddk + g * HD;
+    float* vrow = a.dV + key * a.lddk + g * HD;
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        const int c = 32 * hb + 8 * gg + 4 * h;
+        *reinterpret_cast<float4*>(krow + c) =
+            make_float4(dk[hb][4 * gg], dk[hb][4 * gg + 1], dk[hb][4 * gg + 2], dk[hb][4 * gg + 3]);
+        *reinterpret_cast<float4*>(vrow + c) = make_float4(dvt[hb][4 * gg], dvt[hb][4 * gg + 1],
+                                                           dvt[hb][4 * gg + 2], dvt[hb][4 * gg + 3]);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// backward, queries stationary: block = (query head, 128 queries); per 64-key block
+// S^T = K Q^T and dP^T = V dO^T (A = K / V rows from LDS, B = Q / dO from
+// registers), dS^T as above, dQ^T += K^T dS^T (A = transposed K from LDS).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kT) void k_flash_bwd_dq(FlashBwd a) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * HD];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][64 * HD];
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][HD * 64];
+  const int64_t T = a.T;
+  const int nqb = (int)((T + 127) / 128);
+  const int hq = blockIdx.x / nqb;
+  const int qb = nqb - 1 - (int)(blockIdx.x % nqb);
+  const int hk = hq / a.grp;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int64_t q0 = (int64_t)qb * 128;
+  const int64_t q = q0 + 32 * w + l32;
+  const int64_t qc = min(q, T - 1);
+
+  bf16x8 qf[8], gf[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    qf[s] = *reinterpret_cast<const bf16x8*>(a.Q + qc * a.ldq + hq * HD + 16 * s + 8 * h);
+    gf[s] = *reinterpret_cast<const bf16x8*>(a.dO + qc * a.ldq + hq * HD + 16 * s + 8 * h);
+  }
+  const float lse = a.lse2[(int64_t)hq * T + qc];
+  const float Dq = a.D[(int64_t)hq * T + qc];
+
+  const int64_t kend = min(q0 + 128, T);
+  const int nkb = (int)((kend + 63) / 64);
+  Unit uk, uv;
+  uk.load(a.K, a.ldk, hk * HD, 0, T, tid);
+  uv.load(a.V, a.ldk, hk * HD, 0, T, tid);
+  uk.store_rows(Ks[0], tid);
+  uk.store_transposed(Kt[0], tid);
+  uv.store_rows(Vs[0], tid);
+  if (nkb > 1) {
+    uk.load(a.K, a.ldk, hk * HD, 64, T, tid);
+    uv.load(a.V, a.ldk, hk * HD, 64, T, tid);
+  }
+  __syncthreads();
+
+  f32x16 dq[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[i][r] = 0.f;
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int buf = kb & 1;
+    f32x16 sc[2], dp[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sc[kk][r] = 0.f;
+        dp[kk][r] = 0.f;
+      }
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        sc[kk] = mfma(rt_frag(Ks[buf], 32 * kk + l32, s, h), qf[s], sc[kk]);
+        dp[kk] = mfma(rt_frag(Vs[buf], 32 * kk + l32, s, h), gf[s], dp[kk]);
+      }
+    }
+    if (kb + 1 < nkb) {
+      uk.store_rows(Ks[buf ^ 1], tid);
+      uk.store_transposed(Kt[buf ^ 1], tid);
+      uv.store_rows(Vs[buf ^ 1], tid);
+      if (kb + 2 < nkb) {
+        uk.load(a.K, a.ldk, hk * HD, (int64_t)(kb + 2) * 64, T, tid);
+        uv.load(a.V, a.ldk, hk * HD, (int64_t)(kb + 2) * 64, T, tid);
+      }
+    }
+    const int64_t k0 = (int64_t)kb * 64;
+    const bool edge = k0 + 63 > q0 + 32 * w || k0 + 64 > T;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = exp2f(sc[kk][r] * a.scale2 - lse);
+        if (edge) {
+          const int64_t kr = k0 + 32 * kk + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (kr > q || kr >= T) p = 0.f;
+        }
+        dp[kk][r] = p * (dp[kk][r] - Dq) * a.scale;
+      }
+    bf16x8 sf[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) sf[s] = c_frag(dp[s >> 1], 8 * (s & 1));
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) dq[hb] = mfma(tt_frag(Kt[buf], 32 * hb + l32, s, h), sf[s], dq[hb]);
+    __syncthreads();
+  }
+  if (q < T) {
+    float* qrow = a.dQ + q * a.lddq + hq * HD;
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg)
+        *reinterpret_cast<float4*>(qrow + 32 * hb + 8 * gg + 4 * h) =
+            make_float4(dq[hb][4 * gg], dq[hb][4 * gg + 1], dq[hb][4 * gg + 2], dq[hb][4 * gg + 3]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_flash_fwd(const FlashFwd& a, hipStream_t st) {
+  if (a.T == 0 || a.n_q == 0) return hipSuccess;
+  const int nqb = (int)((a.T + 127) / 128);
+  hipLaunchKernelGGL(k_flash_fwd, dim3((unsigned)(nqb * a.n_q)), dim3(kT), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd_prep(const float* gO, const float* O, int64_t ld, int64_t T, int n_q,
+                                float* D, uint16_t* gOb, int64_t ldb, hipStream_t st) {
+  if (T == 0 || n_q == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_attn_bwd_prep, dim3((unsigned)T), dim3(kT), 0, st, gO, O, ld, T, n_q, D,
+                     gOb, ldb);
+  return hipGetLastError();
+}
+
+hipError_t launch_flash_bwd(const FlashBwd& a, hipStream_t st) {
+  if (a.T == 0 || a.n_q == 0) return hipSuccess;
+  const int nkb = (int)((a.T + 127) / 128);
+  hipLaunchKernelGGL(k_flash_bwd_dkdv, dim3((unsigned)(nkb * (a.n_q / a.grp))), dim3(kT), 0, st,
+                     a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_flash_bwd_dq, dim3((unsigned)(nkb * a.n_q)), dim3(kT), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace omq

@@ -88,12 +88,12 @@ struct Ws {
   Stats wq_qkv, wq_o, wq_gu, wq_d;
   float *Bt_qkv, *Bt_o, *Bt_gu;
   // forward activations
-  float *cos_t, *sin_t, *xn, *r1, *Yqkv, *Qr, *Kr, *S, *O, *h1, *r2, *xn2, *GU, *A, *y;
-  uint16_t *Xqkv, *Qh, *Kh, *Vh, *P, *Xo, *Xf, *Xd;
+  float *cos_t, *sin_t, *xn, *r1, *Yqkv, *Qr, *Kr, *O, *lse2, *h1, *r2, *xn2, *GU, *A, *y;
+  uint16_t *Xqkv, *Qh, *Kh, *Vh, *Xo, *Xf, *Xd;
   Stats a_qkv, a_q, a_k, a_v, a_o, a_f, a_d;
   // backward
-  float *dy, *gX, *gA, *gGU, *gxn2, *dh1, *gO, *gQh, *gKh, *gVh, *gQr, *gKr, *gY, *dP;
-  uint16_t *dyb, *gGUb, *dh1b, *gOb, *dS, *gYb;
+  float *dy, *gX, *gA, *gGU, *gxn2, *dh1, *gO, *Datt, *gQh, *gKh, *gVh, *gQr, *gKr, *gY;
+  uint16_t *dyb, *gGUb, *dh1b, *gOb, *gYb;
   float *cs, *gs_full, *gd_full, *gsa_full;
   float *rq, *csws, *msews;
   size_t total;
@@ -113,11 +113,10 @@ Ws layout(const Dims& m, void* base) {
     w.cos_t = b.take<float>(T * m.hd / 2); w.sin_t = b.take<float>(T * m.hd / 2);
     w.xn = b.take<float>(T * d); w.r1 = b.take<float>(T);
     w.Yqkv = b.take<float>(T * nqkv); w.Qr = b.take<float>(T * dq); w.Kr = b.take<float>(T * dk);
-    w.S = b.take<float>(m.nq * T * T); w.O = b.take<float>(T * dq);
+    w.O = b.take<float>(T * dq); w.lse2 = b.take<float>(m.nq * T);
     w.h1 = b.take<float>(T * d); w.r2 = b.take<float>(T); w.xn2 = b.take<float>(T * d);
     w.Xqkv = b.take<uint16_t>(T * d); w.Qh = b.take<uint16_t>(T * dq);
     w.Kh = b.take<uint16_t>(T * dk); w.Vh = b.take<uint16_t>(T * dk);
-    w.P = b.take<uint16_t>(m.nq * T * T);
     w.Xo = b.take<uint16_t>(T * dq);
     w.a_qkv = take_stats(b, T); w.a_q = take_stats(b, T); w.a_k = take_stats(b, T);
     w.a_v = take_stats(b, T); w.a_o = take_stats(b, T);
@@ -138,12 +137,11 @@ Ws layout(const Dims& m, void* base) {
     w.gxn2 = b.take<float>(T * d); w.dh1 = b.take<float>(T * d);
     w.dh1b = b.take<uint16_t>(T * d);
     w.gO = b.take<float>(T * dq); w.gOb = b.take<uint16_t>(T * dq);
+    w.Datt = b.take<float>(m.nq * T);
     w.gQh = b.take<float>(T * dq); w.gKh = b.take<float>(T * dk); w.gVh = b.take<float>(T * dk);
     w.gQr = b.take<float>(T * dq); w.gKr = b.take<float>(T * dk);
     w.gY = b.take<float>(T * nqkv);
     w.gYb = b.take<uint16_t>(T * nqkv);
-    w.dP = b.take<float>(m.nq * T * T);
-    w.dS = b.take<uint16_t>(m.nq * T * T);
     w.gs_full = b.take<float>(dq); w.gd_full = b.take<float>(dq); w.gsa_full = b.take<float>(dq);
   }
   w.cs = b.take<float>(std::max(nqkv, 2 * F));
@@ -169,7 +167,7 @@ int check(const omq_block_desc* b) {
   if (b->T <= 0 || b->d <= 0 || b->F <= 0) return OMQ_E_SHAPE;
   if (!b->ffn_only) {
     if (b->n_q <= 0 || b->n_kv <= 0 || b->head_dim <= 0 || b->n_q % b->n_kv) return OMQ_E_SHAPE;
-    if (b->head_dim % 8) return OMQ_E_ALIGN;
+    if (b->head_dim != 128) return OMQ_E_SHAPE;   // the fused attention kernels
   }
   if (b->T % 8 || b->d % 8 || b->F % 8) return OMQ_E_ALIGN;
   return OMQ_OK;
@@ -216,7 +214,6 @@ hipError_t run_gemm(const Gemm& g, hipStream_t st, omq_timer* tm) {
   if (rec && e == hipSuccess) {
     e = hipEventRecord(reinterpret_cast<hipEvent_t>(tm->events[2 * tm->count + 1]), st);
     double f = 2.0 * (double)g.M * (double)g.N * (double)g.K * (double)g.batch;
-    if (g.causal != CAUSAL_NONE) f *= 0.5;
     tm->flops += f;
     tm->count += 1;
   }
@@ -280,24 +277,14 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
           nullptr, ab, w.Kh, w.a_k, st));
     CK(aq(w.Yqkv + dq + dk, OMQ_F32, T, dk, nqkv, OMQ_LET_NONE, nullptr, nullptr, ab, w.Vh, w.a_v,
           st));
-    // causal attention, float32 softmax
+    // causal attention, float32 softmax, fused
     {
-      Gemm g;
-      g.A = w.Qh; g.lda = dq; g.strideA = m.hd;
-      g.B = w.Kh; g.ldb = dk; g.strideB = m.hd; g.b_group = m.grp;
-      g.C = w.S; g.ldc = T; g.strideC = T * T;
-      g.M = T; g.N = T; g.K = m.hd; g.batch = (int)m.nq;
-      g.alpha = 1.f / sqrtf((float)m.hd); g.causal = CAUSAL_SKIP_UPPER;
-      CK(run_gemm(g, st, tm));
-    }
-    CK(launch_softmax_causal(w.S, T, (int)m.nq, w.P, nullptr, st));
-    {
-      Gemm g;  // O = P V, V read K-major
-      g.A = w.P; g.lda = T; g.strideA = T * T;
-      g.B = w.Vh; g.ldb = dk; g.tb = 1; g.strideB = m.hd; g.b_group = m.grp;
-      g.C = w.O; g.ldc = dq; g.strideC = m.hd;
-      g.M = T; g.N = m.hd; g.K = T; g.batch = (int)m.nq; g.causal = CAUSAL_K_UPPER;
-      CK(run_gemm(g, st, tm));
+      FlashFwd f;
+      f.Q = w.Qh; f.K = w.Kh; f.V = w.Vh; f.ldq = dq; f.ldk = dk; f.T = T;
+      f.n_q = (int)m.nq; f.grp = (int)m.grp;
+      f.scale2 = (float)(1.4426950408889634 / sqrt((double)m.hd));
+      f.O = w.O; f.ldo = dq; f.lse2 = w.lse2;
+      CK(launch_flash_fwd(f, st));
     }
     // o_proj with its LET site, residual
     CK(aq(w.O, OMQ_F32, T, dq, dq, mode_let, s_o, d_o, ab, w.Xo, w.a_o, st));
@@ -498,39 +485,17 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
   }
   CK(launch_kv_reduce_add(w.gs_full, m.nq, m.nkv, m.hd, dth + t.s_o, st));
   CK(launch_kv_reduce_add(w.gd_full, m.nq, m.nkv, m.hd, dth + t.d_o, st));
-  // attention backward (softmax in float32, recomputed from S)
-  CK(launch_f32_to_bf16(w.gO, T, dq, dq, w.gOb, dq, nullptr, 0, st));
+  // attention backward (scores recomputed from the forward's log-sum-exp)
+  CK(launch_attn_bwd_prep(w.gO, w.O, dq, T, (int)m.nq, w.Datt, w.gOb, dq, st));
   {
-    Gemm g;  // dP = dO V^T
-    g.A = w.gOb; g.lda = dq; g.strideA = m.hd;
-    g.B = w.Vh; g.ldb = dk; g.strideB = m.hd; g.b_group = m.grp;
-    g.C = w.dP; g.ldc = T; g.strideC = T * T;
-    g.M = T; g.N = T; g.K = m.hd; g.batch = (int)m.nq; g.causal = CAUSAL_SKIP_UPPER;
-    CK(run_gemm(g, st, tm));
-  }
-  const float scale = 1.f / sqrtf((float)m.hd);
-  CK(launch_softmax_bwd_causal(w.S, w.dP, w.O, w.gO, T, (int)m.nq, m.hd, dq, scale, w.dS,
-                               nullptr, st));
-  {
-    Gemm g;  // dQ = dS K, K read K-major
-    g.A = w.dS; g.lda = T; g.strideA = T * T;
-    g.B = w.Kh; g.ldb = dk; g.tb = 1; g.strideB = m.hd; g.b_group = m.grp;
-    g.C = w.gQh; g.ldc = dq; g.strideC = m.hd;
-    g.M = T; g.N = m.hd; g.K = T; g.batch = (int)m.nq; g.causal = CAUSAL_K_UPPER;
-    CK(run_gemm(g, st, tm));
-  }
-  for (int r = 0; r < m.grp; ++r) {
-    Gemm g;  // dK_g = sum_h dS_h^T Q_h ;  dV_g = sum_h P_h^T dO_h  (all operands K-major)
-    g.A = w.dS + (int64_t)r * T * T; g.lda = T; g.ta = 1; g.strideA = (int64_t)m.grp * T * T;
-    g.B = w.Qh + (int64_t)r * m.hd; g.ldb = dq; g.tb = 1; g.strideB = (int64_t)m.grp * m.hd;
-    g.C = w.gKh; g.ldc = dk; g.strideC = m.hd;
-    g.M = T; g.N = m.hd; g.K = T; g.batch = (int)m.nkv; g.causal = CAUSAL_K_LOWER;
-    g.accumulate = r > 0;
-    CK(run_gemm(g, st, tm));
-    g.A = w.P + (int64_t)r * T * T;
-    g.B = w.gOb + (int64_t)r * m.hd; g.ldb = dq;
-    g.C = w.gVh;
-    CK(run_gemm(g, st, tm));
+    FlashBwd f;
+    f.Q = w.Qh; f.K = w.Kh; f.V = w.Vh; f.dO = w.gOb; f.ldq = dq; f.ldk = dk; f.T = T;
+    f.n_q = (int)m.nq; f.grp = (int)m.grp;
+    f.scale = (float)(1.0 / sqrt((double)m.hd));
+    f.scale2 = (float)(1.4426950408889634 / sqrt((double)m.hd));
+    f.lse2 = w.lse2; f.D = w.Datt;
+    f.dQ = w.gQh; f.lddq = dq; f.dK = w.gKh; f.dV = w.gVh; f.lddk = dk;
+    CK(launch_flash_bwd(f, st));
   }
   // Q~ / K~ / V quantizers and s_a
   const bool sa = m.use_sa;

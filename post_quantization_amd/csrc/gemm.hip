@@ -193,10 +193,7 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
   tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int bz = blockIdx.y;
-  if (g.causal == CAUSAL_SKIP_UPPER && n0 > m0 + BM - 1) return;
-  int64_t kb = 0, ke = g.K;
-  if (g.causal == CAUSAL_K_UPPER) ke = min(g.K, m0 + BM);
-  if (g.causal == CAUSAL_K_LOWER) kb = (m0 / BK) * BK;
+  const int64_t kb = 0, ke = g.K;
 
   const uint16_t* A = reinterpret_cast<const uint16_t*>(g.A) + bz * g.strideA;
   const uint16_t* B = reinterpret_cast<const uint16_t*>(g.B) + (bz / g.b_group) * g.strideB;
@@ -576,8 +573,8 @@ void launch_nn_dma(const Gemm& g, hipStream_t st) {
                      tiles_n);
 }
 
-// Direct LDS copies need whole tiles (no bounds checks), whole K steps (the causal
-// K ranges start and end on multiples of 64 when K does) and 16-byte aligned rows.
+// Direct LDS copies need whole tiles (no bounds checks), whole K steps and 16-byte
+// aligned rows.
 bool dma_fits(const Gemm& g, int BM, int BN) {
   auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
   return g.M % BM == 0 && g.N % BN == 0 && g.K % BK == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 &&
@@ -654,25 +651,6 @@ __global__ __launch_bounds__(256) void k_gemm_f32(Gemm g) {
     }
 }
 
-// 64 x 64 tile transposes through LDS
-__global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* in, int64_t rows,
-                                                        int64_t cols, int64_t ldi, uint16_t* out,
-                                                        int64_t ldo, int64_t sin, int64_t sout) {
-  __shared__ uint16_t t[64][66];
-  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
-  in += blockIdx.z * sin;
-  out += blockIdx.z * sout;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t r = r0 + i, c = c0 + tx;
-    t[i][tx] = (r < rows && c < cols) ? in[r * ldi + c] : (uint16_t)0;
-  }
-  __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t c = c0 + i, r = r0 + tx;
-    if (c < cols && r < rows) out[c * ldo + r] = t[tx][i];
-  }
-}
 
 __global__ __launch_bounds__(256) void k_f32_to_bf16(const float* in, int64_t rows, int64_t cols,
                                                      int64_t ldi, uint16_t* out, int64_t ldo,
@@ -725,16 +703,6 @@ hipError_t launch_gemm(const Gemm& g, hipStream_t st) {
     dim3 grid((unsigned)((g.N + 63) / 64), (unsigned)((g.M + 63) / 64), (unsigned)g.batch);
     hipLaunchKernelGGL(k_gemm_f32, grid, dim3(256), 0, st, g);
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, int64_t ldi,
-                                 uint16_t* out, int64_t ldo, int batch, int64_t stride_in,
-                                 int64_t stride_out, hipStream_t st) {
-  if (rows == 0 || cols == 0 || batch == 0) return hipSuccess;
-  dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64), (unsigned)batch);
-  hipLaunchKernelGGL(k_transpose_bf16, grid, dim3(256), 0, st, in, rows, cols, ldi, out, ldo,
-                     stride_in, stride_out);
   return hipGetLastError();
 }
 

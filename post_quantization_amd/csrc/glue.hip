@@ -1,6 +1,6 @@
 // Block glue around the quantized linears: RMSNorm, RoPE, SiLU gating, the MSE
 // objective (paper reading, section "框架": block output reconstruction), the
-// full-precision causal softmax and its backward, and the parameter updates
+// grouped-head broadcasts of the LET parameters, and the parameter updates
 // (section "实验证据": AdamW, zero weight decay).
 #include "common.h"
 #include "kernels.h"
@@ -162,63 +162,6 @@ __global__ __launch_bounds__(kThreads) void k_mse_final(const float* part, int n
   if (threadIdx.x == 0) *loss = s / (float)n;
 }
 
-// causal softmax of one row of S (scores already scaled); P is written for the
-// whole row (zeros right of the diagonal) in bf16.
-__global__ __launch_bounds__(kThreads) void k_softmax_causal(const float* S, int64_t T,
-                                                             uint16_t* P) {
-  const int64_t row = blockIdx.x;          // h * T + i
-  const int64_t i = row % T;
-  const float* s = S + row * T;
-  __shared__ float sh[4];
-  float mx = -FLT_MAX;
-  for (int64_t j = threadIdx.x; j <= i; j += kThreads) mx = fmaxf(mx, s[j]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
-  float sum = 0.f;
-  for (int64_t j = threadIdx.x; j <= i; j += kThreads) sum += expf(s[j] - mx);
-  sum = block_sum(sum, sh);
-  const float inv = 1.f / sum;
-  for (int64_t j = threadIdx.x; j < T; j += kThreads)
-    P[row * T + j] = j <= i ? f32_to_bf16(expf(s[j] - mx) * inv) : (uint16_t)0;
-}
-
-// dS = P * (dP - D) * scale, D = sum_d dO * O for this (head, row); P recomputed in
-// float32 from S.
-__global__ __launch_bounds__(kThreads) void k_softmax_bwd_causal(
-    const float* S, const float* dP, const float* O, const float* dO, int64_t T, int n_heads,
-    int64_t hd, int64_t ldo, float scale, uint16_t* dS) {
-  const int64_t row = blockIdx.x;
-  const int64_t i = row % T, h = row / T;
-  const float* s = S + row * T;
-  const float* dp = dP + row * T;
-  __shared__ float sh[4];
-  float dd = 0.f;
-  for (int64_t k = threadIdx.x; k < hd; k += kThreads)
-    dd = fmaf(dO[i * ldo + h * hd + k], O[i * ldo + h * hd + k], dd);
-  const float D = block_sum(dd, sh);
-  float mx = -FLT_MAX;
-  for (int64_t j = threadIdx.x; j <= i; j += kThreads) mx = fmaxf(mx, s[j]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
-  float sum = 0.f;
-  for (int64_t j = threadIdx.x; j <= i; j += kThreads) sum += expf(s[j] - mx);
-  sum = block_sum(sum, sh);
-  const float inv = 1.f / sum;
-  for (int64_t j = threadIdx.x; j < T; j += kThreads) {
-    float v = 0.f;
-    if (j <= i) v = expf(s[j] - mx) * inv * (dp[j] - D) * scale;
-    dS[row * T + j] = f32_to_bf16(v);
-  }
-}
-
 __global__ void k_kv_expand(const float* v, int64_t n_q, int64_t n_kv, int64_t hd, float* out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n_q * hd) return;
@@ -337,28 +280,6 @@ hipError_t launch_mse(const float* y, const float* target, int64_t n, float* los
   if (e != hipSuccess || !loss) return e;
   hipLaunchKernelGGL(k_mse_final, dim3(1), dim3(kThreads), 0, st, ws, nb, n, loss);
   return hipGetLastError();
-}
-
-hipError_t launch_softmax_causal(const float* S, int64_t T, int n_heads, uint16_t* P,
-                                 uint16_t* Pt, hipStream_t st) {
-  if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_softmax_causal, dim3((unsigned)(T * n_heads)), dim3(kThreads), 0, st, S, T,
-                     P);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !Pt) return e;
-  return launch_transpose_bf16(P, T, T, T, Pt, T, n_heads, T * T, T * T, st);
-}
-
-hipError_t launch_softmax_bwd_causal(const float* S, const float* dP, const float* O,
-                                     const float* dO, int64_t T, int n_heads, int64_t hd,
-                                     int64_t ldo, float scale, uint16_t* dS, uint16_t* dSt,
-                                     hipStream_t st) {
-  if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_softmax_bwd_causal, dim3((unsigned)(T * n_heads)), dim3(kThreads), 0, st,
-                     S, dP, O, dO, T, n_heads, hd, ldo, scale, dS);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !dSt) return e;
-  return launch_transpose_bf16(dS, T, T, T, dSt, T, n_heads, T * T, T * T, st);
 }
 
 hipError_t launch_kv_expand(const float* v, int64_t n_q, int64_t n_kv, int64_t hd, float* out,

@@ -66,7 +66,6 @@ hipError_t launch_bias_fold(const void* W, int w_dt, int64_t rows, int64_t cols,
 // ---------------------------------------------------------------------------
 // GEMM  C = alpha A B^T (+ bias) (+ C) ; A [M x K], B [N x K]
 // ---------------------------------------------------------------------------
-enum Causal { CAUSAL_NONE = 0, CAUSAL_SKIP_UPPER = 1, CAUSAL_K_UPPER = 2, CAUSAL_K_LOWER = 3 };
 
 // Straight-through backward fused into a GEMM epilogue (the GEMM's C is dL/dx_hat
 // for rows x cols of x).  Rows may come from up to 3 buffers (concatenated linears).
@@ -94,7 +93,6 @@ struct Gemm {
   int64_t M = 0, N = 0, K = 0;  int batch = 1;
   float alpha = 1.f;
   int accumulate = 0;
-  int causal = CAUSAL_NONE;
   int dt = 1;                                       // OMQ_BF16 or OMQ_F32 operands
   int ta = 0, tb = 0;                               // A is [K x M] / B is [K x N]
   SteEpi ste;                                       // bf16 only; mode 2 writes dL/dx into C
@@ -105,9 +103,6 @@ void gemm_ste_extents(int64_t rows, int64_t cols, int64_t* nslabs, int64_t* ntil
 
 // Transposes: out[c][r] = in[r][c]  (bf16 -> bf16, or float -> bf16 with an
 // optional straight bf16 copy written beside it).
-hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, int64_t ldi,
-                                 uint16_t* out, int64_t ldo, int batch, int64_t stride_in,
-                                 int64_t stride_out, hipStream_t st);
 hipError_t launch_f32_to_bf16(const float* in, int64_t rows, int64_t cols, int64_t ldi,
                               uint16_t* out, int64_t ldo, uint16_t* out_t, int64_t ldt,
                               hipStream_t st);
@@ -133,12 +128,36 @@ hipError_t launch_silu_gate_bwd(const float* gu, const float* ga, int64_t T, int
                                 float* ggu, hipStream_t st);
 hipError_t launch_mse(const float* y, const float* target, int64_t n, float* loss, float* dy,
                       float* ws, hipStream_t st);
-hipError_t launch_softmax_causal(const float* S, int64_t T, int n_heads, uint16_t* P,
-                                 uint16_t* Pt, hipStream_t st);
-hipError_t launch_softmax_bwd_causal(const float* S, const float* dP, const float* O,
-                                     const float* dO, int64_t T, int n_heads, int64_t hd,
-                                     int64_t ldo, float scale, uint16_t* dS, uint16_t* dSt,
-                                     hipStream_t st);
+// fused causal attention, head dimension 128 (csrc/attn.hip).  lse2 is the
+// per-(head, query) log-sum-exp of the scaled scores in the exp2 domain.
+struct FlashFwd {
+  const uint16_t* Q;        // [T x n_q*128] bf16, row stride ldq
+  const uint16_t* K;        // [T x n_kv*128] bf16, row stride ldk
+  const uint16_t* V;        // [T x n_kv*128] bf16, row stride ldk
+  int64_t ldq, ldk, T;
+  int n_q, grp;             // grp = n_q / n_kv
+  float scale2;             // log2(e) / sqrt(128)
+  float* O;                 // [T x n_q*128] fp32, row stride ldo
+  int64_t ldo;
+  float* lse2;              // [n_q x T]
+};
+struct FlashBwd {
+  const uint16_t *Q, *K, *V;
+  const uint16_t* dO;       // bf16, row stride ldq
+  int64_t ldq, ldk, T;
+  int n_q, grp;
+  float scale, scale2;      // 1 / sqrt(128) and log2(e) / sqrt(128)
+  const float* lse2;        // from the forward
+  const float* D;           // [n_q x T] rowsum(dO * O)
+  float* dQ;                // [T x n_q*128] fp32, row stride lddq
+  int64_t lddq;
+  float *dK, *dV;           // [T x n_kv*128] fp32, row stride lddk
+  int64_t lddk;
+};
+hipError_t launch_flash_fwd(const FlashFwd& a, hipStream_t st);
+hipError_t launch_attn_bwd_prep(const float* gO, const float* O, int64_t ld, int64_t T, int n_q,
+                                float* D, uint16_t* gOb, int64_t ldb, hipStream_t st);
+hipError_t launch_flash_bwd(const FlashBwd& a, hipStream_t st);
 hipError_t launch_axpy_bcast(float* y, const float* x, int64_t n, hipStream_t st);
 hipError_t launch_kv_expand(const float* v, int64_t n_q, int64_t n_kv, int64_t hd, float* out,
                             hipStream_t st);

@@ -79,6 +79,10 @@ def test_validation_before_launch():
     assert L.omq_qlinear_fwd(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, 64, None) == -5
     b = omq.BlockDesc(T=64, d=64, n_q=3, n_kv=2, head_dim=16, F=64, wbits=4, abits=4)
     assert omq.block_workspace_size(b) == 0            # n_q not a multiple of n_kv
+    b = omq.BlockDesc(T=64, d=256, n_q=4, n_kv=4, head_dim=64, F=64, wbits=4, abits=4)
+    assert omq.block_workspace_size(b) == 0            # the attention kernels take head_dim 128
+    b = omq.BlockDesc(T=64, d=256, n_q=2, n_kv=2, head_dim=128, F=64, wbits=4, abits=4)
+    assert omq.block_workspace_size(b) > 0
     b = omq.BlockDesc(T=64, d=64, n_q=4, n_kv=2, head_dim=16, F=64, wbits=4, abits=4,
                       optimizer=5)
     assert L.omq_block_step(ctypes.byref(b), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None,
