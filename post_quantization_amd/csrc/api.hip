@@ -312,11 +312,12 @@ int omq_qlinear_bwd(const omq_qlinear_desc* d, const void* X, const void* W, con
   float* g_s = d->use_let ? dtheta + 2 * co : nullptr;
   float* g_d = d->use_let ? dtheta + 2 * co + ci : nullptr;
   // dW = dY^T X_hat and dX_hat = dY W_hat, with dY^T, X_hat and W_hat read K-major
-  if (dl) OMQ_HIP_CHECK(launch_colsum(dY, T, co, co, w.colsum, w.cs, st));
+  if (dl && !bf) OMQ_HIP_CHECK(launch_colsum(dY, T, co, co, w.colsum, w.cs, st));
   if (d->wbits >= 16) OMQ_HIP_CHECK(hipMemsetAsync(dtheta, 0, 2 * co * sizeof(float), st));
   if (bf) {
-    // bf16 path: both straight-through passes run in the GEMM epilogues
-    OMQ_HIP_CHECK(launch_f32_to_bf16(dY, T, co, co, w.dYb, co, nullptr, 0, st));
+    // bf16 path: dY's bf16 copy and column sums in one pass; both straight-through
+    // passes run in the GEMM epilogues
+    OMQ_HIP_CHECK(launch_cvt_bf16_colsum(dY, T, co, w.dYb, dl ? w.colsum : nullptr, w.cs, st));
     int64_t nsl, ntl;
     if (d->wbits < 16 || s) {
       gemm_ste_extents(co, ci, &nsl, &ntl);

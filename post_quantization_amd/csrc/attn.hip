@@ -36,9 +36,12 @@ OMQ_DEV f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Row tile [R][128] bf16: the 16-byte chunk c (8 elements) of row r sits at chunk
-// c ^ (r & 7), so 8 lanes reading chunk c of 8 consecutive rows hit 8 bank groups.
-OMQ_DEV int rt_idx(int r, int c) { return r * HD + ((c ^ (r & 7)) << 3); }
+// Row tile [R][128] bf16 with rows padded to 136 elements (272 bytes): 8 lanes
+// reading the same 16-byte chunk of 8 consecutive rows land 16 bytes apart modulo
+// 128, i.e. in 8 distinct bank groups, and a fragment's address is the row base
+// plus an immediate offset.
+constexpr int RS = HD + 8;
+OMQ_DEV int rt_idx(int r, int c) { return r * RS + (c << 3); }
 
 // Transposed tile [128][64] bf16 (64 positions per row): the 8-byte chunk q (4
 // positions) of row r sits at q ^ ((r & 15) ^ (r >> 4)); 16 lanes reading chunk q of
@@ -58,10 +61,6 @@ OMQ_DEV bf16x8 tt_frag(const uint16_t* t, int r, int s, int h) {
   const u32x2 hi = *reinterpret_cast<const u32x2*>(&t[tt_idx(r, 4 * s + 2 + h)]);
   const u32x4 v = {lo.x, lo.y, hi.x, hi.y};
   return __builtin_bit_cast(bf16x8, v);
-}
-
-OMQ_DEV uint32_t pack_bf16(float a, float b) {
-  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
 }
 
 // 8 consecutive C values r0..r0+7 of one tile as a B-operand fragment
@@ -116,6 +115,10 @@ struct Unit {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
+// 2^x on the transcendental unit (no denormal rescaling: results below 2^-126 are
+// probabilities that vanish against the row sum anyway)
+OMQ_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // ---------------------------------------------------------------------------
 // forward: block = (query head, 128 queries); wave w owns queries q0 + 32w + 0..31,
 // one per lane (both lane halves hold the same query).  Two passes over the keys
@@ -128,7 +131,7 @@ constexpr float kNegInf = -__builtin_huge_valf();
 //      (A = V^T from LDS, B = P from registers).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kT) void k_flash_fwd(FlashFwd a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * HD];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * RS];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[2][HD * 64];
   const int64_t T = a.T;
   const int nqb = (int)((T + 127) / 128);
@@ -198,8 +201,8 @@ __global__ __launch_bounds__(kT) void k_flash_fwd(FlashFwd a) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) add += exp2f(sc[kk][r] - ms);
-    l = l * exp2f(m2 - ms) + add;
+      for (int r = 0; r < 16; ++r) add += fast_exp2(sc[kk][r] - ms);
+    l = l * fast_exp2(m2 - ms) + add;
     m2 = mn;
     __syncthreads();
   }
@@ -236,7 +239,7 @@ __global__ __launch_bounds__(kT) void k_flash_fwd(FlashFwd a) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sc[kk][r] = exp2f(sc[kk][r] - lse2);
+      for (int r = 0; r < 16; ++r) sc[kk][r] = fast_exp2(sc[kk][r] - lse2);
     bf16x8 pf[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) pf[s] = c_frag(sc[s >> 1], 8 * (s & 1));
@@ -290,8 +293,8 @@ __global__ __launch_bounds__(kT) void k_attn_bwd_prep(const float* gO, const flo
 // dV^T += dO^T P and dK^T += Q^T dS (A = transposed Q / dO from LDS, B = P / dS).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kT) void k_flash_bwd_dkdv(FlashBwd a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][64 * HD];
-  __shared__ __attribute__((aligned(16))) uint16_t Gs[2][64 * HD];
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][64 * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t Gs[2][64 * RS];
   __shared__ __attribute__((aligned(16))) uint16_t Qt[2][HD * 64];
   __shared__ __attribute__((aligned(16))) uint16_t Gt[2][HD * 64];
   __shared__ __attribute__((aligned(16))) float Ls[2][64];
@@ -393,7 +396,7 @@ __global__ __launch_bounds__(kT) void k_flash_bwd_dkdv(FlashBwd a) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int r = 4 * gg + c;
-          float p = exp2f(sc[mb][r] * a.scale2 - Lr[c]);
+          float p = fast_exp2(sc[mb][r] * a.scale2 - Lr[c]);
           if (edge) {
             const int64_t qr = q0 + row0 + c;
             if (key > qr || qr >= T) p = 0.f;
@@ -439,8 +442,8 @@ __global__ __launch_bounds__(kT) void k_flash_bwd_dkdv(FlashBwd a) {
 // registers), dS^T as above, dQ^T += K^T dS^T (A = transposed K from LDS).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kT) void k_flash_bwd_dq(FlashBwd a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * HD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][64 * HD];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][64 * RS];
   __shared__ __attribute__((aligned(16))) uint16_t Kt[2][HD * 64];
   const int64_t T = a.T;
   const int nqb = (int)((T + 127) / 128);
@@ -511,7 +514,7 @@ __global__ __launch_bounds__(kT) void k_flash_bwd_dq(FlashBwd a) {
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = exp2f(sc[kk][r] * a.scale2 - lse);
+        float p = fast_exp2(sc[kk][r] * a.scale2 - lse);
         if (edge) {
           const int64_t kr = k0 + 32 * kk + 8 * (r >> 2) + 4 * h + (r & 3);
           if (kr > q || kr >= T) p = 0.f;

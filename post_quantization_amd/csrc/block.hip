@@ -370,8 +370,9 @@ hipError_t lin_bwd_fused(const Ws& w, const LinBwd& L, int64_t T, int wbits, int
                          omq_timer* tm) {
   hipError_t e;
   const int64_t N = L.N, K = L.K;
-  if ((e = launch_f32_to_bf16(L.gY, T, N, N, L.gYb, N, nullptr, 0, st)) != hipSuccess) return e;
-  if (L.fold && (e = launch_colsum(L.gY, T, N, N, w.cs, w.csws, st)) != hipSuccess) return e;
+  if ((e = launch_cvt_bf16_colsum(L.gY, T, N, L.gYb, L.fold ? w.cs : nullptr, w.csws, st)) !=
+      hipSuccess)
+    return e;
   int64_t nsl, ntl;
   // weight side (skipped when no learnable parameter depends on these weights)
   if (wbits < 16 || L.s_w) {

@@ -21,14 +21,15 @@ constexpr int kWave = 64;
 
 OMQ_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// float32 -> bf16, round to nearest even; NaN stays NaN.
-OMQ_DEV uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u)
-    return (u & 0x007fffffu) ? (uint16_t)((u >> 16) | 0x40u) : (uint16_t)(u >> 16);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// float32 -> bf16, round to nearest even (the gfx950 conversion instruction;
+// NaN stays NaN).  Two at a time: a in the low half, b in the high half.
+typedef __attribute__((ext_vector_type(2))) float omq_f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 omq_bf16x2;
+OMQ_DEV uint32_t pack_bf16(float a, float b) {
+  const omq_f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, omq_bf16x2));
 }
+OMQ_DEV uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 // Four consecutive elements of a float32 or bf16 row, widened to float32.
 OMQ_DEV void load4(const void* base, int dt, int64_t idx, float v[4]) {
@@ -50,8 +51,8 @@ OMQ_DEV void store4(void* base, int dt, int64_t idx, const float v[4]) {
         make_float4(v[0], v[1], v[2], v[3]);
   } else {
     uint2 t;
-    t.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-    t.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    t.x = pack_bf16(v[0], v[1]);
+    t.y = pack_bf16(v[2], v[3]);
     *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(base) + idx) = t;
   }
 }

@@ -652,29 +652,6 @@ __global__ __launch_bounds__(256) void k_gemm_f32(Gemm g) {
 }
 
 
-__global__ __launch_bounds__(256) void k_f32_to_bf16(const float* in, int64_t rows, int64_t cols,
-                                                     int64_t ldi, uint16_t* out, int64_t ldo,
-                                                     uint16_t* out_t, int64_t ldt) {
-  __shared__ uint16_t t[64][66];
-  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t r = r0 + i, c = c0 + tx;
-    uint16_t b = 0;
-    if (r < rows && c < cols) {
-      b = f32_to_bf16(in[r * ldi + c]);
-      if (out) out[r * ldo + c] = b;
-    }
-    t[i][tx] = b;
-  }
-  if (!out_t) return;
-  __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t c = c0 + i, r = r0 + tx;
-    if (c < cols && r < rows) out_t[c * ldt + r] = t[tx][i];
-  }
-}
-
 }  // namespace
 
 void gemm_ste_extents(int64_t rows, int64_t cols, int64_t* nslabs, int64_t* ntiles) {
@@ -703,16 +680,6 @@ hipError_t launch_gemm(const Gemm& g, hipStream_t st) {
     dim3 grid((unsigned)((g.N + 63) / 64), (unsigned)((g.M + 63) / 64), (unsigned)g.batch);
     hipLaunchKernelGGL(k_gemm_f32, grid, dim3(256), 0, st, g);
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_f32_to_bf16(const float* in, int64_t rows, int64_t cols, int64_t ldi,
-                              uint16_t* out, int64_t ldo, uint16_t* out_t, int64_t ldt,
-                              hipStream_t st) {
-  if (rows == 0 || cols == 0) return hipSuccess;
-  dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
-  hipLaunchKernelGGL(k_f32_to_bf16, grid, dim3(256), 0, st, in, rows, cols, ldi, out, ldo, out_t,
-                     ldt);
   return hipGetLastError();
 }
 

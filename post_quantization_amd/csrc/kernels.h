@@ -103,9 +103,10 @@ void gemm_ste_extents(int64_t rows, int64_t cols, int64_t* nslabs, int64_t* ntil
 
 // Transposes: out[c][r] = in[r][c]  (bf16 -> bf16, or float -> bf16 with an
 // optional straight bf16 copy written beside it).
-hipError_t launch_f32_to_bf16(const float* in, int64_t rows, int64_t cols, int64_t ldi,
-                              uint16_t* out, int64_t ldo, uint16_t* out_t, int64_t ldt,
-                              hipStream_t st);
+// dY (float32, contiguous rows) -> bf16 copy, plus its column sums when colsum is
+// set (ws: colsum_ws_bytes(rows, cols))
+hipError_t launch_cvt_bf16_colsum(const float* in, int64_t rows, int64_t cols, uint16_t* out,
+                                  float* colsum, float* ws, hipStream_t st);
 // out[c] = sum_r in[r][c]   (deterministic two-stage)
 hipError_t launch_colsum(const float* in, int64_t rows, int64_t cols, int64_t ld, float* out,
                          float* ws, hipStream_t st);

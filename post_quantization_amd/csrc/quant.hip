@@ -592,6 +592,41 @@ __global__ __launch_bounds__(kThreads) void k_colsum_part(const float* in, int64
   part[(int64_t)blockIdx.y * cols + c] = s;
 }
 
+// dY in float32 -> its bf16 copy (the matrix-core operand) and, when `part` is
+// set, the column sums of each kColsumRows-row chunk, in one pass over dY.
+// VEC: 8 consecutive columns per thread (cols % 8 == 0), else one.
+template <int VEC>
+__global__ __launch_bounds__(kThreads) void k_cvt_bf16_colpart(const float* in, int64_t rows,
+                                                               int64_t cols, uint16_t* out,
+                                                               float* part) {
+  const int64_t c = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * VEC;
+  if (c >= cols) return;
+  const int64_t r0 = (int64_t)blockIdx.y * kColsumRows;
+  const int64_t r1 = min(r0 + kColsumRows, rows);
+  float s[VEC];
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) s[j] = 0.f;
+  for (int64_t r = r0; r < r1; ++r) {
+    const float* p = in + r * cols + c;
+    if constexpr (VEC == 8) {
+      const float4 a = *reinterpret_cast<const float4*>(p);
+      const float4 b = *reinterpret_cast<const float4*>(p + 4);
+      s[0] += a.x; s[1] += a.y; s[2] += a.z; s[3] += a.w;
+      s[4] += b.x; s[5] += b.y; s[6] += b.z; s[7] += b.w;
+      *reinterpret_cast<uint4*>(out + r * cols + c) =
+          make_uint4(pack_bf16(a.x, a.y), pack_bf16(a.z, a.w), pack_bf16(b.x, b.y),
+                     pack_bf16(b.z, b.w));
+    } else {
+      s[0] += p[0];
+      out[r * cols + c] = f32_to_bf16(p[0]);
+    }
+  }
+  if (part) {
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) part[(int64_t)blockIdx.y * cols + c + j] = s[j];
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void k_colsum_final(const float* part, int nparts,
                                                            int64_t cols, float* out) {
   const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -749,6 +784,28 @@ hipError_t launch_bias_fold(const void* W, int w_dt, int64_t rows, int64_t cols,
 
 size_t colsum_ws_bytes(int64_t rows, int64_t cols) {
   return (size_t)(((rows + kColsumRows - 1) / kColsumRows) * cols) * sizeof(float) + 256;
+}
+
+hipError_t launch_cvt_bf16_colsum(const float* in, int64_t rows, int64_t cols, uint16_t* out,
+                                  float* colsum, float* ws, hipStream_t st) {
+  if (cols == 0) return hipSuccess;
+  const int64_t np = (rows + kColsumRows - 1) / kColsumRows;
+  if (np == 0) return colsum ? hipMemsetAsync(colsum, 0, cols * sizeof(float), st) : hipSuccess;
+  float* part = colsum ? ws : nullptr;
+  if (cols % 8 == 0) {
+    const unsigned cb = (unsigned)((cols / 8 + kThreads - 1) / kThreads);
+    hipLaunchKernelGGL(k_cvt_bf16_colpart<8>, dim3(cb, (unsigned)np), dim3(kThreads), 0, st, in,
+                       rows, cols, out, part);
+  } else {
+    const unsigned cb = (unsigned)((cols + kThreads - 1) / kThreads);
+    hipLaunchKernelGGL(k_cvt_bf16_colpart<1>, dim3(cb, (unsigned)np), dim3(kThreads), 0, st, in,
+                       rows, cols, out, part);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !colsum) return e;
+  hipLaunchKernelGGL(k_colsum_final, dim3((unsigned)((cols + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, st, ws, (int)np, cols, colsum);
+  return hipGetLastError();
 }
 
 hipError_t launch_colsum(const float* in, int64_t rows, int64_t cols, int64_t ld, float* out,
