@@ -167,13 +167,24 @@ def uses_sa(c):
     return (not c.ffn_only) and c.abits < 16
 
 
+def lwc_rows(c, shape):
+    """Quantizer rows of one weight [C_out, C_in]: one per output channel, or one
+    per group of c.group input channels (group-wise LWC)."""
+    C_out, C_in = shape
+    if c.group:
+        assert C_in % c.group == 0, (C_in, c.group)
+        return C_out * (C_in // c.group)
+    return C_out
+
+
 def theta_layout(c, shapes):
-    """Packed order: per linear a_gamma[C_out], a_beta[C_out]; per LET site
+    """Packed order: per linear a_gamma[rows], a_beta[rows] (rows = C_out, or
+    C_out * C_in / group output-channel major for group-wise LWC); per LET site
     s[C], delta[C]; then s_a[C_k].  Returns [(name, size)]."""
     out = []
     for n in linears(c):
-        out.append(("a_gamma_" + n, shapes[n][0]))
-        out.append(("a_beta_" + n, shapes[n][0]))
+        out.append(("a_gamma_" + n, lwc_rows(c, shapes[n])))
+        out.append(("a_beta_" + n, lwc_rows(c, shapes[n])))
     kvd = c.n_kv * c.head_dim
     site_dim = {"qkv": c.d, "o": kvd, "ffn": c.d}
     for s in let_sites(c):
@@ -221,8 +232,10 @@ def _qlin(ops, S, name, Xop, W, th, c, s=None, delta=None):
         wst = None
         Wop = ops.operand(Wt)
     else:
-        wst = ops.quant(Wt, gamma, beta, c.wbits, "w_" + name)
-        Wop = ops.operand(wst.xhat)
+        # one quantizer row per output channel, or per group of input channels
+        rows = lwc_rows(c, Wt.shape)
+        wst = ops.quant(np.reshape(Wt, (rows, -1)), gamma, beta, c.wbits, "w_" + name)
+        Wop = ops.operand(np.reshape(wst.xhat, Wt.shape))
     Y = Xop @ Wop.T
     if delta is not None:
         Y = Y + quant.bias_fold(W, None, delta)[None, :]
@@ -333,9 +346,12 @@ def _qlin_bwd(S, name, gY, Xop, g, gs=None):
     gXop = gY @ L.Wop
     gWop = gY.T @ Xop
     if L.wst is None:
-        gWt, g_gamma, g_beta = gWop, np.zeros(gWop.shape[0]), np.zeros(gWop.shape[0])
+        rows = lwc_rows(S.c, gWop.shape)
+        gWt, g_gamma, g_beta = gWop, np.zeros(rows), np.zeros(rows)
     else:
-        gWt, g_gamma, g_beta = quant.quantize_rows_bwd(gWop, L.wst)
+        gWt, g_gamma, g_beta = quant.quantize_rows_bwd(np.reshape(gWop, (L.wst.h.size, -1)),
+                                                       L.wst)
+        gWt = np.reshape(gWt, gWop.shape)
     ga, gb = L.gamma.astype(F64), L.beta.astype(F64)
     g["a_gamma_" + name] = g_gamma * ga * (1.0 - ga)
     g["a_beta_" + name] = g_beta * gb * (1.0 - gb)

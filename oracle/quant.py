@@ -166,11 +166,38 @@ def bias_fold(W, B, delta) -> np.ndarray:
     return out
 
 
-def lwc_fakequant(W, a_gamma, a_beta, nbits, s=None, delta=None, B=None):
-    """The weight side of one linear layer: LET on W, LWC, bias fold."""
+def group_rows(Wt, group):
+    """[C_out, C_in] -> [C_out * C_in / group, group]: each output channel split into
+    groups of `group` consecutive input channels, one quantizer row per group
+    (group-wise LWC: clipping strengths, step and zero point per group)."""
+    Wt = np.asarray(Wt)
+    C_out, C_in = Wt.shape
+    assert C_in % group == 0, (C_in, group)
+    return Wt.reshape(C_out * (C_in // group), group)
+
+
+def lwc_fakequant(W, a_gamma, a_beta, nbits, s=None, delta=None, B=None, group=None):
+    """The weight side of one linear layer: LET on W, LWC, bias fold.
+
+    group: None (or C_in) quantizes each output channel as one row; otherwise each
+    run of `group` input channels of an output channel is its own row, with its
+    own logits: a_gamma / a_beta are [C_out * C_in / group], output-channel major.
+    Codes and W_hat keep the [C_out, C_in] shape; h, z and st are per group."""
     Wt = let_weight(W, s) if s is not None else np.asarray(W, dtype=F32)
-    st = quantize_rows(Wt, sigmoid32(a_gamma), sigmoid32(a_beta), nbits)
+    C_out, C_in = Wt.shape
+    g = C_in if group is None else int(group)
+    st = quantize_rows(group_rows(Wt, g), sigmoid32(a_gamma), sigmoid32(a_beta), nbits)
     Bt = bias_fold(W, B, delta) if delta is not None else (
         np.zeros(W.shape[0]) if B is None else np.asarray(B, dtype=F64))
-    return SimpleNamespace(Wt=Wt, st=st, W_hat=st.xhat, codes=st.codes, h=st.h, z=st.z,
-                           B_tilde=Bt)
+    return SimpleNamespace(Wt=Wt, st=st, W_hat=st.xhat.reshape(C_out, C_in),
+                           codes=st.codes.reshape(C_out, C_in), h=st.h, z=st.z,
+                           B_tilde=Bt, group=g)
+
+
+def lwc_bwd(g_What, ref):
+    """Straight-through backward of ``lwc_fakequant`` (result ``ref``) for the
+    upstream gradient w.r.t. W_hat: returns (dL/dW~ [C_out, C_in], dL/dgamma,
+    dL/dbeta), the last two per quantizer row (output channel or group)."""
+    g_What = np.asarray(g_What, F64)
+    gx, gg, gb = quantize_rows_bwd(group_rows(g_What, ref.group), ref.st)
+    return gx.reshape(g_What.shape), gg, gb

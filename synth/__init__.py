@@ -116,6 +116,7 @@ class BlockCfg:
     lr_let: float = 1e-2
     rope_theta: float = 10000.0
     eps: float = 1e-6
+    group: int = 0             # LWC group size along C_in; 0: one group per output channel
 
 
 LINEAR_CFG1 = LinearCfg(cfg=1, T=16, c_in=64, c_out=32, wbits=4, abits=16, let=False,
@@ -130,6 +131,10 @@ BLOCK_CFG4 = BlockCfg(cfg=4, T=2048, d=4096, n_q=32, n_kv=32, F=11008, wbits=4, 
 BLOCK_CFG5_W4 = BlockCfg(cfg=5, T=2048, d=8192, n_q=64, n_kv=8, F=28672, wbits=4, abits=16,
                          n_out=82)
 BLOCK_CFG5_W2 = replace(BLOCK_CFG5_W4, wbits=2)
+# group-wise LWC (128 input channels per clipping group), weight-only: the pages'
+# headline W3A16g128 / W2A16g128 settings on the 7B-shaped block
+BLOCK_CFG4_W3G128 = replace(BLOCK_CFG4, wbits=3, abits=16, group=128)
+BLOCK_CFG4_W2G128 = replace(BLOCK_CFG4, wbits=2, abits=16, group=128)
 
 
 def linear_inputs(c: LinearCfg) -> Dict[str, np.ndarray]:

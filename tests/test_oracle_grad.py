@@ -94,19 +94,23 @@ def test_linear_fd(abits, let):
     _fd(L, th64, g, names, rng, n=6)
 
 
-def _tiny_block(ffn_only=False, n_q=4, n_kv=2, wbits=4, abits=4):
+def _tiny_block(ffn_only=False, n_q=4, n_kv=2, wbits=4, abits=4, group=0):
     return synth.BlockCfg(cfg=4, T=7, d=16, n_q=n_q, n_kv=n_kv, F=24, wbits=wbits,
                           abits=abits, head_dim=8, ffn_only=ffn_only, n_out=2,
-                          out_lo=5.0, out_hi=10.0)
+                          out_lo=5.0, out_hi=10.0, group=group)
 
 
-@pytest.mark.parametrize("kind", ["mha_w4a4", "gqa_w4a4", "gqa_w4a16", "ffn_w3a16", "mha_w16a4"])
+@pytest.mark.parametrize("kind", ["mha_w4a4", "gqa_w4a4", "gqa_w4a16", "ffn_w3a16", "mha_w16a4",
+                                  "mha_w4a4_g8", "ffn_w3a16_g8"])
 def test_block_fd(kind):
     c = {"mha_w4a4": _tiny_block(n_q=2, n_kv=2),
          "gqa_w4a4": _tiny_block(n_q=4, n_kv=2),
          "gqa_w4a16": _tiny_block(n_q=4, n_kv=2, abits=16),
          "ffn_w3a16": _tiny_block(ffn_only=True, wbits=3, abits=16),
-         "mha_w16a4": _tiny_block(n_q=2, n_kv=2, wbits=16, abits=4)}[kind]
+         "mha_w16a4": _tiny_block(n_q=2, n_kv=2, wbits=16, abits=4),
+         # group-wise LWC: 8 input channels per clipping group
+         "mha_w4a4_g8": _tiny_block(n_q=2, n_kv=2, group=8),
+         "ffn_w3a16_g8": _tiny_block(ffn_only=True, wbits=3, abits=16, group=8)}[kind]
     rng = np.random.default_rng(5)
     inp = synth.block_inputs(c)
     # larger weights than N(0, 0.02^2) so the tiny block is far from linear

@@ -186,3 +186,59 @@ def test_let_identity_linear():
     Y = X.astype(np.float64) @ W.astype(np.float64).T + B
     Y2 = Xt @ Wt.T + Bt
     assert np.linalg.norm(Y2 - Y) / np.linalg.norm(Y) < 1e-5
+
+
+# --- group-wise LWC (the pages' g128 setting: clipping per group of input channels)
+
+def test_group_lwc_full_width_is_per_channel():
+    rng = np.random.default_rng(21)
+    W = (rng.standard_normal((12, 64)) * 0.02).astype(F32)
+    ag = rng.uniform(1.0, 5.0, 12).astype(F32)
+    ab = rng.uniform(1.0, 5.0, 12).astype(F32)
+    s = rng.uniform(0.5, 2.0, 64).astype(F32)
+    a = quant.lwc_fakequant(W, ag, ab, 3, s)
+    b = quant.lwc_fakequant(W, ag, ab, 3, s, group=64)
+    assert np.array_equal(a.codes, b.codes) and np.array_equal(a.W_hat, b.W_hat)
+    assert np.array_equal(a.h, b.h) and np.array_equal(a.z, b.z)
+
+
+def test_group_lwc_slices_are_independent_quantizers():
+    """Each (output channel, group) is the per-row quantizer of its own column slice
+    with its own logits (logits stored output-channel major)."""
+    rng = np.random.default_rng(22)
+    C_out, C_in, g = 5, 48, 16
+    G = C_in // g
+    W = (rng.standard_normal((C_out, C_in)) * 0.02).astype(F32)
+    ag = rng.uniform(1.0, 5.0, C_out * G).astype(F32)
+    ab = rng.uniform(1.0, 5.0, C_out * G).astype(F32)
+    r = quant.lwc_fakequant(W, ag, ab, 4, group=g)
+    for o in range(C_out):
+        for k in range(G):
+            sl = W[o:o + 1, k * g:(k + 1) * g]
+            one = quant.quantize_rows(sl, quant.sigmoid32(ag[o * G + k:o * G + k + 1]),
+                                      quant.sigmoid32(ab[o * G + k:o * G + k + 1]), 4)
+            assert np.array_equal(r.codes[o, k * g:(k + 1) * g], one.codes[0])
+            assert np.array_equal(r.W_hat[o, k * g:(k + 1) * g], one.xhat[0])
+            assert r.h[o * G + k] == one.h[0] and r.z[o * G + k] == one.z[0]
+
+
+@pytest.mark.parametrize("nbits", [2, 3, 4])
+def test_group_lwc_minmax(nbits):
+    """gamma = beta = 1 (logits 30): every group of 128 is plain MinMax over its own
+    range: grid ends within half a step of the group's min / max, no clipping."""
+    rng = np.random.default_rng(23)
+    C_out, C_in, g = 8, 512, 128
+    W = (rng.standard_normal((C_out, C_in)) * 0.02).astype(F32)
+    one = np.full(C_out * C_in // g, 30.0, F32)
+    r = quant.lwc_fakequant(W, one, one, nbits, group=g)
+    Q = 2 ** nbits - 1
+    for o in range(C_out):
+        for k in range(C_in // g):
+            x = W[o, k * g:(k + 1) * g].astype(np.float64)
+            j = o * (C_in // g) + k
+            h, z = float(r.h[j]), float(r.z[j])
+            assert abs((0 - z) * h - x.min()) <= h / 2 * (1 + 1e-6)
+            assert abs((Q - z) * h - x.max()) <= h / 2 * (1 + 1e-6)
+            assert np.all(np.abs(r.W_hat[o, k * g:(k + 1) * g] - x) <= h / 2 * (1 + 1e-5) + 1e-12)
+            for c in range(0, g, 37):
+                assert r.codes[o, k * g + c] == _nearest_code(float(x[c] / h), z, Q)
