@@ -33,6 +33,8 @@ def workloads():
         "llama70b_block_w2a16": synth.BLOCK_CFG5_W2,
         "llama7b_ffn_w3a16": synth.FFN_CFG3_W3,
         "llama7b_ffn_w2a16": synth.FFN_CFG3_W2,
+        "llama7b_block_w3a16g128": synth.BLOCK_CFG4_W3G128,
+        "llama7b_block_w2a16g128": synth.BLOCK_CFG4_W2G128,
     }
 
 
@@ -145,10 +147,10 @@ def main():
     n_launch_cap = 64 * (args.steps + 1)
     timer = omq.GemmTimer(n_launch_cap)
     d = omq.BlockDesc(T=c.T, d=c.d, n_q=c.n_q, n_kv=c.n_kv, head_dim=c.head_dim, F=c.F,
-                      wbits=c.wbits, abits=c.abits, ffn_only=c.ffn_only, eps=c.eps,
+                      wbits=c.wbits, abits=c.abits, ffn_only=c.ffn_only, group=c.group, eps=c.eps,
                       rope_theta=c.rope_theta, lr_lwc=c.lr_lwc, lr_let=c.lr_let)
     dt_ = omq.BlockDesc(T=c.T, d=c.d, n_q=c.n_q, n_kv=c.n_kv, head_dim=c.head_dim, F=c.F,
-                        wbits=c.wbits, abits=c.abits, ffn_only=c.ffn_only, eps=c.eps,
+                        wbits=c.wbits, abits=c.abits, ffn_only=c.ffn_only, group=c.group, eps=c.eps,
                         rope_theta=c.rope_theta, lr_lwc=c.lr_lwc, lr_let=c.lr_let, timer=timer)
     offs, n_lwc, total = omq.block_theta_layout(d)
     # initial parameters: clipping logits 4.0, s = 1, delta = 0, s_a = 1
@@ -224,6 +226,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "T": c.T, "d": c.d, "n_q": c.n_q, "n_kv": c.n_kv,
                    "head_dim": c.head_dim, "F": c.F, "wbits": c.wbits, "abits": c.abits,
+                   "lwc_group": c.group or "per_channel",
                    "optimizer": "adamw", "parallelism": "none"},
         "tflops": round(tflops, 2),
         "step_tflop": round(step_flops(c) / 1e12, 4),

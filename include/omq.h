@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define OMQ_ABI_VERSION 1
+#define OMQ_ABI_VERSION 2
 
 /* status codes */
 #define OMQ_OK 0
@@ -81,12 +81,20 @@ int omq_abi_version(void);
  *   h[o] = max((gamma M - beta m) / (2^N - 1), 1e-8);  z[o] = -rint(beta m / h)
  *   codes = clamp(rint(W~ / h) + z, 0, 2^N - 1);  W_hat = (codes - z) h
  *   B_tilde[o] = B[o] + sum_i delta_i W_oi  (original W; B, delta may be NULL = 0)
+ * Group-wise LWC (the pages' g128 setting): with group = 128 each run of 128 input
+ * channels of an output channel is its own quantizer row, with its own logits,
+ * max/min, h and z; those arrays then hold c_out * c_in / 128 entries, index
+ * o * (c_in / 128) + g, and arg_max / arg_min give the column within row o.
+ * group 0 (or c_in) is per output channel; other values return OMQ_E_SHAPE, as
+ * does group 128 when c_in is not a multiple of 128.
  * W: [c_out x c_in] of w_dt.  W_hat: [c_out x c_in] of what_dt (required).
- * h, z: float[c_out] (required).  arg_max, arg_min: int32[c_out] (required).
+ * h, z: float[rows] (required).  arg_max, arg_min: int32[rows] (required), rows
+ * = c_out or c_out * c_in / 128.  a_gamma, a_beta: float[rows].
  * B_tilde: float[c_out] or NULL.  codes: uint8[c_out x c_in] or NULL.
  * n_bits 2..8.
  */
-int omq_lwc_fakequant(const void* W, int w_dt, int64_t c_out, int64_t c_in, int n_bits,
+int omq_lwc_fakequant(const void* W, int w_dt, int64_t c_out, int64_t c_in, int64_t group,
+                      int n_bits,
                       const float* a_gamma, const float* a_beta, const float* s,
                       const float* delta, const float* B, void* W_hat, int what_dt, float* h,
                       float* z, int32_t* arg_max, int32_t* arg_min, float* B_tilde,
@@ -149,13 +157,15 @@ int omq_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int tr
  *   g_s[i] = sum_o gW~_oi W_oi      (if g_s != NULL; s may be NULL = 1)
  *   g_delta[i] = sum_o dy_colsum[o] W_oi   (the bias fold; if g_delta != NULL,
  *     dy_colsum: float[c_out] = sum over tokens of dL/dY)
+ * group: as in omq_lwc_fakequant; with group 128 the sums above run over each
+ * (row, group) and g_a_gamma, g_a_beta have one entry per (row, group).
  * gW_hat: float[c_out x c_in] (dL/dW_hat).  h, z, arg_max, arg_min: the forward's.
- * g_a_gamma, g_a_beta: float[c_out] (required).  g_s, g_delta: float[c_in] or NULL.
+ * g_a_gamma, g_a_beta: float[rows] (required).  g_s, g_delta: float[c_in] or NULL.
  * ws: device workspace of at least omq_lwc_backward_workspace_size(c_out, c_in) bytes.
  */
 size_t omq_lwc_backward_workspace_size(int64_t c_out, int64_t c_in);
 int omq_lwc_backward(const float* gW_hat, const void* W, int w_dt, int64_t c_out, int64_t c_in,
-                     int n_bits, const float* a_gamma, const float* a_beta, const float* s,
+                     int64_t group, int n_bits, const float* a_gamma, const float* a_beta, const float* s,
                      const float* h, const float* z, const int32_t* arg_max,
                      const int32_t* arg_min, const float* dy_colsum, float* g_a_gamma,
                      float* g_a_beta, float* g_s, float* g_delta, void* ws, size_t ws_bytes,
@@ -188,10 +198,12 @@ typedef struct omq_qlinear_desc {
   int abits;   /* 2..8, or 16 = activation quantizer off */
   int use_let; /* 1: theta carries s, delta (LET on this layer) */
   int path;    /* OMQ_PATH_FP32: X, W float32;  OMQ_PATH_BF16: X, W bf16 */
+  int64_t group; /* LWC group along c_in: 0 = per output channel, or 128 */
 } omq_qlinear_desc;
 
 /*
- * theta / dtheta layout (float): a_gamma[c_out], a_beta[c_out], then when use_let
+ * theta / dtheta layout (float): a_gamma[rows], a_beta[rows] (rows = c_out, or
+ * c_out * c_in / 128 with group 128, output-channel major), then when use_let
  * s[c_in], delta[c_in].  omq_qlinear_theta_size gives the element count.
  */
 int64_t omq_qlinear_theta_size(const omq_qlinear_desc* d);
@@ -267,11 +279,14 @@ typedef struct omq_block_desc {
   float lr_lwc, lr_let;
   float beta1, beta2, adam_eps, weight_decay;
   omq_timer* timer;   /* NULL, or per-launch GEMM timing (host struct, caller-owned) */
+  int64_t group;      /* LWC group along C_in: 0 = per output channel, or 128 (every
+                         C_in of the block a multiple of 128) */
 } omq_block_desc;
 
 /*
  * Packed theta order: for each linear of (q, k, v, o, gate, up, down) (ffn_only:
- * gate, up, down) a_gamma[C_out] then a_beta[C_out]; then for each LET site of
+ * gate, up, down) a_gamma[R] then a_beta[R] with R = C_out, or C_out * C_in / 128
+ * for group 128 (output-channel major); then for each LET site of
  * (qkv, o, ffn) (ffn_only: ffn) s[C] then delta[C] (C = d, n_kv*head_dim, d);
  * then s_a[n_kv*head_dim] when abits < 16 and not ffn_only.
  * offsets: int64[2*n_linears + 2*n_sites + 1] host array or NULL; *total: count.

@@ -24,8 +24,9 @@ F32 = np.float32
 F64 = np.float64
 
 
-def forward(X, W, B, theta, wbits, abits, let, ops):
-    """theta: dict with a_gamma, a_beta [C_out] and (when let) s, delta [C_in]."""
+def forward(X, W, B, theta, wbits, abits, let, ops, group=0):
+    """theta: dict with a_gamma, a_beta [C_out] (group-wise LWC: [C_out * C_in /
+    group], output-channel major) and (when let) s, delta [C_in]."""
     gamma = ops.sigmoid(theta["a_gamma"])
     beta = ops.sigmoid(theta["a_beta"])
     if let:
@@ -37,10 +38,11 @@ def forward(X, W, B, theta, wbits, abits, let, ops):
         Wt = ops.to_code(W)
         Xt = ops.to_code(X)
         Bt = np.zeros(W.shape[0]) if B is None else np.asarray(B, dtype=F64)
-    wst = ops.quant(Wt, gamma, beta, wbits, "w") if wbits < 16 else None
+    rows = W.shape[0] * (W.shape[1] // group if group else 1)
+    wst = ops.quant(np.reshape(Wt, (rows, -1)), gamma, beta, wbits, "w") if wbits < 16 else None
     ast, Xh = ops.act(Xt, abits, "a")
     Xop = ops.operand(Xh)
-    Wop = ops.operand(wst.xhat if wst is not None else Wt)
+    Wop = ops.operand(np.reshape(wst.xhat, np.shape(Wt)) if wst is not None else Wt)
     Y = Xop @ Wop.T + Bt[None, :]
     return Y, SimpleNamespace(X=X, W=W, Wt=Wt, Xt=Xt, wst=wst, ast=ast, Xop=Xop, Wop=Wop,
                               gamma=gamma, beta=beta, theta=theta, let=let)
@@ -53,9 +55,12 @@ def backward(dY, sv):
     gXop = dY @ sv.Wop
     gWop = dY.T @ sv.Xop
     if sv.wst is None:
-        gWt, g_gamma, g_beta = gWop, np.zeros(gWop.shape[0]), np.zeros(gWop.shape[0])
+        n = np.asarray(sv.theta["a_gamma"]).size
+        gWt, g_gamma, g_beta = gWop, np.zeros(n), np.zeros(n)
     else:
-        gWt, g_gamma, g_beta = quant.quantize_rows_bwd(gWop, sv.wst)
+        gWt, g_gamma, g_beta = quant.quantize_rows_bwd(np.reshape(gWop, (sv.wst.h.size, -1)),
+                                                       sv.wst)
+        gWt = np.reshape(gWt, gWop.shape)
     ga = sv.gamma.astype(F64)
     gb = sv.beta.astype(F64)
     g["a_gamma"] = g_gamma * ga * (1.0 - ga)
@@ -95,9 +100,9 @@ def init_theta(c_in, c_out, let, a0=4.0):
     return th
 
 
-def calib_step(X, W, B, Ystar, theta, wbits, abits, let, bf16):
+def calib_step(X, W, B, Ystar, theta, wbits, abits, let, bf16, group=0):
     """One fwd + MSE + bwd pass; returns (loss, grads, Y)."""
-    Y, sv = forward(X, W, B, theta, wbits, abits, let, ExactOps(bf16))
+    Y, sv = forward(X, W, B, theta, wbits, abits, let, ExactOps(bf16), group)
     loss, dY = mse(Y, Ystar)
     _, g = backward(dY, sv)
     return loss, g, Y, sv

@@ -43,11 +43,12 @@ class OmqError(RuntimeError):
 
 class QLinearDesc(ctypes.Structure):
     _fields_ = [("struct_size", _sz), ("T", _i64), ("c_in", _i64), ("c_out", _i64),
-                ("wbits", _int), ("abits", _int), ("use_let", _int), ("path", _int)]
+                ("wbits", _int), ("abits", _int), ("use_let", _int), ("path", _int),
+                ("group", _i64)]
 
-    def __init__(self, T, c_in, c_out, wbits, abits, use_let, path):
+    def __init__(self, T, c_in, c_out, wbits, abits, use_let, path, group=0):
         super().__init__(ctypes.sizeof(QLinearDesc), T, c_in, c_out, wbits, abits,
-                         int(use_let), path)
+                         int(use_let), path, group)
 
 
 class OmqTimer(ctypes.Structure):
@@ -101,22 +102,23 @@ class BlockDesc(ctypes.Structure):
                 ("abits", _int), ("ffn_only", _int), ("eps", _f), ("rope_theta", _f),
                 ("optimizer", _int), ("lr_lwc", _f), ("lr_let", _f), ("beta1", _f),
                 ("beta2", _f), ("adam_eps", _f), ("weight_decay", _f),
-                ("timer", ctypes.POINTER(OmqTimer))]
+                ("timer", ctypes.POINTER(OmqTimer)), ("group", _i64)]
 
     def __init__(self, T, d, n_q, n_kv, head_dim, F, wbits, abits, ffn_only=False, eps=1e-6,
                  rope_theta=10000.0, optimizer=OPT_ADAMW, lr_lwc=5e-3, lr_let=1e-2,
-                 beta1=0.9, beta2=0.999, adam_eps=1e-8, weight_decay=0.0, timer=None):
+                 beta1=0.9, beta2=0.999, adam_eps=1e-8, weight_decay=0.0, timer=None,
+                 group=0):
         super().__init__(ctypes.sizeof(BlockDesc), T, d, n_q, n_kv, head_dim, F, wbits, abits,
                          int(ffn_only), eps, rope_theta, optimizer, lr_lwc, lr_let, beta1,
                          beta2, adam_eps, weight_decay,
-                         ctypes.pointer(timer.struct) if timer is not None else None)
+                         ctypes.pointer(timer.struct) if timer is not None else None, group)
 
 
 _SIGS = {
     "omq_status_str": (ctypes.c_char_p, [_int]),
     "omq_abi_version": (_int, []),
-    "omq_lwc_fakequant": (_int, [_vp, _int, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp,
-                                 _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "omq_lwc_fakequant": (_int, [_vp, _int, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp,
+                                 _vp, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "omq_let_apply": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _vp, _int, _vp, _int, _i64, _vp,
                              _vp, _int, _vp, _vp]),
     "omq_act_quant": (_int, [_vp, _int, _i64, _i64, _int, _int, _vp, _vp, _vp, _int, _vp, _vp,
@@ -124,8 +126,8 @@ _SIGS = {
     "omq_gemm": (_int, [_i64, _i64, _i64, _vp, _i64, _int, _vp, _i64, _int, _int, _vp, _f, _vp,
                         _i64, _int, _vp]),
     "omq_lwc_backward_workspace_size": (_sz, [_i64, _i64]),
-    "omq_lwc_backward": (_int, [_vp, _vp, _int, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp,
-                                _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "omq_lwc_backward": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp,
+                                _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "omq_act_quant_backward_workspace_size": (_sz, [_i64, _i64]),
     "omq_act_quant_backward": (_int, [_vp, _i64, _i64, _vp, _int, _int, _int, _vp, _vp, _vp,
                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -199,20 +201,26 @@ def _tdt(code: int):
     return torch.float32 if code == F32 else torch.bfloat16
 
 
+def _lwc_rows(c_out, c_in, group):
+    return c_out * (c_in // group) if group and group != c_in else c_out
+
+
 def lwc_fakequant(W, a_gamma, a_beta, n_bits, s=None, delta=None, B=None, out_dtype=None,
-                  want_bias=False, want_codes=False) -> Dict[str, torch.Tensor]:
+                  want_bias=False, want_codes=False, group=0) -> Dict[str, torch.Tensor]:
     c_out, c_in = W.shape
     dev = W.device
     out_dtype = W.dtype if out_dtype is None else out_dtype
+    rows = _lwc_rows(c_out, c_in, group)
     r = {"W_hat": torch.empty(c_out, c_in, dtype=out_dtype, device=dev),
-         "h": torch.empty(c_out, dtype=torch.float32, device=dev),
-         "z": torch.empty(c_out, dtype=torch.float32, device=dev),
-         "arg_max": torch.empty(c_out, dtype=torch.int32, device=dev),
-         "arg_min": torch.empty(c_out, dtype=torch.int32, device=dev)}
+         "h": torch.empty(rows, dtype=torch.float32, device=dev),
+         "z": torch.empty(rows, dtype=torch.float32, device=dev),
+         "arg_max": torch.empty(rows, dtype=torch.int32, device=dev),
+         "arg_min": torch.empty(rows, dtype=torch.int32, device=dev)}
     r["B_tilde"] = torch.empty(c_out, dtype=torch.float32, device=dev) if want_bias else None
     r["codes"] = torch.empty(c_out, c_in, dtype=torch.uint8, device=dev) if want_codes else None
     _check("omq_lwc_fakequant", lib().omq_lwc_fakequant(
-        _p(W), _dt(W), c_out, c_in, n_bits, _p(a_gamma), _p(a_beta), _p(s), _p(delta), _p(B),
+        _p(W), _dt(W), c_out, c_in, group, n_bits, _p(a_gamma), _p(a_beta), _p(s), _p(delta),
+        _p(B),
         _p(r["W_hat"]), _dt(r["W_hat"]), _p(r["h"]), _p(r["z"]), _p(r["arg_max"]),
         _p(r["arg_min"]), _p(r["B_tilde"]), _p(r["codes"]), _stream()))
     return r
@@ -265,17 +273,19 @@ def gemm(A, B, bias=None, alpha=1.0, C=None, accumulate=False, trans_a=False, tr
 
 
 def lwc_backward(gW_hat, W, n_bits, a_gamma, a_beta, h, z, arg_max, arg_min, s=None,
-                 dy_colsum=None, want_s=False, want_delta=False):
+                 dy_colsum=None, want_s=False, want_delta=False, group=0):
     c_out, c_in = W.shape
     dev = W.device
-    ga = torch.empty(c_out, dtype=torch.float32, device=dev)
-    gb = torch.empty(c_out, dtype=torch.float32, device=dev)
+    rows = _lwc_rows(c_out, c_in, group)
+    ga = torch.empty(rows, dtype=torch.float32, device=dev)
+    gb = torch.empty(rows, dtype=torch.float32, device=dev)
     gs = torch.empty(c_in, dtype=torch.float32, device=dev) if want_s else None
     gd = torch.empty(c_in, dtype=torch.float32, device=dev) if want_delta else None
     nbytes = lib().omq_lwc_backward_workspace_size(c_out, c_in)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     _check("omq_lwc_backward", lib().omq_lwc_backward(
-        _p(gW_hat), _p(W), _dt(W), c_out, c_in, n_bits, _p(a_gamma), _p(a_beta), _p(s), _p(h),
+        _p(gW_hat), _p(W), _dt(W), c_out, c_in, group, n_bits, _p(a_gamma), _p(a_beta), _p(s),
+        _p(h),
         _p(z), _p(arg_max), _p(arg_min), _p(dy_colsum), _p(ga), _p(gb), _p(gs), _p(gd), _p(ws),
         nbytes, _stream()))
     return ga, gb, gs, gd

@@ -22,8 +22,27 @@ const char* omq_status_str(int status) {
 
 int omq_abi_version(void) { return OMQ_ABI_VERSION; }
 
-int omq_lwc_fakequant(const void* W, int w_dt, int64_t c_out, int64_t c_in, int n_bits,
-                      const float* a_gamma, const float* a_beta, const float* s,
+}  // extern "C"
+
+namespace {
+// LWC grouping: 0 or c_in -> 0 (per output channel); 128 with c_in % 128 == 0 -> 128;
+// anything else -> -1 (unsupported)
+int64_t lwc_group(int64_t group, int64_t c_in) {
+  if (group == 0 || group == c_in) return 0;
+  if (group == 128 && c_in % 128 == 0) return 128;
+  return -1;
+}
+// LWC quantizer rows of a qlinear layer: output channels, or (channel, group) pairs
+int64_t qlin_rows(const omq_qlinear_desc* d) {
+  return lwc_group(d->group, d->c_in) > 0 ? d->c_out * (d->c_in / 128) : d->c_out;
+}
+}  // namespace
+
+extern "C" {
+
+
+int omq_lwc_fakequant(const void* W, int w_dt, int64_t c_out, int64_t c_in, int64_t group,
+                      int n_bits, const float* a_gamma, const float* a_beta, const float* s,
                       const float* delta, const float* B, void* W_hat, int what_dt, float* h,
                       float* z, int32_t* arg_max, int32_t* arg_min, float* B_tilde,
                       uint8_t* codes, void* stream) {
@@ -33,6 +52,8 @@ int omq_lwc_fakequant(const void* W, int w_dt, int64_t c_out, int64_t c_in, int 
   if (!dt_ok(w_dt) || !dt_ok(what_dt)) return OMQ_E_DTYPE;
   if (c_out < 0 || c_in <= 0) return OMQ_E_SHAPE;
   if (c_in % 4) return OMQ_E_ALIGN;
+  const int64_t grp = lwc_group(group, c_in);
+  if (grp < 0) return OMQ_E_SHAPE;
   if (!al16(W) || !al16(W_hat) || !al16(s) || !al16(delta) || !al4(codes)) return OMQ_E_ALIGN;
   RowQuantFwd a;
   a.x = W; a.x_dt = w_dt; a.rows = c_out; a.cols = c_in; a.ldx = c_in;
@@ -41,11 +62,18 @@ int omq_lwc_fakequant(const void* W, int w_dt, int64_t c_out, int64_t c_in, int 
   a.out = W_hat; a.out_dt = what_dt; a.ldo = c_in;
   a.h = h; a.z = z; a.amax = arg_max; a.amin = arg_min; a.codes = codes;
   a.fold_delta = delta; a.bias = B; a.bias_out = B_tilde;
+  a.group = grp;
   if (B_tilde && !delta) {
     // no shift: B~ = B
     if (B) OMQ_HIP_CHECK(hipMemcpyAsync(B_tilde, B, c_out * 4, hipMemcpyDeviceToDevice, S(stream)));
     else OMQ_HIP_CHECK(hipMemsetAsync(B_tilde, 0, c_out * 4, S(stream)));
     a.bias_out = nullptr;
+  }
+  if (grp) {
+    // grouped rows: the bias fold runs over whole output channels on its own
+    a.fold_delta = nullptr; a.bias_out = nullptr;
+    if (B_tilde && delta)
+      OMQ_HIP_CHECK(launch_bias_fold(W, w_dt, c_out, c_in, delta, B, B_tilde, S(stream)));
   }
   OMQ_HIP_CHECK(launch_rowquant_fwd(a, S(stream)));
   return OMQ_OK;
@@ -130,7 +158,8 @@ size_t omq_lwc_backward_workspace_size(int64_t c_out, int64_t c_in) {
 }
 
 int omq_lwc_backward(const float* gW_hat, const void* W, int w_dt, int64_t c_out, int64_t c_in,
-                     int n_bits, const float* a_gamma, const float* a_beta, const float* s,
+                     int64_t group, int n_bits, const float* a_gamma, const float* a_beta,
+                     const float* s,
                      const float* h, const float* z, const int32_t* arg_max,
                      const int32_t* arg_min, const float* dy_colsum, float* g_a_gamma,
                      float* g_a_beta, float* g_s, float* g_delta, void* ws, size_t ws_bytes,
@@ -143,6 +172,8 @@ int omq_lwc_backward(const float* gW_hat, const void* W, int w_dt, int64_t c_out
   if (!dt_ok(w_dt)) return OMQ_E_DTYPE;
   if (c_out < 0 || c_in <= 0) return OMQ_E_SHAPE;
   if (c_in % 4) return OMQ_E_ALIGN;
+  const int64_t grp = lwc_group(group, c_in);
+  if (grp < 0) return OMQ_E_SHAPE;
   if (!al16(gW_hat) || !al16(W) || !al16(s) || !al16(dy_colsum)) return OMQ_E_ALIGN;
   if (!ws || ws_bytes < omq_lwc_backward_workspace_size(c_out, c_in)) return OMQ_E_WORKSPACE;
   RowQuantBwd a;
@@ -152,6 +183,7 @@ int omq_lwc_backward(const float* gW_hat, const void* W, int w_dt, int64_t c_out
   a.col_mode = (g_s || g_delta) ? COL_WEIGHT : COL_NONE;
   a.rowvec = dy_colsum; a.g_agamma = g_a_gamma; a.g_abeta = g_a_beta;
   a.out0 = g_s; a.out1 = g_delta; a.ws = reinterpret_cast<float*>(ws);
+  a.group = grp;
   OMQ_HIP_CHECK(launch_rowquant_bwd(a, S(stream)));
   return OMQ_OK;
 }
@@ -192,8 +224,8 @@ int omq_act_quant_backward(const float* gX_hat, int64_t T, int64_t C, const void
 // ---------------------------------------------------------------------------
 
 int64_t omq_qlinear_theta_size(const omq_qlinear_desc* d) {
-  if (!d) return -1;
-  return 2 * d->c_out + (d->use_let ? 2 * d->c_in : 0);
+  if (!d || lwc_group(d->group, d->c_in) < 0) return -1;
+  return 2 * qlin_rows(d) + (d->use_let ? 2 * d->c_in : 0);
 }
 
 namespace {
@@ -214,8 +246,9 @@ QLinWs qlin_layout(const omq_qlinear_desc* d, void* base) {
   const size_t es = bf ? 2 : 4;
   const int64_t T = d->T, ci = d->c_in, co = d->c_out;
   w.What = b.take<char>(co * ci * es);
-  w.wh = b.take<float>(co); w.wz = b.take<float>(co);
-  w.wamax = b.take<int32_t>(co); w.wamin = b.take<int32_t>(co);
+  const int64_t rq = qlin_rows(d);
+  w.wh = b.take<float>(rq); w.wz = b.take<float>(rq);
+  w.wamax = b.take<int32_t>(rq); w.wamin = b.take<int32_t>(rq);
   w.Bt = b.take<float>(co);
   w.Xhat = b.take<char>(T * ci * es);
   w.ah = b.take<float>(T); w.az = b.take<float>(T);
@@ -242,6 +275,7 @@ int qlin_check(const omq_qlinear_desc* d) {
   if (d->T < 0 || d->c_in <= 0 || d->c_out <= 0) return OMQ_E_SHAPE;
   if (d->c_in % 4) return OMQ_E_ALIGN;
   if (d->path == OMQ_PATH_BF16 && (d->T % 8 || d->c_in % 8 || d->c_out % 8)) return OMQ_E_ALIGN;
+  if (lwc_group(d->group, d->c_in) < 0) return OMQ_E_SHAPE;
   return OMQ_OK;
 }
 
@@ -262,11 +296,12 @@ int omq_qlinear_fwd(const omq_qlinear_desc* d, const void* X, const void* W, con
   const QLinWs w = qlin_layout(d, ws);
   const hipStream_t st = S(stream);
   const int dt = d->path == OMQ_PATH_BF16 ? OMQ_BF16 : OMQ_F32;
-  const int64_t T = d->T, ci = d->c_in, co = d->c_out;
+  const int64_t T = d->T, ci = d->c_in, co = d->c_out, rq = qlin_rows(d);
+  const int64_t grp = lwc_group(d->group, ci);
   const float* ag = theta;
-  const float* ab = theta + co;
-  const float* s = d->use_let ? theta + 2 * co : nullptr;
-  const float* dl = d->use_let ? theta + 2 * co + ci : nullptr;
+  const float* ab = theta + rq;
+  const float* s = d->use_let ? theta + 2 * rq : nullptr;
+  const float* dl = d->use_let ? theta + 2 * rq + ci : nullptr;
   // weight side: LET-W, LWC, bias fold
   RowQuantFwd a;
   a.x = W; a.x_dt = dt; a.rows = co; a.cols = ci; a.ldx = ci;
@@ -275,8 +310,12 @@ int omq_qlinear_fwd(const omq_qlinear_desc* d, const void* X, const void* W, con
   a.out = w.What; a.out_dt = dt; a.ldo = ci;
   a.h = w.wh; a.z = w.wz; a.amax = w.wamax; a.amin = w.wamin;
   a.fold_delta = dl; a.bias = B; a.bias_out = dl ? w.Bt : nullptr;
+  if (grp && d->wbits < 16) {     // grouped rows: the bias fold runs on its own
+    a.group = grp; a.fold_delta = nullptr; a.bias_out = nullptr;
+  }
   OMQ_HIP_CHECK(launch_rowquant_fwd(a, st));
-  if (dl && d->wbits >= 16) OMQ_HIP_CHECK(launch_bias_fold(W, dt, co, ci, dl, B, w.Bt, st));
+  if (dl && (d->wbits >= 16 || grp))
+    OMQ_HIP_CHECK(launch_bias_fold(W, dt, co, ci, dl, B, w.Bt, st));
   const float* bias = dl ? w.Bt : B;
   // activation side: LET-X, per-token quantizer
   RowQuantFwd x;
@@ -304,16 +343,17 @@ int omq_qlinear_bwd(const omq_qlinear_desc* d, const void* X, const void* W, con
   const hipStream_t st = S(stream);
   const bool bf = d->path == OMQ_PATH_BF16;
   const int dt = bf ? OMQ_BF16 : OMQ_F32;
-  const int64_t T = d->T, ci = d->c_in, co = d->c_out;
-  const float* s = d->use_let ? theta + 2 * co : nullptr;
-  const float* dl = d->use_let ? theta + 2 * co + ci : nullptr;
+  const int64_t T = d->T, ci = d->c_in, co = d->c_out, rq = qlin_rows(d);
+  const int64_t grp = lwc_group(d->group, ci);
+  const float* s = d->use_let ? theta + 2 * rq : nullptr;
+  const float* dl = d->use_let ? theta + 2 * rq + ci : nullptr;
   float* g_ag = dtheta;
-  float* g_ab = dtheta + co;
-  float* g_s = d->use_let ? dtheta + 2 * co : nullptr;
-  float* g_d = d->use_let ? dtheta + 2 * co + ci : nullptr;
+  float* g_ab = dtheta + rq;
+  float* g_s = d->use_let ? dtheta + 2 * rq : nullptr;
+  float* g_d = d->use_let ? dtheta + 2 * rq + ci : nullptr;
   // dW = dY^T X_hat and dX_hat = dY W_hat, with dY^T, X_hat and W_hat read K-major
   if (dl && !bf) OMQ_HIP_CHECK(launch_colsum(dY, T, co, co, w.colsum, w.cs, st));
-  if (d->wbits >= 16) OMQ_HIP_CHECK(hipMemsetAsync(dtheta, 0, 2 * co * sizeof(float), st));
+  if (d->wbits >= 16) OMQ_HIP_CHECK(hipMemsetAsync(dtheta, 0, 2 * rq * sizeof(float), st));
   if (bf) {
     // bf16 path: dY's bf16 copy and column sums in one pass; both straight-through
     // passes run in the GEMM epilogues
@@ -331,15 +371,16 @@ int omq_qlinear_bwd(const omq_qlinear_desc* d, const void* X, const void* W, con
       se.x_dt = OMQ_BF16; se.ldx = ci; se.let_mode = s ? OMQ_LET_MUL : OMQ_LET_NONE; se.s = s;
       se.h = w.wh; se.z = w.wz; se.nbits = d->wbits; se.rowvec = dl ? w.colsum : nullptr;
       se.col_mode = s ? COL_WEIGHT : COL_NONE; se.rowpart = rowpart; se.colpart = colpart;
+      se.grouped = grp > 0;      // one 128-column tile = one group
       OMQ_HIP_CHECK(launch_gemm(g, st));
       RowQuantBwd a;
       a.x = W; a.x_dt = OMQ_BF16; a.rows = co; a.cols = ci; a.ldx = ci;
       a.let_mode = se.let_mode; a.s = s; a.nbits = d->wbits;
       a.h = w.wh; a.z = w.wz; a.amax = w.wamax; a.amin = w.wamin;
-      a.a_gamma = theta; a.a_beta = theta + co; a.g_agamma = g_ag; a.g_abeta = g_ab;
-      a.col_mode = se.col_mode; a.out0 = g_s; a.out1 = g_d;
+      a.a_gamma = theta; a.a_beta = theta + rq; a.g_agamma = g_ag; a.g_abeta = g_ab;
+      a.col_mode = se.col_mode; a.out0 = g_s; a.out1 = g_d; a.group = grp;
       OMQ_HIP_CHECK(launch_ste_colfinal(a, (int)ntl, colpart, st));
-      OMQ_HIP_CHECK(launch_ste_rowfinal(a, (int)nsl, rowpart, st));
+      OMQ_HIP_CHECK(launch_ste_rowfinal(a, grp ? 1 : (int)nsl, rowpart, st));
     }
     if (dX || s) {
       gemm_ste_extents(T, ci, &nsl, &ntl);
@@ -377,9 +418,10 @@ int omq_qlinear_bwd(const omq_qlinear_desc* d, const void* X, const void* W, con
   a.g = w.gW; a.ldg = ci; a.x = W; a.x_dt = dt; a.rows = co; a.cols = ci; a.ldx = ci;
   a.let_mode = s ? OMQ_LET_MUL : OMQ_LET_NONE; a.s = s; a.nbits = d->wbits;
   a.h = w.wh; a.z = w.wz; a.amax = w.wamax; a.amin = w.wamin;
-  a.a_gamma = theta; a.a_beta = theta + co;
+  a.a_gamma = theta; a.a_beta = theta + rq;
   a.col_mode = s ? COL_WEIGHT : COL_NONE; a.rowvec = dl ? w.colsum : nullptr;
   a.g_agamma = g_ag; a.g_abeta = g_ab; a.out0 = g_s; a.out1 = g_d; a.ws = w.rq;
+  a.group = grp;
   OMQ_HIP_CHECK(launch_rowquant_bwd(a, st));
   if (dX || s) {
     RowQuantBwd x;

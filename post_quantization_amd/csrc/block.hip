@@ -19,8 +19,11 @@ enum { LQ = 0, LK, LV, LO, LG, LU, LD, NLIN };
 
 struct Dims {
   int64_t T, d, nq, nkv, hd, F, dq, dk, nqkv;
+  int64_t group;   // LWC group along C_in: 0 (per output channel) or 128
   int grp;
   bool ffn_only, use_sa;
+  // LWC quantizer rows per output channel of a weight with C_in = cin
+  int64_t g_of(int64_t cin) const { return group ? cin / group : 1; }
 };
 
 Dims dims_of(const omq_block_desc* b) {
@@ -30,6 +33,7 @@ Dims dims_of(const omq_block_desc* b) {
   m.grp = (int)(m.nkv ? m.nq / m.nkv : 1);
   m.ffn_only = b->ffn_only != 0;
   m.use_sa = !m.ffn_only && b->abits < 16;
+  m.group = b->group;
   return m;
 }
 
@@ -44,13 +48,15 @@ struct Theta {  // offsets (elements) into the packed parameter vector
 Theta theta_of(const Dims& m) {
   Theta t;
   const int64_t cout[NLIN] = {m.dq, m.dk, m.dk, m.d, m.F, m.F, m.d};
+  const int64_t cin[NLIN] = {m.d, m.d, m.d, m.dq, m.d, m.d, m.F};
   int64_t o = 0;
   int e = 0;
   for (int l = 0; l < NLIN; ++l) {
     t.ag[l] = t.ab[l] = -1;
     if (m.ffn_only && l < LG) continue;
-    t.ag[l] = o; t.offs[e++] = o; o += cout[l];
-    t.ab[l] = o; t.offs[e++] = o; o += cout[l];
+    const int64_t rows = cout[l] * m.g_of(cin[l]);
+    t.ag[l] = o; t.offs[e++] = o; o += rows;
+    t.ab[l] = o; t.offs[e++] = o; o += rows;
   }
   t.n_lwc = o;
   t.s_qkv = t.d_qkv = t.s_o = t.d_o = t.s_a = -1;
@@ -108,7 +114,7 @@ Ws layout(const Dims& m, void* base) {
   if (att) {
     w.s_o_x = b.take<float>(dq); w.d_o_x = b.take<float>(dq); w.sa_q = b.take<float>(dq);
     w.Wqkv = b.take<uint16_t>(nqkv * d); w.Wo = b.take<uint16_t>(d * dq);
-    w.wq_qkv = take_stats(b, nqkv); w.wq_o = take_stats(b, d);
+    w.wq_qkv = take_stats(b, nqkv * m.g_of(d)); w.wq_o = take_stats(b, d * m.g_of(dq));
     w.Bt_qkv = b.take<float>(nqkv); w.Bt_o = b.take<float>(d);
     w.cos_t = b.take<float>(T * m.hd / 2); w.sin_t = b.take<float>(T * m.hd / 2);
     w.xn = b.take<float>(T * d); w.r1 = b.take<float>(T);
@@ -122,7 +128,7 @@ Ws layout(const Dims& m, void* base) {
     w.a_v = take_stats(b, T); w.a_o = take_stats(b, T);
   }
   w.Wgu = b.take<uint16_t>(2 * F * d); w.Wd = b.take<uint16_t>(d * F);
-  w.wq_gu = take_stats(b, 2 * F); w.wq_d = take_stats(b, d);
+  w.wq_gu = take_stats(b, 2 * F * m.g_of(d)); w.wq_d = take_stats(b, d * m.g_of(F));
   w.Bt_gu = b.take<float>(2 * F);
   w.GU = b.take<float>(T * 2 * F); w.A = b.take<float>(T * F); w.y = b.take<float>(T * d);
   w.Xf = b.take<uint16_t>(T * d); w.Xd = b.take<uint16_t>(T * F);
@@ -170,23 +176,30 @@ int check(const omq_block_desc* b) {
     if (b->head_dim != 128) return OMQ_E_SHAPE;   // the fused attention kernels
   }
   if (b->T % 8 || b->d % 8 || b->F % 8) return OMQ_E_ALIGN;
+  // group-wise LWC in groups of 128 input channels: every C_in (d, F, and the
+  // attention width) a multiple of 128
+  if (b->group != 0 && (b->group != 128 || b->d % 128 || b->F % 128)) return OMQ_E_SHAPE;
   return OMQ_OK;
 }
 
 // one linear's weight side: LET-W (s), LWC (theta logits), bias fold (delta)
 hipError_t wfq(const void* W, int64_t rows, int64_t cols, const float* s, const float* delta,
                const float* th, const Theta& t, int l, int wbits, bool fp, uint16_t* out,
-               const Stats& st, int64_t row0, float* Bt, hipStream_t stream) {
+               const Stats& st, int64_t row0, float* Bt, int64_t group, hipStream_t stream) {
   RowQuantFwd a;
   a.x = W; a.x_dt = OMQ_BF16; a.rows = rows; a.cols = cols; a.ldx = cols;
   a.let_mode = (s && !fp) ? OMQ_LET_MUL : OMQ_LET_NONE; a.s = s;
   a.nbits = fp ? 16 : wbits;
   a.a_gamma = fp ? nullptr : th + t.ag[l]; a.a_beta = fp ? nullptr : th + t.ab[l];
   a.out = out + row0 * cols; a.out_dt = OMQ_BF16; a.ldo = cols;
-  a.h = st.h + row0; a.z = st.z + row0; a.amax = st.amax + row0; a.amin = st.amin + row0;
-  if (!fp && delta) { a.fold_delta = delta; a.bias_out = Bt + row0; }
+  // quantizer state of these rows: per output channel, or per (channel, group)
+  const int64_t q0 = row0 * (group && a.nbits < 16 ? cols / group : 1);
+  a.h = st.h + q0; a.z = st.z + q0; a.amax = st.amax + q0; a.amin = st.amin + q0;
+  const bool grouped = group && a.nbits < 16;
+  if (grouped) a.group = group;
+  if (!fp && delta && !grouped) { a.fold_delta = delta; a.bias_out = Bt + row0; }
   hipError_t e = launch_rowquant_fwd(a, stream);
-  if (e == hipSuccess && !fp && delta && a.nbits >= 16)
+  if (e == hipSuccess && !fp && delta && (a.nbits >= 16 || grouped))
     e = launch_bias_fold(W, OMQ_BF16, rows, cols, delta, nullptr, Bt + row0, stream);
   return e;
 }
@@ -258,10 +271,13 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
     const float* d_o = fp ? nullptr : w.d_o_x;
     CK(launch_rope_tables(T, m.hd, bd->rope_theta, w.cos_t, w.sin_t, st));
     // weight side of q, k, v, o
-    CK(wfq(W[LQ], dq, d, s_qkv, d_qkv, th, t, LQ, wb, fp, w.Wqkv, w.wq_qkv, 0, w.Bt_qkv, st));
-    CK(wfq(W[LK], dk, d, s_qkv, d_qkv, th, t, LK, wb, fp, w.Wqkv, w.wq_qkv, dq, w.Bt_qkv, st));
-    CK(wfq(W[LV], dk, d, s_qkv, d_qkv, th, t, LV, wb, fp, w.Wqkv, w.wq_qkv, dq + dk, w.Bt_qkv, st));
-    CK(wfq(W[LO], d, dq, s_o, d_o, th, t, LO, wb, fp, w.Wo, w.wq_o, 0, w.Bt_o, st));
+    CK(wfq(W[LQ], dq, d, s_qkv, d_qkv, th, t, LQ, wb, fp, w.Wqkv, w.wq_qkv, 0, w.Bt_qkv,
+               m.group, st));
+    CK(wfq(W[LK], dk, d, s_qkv, d_qkv, th, t, LK, wb, fp, w.Wqkv, w.wq_qkv, dq, w.Bt_qkv,
+               m.group, st));
+    CK(wfq(W[LV], dk, d, s_qkv, d_qkv, th, t, LV, wb, fp, w.Wqkv, w.wq_qkv, dq + dk,
+               w.Bt_qkv, m.group, st));
+    CK(wfq(W[LO], d, dq, s_o, d_o, th, t, LO, wb, fp, w.Wo, w.wq_o, 0, w.Bt_o, m.group, st));
     // attention input
     CK(launch_rmsnorm(x, OMQ_BF16, T, d, bd->eps, w.xn, w.r1, st));
     CK(aq(w.xn, OMQ_F32, T, d, d, mode_let, s_qkv, d_qkv, ab, w.Xqkv, w.a_qkv, st));
@@ -298,9 +314,12 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
     xf_dt = OMQ_BF16;
   }
   // FFN
-  CK(wfq(W[LG], F, d, s_ffn, d_ffn, th, t, LG, wb, fp, w.Wgu, w.wq_gu, 0, w.Bt_gu, st));
-  CK(wfq(W[LU], F, d, s_ffn, d_ffn, th, t, LU, wb, fp, w.Wgu, w.wq_gu, F, w.Bt_gu, st));
-  CK(wfq(W[LD], d, F, nullptr, nullptr, th, t, LD, wb, fp, w.Wd, w.wq_d, 0, nullptr, st));
+  CK(wfq(W[LG], F, d, s_ffn, d_ffn, th, t, LG, wb, fp, w.Wgu, w.wq_gu, 0, w.Bt_gu, m.group,
+             st));
+  CK(wfq(W[LU], F, d, s_ffn, d_ffn, th, t, LU, wb, fp, w.Wgu, w.wq_gu, F, w.Bt_gu, m.group,
+             st));
+  CK(wfq(W[LD], d, F, nullptr, nullptr, th, t, LD, wb, fp, w.Wd, w.wq_d, 0, nullptr, m.group,
+             st));
   CK(aq(xf, xf_dt, T, d, d, mode_let, s_ffn, d_ffn, ab, w.Xf, w.a_f, st));
   CK(gemm(w.Xf, d, w.Wgu, d, w.GU, 2 * F, T, 2 * F, d, fp ? nullptr : w.Bt_gu, nullptr, 0, 0, st,
           tm));
@@ -353,6 +372,7 @@ struct LinBwd {
   float* gs_w;
   float* gd_w;
   int acc_w;             // accumulate into gs_w / gd_w
+  int64_t group;         // LWC group along K (0 or 128)
   // activation side
   const void* X;
   int x_dt;
@@ -396,6 +416,9 @@ hipError_t lin_bwd_fused(const Ws& w, const LinBwd& L, int64_t T, int wbits, int
     se.rowvec = L.fold ? w.cs : nullptr;
     se.col_mode = L.s_w ? COL_WEIGHT : COL_NONE;
     se.rowpart = rowpart; se.colpart = colpart;
+    const bool grouped = L.group > 0 && wbits < 16;
+    se.grouped = grouped;        // one 128-column tile of a row = one group
+    const int64_t qg = grouped ? K / L.group : 1;
     if ((e = run_gemm(g, st, tm)) != hipSuccess) return e;
     RowQuantBwd a;
     a.cols = K; a.col_mode = se.col_mode; a.out0 = L.gs_w; a.out1 = L.fold ? L.gd_w : nullptr;
@@ -407,11 +430,15 @@ hipError_t lin_bwd_fused(const Ws& w, const LinBwd& L, int64_t T, int wbits, int
       RowQuantBwd b;
       b.x = sg.W; b.x_dt = OMQ_BF16; b.rows = sg.rows; b.cols = K; b.ldx = K;
       b.let_mode = se.let_mode; b.s = L.s_w; b.nbits = wbits;
-      b.h = L.wst.h + r0; b.z = L.wst.z + r0; b.amax = L.wst.amax + r0; b.amin = L.wst.amin + r0;
+      const int64_t q0 = r0 * qg;
+      b.h = L.wst.h + q0; b.z = L.wst.z + q0; b.amax = L.wst.amax + q0;
+      b.amin = L.wst.amin + q0;
       b.a_gamma = th + t.ag[sg.l]; b.a_beta = th + t.ab[sg.l];
       b.g_agamma = dth + t.ag[sg.l]; b.g_abeta = dth + t.ab[sg.l];
       b.col_mode = se.col_mode; b.out0 = L.gs_w;
-      if ((e = launch_ste_rowfinal(b, (int)nsl, rowpart + r0 * nsl * 2, st)) != hipSuccess)
+      if (grouped) b.group = L.group;
+      if ((e = launch_ste_rowfinal(b, grouped ? 1 : (int)nsl, rowpart + r0 * nsl * 2, st)) !=
+          hipSuccess)
         return e;
       r0 += sg.rows;
     }
@@ -451,6 +478,7 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
   {
     const WSeg segs[1] = {{W[LD], d, LD}};
     LinBwd L{};
+    L.group = m.group;
     L.gY = w.dy; L.N = d; L.K = F; L.Xh = w.Xd; L.Wh = w.Wd; L.gYb = w.dyb;
     L.segs = segs; L.nseg = 1; L.wst = w.wq_d;
     L.X = w.A; L.x_dt = OMQ_F32; L.a_mode = OMQ_LET_NONE; L.ast = w.a_d; L.gx_out = w.gA;
@@ -461,6 +489,7 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
   {
     const WSeg segs[2] = {{W[LG], F, LG}, {W[LU], F, LU}};
     LinBwd L{};
+    L.group = m.group;
     L.gY = w.gGU; L.N = 2 * F; L.K = d; L.Xh = w.Xf; L.Wh = w.Wgu; L.gYb = w.gGUb;
     L.segs = segs; L.nseg = 2; L.wst = w.wq_gu; L.s_w = th + t.s_ffn; L.fold = true;
     L.gs_w = dth + t.s_ffn; L.gd_w = dth + t.d_ffn; L.acc_w = 1;
@@ -477,6 +506,7 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
   {
     const WSeg segs[1] = {{W[LO], d, LO}};
     LinBwd L{};
+    L.group = m.group;
     L.gY = w.dh1; L.N = d; L.K = dq; L.Xh = w.Xo; L.Wh = w.Wo; L.gYb = w.dh1b;
     L.segs = segs; L.nseg = 1; L.wst = w.wq_o; L.s_w = w.s_o_x; L.fold = true;
     L.gs_w = w.gs_full; L.gd_w = w.gd_full; L.acc_w = 0;
@@ -515,6 +545,7 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
   {
     const WSeg segs[3] = {{W[LQ], dq, LQ}, {W[LK], dk, LK}, {W[LV], dk, LV}};
     LinBwd L{};
+    L.group = m.group;
     L.gY = w.gY; L.N = nqkv; L.K = d; L.Xh = w.Xqkv; L.Wh = w.Wqkv; L.gYb = w.gYb;
     L.segs = segs; L.nseg = 3; L.wst = w.wq_qkv; L.s_w = th + t.s_qkv; L.fold = true;
     L.gs_w = dth + t.s_qkv; L.gd_w = dth + t.d_qkv; L.acc_w = 1;

@@ -367,8 +367,9 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
     fetch(0, xa, xa2);
     const int64_t rme = wr0 + (lane & (RW - 1));
     const bool rmv = rme < M;
-    const float h_l = (!pass && rmv) ? e.h[rme] : 1.f;
-    const float z_l = (!pass && rmv) ? e.z[rme] : 0.f;
+    const int64_t hz = e.grouped ? rme * tiles_n + tn : rme;
+    const float h_l = (!pass && rmv) ? e.h[hz] : 1.f;
+    const float z_l = (!pass && rmv) ? e.z[hz] : 0.f;
     const float v_l = (e.rowvec && rmv) ? e.rowvec[rme] : 0.f;
     float s_c[2] = {1.f, 1.f}, d_c[2] = {0.f, 0.f};
     if (colv && e.let_mode != OMQ_LET_NONE) { s_c[0] = e.s[gn]; s_c[1] = e.s[gn + 1]; }

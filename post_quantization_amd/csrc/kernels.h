@@ -20,6 +20,11 @@ struct RowQuantFwd {
   uint8_t* codes = nullptr;                         // [rows x cols], ld = cols
   const float* fold_delta = nullptr;                // bias fold: sum_i fold_delta_i x_ri
   const float* bias = nullptr;  float* bias_out = nullptr;
+  // 128: each run of 128 columns of a row is its own quantizer (group-wise LWC);
+  // h, z, arg_max/arg_min (column within the row), logits are then per
+  // (row, group), index row * cols/128 + group.  0: one quantizer per row.
+  // Grouped rows take no fold_delta (the bias fold runs on its own).
+  int64_t group = 0;
 };
 hipError_t launch_rowquant_fwd(const RowQuantFwd& a, hipStream_t st);
 
@@ -43,6 +48,7 @@ struct RowQuantBwd {
   float* out0 = nullptr;  float* out1 = nullptr;    // column results (g_s, g_delta)
   int accumulate = 0;                               // add into out0/out1
   float* ws = nullptr;                              // partial buffers
+  int64_t group = 0;                                // as in RowQuantFwd (128 or 0)
 };
 size_t rowquant_bwd_ws_bytes(int64_t rows, int64_t cols);
 hipError_t launch_rowquant_bwd(const RowQuantBwd& a, hipStream_t st);
@@ -81,6 +87,10 @@ struct SteEpi {
   int col_mode = 0;
   float* rowpart = nullptr;                         // [rows][tiles_n][2]
   float* colpart = nullptr;                         // [tiles_m][2][cols]
+  // weight rows with group-wise LWC in groups of 128 columns: h, z are per (row,
+  // 128-column tile), index row * tiles_n + tile; the row partials of a tile are
+  // then exactly those of one (row, group)
+  int grouped = 0;
 };
 
 struct Gemm {

@@ -326,6 +326,82 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_wave(RowQuantFwd a) {
   }
 }
 
+// Group-wise forward (groups of 128 columns): 16 lanes per group with 8 columns
+// each, 4 groups per wave, 16 per block; reductions stay inside each 16-lane group.
+template <int XDT>
+__global__ __launch_bounds__(kThreads) void k_rowquant_fwd_g128(RowQuantFwd a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t G = a.cols / 128;
+  const int64_t p = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 6) * 4 + (lane >> 4);
+  const bool pv = p < a.rows * G;             // every lane takes part in the shuffles
+  const int64_t r = pv ? p / G : 0, k = pv ? p % G : 0;
+  const int64_t c = k * 128 + (lane & 15) * 8;
+  const char* xr = reinterpret_cast<const char*>(a.x) + r * a.ldx * (XDT == OMQ_F32 ? 4 : 2);
+  float xt[8];
+  float vmax = -FLT_MAX, vmin = FLT_MAX;
+  int imax = 0x7fffffff, imin = 0x7fffffff;
+  if (pv) {
+    float v[8];
+    load8(xr, XDT, c, v);
+    if (a.let_mode == OMQ_LET_DIV) {
+      float sv[8], dv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      load8f(a.s, c, 8, sv);
+      if (a.delta) load8f(a.delta, c, 8, dv);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xt[j] = (v[j] - dv[j]) / sv[j];
+    } else if (a.let_mode == OMQ_LET_MUL) {
+      float sv[8];
+      load8f(a.s, c, 8, sv);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xt[j] = sv[j] * v[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xt[j] = v[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (xt[j] > vmax || imax == 0x7fffffff) { vmax = xt[j]; imax = (int)(c + j); }
+      if (xt[j] < vmin || imin == 0x7fffffff) { vmin = xt[j]; imin = (int)(c + j); }
+    }
+  }
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) {
+    const float v2 = __shfl_xor(vmax, o, kWave);
+    const int i2 = __shfl_xor(imax, o, kWave);
+    argmax_merge(vmax, imax, v2, i2);
+    const float w2 = __shfl_xor(vmin, o, kWave);
+    const int j2 = __shfl_xor(imin, o, kWave);
+    argmin_merge(vmin, imin, w2, j2);
+  }
+  if (!pv) return;
+  const float gamma = a.a_gamma ? sigmoid_f32(a.a_gamma[p]) : 1.f;
+  const float beta = a.a_beta ? sigmoid_f32(a.a_beta[p]) : 1.f;
+  const RowQ q = row_step(vmax, vmin, gamma, beta, a.nbits);
+  if ((lane & 15) == 0) {
+    if (a.h) a.h[p] = q.h;
+    if (a.z) a.z[p] = q.z;
+    if (a.amax) a.amax[p] = imax;
+    if (a.amin) a.amin[p] = imin;
+  }
+  const float rh = 1.f / q.h;
+  float o[8];
+  uint32_t cw[2] = {0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float u;
+    const float rr = rint_quot(xt[j], q.h, rh, u) + q.z;
+    const float qq = fminf(fmaxf(rr, 0.f), q.Q);
+    o[j] = (qq - q.z) * q.h;
+    cw[j >> 2] |= ((uint32_t)qq) << (8 * (j & 3));
+  }
+  store4(a.out, a.out_dt, r * a.ldo + c, o);
+  store4(a.out, a.out_dt, r * a.ldo + c + 4, o + 4);
+  if (a.codes) {
+    *reinterpret_cast<uint32_t*>(a.codes + r * a.cols + c) = cw[0];
+    *reinterpret_cast<uint32_t*>(a.codes + r * a.cols + c + 4) = cw[1];
+  }
+}
+
 // ---------------------------------------------------------------------------
 // backward tile pass: grid (col slabs, row tiles); wave w takes rows w, w+4, ...
 // ---------------------------------------------------------------------------
@@ -353,19 +429,30 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_bwd_tile(RowQuantBwd a, i
     rc[i] = 1.f / sc[i];
   }
 
+  // grouped rows: the 32 lanes of a half-wave cover one 128-column group per k
+  const bool grouped = a.group > 0;
+  const int64_t G = grouped ? cols / 128 : 1;
   for (int rr_ = wid; rr_ < rows_per_tile; rr_ += 4) {
     const int64_t r = r0 + rr_;
     if (r >= rows) break;
     const char* xr = reinterpret_cast<const char*>(a.x) + r * a.ldx * (XDT == OMQ_F32 ? 4 : 2);
     const float* gr = a.g + r * a.ldg;
-    const float h = pass ? 1.f : a.h[r];
-    const float rh = 1.f / h;
-    const float z = pass ? 0.f : a.z[r];
+    float hk[4], zk[4], rhk[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t gi = grouped ? min(r * G + (c0 + 256 * k) / 128 + (lane >> 5), rows * G - 1)
+                                 : r;
+      hk[k] = pass ? 1.f : a.h[gi];
+      zk[k] = pass ? 0.f : a.z[gi];
+      rhk[k] = 1.f / hk[k];
+    }
     const float vrow = a.rowvec ? a.rowvec[r] : 0.f;
-    float sh = 0.f, sz = 0.f;
+    float shk[4] = {0.f, 0.f, 0.f, 0.f}, szk[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int64_t c = c0 + lane * 4 + 256 * k;
+      const float h = hk[k], rh = rhk[k], z = zk[k];
+      float sh = 0.f, sz = 0.f;
       if (c >= cols) continue;
       float v[4];
       load4(xr, XDT, c, v);
@@ -413,13 +500,35 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_bwd_tile(RowQuantBwd a, i
       }
       if (a.gx)
         *reinterpret_cast<float4*>(a.gx + r * a.ldgx + c) = make_float4(up[0], up[1], up[2], up[3]);
+      shk[k] = sh;
+      szk[k] = sz;
     }
     if (!pass) {
-      sh = wave_sum(sh);
-      sz = wave_sum(sz);
-      if (lane == 0) {
-        rowpart[(r * gridDim.x + blockIdx.x) * 2 + 0] = sh;
-        rowpart[(r * gridDim.x + blockIdx.x) * 2 + 1] = sz;
+      if (grouped) {
+        // one partial per (row, group): sum over the half-wave
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          float sh = shk[k], sz = szk[k];
+#pragma unroll
+          for (int o = 16; o > 0; o >>= 1) {
+            sh += __shfl_xor(sh, o, kWave);
+            sz += __shfl_xor(sz, o, kWave);
+          }
+          const int64_t cg = c0 + 256 * k + 128 * (lane >> 5);
+          if ((lane & 31) == 0 && cg < cols) {
+            rowpart[(r * G + cg / 128) * 2 + 0] = sh;
+            rowpart[(r * G + cg / 128) * 2 + 1] = sz;
+          }
+        }
+      } else {
+        float sh = shk[0] + shk[1] + shk[2] + shk[3];
+        float sz = szk[0] + szk[1] + szk[2] + szk[3];
+        sh = wave_sum(sh);
+        sz = wave_sum(sz);
+        if (lane == 0) {
+          rowpart[(r * gridDim.x + blockIdx.x) * 2 + 0] = sh;
+          rowpart[(r * gridDim.x + blockIdx.x) * 2 + 1] = sz;
+        }
       }
     }
   }
@@ -481,24 +590,27 @@ __global__ __launch_bounds__(kThreads) void k_colpart_reduce(const float* part2,
 template <int XDT>
 __global__ __launch_bounds__(kThreads) void k_rowquant_bwd_rows(RowQuantBwd a, int nslabs,
                                                                 const float* rowpart) {
-  const int64_t r = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (r >= a.rows) return;
+  // quantizer rows: rows, or (row, group) pairs p = row * ng + group
+  const int64_t ng = a.group > 0 ? a.cols / 128 : 1;
+  const int64_t p = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (p >= a.rows * ng) return;
+  const int64_t r = p / ng;
   float gh = 0.f, gzs = 0.f;
   for (int s = 0; s < nslabs; ++s) {
-    gh += rowpart[(r * nslabs + s) * 2 + 0];
-    gzs += rowpart[(r * nslabs + s) * 2 + 1];
+    gh += rowpart[(p * nslabs + s) * 2 + 0];
+    gzs += rowpart[(p * nslabs + s) * 2 + 1];
   }
   const char* xr = reinterpret_cast<const char*>(a.x) + r * a.ldx * (XDT == OMQ_F32 ? 4 : 2);
   auto xval = [&](int64_t c) -> float {
     return XDT == OMQ_F32 ? reinterpret_cast<const float*>(xr)[c]
                           : bf16_to_f32(reinterpret_cast<const uint16_t*>(xr)[c]);
   };
-  const int iM = a.amax[r], im = a.amin[r];
+  const int iM = a.amax[p], im = a.amin[p];
   const float xM = xval(iM), xm = xval(im);
   const float M = let_x(xM, a.let_mode, a.s, a.delta, iM);
   const float m = let_x(xm, a.let_mode, a.s, a.delta, im);
-  const float gamma = a.a_gamma ? sigmoid_f32(a.a_gamma[r]) : 1.f;
-  const float beta = a.a_beta ? sigmoid_f32(a.a_beta[r]) : 1.f;
+  const float gamma = a.a_gamma ? sigmoid_f32(a.a_gamma[p]) : 1.f;
+  const float beta = a.a_beta ? sigmoid_f32(a.a_beta[p]) : 1.f;
   const RowQ q = row_step(M, m, gamma, beta, a.nbits);
   const float h = q.h;
   const float gz = -h * gzs;
@@ -506,8 +618,8 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_bwd_rows(RowQuantBwd a, i
   const float gt1 = G / q.Q;
   const float gt2 = -G / q.Q - gz / h;
   const float gM = gt1 * gamma, gm = gt2 * beta;
-  if (a.g_agamma) a.g_agamma[r] = (gt1 * M) * gamma * (1.f - gamma);
-  if (a.g_abeta) a.g_abeta[r] = (gt2 * m) * beta * (1.f - beta);
+  if (a.g_agamma) a.g_agamma[p] = (gt1 * M) * gamma * (1.f - gamma);
+  if (a.g_abeta) a.g_abeta[p] = (gt2 * m) * beta * (1.f - beta);
   // scatter of dL/dmax and dL/dmin into the gradient of x~ at arg_max / arg_min
   const int idx[2] = {iM, im};
   const float gv[2] = {gM, gm};
@@ -673,6 +785,17 @@ bool launch_fwd_reg(const RowQuantFwd& a, hipStream_t st) {
 
 hipError_t launch_rowquant_fwd(const RowQuantFwd& a, hipStream_t st) {
   if (a.rows == 0 || a.cols == 0) return hipSuccess;
+  if (a.group > 0) {           // groups of 128 (the caller checked cols % 128 == 0)
+    if (a.group != 128 || a.cols % 128 || a.nbits >= 16 || a.fold_delta)
+      return hipErrorInvalidValue;
+    const int64_t n = a.rows * (a.cols / 128);
+    dim3 gg((unsigned)((n + 15) / 16));
+    if (a.x_dt == OMQ_F32)
+      hipLaunchKernelGGL(k_rowquant_fwd_g128<OMQ_F32>, gg, dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL(k_rowquant_fwd_g128<OMQ_BF16>, gg, dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)a.rows);
   if (a.nbits < 16) {
     bool done = a.x_dt == OMQ_F32 ? launch_fwd_wave<OMQ_F32>(a, st)
@@ -689,7 +812,8 @@ hipError_t launch_rowquant_fwd(const RowQuantFwd& a, hipStream_t st) {
 }
 
 size_t rowquant_bwd_ws_bytes(int64_t rows, int64_t cols) {
-  const int64_t nslabs = (cols + kSlab - 1) / kSlab;
+  // row partials per column slab, or per 128-column group for grouped rows
+  const int64_t nslabs = (cols + 127) / 128;
   const int R = bwd_rows_per_tile(rows);
   const int64_t ntiles = (rows + R - 1) / R;
   return ste_partials_floats(rows, cols, nslabs, ntiles) * sizeof(float);
@@ -697,11 +821,12 @@ size_t rowquant_bwd_ws_bytes(int64_t rows, int64_t cols) {
 
 hipError_t launch_rowquant_bwd(const RowQuantBwd& a, hipStream_t st) {
   if (a.rows == 0 || a.cols == 0) return hipSuccess;
+  if (a.group > 0 && (a.group != 128 || a.cols % 128)) return hipErrorInvalidValue;
   const int64_t nslabs = (a.cols + kSlab - 1) / kSlab;
   const int R = bwd_rows_per_tile(a.rows);
   const int64_t ntiles = (a.rows + R - 1) / R;
   float* rowpart = a.ws;
-  float* colpart = a.ws + nslabs * a.rows * 2;
+  float* colpart = a.ws + ((a.cols + 127) / 128) * a.rows * 2;
   dim3 grid((unsigned)nslabs, (unsigned)ntiles);
   if (a.x_dt == OMQ_F32)
     hipLaunchKernelGGL(k_rowquant_bwd_tile<OMQ_F32>, grid, dim3(kThreads), 0, st, a, R, rowpart,
@@ -713,7 +838,7 @@ hipError_t launch_rowquant_bwd(const RowQuantBwd& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   e = launch_ste_colfinal(a, (int)ntiles, colpart, st);
   if (e != hipSuccess) return e;
-  return launch_ste_rowfinal(a, (int)nslabs, rowpart, st);
+  return launch_ste_rowfinal(a, a.group > 0 ? 1 : (int)nslabs, rowpart, st);
 }
 
 size_t ste_partials_floats(int64_t rows, int64_t cols, int64_t nslabs, int64_t ntiles) {
@@ -742,7 +867,8 @@ hipError_t launch_ste_rowfinal(const RowQuantBwd& a, int nslabs, const float* ro
                                hipStream_t st) {
   hipError_t e = hipSuccess;
   if (a.nbits < 16 && a.rows > 0) {
-    dim3 g2((unsigned)((a.rows + kThreads - 1) / kThreads));
+    const int64_t n = a.rows * (a.group > 0 ? a.cols / 128 : 1);
+    dim3 g2((unsigned)((n + kThreads - 1) / kThreads));
     if (a.x_dt == OMQ_F32)
       hipLaunchKernelGGL(k_rowquant_bwd_rows<OMQ_F32>, g2, dim3(kThreads), 0, st, a,
                          (int)nslabs, rowpart);

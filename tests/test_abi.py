@@ -27,7 +27,7 @@ def test_every_declared_symbol_is_exported():
     assert len(names) >= 20
     for n in names:
         assert hasattr(L, n), n
-    assert omq.abi_version() == 1
+    assert omq.abi_version() == 2
 
 
 def test_status_strings():
@@ -43,10 +43,10 @@ FAKE = 0x10000  # a 16-byte aligned non-NULL address; never dereferenced (valida
 def test_validation_before_launch():
     L = omq.lib()
     # missing required pointer
-    assert L.omq_lwc_fakequant(None, 1, 4, 8, 4, FAKE, FAKE, None, None, None, FAKE, 1, FAKE,
+    assert L.omq_lwc_fakequant(None, 1, 4, 8, 0, 4, FAKE, FAKE, None, None, None, FAKE, 1, FAKE,
                                FAKE, FAKE, FAKE, None, None, None) == -1
     # bit width out of range
-    assert L.omq_lwc_fakequant(FAKE, 1, 4, 8, 9, FAKE, FAKE, None, None, None, FAKE, 1, FAKE,
+    assert L.omq_lwc_fakequant(FAKE, 1, 4, 8, 0, 9, FAKE, FAKE, None, None, None, FAKE, 1, FAKE,
                                FAKE, FAKE, FAKE, None, None, None) == -1
     assert L.omq_act_quant(FAKE, 1, 4, 8, 1, 0, None, None, FAKE, 1, FAKE, FAKE, FAKE, FAKE,
                            None, None) == -1
@@ -67,8 +67,13 @@ def test_validation_before_launch():
     assert L.omq_gemm(4, 4, 16, FAKE, 8, 0, FAKE, 16, 0, 1, None, 1.0, FAKE, 4, 0, None) == -2
     # transposed A: its contiguous extent is M (here 12, not a multiple of 8)
     assert L.omq_gemm(12, 8, 16, FAKE, 12, 1, FAKE, 16, 0, 1, None, 1.0, FAKE, 8, 0, None) == -4
+    # unsupported LWC group (only per channel or 128 input channels)
+    assert L.omq_lwc_fakequant(FAKE, 1, 4, 256, 64, 4, FAKE, FAKE, None, None, None, FAKE, 1,
+                               FAKE, FAKE, FAKE, FAKE, None, None, None) == -2
+    assert L.omq_lwc_fakequant(FAKE, 1, 4, 200, 128, 4, FAKE, FAKE, None, None, None, FAKE, 1,
+                               FAKE, FAKE, FAKE, FAKE, None, None, None) == -2
     # workspace too small
-    assert L.omq_lwc_backward(FAKE, FAKE, 1, 8, 8, 4, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+    assert L.omq_lwc_backward(FAKE, FAKE, 1, 8, 8, 0, 4, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
                               None, FAKE, FAKE, None, None, FAKE, 16, None) == -5
     assert L.omq_adamw(FAKE, FAKE, FAKE, FAKE, 10, 4, 1e-3, 1e-3, 0.9, 0.999, 1e-8, 0.0, 0,
                        None) == -1
@@ -89,12 +94,12 @@ def test_validation_before_launch():
                             FAKE, 1 << 30, None) == -1
 
 
-@pytest.mark.parametrize("kind", ["mha_w4a4", "gqa_w4a16", "ffn_w2a16"])
+@pytest.mark.parametrize("kind", ["mha_w4a4", "gqa_w4a16", "ffn_w2a16", "mha_w3a16g128"])
 def test_block_theta_layout_matches_oracle(kind):
     c = {"mha_w4a4": synth.BLOCK_CFG4, "gqa_w4a16": synth.BLOCK_CFG5_W4,
-         "ffn_w2a16": synth.FFN_CFG3_W2}[kind]
+         "ffn_w2a16": synth.FFN_CFG3_W2, "mha_w3a16g128": synth.BLOCK_CFG4_W3G128}[kind]
     d = omq.BlockDesc(T=c.T, d=c.d, n_q=c.n_q, n_kv=c.n_kv, head_dim=c.head_dim, F=c.F,
-                      wbits=c.wbits, abits=c.abits, ffn_only=c.ffn_only)
+                      wbits=c.wbits, abits=c.abits, ffn_only=c.ffn_only, group=c.group)
     offs, n_lwc, total = omq.block_theta_layout(d)
     lay = ob.theta_layout(c, synth.block_weight_shapes(c))
     sizes = [n for _, n in lay]

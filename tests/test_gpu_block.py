@@ -32,12 +32,17 @@ CASES = {
     "gqa_w2a16": synth.reduced(synth.BLOCK_CFG5_W2, T=256, d=1024, n_q=8, n_kv=2, F=2816,
                                n_out=10),
     "ffn_w3a16": synth.reduced(synth.FFN_CFG3_W3, T=256, d=512, F=1376, n_out=5),
+    # group-wise LWC, 128 input channels per group (every C_in a multiple of 128)
+    "mha_w3a16g128": synth.reduced(synth.BLOCK_CFG4_W3G128, T=256, d=512, n_q=4, n_kv=4,
+                                   F=1408, n_out=5),
+    "gqa_w2a16g128": synth.reduced(synth.BLOCK_CFG4_W2G128, T=256, d=1024, n_q=8, n_kv=2,
+                                   F=2816, n_out=10),
 }
 
 
 def desc_of(c):
     return omq.BlockDesc(T=c.T, d=c.d, n_q=c.n_q, n_kv=c.n_kv, head_dim=c.head_dim, F=c.F,
-                         wbits=c.wbits, abits=c.abits, ffn_only=c.ffn_only, eps=c.eps,
+                         wbits=c.wbits, abits=c.abits, ffn_only=c.ffn_only, group=c.group, eps=c.eps,
                          rope_theta=c.rope_theta, lr_lwc=c.lr_lwc, lr_let=c.lr_let)
 
 

@@ -56,6 +56,52 @@ def test_lwc_fakequant_bitexact(c_out, c_in, nbits, let, out):
     assert rel(host(r["B_tilde"]), ref.B_tilde) < 1e-5
 
 
+@pytest.mark.parametrize("c_out,c_in,nbits,let,wdt", [
+    (40, 1024, 2, True, "bf16"), (96, 384, 3, False, "f32"), (4096, 4096, 4, True, "bf16"),
+    (33, 11008, 3, True, "bf16")])
+def test_lwc_group128_bitexact(c_out, c_in, nbits, let, wdt):
+    """Group-wise LWC: per (row, 128-column group) logits, max/min, h, z and codes
+    equal the oracle's bit for bit; arg_max / arg_min are columns of the row."""
+    log("lwc_g128", c_out, c_in, nbits, let, wdt)
+    rng = np.random.default_rng(c_out + 3 * c_in)
+    G = c_in // 128
+    W = synth.normal(94, c_out, (c_out, c_in), synth.WEIGHT_STD, bf16=(wdt == "bf16"))
+    ag = rng.uniform(0.0, 6.0, c_out * G).astype(F32)
+    ab = rng.uniform(0.0, 6.0, c_out * G).astype(F32)
+    s = rng.uniform(0.5, 2.0, c_in).astype(F32) if let else None
+    d = (rng.standard_normal(c_in) * 0.1).astype(F32) if let else None
+    B = rng.standard_normal(c_out).astype(F32)
+    ref = quant.lwc_fakequant(W, ag, ab, nbits, s, d, B, group=128)
+    tdt = torch.bfloat16 if wdt == "bf16" else torch.float32
+    r = omq.lwc_fakequant(dev(W, tdt), dev(ag), dev(ab), nbits, dev(s) if let else None,
+                          dev(d) if let else None, dev(B), out_dtype=torch.float32,
+                          want_bias=True, want_codes=True, group=128)
+    torch.cuda.synchronize()
+    base = (np.arange(c_out * G) % G) * 128
+    assert np.array_equal(host(r["arg_max"]), ref.st.iM + base)
+    assert np.array_equal(host(r["arg_min"]), ref.st.im + base)
+    assert np.array_equal(host(r["h"]), ref.h)
+    assert np.array_equal(host(r["z"]), ref.z)
+    assert np.array_equal(host(r["codes"]), ref.codes)
+    assert np.array_equal(host(r["W_hat"]), ref.W_hat)
+    assert rel(host(r["B_tilde"]), ref.B_tilde) < 1e-5
+    # straight-through backward, grouped (tile pass)
+    g = (rng.standard_normal((c_out, c_in)) * 1e-3).astype(F32)
+    v = rng.standard_normal(c_out).astype(F32)
+    gWt, gg, gb = quant.lwc_bwd(g, ref)
+    gam, bet = ref.st.gamma.astype(np.float64), ref.st.beta.astype(np.float64)
+    ga, gbb, gs, gd = omq.lwc_backward(dev(g), dev(W, tdt), nbits, dev(ag), dev(ab), r["h"],
+                                       r["z"], r["arg_max"], r["arg_min"],
+                                       s=dev(s) if let else None, dy_colsum=dev(v),
+                                       want_s=let, want_delta=True, group=128)
+    torch.cuda.synchronize()
+    assert rel(host(ga), gg * gam * (1 - gam)) < 1e-4
+    assert rel(host(gbb), gb * bet * (1 - bet)) < 1e-4
+    if let:
+        assert rel(host(gs), np.sum(gWt * W.astype(np.float64), axis=0)) < 1e-4
+    assert rel(host(gd), W.astype(np.float64).T @ v) < 1e-5
+
+
 @pytest.mark.parametrize("T,C,nbits,mode,xdt", [
     (48, 200, 4, "div", "f32"), (33, 4096, 4, "div", "bf16"), (64, 4096, 8, "mul", "f32"),
     (40, 11008, 4, "none", "f32"), (2048, 4096, 4, "div", "bf16")])

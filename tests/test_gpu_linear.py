@@ -25,19 +25,19 @@ def _theta_vec(th, let):
     return np.concatenate(parts).astype(F32)
 
 
-def _split(vec, c_in, c_out, let):
-    out = {"a_gamma": vec[:c_out], "a_beta": vec[c_out:2 * c_out]}
+def _split(vec, c_in, rows, let):
+    out = {"a_gamma": vec[:rows], "a_beta": vec[rows:2 * rows]}
     if let:
-        out["s"] = vec[2 * c_out:2 * c_out + c_in]
-        out["delta"] = vec[2 * c_out + c_in:]
+        out["s"] = vec[2 * rows:2 * rows + c_in]
+        out["delta"] = vec[2 * rows + c_in:]
     return out
 
 
-def _run_gpu(c, X, W, B, Ystar, theta_vec):
+def _run_gpu(c, X, W, B, Ystar, theta_vec, group=0):
     bf = not c.fp32
     tdt = torch.bfloat16 if bf else torch.float32
     d = omq.QLinearDesc(c.T, c.c_in, c.c_out, c.wbits, c.abits, c.let,
-                        omq.PATH_BF16 if bf else omq.PATH_FP32)
+                        omq.PATH_BF16 if bf else omq.PATH_FP32, group)
     ws = torch.empty(omq.qlinear_workspace_size(d), dtype=torch.uint8, device=DEV)
     tX, tW, tB = dev(X, tdt), dev(W, tdt), dev(B)
     th = dev(theta_vec)
@@ -101,3 +101,39 @@ def test_cfg2_bf16_w4a4_let(size):
         log("grad", k, e)
         assert e < 2e-2, k
     assert rel(dXg, gX) < 2e-2
+
+
+@pytest.mark.parametrize("path,wbits", [("bf16", 3), ("fp32", 2)])
+def test_group128_lwc_linear(path, wbits):
+    """Group-wise LWC (128 input channels per clipping group) with LET, weight-only:
+    forward, loss and every gradient against the oracle, on both paths (bf16: the
+    group state read per 128-column tile inside the fused dW epilogue; fp32: the
+    grouped tile pass)."""
+    fp32 = path == "fp32"
+    c = synth.reduced(synth.LINEAR_CFG2, T=256, c_in=640, c_out=264, n_out=6, wbits=wbits,
+                      abits=16, fp32=fp32)
+    log("g128 linear", path, wbits)
+    inp = synth.linear_inputs(c)
+    X, W, B = inp["X"], inp["W"], inp["B"]
+    rng = np.random.default_rng(31)
+    rows = c.c_out * (c.c_in // 128)
+    th = ol.init_theta(c.c_in, c.c_out, True)
+    th["a_gamma"] = rng.uniform(2.0, 5.0, rows).astype(F32)
+    th["a_beta"] = rng.uniform(2.0, 5.0, rows).astype(F32)
+    th["s"] = rng.uniform(0.7, 1.4, c.c_in).astype(F32)
+    th["delta"] = (rng.standard_normal(c.c_in) * 0.05).astype(F32)
+    Ystar = ol.reference(X, W, B)
+    Yg, lg, dXg, dthg = _run_gpu(c, X, W, B, Ystar, _theta_vec(th, True), group=128)
+    loss, g, Y, sv = ol.calib_step(X, W, B, Ystar, th, c.wbits, c.abits, True, bf16=not fp32,
+                                   group=128)
+    gX, _ = ol.backward(2 * (Y - Ystar) / Y.size, sv)
+    tol = 1e-4 if fp32 else 2e-2
+    log("loss gpu", lg, "oracle", loss)
+    assert rel(Yg, Y) < (1e-5 if fp32 else 1e-4)
+    assert abs(lg - loss) <= tol * loss
+    gsplit = _split(dthg, c.c_in, rows, True)
+    for k in ("a_gamma", "a_beta", "s", "delta"):
+        e = rel(gsplit[k], g[k])
+        log("grad", k, e)
+        assert e < tol, k
+    assert rel(dXg, gX) < tol

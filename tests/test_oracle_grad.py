@@ -63,30 +63,32 @@ def test_quantizer_rows_fd():
     _fd(L, p0, {"x": gx, "gamma": gg, "beta": gb}, ["x", "gamma", "beta"], rng, n=12)
 
 
-@pytest.mark.parametrize("abits,let", [(4, True), (16, True), (8, False)])
-def test_linear_fd(abits, let):
+@pytest.mark.parametrize("abits,let,group", [(4, True, 0), (16, True, 0), (8, False, 0),
+                                             (4, True, 8), (16, False, 8)])
+def test_linear_fd(abits, let, group):
     rng = np.random.default_rng(1)
     c = synth.reduced(synth.LINEAR_CFG1, T=12, c_in=24, c_out=10)
     inp = synth.linear_inputs(c)
     X, W, B = inp["X"], inp["W"], inp["B"] + rng.standard_normal(10).astype(F32)
     th = ol.init_theta(24, 10, let)
-    th["a_gamma"] = rng.uniform(0.5, 4.0, 10).astype(F32)
-    th["a_beta"] = rng.uniform(0.5, 4.0, 10).astype(F32)
+    rows = 10 * (24 // group if group else 1)
+    th["a_gamma"] = rng.uniform(0.5, 4.0, rows).astype(F32)
+    th["a_beta"] = rng.uniform(0.5, 4.0, rows).astype(F32)
     if let:
         th["s"] = rng.uniform(0.5, 2.0, 24).astype(F32)
         th["delta"] = (rng.standard_normal(24) * 0.3).astype(F32)
     Ystar = ol.reference(X, W, B)
     ex = ExactOps(bf16=False)
-    ol.forward(X, W, B, th, 4, abits, let, ex)
+    ol.forward(X, W, B, th, 4, abits, let, ex, group)
     ops = SmoothOps(ex.states)
     th64 = {k: v.astype(F64) for k, v in th.items()}
     th64["X"] = X.astype(F64)
 
     def L(p):
-        Y, _ = ol.forward(p["X"], W, B, p, 4, abits, let, ops)
+        Y, _ = ol.forward(p["X"], W, B, p, 4, abits, let, ops, group)
         return ol.mse(Y, Ystar)[0]
 
-    Y, sv = ol.forward(th64["X"], W, B, th64, 4, abits, let, ops)
+    Y, sv = ol.forward(th64["X"], W, B, th64, 4, abits, let, ops, group)
     loss, dY = ol.mse(Y, Ystar)
     gX, g = ol.backward(dY, sv)
     g["X"] = gX
