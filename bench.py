@@ -105,12 +105,103 @@ def cpu_baseline(c, inp, tokens):
             "host": platform.processor() or platform.machine()}
 
 
+DECODE_WORKLOADS = {"llama7b_w4a16g128_decode": 1, "llama7b_w4a16g128_decode_t16": 16}
+
+
+def decode_main(args):
+    """Deployment form (packed 4-bit codes, g128 steps): the 7 linear products of
+    one 7B-shaped block at T tokens (single-token decode by default), timed per
+    launch with HIP events on the launching stream; tokens/s for a 32-block model."""
+    import numpy as np
+    import torch
+    import post_quantization_amd as omq
+    import synth
+    from oracle import export as ex
+    from oracle import quant
+
+    T = DECODE_WORKLOADS[args.workload]
+    c = synth.BLOCK_CFG4
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    inp = synth.block_inputs(c)
+    shapes = synth.block_weight_shapes(c)
+    layers = []
+    for n in synth.WEIGHT_NAMES:
+        N, K = shapes[n]
+        W = torch.from_numpy(inp["W_" + n]).to(torch.bfloat16).to(dev)
+        logits = torch.full((N * K // 128,), 4.0, dtype=torch.float32, device=dev)
+        r = omq.lwc_fakequant(W, logits, logits, 4, out_dtype=torch.bfloat16, want_codes=True,
+                              group=128)
+        layers.append((n, N, K, omq.pack_codes(r["codes"], 4), r["h"], r["z"], r["codes"]))
+    rng = np.random.default_rng(0)
+    Xs = {K: torch.from_numpy(synth.to_bf16(rng.standard_normal((T, K)).astype(np.float32)))
+          .to(torch.bfloat16).to(dev) for K in {k for _, _, k, *_ in layers}}
+    Ys = {n: torch.empty(T, N, dtype=torch.float32, device=dev) for n, N, *_ in layers}
+
+    def block():
+        for n, N, K, words, h, z, _ in layers:
+            omq.w4a16_gemm(Xs[K], words, N, h, z, 128, None, Ys[n])
+
+    for _ in range(args.warmup):
+        block()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps * len(layers))]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    i = 0
+    for _ in range(args.steps):
+        for n, N, K, words, h, z, _ in layers:
+            ev[i][0].record()
+            omq.w4a16_gemm(Xs[K], words, N, h, z, 128, None, Ys[n])
+            ev[i][1].record()
+            i += 1
+    e1.record()
+    torch.cuda.synchronize()
+    ms_block = e0.elapsed_time(e1) / args.steps
+    durs = [a.elapsed_time(b) for a, b in ev]
+    per_layer = [(N * K // 2 + N * (K // 128) * 8 + T * K * 2 + T * N * 4)
+                 for _, N, K, *_ in layers]
+    bytes_launch = sum(per_layer) / len(per_layer)
+    avg_s = sum(durs) / len(durs) / 1e3
+    achieved = bytes_launch / avg_s / 1e9
+    tok_s = T * 1000.0 / (ms_block * 32)
+    cpu = None
+    if not args.no_cpu_baseline:
+        t0 = time.perf_counter()
+        for n, N, K, words, h, z, codes in layers:
+            ex.wa16_linear(Xs[K].float().cpu().numpy(), ex.pack_codes(codes.cpu().numpy(), 4),
+                           h.cpu().numpy(), z.cpu().numpy(), 4, K, 128)
+        dt = time.perf_counter() - t0
+        cpu = {"value": T / (dt * 32), "unit": "tokens/s", "cores": os.cpu_count(),
+               "kind": "oracle",
+               "sample": "the oracle's packed product (unpack, dequant, bf16, float64 matmul) "
+                         "for the 7 linears of one block at %d token(s), %.2f s, x32 blocks"
+                         % (T, dt)}
+    out = {
+        "metric": "W4A16g128 decode tokens/s, LLaMA-7B-shaped linears (32 blocks), 1 GPU",
+        "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_block, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": T, "d": c.d, "F": c.F, "wbits": 4,
+                   "lwc_group": 128, "step": "the 7 linear products of one block"},
+        "roofline": {"kernel": "k_w4a16_gemm", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "launches": len(durs), "avg_launch_us": round(avg_s * 1e6, 2),
+                     "bytes_per_launch": int(bytes_launch)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="llama7b_block_w4a4", choices=list(workloads()))
+    ap.add_argument("--workload", default="llama7b_block_w4a4",
+                    choices=list(workloads()) + list(DECODE_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -126,6 +217,10 @@ def main():
     import torch
     import post_quantization_amd as omq
     import synth
+
+    if args.workload in DECODE_WORKLOADS:
+        decode_main(args)
+        return
 
     if args.copy_calibration:
         a = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")    # 1 GiB

@@ -145,6 +145,53 @@ int omq_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int tr
              float* C, int64_t ldc, int accumulate, void* stream);
 
 /*
+ * Deployment form of a calibrated layer (paper reading, section "LWC": the deployed
+ * weight is the integer code q with step h and zero point z, W_hat = (q - z) h;
+ * section "LET": after calibration the transformation is folded into the
+ * neighbouring parameters, so the deployed block keeps its original operators).
+ *
+ * Packed codes: along each row, floor(32 / n_bits) codes per 32-bit word, code j
+ * of a word in bits [j n_bits, (j+1) n_bits), lowest column first, unused high bits
+ * zero; ceil(cols / per_word) words per row.
+ *
+ * omq_pack_codes -- codes: uint8 [rows x cols] (values < 2^n_bits, e.g. the codes
+ * output of omq_lwc_fakequant); words: uint32 [rows x ceil(cols / per_word)].
+ * n_bits 2..8.
+ */
+int omq_pack_codes(const uint8_t* codes, int64_t rows, int64_t cols, int n_bits,
+                   uint32_t* words, void* stream);
+
+/*
+ * omq_fold_linear -- weight-only (A16) fold of a calibrated linear's LET sites:
+ *   bias_out[n] = B[n] - sum_k W_hat[n,k] delta[k] / s[k]      (input site: the
+ *     layer then takes X / s, i.e. the normalization in front gets gain 1 / s)
+ *   then, with s_o (the attention-output site folded into the value projection,
+ *   per output row n of W_v): bias_out[n] = (bias_out[n] - delta_o[n]) / s_o[n] and
+ *   h_out[n, g] = h[n, g] / s_o[n].
+ * words: packed codes [N x K]; h, z: float[N] or float[N x K/128] (group 0 or 128);
+ * B (the layer's B~ = B + delta W), s, delta, s_o, delta_o: float, each may be NULL
+ * (B NULL = 0; delta NULL: no input-site term; s_o NULL: no value fold).
+ * bias_out: float[N] (required); h_out: float like h (required when s_o is set).
+ */
+int omq_fold_linear(const uint32_t* words, int n_bits, int64_t N, int64_t K, const float* h,
+                    const float* z, int64_t group, const float* B, const float* s,
+                    const float* delta, const float* s_o, const float* delta_o,
+                    float* bias_out, float* h_out, void* stream);
+
+/*
+ * omq_w4a16_gemm -- weight-only product on packed 4-bit codes:
+ *   Y[T x N] = X[T x K] W_hat^T + bias,  W_hat[n, k] = bf16((q[n,k] - z) h)
+ * with (h, z) per output row (group 0) or per 128-column group (group 128, index
+ * n * K/128 + k/128); the dequantized value is the calibration's fake-quant weight.
+ * X: bf16 [T x K] contiguous; words: uint32 [N x K/8]; bias: float[N] or NULL;
+ * Y: float [T x N], overwritten.  K a multiple of 64 (and of 128 for group 128).
+ * Built for small T (decode: the weight codes are re-read for every 32 tokens).
+ */
+int omq_w4a16_gemm(const void* X, int64_t T, int64_t K, const uint32_t* words, int64_t N,
+                   const float* h, const float* z, int64_t group, const float* bias, float* Y,
+                   void* stream);
+
+/*
  * omq_lwc_backward -- straight-through backward of omq_lwc_fakequant.
  * Only rint is straight-through (the LWC blog, section 2.2: the gradient bypasses
  * the rounding); clamp, max/min, h and z are differentiated exactly.  Per row o,

@@ -19,7 +19,7 @@ __all__ = [
     "qlinear_workspace_size", "qlinear_fwd", "qlinear_bwd", "sgd", "adamw", "BlockDesc",
     "block_theta_layout", "block_workspace_size", "block_forward", "block_step",
     "F32", "BF16", "LET_NONE", "LET_DIV", "LET_MUL", "PATH_FP32", "PATH_BF16",
-    "OPT_ADAMW", "OPT_SGD", "GemmTimer",
+    "OPT_ADAMW", "OPT_SGD", "GemmTimer", "pack_codes", "fold_linear", "w4a16_gemm",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -137,6 +137,10 @@ _SIGS = {
                                _vp]),
     "omq_qlinear_bwd": (_int, [ctypes.POINTER(QLinearDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                _sz, _vp]),
+    "omq_pack_codes": (_int, [_vp, _i64, _i64, _int, _vp, _vp]),
+    "omq_fold_linear": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp,
+                               _vp, _vp, _vp]),
+    "omq_w4a16_gemm": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _vp]),
     "omq_sgd": (_int, [_vp, _vp, _i64, _i64, _f, _f, _vp]),
     "omq_adamw": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _f, _f, _f, _f, _f, _f, _i64, _vp]),
     "omq_block_theta_layout": (_int, [ctypes.POINTER(BlockDesc), _vp, _vp, _vp, _vp]),
@@ -375,3 +379,39 @@ def block_step(desc, x, y_target, weights, theta, dtheta, adam_m, adam_v, step, 
     _check("omq_block_step", lib().omq_block_step(
         ctypes.byref(desc), _p(x), _p(y_target), ctypes.addressof(arr), _p(theta), _p(dtheta),
         _p(adam_m), _p(adam_v), step, _p(loss), _p(ws), ws.numel(), _stream()))
+
+
+# ---------------------------------------------------------------------------
+# deployment form
+# ---------------------------------------------------------------------------
+
+def pack_codes(codes: torch.Tensor, n_bits: int) -> torch.Tensor:
+    """uint8 codes [rows x cols] -> packed int32 words [rows x ceil(cols / (32 // n_bits))]."""
+    rows, cols = codes.shape
+    per = 32 // n_bits
+    words = torch.empty(rows, (cols + per - 1) // per, dtype=torch.int32, device=codes.device)
+    _check("omq_pack_codes", lib().omq_pack_codes(_p(codes), rows, cols, n_bits, _p(words),
+                                                   _stream()))
+    return words
+
+
+def fold_linear(words, n_bits, N, K, h, z, group=0, B=None, s=None, delta=None, s_o=None,
+                delta_o=None):
+    """Weight-only LET fold: returns (bias_out [N], h_out or None)."""
+    dev = words.device
+    bias = torch.empty(N, dtype=torch.float32, device=dev)
+    h_out = torch.empty_like(h) if s_o is not None else None
+    _check("omq_fold_linear", lib().omq_fold_linear(
+        _p(words), n_bits, N, K, _p(h), _p(z), group, _p(B), _p(s), _p(delta), _p(s_o),
+        _p(delta_o), _p(bias), _p(h_out), _stream()))
+    return bias, h_out
+
+
+def w4a16_gemm(X, words, N, h, z, group=0, bias=None, Y=None):
+    """Y [T x N] float32 = X (bf16 [T x K]) W_hat^T + bias from packed 4-bit codes."""
+    T, K = X.shape
+    if Y is None:
+        Y = torch.empty(T, N, dtype=torch.float32, device=X.device)
+    _check("omq_w4a16_gemm", lib().omq_w4a16_gemm(
+        _p(X), T, K, _p(words), N, _p(h), _p(z), group, _p(bias), _p(Y), _stream()))
+    return Y

@@ -435,6 +435,50 @@ int omq_qlinear_bwd(const omq_qlinear_desc* d, const void* X, const void* W, con
   return OMQ_OK;
 }
 
+int omq_pack_codes(const uint8_t* codes, int64_t rows, int64_t cols, int n_bits,
+                   uint32_t* words, void* stream) {
+  if (!codes || !words) return OMQ_E_INVALID_ARG;
+  if (n_bits < 2 || n_bits > 8) return OMQ_E_INVALID_ARG;
+  if (rows < 0 || cols < 0) return OMQ_E_SHAPE;
+  if (!al4(words)) return OMQ_E_ALIGN;
+  OMQ_HIP_CHECK(launch_pack_codes(codes, rows, cols, n_bits, words, S(stream)));
+  return OMQ_OK;
+}
+
+int omq_fold_linear(const uint32_t* words, int n_bits, int64_t N, int64_t K, const float* h,
+                    const float* z, int64_t group, const float* B, const float* s,
+                    const float* delta, const float* s_o, const float* delta_o,
+                    float* bias_out, float* h_out, void* stream) {
+  if (!words || !h || !z || !bias_out) return OMQ_E_INVALID_ARG;
+  if ((delta && !s) || (s_o && !h_out)) return OMQ_E_INVALID_ARG;
+  if (n_bits < 2 || n_bits > 8) return OMQ_E_INVALID_ARG;
+  if (N < 0 || K <= 0) return OMQ_E_SHAPE;
+  const int64_t grp = lwc_group(group, K);
+  if (grp < 0) return OMQ_E_SHAPE;
+  DeployFold a;
+  a.words = words; a.nbits = n_bits; a.N = N; a.K = K; a.h = h; a.z = z; a.group = grp;
+  a.B = B; a.s = s; a.delta = delta; a.s_o = s_o; a.delta_o = delta_o;
+  a.bias_out = bias_out; a.h_out = h_out;
+  OMQ_HIP_CHECK(launch_fold_linear(a, S(stream)));
+  return OMQ_OK;
+}
+
+int omq_w4a16_gemm(const void* X, int64_t T, int64_t K, const uint32_t* words, int64_t N,
+                   const float* h, const float* z, int64_t group, const float* bias, float* Y,
+                   void* stream) {
+  if (!X || !words || !h || !z || !Y) return OMQ_E_INVALID_ARG;
+  if (T < 0 || N < 0 || K <= 0) return OMQ_E_SHAPE;
+  if (K % 64) return OMQ_E_ALIGN;
+  const int64_t grp = lwc_group(group, K);
+  if (grp < 0) return OMQ_E_SHAPE;
+  if (!al16(X) || !al16(words)) return OMQ_E_ALIGN;
+  DeployGemm a;
+  a.X = X; a.T = T; a.K = K; a.words = words; a.N = N; a.h = h; a.z = z; a.group = grp;
+  a.bias = bias; a.Y = Y;
+  OMQ_HIP_CHECK(launch_w4a16_gemm(a, S(stream)));
+  return OMQ_OK;
+}
+
 int omq_sgd(float* theta, const float* grad, int64_t n, int64_t n_lwc, float lr_lwc,
             float lr_let, void* stream) {
   if (!theta || !grad) return OMQ_E_INVALID_ARG;

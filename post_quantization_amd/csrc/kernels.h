@@ -169,6 +169,24 @@ hipError_t launch_flash_fwd(const FlashFwd& a, hipStream_t st);
 hipError_t launch_attn_bwd_prep(const float* gO, const float* O, int64_t ld, int64_t T, int n_q,
                                 float* D, uint16_t* gOb, int64_t ldb, hipStream_t st);
 hipError_t launch_flash_bwd(const FlashBwd& a, hipStream_t st);
+// deployment form (csrc/deploy.hip)
+struct DeployFold {
+  const uint32_t* words = nullptr;  int nbits = 4;  int64_t N = 0, K = 0;
+  const float* h = nullptr;  const float* z = nullptr;  int64_t group = 0;
+  const float* B = nullptr;  const float* s = nullptr;  const float* delta = nullptr;
+  const float* s_o = nullptr;  const float* delta_o = nullptr;
+  float* bias_out = nullptr;  float* h_out = nullptr;
+};
+struct DeployGemm {
+  const void* X = nullptr;  int64_t T = 0, K = 0;
+  const uint32_t* words = nullptr;  int64_t N = 0;
+  const float* h = nullptr;  const float* z = nullptr;  int64_t group = 0;
+  const float* bias = nullptr;  float* Y = nullptr;
+};
+hipError_t launch_pack_codes(const uint8_t* codes, int64_t rows, int64_t cols, int nbits,
+                             uint32_t* words, hipStream_t st);
+hipError_t launch_fold_linear(const DeployFold& a, hipStream_t st);
+hipError_t launch_w4a16_gemm(const DeployGemm& a, hipStream_t st);
 hipError_t launch_axpy_bcast(float* y, const float* x, int64_t n, hipStream_t st);
 hipError_t launch_kv_expand(const float* v, int64_t n_q, int64_t n_kv, int64_t hd, float* out,
                             hipStream_t st);

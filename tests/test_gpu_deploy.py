@@ -1,0 +1,91 @@
+"""GPU parity of the deployment form against the oracle (oracle/export.py),
+through the C ABI: packing of the calibrated codes (bit-exact), the weight-only
+LET folds, and the product on packed 4-bit codes, per output channel and with
+128-channel groups, for token counts from single-token decode to a few tiles."""
+import numpy as np
+import pytest
+import torch
+
+import post_quantization_amd as omq
+from oracle import export as ex
+from oracle import quant
+import synth
+from gpu_util import dev, host, log, rel
+
+pytestmark = pytest.mark.gpu
+
+F32 = np.float32
+
+
+@pytest.mark.parametrize("nbits,cols", [(4, 4096), (4, 100), (2, 1000), (3, 517), (8, 36)])
+def test_pack_codes_bitexact(nbits, cols):
+    log("pack", nbits, cols)
+    rng = np.random.default_rng(nbits * 1000 + cols)
+    codes = rng.integers(0, 2 ** nbits, (37, cols)).astype(np.uint8)
+    words = omq.pack_codes(torch.from_numpy(codes).cuda(), nbits)
+    torch.cuda.synchronize()
+    got = host(words).view(np.uint32)
+    assert np.array_equal(got, ex.pack_codes(codes, nbits))
+
+
+def _calibrated_layer(N, K, group, nbits, rng, let=True):
+    """Synthetic weights through the GPU fake quantizer (codes, h, z) and the oracle's."""
+    W = synth.normal(95, N + K, (N, K), synth.WEIGHT_STD)
+    rows = N * (K // group if group else 1)
+    ag = rng.uniform(1.0, 5.0, rows).astype(F32)
+    ab = rng.uniform(1.0, 5.0, rows).astype(F32)
+    s = rng.uniform(0.5, 2.0, K).astype(F32) if let else None
+    ref = quant.lwc_fakequant(W, ag, ab, nbits, s, group=group or None)
+    r = omq.lwc_fakequant(dev(W, torch.bfloat16), dev(ag), dev(ab), nbits,
+                          dev(s) if let else None, out_dtype=torch.bfloat16, want_codes=True,
+                          group=group)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(r["codes"]), ref.codes)
+    return W, s, ref, r
+
+
+@pytest.mark.parametrize("N,K,group", [(96, 4096, 128), (300, 1024, 0), (4096, 4096, 128)])
+def test_fold_linear(N, K, group):
+    log("fold", N, K, group)
+    rng = np.random.default_rng(N + K)
+    W, s, ref, r = _calibrated_layer(N, K, group, 4, rng)
+    words = omq.pack_codes(r["codes"], 4)
+    delta = (rng.standard_normal(K) * 0.1).astype(F32)
+    Bt = rng.standard_normal(N).astype(F32)
+    s_o = rng.uniform(0.5, 2.0, N).astype(F32)
+    d_o = (rng.standard_normal(N) * 0.1).astype(F32)
+    W_hat = ex.dequant(ref.codes, ref.h, ref.z, group or None)
+    # input site only
+    b1, _ = omq.fold_linear(words, 4, N, K, r["h"], r["z"], group, dev(Bt), dev(s), dev(delta))
+    _, eb1 = ex.fold_input_site(W_hat, Bt, s, delta)
+    # input site, then the attention-output pair folded into this (value) projection
+    b2, h2 = omq.fold_linear(words, 4, N, K, r["h"], r["z"], group, dev(Bt), dev(s), dev(delta),
+                             dev(s_o), dev(d_o))
+    torch.cuda.synchronize()
+    G = K // group if group else 1
+    eh2, eb2 = ex.fold_value_site(ref.h.reshape(N, G), eb1[:, None], s_o[:, None],
+                                  d_o[:, None])
+    assert rel(host(b1), eb1) < 1e-5
+    assert rel(host(b2), eb2[:, 0]) < 1e-5
+    assert np.allclose(host(h2).reshape(N, G), eh2, rtol=2 ** -23, atol=0)
+
+
+@pytest.mark.parametrize("T,N,K,group", [(1, 4096, 4096, 128), (7, 300, 4096, 128),
+                                         (32, 1024, 11008, 128), (100, 512, 1024, 0),
+                                         (16, 22016, 4096, 128)])
+def test_w4a16_gemm(T, N, K, group):
+    log("w4a16", T, N, K, group)
+    rng = np.random.default_rng(T * 7 + N + K)
+    W, s, ref, r = _calibrated_layer(N, K, group, 4, rng, let=False)
+    words = omq.pack_codes(r["codes"], 4)
+    X = synth.to_bf16(rng.standard_normal((T, K)).astype(F32))
+    bias = rng.standard_normal(N).astype(F32)
+    Y = omq.w4a16_gemm(dev(X, torch.bfloat16), words, N, r["h"], r["z"], group, dev(bias))
+    torch.cuda.synchronize()
+    expect = ex.wa16_linear(X, ex.pack_codes(ref.codes, 4), ref.h, ref.z, 4, K,
+                            group or None, bias)
+    assert rel(host(Y), expect) < 1e-5
+    # the same product through the fake-quant weight and the matrix-core GEMM
+    Y2 = omq.gemm(dev(X, torch.bfloat16), r["W_hat"], bias=dev(bias))
+    torch.cuda.synchronize()
+    assert rel(host(Y), host(Y2)) < 1e-5
