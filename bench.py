@@ -195,13 +195,69 @@ def decode_main(args):
     print(json.dumps(out), flush=True)
 
 
+EXPORT_WORKLOADS = {"llama7b_block_w4a16g128_export": 4}
+
+
+def export_main(args):
+    """Deployment export of a calibrated 7B-shaped weight-only block (fake quantizer
+    with codes, packing, LET folds), weights resident in HBM, timed with HIP events."""
+    import numpy as np
+    import torch
+    import post_quantization_amd as omq
+    from post_quantization_amd import export
+    import synth
+
+    c = synth.replace(synth.BLOCK_CFG4_W3G128, wbits=EXPORT_WORKLOADS[args.workload])
+    torch.cuda.set_device(0)
+    inp = synth.block_inputs(c)
+    W = [torch.from_numpy(inp["W_" + n]).to(torch.bfloat16).cuda() for n in synth.WEIGHT_NAMES]
+    d = omq.BlockDesc(T=c.T, d=c.d, n_q=c.n_q, n_kv=c.n_kv, head_dim=c.head_dim, F=c.F,
+                      wbits=c.wbits, abits=c.abits, group=c.group)
+    offs, n_lwc, total = omq.block_theta_layout(d)
+    rng = np.random.default_rng(0)
+    th = rng.uniform(0.9, 1.1, total).astype(np.float32)
+    th[:n_lwc] = 4.0
+    theta = torch.from_numpy(th).cuda()
+    for _ in range(args.warmup):
+        export.export_block(d, W, theta)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        export.export_block(d, W, theta)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    shapes = synth.block_weight_shapes(c)
+    nw = sum(a * b for a, b in shapes.values())
+    # weight read 2 B, fake-quant weight 2 B and codes 1 B written, codes re-read 1 B,
+    # packed codes written and re-read by the fold 2 x 0.5 B
+    traffic = 7.0 * nw
+    gbs = traffic / (ms * 1e-3) / 1e9
+    out = {
+        "metric": "W4A16g128 deployment export, LLaMA-7B-shaped block (blocks/s), 1 GPU",
+        "value": round(1000.0 / ms, 3), "unit": "blocks/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "d": c.d, "F": c.F, "wbits": c.wbits,
+                   "lwc_group": c.group, "weights": nw},
+        "roofline": {"kernel": "export pipeline (fake quantizer, pack, fold)", "bound": "hbm",
+                     "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "bytes_per_step": int(traffic)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama7b_block_w4a4",
-                    choices=list(workloads()) + list(DECODE_WORKLOADS))
+                    choices=list(workloads()) + list(DECODE_WORKLOADS) +
+                    list(EXPORT_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -220,6 +276,9 @@ def main():
 
     if args.workload in DECODE_WORKLOADS:
         decode_main(args)
+        return
+    if args.workload in EXPORT_WORKLOADS:
+        export_main(args)
         return
 
     if args.copy_calibration:

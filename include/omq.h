@@ -171,12 +171,13 @@ int omq_pack_codes(const uint8_t* codes, int64_t rows, int64_t cols, int n_bits,
  * words: packed codes [N x K]; h, z: float[N] or float[N x K/128] (group 0 or 128);
  * B (the layer's B~ = B + delta W), s, delta, s_o, delta_o: float, each may be NULL
  * (B NULL = 0; delta NULL: no input-site term; s_o NULL: no value fold).
- * bias_out: float[N] (required); h_out: float like h (required when s_o is set).
+ * bias_out: float[N] (required); h_out: float like h (required when s_o is set);
+ * gain_out: float[K] or NULL, receives the input site's gain 1 / s (needs s).
  */
 int omq_fold_linear(const uint32_t* words, int n_bits, int64_t N, int64_t K, const float* h,
                     const float* z, int64_t group, const float* B, const float* s,
                     const float* delta, const float* s_o, const float* delta_o,
-                    float* bias_out, float* h_out, void* stream);
+                    float* bias_out, float* h_out, float* gain_out, void* stream);
 
 /*
  * omq_w4a16_gemm -- weight-only product on packed 4-bit codes:

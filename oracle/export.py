@@ -33,6 +33,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from . import quant
+
 F32 = np.float32
 F64 = np.float64
 
@@ -95,10 +97,88 @@ def fold_value_site(h_v, b_v, s_o, delta_o):
 def wa16_linear(X, words, h, z, nbits, C, group=None, bias=None):
     """Y = X W_hat^T (+ bias) from packed codes, W_hat rounded to bf16 as the
     matrix-core operand; X as given (bf16 values); float64 product."""
-    from . import quant
     codes = unpack_codes(words, nbits, C)
     Wop = quant.bf16(dequant(codes, h, z, group))
     Y = np.asarray(X, F64) @ Wop.T
     if bias is not None:
         Y = Y + np.asarray(bias, F64)[None, :]
     return Y
+
+
+def export_block(c, Wd, th):
+    """Deployment form of a calibrated weight-only block (abits = 16, so s_a is not
+    learned): per linear the packed codes of Q(W~) with (h, z) and a bias; the
+    attention-output pair folded into v; the input sites' 1/s as the gains of the
+    norms in front (as the FFN input's scale when the block is the FFN alone).
+    Returns {name: float64 / uint32 array}."""
+    from . import block as ob
+    assert c.abits >= 16
+    group = c.group or None
+    out = {}
+
+    def lin(name, W, s, delta):
+        r = quant.lwc_fakequant(W, th["a_gamma_" + name], th["a_beta_" + name], c.wbits, s,
+                                group=group)
+        out[name + ".words"] = pack_codes(r.codes, c.wbits)
+        out[name + ".h"] = r.h.astype(F64)
+        out[name + ".z"] = r.z.astype(F64)
+        bias = np.zeros(W.shape[0])
+        if delta is not None:
+            _, bias = fold_input_site(r.W_hat, quant.bias_fold(W, None, delta), s, delta)
+        out[name + ".bias"] = bias
+
+    if not c.ffn_only:
+        s, d = th["s_qkv"], th["delta_qkv"]
+        for n in ("q", "k", "v"):
+            lin(n, Wd["W_" + n], s, d)
+        G = out["v.h"].size // Wd["W_v"].shape[0]
+        h2, b2 = fold_value_site(out["v.h"].reshape(-1, G), out["v.bias"][:, None],
+                                 np.asarray(th["s_o"], F64)[:, None],
+                                 np.asarray(th["delta_o"], F64)[:, None])
+        out["v.h"], out["v.bias"] = h2.reshape(-1), b2[:, 0]
+        out["attn_norm.gain"] = 1.0 / np.asarray(s, F64)
+        s_o = ob.kv_broadcast(th["s_o"], c.n_q, c.n_kv, c.head_dim)
+        d_o = ob.kv_broadcast(th["delta_o"], c.n_q, c.n_kv, c.head_dim)
+        lin("o", Wd["W_o"], s_o, None)
+        out["o.bias"] = quant.bias_fold(Wd["W_o"], None, d_o)
+    s, d = th["s_ffn"], th["delta_ffn"]
+    lin("gate", Wd["W_gate"], s, d)
+    lin("up", Wd["W_up"], s, d)
+    lin("down", Wd["W_down"], None, None)
+    out["ffn_in.gain"] = 1.0 / np.asarray(s, F64)
+    return out
+
+
+def deployed_forward(c, x, exp, cast=None):
+    """The exported block run with its original operators only: norm (times the
+    folded gain), linears from packed codes plus bias, RoPE, causal attention,
+    SiLU gate, residuals.  cast: how a weight enters its product (None: exact)."""
+    from . import block as ob
+    cast = cast or (lambda a: np.asarray(a, F64))
+    group = c.group or None
+
+    def dlin(name, X, N, K):
+        W = dequant(unpack_codes(exp[name + ".words"], c.wbits, K), exp[name + ".h"],
+                    exp[name + ".z"], group)
+        return np.asarray(X, F64) @ cast(W).T + exp[name + ".bias"][None, :]
+
+    x = np.asarray(x, F64)
+    hd = c.head_dim
+    dq, dk = c.n_q * hd, c.n_kv * hd
+    if not c.ffn_only:
+        xn, _ = ob.rmsnorm(x, c.eps)
+        X = xn * exp["attn_norm.gain"][None, :]
+        Q = dlin("q", X, dq, c.d)
+        K = dlin("k", X, dk, c.d)
+        V = dlin("v", X, dk, c.d)
+        cos, sin = ob.rope_tables(c.T, hd, c.rope_theta)
+        O, _ = ob.attention(ob.rope(Q, c.n_q, hd, cos, sin), ob.rope(K, c.n_kv, hd, cos, sin), V,
+                            c.n_q, c.n_kv, hd)
+        h1 = x + dlin("o", O, c.d, dq)
+        xn2, _ = ob.rmsnorm(h1, c.eps)
+    else:
+        h1, xn2 = None, x
+    X2 = xn2 * exp["ffn_in.gain"][None, :]
+    A = ob.silu(dlin("gate", X2, c.F, c.d)) * dlin("up", X2, c.F, c.d)
+    D = dlin("down", A, c.d, c.F)
+    return D if c.ffn_only else h1 + D

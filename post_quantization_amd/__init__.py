@@ -139,7 +139,7 @@ _SIGS = {
                                _sz, _vp]),
     "omq_pack_codes": (_int, [_vp, _i64, _i64, _int, _vp, _vp]),
     "omq_fold_linear": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp,
-                               _vp, _vp, _vp]),
+                               _vp, _vp, _vp, _vp]),
     "omq_w4a16_gemm": (_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _vp]),
     "omq_sgd": (_int, [_vp, _vp, _i64, _i64, _f, _f, _vp]),
     "omq_adamw": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _f, _f, _f, _f, _f, _f, _i64, _vp]),
@@ -396,15 +396,17 @@ def pack_codes(codes: torch.Tensor, n_bits: int) -> torch.Tensor:
 
 
 def fold_linear(words, n_bits, N, K, h, z, group=0, B=None, s=None, delta=None, s_o=None,
-                delta_o=None):
-    """Weight-only LET fold: returns (bias_out [N], h_out or None)."""
+                delta_o=None, want_gain=False):
+    """Weight-only LET fold: returns (bias_out [N], h_out or None), and the input
+    site's gain 1/s [K] as a third item when want_gain."""
     dev = words.device
     bias = torch.empty(N, dtype=torch.float32, device=dev)
     h_out = torch.empty_like(h) if s_o is not None else None
+    gain = torch.empty(K, dtype=torch.float32, device=dev) if want_gain else None
     _check("omq_fold_linear", lib().omq_fold_linear(
         _p(words), n_bits, N, K, _p(h), _p(z), group, _p(B), _p(s), _p(delta), _p(s_o),
-        _p(delta_o), _p(bias), _p(h_out), _stream()))
-    return bias, h_out
+        _p(delta_o), _p(bias), _p(h_out), _p(gain), _stream()))
+    return (bias, h_out, gain) if want_gain else (bias, h_out)
 
 
 def w4a16_gemm(X, words, N, h, z, group=0, bias=None, Y=None):

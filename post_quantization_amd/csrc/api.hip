@@ -448,9 +448,9 @@ int omq_pack_codes(const uint8_t* codes, int64_t rows, int64_t cols, int n_bits,
 int omq_fold_linear(const uint32_t* words, int n_bits, int64_t N, int64_t K, const float* h,
                     const float* z, int64_t group, const float* B, const float* s,
                     const float* delta, const float* s_o, const float* delta_o,
-                    float* bias_out, float* h_out, void* stream) {
+                    float* bias_out, float* h_out, float* gain_out, void* stream) {
   if (!words || !h || !z || !bias_out) return OMQ_E_INVALID_ARG;
-  if ((delta && !s) || (s_o && !h_out)) return OMQ_E_INVALID_ARG;
+  if ((delta && !s) || (s_o && !h_out) || (gain_out && !s)) return OMQ_E_INVALID_ARG;
   if (n_bits < 2 || n_bits > 8) return OMQ_E_INVALID_ARG;
   if (N < 0 || K <= 0) return OMQ_E_SHAPE;
   const int64_t grp = lwc_group(group, K);
@@ -458,7 +458,7 @@ int omq_fold_linear(const uint32_t* words, int n_bits, int64_t N, int64_t K, con
   DeployFold a;
   a.words = words; a.nbits = n_bits; a.N = N; a.K = K; a.h = h; a.z = z; a.group = grp;
   a.B = B; a.s = s; a.delta = delta; a.s_o = s_o; a.delta_o = delta_o;
-  a.bias_out = bias_out; a.h_out = h_out;
+  a.bias_out = bias_out; a.h_out = h_out; a.gain_out = gain_out;
   OMQ_HIP_CHECK(launch_fold_linear(a, S(stream)));
   return OMQ_OK;
 }

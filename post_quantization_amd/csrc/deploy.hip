@@ -76,6 +76,10 @@ __global__ __launch_bounds__(256) void k_fold_linear(DeployFold a) {
   if (a.s_o && a.h_out) {
     for (int64_t g = lane; g < G; g += 64) a.h_out[n * G + g] = a.h[n * G + g] / a.s_o[n];
   }
+  // the input site's gain, written by the waves of the first output rows
+  if (a.gain_out)
+    for (int64_t k = n * 64 + lane; k < a.K && n * 64 < a.K; k += a.N * 64)
+      a.gain_out[k] = 1.f / a.s[k];
 }
 
 // Y[T x N] = X[T x K] W_hat^T (+ bias), W_hat from 4-bit packed codes with (h, z)

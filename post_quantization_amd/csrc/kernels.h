@@ -175,7 +175,7 @@ struct DeployFold {
   const float* h = nullptr;  const float* z = nullptr;  int64_t group = 0;
   const float* B = nullptr;  const float* s = nullptr;  const float* delta = nullptr;
   const float* s_o = nullptr;  const float* delta_o = nullptr;
-  float* bias_out = nullptr;  float* h_out = nullptr;
+  float* bias_out = nullptr;  float* h_out = nullptr;  float* gain_out = nullptr;
 };
 struct DeployGemm {
   const void* X = nullptr;  int64_t T = 0, K = 0;

@@ -89,3 +89,47 @@ def test_w4a16_gemm(T, N, K, group):
     Y2 = omq.gemm(dev(X, torch.bfloat16), r["W_hat"], bias=dev(bias))
     torch.cuda.synchronize()
     assert rel(host(Y), host(Y2)) < 1e-5
+
+
+@pytest.mark.parametrize("kind", ["gqa_w4a16g128", "mha_w3a16", "ffn_w2a16g128"])
+def test_export_block(kind):
+    """The exported weight-only block (packed codes, (h, z), folded biases, gains)
+    against the oracle's export of the same calibrated parameters."""
+    from oracle import block as ob
+    from post_quantization_amd import export
+    c = {"gqa_w4a16g128": synth.reduced(synth.BLOCK_CFG4_W3G128, wbits=4, d=512, n_q=4,
+                                        n_kv=2, F=1408),
+         "mha_w3a16": synth.reduced(synth.BLOCK_CFG4_W3G128, group=0, d=384, n_q=3, n_kv=3,
+                                    F=1032),
+         "ffn_w2a16g128": synth.reduced(synth.FFN_CFG3_W2, group=128, d=512, F=1408)}[kind]
+    log("export", kind)
+    rng = np.random.default_rng(12)
+    shapes = synth.block_weight_shapes(c)
+    inp = synth.block_inputs(c)
+    Wd = {k: v for k, v in inp.items() if k.startswith("W_")}
+    th = ob.init_theta(c, shapes)
+    for k in th:
+        if k.startswith("a_"):
+            th[k] = rng.uniform(1.0, 5.0, th[k].size).astype(F32)
+        elif k.startswith("s"):
+            th[k] = rng.uniform(0.7, 1.4, th[k].size).astype(F32)
+        else:
+            th[k] = (rng.standard_normal(th[k].size) * 0.05).astype(F32)
+    d = omq.BlockDesc(T=c.T, d=c.d, n_q=c.n_q, n_kv=c.n_kv, head_dim=c.head_dim, F=c.F,
+                      wbits=c.wbits, abits=c.abits, ffn_only=c.ffn_only, group=c.group)
+    W = [dev(Wd["W_" + n], torch.bfloat16) if ("W_" + n) in Wd else None
+         for n in synth.WEIGHT_NAMES]
+    got = export.export_block(d, W, dev(ob.pack(c, shapes, th)))
+    torch.cuda.synchronize()
+    want = ex.export_block(c, Wd, th)
+    assert set(got) == set(want)
+    for k, v in want.items():
+        g = host(got[k])
+        if k.endswith(".words"):
+            assert np.array_equal(g.view(np.uint32), v), k
+        elif k.endswith(".z") or (k.endswith(".h") and not k.startswith("v.")):
+            assert np.array_equal(g, v.astype(F32)), k
+        elif k.endswith(".bias"):
+            assert rel(g, v) < 1e-5, k
+        else:                        # v.h (divided by s_o) and the gains 1/s
+            assert np.allclose(g, v, rtol=2 ** -23, atol=0), k

@@ -88,3 +88,43 @@ def test_wa16_linear_matches_fakequant_product():
     words = ex.pack_codes(r.codes, 4)
     Y = ex.wa16_linear(X, words, r.h, r.z, 4, 256, group=128)
     assert np.allclose(Y, X @ quant.bf16(r.W_hat).T, rtol=0, atol=0)
+
+
+@pytest.mark.parametrize("kind", ["mha", "gqa_g8", "ffn"])
+def test_exported_block_reproduces_the_calibrated_forward(kind):
+    """Weight-only: the block rebuilt from packed codes, folded biases and gains,
+    with no LET operators left, gives the calibration forward's output (exact
+    float64 products on both sides; the only difference is X~'s float32 rounding
+    in the calibration path)."""
+    import synth
+    from oracle import block as ob
+    from oracle.ops import ExactOps
+    c = {"mha": synth.BlockCfg(cfg=4, T=9, d=16, n_q=2, n_kv=2, F=24, wbits=4, abits=16,
+                               head_dim=8, n_out=2, out_lo=5.0, out_hi=10.0),
+         "gqa_g8": synth.BlockCfg(cfg=4, T=9, d=16, n_q=4, n_kv=2, F=24, wbits=3, abits=16,
+                                  head_dim=8, n_out=2, out_lo=5.0, out_hi=10.0, group=8),
+         "ffn": synth.BlockCfg(cfg=3, T=9, d=16, n_q=2, n_kv=2, F=24, wbits=2, abits=16,
+                               head_dim=8, ffn_only=True, n_out=2, out_lo=5.0,
+                               out_hi=10.0)}[kind]
+    rng = np.random.default_rng(8)
+    inp = synth.block_inputs(c)
+    Wd = {k: v for k, v in inp.items() if k.startswith("W_")}
+    shapes = synth.block_weight_shapes(c)
+    th = ob.init_theta(c, shapes)
+    for k in th:
+        if k.startswith("a_"):
+            th[k] = rng.uniform(0.5, 4.0, th[k].size).astype(F32)
+        elif k.startswith("s"):
+            th[k] = rng.uniform(0.6, 1.6, th[k].size).astype(F32)
+        else:
+            th[k] = (rng.standard_normal(th[k].size) * 0.2).astype(F32)
+    y_cal, _ = ob.forward(c, inp["x"], Wd, th, ExactOps(bf16=False))
+    exp = ex.export_block(c, Wd, th)
+    y_dep = ex.deployed_forward(c, inp["x"], exp)
+    assert np.max(np.abs(y_dep - y_cal)) <= 1e-5 * np.max(np.abs(y_cal))
+    # and the fold is not vacuous: without the gain the block's update changes
+    upd = y_cal - (0 if c.ffn_only else np.asarray(inp["x"], np.float64))
+    bad = dict(exp)
+    bad["ffn_in.gain"] = np.ones_like(exp["ffn_in.gain"])
+    assert np.max(np.abs(ex.deployed_forward(c, inp["x"], bad) - y_cal)) > 1e-2 * np.max(
+        np.abs(upd))
