@@ -167,6 +167,29 @@ def block_inputs(c: BlockCfg) -> Dict[str, np.ndarray]:
     return out
 
 
+def stack_inputs(c: BlockCfg, n_blocks: int, n_samples: int):
+    """A stack of n_blocks blocks and n_samples calibration samples.
+
+    Block b's weights use tensor ids 100 b + 10 + i (block 0 is block_inputs'
+    weights); sample s is an outlier-activation draw with tensor id 100000 + s and
+    its factors from id 101000 + s, on the same outlier channels for every sample
+    (the channels block_inputs picks).  Returns (list of weight dicts, samples
+    float32 [n_samples, T, d] with bf16-exact values)."""
+    assert n_samples <= 1000 and n_blocks <= 900
+    shapes = block_weight_shapes(c)
+    names = ("gate", "up", "down") if c.ffn_only else WEIGHT_NAMES
+    blocks = []
+    for b in range(n_blocks):
+        blocks.append({"W_" + n: normal(c.cfg, 100 * b + 10 + i, shapes[n], WEIGHT_STD)
+                       for i, n in enumerate(WEIGHT_NAMES) if n in names})
+    ch = tuple(int(v) for v in rng(c.cfg, 1002).choice(c.d, size=c.n_out, replace=False))
+    xs = np.empty((n_samples, c.T, c.d), dtype=np.float32)
+    for s in range(n_samples):
+        xs[s] = outlier_activations(c.cfg, 100000 + s, c.T, c.d, c.n_out, c.out_lo, c.out_hi,
+                                    channels=ch)
+    return blocks, xs
+
+
 def reduced(c, **kw):
     """The same workload at other sizes (parity cases the oracle finishes fast)."""
     return replace(c, **kw)
