@@ -250,6 +250,74 @@ def export_main(args):
     print(json.dumps(out), flush=True)
 
 
+CALIB_WORKLOADS = {"llama7b_w4a4_model_calib": ("BLOCK_CFG4", 32, 20)}
+
+
+def calib_main(args):
+    """Sequential multi-block calibration with the pages' schedule (128 samples,
+    batch 1, 20 epochs per block, AdamW) on a stack of --calib-blocks LLaMA-7B-shaped
+    W4A4 blocks: per block the cached full-precision targets, the calibration steps,
+    and the calibrated block's outputs for the next block.  The whole-model time is
+    the measured per-block time times the model's 32 blocks (all blocks have the same
+    shape and schedule)."""
+    import torch
+    import post_quantization_amd as omq
+    from post_quantization_amd import driver
+    import synth
+
+    name, model_blocks, epochs = CALIB_WORKLOADS[args.workload]
+    c = getattr(synth, name)
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    nb, ns = args.calib_blocks, args.calib_samples
+    W = []
+    for b in range(nb):
+        g = torch.Generator(device=dev)
+        g.manual_seed(1000 + b)
+        shapes = synth.block_weight_shapes(c)
+        W.append([(torch.randn(shapes[n], generator=g, device=dev) * synth.WEIGHT_STD)
+                  .to(torch.bfloat16) for n in synth.WEIGHT_NAMES])
+    xs = synth.stack_samples_device(c, ns, dev)
+    d = omq.BlockDesc(T=c.T, d=c.d, n_q=c.n_q, n_kv=c.n_kv, head_dim=c.head_dim, F=c.F,
+                      wbits=c.wbits, abits=c.abits, ffn_only=c.ffn_only, group=c.group,
+                      eps=c.eps, rope_theta=c.rope_theta, lr_lwc=c.lr_lwc, lr_let=c.lr_let)
+
+    def on_block(b, x, th):
+        print("block %d calibrated" % b, flush=True)
+
+    # a short warm run (one block, 2 samples, 1 epoch) so the timed run starts warm
+    driver.calibrate(d, W[:1], xs[:2], 1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    res = driver.calibrate(d, W, xs, epochs, on_block=on_block)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_block = wall / nb
+    steps_per_block = ns * epochs
+    model_h = per_block * model_blocks / 3600.0
+    sps = steps_per_block / per_block
+    tflops = step_flops(c) * sps / 1e12
+    out = {
+        "metric": "whole-model OmniQuant calibration time, LLaMA-7B-shaped W4A4 (32 blocks, "
+                  "%d samples x %d epochs per block), 1 GPU" % (ns, epochs),
+        "value": round(model_h, 4), "unit": "hours", "n_gpus": 1, "steps": nb, "warmup": 1,
+        "ms_per_step": round(per_block * 1e3, 1), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "T": c.T, "d": c.d, "F": c.F, "wbits": c.wbits,
+                   "abits": c.abits, "samples": ns, "epochs": epochs, "blocks_timed": nb,
+                   "model_blocks": model_blocks, "optimizer": "adamw", "batch": 1},
+        "seconds_per_block": [round(s, 3) for s in res.seconds],
+        "calib_steps_per_s": round(sps, 3),
+        "extrapolation": "measured seconds per block x %d blocks" % model_blocks,
+        "roofline": {"kernel": "whole calibration step (every kernel of the step)",
+                     "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -257,7 +325,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama7b_block_w4a4",
                     choices=list(workloads()) + list(DECODE_WORKLOADS) +
-                    list(EXPORT_WORKLOADS))
+                    list(EXPORT_WORKLOADS) + list(CALIB_WORKLOADS))
+    ap.add_argument("--calib-blocks", type=int, default=2,
+                    help="blocks timed by the whole-model calibration workload")
+    ap.add_argument("--calib-samples", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -279,6 +350,9 @@ def main():
         return
     if args.workload in EXPORT_WORKLOADS:
         export_main(args)
+        return
+    if args.workload in CALIB_WORKLOADS:
+        calib_main(args)
         return
 
     if args.copy_calibration:
@@ -306,17 +380,9 @@ def main():
     dt_ = omq.BlockDesc(T=c.T, d=c.d, n_q=c.n_q, n_kv=c.n_kv, head_dim=c.head_dim, F=c.F,
                         wbits=c.wbits, abits=c.abits, ffn_only=c.ffn_only, group=c.group, eps=c.eps,
                         rope_theta=c.rope_theta, lr_lwc=c.lr_lwc, lr_let=c.lr_let, timer=timer)
-    offs, n_lwc, total = omq.block_theta_layout(d)
+    from post_quantization_amd import driver
     # initial parameters: clipping logits 4.0, s = 1, delta = 0, s_a = 1
-    th0 = np.ones(total, np.float32)
-    th0[:n_lwc] = 4.0
-    ends = list(offs[1:]) + [total]
-    for j, (a, b) in enumerate(zip(offs, ends)):
-        if a >= n_lwc and (j - offs.index(n_lwc)) % 2 == 1 and b - a > 0:
-            th0[a:b] = 0.0                       # the delta entries
-    if not c.ffn_only and c.abits < 16:
-        th0[offs[-1]:] = 1.0                     # s_a
-    theta = torch.from_numpy(th0).to(dev)
+    theta = driver.init_theta(d, dev)
     dtheta = torch.zeros_like(theta)
     m = torch.zeros_like(theta)
     v = torch.zeros_like(theta)

@@ -190,6 +190,22 @@ def stack_inputs(c: BlockCfg, n_blocks: int, n_samples: int):
     return blocks, xs
 
 
+def stack_samples_device(c: BlockCfg, n_samples: int, device, seed: int = 0):
+    """n_samples calibration samples [n, T, d] bf16 drawn on the device (for the
+    full-size throughput runs, where the numpy draws of stack_inputs take minutes):
+    the same recipe (N(0, 1), the block_inputs outlier channels scaled by U(lo, hi)
+    per sample) from torch's seeded generator; not the values stack_inputs gives."""
+    import torch
+    ch = torch.as_tensor(rng(c.cfg, 1002).choice(c.d, size=c.n_out, replace=False),
+                         device=device)
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1000003 + int(c.cfg))
+    x = torch.randn(n_samples, c.T, c.d, generator=g, device=device, dtype=torch.float32)
+    fac = torch.rand(n_samples, 1, c.n_out, generator=g, device=device) * (c.out_hi - c.out_lo)
+    x[:, :, ch] *= fac + c.out_lo
+    return x.to(torch.bfloat16)
+
+
 def reduced(c, **kw):
     """The same workload at other sizes (parity cases the oracle finishes fast)."""
     return replace(c, **kw)

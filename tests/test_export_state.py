@@ -1,6 +1,7 @@
-"""CPU checks of the export helpers: the parameter-vector names follow the
+"""CPU checks of the export and driver helpers: the parameter-vector names follow the
 library's packed layout (and the oracle's), and the saved calibration state and
-exported tensors survive a save / load round trip."""
+exported tensors survive a save / load round trip, and the driver's starting
+parameters are the oracle's."""
 import numpy as np
 import pytest
 import torch
@@ -39,3 +40,16 @@ def test_state_round_trip(tmp_path):
     assert abs(meta["lr_let"] - 1e-2) < 1e-9
     for a, b in ((th, th2), (m, m2), (v, v2)):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("c", [synth.BLOCK_CFG4, synth.BLOCK_CFG5_W2, synth.FFN_CFG3_W3,
+                               synth.BLOCK_CFG4_W2G128])
+def test_driver_initial_parameters(c):
+    """The multi-block driver starts every block from the oracle's initial
+    parameters (logits 4, s = 1, delta = 0, s_a = 1) in the packed layout."""
+    from post_quantization_amd import driver
+    d = omq.BlockDesc(T=c.T, d=c.d, n_q=c.n_q, n_kv=c.n_kv, head_dim=c.head_dim, F=c.F,
+                      wbits=c.wbits, abits=c.abits, ffn_only=c.ffn_only, group=c.group)
+    shapes = synth.block_weight_shapes(c)
+    want = ob.pack(c, shapes, ob.init_theta(c, shapes))
+    assert np.array_equal(driver.init_theta(d, "cpu").numpy(), want)
