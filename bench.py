@@ -116,8 +116,6 @@ def decode_main(args):
     import torch
     import post_quantization_amd as omq
     import synth
-    from oracle import export as ex
-    from oracle import quant
 
     T = DECODE_WORKLOADS[args.workload]
     c = synth.BLOCK_CFG4
@@ -168,6 +166,7 @@ def decode_main(args):
     tok_s = T * 1000.0 / (ms_block * 32)
     cpu = None
     if not args.no_cpu_baseline:
+        from oracle import export as ex
         t0 = time.perf_counter()
         for n, N, K, words, h, z, codes in layers:
             ex.wa16_linear(Xs[K].float().cpu().numpy(), ex.pack_codes(codes.cpu().numpy(), 4),
