@@ -5,10 +5,11 @@
 // In LDS both operands are held K-contiguous, the layout the matrix cores read:
 // a lane of v_mfma_f32_32x32x16_bf16 holds 8 consecutive k of one row of A and 8
 // consecutive k of one column of B^T.  An operand stored K-major in HBM ("T",
-// [K x M] with M contiguous) is loaded as 4 k-rows x 8 contiguous elements per
-// thread (coalesced row segments) and transposed in registers with byte
-// permutes on its way into LDS, so no product of the backward needs a
-// transposed copy in HBM.
+// [K x M] with M contiguous) is copied into LDS in that layout and transposed by
+// the LDS read itself (ds_read_b64_tr_b16) when every tile is whole, or loaded as
+// 4 k-rows x 8 contiguous elements per thread and transposed in registers with
+// byte permutes on its way into LDS otherwise, so no product of the backward needs
+// a transposed copy in HBM.
 //
 // Tile 128 x 128 x 64, 256 threads = 4 waves in a 2 x 2 grid, each wave 64 x 64 as
 // 2 x 2 MFMA 32x32x16 blocks (64 float accumulators per lane).  Global loads are
@@ -168,21 +169,95 @@ OMQ_DEV void dma_tile(const uint16_t* P, int64_t ld, int64_t row0, int64_t k0, u
   }
 }
 
+// K-major tiles in LDS are [64 k-rows][R] bf16, the tile as it lies in HBM, with the
+// 16-byte chunk index of k-row kr XOR-swizzled by ((kr & 3) << 1) | ((kr & 1) << 3):
+// a transposing read of one 16-lane group touches 4 consecutive k-rows x 32 bytes,
+// which then fall on distinct banks, and so do the 16-lane group reading the other
+// 32 bytes of the same rows.
+template <int R>
+OMQ_DEV int ldsT_idx(int kr, int col) {
+  static_assert(R >= 128, "the swizzle spans 16 chunks");
+  return kr * R + ((((col >> 3) ^ (((kr & 3) << 1) | ((kr & 1) << 3)))) << 3) + (col & 7);
+}
+
+// Direct global -> LDS copy of a full 64 x R tile of a K-major operand ([K x rows],
+// rows contiguous): one wave instruction fills 1 KB = 1024 / (2R) k-rows, lane l at
+// byte 16 l, so lane l fetches the chunk the swizzle places at its slot.
+template <int R, int NW>
+OMQ_DEV void dma_tile_t(const uint16_t* P, int64_t ld, int64_t col0, int64_t k0, uint16_t* S,
+                        int wid, int lane) {
+  constexpr int CPR = R / 8;                       // 16-byte chunks per k-row
+  constexpr int RPI = 64 / CPR;                    // k-rows per wave instruction
+  constexpr int NI = BK / RPI;                     // instructions per tile
+  static_assert(NI % NW == 0, "k-row blocks must divide over the waves");
+#pragma unroll
+  for (int i = 0; i < NI / NW; ++i) {
+    const int b = wid + NW * i;
+    const int kr = b * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ (((kr & 3) << 1) | ((kr & 1) << 3));
+    __builtin_amdgcn_global_load_lds(
+        (const void*)(P + (k0 + kr) * ld + col0 + c * 8),
+        (__attribute__((address_space(3))) void*)(S + b * RPI * R), 16, 0, 0);
+  }
+}
+
+// direct copy of one operand tile: K-contiguous (R rows x 64) or K-major (64 x R)
+template <int TR, int R, int NW>
+OMQ_DEV void dma_copy(const uint16_t* P, int64_t ld, int64_t r0, int64_t k0, uint16_t* S, int wid,
+                      int lane) {
+  if constexpr (TR) dma_tile_t<R, NW>(P, ld, r0, k0, S, wid, lane);
+  else dma_tile<R, NW>(P, ld, r0, k0, S, wid, lane);
+}
+
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(8))) short i16x8;
+
+// Matrix-core fragment (8 consecutive k of one row, in the lane order of
+// v_mfma_f32_32x32x16_bf16: row rb + (lane & 31), k kb + 8 (lane >> 5) + 0..7) of a
+// K-major LDS tile, from two transposing reads.  In each 16-lane group the read
+// hands lane i element j of the 4-element chunk that lane 4j + i/4 addressed, at
+// position i % 4; so lane 4j + q of the group addresses k-row j, columns 4q..4q+3
+// of its 16 rows, and lane i receives 4 consecutive k of row i.
+template <int R>
+OMQ_DEV bf16x8 tr_frag(const uint16_t* S, int rb, int kb, int lane) {
+  const int G = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
+  const int kr = kb + 8 * (G >> 1) + j;
+  const int col = rb + 16 * (G & 1) + 4 * q;
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(S + ldsT_idx<R>(kr, col)));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(S + ldsT_idx<R>(kr + 4, col)));
+  const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // wait until at most N vector-memory operations of this wave are outstanding
 template <int N>
 OMQ_DEV void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Straight-through epilogue variants, fixed at compile time so the per-element
+// arithmetic is straight-line code: EPI = mode | let << 2 | xf << 4, with mode 1 the
+// weight side (rows = output channels, x = the weights, column partials of the LET
+// scale) and mode 2 the activation side (rows = tokens, x = the activations, dL/dx
+// written, column partials of the LET pair); let 0 none, 1 divide (activations),
+// 2 multiply (weights); xf: x stored in fp32 (else bf16).  0 = no epilogue.
+constexpr int kLetNone = 0, kLetDiv = 1, kLetMul = 2;
+constexpr int epi_code(int mode, int let, int xf) { return mode | (let << 2) | (xf << 4); }
+
 // BM x BN tile, WM x WN waves, each wave (BM/WM) x (BN/WN) as 32x32 MFMA blocks.
-// DMA: K-contiguous operands are copied straight into LDS (the launcher only sets
-// it when every tile is full and the operands are 16-byte aligned); K-major
-// operands are always staged through registers.
+// DMA: both operands are copied straight into LDS (the launcher only sets it when
+// every tile is full and the operands are 16-byte aligned), K-major ones read back
+// through the transposing LDS read; otherwise both are staged through registers.
 template <int BM, int BN, int WM, int WN, int TA, int TB, int EPI, int DMA>
 __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m, int tiles_n) {
   constexpr int NT = WM * WN * 64, NW = WM * WN;
   constexpr int FM = BM / WM / 32, FN = BN / WN / 32;   // MFMA blocks per wave
-  constexpr bool kDmaA = DMA && !TA, kDmaB = DMA && !TB;
+  constexpr bool kDmaA = DMA, kDmaB = DMA;
+  static_assert(EPI == 0 || (BM == 128 && BN == 128 && WM * WN == 4),
+                "straight-through epilogue tile");
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * LDP];
   uint16_t (*As)[BM * LDP] = reinterpret_cast<uint16_t (*)[BM * LDP]>(smem);
   uint16_t (*Bs)[BN * LDP] = reinterpret_cast<uint16_t (*)[BN * LDP]>(smem + 2 * BM * LDP);
@@ -201,14 +276,6 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
 
   Stage<TA, BM, NT> sa;
   Stage<TB, BN, NT> sb;
-  // register-staged loads a wave issues per K step (they stay in flight across a step)
-  constexpr int kStaged = (kDmaA ? 0 : (TA ? 4 : 1) * Stage<TA, BM, NT>::kN) +
-                          (kDmaB ? 0 : (TB ? 4 : 1) * Stage<TB, BN, NT>::kN);
-  // the vmcnt waits below count on every wave issuing exactly kStaged staged loads
-  static_assert(!DMA || ((kDmaA || Stage<TA, BM, NT>::kUnits % NT == 0) &&
-                         (kDmaB || Stage<TB, BN, NT>::kUnits % NT == 0)),
-                "staged tiles must divide evenly over the threads");
-
   f32x16 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -217,25 +284,67 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // Pipeline per K step: start the copies of the next tile into the other LDS
-  // buffer (direct for DMA operands, register-staged tiles loaded one step earlier
-  // otherwise), issue the staged loads two tiles ahead, then run the MFMAs with the
-  // fragments of each 16-k slice read one slice ahead; wait for the direct copies
-  // and meet at one barrier.
+  // The straight-through epilogue reads x for
+  // each of the RW rows a wave finishes, 2 columns per lane, in batches of RB rows
+  // fetched two batches ahead of their use.
+  constexpr int kMode = EPI & 3, kLet = (EPI >> 2) & 3;
+  constexpr bool kXF = (EPI >> 4) & 1;
+  static_assert(EPI == 0 || (kMode == 1 && kLet != kLetDiv && !kXF) ||
+                    (kMode == 2 && kLet != kLetMul), "epilogue variant");
+  constexpr int RW = BM / 4;                      // epilogue rows per wave
+  constexpr int RB = 8;                           // rows per batch
+  constexpr int XR = kXF ? 2 : 1;                 // 32-bit words of x per lane and row
+  const int64_t gn = n0 + 2 * lane;               // the epilogue lane's two columns
+  const int64_t wr0 = m0 + wid * RW;              // first epilogue row of this wave
+  // direct copies imply whole tiles: no row or column bounds in the epilogue
+  constexpr bool kFull = DMA;
+  auto fetch_x = [&](int b, uint32_t (&xb)[RB][XR]) {
+    if constexpr (EPI != 0) {
+      const SteEpi& e = g.ste;
+      const bool colv = kFull || gn < N;          // N is a multiple of 8
+#pragma unroll
+      for (int q = 0; q < RB; ++q) {
+        const int64_t gm = wr0 + b * RB + q;      // wave-uniform
+#pragma unroll
+        for (int w = 0; w < XR; ++w) xb[q][w] = 0u;
+        if (kFull || gm < M) {
+          const int sg = (e.nseg > 1 && gm >= e.seg_end[0]) + (e.nseg > 2 && gm >= e.seg_end[1]);
+          const int64_t lr = gm - (sg == 0 ? 0 : e.seg_end[sg - 1]);
+          // the row's 2-column words start at column n0; lane l reads word l
+          const uint32_t* xr = reinterpret_cast<const uint32_t*>(
+              reinterpret_cast<const char*>(e.xseg[sg]) + (lr * e.ldx + n0) * (kXF ? 4 : 2));
+          if (colv) {
+            if constexpr (kXF) {
+              const uint2 t = reinterpret_cast<const uint2*>(xr)[lane];
+              xb[q][0] = t.x;
+              xb[q][1] = t.y;
+            } else {
+              xb[q][0] = xr[lane];
+            }
+          }
+        }
+      }
+    }
+  };
+
+  // Pipeline per K step.  Direct copies: the next tile is copied into the other LDS
+  // buffer while this one is consumed.  Register staging: the next tile (loaded one
+  // step earlier) is stored into the other buffer and the tile after it is loaded.
+  // 128 x 128 tiles read every fragment of the buffer first and then run the MFMAs;
+  // 256 x 256 tiles (twice the fragments per wave) read each 16-k slice one slice
+  // ahead of its MFMAs.  One barrier per step.
   const int nk = (int)((ke - kb + BK - 1) / BK);
   if (nk > 0) {
-    if (kDmaA) dma_tile<BM, NW>(A, g.lda, m0, kb, As[0], wid, lane);
+    if (kDmaA) dma_copy<TA, BM, NW>(A, g.lda, m0, kb, As[0], wid, lane);
     else { sa.load(A, g.lda, M, m0, kb, ke, tid); sa.store(As[0], tid); }
-    if (kDmaB) dma_tile<BN, NW>(B, g.ldb, n0, kb, Bs[0], wid, lane);
+    if (kDmaB) dma_copy<TB, BN, NW>(B, g.ldb, n0, kb, Bs[0], wid, lane);
     else { sb.load(B, g.ldb, N, n0, kb, ke, tid); sb.store(Bs[0], tid); }
     if (nk > 1) {
       if (!kDmaA) sa.load(A, g.lda, M, m0, kb + BK, ke, tid);
       if (!kDmaB) sb.load(B, g.ldb, N, n0, kb + BK, ke, tid);
     }
   }
-  if constexpr (kDmaA || kDmaB) {
-    if (nk > 1) wait_vmem<kStaged>(); else wait_vmem<0>();
-  }
+  if constexpr (DMA) wait_vmem<0>();
   __syncthreads();
   const int fr = lane & 31, fk = (lane >> 5) * 8;
   const int ar = wm * (BM / WM) + fr, br = wn * (BN / WN) + fr;
@@ -243,12 +352,12 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
     const int buf = kt & 1;
     const uint16_t* Ab = As[buf];
     const uint16_t* Bb = Bs[buf];
-    // next tile into the other buffer; staged loads two tiles ahead
+    // next tile into the other buffer (staged: the tile after it into registers)
     auto issue_next = [&]() {
       if (kt + 1 < nk) {
         const int64_t k1 = kb + (int64_t)(kt + 1) * BK;
-        if (kDmaA) dma_tile<BM, NW>(A, g.lda, m0, k1, As[buf ^ 1], wid, lane);
-        if (kDmaB) dma_tile<BN, NW>(B, g.ldb, n0, k1, Bs[buf ^ 1], wid, lane);
+        if (kDmaA) dma_copy<TA, BM, NW>(A, g.lda, m0, k1, As[buf ^ 1], wid, lane);
+        if (kDmaB) dma_copy<TB, BN, NW>(B, g.ldb, n0, k1, Bs[buf ^ 1], wid, lane);
         if (!kDmaA) sa.store(As[buf ^ 1], tid);
         if (!kDmaB) sb.store(Bs[buf ^ 1], tid);
         if (kt + 2 < nk) {
@@ -258,29 +367,30 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
         }
       }
     };
-    if constexpr (DMA) {
-      // copies first, then the fragments of each 16-k slice read one slice ahead
-      // of their MFMAs
+    // fragment i of A / j of B for the 16-k slice kk
+    auto fa = [&](int i, int kk) -> bf16x8 {
+      if constexpr (DMA && TA) return tr_frag<BM>(Ab, wm * (BM / WM) + i * 32, kk * 16, lane);
+      else return *reinterpret_cast<const bf16x8*>(&Ab[lds_idx(ar + i * 32, kk * 16 + fk)]);
+    };
+    auto fb = [&](int j, int kk) -> bf16x8 {
+      if constexpr (DMA && TB) return tr_frag<BN>(Bb, wn * (BN / WN) + j * 32, kk * 16, lane);
+      else return *reinterpret_cast<const bf16x8*>(&Bb[lds_idx(br + j * 32, kk * 16 + fk)]);
+    };
+    if constexpr (DMA && BM > 128) {
       issue_next();
       bf16x8 af[2][FM], bf[2][FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[0][i] = *reinterpret_cast<const bf16x8*>(&Ab[lds_idx(ar + i * 32, fk)]);
+      for (int i = 0; i < FM; ++i) af[0][i] = fa(i, 0);
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bf[0][j] = *reinterpret_cast<const bf16x8*>(&Bb[lds_idx(br + j * 32, fk)]);
+      for (int j = 0; j < FN; ++j) bf[0][j] = fb(j, 0);
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {
         const int cu = kk & 1;
         if (kk + 1 < BK / 16) {
 #pragma unroll
-          for (int i = 0; i < FM; ++i)
-            af[cu ^ 1][i] = *reinterpret_cast<const bf16x8*>(
-                &Ab[lds_idx(ar + i * 32, (kk + 1) * 16 + fk)]);
+          for (int i = 0; i < FM; ++i) af[cu ^ 1][i] = fa(i, kk + 1);
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
-            bf[cu ^ 1][j] = *reinterpret_cast<const bf16x8*>(
-                &Bb[lds_idx(br + j * 32, (kk + 1) * 16 + fk)]);
+          for (int j = 0; j < FN; ++j) bf[cu ^ 1][j] = fb(j, kk + 1);
         }
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -290,17 +400,13 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
                                                                 0, 0, 0);
       }
     } else {
-      // every fragment of this buffer read first, then the next tile's stores and
-      // loads, then the MFMAs while those are in flight
       bf16x8 af[BK / 16][FM], bf[BK / 16][FN];
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-          af[kk][i] = *reinterpret_cast<const bf16x8*>(&Ab[lds_idx(ar + i * 32, kk * 16 + fk)]);
+        for (int i = 0; i < FM; ++i) af[kk][i] = fa(i, kk);
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          bf[kk][j] = *reinterpret_cast<const bf16x8*>(&Bb[lds_idx(br + j * 32, kk * 16 + fk)]);
+        for (int j = 0; j < FN; ++j) bf[kk][j] = fb(j, kk);
       }
       issue_next();
 #pragma unroll
@@ -312,10 +418,9 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk][i], bf[kk][j], acc[i][j],
                                                                 0, 0, 0);
     }
-    // the direct copies into the other buffer must land before the barrier; the
-    // staged loads of the tile after next may stay in flight
-    if constexpr (kDmaA || kDmaB) {
-      if (kt + 2 < nk) wait_vmem<kStaged>(); else wait_vmem<0>();
+    // the direct copies into the other buffer must land before the barrier
+    if constexpr (DMA) {
+      if (kt + 1 < nk) wait_vmem<0>();
     }
     __syncthreads();
   }
@@ -328,43 +433,18 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
     // forward's in-range decision from x and the row's (h, z), reduces the per-row
     // partials (g_h, sum g (1 - in)) over the tile's 128 columns, accumulates the
     // per-column partials over its rows, and for token rows writes dL/dx (through
-    // the LET) into C.
-    static_assert(BM == 128 && BN == 128 && WM * WN == 4, "straight-through epilogue tile");
+    // the LET) into C.  Rows go in batches of 8: the batch's gradients are read
+    // from LDS first, its 8 rows are then independent chains of arithmetic, and
+    // their partials are written last.
     float* T = reinterpret_cast<float*>(smem);     // [128][128] fp32 = the whole buffer
     const SteEpi& e = g.ste;
     const bool pass = e.nbits >= 16;
     const float Q = pass ? 0.f : (float)((1 << e.nbits) - 1);
-    const int esz = e.x_dt == OMQ_F32 ? 4 : 2;
-    const int64_t gn = n0 + 2 * lane;             // this lane's two columns
-    const bool colv = gn < N;                     // N is a multiple of 8
-    constexpr int RW = BM / 4;                    // rows per wave
-    const int64_t wr0 = m0 + wid * RW;            // first row of this wave
-    // x is fetched 8 rows at a time, one batch ahead of its use (the first batch
-    // before the accumulators go through LDS); the per-row h, z and bias-fold
-    // scalars come from one lane-indexed load each (lane q holds row q).
-    constexpr int RB = 8;
-    auto fetch = [&](int b, uint32_t (&xa)[RB], uint32_t (&xa2)[RB]) {
-#pragma unroll
-      for (int q = 0; q < RB; ++q) {
-        const int64_t gm = wr0 + b * RB + q;
-        xa[q] = 0u;
-        xa2[q] = 0u;
-        if (gm < M && colv) {
-          const int sg = (e.nseg > 1 && gm >= e.seg_end[0]) + (e.nseg > 2 && gm >= e.seg_end[1]);
-          const int64_t lr = gm - (sg == 0 ? 0 : e.seg_end[sg - 1]);
-          const char* xr = reinterpret_cast<const char*>(e.xseg[sg]) + lr * e.ldx * esz;
-          if (e.x_dt == OMQ_F32) {
-            const uint2 t = *reinterpret_cast<const uint2*>(reinterpret_cast<const float*>(xr) + gn);
-            xa[q] = t.x;
-            xa2[q] = t.y;
-          } else {
-            xa[q] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(xr) + gn);
-          }
-        }
-      }
-    };
-    uint32_t xa[RB], xa2[RB], xn[RB], xn2[RB];
-    fetch(0, xa, xa2);
+    const bool colv = gn < N;
+    // x of the first two batches, in flight while the accumulators are parked
+    uint32_t x0[RB][XR], x1[RB][XR], x2[RB][XR];
+    fetch_x(0, x0);
+    fetch_x(1, x1);
     const int64_t rme = wr0 + (lane & (RW - 1));
     const bool rmv = rme < M;
     const int64_t hz = e.grouped ? rme * tiles_n + tn : rme;
@@ -372,8 +452,8 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
     const float z_l = (!pass && rmv) ? e.z[hz] : 0.f;
     const float v_l = (e.rowvec && rmv) ? e.rowvec[rme] : 0.f;
     float s_c[2] = {1.f, 1.f}, d_c[2] = {0.f, 0.f};
-    if (colv && e.let_mode != OMQ_LET_NONE) { s_c[0] = e.s[gn]; s_c[1] = e.s[gn + 1]; }
-    if (colv && e.let_mode == OMQ_LET_DIV && e.delta) {
+    if (colv && kLet != kLetNone) { s_c[0] = e.s[gn]; s_c[1] = e.s[gn + 1]; }
+    if (colv && kLet == kLetDiv && e.delta) {
       d_c[0] = e.delta[gn];
       d_c[1] = e.delta[gn + 1];
     }
@@ -392,80 +472,117 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
     const float rh_l = 1.f / h_l;
     float ca0[2] = {0.f, 0.f}, ca1[2] = {0.f, 0.f};
     float* Cp = g.C + bz * g.strideC;
+#pragma unroll 1
     for (int b = 0; b < RW / RB; ++b) {
       if (wr0 + b * RB >= M) break;                // wave-uniform
-      if (b + 1 < RW / RB) fetch(b + 1, xn, xn2);
+      if (b + 2 < RW / RB) fetch_x(b + 2, x2);
+      float gv[RB][2], xv[RB][2], xt[RB][2], xd[RB][2], u[RB][2], rr[RB][2];
+      float hh[RB], zz[RB], vr[RB];
+#pragma unroll
+      for (int q = 0; q < RB; ++q) {
+        const float2 t = *reinterpret_cast<const float2*>(&T[(wid * RW + b * RB + q) * BN + 2 * lane]);
+        const bool ok = kFull || (colv && wr0 + b * RB + q < M);
+        gv[q][0] = ok ? t.x : 0.f;
+        gv[q][1] = ok ? t.y : 0.f;
+      }
+      // x~ and the rounding of x~ / h by the reciprocal product for every element
+      // of the batch; an element whose product lies within |u| 2^-20 of a
+      // half-integer (or is not finite) takes the exact quotient below
+      bool near = false;
 #pragma unroll
       for (int q = 0; q < RB; ++q) {
         const int rw = b * RB + q;
-        const int64_t gm = wr0 + rw;
-        if (gm >= M) break;                        // wave-uniform
-        const float hh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(h_l), rw));
+        hh[q] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(h_l), rw));
         const float rhh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rh_l), rw));
-        const float zz = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z_l), rw));
-        const float vr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v_l), rw));
-        const float2 gv2 = *reinterpret_cast<const float2*>(&T[(wid * RW + rw) * BN + 2 * lane]);
-        const float gvv[2] = {gv2.x, gv2.y};
-        float xv[2];
-        if (e.x_dt == OMQ_F32) {
-          xv[0] = __uint_as_float(xa[q]);
-          xv[1] = __uint_as_float(xa2[q]);
+        zz[q] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z_l), rw));
+        vr[q] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v_l), rw));
+        if constexpr (kXF) {
+          xv[q][0] = __uint_as_float(x0[q][0]);
+          xv[q][1] = __uint_as_float(x0[q][1]);
         } else {
-          xv[0] = __uint_as_float(xa[q] << 16);
-          xv[1] = __uint_as_float(xa[q] & 0xffff0000u);
+          xv[q][0] = __uint_as_float(x0[q][0] << 16);
+          xv[q][1] = __uint_as_float(x0[q][0] & 0xffff0000u);
         }
-        float ph = 0.f, pz = 0.f;
-        if (colv) {
-          float up[2];
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          // x~: exact for MUL / NONE; for DIV within 2 ulp (it enters sums only; the
+          // decisions follow the exact quotient)
+          xd[q][c2] = xv[q][c2] - d_c[c2];
+          if constexpr (kLet == kLetDiv) xt[q][c2] = xd[q][c2] * r_c[c2];
+          else if constexpr (kLet == kLetMul) xt[q][c2] = s_c[c2] * xv[q][c2];
+          else xt[q][c2] = xv[q][c2];
+          u[q][c2] = xt[q][c2] * rhh;
+          rr[q][c2] = rintf(u[q][c2]);
+          near |= !(fabsf(fabsf(u[q][c2] - rr[q][c2]) - 0.5f) > fabsf(u[q][c2]) * 0x1p-20f);
+        }
+      }
+      // (wave-uniform branches: divergent ones would be flattened into a division
+      // for every element)
+      if (!pass && __builtin_amdgcn_ballot_w64(near) != 0) {
+#pragma unroll
+        for (int q = 0; q < RB; ++q)
 #pragma unroll
           for (int c2 = 0; c2 < 2; ++c2) {
-            // x~: exact for MUL / NONE; for DIV within 2 ulp (it only enters sums),
-            // the in-range decision below still follows the exact quotient
-            const float xd = xv[c2] - d_c[c2];
-            float xt = xv[c2];
-            if (e.let_mode == OMQ_LET_DIV) xt = xd * r_c[c2];
-            else if (e.let_mode == OMQ_LET_MUL) xt = s_c[c2] * xv[c2];
-            const float gv = gvv[c2];
-            float gns = gv;
-            if (!pass) {
-              float u;
-              const float rq = (e.let_mode == OMQ_LET_DIV
-                                    ? rint_quot2(xd, s_c[c2], r_c[c2], hh, rhh, u)
-                                    : rint_quot(xt, hh, rhh, u)) + zz;
-              const bool in = (rq >= 0.f) && (rq <= Q);
-              const float qmz = fminf(fmaxf(rq, 0.f), Q) - zz;
-              ph += gv * (qmz - (in ? u : 0.f));
-              pz += in ? 0.f : gv;
-              gns = in ? gv : 0.f;
+            const bool ne =
+                !(fabsf(fabsf(u[q][c2] - rr[q][c2]) - 0.5f) > fabsf(u[q][c2]) * 0x1p-20f);
+            if (__builtin_amdgcn_ballot_w64(ne) != 0) {
+              if (ne) {
+                u[q][c2] = kLet == kLetDiv ? (xd[q][c2] / s_c[c2]) / hh[q] : xt[q][c2] / hh[q];
+                rr[q][c2] = rintf(u[q][c2]);
+              }
             }
-            if (e.col_mode == COL_WEIGHT) {
-              ca0[c2] += gns * xv[c2];
-              ca1[c2] += vr * xv[c2];
-            } else if (e.col_mode == COL_ACT_DIV) {
-              ca0[c2] += gns * (-xt * r_c[c2]);
-              ca1[c2] += gns * (-r_c[c2]);
-            } else if (e.col_mode == COL_ACT_MUL) {
-              ca0[c2] += gns * xv[c2];
-            }
-            up[c2] = e.let_mode == OMQ_LET_DIV ? gns * r_c[c2]
-                     : e.let_mode == OMQ_LET_MUL ? gns * s_c[c2] : gns;
           }
-          if (e.mode == 2)
+      }
+      float ph[RB], pz[RB];
+#pragma unroll
+      for (int q = 0; q < RB; ++q) {
+        ph[q] = 0.f;
+        pz[q] = 0.f;
+        float up[2];
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          const float g1 = gv[q][c2];
+          float gns = g1;
+          if (!pass) {
+            const float rq = rr[q][c2] + zz[q];
+            const bool in = (rq >= 0.f) && (rq <= Q);
+            const float qmz = fminf(fmaxf(rq, 0.f), Q) - zz[q];
+            ph[q] += g1 * (qmz - (in ? u[q][c2] : 0.f));
+            pz[q] += in ? 0.f : g1;
+            gns = in ? g1 : 0.f;
+          }
+          if constexpr (kMode == 1 && kLet == kLetMul) {
+            ca0[c2] += gns * xv[q][c2];
+            ca1[c2] += vr[q] * xv[q][c2];
+          } else if constexpr (kMode == 2 && kLet == kLetDiv) {
+            ca0[c2] += gns * (-xt[q][c2] * r_c[c2]);
+            ca1[c2] += gns * (-r_c[c2]);
+          }
+          up[c2] = kLet == kLetDiv ? gns * r_c[c2] : kLet == kLetMul ? gns * s_c[c2] : gns;
+        }
+        if constexpr (kMode == 2) {
+          const int64_t gm = wr0 + b * RB + q;
+          if (kFull || (gm < M && colv))
             *reinterpret_cast<float2*>(&Cp[gm * g.ldc + gn]) = make_float2(up[0], up[1]);
         }
-        if (!pass) {
-          // the row's gradients are consumed: its LDS row now holds the lanes'
-          // partials (g_h in columns 0..63, out-of-range sum in 64..127)
-          float* tr = &T[(wid * RW + rw) * BN];
-          tr[lane] = ph;
-          tr[64 + lane] = pz;
+      }
+      if (!pass) {
+        // the batch's gradients are consumed: its LDS rows now hold the lanes'
+        // partials (g_h in columns 0..63, out-of-range sum in 64..127)
+#pragma unroll
+        for (int q = 0; q < RB; ++q) {
+          float* tr = &T[(wid * RW + b * RB + q) * BN];
+          tr[lane] = ph[q];
+          tr[64 + lane] = pz[q];
         }
       }
 #pragma unroll
-      for (int q = 0; q < RB; ++q) {
-        xa[q] = xn[q];
-        xa2[q] = xn2[q];
-      }
+      for (int q = 0; q < RB; ++q)
+#pragma unroll
+        for (int w = 0; w < XR; ++w) {
+          x0[q][w] = x1[q][w];
+          x1[q][w] = x2[q][w];
+        }
     }
     if (!pass) {
       // lane l sums row (l & 31)'s 64 partials of kind (l >> 5), starting at a
@@ -480,7 +597,7 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
         e.rowpart[(gm * tiles_n + tn) * 2 + half] = sum;
       }
     }
-    if (e.col_mode != COL_NONE) {
+    if constexpr ((kMode == 1 && kLet == kLetMul) || (kMode == 2 && kLet == kLetDiv)) {
       __syncthreads();                             // every wave is done reading T
       T[(wid * 2 + 0) * BN + 2 * lane] = ca0[0];
       T[(wid * 2 + 0) * BN + 2 * lane + 1] = ca0[1];
@@ -565,13 +682,23 @@ void launch_cfg(const Gemm& g, hipStream_t st) {
                        tiles_n);
 }
 
-// both operands K-contiguous, every tile full: direct-to-LDS operand copies
+// every tile full: direct-to-LDS operand copies, for any operand layouts
 template <int BM, int BN, int WM, int WN>
-void launch_nn_dma(const Gemm& g, hipStream_t st) {
+void launch_dma(const Gemm& g, hipStream_t st) {
   const int tiles_m = (int)(g.M / BM), tiles_n = (int)(g.N / BN);
   const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)g.batch), block(WM * WN * 64);
-  hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, 0, 0, 0, 1>), grid, block, 0, st, g, tiles_m,
-                     tiles_n);
+  if (!g.ta && !g.tb)
+    hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, 0, 0, 0, 1>), grid, block, 0, st, g, tiles_m,
+                       tiles_n);
+  else if (!g.ta && g.tb)
+    hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, 0, 1, 0, 1>), grid, block, 0, st, g, tiles_m,
+                       tiles_n);
+  else if (g.ta && !g.tb)
+    hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, 1, 0, 0, 1>), grid, block, 0, st, g, tiles_m,
+                       tiles_n);
+  else
+    hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, 1, 1, 0, 1>), grid, block, 0, st, g, tiles_m,
+                       tiles_n);
 }
 
 // Direct LDS copies need whole tiles (no bounds checks), whole K steps and 16-byte
@@ -586,16 +713,48 @@ bool dma_fits(const Gemm& g, int BM, int BN) {
 // 64-column slabs), for the two layouts the backward uses
 constexpr int kSteBM = 128, kSteBN = 128, kSteWM = 2, kSteWN = 2;
 
-void launch_ste(const Gemm& g, hipStream_t st) {
+template <int EPI>
+void launch_ste_x(const Gemm& g, hipStream_t st) {
+  constexpr int TA = (EPI & 3) == 1;             // weight side: dY^T is the K-major A
   const int tiles_m = (int)((g.M + kSteBM - 1) / kSteBM);
   const int tiles_n = (int)((g.N + kSteBN - 1) / kSteBN);
   const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)g.batch), block(kSteWM * kSteWN * 64);
-  if (g.ta)
-    hipLaunchKernelGGL((k_gemm_bf16<kSteBM, kSteBN, kSteWM, kSteWN, 1, 1, 1, 0>), grid, block, 0, st,
-                       g, tiles_m, tiles_n);
+  if (dma_fits(g, kSteBM, kSteBN))
+    hipLaunchKernelGGL((k_gemm_bf16<kSteBM, kSteBN, kSteWM, kSteWN, TA, 1, EPI, 1>), grid, block, 0,
+                       st, g, tiles_m, tiles_n);
   else
-    hipLaunchKernelGGL((k_gemm_bf16<kSteBM, kSteBN, kSteWM, kSteWN, 0, 1, 1, 0>), grid, block, 0, st,
-                       g, tiles_m, tiles_n);
+    hipLaunchKernelGGL((k_gemm_bf16<kSteBM, kSteBN, kSteWM, kSteWN, TA, 1, EPI, 0>), grid, block, 0,
+                       st, g, tiles_m, tiles_n);
+}
+
+// The backward's two layouts: the weight side (dW = dY^T X^, both K-major, x = the
+// bf16 weights, LET multiply with the scale's column partials, or no LET) and the
+// activation side (dX = dY W^, W^ K-major, x = the activations, LET divide with the
+// pair's column partials, or no LET).
+hipError_t launch_ste(const Gemm& g, hipStream_t st) {
+  const SteEpi& e = g.ste;
+  const bool xf = e.x_dt == OMQ_F32;
+  if (e.mode == 1 && g.ta && g.tb && !xf) {
+    if (e.let_mode == OMQ_LET_MUL && e.col_mode == COL_WEIGHT)
+      launch_ste_x<epi_code(1, kLetMul, 0)>(g, st);
+    else if (e.let_mode == OMQ_LET_NONE && e.col_mode == COL_NONE)
+      launch_ste_x<epi_code(1, kLetNone, 0)>(g, st);
+    else
+      return hipErrorInvalidValue;
+  } else if (e.mode == 2 && !g.ta && g.tb) {
+    if (e.let_mode == OMQ_LET_DIV && e.col_mode == COL_ACT_DIV) {
+      if (xf) launch_ste_x<epi_code(2, kLetDiv, 1)>(g, st);
+      else launch_ste_x<epi_code(2, kLetDiv, 0)>(g, st);
+    } else if (e.let_mode == OMQ_LET_NONE && e.col_mode == COL_NONE) {
+      if (xf) launch_ste_x<epi_code(2, kLetNone, 1)>(g, st);
+      else launch_ste_x<epi_code(2, kLetNone, 0)>(g, st);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 // float32 operands (the fp32 path): 64 x 64 tiles, 4 x 4 outputs per thread.
@@ -662,19 +821,15 @@ void gemm_ste_extents(int64_t rows, int64_t cols, int64_t* nslabs, int64_t* ntil
 
 hipError_t launch_gemm(const Gemm& g, hipStream_t st) {
   if (g.M == 0 || g.N == 0 || g.batch == 0) return hipSuccess;
-  if (g.dt == OMQ_BF16 && g.ste.mode != 0) {
-    if (!g.tb) return hipErrorInvalidValue;   // the backward's layouts: (T, T) and (N, T)
-    launch_ste(g, st);
-    return hipGetLastError();
-  }
+  if (g.dt == OMQ_BF16 && g.ste.mode != 0) return launch_ste(g, st);
   if (g.dt == OMQ_BF16) {
     // 256 x 256 tiles halve the operand traffic per flop; they pay once there are
     // enough of them to keep every CU busy for two rounds
     const int64_t big_tiles = (g.M / 256) * (g.N / 256) * g.batch;
-    if (!g.ta && !g.tb && big_tiles >= 512 && dma_fits(g, 256, 256))
-      launch_nn_dma<256, 256, 2, 4>(g, st);
-    else if (!g.ta && !g.tb && dma_fits(g, 128, 128))
-      launch_nn_dma<128, 128, 2, 2>(g, st);
+    if (big_tiles >= 512 && dma_fits(g, 256, 256))
+      launch_dma<256, 256, 2, 4>(g, st);
+    else if (dma_fits(g, 128, 128))
+      launch_dma<128, 128, 2, 2>(g, st);
     else
       launch_cfg<128, 128, 2, 2>(g, st);
   } else {

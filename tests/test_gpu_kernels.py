@@ -242,6 +242,8 @@ def test_act_quant_passthrough_and_let_apply():
     (4096, 8192, 512, "bf16", 0, 0), (256, 256, 4104, "bf16", 0, 0),
     (200, 136, 328, "bf16", 0, 1), (200, 136, 328, "bf16", 1, 0), (200, 136, 328, "bf16", 1, 1),
     (2048, 4096, 2048, "bf16", 1, 1), (2048, 4096, 11008, "bf16", 0, 1),
+    (4096, 8192, 512, "bf16", 1, 0), (4096, 8192, 256, "bf16", 0, 1),
+    (4096, 8192, 320, "bf16", 1, 1), (384, 640, 192, "bf16", 1, 1),
     (70, 50, 36, "f32", 1, 1)])
 def test_gemm(M, N, K, dt, ta, tb):
     log("gemm", M, N, K, dt, ta, tb)
