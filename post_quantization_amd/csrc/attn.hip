@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kT) void k_flash_fwd(FlashFwd a) {
   const int hq = blockIdx.x / nqb;
   const int qb = nqb - 1 - (int)(blockIdx.x % nqb);       // longest rows first
   const int hk = hq / a.grp;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), h = lane >> 5, l32 = lane & 31;
   const int64_t q0 = (int64_t)qb * 128;
   const int64_t q = q0 + 32 * w + l32;
   const int64_t qc = min(q, T - 1);
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(kT) void k_flash_bwd_dkdv(FlashBwd a) {
   const int nkb = (int)((T + 127) / 128);
   const int g = blockIdx.x / nkb;
   const int kb = (int)(blockIdx.x % nkb);                 // longest (kb = 0) first
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), h = lane >> 5, l32 = lane & 31;
   const int64_t k0 = (int64_t)kb * 128;
   const int64_t key = k0 + 32 * w + l32;
   const int64_t kc = min(key, T - 1);
@@ -450,7 +450,7 @@ __global__ __launch_bounds__(kT) void k_flash_bwd_dq(FlashBwd a) {
   const int hq = blockIdx.x / nqb;
   const int qb = nqb - 1 - (int)(blockIdx.x % nqb);
   const int hk = hq / a.grp;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), h = lane >> 5, l32 = lane & 31;
   const int64_t q0 = (int64_t)qb * 128;
   const int64_t q = q0 + 32 * w + l32;
   const int64_t qc = min(q, T - 1);

@@ -129,6 +129,11 @@ OMQ_DEV float rint_quot2(float xd, float s, float rs, float h, float rh, float& 
   return r;
 }
 
+// index of the calling wave in its block, in a scalar register (it is uniform
+// within the wave, which the compiler cannot tell from threadIdx.x >> 6): rows,
+// offsets and addresses derived from it then stay scalar
+OMQ_DEV int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 OMQ_DEV RowQ row_step(float M, float m, float gamma, float beta, int nbits) {
   RowQ r;
   r.Q = (float)((1 << nbits) - 1);

@@ -47,7 +47,7 @@ OMQ_DEV void dequant8(uint32_t w, float h, float z, float out[8]) {
 // - delta_o[n]) / s_o[n]; with s_o, also h_out = h / s_o for the row's steps.
 __global__ __launch_bounds__(256) void k_fold_linear(DeployFold a) {
   const int lane = threadIdx.x & 63;
-  const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t n = (int64_t)blockIdx.x * 4 + wave_id();
   if (n >= a.N) return;
   const int P = 32 / a.nbits;
   const int64_t nw = (a.K + P - 1) / P;
@@ -95,7 +95,7 @@ constexpr int kBatch = 4;
 
 __global__ __launch_bounds__(kWaves * 64) void k_w4a16_gemm(DeployGemm a) {
   __shared__ float red[kWaves][32][33];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), hf = lane >> 5, l32 = lane & 31;
   const int64_t n0 = (int64_t)blockIdx.x * 32, t0 = (int64_t)blockIdx.y * 32;
   const int64_t n = n0 + l32, t = t0 + l32;
   const bool nv = n < a.N, tv = t < a.T;

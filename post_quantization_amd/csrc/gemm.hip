@@ -262,10 +262,7 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
   uint16_t (*As)[BM * LDP] = reinterpret_cast<uint16_t (*)[BM * LDP]>(smem);
   uint16_t (*Bs)[BN * LDP] = reinterpret_cast<uint16_t (*)[BN * LDP]>(smem + 2 * BM * LDP);
 
-  // the wave index is uniform within the wave: keeping it scalar keeps every
-  // per-wave row and address computation in scalar registers
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tid = threadIdx.x, lane = tid & 63, wid = wave_id();
   const int wm = wid / WN, wn = wid % WN;
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);

@@ -16,7 +16,7 @@ constexpr int kThreads = 256;
 
 OMQ_DEV float block_sum(float v, float* sh) {
   v = wave_sum(v);
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wid = wave_id();
   __syncthreads();
   if (lane == 0) sh[wid] = v;
   __syncthreads();

@@ -36,7 +36,7 @@ template <int XDT>
 __global__ __launch_bounds__(kThreads) void k_rowquant_fwd(RowQuantFwd a) {
   const int64_t r = blockIdx.x;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wid = tid >> 6;
+  const int lane = tid & 63, wid = wave_id();
   const char* xr = reinterpret_cast<const char*>(a.x) + r * a.ldx * (XDT == OMQ_F32 ? 4 : 2);
   const int64_t cols = a.cols;
 
@@ -119,7 +119,7 @@ template <int XDT, int NCH>
 __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_reg(RowQuantFwd a) {
   const int64_t r = blockIdx.x;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wid = tid >> 6;
+  const int lane = tid & 63, wid = wave_id();
   const char* xr = reinterpret_cast<const char*>(a.x) + r * a.ldx * (XDT == OMQ_F32 ? 4 : 2);
   const int64_t cols = a.cols;
   float xt[NCH][4];
@@ -234,7 +234,7 @@ OMQ_DEV void load8f(const float* p, int64_t c, int n, float v[8]) {
 template <int XDT, int NC>
 __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_wave(RowQuantFwd a) {
   const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t r = (int64_t)blockIdx.x * 4 + wave_id();
   if (r >= a.rows) return;
   const char* xr = reinterpret_cast<const char*>(a.x) + r * a.ldx * (XDT == OMQ_F32 ? 4 : 2);
   const int64_t cols = a.cols;
@@ -332,7 +332,7 @@ template <int XDT>
 __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_g128(RowQuantFwd a) {
   const int lane = threadIdx.x & 63;
   const int64_t G = a.cols / 128;
-  const int64_t p = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 6) * 4 + (lane >> 4);
+  const int64_t p = (int64_t)blockIdx.x * 16 + wave_id() * 4 + (lane >> 4);
   const bool pv = p < a.rows * G;             // every lane takes part in the shuffles
   const int64_t r = pv ? p / G : 0, k = pv ? p % G : 0;
   const int64_t c = k * 128 + (lane & 15) * 8;
@@ -409,7 +409,7 @@ template <int XDT>
 __global__ __launch_bounds__(kThreads) void k_rowquant_bwd_tile(RowQuantBwd a, int rows_per_tile,
                                                                 float* rowpart, float* colpart) {
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wid = tid >> 6;
+  const int lane = tid & 63, wid = wave_id();
   const int64_t c0 = (int64_t)blockIdx.x * kSlab;
   const int64_t r0 = (int64_t)blockIdx.y * rows_per_tile;
   const int64_t cols = a.cols, rows = a.rows;
