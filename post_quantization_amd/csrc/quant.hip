@@ -586,20 +586,32 @@ __global__ __launch_bounds__(kThreads) void k_colpart_reduce(const float* part2,
   if (out1) out1[c] = (accumulate ? out1[c] : 0.f) + s1;
 }
 
-// row finalize: one thread per row.  LWC-logit gradients and the max/min scatter.
-template <int XDT>
+// row finalize: LPR lanes per quantizer row sum its per-slab partials (coalesced
+// reads, then a shuffle reduction), one of them finishes the row: LWC-logit
+// gradients and the max/min scatter.
+template <int XDT, int LPR>
 __global__ __launch_bounds__(kThreads) void k_rowquant_bwd_rows(RowQuantBwd a, int nslabs,
                                                                 const float* rowpart) {
   // quantizer rows: rows, or (row, group) pairs p = row * ng + group
   const int64_t ng = a.group > 0 ? a.cols / 128 : 1;
-  const int64_t p = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (p >= a.rows * ng) return;
-  const int64_t r = p / ng;
+  const int64_t p = ((int64_t)blockIdx.x * kThreads + threadIdx.x) / LPR;
+  const int sub = (int)(threadIdx.x % LPR);
+  const bool valid = p < a.rows * ng;
   float gh = 0.f, gzs = 0.f;
-  for (int s = 0; s < nslabs; ++s) {
-    gh += rowpart[(p * nslabs + s) * 2 + 0];
-    gzs += rowpart[(p * nslabs + s) * 2 + 1];
+  if (valid) {
+    for (int s = sub; s < nslabs; s += LPR) {
+      const float2 v = *reinterpret_cast<const float2*>(&rowpart[(p * nslabs + s) * 2]);
+      gh += v.x;
+      gzs += v.y;
+    }
   }
+#pragma unroll
+  for (int o = LPR / 2; o > 0; o >>= 1) {
+    gh += __shfl_xor(gh, o);
+    gzs += __shfl_xor(gzs, o);
+  }
+  if (!valid || sub != 0) return;
+  const int64_t r = p / ng;
   const char* xr = reinterpret_cast<const char*>(a.x) + r * a.ldx * (XDT == OMQ_F32 ? 4 : 2);
   auto xval = [&](int64_t c) -> float {
     return XDT == OMQ_F32 ? reinterpret_cast<const float*>(xr)[c]
@@ -868,13 +880,24 @@ hipError_t launch_ste_rowfinal(const RowQuantBwd& a, int nslabs, const float* ro
   hipError_t e = hipSuccess;
   if (a.nbits < 16 && a.rows > 0) {
     const int64_t n = a.rows * (a.group > 0 ? a.cols / 128 : 1);
-    dim3 g2((unsigned)((n + kThreads - 1) / kThreads));
-    if (a.x_dt == OMQ_F32)
-      hipLaunchKernelGGL(k_rowquant_bwd_rows<OMQ_F32>, g2, dim3(kThreads), 0, st, a,
-                         (int)nslabs, rowpart);
-    else
-      hipLaunchKernelGGL(k_rowquant_bwd_rows<OMQ_BF16>, g2, dim3(kThreads), 0, st, a,
-                         (int)nslabs, rowpart);
+    // one slab per row: a lane per row; else 16 lanes share a row's slabs
+    if (nslabs == 1) {
+      dim3 g2((unsigned)((n + kThreads - 1) / kThreads));
+      if (a.x_dt == OMQ_F32)
+        hipLaunchKernelGGL((k_rowquant_bwd_rows<OMQ_F32, 1>), g2, dim3(kThreads), 0, st, a,
+                           (int)nslabs, rowpart);
+      else
+        hipLaunchKernelGGL((k_rowquant_bwd_rows<OMQ_BF16, 1>), g2, dim3(kThreads), 0, st, a,
+                           (int)nslabs, rowpart);
+    } else {
+      dim3 g2((unsigned)((n * 16 + kThreads - 1) / kThreads));
+      if (a.x_dt == OMQ_F32)
+        hipLaunchKernelGGL((k_rowquant_bwd_rows<OMQ_F32, 16>), g2, dim3(kThreads), 0, st, a,
+                           (int)nslabs, rowpart);
+      else
+        hipLaunchKernelGGL((k_rowquant_bwd_rows<OMQ_BF16, 16>), g2, dim3(kThreads), 0, st, a,
+                           (int)nslabs, rowpart);
+    }
     e = hipGetLastError();
   }
   return e;
