@@ -231,7 +231,9 @@ OMQ_DEV void load8f(const float* p, int64_t c, int n, float v[8]) {
   }
 }
 
-template <int XDT, int NC>
+// FULL: every 512-column chunk of the row is whole (cols is a multiple of 512), so
+// no column bounds are checked.
+template <int XDT, int NC, int LET, bool FULL>
 __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_wave(RowQuantFwd a) {
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * 4 + wave_id();
@@ -244,8 +246,8 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_wave(RowQuantFwd a) {
 #pragma unroll
   for (int k = 0; k < NC; ++k) {
     const int64_t c = ((int64_t)k * 64 + lane) * 8;
-    if (c < cols) {
-      const int n = c + 8 <= cols ? 8 : 4;          // rows are multiples of 4 long
+    if (FULL || c < cols) {
+      const int n = FULL || c + 8 <= cols ? 8 : 4;  // rows are multiples of 4 long
       float v[8];
       if (n == 8) {
         load8(xr, XDT, c, v);
@@ -253,13 +255,13 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_wave(RowQuantFwd a) {
         load4(xr, XDT, c, v);
         v[4] = v[5] = v[6] = v[7] = 0.f;
       }
-      if (a.let_mode == OMQ_LET_DIV) {
+      if constexpr (LET == OMQ_LET_DIV) {
         float sv[8], dv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         load8f(a.s, c, n, sv);
         if (a.delta) load8f(a.delta, c, n, dv);
 #pragma unroll
         for (int j = 0; j < 8; ++j) xt[k][j] = (v[j] - dv[j]) / sv[j];
-      } else if (a.let_mode == OMQ_LET_MUL) {
+      } else if constexpr (LET == OMQ_LET_MUL) {
         float sv[8];
         load8f(a.s, c, n, sv);
 #pragma unroll
@@ -277,12 +279,22 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_wave(RowQuantFwd a) {
       }
     }
   }
+  // the lane's max / min with the lowest column among equal values (columns are
+  // visited in increasing order)
+  if constexpr (FULL) {
+    vmax = vmin = xt[0][0];
+    imax = imin = lane * 8;
+  }
 #pragma unroll
   for (int k = 0; k < NC; ++k) {
     const int64_t c = ((int64_t)k * 64 + lane) * 8;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      if (c + j < cols) {
+      if constexpr (FULL) {
+        if (k == 0 && j == 0) continue;
+        if (xt[k][j] > vmax) { vmax = xt[k][j]; imax = (int)(c + j); }
+        if (xt[k][j] < vmin) { vmin = xt[k][j]; imin = (int)(c + j); }
+      } else if (c + j < cols) {
         if (xt[k][j] > vmax || imax == 0x7fffffff) { vmax = xt[k][j]; imax = (int)(c + j); }
         if (xt[k][j] < vmin || imin == 0x7fffffff) { vmin = xt[k][j]; imin = (int)(c + j); }
       }
@@ -301,24 +313,76 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_wave(RowQuantFwd a) {
     if (a.amin) a.amin[r] = imin;
     if (a.bias_out) a.bias_out[r] = (a.bias ? a.bias[r] : 0.f) + dot;
   }
+  // rint(x~ / h) for every element by the reciprocal product, then the exact
+  // quotient for the (rare) elements whose product lies within |u| 2^-20 of a
+  // half-integer or is not finite, behind wave-uniform branches (divergent ones
+  // would be flattened into a division for every element)
   const float rh = 1.f / q.h;
+  bool near = false;
+#pragma unroll
+  for (int k = 0; k < NC; ++k)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float u = xt[k][j] * rh;
+      const float rr = rintf(u);
+      near |= !(fabsf(fabsf(u - rr) - 0.5f) > fabsf(u) * 0x1p-20f);
+      xt[k][j] = rr;                                // xt now holds rint(x~ / h)
+    }
+  if (__builtin_amdgcn_ballot_w64(near) != 0) {
+    // recompute the chunk's x~ exactly where needed
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      const int64_t c = ((int64_t)k * 64 + lane) * 8;
+      bool nk = false;
+      float v[8];
+      if (FULL || c < cols) {
+        const int n = FULL || c + 8 <= cols ? 8 : 4;
+        if (n == 8) {
+          load8(xr, XDT, c, v);
+        } else {
+          load4(xr, XDT, c, v);
+          v[4] = v[5] = v[6] = v[7] = 0.f;
+        }
+        float sv[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+        float dv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if constexpr (LET != OMQ_LET_NONE) load8f(a.s, c, n, sv);
+        if constexpr (LET == OMQ_LET_DIV) {
+          if (a.delta) load8f(a.delta, c, n, dv);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float x1 = LET == OMQ_LET_DIV ? (v[j] - dv[j]) / sv[j]
+                           : LET == OMQ_LET_MUL ? sv[j] * v[j] : v[j];
+          v[j] = x1;
+          const float u = x1 * rh;
+          const float rr = rintf(u);
+          nk |= !(fabsf(fabsf(u - rr) - 0.5f) > fabsf(u) * 0x1p-20f);
+        }
+      }
+      if (__builtin_amdgcn_ballot_w64(nk) != 0) {
+        if (nk) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) xt[k][j] = rintf(v[j] / q.h);
+        }
+      }
+    }
+  }
 #pragma unroll
   for (int k = 0; k < NC; ++k) {
     const int64_t c = ((int64_t)k * 64 + lane) * 8;
-    if (c < cols) {
+    if (FULL || c < cols) {
       float o[8];
       uint32_t cw[2] = {0u, 0u};
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        float u;
-        const float rr = rint_quot(xt[k][j], q.h, rh, u) + q.z;
+        const float rr = xt[k][j] + q.z;
         const float qq = fminf(fmaxf(rr, 0.f), q.Q);
         o[j] = (qq - q.z) * q.h;
         cw[j >> 2] |= ((uint32_t)qq) << (8 * (j & 3));
       }
       store4(a.out, a.out_dt, r * a.ldo + c, o);
       if (a.codes) *reinterpret_cast<uint32_t*>(a.codes + r * cols + c) = cw[0];
-      if (c + 8 <= cols) {
+      if (FULL || c + 8 <= cols) {
         store4(a.out, a.out_dt, r * a.ldo + c + 4, o + 4);
         if (a.codes) *reinterpret_cast<uint32_t*>(a.codes + r * cols + c + 4) = cw[1];
       }
@@ -770,12 +834,27 @@ bool launch_fwd_wave(const RowQuantFwd& a, hipStream_t st) {
   if (XDT == OMQ_BF16 && (a.ldx % 8)) return false;
   const int64_t nc = (a.cols + 511) / 512;
   dim3 grid((unsigned)((a.rows + 3) / 4));
-#define OMQ_FWD_WAVE(N)                                                                   \
-  if (nc <= N) {                                                                          \
-    hipLaunchKernelGGL((k_rowquant_fwd_wave<XDT, N>), grid, dim3(kThreads), 0, st, a);   \
-    return true;                                                                          \
+#define OMQ_FWD_WAVE_L(N, F)                                                                  \
+  if (a.let_mode == OMQ_LET_DIV)                                                              \
+    hipLaunchKernelGGL((k_rowquant_fwd_wave<XDT, N, OMQ_LET_DIV, F>), grid, dim3(kThreads), 0, \
+                       st, a);                                                                \
+  else if (a.let_mode == OMQ_LET_MUL)                                                         \
+    hipLaunchKernelGGL((k_rowquant_fwd_wave<XDT, N, OMQ_LET_MUL, F>), grid, dim3(kThreads), 0, \
+                       st, a);                                                                \
+  else                                                                                        \
+    hipLaunchKernelGGL((k_rowquant_fwd_wave<XDT, N, OMQ_LET_NONE, F>), grid, dim3(kThreads), 0,\
+                       st, a);
+#define OMQ_FWD_WAVE(N)                                                                       \
+  if (nc <= N) {                                                                              \
+    if (a.cols == N * 512) {                                                                  \
+      OMQ_FWD_WAVE_L(N, true)                                                                 \
+    } else {                                                                                  \
+      OMQ_FWD_WAVE_L(N, false)                                                                \
+    }                                                                                         \
+    return true;                                                                              \
   }
   OMQ_FWD_WAVE(1) OMQ_FWD_WAVE(2) OMQ_FWD_WAVE(4) OMQ_FWD_WAVE(8)
+#undef OMQ_FWD_WAVE_L
 #undef OMQ_FWD_WAVE
   return false;
 }
