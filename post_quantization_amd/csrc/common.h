@@ -57,6 +57,23 @@ OMQ_DEV void store4(void* base, int dt, int64_t idx, const float v[4]) {
   }
 }
 
+// 8 consecutive values as one 16-byte (bf16) or two 16-byte (fp32) stores: whole
+// cache lines per wave instruction
+OMQ_DEV void store8(void* base, int dt, int64_t idx, const float v[8]) {
+  if (dt == OMQ_F32) {
+    float* p = reinterpret_cast<float*>(base) + idx;
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  } else {
+    uint4 t;
+    t.x = pack_bf16(v[0], v[1]);
+    t.y = pack_bf16(v[2], v[3]);
+    t.z = pack_bf16(v[4], v[5]);
+    t.w = pack_bf16(v[6], v[7]);
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(base) + idx) = t;
+  }
+}
+
 // gamma = sigmoid(a) evaluated in double and rounded once to float.
 OMQ_DEV float sigmoid_f32(float a) { return (float)(1.0 / (1.0 + exp(-(double)a))); }
 

@@ -390,6 +390,173 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_wave(RowQuantFwd a) {
   }
 }
 
+// Whole rows (cols = 512 NC), one wave per row, the row staged in LDS: the wave
+// copies its row straight from HBM into its own LDS slot, then reads it twice:
+// pass 1 forms x~ and its max / min (lowest column among equal values), pass 2
+// rounds and stores.  Registers hold one 8-element chunk at a time, so many rows'
+// copies are in flight per compute unit.  For fp32 input pass 1 writes x~ back
+// over the raw value (the LET division happens once per element).  Same results as
+// k_rowquant_fwd_wave.
+template <int XDT, int NC, int LET>
+__global__ __launch_bounds__(kThreads) void k_rowquant_fwd_lds(RowQuantFwd a) {
+  constexpr int ESZ = XDT == OMQ_F32 ? 4 : 2;
+  constexpr int NH = ESZ / 2;                      // 1 KB copies per 8-element chunk
+  __shared__ uint4 slot[4][NC * NH * 64];
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int64_t r = (int64_t)blockIdx.x * 4 + w;
+  if (r >= a.rows) return;
+  uint4* my = slot[w];
+  {
+    // lane l's 16-byte piece h of chunk k lands at my[(k NH + h) 64 + l]
+    const char* xr = reinterpret_cast<const char*>(a.x) + r * a.ldx * ESZ;
+#pragma unroll
+    for (int k = 0; k < NC; ++k)
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(xr + ((int64_t)k * 64 + lane) * 8 * ESZ + 16 * h),
+            (__attribute__((address_space(3))) void*)(my + (k * NH + h) * 64), 16, 0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  // x~ of chunk k for this lane (8 consecutive columns c .. c+7)
+  auto chunk = [&](int k, float (&xt)[8], float& dot, bool first) {
+    const int64_t c = ((int64_t)k * 64 + lane) * 8;
+    float v[8];
+    if constexpr (XDT == OMQ_F32) {
+      const uint4 t0 = my[(2 * k) * 64 + lane], t1 = my[(2 * k + 1) * 64 + lane];
+      const uint32_t wv[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = __uint_as_float(wv[j]);
+      if (!first) {                                // pass 1 stored x~ itself
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xt[j] = v[j];
+        return;
+      }
+    } else {
+      const uint4 t0 = my[k * 64 + lane];
+      const uint32_t wv[4] = {t0.x, t0.y, t0.z, t0.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[2 * q] = __uint_as_float(wv[q] << 16);
+        v[2 * q + 1] = __uint_as_float(wv[q] & 0xffff0000u);
+      }
+    }
+    if constexpr (LET == OMQ_LET_DIV) {
+      float sv[8], dv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      load8f(a.s, c, 8, sv);
+      if (a.delta) load8f(a.delta, c, 8, dv);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xt[j] = (v[j] - dv[j]) / sv[j];
+    } else if constexpr (LET == OMQ_LET_MUL) {
+      float sv[8];
+      load8f(a.s, c, 8, sv);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xt[j] = sv[j] * v[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xt[j] = v[j];
+    }
+    if (first && a.fold_delta) {
+      float fv[8];
+      load8f(a.fold_delta, c, 8, fv);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dot = fmaf(fv[j], v[j], dot);
+    }
+    if constexpr (XDT == OMQ_F32) {
+      if (first) {
+        my[(2 * k) * 64 + lane] =
+            make_uint4(__float_as_uint(xt[0]), __float_as_uint(xt[1]), __float_as_uint(xt[2]),
+                       __float_as_uint(xt[3]));
+        my[(2 * k + 1) * 64 + lane] =
+            make_uint4(__float_as_uint(xt[4]), __float_as_uint(xt[5]), __float_as_uint(xt[6]),
+                       __float_as_uint(xt[7]));
+      }
+    }
+  };
+  // pass 1: max / min with the lowest column among equal values (columns are
+  // visited in increasing order; chunk 0 seeds the lane's values)
+  float vmax, vmin, dot = 0.f;
+  int imax, imin;
+  {
+    float xt[8];
+    chunk(0, xt, dot, true);
+    vmax = vmin = xt[0];
+    imax = imin = lane * 8;
+#pragma unroll
+    for (int j = 1; j < 8; ++j) {
+      if (xt[j] > vmax) { vmax = xt[j]; imax = lane * 8 + j; }
+      if (xt[j] < vmin) { vmin = xt[j]; imin = lane * 8 + j; }
+    }
+  }
+  // (two chunks per iteration: unrolling all of them would hoist every chunk's loads
+  // and take the registers the occupancy needs)
+#pragma unroll 2
+  for (int k = 1; k < NC; ++k) {
+    float xt[8];
+    chunk(k, xt, dot, true);
+    const int c = (k * 64 + lane) * 8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (xt[j] > vmax) { vmax = xt[j]; imax = c + j; }
+      if (xt[j] < vmin) { vmin = xt[j]; imin = c + j; }
+    }
+  }
+  wave_argmax(vmax, imax);
+  wave_argmin(vmin, imin);
+  dot = wave_sum(dot);
+  const float gamma = a.a_gamma ? sigmoid_f32(a.a_gamma[r]) : 1.f;
+  const float beta = a.a_beta ? sigmoid_f32(a.a_beta[r]) : 1.f;
+  const RowQ q = row_step(vmax, vmin, gamma, beta, a.nbits);
+  if (lane == 0) {
+    if (a.h) a.h[r] = q.h;
+    if (a.z) a.z[r] = q.z;
+    if (a.amax) a.amax[r] = imax;
+    if (a.amin) a.amin[r] = imin;
+    if (a.bias_out) a.bias_out[r] = (a.bias ? a.bias[r] : 0.f) + dot;
+  }
+  // pass 2: rint(x~ / h) by the reciprocal product.  u = x~ rh lies within 3 ulp of
+  // the exact quotient, so they can round apart only within |u| 2^-20 of a
+  // half-integer; the test uses the row's bound max|x~| rh 2^-20 >= |u| 2^-20 (a few
+  // more elements take the exact path, none fewer).  A chunk with such an element (or
+  // a non-finite u) takes the exact quotient behind a wave-uniform branch (a
+  // divergent one would be flattened into a division for every element).
+  const float rh = 1.f / q.h;
+  const float thr = fmaxf(fabsf(vmax), fabsf(vmin)) * rh * 0x1p-20f;
+  const bool want_codes = a.codes != nullptr;
+#pragma unroll 2
+  for (int k = 0; k < NC; ++k) {
+    const int64_t c = ((int64_t)k * 64 + lane) * 8;
+    float xt[8], rr[8];
+    chunk(k, xt, dot, false);
+    bool near = false;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float u = xt[j] * rh;
+      rr[j] = rintf(u);
+      near |= !(fabsf(fabsf(u - rr[j]) - 0.5f) > thr);
+    }
+    if (__builtin_amdgcn_ballot_w64(near) != 0) {
+      if (near) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) rr[j] = rintf(xt[j] / q.h);
+      }
+    }
+    float o[8], qq[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      qq[j] = __builtin_amdgcn_fmed3f(rr[j] + q.z, 0.f, q.Q);
+      o[j] = (qq[j] - q.z) * q.h;
+    }
+    store8(a.out, a.out_dt, r * a.ldo + c, o);
+    if (want_codes) {
+      uint32_t cw[2] = {0u, 0u};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) cw[j >> 2] |= ((uint32_t)qq[j]) << (8 * (j & 3));
+      *reinterpret_cast<uint2*>(a.codes + r * a.cols + c) = make_uint2(cw[0], cw[1]);
+    }
+  }
+}
+
 // Group-wise forward (groups of 128 columns): 16 lanes per group with 8 columns
 // each, 4 groups per wave, 16 per block; reductions stay inside each 16-lane group.
 template <int XDT>
@@ -844,16 +1011,27 @@ bool launch_fwd_wave(const RowQuantFwd& a, hipStream_t st) {
   else                                                                                        \
     hipLaunchKernelGGL((k_rowquant_fwd_wave<XDT, N, OMQ_LET_NONE, F>), grid, dim3(kThreads), 0,\
                        st, a);
+#define OMQ_FWD_LDS(N)                                                                        \
+  if (a.let_mode == OMQ_LET_DIV)                                                              \
+    hipLaunchKernelGGL((k_rowquant_fwd_lds<XDT, N, OMQ_LET_DIV>), grid, dim3(kThreads), 0, st, \
+                       a);                                                                    \
+  else if (a.let_mode == OMQ_LET_MUL)                                                         \
+    hipLaunchKernelGGL((k_rowquant_fwd_lds<XDT, N, OMQ_LET_MUL>), grid, dim3(kThreads), 0, st, \
+                       a);                                                                    \
+  else                                                                                        \
+    hipLaunchKernelGGL((k_rowquant_fwd_lds<XDT, N, OMQ_LET_NONE>), grid, dim3(kThreads), 0, st,\
+                       a);
 #define OMQ_FWD_WAVE(N)                                                                       \
   if (nc <= N) {                                                                              \
     if (a.cols == N * 512) {                                                                  \
-      OMQ_FWD_WAVE_L(N, true)                                                                 \
+      OMQ_FWD_LDS(N)                                                                          \
     } else {                                                                                  \
       OMQ_FWD_WAVE_L(N, false)                                                                \
     }                                                                                         \
     return true;                                                                              \
   }
   OMQ_FWD_WAVE(1) OMQ_FWD_WAVE(2) OMQ_FWD_WAVE(4) OMQ_FWD_WAVE(8)
+#undef OMQ_FWD_LDS
 #undef OMQ_FWD_WAVE_L
 #undef OMQ_FWD_WAVE
   return false;
