@@ -115,6 +115,10 @@ struct Unit {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
+// paired causal blocks (a long and a short query or key block per workgroup) are
+// used when that still leaves at least one workgroup per compute unit
+constexpr int64_t kPairMinBlocks = 256;
+
 // 2^x on the transcendental unit (no denormal rescaling: results below 2^-126 are
 // probabilities that vanish against the row sum anyway)
 OMQ_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -130,134 +134,142 @@ OMQ_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 //      two-step softmax, and as the backward's recomputation), O^T += V^T P^T
 //      (A = V^T from LDS, B = P from registers).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kT) void k_flash_fwd(FlashFwd a) {
+__global__ __launch_bounds__(kT) void k_flash_fwd(FlashFwd a, int pair) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * RS];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[2][HD * 64];
   const int64_t T = a.T;
   const int nqb = (int)((T + 127) / 128);
-  const int hq = blockIdx.x / nqb;
-  const int qb = nqb - 1 - (int)(blockIdx.x % nqb);       // longest rows first
+  // pair: the block takes query blocks nqb-1-p and then p (equal work per block
+  // under the causal mask); else query block nqb-1-p alone (longest rows first)
+  const int npb = pair ? (nqb + 1) / 2 : nqb;
+  const int hq = blockIdx.x / npb;
+  const int p = (int)(blockIdx.x % npb);
+  const int nunits = (pair && p != nqb - 1 - p) ? 2 : 1;
   const int hk = hq / a.grp;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), h = lane >> 5, l32 = lane & 31;
-  const int64_t q0 = (int64_t)qb * 128;
-  const int64_t q = q0 + 32 * w + l32;
-  const int64_t qc = min(q, T - 1);
+  for (int u = 0; u < nunits; ++u) {
+    const int qb = u == 0 ? nqb - 1 - p : p;
+    if (u > 0) __syncthreads();                          // LDS of the previous unit
+    const int64_t q0 = (int64_t)qb * 128;
+    const int64_t q = q0 + 32 * w + l32;
+    const int64_t qc = min(q, T - 1);
 
-  bf16x8 qf[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s)
-    qf[s] = *reinterpret_cast<const bf16x8*>(a.Q + qc * a.ldq + hq * HD + 16 * s + 8 * h);
+    bf16x8 qf[8];
+  #pragma unroll
+    for (int s = 0; s < 8; ++s)
+      qf[s] = *reinterpret_cast<const bf16x8*>(a.Q + qc * a.ldq + hq * HD + 16 * s + 8 * h);
 
-  const int64_t kend = min(q0 + 128, T);
-  const int nkb = (int)((kend + 63) / 64);
-  // scaled, masked scores of key block kb for this lane's query
-  auto scores = [&](const uint16_t* Kb, int kb, f32x16 (&sc)[2]) {
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sc[kk][r] = 0.f;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) sc[kk] = mfma(rt_frag(Kb, 32 * kk + l32, s, h), qf[s], sc[kk]);
-    }
-    const int64_t k0 = (int64_t)kb * 64;
-    const bool edge = k0 + 63 > q0 + 32 * w || k0 + 64 > T;   // wave-uniform
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = sc[kk][r] * a.scale2;
-        if (edge) {
-          const int64_t key = k0 + 32 * kk + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (key > q || key >= T) v = kNegInf;
+    const int64_t kend = min(q0 + 128, T);
+    const int nkb = (int)((kend + 63) / 64);
+    // scaled, masked scores of key block kb for this lane's query
+    auto scores = [&](const uint16_t* Kb, int kb, f32x16 (&sc)[2]) {
+  #pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) sc[kk][r] = 0.f;
+  #pragma unroll
+        for (int s = 0; s < 8; ++s) sc[kk] = mfma(rt_frag(Kb, 32 * kk + l32, s, h), qf[s], sc[kk]);
+      }
+      const int64_t k0 = (int64_t)kb * 64;
+      const bool edge = k0 + 63 > q0 + 32 * w || k0 + 64 > T;   // wave-uniform
+  #pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float v = sc[kk][r] * a.scale2;
+          if (edge) {
+            const int64_t key = k0 + 32 * kk + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (key > q || key >= T) v = kNegInf;
+          }
+          sc[kk][r] = v;
         }
-        sc[kk][r] = v;
-      }
-  };
+    };
 
-  // pass 1: log-sum-exp
-  Unit uk, uv;
-  uk.load(a.K, a.ldk, hk * HD, 0, T, tid);
-  uk.store_rows(Ks[0], tid);
-  if (nkb > 1) uk.load(a.K, a.ldk, hk * HD, 64, T, tid);
-  __syncthreads();
-  float m2 = kNegInf, l = 0.f;
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    f32x16 sc[2];
-    scores(Ks[buf], kb, sc);
-    if (kb + 1 < nkb) {
-      uk.store_rows(Ks[buf ^ 1], tid);
-      if (kb + 2 < nkb) uk.load(a.K, a.ldk, hk * HD, (int64_t)(kb + 2) * 64, T, tid);
-    }
-    float mx = kNegInf;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kk][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mn = fmaxf(m2, mx);
-    const float ms = mn == kNegInf ? 0.f : mn;
-    float add = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) add += fast_exp2(sc[kk][r] - ms);
-    l = l * fast_exp2(m2 - ms) + add;
-    m2 = mn;
+    // pass 1: log-sum-exp
+    Unit uk, uv;
+    uk.load(a.K, a.ldk, hk * HD, 0, T, tid);
+    uk.store_rows(Ks[0], tid);
+    if (nkb > 1) uk.load(a.K, a.ldk, hk * HD, 64, T, tid);
     __syncthreads();
-  }
-  l += __shfl_xor(l, 32, 64);
-  const float lse2 = m2 + log2f(l);
-
-  // pass 2: normalized probabilities into O^T += V^T P^T
-  uk.load(a.K, a.ldk, hk * HD, 0, T, tid);
-  uv.load(a.V, a.ldk, hk * HD, 0, T, tid);
-  uk.store_rows(Ks[0], tid);
-  uv.store_transposed(Vt[0], tid);
-  if (nkb > 1) {
-    uk.load(a.K, a.ldk, hk * HD, 64, T, tid);
-    uv.load(a.V, a.ldk, hk * HD, 64, T, tid);
-  }
-  __syncthreads();
-  f32x16 o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    f32x16 sc[2];
-    scores(Ks[buf], kb, sc);
-    if (kb + 1 < nkb) {
-      uk.store_rows(Ks[buf ^ 1], tid);
-      uv.store_transposed(Vt[buf ^ 1], tid);
-      if (kb + 2 < nkb) {
-        uk.load(a.K, a.ldk, hk * HD, (int64_t)(kb + 2) * 64, T, tid);
-        uv.load(a.V, a.ldk, hk * HD, (int64_t)(kb + 2) * 64, T, tid);
+    float m2 = kNegInf, l = 0.f;
+    for (int kb = 0; kb < nkb; ++kb) {
+      const int buf = kb & 1;
+      f32x16 sc[2];
+      scores(Ks[buf], kb, sc);
+      if (kb + 1 < nkb) {
+        uk.store_rows(Ks[buf ^ 1], tid);
+        if (kb + 2 < nkb) uk.load(a.K, a.ldk, hk * HD, (int64_t)(kb + 2) * 64, T, tid);
       }
+      float mx = kNegInf;
+  #pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kk][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mn = fmaxf(m2, mx);
+      const float ms = mn == kNegInf ? 0.f : mn;
+      float add = 0.f;
+  #pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) add += fast_exp2(sc[kk][r] - ms);
+      l = l * fast_exp2(m2 - ms) + add;
+      m2 = mn;
+      __syncthreads();
     }
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sc[kk][r] = fast_exp2(sc[kk][r] - lse2);
-    bf16x8 pf[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) pf[s] = c_frag(sc[s >> 1], 8 * (s & 1));
-#pragma unroll
-    for (int hb = 0; hb < 4; ++hb)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) o[hb] = mfma(tt_frag(Vt[buf], 32 * hb + l32, s, h), pf[s], o[hb]);
+    l += __shfl_xor(l, 32, 64);
+    const float lse2 = m2 + log2f(l);
+
+    // pass 2: normalized probabilities into O^T += V^T P^T
+    uk.load(a.K, a.ldk, hk * HD, 0, T, tid);
+    uv.load(a.V, a.ldk, hk * HD, 0, T, tid);
+    uk.store_rows(Ks[0], tid);
+    uv.store_transposed(Vt[0], tid);
+    if (nkb > 1) {
+      uk.load(a.K, a.ldk, hk * HD, 64, T, tid);
+      uv.load(a.V, a.ldk, hk * HD, 64, T, tid);
+    }
     __syncthreads();
-  }
-  if (q < T) {
-    float* orow = a.O + q * a.ldo + hq * HD;
-#pragma unroll
-    for (int hb = 0; hb < 4; ++hb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<float4*>(orow + 32 * hb + 8 * g + 4 * h) =
-            make_float4(o[hb][4 * g], o[hb][4 * g + 1], o[hb][4 * g + 2], o[hb][4 * g + 3]);
-    if (h == 0) a.lse2[(int64_t)hq * T + q] = lse2;
+    f32x16 o[4];
+  #pragma unroll
+    for (int i = 0; i < 4; ++i)
+  #pragma unroll
+      for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
+    for (int kb = 0; kb < nkb; ++kb) {
+      const int buf = kb & 1;
+      f32x16 sc[2];
+      scores(Ks[buf], kb, sc);
+      if (kb + 1 < nkb) {
+        uk.store_rows(Ks[buf ^ 1], tid);
+        uv.store_transposed(Vt[buf ^ 1], tid);
+        if (kb + 2 < nkb) {
+          uk.load(a.K, a.ldk, hk * HD, (int64_t)(kb + 2) * 64, T, tid);
+          uv.load(a.V, a.ldk, hk * HD, (int64_t)(kb + 2) * 64, T, tid);
+        }
+      }
+  #pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) sc[kk][r] = fast_exp2(sc[kk][r] - lse2);
+      bf16x8 pf[4];
+  #pragma unroll
+      for (int s = 0; s < 4; ++s) pf[s] = c_frag(sc[s >> 1], 8 * (s & 1));
+  #pragma unroll
+      for (int hb = 0; hb < 4; ++hb)
+  #pragma unroll
+        for (int s = 0; s < 4; ++s) o[hb] = mfma(tt_frag(Vt[buf], 32 * hb + l32, s, h), pf[s], o[hb]);
+      __syncthreads();
+    }
+    if (q < T) {
+      float* orow = a.O + q * a.ldo + hq * HD;
+  #pragma unroll
+      for (int hb = 0; hb < 4; ++hb)
+  #pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<float4*>(orow + 32 * hb + 8 * g + 4 * h) =
+              make_float4(o[hb][4 * g], o[hb][4 * g + 1], o[hb][4 * g + 2], o[hb][4 * g + 3]);
+      if (h == 0) a.lse2[(int64_t)hq * T + q] = lse2;
+    }
   }
 }
 
@@ -292,7 +304,7 @@ __global__ __launch_bounds__(kT) void k_attn_bwd_prep(const float* gO, const flo
 // from LDS, B = K / V from registers), P = exp2(S c - lse2), dS = P (dP - D) / sqrt(hd),
 // dV^T += dO^T P and dK^T += Q^T dS (A = transposed Q / dO from LDS, B = P / dS).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kT) void k_flash_bwd_dkdv(FlashBwd a) {
+__global__ __launch_bounds__(kT) void k_flash_bwd_dkdv(FlashBwd a, int pair) {
   __shared__ __attribute__((aligned(16))) uint16_t Qs[2][64 * RS];
   __shared__ __attribute__((aligned(16))) uint16_t Gs[2][64 * RS];
   __shared__ __attribute__((aligned(16))) uint16_t Qt[2][HD * 64];
@@ -301,138 +313,146 @@ __global__ __launch_bounds__(kT) void k_flash_bwd_dkdv(FlashBwd a) {
   __shared__ __attribute__((aligned(16))) float Ds[2][64];
   const int64_t T = a.T;
   const int nkb = (int)((T + 127) / 128);
-  const int g = blockIdx.x / nkb;
-  const int kb = (int)(blockIdx.x % nkb);                 // longest (kb = 0) first
+  // pair: key blocks p and then nkb-1-p (equal causal work per block); else key
+  // block p alone (kb = 0, the longest, first)
+  const int npb = pair ? (nkb + 1) / 2 : nkb;
+  const int g = blockIdx.x / npb;
+  const int p = (int)(blockIdx.x % npb);
+  const int nunits = (pair && p != nkb - 1 - p) ? 2 : 1;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), h = lane >> 5, l32 = lane & 31;
-  const int64_t k0 = (int64_t)kb * 128;
-  const int64_t key = k0 + 32 * w + l32;
-  const int64_t kc = min(key, T - 1);
+  for (int u = 0; u < nunits; ++u) {
+    const int kb = u == 0 ? p : nkb - 1 - p;
+    if (u > 0) __syncthreads();                          // LDS of the previous unit
+    const int64_t k0 = (int64_t)kb * 128;
+    const int64_t key = k0 + 32 * w + l32;
+    const int64_t kc = min(key, T - 1);
 
-  bf16x8 kf[8], vf[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    kf[s] = *reinterpret_cast<const bf16x8*>(a.K + kc * a.ldk + g * HD + 16 * s + 8 * h);
-    vf[s] = *reinterpret_cast<const bf16x8*>(a.V + kc * a.ldk + g * HD + 16 * s + 8 * h);
-  }
-  const int nqb = (int)((T + 63) / 64);
-  const int qb0 = (int)(k0 / 64);
-  const int per = nqb - qb0;                              // query blocks per head
-  const int nit = per * a.grp;
-  auto qbase = [&](int it, int& hq) -> int64_t {
-    hq = g * a.grp + it / per;
-    return (int64_t)(qb0 + it % per) * 64;
-  };
+    bf16x8 kf[8], vf[8];
+  #pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      kf[s] = *reinterpret_cast<const bf16x8*>(a.K + kc * a.ldk + g * HD + 16 * s + 8 * h);
+      vf[s] = *reinterpret_cast<const bf16x8*>(a.V + kc * a.ldk + g * HD + 16 * s + 8 * h);
+    }
+    const int nqb = (int)((T + 63) / 64);
+    const int qb0 = (int)(k0 / 64);
+    const int per = nqb - qb0;                              // query blocks per head
+    const int nit = per * a.grp;
+    auto qbase = [&](int it, int& hq) -> int64_t {
+      hq = g * a.grp + it / per;
+      return (int64_t)(qb0 + it % per) * 64;
+    };
 
-  Unit uq, ug;
-  float lv = 0.f, dv = 0.f;
-  auto load = [&](int it) {
-    int hq;
-    const int64_t q0 = qbase(it, hq);
-    uq.load(a.Q, a.ldq, hq * HD, q0, T, tid);
-    ug.load(a.dO, a.ldq, hq * HD, q0, T, tid);
-    if (tid < 64) {
-      const int64_t qq = min(q0 + tid, T - 1);
-      lv = a.lse2[(int64_t)hq * T + qq];
-      dv = a.D[(int64_t)hq * T + qq];
+    Unit uq, ug;
+    float lv = 0.f, dv = 0.f;
+    auto load = [&](int it) {
+      int hq;
+      const int64_t q0 = qbase(it, hq);
+      uq.load(a.Q, a.ldq, hq * HD, q0, T, tid);
+      ug.load(a.dO, a.ldq, hq * HD, q0, T, tid);
+      if (tid < 64) {
+        const int64_t qq = min(q0 + tid, T - 1);
+        lv = a.lse2[(int64_t)hq * T + qq];
+        dv = a.D[(int64_t)hq * T + qq];
+      }
+    };
+    auto store = [&](int buf) {
+      uq.store_rows(Qs[buf], tid);
+      uq.store_transposed(Qt[buf], tid);
+      ug.store_rows(Gs[buf], tid);
+      ug.store_transposed(Gt[buf], tid);
+      if (tid < 64) {
+        Ls[buf][tid] = lv;
+        Ds[buf][tid] = dv;
+      }
+    };
+    if (nit > 0) {
+      load(0);
+      store(0);
+      if (nit > 1) load(1);
     }
-  };
-  auto store = [&](int buf) {
-    uq.store_rows(Qs[buf], tid);
-    uq.store_transposed(Qt[buf], tid);
-    ug.store_rows(Gs[buf], tid);
-    ug.store_transposed(Gt[buf], tid);
-    if (tid < 64) {
-      Ls[buf][tid] = lv;
-      Ds[buf][tid] = dv;
-    }
-  };
-  if (nit > 0) {
-    load(0);
-    store(0);
-    if (nit > 1) load(1);
-  }
-  __syncthreads();
+    __syncthreads();
 
-  f32x16 dk[4], dvt[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dk[i][r] = 0.f;
-      dvt[i][r] = 0.f;
-    }
-  for (int it = 0; it < nit; ++it) {
-    const int buf = it & 1;
-    int hq;
-    const int64_t q0 = qbase(it, hq);
-    f32x16 sc[2], dp[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
+    f32x16 dk[4], dvt[4];
+  #pragma unroll
+    for (int i = 0; i < 4; ++i)
+  #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        sc[mb][r] = 0.f;
-        dp[mb][r] = 0.f;
+        dk[i][r] = 0.f;
+        dvt[i][r] = 0.f;
       }
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        sc[mb] = mfma(rt_frag(Qs[buf], 32 * mb + l32, s, h), kf[s], sc[mb]);
-        dp[mb] = mfma(rt_frag(Gs[buf], 32 * mb + l32, s, h), vf[s], dp[mb]);
-      }
-    }
-    if (it + 1 < nit) {
-      store(buf ^ 1);
-      if (it + 2 < nit) load(it + 2);
-    }
-    const bool edge = q0 < k0 + 127 || q0 + 64 > T;        // block-uniform
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        const int row0 = 32 * mb + 8 * gg + 4 * h;
-        const float4 L4 = *reinterpret_cast<const float4*>(&Ls[buf][row0]);
-        const float4 D4 = *reinterpret_cast<const float4*>(&Ds[buf][row0]);
-        const float Lr[4] = {L4.x, L4.y, L4.z, L4.w};
-        const float Dr[4] = {D4.x, D4.y, D4.z, D4.w};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int r = 4 * gg + c;
-          float p = fast_exp2(sc[mb][r] * a.scale2 - Lr[c]);
-          if (edge) {
-            const int64_t qr = q0 + row0 + c;
-            if (key > qr || qr >= T) p = 0.f;
-          }
-          sc[mb][r] = p;
-          dp[mb][r] = p * (dp[mb][r] - Dr[c]) * a.scale;
+    for (int it = 0; it < nit; ++it) {
+      const int buf = it & 1;
+      int hq;
+      const int64_t q0 = qbase(it, hq);
+      f32x16 sc[2], dp[2];
+  #pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sc[mb][r] = 0.f;
+          dp[mb][r] = 0.f;
+        }
+  #pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          sc[mb] = mfma(rt_frag(Qs[buf], 32 * mb + l32, s, h), kf[s], sc[mb]);
+          dp[mb] = mfma(rt_frag(Gs[buf], 32 * mb + l32, s, h), vf[s], dp[mb]);
         }
       }
-    bf16x8 pf[4], sf[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      pf[s] = c_frag(sc[s >> 1], 8 * (s & 1));
-      sf[s] = c_frag(dp[s >> 1], 8 * (s & 1));
-    }
-#pragma unroll
-    for (int hb = 0; hb < 4; ++hb)
-#pragma unroll
+      if (it + 1 < nit) {
+        store(buf ^ 1);
+        if (it + 2 < nit) load(it + 2);
+      }
+      const bool edge = q0 < k0 + 127 || q0 + 64 > T;        // block-uniform
+  #pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+  #pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          const int row0 = 32 * mb + 8 * gg + 4 * h;
+          const float4 L4 = *reinterpret_cast<const float4*>(&Ls[buf][row0]);
+          const float4 D4 = *reinterpret_cast<const float4*>(&Ds[buf][row0]);
+          const float Lr[4] = {L4.x, L4.y, L4.z, L4.w};
+          const float Dr[4] = {D4.x, D4.y, D4.z, D4.w};
+  #pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int r = 4 * gg + c;
+            float p = fast_exp2(sc[mb][r] * a.scale2 - Lr[c]);
+            if (edge) {
+              const int64_t qr = q0 + row0 + c;
+              if (key > qr || qr >= T) p = 0.f;
+            }
+            sc[mb][r] = p;
+            dp[mb][r] = p * (dp[mb][r] - Dr[c]) * a.scale;
+          }
+        }
+      bf16x8 pf[4], sf[4];
+  #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        dvt[hb] = mfma(tt_frag(Gt[buf], 32 * hb + l32, s, h), pf[s], dvt[hb]);
-        dk[hb] = mfma(tt_frag(Qt[buf], 32 * hb + l32, s, h), sf[s], dk[hb]);
+        pf[s] = c_frag(sc[s >> 1], 8 * (s & 1));
+        sf[s] = c_frag(dp[s >> 1], 8 * (s & 1));
       }
-    __syncthreads();
-  }
-  if (key < T) {
-    float* krow = a.dK + key * a.lddk + g * HD;
-    float* vrow = a.dV + key * a.lddk + g * HD;
-#pragma unroll
-    for (int hb = 0; hb < 4; ++hb)
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        const int c = 32 * hb + 8 * gg + 4 * h;
-        *reinterpret_cast<float4*>(krow + c) =
-            make_float4(dk[hb][4 * gg], dk[hb][4 * gg + 1], dk[hb][4 * gg + 2], dk[hb][4 * gg + 3]);
-        *reinterpret_cast<float4*>(vrow + c) = make_float4(dvt[hb][4 * gg], dvt[hb][4 * gg + 1],
-                                                           dvt[hb][4 * gg + 2], dvt[hb][4 * gg + 3]);
-      }
+  #pragma unroll
+      for (int hb = 0; hb < 4; ++hb)
+  #pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          dvt[hb] = mfma(tt_frag(Gt[buf], 32 * hb + l32, s, h), pf[s], dvt[hb]);
+          dk[hb] = mfma(tt_frag(Qt[buf], 32 * hb + l32, s, h), sf[s], dk[hb]);
+        }
+      __syncthreads();
+    }
+    if (key < T) {
+      float* krow = a.dK + key * a.lddk + g * HD;
+      float* vrow = a.dV + key * a.lddk + g * HD;
+  #pragma unroll
+      for (int hb = 0; hb < 4; ++hb)
+  #pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          const int c = 32 * hb + 8 * gg + 4 * h;
+          *reinterpret_cast<float4*>(krow + c) =
+              make_float4(dk[hb][4 * gg], dk[hb][4 * gg + 1], dk[hb][4 * gg + 2], dk[hb][4 * gg + 3]);
+          *reinterpret_cast<float4*>(vrow + c) = make_float4(dvt[hb][4 * gg], dvt[hb][4 * gg + 1],
+                                                             dvt[hb][4 * gg + 2], dvt[hb][4 * gg + 3]);
+        }
+    }
   }
 }
 
@@ -441,103 +461,110 @@ __global__ __launch_bounds__(kT) void k_flash_bwd_dkdv(FlashBwd a) {
 // S^T = K Q^T and dP^T = V dO^T (A = K / V rows from LDS, B = Q / dO from
 // registers), dS^T as above, dQ^T += K^T dS^T (A = transposed K from LDS).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kT) void k_flash_bwd_dq(FlashBwd a) {
+__global__ __launch_bounds__(kT) void k_flash_bwd_dq(FlashBwd a, int pair) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * RS];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][64 * RS];
   __shared__ __attribute__((aligned(16))) uint16_t Kt[2][HD * 64];
   const int64_t T = a.T;
   const int nqb = (int)((T + 127) / 128);
-  const int hq = blockIdx.x / nqb;
-  const int qb = nqb - 1 - (int)(blockIdx.x % nqb);
+  // pair: query blocks nqb-1-p and then p (equal causal work per block)
+  const int npb = pair ? (nqb + 1) / 2 : nqb;
+  const int hq = blockIdx.x / npb;
+  const int p = (int)(blockIdx.x % npb);
+  const int nunits = (pair && p != nqb - 1 - p) ? 2 : 1;
   const int hk = hq / a.grp;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), h = lane >> 5, l32 = lane & 31;
-  const int64_t q0 = (int64_t)qb * 128;
-  const int64_t q = q0 + 32 * w + l32;
-  const int64_t qc = min(q, T - 1);
+  for (int u = 0; u < nunits; ++u) {
+    const int qb = u == 0 ? nqb - 1 - p : p;
+    if (u > 0) __syncthreads();                          // LDS of the previous unit
+    const int64_t q0 = (int64_t)qb * 128;
+    const int64_t q = q0 + 32 * w + l32;
+    const int64_t qc = min(q, T - 1);
 
-  bf16x8 qf[8], gf[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    qf[s] = *reinterpret_cast<const bf16x8*>(a.Q + qc * a.ldq + hq * HD + 16 * s + 8 * h);
-    gf[s] = *reinterpret_cast<const bf16x8*>(a.dO + qc * a.ldq + hq * HD + 16 * s + 8 * h);
-  }
-  const float lse = a.lse2[(int64_t)hq * T + qc];
-  const float Dq = a.D[(int64_t)hq * T + qc];
-
-  const int64_t kend = min(q0 + 128, T);
-  const int nkb = (int)((kend + 63) / 64);
-  Unit uk, uv;
-  uk.load(a.K, a.ldk, hk * HD, 0, T, tid);
-  uv.load(a.V, a.ldk, hk * HD, 0, T, tid);
-  uk.store_rows(Ks[0], tid);
-  uk.store_transposed(Kt[0], tid);
-  uv.store_rows(Vs[0], tid);
-  if (nkb > 1) {
-    uk.load(a.K, a.ldk, hk * HD, 64, T, tid);
-    uv.load(a.V, a.ldk, hk * HD, 64, T, tid);
-  }
-  __syncthreads();
-
-  f32x16 dq[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dq[i][r] = 0.f;
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    f32x16 sc[2], dp[2];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sc[kk][r] = 0.f;
-        dp[kk][r] = 0.f;
-      }
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        sc[kk] = mfma(rt_frag(Ks[buf], 32 * kk + l32, s, h), qf[s], sc[kk]);
-        dp[kk] = mfma(rt_frag(Vs[buf], 32 * kk + l32, s, h), gf[s], dp[kk]);
-      }
+    bf16x8 qf[8], gf[8];
+  #pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      qf[s] = *reinterpret_cast<const bf16x8*>(a.Q + qc * a.ldq + hq * HD + 16 * s + 8 * h);
+      gf[s] = *reinterpret_cast<const bf16x8*>(a.dO + qc * a.ldq + hq * HD + 16 * s + 8 * h);
     }
-    if (kb + 1 < nkb) {
-      uk.store_rows(Ks[buf ^ 1], tid);
-      uk.store_transposed(Kt[buf ^ 1], tid);
-      uv.store_rows(Vs[buf ^ 1], tid);
-      if (kb + 2 < nkb) {
-        uk.load(a.K, a.ldk, hk * HD, (int64_t)(kb + 2) * 64, T, tid);
-        uv.load(a.V, a.ldk, hk * HD, (int64_t)(kb + 2) * 64, T, tid);
-      }
+    const float lse = a.lse2[(int64_t)hq * T + qc];
+    const float Dq = a.D[(int64_t)hq * T + qc];
+
+    const int64_t kend = min(q0 + 128, T);
+    const int nkb = (int)((kend + 63) / 64);
+    Unit uk, uv;
+    uk.load(a.K, a.ldk, hk * HD, 0, T, tid);
+    uv.load(a.V, a.ldk, hk * HD, 0, T, tid);
+    uk.store_rows(Ks[0], tid);
+    uk.store_transposed(Kt[0], tid);
+    uv.store_rows(Vs[0], tid);
+    if (nkb > 1) {
+      uk.load(a.K, a.ldk, hk * HD, 64, T, tid);
+      uv.load(a.V, a.ldk, hk * HD, 64, T, tid);
     }
-    const int64_t k0 = (int64_t)kb * 64;
-    const bool edge = k0 + 63 > q0 + 32 * w || k0 + 64 > T;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(sc[kk][r] * a.scale2 - lse);
-        if (edge) {
-          const int64_t kr = k0 + 32 * kk + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (kr > q || kr >= T) p = 0.f;
-        }
-        dp[kk][r] = p * (dp[kk][r] - Dq) * a.scale;
-      }
-    bf16x8 sf[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) sf[s] = c_frag(dp[s >> 1], 8 * (s & 1));
-#pragma unroll
-    for (int hb = 0; hb < 4; ++hb)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) dq[hb] = mfma(tt_frag(Kt[buf], 32 * hb + l32, s, h), sf[s], dq[hb]);
     __syncthreads();
-  }
-  if (q < T) {
-    float* qrow = a.dQ + q * a.lddq + hq * HD;
-#pragma unroll
-    for (int hb = 0; hb < 4; ++hb)
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg)
-        *reinterpret_cast<float4*>(qrow + 32 * hb + 8 * gg + 4 * h) =
-            make_float4(dq[hb][4 * gg], dq[hb][4 * gg + 1], dq[hb][4 * gg + 2], dq[hb][4 * gg + 3]);
+
+    f32x16 dq[4];
+  #pragma unroll
+    for (int i = 0; i < 4; ++i)
+  #pragma unroll
+      for (int r = 0; r < 16; ++r) dq[i][r] = 0.f;
+    for (int kb = 0; kb < nkb; ++kb) {
+      const int buf = kb & 1;
+      f32x16 sc[2], dp[2];
+  #pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sc[kk][r] = 0.f;
+          dp[kk][r] = 0.f;
+        }
+  #pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          sc[kk] = mfma(rt_frag(Ks[buf], 32 * kk + l32, s, h), qf[s], sc[kk]);
+          dp[kk] = mfma(rt_frag(Vs[buf], 32 * kk + l32, s, h), gf[s], dp[kk]);
+        }
+      }
+      if (kb + 1 < nkb) {
+        uk.store_rows(Ks[buf ^ 1], tid);
+        uk.store_transposed(Kt[buf ^ 1], tid);
+        uv.store_rows(Vs[buf ^ 1], tid);
+        if (kb + 2 < nkb) {
+          uk.load(a.K, a.ldk, hk * HD, (int64_t)(kb + 2) * 64, T, tid);
+          uv.load(a.V, a.ldk, hk * HD, (int64_t)(kb + 2) * 64, T, tid);
+        }
+      }
+      const int64_t k0 = (int64_t)kb * 64;
+      const bool edge = k0 + 63 > q0 + 32 * w || k0 + 64 > T;
+  #pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = fast_exp2(sc[kk][r] * a.scale2 - lse);
+          if (edge) {
+            const int64_t kr = k0 + 32 * kk + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (kr > q || kr >= T) p = 0.f;
+          }
+          dp[kk][r] = p * (dp[kk][r] - Dq) * a.scale;
+        }
+      bf16x8 sf[4];
+  #pragma unroll
+      for (int s = 0; s < 4; ++s) sf[s] = c_frag(dp[s >> 1], 8 * (s & 1));
+  #pragma unroll
+      for (int hb = 0; hb < 4; ++hb)
+  #pragma unroll
+        for (int s = 0; s < 4; ++s) dq[hb] = mfma(tt_frag(Kt[buf], 32 * hb + l32, s, h), sf[s], dq[hb]);
+      __syncthreads();
+    }
+    if (q < T) {
+      float* qrow = a.dQ + q * a.lddq + hq * HD;
+  #pragma unroll
+      for (int hb = 0; hb < 4; ++hb)
+  #pragma unroll
+        for (int gg = 0; gg < 4; ++gg)
+          *reinterpret_cast<float4*>(qrow + 32 * hb + 8 * gg + 4 * h) =
+              make_float4(dq[hb][4 * gg], dq[hb][4 * gg + 1], dq[hb][4 * gg + 2], dq[hb][4 * gg + 3]);
+    }
   }
 }
 
@@ -546,7 +573,10 @@ __global__ __launch_bounds__(kT) void k_flash_bwd_dq(FlashBwd a) {
 hipError_t launch_flash_fwd(const FlashFwd& a, hipStream_t st) {
   if (a.T == 0 || a.n_q == 0) return hipSuccess;
   const int nqb = (int)((a.T + 127) / 128);
-  hipLaunchKernelGGL(k_flash_fwd, dim3((unsigned)(nqb * a.n_q)), dim3(kT), 0, st, a);
+  // pair the causal query blocks when that still leaves a block per compute unit
+  const int pair = (int64_t)((nqb + 1) / 2) * a.n_q >= kPairMinBlocks;
+  const int npb = pair ? (nqb + 1) / 2 : nqb;
+  hipLaunchKernelGGL(k_flash_fwd, dim3((unsigned)(npb * a.n_q)), dim3(kT), 0, st, a, pair);
   return hipGetLastError();
 }
 
@@ -561,11 +591,16 @@ hipError_t launch_attn_bwd_prep(const float* gO, const float* O, int64_t ld, int
 hipError_t launch_flash_bwd(const FlashBwd& a, hipStream_t st) {
   if (a.T == 0 || a.n_q == 0) return hipSuccess;
   const int nkb = (int)((a.T + 127) / 128);
-  hipLaunchKernelGGL(k_flash_bwd_dkdv, dim3((unsigned)(nkb * (a.n_q / a.grp))), dim3(kT), 0, st,
-                     a);
+  const int npb = (nkb + 1) / 2;
+  const int n_kv = a.n_q / a.grp;
+  const int pair_kv = (int64_t)npb * n_kv >= kPairMinBlocks;
+  hipLaunchKernelGGL(k_flash_bwd_dkdv, dim3((unsigned)((pair_kv ? npb : nkb) * n_kv)), dim3(kT), 0,
+                     st, a, pair_kv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_flash_bwd_dq, dim3((unsigned)(nkb * a.n_q)), dim3(kT), 0, st, a);
+  const int pair_q = (int64_t)npb * a.n_q >= kPairMinBlocks;
+  hipLaunchKernelGGL(k_flash_bwd_dq, dim3((unsigned)((pair_q ? npb : nkb) * a.n_q)), dim3(kT), 0,
+                     st, a, pair_q);
   return hipGetLastError();
 }
 
