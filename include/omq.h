@@ -186,7 +186,9 @@ int omq_fold_linear(const uint32_t* words, int n_bits, int64_t N, int64_t K, con
  * n * K/128 + k/128); the dequantized value is the calibration's fake-quant weight.
  * X: bf16 [T x K] contiguous; words: uint32 [N x K/8]; bias: float[N] or NULL;
  * Y: float [T x N], overwritten.  K a multiple of 64 (and of 128 for group 128).
- * Built for small T (decode: the weight codes are re-read for every 32 tokens).
+ * Built for small T: up to 8 tokens on the vector units (one wave per output row,
+ * bf16-pair dot products), more on the matrix cores (the weight codes are re-read
+ * for every 32 tokens).  Launches only kernels, so it can be captured in a graph.
  */
 int omq_w4a16_gemm(const void* X, int64_t T, int64_t K, const uint32_t* words, int64_t N,
                    const float* h, const float* z, int64_t group, const float* bias, float* Y,

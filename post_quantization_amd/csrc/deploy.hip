@@ -83,7 +83,8 @@ __global__ __launch_bounds__(256) void k_fold_linear(DeployFold a) {
 }
 
 // Y[T x N] = X[T x K] W_hat^T (+ bias), W_hat from 4-bit packed codes with (h, z)
-// per row or per 128-column group.  Block: 32 output rows x 32 tokens over all of
+// per row or per 128-column group, on the matrix cores (more than 8 tokens).
+// Block: 32 output rows x 32 tokens over all of
 // K, 16 waves taking the 64-column blocks of K in turn, 4 blocks at a time with
 // all their code loads issued before the arithmetic (memory-level parallelism is
 // what a bandwidth-bound small-T product needs).  In a 64-column block, lane half
@@ -158,6 +159,82 @@ __global__ __launch_bounds__(kWaves * 64) void k_w4a16_gemm(DeployGemm a) {
   }
 }
 
+// Y[T x N] for a few tokens (T <= TM) on the vector units: one wave per output row
+// streams the row's packed codes with 16-byte loads (32 columns per lane and load,
+// always inside one 128-column group), dequantizes each pair of columns to bf16
+// exactly as the matrix-core kernel forms its operand, and accumulates bf16-pair
+// dot products with the tokens' bf16 pairs in fp32; one wave reduction per token.
+// A bandwidth-bound product: each code is read once per TM tokens, x comes from the
+// caches.
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+template <int TM>
+__global__ __launch_bounds__(256) void k_w4a16_gemv(DeployGemm a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t n = (int64_t)blockIdx.x * 4 + wave_id();
+  if (n >= a.N) return;
+  const int64_t nw = a.K / 8;                      // words per row
+  const int64_t G = a.group ? a.K / a.group : 1;
+  const uint32_t* wr = a.words + n * nw;
+  const uint32_t* X = reinterpret_cast<const uint32_t*>(a.X);   // bf16 pairs
+  const int64_t xw = a.K / 2;                      // pairs per token
+  float acc[TM];
+#pragma unroll
+  for (int t = 0; t < TM; ++t) acc[t] = 0.f;
+  // one 16-byte chunk (32 columns) of codes into the accumulators
+  auto chunk = [&](const u32x4 cw, int64_t j) {
+    const int64_t col0 = j * 8;
+    const int64_t gi = n * G + (a.group ? col0 / a.group : 0);
+    const float hh = a.h[gi], zz = a.z[gi];
+    // W_hat pairs (columns col0 + 2p, col0 + 2p + 1), p = 0..15
+    uint32_t wp[16];
+    const uint32_t ws[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t lo = ws[s] & 0x0f0f0f0fu, hi = (ws[s] >> 4) & 0x0f0f0f0fu;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const float f0 = ((float)((lo >> (8 * b)) & 0xffu) - zz) * hh;
+        const float f1 = ((float)((hi >> (8 * b)) & 0xffu) - zz) * hh;
+        wp[4 * s + b] = pack_bf16(f0, f1);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      if (t < a.T) {                               // uniform
+        const u32x4* xr = reinterpret_cast<const u32x4*>(X + t * xw + col0 / 2);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const u32x4 xv = xr[v];
+          const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[t] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wp[4 * v + e]),
+                                                      __builtin_bit_cast(bf16x2, xs[e]), acc[t],
+                                                      false);
+        }
+      }
+    }
+  };
+  // two chunks' code loads in flight before their arithmetic
+  int64_t j = (int64_t)lane * 4;
+  for (; j + 256 < nw; j += 512) {
+    const u32x4 c0 = *reinterpret_cast<const u32x4*>(wr + j);
+    const u32x4 c1 = *reinterpret_cast<const u32x4*>(wr + j + 256);
+    chunk(c0, j);
+    chunk(c1, j + 256);
+  }
+  if (j < nw) chunk(*reinterpret_cast<const u32x4*>(wr + j), j);
+  const float b = a.bias ? a.bias[n] : 0.f;
+#pragma unroll
+  for (int t = 0; t < TM; ++t) {
+    if (t < a.T) {
+      const float v = wave_sum(acc[t]);
+      if (lane == 0) a.Y[t * a.N + n] = v + b;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_pack_codes(const uint8_t* codes, int64_t rows, int64_t cols, int nbits,
@@ -178,6 +255,16 @@ hipError_t launch_fold_linear(const DeployFold& a, hipStream_t st) {
 
 hipError_t launch_w4a16_gemm(const DeployGemm& a, hipStream_t st) {
   if (a.N == 0 || a.T == 0) return hipSuccess;
+  // a few tokens: the vector-unit product, one wave per output row (at 16 tokens
+  // the matrix-core kernel is 3x faster: every wave would re-read all the tokens)
+  if (a.T <= 8) {
+    const dim3 g((unsigned)((a.N + 3) / 4));
+    if (a.T == 1) hipLaunchKernelGGL(k_w4a16_gemv<1>, g, dim3(256), 0, st, a);
+    else if (a.T == 2) hipLaunchKernelGGL(k_w4a16_gemv<2>, g, dim3(256), 0, st, a);
+    else if (a.T <= 4) hipLaunchKernelGGL(k_w4a16_gemv<4>, g, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(k_w4a16_gemv<8>, g, dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)((a.N + 31) / 32), (unsigned)((a.T + 31) / 32));
   hipLaunchKernelGGL(k_w4a16_gemm, grid, dim3(kWaves * 64), 0, st, a);
   return hipGetLastError();

@@ -10,7 +10,7 @@ import post_quantization_amd as omq
 from oracle import export as ex
 from oracle import quant
 import synth
-from gpu_util import dev, host, log, rel
+from gpu_util import DEV, dev, host, log, rel
 
 pytestmark = pytest.mark.gpu
 
@@ -133,3 +133,41 @@ def test_export_block(kind):
             assert rel(g, v) < 1e-5, k
         else:                        # v.h (divided by s_o) and the gains 1/s
             assert np.allclose(g, v, rtol=2 ** -23, atol=0), k
+
+
+def test_w4a16_gemm_graph_replays():
+    """The packed-code product captured into a HIP graph (as a decode loop replays
+    it): every replay, with eager work and synchronizations in between, equals the
+    eager result bit for bit, for the vector-unit (T = 1) and matrix-core (T = 16)
+    kernels."""
+    rng = np.random.default_rng(5)
+    cases = []
+    for T, N, K in ((1, 1024, 4096), (16, 512, 2048)):
+        W, s, ref, r = _calibrated_layer(N, K, 128, 4, rng, let=False)
+        words = omq.pack_codes(r["codes"], 4)
+        X = dev(synth.to_bf16(rng.standard_normal((T, K)).astype(F32)), torch.bfloat16)
+        Y = torch.empty(T, N, dtype=torch.float32, device=DEV)
+        eager = omq.w4a16_gemm(X, words, N, r["h"], r["z"], 128).clone()
+        cases.append((X, words, N, r["h"], r["z"], Y, eager))
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for X, words, N, h, z, Y, _ in cases:
+            omq.w4a16_gemm(X, words, N, h, z, 128, None, Y)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for X, words, N, h, z, Y, _ in cases:
+            omq.w4a16_gemm(X, words, N, h, z, 128, None, Y)
+    for rep in range(3):
+        for _, _, _, _, _, Y, _ in cases:
+            Y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for _, _, _, _, _, Y, eager in cases:
+            assert torch.equal(Y, eager), rep
+        # eager work between replays
+        omq.w4a16_gemm(cases[0][0], cases[0][1], cases[0][2], cases[0][3], cases[0][4], 128)
+        torch.cuda.synchronize()
