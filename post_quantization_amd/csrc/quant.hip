@@ -636,7 +636,9 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_g128(RowQuantFwd a) {
 // ---------------------------------------------------------------------------
 // backward tile pass: grid (col slabs, row tiles); wave w takes rows w, w+4, ...
 // ---------------------------------------------------------------------------
-template <int XDT>
+// LET and COL (the column-partial kind) are fixed at compile time, so the
+// per-element arithmetic is straight-line code.
+template <int XDT, int LET, int COL>
 __global__ __launch_bounds__(kThreads) void k_rowquant_bwd_tile(RowQuantBwd a, int rows_per_tile,
                                                                 float* rowpart, float* colpart) {
   const int tid = threadIdx.x;
@@ -654,9 +656,9 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_bwd_tile(RowQuantBwd a, i
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int64_t c = c0 + lane * 4 + 256 * (i >> 2) + (i & 3);
-    const bool cv = c < cols && a.let_mode != OMQ_LET_NONE;
+    const bool cv = c < cols && LET != OMQ_LET_NONE;
     sc[i] = cv ? a.s[c] : 1.f;
-    dc[i] = (cv && a.let_mode == OMQ_LET_DIV && a.delta) ? a.delta[c] : 0.f;
+    dc[i] = (cv && LET == OMQ_LET_DIV && a.delta) ? a.delta[c] : 0.f;
     rc[i] = 1.f / sc[i];
   }
 
@@ -679,57 +681,81 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_bwd_tile(RowQuantBwd a, i
     }
     const float vrow = a.rowvec ? a.rowvec[r] : 0.f;
     float shk[4] = {0.f, 0.f, 0.f, 0.f}, szk[4] = {0.f, 0.f, 0.f, 0.f};
+    // the row's 16 elements of this lane: x~, then rint(x~ / h) by the reciprocal
+    // product; elements within |u| 2^-20 of a half-integer (or not finite) take the
+    // exact quotient behind wave-uniform branches (a divergent branch per element
+    // would be flattened into a division for every element)
+    float v[16], gg[16], xd[16], xt[16], u[16], rq[16];
+    bool near = false;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int64_t c = c0 + lane * 4 + 256 * k;
-      const float h = hk[k], rh = rhk[k], z = zk[k];
+      const bool ok = c < cols;
+      float vv[4] = {0.f, 0.f, 0.f, 0.f};
+      float4 g4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (ok) {
+        load4(xr, XDT, c, vv);
+        g4 = *reinterpret_cast<const float4*>(gr + c);
+      }
+      const float g1[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ai = k * 4 + j;
+        v[ai] = vv[j];
+        gg[ai] = g1[j];
+        // x~ (exact for MUL / NONE; within 2 ulp for DIV, used only in sums)
+        xd[ai] = v[ai] - dc[ai];
+        xt[ai] = LET == OMQ_LET_DIV ? xd[ai] * rc[ai]
+                 : LET == OMQ_LET_MUL ? sc[ai] * v[ai] : v[ai];
+        u[ai] = xt[ai] * rhk[k];
+        rq[ai] = rintf(u[ai]);
+        near |= ok && !(fabsf(fabsf(u[ai] - rq[ai]) - 0.5f) > fabsf(u[ai]) * 0x1p-20f);
+      }
+    }
+    if (!pass && __builtin_amdgcn_ballot_w64(near) != 0) {
+#pragma unroll
+      for (int ai = 0; ai < 16; ++ai) {
+        const bool ne = !(fabsf(fabsf(u[ai] - rq[ai]) - 0.5f) > fabsf(u[ai]) * 0x1p-20f);
+        if (__builtin_amdgcn_ballot_w64(ne) != 0) {
+          if (ne) {
+            u[ai] = LET == OMQ_LET_DIV ? (xd[ai] / sc[ai]) / hk[ai >> 2] : xt[ai] / hk[ai >> 2];
+            rq[ai] = rintf(u[ai]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t c = c0 + lane * 4 + 256 * k;
+      const float z = zk[k];
       float sh = 0.f, sz = 0.f;
-      if (c >= cols) continue;
-      float v[4];
-      load4(xr, XDT, c, v);
-      const float4 g4 = *reinterpret_cast<const float4*>(gr + c);
-      const float gg[4] = {g4.x, g4.y, g4.z, g4.w};
       float up[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int ai = k * 4 + j;
-        // x~ (exact for MUL / NONE; within 2 ulp for DIV, used only in sums)
-        const float xd = v[j] - dc[ai];
-        const float xt = a.let_mode == OMQ_LET_DIV ? xd * rc[ai]
-                         : a.let_mode == OMQ_LET_MUL ? sc[ai] * v[j] : v[j];
         float gns;
         if (pass) {
-          gns = gg[j];
+          gns = gg[ai];
         } else {
-          float u;
-          const float rr = (a.let_mode == OMQ_LET_DIV ? rint_quot2(xd, sc[ai], rc[ai], h, rh, u)
-                                                      : rint_quot(xt, h, rh, u)) + z;
+          const float rr = rq[ai] + z;
           const bool in = (rr >= 0.f) && (rr <= Q);
           const float qmz = fminf(fmaxf(rr, 0.f), Q) - z;
-          sh += gg[j] * (qmz - (in ? u : 0.f));
-          sz += in ? 0.f : gg[j];
-          gns = in ? gg[j] : 0.f;
+          sh += gg[ai] * (qmz - (in ? u[ai] : 0.f));
+          sz += in ? 0.f : gg[ai];
+          gns = in ? gg[ai] : 0.f;
         }
-        switch (a.col_mode) {
-          case COL_WEIGHT:
-            acc0[ai] += gns * v[j];
-            acc1[ai] += vrow * v[j];
-            break;
-          case COL_ACT_DIV:
-            acc0[ai] += gns * (-xt * rc[ai]);
-            acc1[ai] += gns * (-rc[ai]);
-            break;
-          case COL_ACT_MUL:
-            acc0[ai] += gns * v[j];
-            break;
-          default:
-            break;
+        if constexpr (COL == COL_WEIGHT) {
+          acc0[ai] += gns * v[ai];
+          acc1[ai] += vrow * v[ai];
+        } else if constexpr (COL == COL_ACT_DIV) {
+          acc0[ai] += gns * (-xt[ai] * rc[ai]);
+          acc1[ai] += gns * (-rc[ai]);
+        } else if constexpr (COL == COL_ACT_MUL) {
+          acc0[ai] += gns * v[ai];
         }
-        if (a.let_mode == OMQ_LET_DIV) up[j] = gns * rc[ai];
-        else if (a.let_mode == OMQ_LET_MUL) up[j] = gns * sc[ai];
-        else up[j] = gns;
+        up[j] = LET == OMQ_LET_DIV ? gns * rc[ai] : LET == OMQ_LET_MUL ? gns * sc[ai] : gns;
       }
-      if (a.gx)
+      if (a.gx && c < cols)
         *reinterpret_cast<float4*>(a.gx + r * a.ldgx + c) = make_float4(up[0], up[1], up[2], up[3]);
       shk[k] = sh;
       szk[k] = sz;
@@ -763,7 +789,7 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_bwd_tile(RowQuantBwd a, i
       }
     }
   }
-  if (a.col_mode == COL_NONE) return;
+  if constexpr (COL == COL_NONE) return;
   __shared__ float red[4][2][kSlab];
 #pragma unroll
   for (int k = 0; k < 4; ++k)
@@ -1097,12 +1123,22 @@ hipError_t launch_rowquant_bwd(const RowQuantBwd& a, hipStream_t st) {
   float* rowpart = a.ws;
   float* colpart = a.ws + ((a.cols + 127) / 128) * a.rows * 2;
   dim3 grid((unsigned)nslabs, (unsigned)ntiles);
-  if (a.x_dt == OMQ_F32)
-    hipLaunchKernelGGL(k_rowquant_bwd_tile<OMQ_F32>, grid, dim3(kThreads), 0, st, a, R, rowpart,
-                       colpart);
-  else
-    hipLaunchKernelGGL(k_rowquant_bwd_tile<OMQ_BF16>, grid, dim3(kThreads), 0, st, a, R, rowpart,
-                       colpart);
+  if (a.let_mode < OMQ_LET_NONE || a.let_mode > OMQ_LET_MUL || a.col_mode < COL_NONE ||
+      a.col_mode > COL_ACT_MUL)
+    return hipErrorInvalidValue;
+  // every (x dtype, LET mode, column kind) instance
+#define OMQ_TILE(XD, L, C)                                                                   \
+  if (a.x_dt == XD && a.let_mode == L && a.col_mode == C)                                    \
+    hipLaunchKernelGGL((k_rowquant_bwd_tile<XD, L, C>), grid, dim3(kThreads), 0, st, a, R,   \
+                       rowpart, colpart);
+#define OMQ_TILE_L(XD, L)                                                                    \
+  OMQ_TILE(XD, L, COL_NONE) OMQ_TILE(XD, L, COL_WEIGHT) OMQ_TILE(XD, L, COL_ACT_DIV)         \
+  OMQ_TILE(XD, L, COL_ACT_MUL)
+  OMQ_TILE_L(OMQ_F32, OMQ_LET_NONE) OMQ_TILE_L(OMQ_F32, OMQ_LET_DIV)
+  OMQ_TILE_L(OMQ_F32, OMQ_LET_MUL) OMQ_TILE_L(OMQ_BF16, OMQ_LET_NONE)
+  OMQ_TILE_L(OMQ_BF16, OMQ_LET_DIV) OMQ_TILE_L(OMQ_BF16, OMQ_LET_MUL)
+#undef OMQ_TILE_L
+#undef OMQ_TILE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = launch_ste_colfinal(a, (int)ntiles, colpart, st);
