@@ -809,40 +809,6 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_bwd_tile(RowQuantBwd a, i
   }
 }
 
-// column finalize, level 1: split the row tiles into kColSplit groups so the
-// reduction runs on (cols / 256) x kColSplit blocks; level 2 sums the groups in a
-// fixed order: out[c] (+)= sum over row tiles.
-constexpr int kColSplit = 32;
-
-__global__ __launch_bounds__(kThreads) void k_colpart_split(const float* colpart, int ntiles,
-                                                            int64_t cols, float* part2) {
-  const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (c >= cols) return;
-  const int per = (ntiles + kColSplit - 1) / kColSplit;
-  const int t0 = blockIdx.y * per, t1 = min(ntiles, t0 + per);
-  float s0 = 0.f, s1 = 0.f;
-  for (int t = t0; t < t1; ++t) {
-    s0 += colpart[((int64_t)t * 2 + 0) * cols + c];
-    s1 += colpart[((int64_t)t * 2 + 1) * cols + c];
-  }
-  part2[((int64_t)blockIdx.y * 2 + 0) * cols + c] = s0;
-  part2[((int64_t)blockIdx.y * 2 + 1) * cols + c] = s1;
-}
-
-__global__ __launch_bounds__(kThreads) void k_colpart_reduce(const float* part2, int nsplit,
-                                                             int64_t cols, float* out0,
-                                                             float* out1, int accumulate) {
-  const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (c >= cols) return;
-  float s0 = 0.f, s1 = 0.f;
-  for (int t = 0; t < nsplit; ++t) {
-    s0 += part2[((int64_t)t * 2 + 0) * cols + c];
-    s1 += part2[((int64_t)t * 2 + 1) * cols + c];
-  }
-  if (out0) out0[c] = (accumulate ? out0[c] : 0.f) + s0;
-  if (out1) out1[c] = (accumulate ? out1[c] : 0.f) + s1;
-}
-
 // row finalize: LPR lanes per quantizer row sum its per-slab partials (coalesced
 // reads, then a shuffle reduction), one of them finishes the row: LWC-logit
 // gradients and the max/min scatter.
@@ -1008,13 +974,44 @@ __global__ __launch_bounds__(kThreads) void k_cvt_bf16_colpart(const float* in, 
   }
 }
 
-__global__ __launch_bounds__(kThreads) void k_colsum_final(const float* part, int nparts,
-                                                           int64_t cols, float* out) {
-  const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (c >= cols) return;
-  float s = 0.f;
-  for (int p = 0; p < nparts; ++p) s += part[(int64_t)p * cols + c];
-  out[c] = s;
+
+// Column sums of partial rows: out_k[c] (+)= sum_t part[(t * nk + k) * cols + c] for
+// the nk (1 or 2) kinds.  A workgroup takes 64 columns; its 16 waves take the
+// partial rows t = w, w + 16, ... (one coalesced 256-byte segment per row), and the
+// 16 wave sums are added in LDS in a fixed order, so the result is deterministic.
+constexpr int kSumWaves = 16;
+
+__global__ __launch_bounds__(kSumWaves * 64) void k_part_colsum(const float* part, int nparts,
+                                                                int nk, int64_t cols,
+                                                                float* out0, float* out1,
+                                                                int accumulate) {
+  __shared__ float red[2][kSumWaves][64];
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int64_t c = (int64_t)blockIdx.x * 64 + lane;
+  float s[2] = {0.f, 0.f};
+  if (c < cols) {
+#pragma unroll 4
+    for (int t = w; t < nparts; t += kSumWaves)
+      for (int k = 0; k < nk; ++k) s[k] += part[((int64_t)t * nk + k) * cols + c];
+  }
+  red[0][w][lane] = s[0];
+  red[1][w][lane] = s[1];
+  __syncthreads();
+  if (w < nk && c < cols) {
+    float t = 0.f;
+#pragma unroll
+    for (int q = 0; q < kSumWaves; ++q) t += red[w][q][lane];
+    float* o = w == 0 ? out0 : out1;
+    if (o) o[c] = (accumulate ? o[c] : 0.f) + t;
+  }
+}
+
+hipError_t launch_part_colsum(const float* part, int nparts, int nk, int64_t cols, float* out0,
+                              float* out1, int accumulate, hipStream_t st) {
+  if (cols == 0 || (!out0 && !out1)) return hipSuccess;
+  hipLaunchKernelGGL(k_part_colsum, dim3((unsigned)((cols + 63) / 64)), dim3(kSumWaves * 64), 0,
+                     st, part, nparts, nk, cols, out0, out1, accumulate);
+  return hipGetLastError();
 }
 
 int bwd_rows_per_tile(int64_t rows) { return rows >= 8192 ? 32 : 16; }
@@ -1147,25 +1144,13 @@ hipError_t launch_rowquant_bwd(const RowQuantBwd& a, hipStream_t st) {
 }
 
 size_t ste_partials_floats(int64_t rows, int64_t cols, int64_t nslabs, int64_t ntiles) {
-  return (size_t)(nslabs * rows * 2 + ntiles * 2 * cols + kColSplit * 2 * cols) + 64;
+  return (size_t)(nslabs * rows * 2 + ntiles * 2 * cols) + 64;
 }
 
 hipError_t launch_ste_colfinal(const RowQuantBwd& a, int ntiles, float* colpart,
                                hipStream_t st) {
-  hipError_t e = hipSuccess;
-  if (a.col_mode != COL_NONE && (a.out0 || a.out1)) {
-    float* part2 = colpart + (int64_t)ntiles * 2 * a.cols;
-    const unsigned cb = (unsigned)((a.cols + kThreads - 1) / kThreads);
-    const int nsplit = (int)std::min<int64_t>(kColSplit, ntiles);
-    hipLaunchKernelGGL(k_colpart_split, dim3(cb, (unsigned)nsplit), dim3(kThreads), 0, st,
-                       colpart, (int)ntiles, a.cols, part2);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_colpart_reduce, dim3(cb), dim3(kThreads), 0, st, part2, nsplit, a.cols,
-                       a.out0, a.out1, a.accumulate);
-    e = hipGetLastError();
-  }
-  return e;
+  if (a.col_mode == COL_NONE || !(a.out0 || a.out1)) return hipSuccess;
+  return launch_part_colsum(colpart, ntiles, 2, a.cols, a.out0, a.out1, a.accumulate, st);
 }
 
 hipError_t launch_ste_rowfinal(const RowQuantBwd& a, int nslabs, const float* rowpart,
@@ -1245,9 +1230,7 @@ hipError_t launch_cvt_bf16_colsum(const float* in, int64_t rows, int64_t cols, u
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !colsum) return e;
-  hipLaunchKernelGGL(k_colsum_final, dim3((unsigned)((cols + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, st, ws, (int)np, cols, colsum);
-  return hipGetLastError();
+  return launch_part_colsum(ws, (int)np, 1, cols, colsum, nullptr, 0, st);
 }
 
 hipError_t launch_colsum(const float* in, int64_t rows, int64_t cols, int64_t ld, float* out,
@@ -1262,8 +1245,7 @@ hipError_t launch_colsum(const float* in, int64_t rows, int64_t cols, int64_t ld
                      ld, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_colsum_final, dim3(cb), dim3(kThreads), 0, st, ws, (int)np, cols, out);
-  return hipGetLastError();
+  return launch_part_colsum(ws, (int)np, 1, cols, out, nullptr, 0, st);
 }
 
 }  // namespace omq
