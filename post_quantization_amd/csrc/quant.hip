@@ -943,9 +943,10 @@ __global__ __launch_bounds__(kThreads) void k_colsum_part(const float* in, int64
 // set, the column sums of each kColsumRows-row chunk, in one pass over dY.
 // VEC: 8 consecutive columns per thread (cols % 8 == 0), else one.
 template <int VEC>
-__global__ __launch_bounds__(kThreads) void k_cvt_bf16_colpart(const float* in, int64_t rows,
-                                                               int64_t cols, uint16_t* out,
-                                                               float* part) {
+__global__ __launch_bounds__(kThreads) void k_cvt_bf16_colpart(const float* __restrict__ in,
+                                                               int64_t rows, int64_t cols,
+                                                               uint16_t* __restrict__ out,
+                                                               float* __restrict__ part) {
   const int64_t c = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * VEC;
   if (c >= cols) return;
   const int64_t r0 = (int64_t)blockIdx.y * kColsumRows;
@@ -953,6 +954,8 @@ __global__ __launch_bounds__(kThreads) void k_cvt_bf16_colpart(const float* in, 
   float s[VEC];
 #pragma unroll
   for (int j = 0; j < VEC; ++j) s[j] = 0.f;
+  // (4 rows in flight: the loads of the next rows do not wait for this row's stores)
+#pragma unroll 4
   for (int64_t r = r0; r < r1; ++r) {
     const float* p = in + r * cols + c;
     if constexpr (VEC == 8) {
