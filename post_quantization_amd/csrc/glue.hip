@@ -111,6 +111,76 @@ __global__ __launch_bounds__(kThreads) void k_rope(const float* x, int64_t ldx, 
 
 OMQ_DEV float sigmoidf_(float x) { return 1.f / (1.f + expf(-x)); }
 
+// Row-parallel forms of the elementwise kernels below: blockIdx.y is the token,
+// each thread takes 4 consecutive columns with 16-byte accesses (the launchers use
+// them when the widths and strides are multiples of 4 and the pointers 16-byte
+// aligned); the per-element arithmetic is the same.
+__global__ __launch_bounds__(kThreads) void k_rope4(const float* __restrict__ x, int64_t ldx,
+                                                    int n_heads, int hd,
+                                                    const float* __restrict__ cos_t,
+                                                    const float* __restrict__ sin_t, int inverse,
+                                                    float* __restrict__ y, int64_t ldy) {
+  const int half = hd / 2;
+  const int j = (blockIdx.x * kThreads + threadIdx.x) * 4;   // over n_heads * half
+  if (j >= n_heads * half) return;
+  const int64_t t = blockIdx.y;
+  const int hh = j / half, k = j % half;
+  const float4 c = *reinterpret_cast<const float4*>(cos_t + t * half + k);
+  const float4 s = *reinterpret_cast<const float4*>(sin_t + t * half + k);
+  const float* xr = x + t * ldx + (int64_t)hh * hd + k;
+  const float4 a = *reinterpret_cast<const float4*>(xr);
+  const float4 b = *reinterpret_cast<const float4*>(xr + half);
+  float4 ya, yb;
+  if (!inverse) {
+    ya = make_float4(a.x * c.x - b.x * s.x, a.y * c.y - b.y * s.y, a.z * c.z - b.z * s.z,
+                     a.w * c.w - b.w * s.w);
+    yb = make_float4(b.x * c.x + a.x * s.x, b.y * c.y + a.y * s.y, b.z * c.z + a.z * s.z,
+                     b.w * c.w + a.w * s.w);
+  } else {
+    ya = make_float4(a.x * c.x + b.x * s.x, a.y * c.y + b.y * s.y, a.z * c.z + b.z * s.z,
+                     a.w * c.w + b.w * s.w);
+    yb = make_float4(b.x * c.x - a.x * s.x, b.y * c.y - a.y * s.y, b.z * c.z - a.z * s.z,
+                     b.w * c.w - a.w * s.w);
+  }
+  float* yr = y + t * ldy + (int64_t)hh * hd + k;
+  *reinterpret_cast<float4*>(yr) = ya;
+  *reinterpret_cast<float4*>(yr + half) = yb;
+}
+
+__global__ __launch_bounds__(kThreads) void k_silu_gate4(const float* __restrict__ gu, int64_t F,
+                                                         float* __restrict__ a) {
+  const int64_t f = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4;
+  if (f >= F) return;
+  const int64_t t = blockIdx.y;
+  const float4 g = *reinterpret_cast<const float4*>(gu + t * 2 * F + f);
+  const float4 u = *reinterpret_cast<const float4*>(gu + t * 2 * F + F + f);
+  *reinterpret_cast<float4*>(a + t * F + f) =
+      make_float4(g.x * sigmoidf_(g.x) * u.x, g.y * sigmoidf_(g.y) * u.y,
+                  g.z * sigmoidf_(g.z) * u.z, g.w * sigmoidf_(g.w) * u.w);
+}
+
+__global__ __launch_bounds__(kThreads) void k_silu_gate_bwd4(const float* __restrict__ gu,
+                                                             const float* __restrict__ ga,
+                                                             int64_t F, float* __restrict__ ggu) {
+  const int64_t f = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4;
+  if (f >= F) return;
+  const int64_t t = blockIdx.y;
+  const float4 g4 = *reinterpret_cast<const float4*>(gu + t * 2 * F + f);
+  const float4 u4 = *reinterpret_cast<const float4*>(gu + t * 2 * F + F + f);
+  const float4 d4 = *reinterpret_cast<const float4*>(ga + t * F + f);
+  const float g[4] = {g4.x, g4.y, g4.z, g4.w}, u[4] = {u4.x, u4.y, u4.z, u4.w};
+  const float d[4] = {d4.x, d4.y, d4.z, d4.w};
+  float og[4], ou[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float sg = sigmoidf_(g[e]);
+    og[e] = d[e] * u[e] * sg * (1.f + g[e] * (1.f - sg));
+    ou[e] = d[e] * g[e] * sg;
+  }
+  *reinterpret_cast<float4*>(ggu + t * 2 * F + f) = make_float4(og[0], og[1], og[2], og[3]);
+  *reinterpret_cast<float4*>(ggu + t * 2 * F + F + f) = make_float4(ou[0], ou[1], ou[2], ou[3]);
+}
+
 __global__ __launch_bounds__(kThreads) void k_silu_gate(const float* gu, int64_t T, int64_t F,
                                                         float* a) {
   const int64_t n = T * F;
@@ -238,6 +308,8 @@ hipError_t launch_rmsnorm_bwd(const float* gy, const float* x, const float* rstd
   return hipGetLastError();
 }
 
+static bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 hipError_t launch_rope_tables(int64_t T, int64_t hd, float theta, float* cos_t, float* sin_t,
                               hipStream_t st) {
   const int64_t n = T * (hd / 2);
@@ -252,6 +324,14 @@ hipError_t launch_rope(const float* x, int64_t ldx, int64_t T, int64_t n_heads, 
                        hipStream_t st) {
   const int64_t n = T * n_heads * (hd / 2);
   if (n == 0) return hipSuccess;
+  if ((hd / 2) % 4 == 0 && ldx % 4 == 0 && ldy % 4 == 0 && al16(x) && al16(y) && al16(cos_t) &&
+      al16(sin_t) && T < 65536) {
+    const int64_t w = n_heads * (hd / 2) / 4;
+    hipLaunchKernelGGL(k_rope4, dim3((unsigned)((w + kThreads - 1) / kThreads), (unsigned)T),
+                       dim3(kThreads), 0, st, x, ldx, (int)n_heads, (int)hd, cos_t, sin_t, inverse,
+                       y, ldy);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_rope, dim3(grid_for(n)), dim3(kThreads), 0, st, x, ldx, T, n_heads, hd,
                      cos_t, sin_t, inverse, y, ldy);
   return hipGetLastError();
@@ -259,6 +339,11 @@ hipError_t launch_rope(const float* x, int64_t ldx, int64_t T, int64_t n_heads, 
 
 hipError_t launch_silu_gate(const float* gu, int64_t T, int64_t F, float* a, hipStream_t st) {
   if (T * F == 0) return hipSuccess;
+  if (F % 4 == 0 && al16(gu) && al16(a) && T < 65536) {
+    hipLaunchKernelGGL(k_silu_gate4, dim3((unsigned)((F / 4 + kThreads - 1) / kThreads), (unsigned)T),
+                       dim3(kThreads), 0, st, gu, F, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_silu_gate, dim3(grid_for(T * F)), dim3(kThreads), 0, st, gu, T, F, a);
   return hipGetLastError();
 }
@@ -266,6 +351,12 @@ hipError_t launch_silu_gate(const float* gu, int64_t T, int64_t F, float* a, hip
 hipError_t launch_silu_gate_bwd(const float* gu, const float* ga, int64_t T, int64_t F,
                                 float* ggu, hipStream_t st) {
   if (T * F == 0) return hipSuccess;
+  if (F % 4 == 0 && al16(gu) && al16(ga) && al16(ggu) && T < 65536) {
+    hipLaunchKernelGGL(k_silu_gate_bwd4,
+                       dim3((unsigned)((F / 4 + kThreads - 1) / kThreads), (unsigned)T),
+                       dim3(kThreads), 0, st, gu, ga, F, ggu);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_silu_gate_bwd, dim3(grid_for(T * F)), dim3(kThreads), 0, st, gu, ga, T, F,
                      ggu);
   return hipGetLastError();
