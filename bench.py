@@ -22,6 +22,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "LWC+LET block fwd+bwd calib steps/s & TFLOP/s, LLaMA-7B-shaped, W4A4, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 matrix-core peak
 PEAK_HBM_GBS = 8000.0
 
 
@@ -450,12 +451,27 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
     loss_last = float(loss.cpu()[0])
     durs = timer.durations_ms()
-    n_l = len(durs)
+    kinds = timer.kinds()
     gemm_ms = sum(durs)
-    gemm_flops = timer.struct.flops
-    avg_dur_s = gemm_ms / n_l / 1e3
-    flops_per_launch = gemm_flops / n_l
+    # the bf16 matrix-core GEMMs (every backward product; the forward's too unless
+    # it runs on integer codes) and the int8 code products, each against its peak
+    bf_d = [t for t, k in zip(durs, kinds) if k == 0]
+    i8_d = [t for t, k in zip(durs, kinds) if k == 1]
+    n_l = len(bf_d)
+    avg_dur_s = sum(bf_d) / n_l / 1e3
+    flops_per_launch = (timer.struct.flops - timer.struct.flops_codes) / n_l
     achieved = flops_per_launch / avg_dur_s / 1e12
+    codes_roof = None
+    if i8_d:
+        i8_ops = timer.struct.flops_codes / len(i8_d)
+        i8_avg_s = sum(i8_d) / len(i8_d) / 1e3
+        codes_roof = {
+            "kernel": "k_gemm_bf16<..., I8 = 1> (the forward's products on int8 codes)",
+            "bound": "mfma", "achieved": round(i8_ops / i8_avg_s / 1e12, 2),
+            "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+            "frac": round(i8_ops / i8_avg_s / 1e12 / PEAK_INT8_TOPS, 4),
+            "launches": len(i8_d), "avg_launch_us": round(i8_avg_s * 1e6, 2),
+            "share_of_step": round(sum(i8_d) / (ms * args.steps), 4)}
     sps = 1000.0 / ms
     tflops = step_flops(c) * sps / 1e12
 
@@ -487,7 +503,7 @@ def main():
         "loss_first_warmup": loss_first,
         "loss_last": loss_last,
         "roofline": {
-            "kernel": "k_gemm_bf16 (all matrix-core GEMM launches of the timed steps)",
+            "kernel": "k_gemm_bf16 (the bf16 matrix-core GEMM launches of the timed steps)",
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
@@ -496,8 +512,10 @@ def main():
             "traffic": measured_traffic(args.workload),
             "launches": n_l,
             "avg_launch_us": round(avg_dur_s * 1e6, 2),
+            "share_of_step": round(sum(bf_d) / (ms * args.steps), 4),
             "gemm_share_of_step": round(gemm_ms / (ms * args.steps), 4),
         },
+        "roofline_codes": codes_roof,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define OMQ_ABI_VERSION 2
+#define OMQ_ABI_VERSION 3
 
 /* status codes */
 #define OMQ_OK 0
@@ -143,6 +143,36 @@ int omq_act_quant(const void* X, int x_dt, int64_t T, int64_t C, int n_bits, int
 int omq_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int trans_a,
              const void* B, int64_t ldb, int trans_b, int dt, const float* bias, float alpha,
              float* C, int64_t ldc, int accumulate, void* stream);
+
+/*
+ * omq_code_gemm -- the weight-activation quantized product on integer codes (paper
+ * reading, section "LWC": a quantized value is (q - z) h with integer code q, step
+ * h and zero point z per quantizer row; section "LET": Y = Q_a(X~) Q_w(W~)^T + B~):
+ *   C[m, n] = h_a[m] h_b[n] sum_k (qa[m,k] - z_a[m]) (qb[n,k] - z_b[n]) + bias[n]
+ * the same product as omq_gemm on the fake-quantized operands, computed exactly:
+ * the matrix cores sum the int8 code products in int32, the zero points enter
+ * through the rows' code sums, sum_k (qa - z_a)(qb - z_b) = S - z_b sum_a - z_a
+ * sum_b + K z_a z_b, formed in double without rounding, and the result is rounded
+ * once to float (before bias).
+ * qa: uint8 [M x K], row stride lda; qb: uint8 [N x K], row stride ldb (codes below
+ * 128, i.e. n_bits up to 7, as the codes output of omq_act_quant and
+ * omq_lwc_fakequant with group 0).  h_a, z_a: float[M]; h_b, z_b: float[N] (z
+ * integer-valued); sum_a: int32[M], sum_b: int32[N], the rows' code sums (see
+ * omq_code_rowsum).  bias: float[N] or NULL.  C: float [M x N], row stride ldc,
+ * overwritten.  K, lda, ldb multiples of 16, qa and qb 16-byte aligned
+ * (OMQ_E_ALIGN), K at most 131072 (OMQ_E_SHAPE).
+ */
+int omq_code_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* qa, int64_t lda,
+                  const float* h_a, const float* z_a, const int32_t* sum_a, const uint8_t* qb,
+                  int64_t ldb, const float* h_b, const float* z_b, const int32_t* sum_b,
+                  const float* bias, float* C, int64_t ldc, void* stream);
+
+/*
+ * omq_code_rowsum -- sums[r] = sum over c < cols of codes[r * ld + c] (int32), the
+ * code sums omq_code_gemm takes.  codes: uint8, rows x cols with row stride ld.
+ */
+int omq_code_rowsum(const uint8_t* codes, int64_t rows, int64_t cols, int64_t ld, int32_t* sums,
+                    void* stream);
 
 /*
  * Deployment form of a calibrated layer (paper reading, section "LWC": the deployed
@@ -298,12 +328,17 @@ int omq_adamw(float* theta, const float* grad, float* m, float* v, int64_t n, in
  * events[2*count+1] after each GEMM launch it issues on the call's stream,
  * increments count, and adds the launch's algorithmic FLOPs to flops (2 M N K per
  * batch entry; the causal attention products count their causal half).
+ * kinds (int[capacity] or NULL) receives each recorded launch's operand kind:
+ * 0 bf16 (or float32) operands, 1 int8 codes (the forward's products on integer
+ * codes, see omq_code_gemm); flops_codes sums the latter's share of flops.
  */
 typedef struct omq_timer {
   void** events;
   int capacity;
   int count;
   double flops;
+  int* kinds;
+  double flops_codes;
 } omq_timer;
 
 /*

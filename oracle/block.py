@@ -21,7 +21,11 @@ Readings of what the pages leave open (all listed in the design doc):
 * LET sites: one (s, delta) shared by the q/k/v input, one by the gate/up input,
   one on the o_proj input; with grouped-query attention s_o, delta_o and s_a live
   on the KV channels and are broadcast over the query heads of each group;
-* the block's quantized input is the same x as the full-precision target.
+* the block's quantized input is the same x as the full-precision target;
+* operand precision of the bf16 path (ops.ExactOps): every product takes bf16
+  operands, except the forward's four quantized products with per-row quantizers
+  on both sides below 8 bits (and input widths a multiple of 16), which the GPU
+  forms exactly on the integer codes.
 
 Parity: pinned by tests/test_oracle_block.py (full-precision block vs torch's
 rms_norm / scaled_dot_product_attention / silu; RoPE invariants; LET identity of
@@ -223,8 +227,10 @@ def unpack(c, shapes, flat):
 # forward
 # ---------------------------------------------------------------------------
 
-def _qlin(ops, S, name, Xop, W, th, c, s=None, delta=None):
-    """One quantized linear on an already-quantized operand Xop."""
+def _qlin(ops, S, name, Xop, W, th, c, s=None, delta=None, Xfw=None):
+    """One quantized linear on an already-quantized operand Xop (the backward's
+    operand); Xfw, when given, is the exact quantized input the forward product
+    takes instead, with the exact quantized weight (the product on integer codes)."""
     gamma = ops.sigmoid(th["a_gamma_" + name])
     beta = ops.sigmoid(th["a_beta_" + name])
     Wt = ops.let_weight(W, s) if s is not None else ops.to_code(W)
@@ -236,10 +242,13 @@ def _qlin(ops, S, name, Xop, W, th, c, s=None, delta=None):
         rows = lwc_rows(c, Wt.shape)
         wst = ops.quant(np.reshape(Wt, (rows, -1)), gamma, beta, c.wbits, "w_" + name)
         Wop = ops.operand(np.reshape(wst.xhat, Wt.shape))
-    Y = Xop @ Wop.T
+    if Xfw is not None and wst is not None:
+        Y = np.asarray(Xfw, F64) @ np.reshape(wst.xhat, Wt.shape).astype(F64).T
+    else:
+        Y = Xop @ Wop.T
     if delta is not None:
         Y = Y + quant.bias_fold(W, None, delta)[None, :]
-    S[name] = SimpleNamespace(gamma=gamma, beta=beta, wst=wst, Wop=Wop, W=W, s=s)
+    S[name] = SimpleNamespace(gamma=gamma, beta=beta, wst=wst, Wop=Wop, W=W, s=s, Y=Y)
     return Y
 
 
@@ -249,6 +258,12 @@ def forward(c, x, Wd, th, ops=None):
         ops = ExactOps(bf16=True)
     S = SimpleNamespace(c=c, ops=ops, th=th)
     S.lin = {}
+    # the forward's quantized products on integer codes (exact operands)
+    cp = getattr(ops, "code_product", None)
+    exact = cp is not None and cp(c)
+
+    def fw(Xh):
+        return Xh if exact else None
     x64 = np.asarray(x, F64)
     hd, n_q, n_kv = c.head_dim, c.n_q, c.n_kv
     sv = {}
@@ -258,9 +273,9 @@ def forward(c, x, Wd, th, ops=None):
         Xt_qkv = ops.let_act(xn, s_qkv, d_qkv)
         a_qkv, Xh = ops.act(Xt_qkv, c.abits, "a_qkv")
         Xop_qkv = ops.operand(Xh)
-        Yq = _qlin(ops, sv, "q", Xop_qkv, Wd["W_q"], th, c, s_qkv, d_qkv)
-        Yk = _qlin(ops, sv, "k", Xop_qkv, Wd["W_k"], th, c, s_qkv, d_qkv)
-        Yv = _qlin(ops, sv, "v", Xop_qkv, Wd["W_v"], th, c, s_qkv, d_qkv)
+        Yq = _qlin(ops, sv, "q", Xop_qkv, Wd["W_q"], th, c, s_qkv, d_qkv, fw(Xh))
+        Yk = _qlin(ops, sv, "k", Xop_qkv, Wd["W_k"], th, c, s_qkv, d_qkv, fw(Xh))
+        Yv = _qlin(ops, sv, "v", Xop_qkv, Wd["W_v"], th, c, s_qkv, d_qkv, fw(Xh))
         cos, sin = rope_tables(c.T, hd, c.rope_theta)
         Qr = rope(Yq, n_q, hd, cos, sin)
         Kr = rope(Yk, n_kv, hd, cos, sin)
@@ -282,7 +297,7 @@ def forward(c, x, Wd, th, ops=None):
         Xt_o = ops.let_act(O, s_o, d_o)
         a_o, Xh_o = ops.act(Xt_o, c.abits, "a_o")
         Xop_o = ops.operand(Xh_o)
-        h1 = x64 + _qlin(ops, sv, "o", Xop_o, Wd["W_o"], th, c, s_o, d_o)
+        h1 = x64 + _qlin(ops, sv, "o", Xop_o, Wd["W_o"], th, c, s_o, d_o, fw(Xh_o))
         xn2, r2 = rmsnorm(h1, c.eps)
         S.__dict__.update(xn=xn, r1=r1, Xt_qkv=Xt_qkv, a_qkv=a_qkv, Xop_qkv=Xop_qkv,
                           cos=cos, sin=sin, Qr=Qr, Kr=Kr, Qt=Qt, Kt=Kt, Yv=Yv, sa_q=sa_q,
@@ -295,12 +310,12 @@ def forward(c, x, Wd, th, ops=None):
     Xt_f = ops.let_act(xn2, s_f, d_f)
     a_f, Xh_f = ops.act(Xt_f, c.abits, "a_ffn")
     Xop_f = ops.operand(Xh_f)
-    G = _qlin(ops, sv, "gate", Xop_f, Wd["W_gate"], th, c, s_f, d_f)
-    U = _qlin(ops, sv, "up", Xop_f, Wd["W_up"], th, c, s_f, d_f)
+    G = _qlin(ops, sv, "gate", Xop_f, Wd["W_gate"], th, c, s_f, d_f, fw(Xh_f))
+    U = _qlin(ops, sv, "up", Xop_f, Wd["W_up"], th, c, s_f, d_f, fw(Xh_f))
     A = silu(G) * U
     a_d, Xh_d = ops.act(A, c.abits, "a_down")
     Xop_d = ops.operand(Xh_d)
-    D = _qlin(ops, sv, "down", Xop_d, Wd["W_down"], th, c)
+    D = _qlin(ops, sv, "down", Xop_d, Wd["W_down"], th, c, Xfw=fw(Xh_d))
     y = D if c.ffn_only else h1 + D
     S.__dict__.update(xn2=xn2, Xt_f=Xt_f, a_f=a_f, Xop_f=Xop_f, G=G, U=U, A=A, a_d=a_d,
                       Xop_d=Xop_d, y=y)

@@ -62,3 +62,14 @@ class ExactOps:
         if self.bf16:
             return quant.bf16(a)
         return np.asarray(a, dtype=F64)
+
+    def code_product(self, c):
+        """Whether the bf16 path forms the block forward's four quantized products
+        (quantized activations times LWC weights) on the integer codes: exactly
+        (q_x - z_x) h_x times (q_w - z_w) h_w, no operand rounding.  It does so for
+        per-row quantizers with codes below 128 on both sides and every input width
+        a multiple of 16; otherwise the operands enter as bf16 like any other.  The
+        backward's products take the bf16 operands either way."""
+        widths = [c.d, c.F] + ([] if c.ffn_only else [c.n_q * c.head_dim])
+        return (self.bf16 and c.wbits <= 7 and c.abits <= 7 and not c.group
+                and all(w % 16 == 0 for w in widths))

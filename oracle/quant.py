@@ -194,6 +194,21 @@ def lwc_fakequant(W, a_gamma, a_beta, nbits, s=None, delta=None, B=None, group=N
                            B_tilde=Bt, group=g)
 
 
+def code_product(qa, h_a, z_a, qb, h_b, z_b, bias=None) -> np.ndarray:
+    """The quantized product Y = Q_a(X~) Q_w(W~)^T + B~ (section "LET") written on
+    the integer codes: each operand row r holds (q_r - z_r) h_r (section "LWC",
+    dequantization), so Y = ((qa - z_a) h_a) ((qb - z_b) h_b)^T + bias, float64.
+    qa [M, K], qb [N, K] codes; h_*, z_* per row; bias [N] or None."""
+    A = (np.asarray(qa, dtype=F64) - np.asarray(z_a, dtype=F64)[:, None]) * \
+        np.asarray(h_a, dtype=F64)[:, None]
+    B = (np.asarray(qb, dtype=F64) - np.asarray(z_b, dtype=F64)[:, None]) * \
+        np.asarray(h_b, dtype=F64)[:, None]
+    out = A @ B.T
+    if bias is not None:
+        out = out + np.asarray(bias, dtype=F64)[None, :]
+    return out
+
+
 def lwc_bwd(g_What, ref):
     """Straight-through backward of ``lwc_fakequant`` (result ``ref``) for the
     upstream gradient w.r.t. W_hat: returns (dL/dW~ [C_out, C_in], dL/dgamma,

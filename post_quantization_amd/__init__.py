@@ -53,7 +53,8 @@ class QLinearDesc(ctypes.Structure):
 
 class OmqTimer(ctypes.Structure):
     _fields_ = [("events", ctypes.POINTER(ctypes.c_void_p)), ("capacity", _int),
-                ("count", _int), ("flops", ctypes.c_double)]
+                ("count", _int), ("flops", ctypes.c_double),
+                ("kinds", ctypes.POINTER(ctypes.c_int)), ("flops_codes", ctypes.c_double)]
 
 
 def _hip():
@@ -77,12 +78,19 @@ class GemmTimer:
             if rc != 0:
                 raise OmqError("hipEventCreate failed (%d)" % rc)
             self._ev[i] = e.value
+        self._kinds = (ctypes.c_int * capacity)()
         self.struct = OmqTimer(ctypes.cast(self._ev, ctypes.POINTER(ctypes.c_void_p)), capacity,
-                               0, 0.0)
+                               0, 0.0, ctypes.cast(self._kinds, ctypes.POINTER(ctypes.c_int)),
+                               0.0)
 
     def reset(self):
         self.struct.count = 0
         self.struct.flops = 0.0
+        self.struct.flops_codes = 0.0
+
+    def kinds(self):
+        """Per recorded launch: 0 bf16 / float32 operands, 1 int8 codes."""
+        return [self._kinds[i] for i in range(self.struct.count)]
 
     def durations_ms(self):
         out = []
@@ -125,6 +133,9 @@ _SIGS = {
                              _vp, _vp, _vp, _vp]),
     "omq_gemm": (_int, [_i64, _i64, _i64, _vp, _i64, _int, _vp, _i64, _int, _int, _vp, _f, _vp,
                         _i64, _int, _vp]),
+    "omq_code_gemm": (_int, [_i64, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp,
+                             _vp, _vp, _vp, _i64, _vp]),
+    "omq_code_rowsum": (_int, [_vp, _i64, _i64, _i64, _vp, _vp]),
     "omq_lwc_backward_workspace_size": (_sz, [_i64, _i64]),
     "omq_lwc_backward": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -273,6 +284,33 @@ def gemm(A, B, bias=None, alpha=1.0, C=None, accumulate=False, trans_a=False, tr
     _check("omq_gemm", lib().omq_gemm(M, N, K, _p(A), A.shape[1], int(trans_a), _p(B),
                                       B.shape[1], int(trans_b), _dt(A), _p(bias), alpha, _p(C),
                                       N, int(accumulate), _stream()))
+    return C
+
+
+def code_rowsum(codes):
+    """int32 sums of each row of a uint8 code matrix."""
+    rows, cols = codes.shape
+    sums = torch.empty(rows, dtype=torch.int32, device=codes.device)
+    _check("omq_code_rowsum", lib().omq_code_rowsum(_p(codes), rows, cols, cols, _p(sums),
+                                                    _stream()))
+    return sums
+
+
+def code_gemm(qa, h_a, z_a, qb, h_b, z_b, sum_a=None, sum_b=None, bias=None, C=None):
+    """C = ((qa - z_a) h_a) ((qb - z_b) h_b)^T + bias from uint8 codes qa [M x K], qb
+    [N x K] with per-row steps and zero points; the code sums default to
+    code_rowsum of each operand."""
+    M, K = qa.shape
+    N = qb.shape[0]
+    if sum_a is None:
+        sum_a = code_rowsum(qa)
+    if sum_b is None:
+        sum_b = code_rowsum(qb)
+    if C is None:
+        C = torch.empty(M, N, dtype=torch.float32, device=qa.device)
+    _check("omq_code_gemm", lib().omq_code_gemm(
+        M, N, K, _p(qa), K, _p(h_a), _p(z_a), _p(sum_a), _p(qb), K, _p(h_b), _p(z_b), _p(sum_b),
+        _p(bias), _p(C), N, _stream()))
     return C
 
 

@@ -22,6 +22,9 @@ struct Dims {
   int64_t group;   // LWC group along C_in: 0 (per output channel) or 128
   int grp;
   bool ffn_only, use_sa;
+  // the forward's four products on integer codes (int8 matrix cores): weights and
+  // activations quantized per row with codes below 128, every C_in a multiple of 16
+  bool codes;
   // LWC quantizer rows per output channel of a weight with C_in = cin
   int64_t g_of(int64_t cin) const { return group ? cin / group : 1; }
 };
@@ -34,6 +37,8 @@ Dims dims_of(const omq_block_desc* b) {
   m.ffn_only = b->ffn_only != 0;
   m.use_sa = !m.ffn_only && b->abits < 16;
   m.group = b->group;
+  m.codes = b->wbits <= 7 && b->abits <= 7 && m.group == 0 && m.d % 16 == 0 && m.F % 16 == 0 &&
+            (m.ffn_only || m.dq % 16 == 0);
   return m;
 }
 
@@ -77,12 +82,14 @@ Theta theta_of(const Dims& m) {
 struct Stats {  // per-row quantizer state
   float *h, *z;
   int32_t *amax, *amin;
+  int32_t* qsum;   // code sums (integer-code products)
 };
 
 Stats take_stats(Bump& b, int64_t n) {
   Stats s;
   s.h = b.take<float>(n); s.z = b.take<float>(n);
   s.amax = b.take<int32_t>(n); s.amin = b.take<int32_t>(n);
+  s.qsum = b.take<int32_t>(n);
   return s;
 }
 
@@ -102,6 +109,8 @@ struct Ws {
   uint16_t *dyb, *gGUb, *dh1b, *gOb, *gYb;
   float *cs, *gs_full, *gd_full, *gsa_full;
   float *rq, *csws, *msews;
+  // integer codes of the forward's product operands (weights, activations)
+  uint8_t *Cqkv, *Co, *Cgu, *Cd, *Cxqkv, *Cxo, *Cxf, *Cxd;
   size_t total;
 };
 
@@ -162,6 +171,14 @@ Ws layout(const Dims& m, void* base) {
   w.rq = b.take<float>(rq / 4);
   w.csws = b.take<float>(colsum_ws_bytes(T, std::max(nqkv, 2 * F)) / 4);
   w.msews = b.take<float>(2048);
+  if (m.codes) {
+    if (att) {
+      w.Cqkv = b.take<uint8_t>(nqkv * d); w.Co = b.take<uint8_t>(d * dq);
+      w.Cxqkv = b.take<uint8_t>(T * d); w.Cxo = b.take<uint8_t>(T * dq);
+    }
+    w.Cgu = b.take<uint8_t>(2 * F * d); w.Cd = b.take<uint8_t>(d * F);
+    w.Cxf = b.take<uint8_t>(T * d); w.Cxd = b.take<uint8_t>(T * F);
+  }
   w.total = b.off;
   return w;
 }
@@ -185,7 +202,8 @@ int check(const omq_block_desc* b) {
 // one linear's weight side: LET-W (s), LWC (theta logits), bias fold (delta)
 hipError_t wfq(const void* W, int64_t rows, int64_t cols, const float* s, const float* delta,
                const float* th, const Theta& t, int l, int wbits, bool fp, uint16_t* out,
-               const Stats& st, int64_t row0, float* Bt, int64_t group, hipStream_t stream) {
+               const Stats& st, int64_t row0, float* Bt, int64_t group, uint8_t* codes,
+               hipStream_t stream) {
   RowQuantFwd a;
   a.x = W; a.x_dt = OMQ_BF16; a.rows = rows; a.cols = cols; a.ldx = cols;
   a.let_mode = (s && !fp) ? OMQ_LET_MUL : OMQ_LET_NONE; a.s = s;
@@ -198,6 +216,7 @@ hipError_t wfq(const void* W, int64_t rows, int64_t cols, const float* s, const 
   const bool grouped = group && a.nbits < 16;
   if (grouped) a.group = group;
   if (!fp && delta && !grouped) { a.fold_delta = delta; a.bias_out = Bt + row0; }
+  if (codes && !fp) { a.codes = codes + row0 * cols; a.qsum = st.qsum + row0; }
   hipError_t e = launch_rowquant_fwd(a, stream);
   if (e == hipSuccess && !fp && delta && (a.nbits >= 16 || grouped))
     e = launch_bias_fold(W, OMQ_BF16, rows, cols, delta, nullptr, Bt + row0, stream);
@@ -207,12 +226,13 @@ hipError_t wfq(const void* W, int64_t rows, int64_t cols, const float* s, const 
 // per-token quantizer with fused LET on its input
 hipError_t aq(const void* X, int x_dt, int64_t T, int64_t C, int64_t ldx, int mode,
               const float* s, const float* delta, int abits, uint16_t* out, const Stats& st,
-              hipStream_t stream) {
+              hipStream_t stream, uint8_t* codes = nullptr) {
   RowQuantFwd a;
   a.x = X; a.x_dt = x_dt; a.rows = T; a.cols = C; a.ldx = ldx;
   a.let_mode = mode; a.s = s; a.delta = delta; a.nbits = abits;
   a.out = out; a.out_dt = OMQ_BF16; a.ldo = C;
   a.h = st.h; a.z = st.z; a.amax = st.amax; a.amin = st.amin;
+  if (codes && abits < 16) { a.codes = codes; a.qsum = st.qsum; }
   return launch_rowquant_fwd(a, stream);
 }
 
@@ -228,6 +248,8 @@ hipError_t run_gemm(const Gemm& g, hipStream_t st, omq_timer* tm) {
     e = hipEventRecord(reinterpret_cast<hipEvent_t>(tm->events[2 * tm->count + 1]), st);
     double f = 2.0 * (double)g.M * (double)g.N * (double)g.K * (double)g.batch;
     tm->flops += f;
+    if (tm->kinds) tm->kinds[tm->count] = g.codes ? 1 : 0;
+    if (g.codes) tm->flops_codes += f;
     tm->count += 1;
   }
   return e;
@@ -239,6 +261,20 @@ hipError_t gemm(const void* A, int64_t lda, const void* B, int64_t ldb, float* C
   Gemm g;
   g.A = A; g.lda = lda; g.B = B; g.ldb = ldb; g.C = C; g.ldc = ldc;
   g.M = M; g.N = N; g.K = K; g.bias = bias; g.resid = resid; g.resid_dt = resid_dt; g.ldr = ldr;
+  return run_gemm(g, st, tm);
+}
+
+// the forward product Y = X_hat W_hat^T (+ bias) (+ resid) on the operands' integer
+// codes: X [T x K] per-token, W [N x K] per-output-channel quantizer rows
+hipError_t code_gemm(const uint8_t* qx, const Stats& sx, const uint8_t* qw, const Stats& sw,
+                     float* C, int64_t ldc, int64_t T, int64_t N, int64_t K, const float* bias,
+                     const void* resid, int resid_dt, int64_t ldr, hipStream_t st,
+                     omq_timer* tm) {
+  Gemm g;
+  g.codes = 1;
+  g.A = qx; g.lda = K; g.B = qw; g.ldb = K; g.C = C; g.ldc = ldc;
+  g.M = T; g.N = N; g.K = K; g.bias = bias; g.resid = resid; g.resid_dt = resid_dt; g.ldr = ldr;
+  g.ha = sx.h; g.za = sx.z; g.sa = sx.qsum; g.hb = sw.h; g.zb = sw.z; g.sb = sw.qsum;
   return run_gemm(g, st, tm);
 }
 
@@ -259,6 +295,7 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
   const int mode_let = fp ? OMQ_LET_NONE : OMQ_LET_DIV;
   const float* xf = nullptr;  // FFN input
   int xf_dt = OMQ_F32;
+  const bool cq = m.codes && !fp;  // forward products on integer codes
   if (!m.ffn_only) {
     const float* s_qkv = fp ? nullptr : th + t.s_qkv;
     const float* d_qkv = fp ? nullptr : th + t.d_qkv;
@@ -272,17 +309,23 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
     CK(launch_rope_tables(T, m.hd, bd->rope_theta, w.cos_t, w.sin_t, st));
     // weight side of q, k, v, o
     CK(wfq(W[LQ], dq, d, s_qkv, d_qkv, th, t, LQ, wb, fp, w.Wqkv, w.wq_qkv, 0, w.Bt_qkv,
-               m.group, st));
+               m.group, cq ? w.Cqkv : nullptr, st));
     CK(wfq(W[LK], dk, d, s_qkv, d_qkv, th, t, LK, wb, fp, w.Wqkv, w.wq_qkv, dq, w.Bt_qkv,
-               m.group, st));
+               m.group, cq ? w.Cqkv : nullptr, st));
     CK(wfq(W[LV], dk, d, s_qkv, d_qkv, th, t, LV, wb, fp, w.Wqkv, w.wq_qkv, dq + dk,
-               w.Bt_qkv, m.group, st));
-    CK(wfq(W[LO], d, dq, s_o, d_o, th, t, LO, wb, fp, w.Wo, w.wq_o, 0, w.Bt_o, m.group, st));
+               w.Bt_qkv, m.group, cq ? w.Cqkv : nullptr, st));
+    CK(wfq(W[LO], d, dq, s_o, d_o, th, t, LO, wb, fp, w.Wo, w.wq_o, 0, w.Bt_o, m.group,
+           cq ? w.Co : nullptr, st));
     // attention input
     CK(launch_rmsnorm(x, OMQ_BF16, T, d, bd->eps, w.xn, w.r1, st));
-    CK(aq(w.xn, OMQ_F32, T, d, d, mode_let, s_qkv, d_qkv, ab, w.Xqkv, w.a_qkv, st));
-    CK(gemm(w.Xqkv, d, w.Wqkv, d, w.Yqkv, nqkv, T, nqkv, d, fp ? nullptr : w.Bt_qkv, nullptr, 0,
-            0, st, tm));
+    CK(aq(w.xn, OMQ_F32, T, d, d, mode_let, s_qkv, d_qkv, ab, w.Xqkv, w.a_qkv, st,
+          cq ? w.Cxqkv : nullptr));
+    if (cq)
+      CK(code_gemm(w.Cxqkv, w.a_qkv, w.Cqkv, w.wq_qkv, w.Yqkv, nqkv, T, nqkv, d, w.Bt_qkv, nullptr,
+                   0, 0, st, tm));
+    else
+      CK(gemm(w.Xqkv, d, w.Wqkv, d, w.Yqkv, nqkv, T, nqkv, d, fp ? nullptr : w.Bt_qkv, nullptr,
+              0, 0, st, tm));
     CK(launch_rope(w.Yqkv, nqkv, T, m.nq, m.hd, w.cos_t, w.sin_t, 0, w.Qr, dq, st));
     CK(launch_rope(w.Yqkv + dq, nqkv, T, m.nkv, m.hd, w.cos_t, w.sin_t, 0, w.Kr, dk, st));
     // s_a on the affinity, then Q/K/V quantized per token
@@ -303,9 +346,14 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
       CK(launch_flash_fwd(f, st));
     }
     // o_proj with its LET site, residual
-    CK(aq(w.O, OMQ_F32, T, dq, dq, mode_let, s_o, d_o, ab, w.Xo, w.a_o, st));
-    CK(gemm(w.Xo, dq, w.Wo, dq, w.h1, d, T, d, dq, fp ? nullptr : w.Bt_o, x, OMQ_BF16, d, st,
-            tm));
+    CK(aq(w.O, OMQ_F32, T, dq, dq, mode_let, s_o, d_o, ab, w.Xo, w.a_o, st,
+          cq ? w.Cxo : nullptr));
+    if (cq)
+      CK(code_gemm(w.Cxo, w.a_o, w.Co, w.wq_o, w.h1, d, T, d, dq, w.Bt_o, x, OMQ_BF16, d, st,
+                   tm));
+    else
+      CK(gemm(w.Xo, dq, w.Wo, dq, w.h1, d, T, d, dq, fp ? nullptr : w.Bt_o, x, OMQ_BF16, d, st,
+              tm));
     CK(launch_rmsnorm(w.h1, OMQ_F32, T, d, bd->eps, w.xn2, w.r2, st));
     xf = w.xn2;
     xf_dt = OMQ_F32;
@@ -315,18 +363,27 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
   }
   // FFN
   CK(wfq(W[LG], F, d, s_ffn, d_ffn, th, t, LG, wb, fp, w.Wgu, w.wq_gu, 0, w.Bt_gu, m.group,
-             st));
+         cq ? w.Cgu : nullptr, st));
   CK(wfq(W[LU], F, d, s_ffn, d_ffn, th, t, LU, wb, fp, w.Wgu, w.wq_gu, F, w.Bt_gu, m.group,
-             st));
+         cq ? w.Cgu : nullptr, st));
   CK(wfq(W[LD], d, F, nullptr, nullptr, th, t, LD, wb, fp, w.Wd, w.wq_d, 0, nullptr, m.group,
-             st));
-  CK(aq(xf, xf_dt, T, d, d, mode_let, s_ffn, d_ffn, ab, w.Xf, w.a_f, st));
-  CK(gemm(w.Xf, d, w.Wgu, d, w.GU, 2 * F, T, 2 * F, d, fp ? nullptr : w.Bt_gu, nullptr, 0, 0, st,
-          tm));
+         cq ? w.Cd : nullptr, st));
+  CK(aq(xf, xf_dt, T, d, d, mode_let, s_ffn, d_ffn, ab, w.Xf, w.a_f, st, cq ? w.Cxf : nullptr));
+  if (cq)
+    CK(code_gemm(w.Cxf, w.a_f, w.Cgu, w.wq_gu, w.GU, 2 * F, T, 2 * F, d, w.Bt_gu, nullptr, 0, 0,
+                 st, tm));
+  else
+    CK(gemm(w.Xf, d, w.Wgu, d, w.GU, 2 * F, T, 2 * F, d, fp ? nullptr : w.Bt_gu, nullptr, 0, 0,
+            st, tm));
   CK(launch_silu_gate(w.GU, T, F, w.A, st));
-  CK(aq(w.A, OMQ_F32, T, F, F, OMQ_LET_NONE, nullptr, nullptr, ab, w.Xd, w.a_d, st));
-  CK(gemm(w.Xd, F, w.Wd, F, w.y, d, T, d, F, nullptr, m.ffn_only ? nullptr : w.h1, OMQ_F32, d,
-          st, tm));
+  CK(aq(w.A, OMQ_F32, T, F, F, OMQ_LET_NONE, nullptr, nullptr, ab, w.Xd, w.a_d, st,
+        cq ? w.Cxd : nullptr));
+  if (cq)
+    CK(code_gemm(w.Cxd, w.a_d, w.Cd, w.wq_d, w.y, d, T, d, F, nullptr,
+                 m.ffn_only ? nullptr : w.h1, OMQ_F32, d, st, tm));
+  else
+    CK(gemm(w.Xd, F, w.Wd, F, w.y, d, T, d, F, nullptr, m.ffn_only ? nullptr : w.h1, OMQ_F32, d,
+            st, tm));
   return OMQ_OK;
 }
 

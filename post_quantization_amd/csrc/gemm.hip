@@ -21,12 +21,16 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace omq {
 
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(16))) int i32x16;
 
 constexpr int BK = 64, LDP = BK;
 
@@ -251,13 +255,18 @@ constexpr int epi_code(int mode, int let, int xf) { return mode | (let << 2) | (
 // DMA: both operands are copied straight into LDS (the launcher only sets it when
 // every tile is full and the operands are 16-byte aligned), K-major ones read back
 // through the transposing LDS read; otherwise both are staged through registers.
-template <int BM, int BN, int WM, int WN, int TA, int TB, int EPI, int DMA>
+// I8: the operands are int8 codes, K contiguous, moved through exactly the same
+// tiles as bf16 pairs (a 64-wide bf16 k-step is 128 codes), and the matrix cores
+// run v_mfma_i32_32x32x32_i8, whose lane holds 16 consecutive codes where the bf16
+// form holds 8 elements: the same 16 bytes.  The epilogue dequantizes.
+template <int BM, int BN, int WM, int WN, int TA, int TB, int EPI, int DMA, int I8 = 0>
 __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m, int tiles_n) {
   constexpr int NT = WM * WN * 64, NW = WM * WN;
   constexpr int FM = BM / WM / 32, FN = BN / WN / 32;   // MFMA blocks per wave
   constexpr bool kDmaA = DMA, kDmaB = DMA;
   static_assert(EPI == 0 || (BM == 128 && BN == 128 && WM * WN == 4),
                 "straight-through epilogue tile");
+  static_assert(!I8 || (EPI == 0 && TA == 0 && TB == 0), "integer codes: plain K-contiguous");
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * LDP];
   uint16_t (*As)[BM * LDP] = reinterpret_cast<uint16_t (*)[BM * LDP]>(smem);
   uint16_t (*Bs)[BN * LDP] = reinterpret_cast<uint16_t (*)[BN * LDP]>(smem + 2 * BM * LDP);
@@ -268,21 +277,25 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
   tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int bz = blockIdx.y;
-  const int64_t kb = 0, ke = g.K;
+  // K extent and leading dimensions in 16-bit units (codes: pairs of bytes)
+  const int64_t kb = 0, ke = I8 ? g.K >> 1 : g.K;
+  const int64_t lda = I8 ? g.lda >> 1 : g.lda, ldb = I8 ? g.ldb >> 1 : g.ldb;
 
-  const uint16_t* A = reinterpret_cast<const uint16_t*>(g.A) + bz * g.strideA;
-  const uint16_t* B = reinterpret_cast<const uint16_t*>(g.B) + (bz / g.b_group) * g.strideB;
+  const uint16_t* A = reinterpret_cast<const uint16_t*>(g.A) + bz * (I8 ? g.strideA >> 1 : g.strideA);
+  const uint16_t* B = reinterpret_cast<const uint16_t*>(g.B) +
+                      (bz / g.b_group) * (I8 ? g.strideB >> 1 : g.strideB);
   const int64_t M = g.M, N = g.N;
 
   Stage<TA, BM, NT> sa;
   Stage<TB, BN, NT> sb;
-  f32x16 acc[FM][FN];
+  typedef std::conditional_t<I8 != 0, i32x16, f32x16> AccT;
+  AccT acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
   // The straight-through epilogue reads x for
   // each of the RW rows a wave finishes, 2 columns per lane, in batches of RB rows
@@ -335,18 +348,25 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
   // ahead of its MFMAs.  One barrier per step.
   const int nk = (int)((ke - kb + BK - 1) / BK);
   if (nk > 0) {
-    if (kDmaA) dma_copy<TA, BM, NW>(A, g.lda, m0, kb, As[0], wid, lane);
-    else { sa.load(A, g.lda, M, m0, kb, ke, tid); sa.store(As[0], tid); }
-    if (kDmaB) dma_copy<TB, BN, NW>(B, g.ldb, n0, kb, Bs[0], wid, lane);
-    else { sb.load(B, g.ldb, N, n0, kb, ke, tid); sb.store(Bs[0], tid); }
+    if (kDmaA) dma_copy<TA, BM, NW>(A, lda, m0, kb, As[0], wid, lane);
+    else { sa.load(A, lda, M, m0, kb, ke, tid); sa.store(As[0], tid); }
+    if (kDmaB) dma_copy<TB, BN, NW>(B, ldb, n0, kb, Bs[0], wid, lane);
+    else { sb.load(B, ldb, N, n0, kb, ke, tid); sb.store(Bs[0], tid); }
     if (nk > 1) {
-      if (!kDmaA) sa.load(A, g.lda, M, m0, kb + BK, ke, tid);
-      if (!kDmaB) sb.load(B, g.ldb, N, n0, kb + BK, ke, tid);
+      if (!kDmaA) sa.load(A, lda, M, m0, kb + BK, ke, tid);
+      if (!kDmaB) sb.load(B, ldb, N, n0, kb + BK, ke, tid);
     }
   }
   if constexpr (DMA) wait_vmem<0>();
   __syncthreads();
   const int fr = lane & 31, fk = (lane >> 5) * 8;
+  auto mfma = [](AccT& c, bf16x8 a, bf16x8 b) {
+    if constexpr (I8)
+      c = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
+                                                __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
+    else
+      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  };
   const int ar = wm * (BM / WM) + fr, br = wn * (BN / WN) + fr;
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
@@ -356,14 +376,14 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
     auto issue_next = [&]() {
       if (kt + 1 < nk) {
         const int64_t k1 = kb + (int64_t)(kt + 1) * BK;
-        if (kDmaA) dma_copy<TA, BM, NW>(A, g.lda, m0, k1, As[buf ^ 1], wid, lane);
-        if (kDmaB) dma_copy<TB, BN, NW>(B, g.ldb, n0, k1, Bs[buf ^ 1], wid, lane);
+        if (kDmaA) dma_copy<TA, BM, NW>(A, lda, m0, k1, As[buf ^ 1], wid, lane);
+        if (kDmaB) dma_copy<TB, BN, NW>(B, ldb, n0, k1, Bs[buf ^ 1], wid, lane);
         if (!kDmaA) sa.store(As[buf ^ 1], tid);
         if (!kDmaB) sb.store(Bs[buf ^ 1], tid);
         if (kt + 2 < nk) {
           const int64_t k2 = kb + (int64_t)(kt + 2) * BK;
-          if (!kDmaA) sa.load(A, g.lda, M, m0, k2, ke, tid);
-          if (!kDmaB) sb.load(B, g.ldb, N, n0, k2, ke, tid);
+          if (!kDmaA) sa.load(A, lda, M, m0, k2, ke, tid);
+          if (!kDmaB) sb.load(B, ldb, N, n0, k2, ke, tid);
         }
       }
     };
@@ -396,8 +416,7 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cu][i], bf[cu][j], acc[i][j],
-                                                                0, 0, 0);
+            mfma(acc[i][j], af[cu][i], bf[cu][j]);
       }
     } else {
       bf16x8 af[BK / 16][FM], bf[BK / 16][FN];
@@ -415,8 +434,7 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk][i], bf[kk][j], acc[i][j],
-                                                                0, 0, 0);
+            mfma(acc[i][j], af[kk][i], bf[kk][j]);
     }
     // the direct copies into the other buffer must land before the barrier
     if constexpr (DMA) {
@@ -622,46 +640,152 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
   }
   float* C = g.C ? g.C + bz * g.strideC : nullptr;
   uint16_t* Cb = g.Cb ? g.Cb + bz * g.strideC : nullptr;
-  if (m0 + BM <= M && n0 + BN <= N && !g.resid && !g.accumulate && !Cb) {
-    // whole tile, plain fp32 store (+ bias): no per-element conditions
+  // the lane's columns (one per 32-column block) and the first of its rows; a
+  // lane holds rows row0 + 32 i + 8 (r / 4) + r % 4 of accumulator (i, j, r)
+  int64_t gnj[FN];
+  float bias[FN];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int64_t gn = n0 + wn * (BN / WN) + j * 32 + (lane & 31);
-      const float bias = g.bias ? g.bias[gn] : 0.f;
-      float* Cc = C + (m0 + wm * (BM / WM) + 4 * (lane >> 5)) * g.ldc + gn;
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          Cc[(i * 32 + 8 * (r >> 2) + (r & 3)) * g.ldc] = g.alpha * acc[i][j][r] + bias;
-    }
-    return;
+  for (int j = 0; j < FN; ++j) {
+    gnj[j] = n0 + wn * (BN / WN) + j * 32 + (lane & 31);
+    bias[j] = (g.bias && gnj[j] < N) ? g.bias[gnj[j]] : 0.f;
   }
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
+  const int lr0 = wm * (BM / WM) + 4 * (lane >> 5);
+  const int64_t row0 = m0 + lr0;
+  // Integer codes: C = ha hb (S - zb Ra - za (Rb - K zb)) with S the integer sum of
+  // code products and Ra, Rb the rows' code sums, i.e. sum_k (qa - za)(qb - zb)
+  // without rounding (every term an integer below 2^53), then one rounding to
+  // float.  The rows' and columns' (h, z, code sum) go through LDS (the K loop
+  // ended on a barrier, so the operand buffers are free).
+  float* qs = reinterpret_cast<float*>(smem);      // [3][BM] rows, then [3][BN] columns
+  double hb[FN], zb[FN], cb[FN];
+  if constexpr (I8) {
+    for (int t = tid; t < BM; t += NT) {
+      const int64_t gm = m0 + t;
+      const bool ok = gm < M;
+      qs[t] = ok ? g.ha[gm] : 0.f;
+      qs[BM + t] = ok ? g.za[gm] : 0.f;
+      qs[2 * BM + t] = ok ? (float)g.sa[gm] : 0.f;
+    }
+    for (int t = tid; t < BN; t += NT) {
+      const int64_t gn = n0 + t;
+      const bool ok = gn < N;
+      qs[3 * BM + t] = ok ? g.hb[gn] : 0.f;
+      qs[3 * BM + BN + t] = ok ? g.zb[gn] : 0.f;
+      qs[3 * BM + 2 * BN + t] = ok ? (float)g.sb[gn] : 0.f;
+    }
+    __syncthreads();
+    const double Kd = (double)g.K;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int64_t gn = n0 + wn * (BN / WN) + j * 32 + (lane & 31);
-      if (gn >= N) continue;
-      const float bias = g.bias ? g.bias[gn] : 0.f;
+      const int col = wn * (BN / WN) + j * 32 + (lane & 31);
+      hb[j] = (double)qs[3 * BM + col];
+      zb[j] = (double)qs[3 * BM + BN + col];
+      cb[j] = (double)qs[3 * BM + 2 * BN + col] - Kd * zb[j];
+    }
+  }
+  // Whole tiles take every load and store of a 32-row slice without per-element
+  // conditions, so each slice's residual (and accumulated C) reads are in flight
+  // together; partial tiles check every element.
+  const bool whole = m0 + BM <= M && n0 + BN <= N;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t gm = m0 + wm * (BM / WM) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (gm >= M) continue;
-        float v = g.alpha * acc[i][j][r] + bias;
-        if (g.resid) {
-          v += g.resid_dt == OMQ_F32
-                   ? reinterpret_cast<const float*>(g.resid)[gm * g.ldr + gn]
-                   : bf16_to_f32(reinterpret_cast<const uint16_t*>(g.resid)[gm * g.ldr + gn]);
-        }
-        if (Cb) {
-          Cb[gm * g.ldc + gn] = f32_to_bf16(v);
+  for (int i = 0; i < FM; ++i) {
+    float v[FN][16];
+    if constexpr (I8) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int rb = lr0 + i * 32 + 8 * r4;
+        const float4 h4 = *reinterpret_cast<const float4*>(&qs[rb]);
+        const float4 z4 = *reinterpret_cast<const float4*>(&qs[BM + rb]);
+        const float4 s4 = *reinterpret_cast<const float4*>(&qs[2 * BM + rb]);
+        const float hr[4] = {h4.x, h4.y, h4.z, h4.w}, zr[4] = {z4.x, z4.y, z4.z, z4.w};
+        const float sr[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const double S = (double)acc[i][j][4 * r4 + q];
+            const double D = fma(-(double)zr[q], cb[j], fma(-zb[j], (double)sr[q], S));
+            v[j][4 * r4 + q] = (float)(((double)hr[q] * hb[j]) * D) + bias[j];
+          }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[j][r] = g.alpha * acc[i][j][r] + bias[j];
+    }
+    const int64_t ri = row0 + i * 32;
+    auto roff = [](int r) { return 8 * (r >> 2) + (r & 3); };
+    if (whole) {
+      if (g.resid) {
+        float rv[FN][16];
+        if (g.resid_dt == OMQ_F32) {
+          const float* R = reinterpret_cast<const float*>(g.resid) + ri * g.ldr;
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) rv[j][r] = R[roff(r) * g.ldr + gnj[j]];
         } else {
-          if (g.accumulate) v += C[gm * g.ldc + gn];
-          C[gm * g.ldc + gn] = v;
+          const uint16_t* R = reinterpret_cast<const uint16_t*>(g.resid) + ri * g.ldr;
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) rv[j][r] = bf16_to_f32(R[roff(r) * g.ldr + gnj[j]]);
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) v[j][r] += rv[j][r];
+      }
+      if (Cb) {
+        uint16_t* Cr = Cb + ri * g.ldc;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) Cr[roff(r) * g.ldc + gnj[j]] = f32_to_bf16(v[j][r]);
+      } else {
+        float* Cr = C + ri * g.ldc;
+        if (g.accumulate) {
+          float cv[FN][16];
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) cv[j][r] = Cr[roff(r) * g.ldc + gnj[j]];
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) v[j][r] += cv[j][r];
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) Cr[roff(r) * g.ldc + gnj[j]] = v[j][r];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int64_t gn = gnj[j];
+        if (gn >= N) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t gm = ri + roff(r);
+          if (gm >= M) continue;
+          float x = v[j][r];
+          if (g.resid) {
+            x += g.resid_dt == OMQ_F32
+                     ? reinterpret_cast<const float*>(g.resid)[gm * g.ldr + gn]
+                     : bf16_to_f32(reinterpret_cast<const uint16_t*>(g.resid)[gm * g.ldr + gn]);
+          }
+          if (Cb) {
+            Cb[gm * g.ldc + gn] = f32_to_bf16(x);
+          } else {
+            if (g.accumulate) x += C[gm * g.ldc + gn];
+            C[gm * g.ldc + gn] = x;
+          }
         }
       }
     }
+  }
 }
 
 template <int BM, int BN, int WM, int WN>
@@ -699,6 +823,15 @@ void launch_dma(const Gemm& g, hipStream_t st) {
   else
     hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, 1, 1, 0, 1>), grid, block, 0, st, g, tiles_m,
                        tiles_n);
+}
+
+// integer-code operands (K contiguous): direct copies when every tile is whole
+template <int BM, int BN, int WM, int WN, int DMA>
+void launch_codes(const Gemm& g, hipStream_t st) {
+  const int tiles_m = (int)((g.M + BM - 1) / BM), tiles_n = (int)((g.N + BN - 1) / BN);
+  const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)g.batch), block(WM * WN * 64);
+  hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, 0, 0, 0, DMA, 1>), grid, block, 0, st, g,
+                     tiles_m, tiles_n);
 }
 
 // Direct LDS copies need whole tiles (no bounds checks), whole K steps and 16-byte
@@ -819,8 +952,33 @@ void gemm_ste_extents(int64_t rows, int64_t cols, int64_t* nslabs, int64_t* ntil
   *ntiles = (rows + kSteBM - 1) / kSteBM;
 }
 
+// Integer codes: K and the leading dimensions in bytes, multiples of 16 (whole
+// 16-byte chunks), rows 16-byte aligned; K up to 2^17 keeps every sum of code
+// products in int32 and every code sum exact in float.  Tiles as for bf16, on the
+// operands' 16-bit view.
+hipError_t launch_gemm_codes(const Gemm& g, hipStream_t st) {
+  auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  if (g.ta || g.tb || g.ste.mode || g.batch != 1) return hipErrorInvalidValue;
+  if (g.K % 16 || g.lda % 16 || g.ldb % 16 || g.K > (1 << 17) || !al16(g.A) || !al16(g.B))
+    return hipErrorInvalidValue;
+  if (!g.ha || !g.za || !g.sa || !g.hb || !g.zb || !g.sb) return hipErrorInvalidValue;
+  Gemm v = g;                                     // the 16-bit view
+  v.K = g.K / 2;
+  v.lda = g.lda / 2;
+  v.ldb = g.ldb / 2;
+  const int64_t big_tiles = (g.M / 256) * (g.N / 256);
+  if (big_tiles >= 512 && dma_fits(v, 256, 256))
+    launch_codes<256, 256, 2, 4, 1>(g, st);
+  else if (dma_fits(v, 128, 128))
+    launch_codes<128, 128, 2, 2, 1>(g, st);
+  else
+    launch_codes<128, 128, 2, 2, 0>(g, st);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(const Gemm& g, hipStream_t st) {
   if (g.M == 0 || g.N == 0 || g.batch == 0) return hipSuccess;
+  if (g.codes) return launch_gemm_codes(g, st);
   if (g.dt == OMQ_BF16 && g.ste.mode != 0) return launch_ste(g, st);
   if (g.dt == OMQ_BF16) {
     // 256 x 256 tiles halve the operand traffic per flop; they pay once there are

@@ -18,6 +18,7 @@ struct RowQuantFwd {
   void* out = nullptr;  int out_dt = 0;  int64_t ldo = 0;
   float* h = nullptr;  float* z = nullptr;  int32_t* amax = nullptr;  int32_t* amin = nullptr;
   uint8_t* codes = nullptr;                         // [rows x cols], ld = cols
+  int32_t* qsum = nullptr;                          // per-row sum of the codes (group 0)
   const float* fold_delta = nullptr;                // bias fold: sum_i fold_delta_i x_ri
   const float* bias = nullptr;  float* bias_out = nullptr;
   // 128: each run of 128 columns of a row is its own quantizer (group-wise LWC);
@@ -104,10 +105,20 @@ struct Gemm {
   float alpha = 1.f;
   int accumulate = 0;
   int dt = 1;                                       // OMQ_BF16 or OMQ_F32 operands
+  // Integer-code product (dt ignored): A, B are uint8 codes [M x K], [N x K] (K
+  // contiguous, ta = tb = 0, lda/ldb in bytes, values < 128) of row quantizers
+  // with steps ha/hb, zero points za/zb and code sums sa/sb per row; C =
+  // ha hb sum_k (qa - za)(qb - zb) (+ bias) (+ resid) (+ C), alpha unused.
+  int codes = 0;
+  const float *ha = nullptr, *za = nullptr, *hb = nullptr, *zb = nullptr;
+  const int32_t *sa = nullptr, *sb = nullptr;
   int ta = 0, tb = 0;                               // A is [K x M] / B is [K x N]
   SteEpi ste;                                       // bf16 only; mode 2 writes dL/dx into C
 };
 hipError_t launch_gemm(const Gemm& g, hipStream_t st);
+// sums[r] = sum_c codes[r * ld + c]
+hipError_t launch_code_rowsum(const uint8_t* codes, int64_t rows, int64_t cols, int64_t ld,
+                              int32_t* sums, hipStream_t st);
 // The fused form's partial-buffer extents for a C of rows x cols.
 void gemm_ste_extents(int64_t rows, int64_t cols, int64_t* nslabs, int64_t* ntiles);
 

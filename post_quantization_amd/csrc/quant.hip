@@ -29,6 +29,15 @@ OMQ_DEV float let_x(float x, int mode, const float* s, const float* delta, int64
   return x;
 }
 
+// the block's code sum into *out (every thread of the 4-wave block calls it)
+OMQ_DEV void block_qsum(int qs, int32_t* out) {
+  __shared__ int s_qs[4];
+  qs = wave_sum(qs);
+  if ((threadIdx.x & 63) == 0) s_qs[wave_id()] = qs;
+  __syncthreads();
+  if (threadIdx.x == 0) *out = s_qs[0] + s_qs[1] + s_qs[2] + s_qs[3];
+}
+
 // ---------------------------------------------------------------------------
 // forward: one 256-thread block per row
 // ---------------------------------------------------------------------------
@@ -94,6 +103,7 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd(RowQuantFwd a) {
     if (a.bias_out) a.bias_out[r] = (a.bias ? a.bias[r] : 0.f) + D;
   }
   const float rh = 1.f / q.h;
+  int qs = 0;
   for (int64_t c = (int64_t)tid * 4; c < cols; c += 4 * kThreads) {
     float v[4], o[4];
     load4(xr, XDT, c, v);
@@ -106,10 +116,12 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd(RowQuantFwd a) {
       float qq = fminf(fmaxf(rr, 0.f), q.Q);
       o[j] = (qq - q.z) * q.h;
       cw |= ((uint32_t)qq) << (8 * j);
+      qs += (int)qq;
     }
     store4(a.out, a.out_dt, r * a.ldo + c, o);
     if (a.codes) *reinterpret_cast<uint32_t*>(a.codes + r * cols + c) = cw;
   }
+  if (a.qsum) block_qsum(qs, a.qsum + r);
 }
 
 // Single-pass variant: the row (up to NCH * 1024 elements) stays in registers
@@ -180,6 +192,7 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_reg(RowQuantFwd a) {
     if (a.bias_out) a.bias_out[r] = (a.bias ? a.bias[r] : 0.f) + D;
   }
   const float rh = 1.f / q.h;
+  int qs = 0;
 #pragma unroll
   for (int k = 0; k < NCH; ++k) {
     const int64_t c = ((int64_t)k * kThreads + tid) * 4;
@@ -193,11 +206,13 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_reg(RowQuantFwd a) {
         const float qq = fminf(fmaxf(rr, 0.f), q.Q);
         o[j] = (qq - q.z) * q.h;
         cw |= ((uint32_t)qq) << (8 * j);
+        qs += (int)qq;
       }
       store4(a.out, a.out_dt, r * a.ldo + c, o);
       if (a.codes) *reinterpret_cast<uint32_t*>(a.codes + r * cols + c) = cw;
     }
   }
+  if (a.qsum) block_qsum(qs, a.qsum + r);
 }
 
 // One wave per row (rows up to NC * 512 elements): each lane keeps NC chunks of
@@ -367,18 +382,21 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_wave(RowQuantFwd a) {
       }
     }
   }
+  int qs = 0;
 #pragma unroll
   for (int k = 0; k < NC; ++k) {
     const int64_t c = ((int64_t)k * 64 + lane) * 8;
     if (FULL || c < cols) {
       float o[8];
       uint32_t cw[2] = {0u, 0u};
+      const int n = FULL || c + 8 <= cols ? 8 : 4;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float rr = xt[k][j] + q.z;
         const float qq = fminf(fmaxf(rr, 0.f), q.Q);
         o[j] = (qq - q.z) * q.h;
         cw[j >> 2] |= ((uint32_t)qq) << (8 * (j & 3));
+        if (j < n) qs += (int)qq;
       }
       store4(a.out, a.out_dt, r * a.ldo + c, o);
       if (a.codes) *reinterpret_cast<uint32_t*>(a.codes + r * cols + c) = cw[0];
@@ -387,6 +405,10 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_wave(RowQuantFwd a) {
         if (a.codes) *reinterpret_cast<uint32_t*>(a.codes + r * cols + c + 4) = cw[1];
       }
     }
+  }
+  if (a.qsum) {
+    qs = wave_sum(qs);
+    if (lane == 0) a.qsum[r] = qs;
   }
 }
 
@@ -523,6 +545,7 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_lds(RowQuantFwd a) {
   const float rh = 1.f / q.h;
   const float thr = fmaxf(fabsf(vmax), fabsf(vmin)) * rh * 0x1p-20f;
   const bool want_codes = a.codes != nullptr;
+  int qs = 0;
 #pragma unroll 2
   for (int k = 0; k < NC; ++k) {
     const int64_t c = ((int64_t)k * 64 + lane) * 8;
@@ -551,9 +574,16 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_lds(RowQuantFwd a) {
     if (want_codes) {
       uint32_t cw[2] = {0u, 0u};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) cw[j >> 2] |= ((uint32_t)qq[j]) << (8 * (j & 3));
+      for (int j = 0; j < 8; ++j) {
+        cw[j >> 2] |= ((uint32_t)qq[j]) << (8 * (j & 3));
+        qs += (int)qq[j];
+      }
       *reinterpret_cast<uint2*>(a.codes + r * a.cols + c) = make_uint2(cw[0], cw[1]);
     }
+  }
+  if (a.qsum) {
+    qs = wave_sum(qs);
+    if (lane == 0) a.qsum[r] = qs;
   }
 }
 
@@ -1080,6 +1110,8 @@ bool launch_fwd_reg(const RowQuantFwd& a, hipStream_t st) {
 
 hipError_t launch_rowquant_fwd(const RowQuantFwd& a, hipStream_t st) {
   if (a.rows == 0 || a.cols == 0) return hipSuccess;
+  // code sums come with the codes, per whole row
+  if (a.qsum && (!a.codes || a.group > 0 || a.nbits >= 16)) return hipErrorInvalidValue;
   if (a.group > 0) {           // groups of 128 (the caller checked cols % 128 == 0)
     if (a.group != 128 || a.cols % 128 || a.nbits >= 16 || a.fold_delta)
       return hipErrorInvalidValue;
@@ -1103,6 +1135,28 @@ hipError_t launch_rowquant_fwd(const RowQuantFwd& a, hipStream_t st) {
     hipLaunchKernelGGL(k_rowquant_fwd<OMQ_F32>, grid, dim3(kThreads), 0, st, a);
   else
     hipLaunchKernelGGL(k_rowquant_fwd<OMQ_BF16>, grid, dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+// sums of uint8 codes per row: one wave per row (off the calibration path, where the
+// quantizer forms the sums while it writes the codes)
+__global__ __launch_bounds__(kThreads) void k_code_rowsum(const uint8_t* codes, int64_t rows,
+                                                          int64_t cols, int64_t ld, int32_t* sums) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + wave_id();
+  if (r >= rows) return;
+  const uint8_t* p = codes + r * ld;
+  int s = 0;
+  for (int64_t c = lane; c < cols; c += 64) s += p[c];
+  s = wave_sum(s);
+  if (lane == 0) sums[r] = s;
+}
+
+hipError_t launch_code_rowsum(const uint8_t* codes, int64_t rows, int64_t cols, int64_t ld,
+                              int32_t* sums, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_code_rowsum, dim3((unsigned)((rows + 3) / 4)), dim3(kThreads), 0, st, codes,
+                     rows, cols, ld, sums);
   return hipGetLastError();
 }
 

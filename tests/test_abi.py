@@ -27,7 +27,7 @@ def test_every_declared_symbol_is_exported():
     assert len(names) >= 20
     for n in names:
         assert hasattr(L, n), n
-    assert omq.abi_version() == 2
+    assert omq.abi_version() == 3
 
 
 def test_status_strings():
@@ -67,6 +67,16 @@ def test_validation_before_launch():
     assert L.omq_gemm(4, 4, 16, FAKE, 8, 0, FAKE, 16, 0, 1, None, 1.0, FAKE, 4, 0, None) == -2
     # transposed A: its contiguous extent is M (here 12, not a multiple of 8)
     assert L.omq_gemm(12, 8, 16, FAKE, 12, 1, FAKE, 16, 0, 1, None, 1.0, FAKE, 8, 0, None) == -4
+    # integer-code product: K, lda, ldb multiples of 16, 16-byte aligned codes, K <= 2^17
+    assert L.omq_code_gemm(4, 4, 24, FAKE, 24, FAKE, FAKE, FAKE, FAKE, 24, FAKE, FAKE, FAKE,
+                           None, FAKE, 4, None) == -4
+    assert L.omq_code_gemm(4, 4, 32, FAKE + 8, 32, FAKE, FAKE, FAKE, FAKE, 32, FAKE, FAKE, FAKE,
+                           None, FAKE, 4, None) == -4
+    assert L.omq_code_gemm(4, 4, 32, FAKE, 32, FAKE, FAKE, None, FAKE, 32, FAKE, FAKE, FAKE,
+                           None, FAKE, 4, None) == -1
+    assert L.omq_code_gemm(4, 4, 1 << 18, FAKE, 1 << 18, FAKE, FAKE, FAKE, FAKE, 1 << 18, FAKE,
+                           FAKE, FAKE, None, FAKE, 4, None) == -2
+    assert L.omq_code_rowsum(FAKE, 4, 32, 16, FAKE, None) == -2
     # unsupported LWC group (only per channel or 128 input channels)
     assert L.omq_lwc_fakequant(FAKE, 1, 4, 256, 64, 4, FAKE, FAKE, None, None, None, FAKE, 1,
                                FAKE, FAKE, FAKE, FAKE, None, None, None) == -2

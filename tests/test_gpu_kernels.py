@@ -268,6 +268,45 @@ def test_gemm(M, N, K, dt, ta, tb):
     assert rel(host(C2)[rows], 1.5 * (A[rows].astype(np.float64) @ B.astype(np.float64).T) + bias) < 2e-5
 
 
+@pytest.mark.parametrize("M,N,K,abits,wbits", [
+    (256, 384, 4096, 4, 4),       # whole tiles: direct LDS copies
+    (200, 136, 1376, 4, 3),       # ragged rows, columns and k-steps: register staging
+    (512, 768, 11008, 7, 4),      # the FFN down width, 7-bit codes
+    (2048, 1024, 512, 4, 2)])
+def test_code_gemm(M, N, K, abits, wbits):
+    """The product on integer codes against the oracle's code product, with the codes,
+    steps and zero points the oracle's quantizers give for synthetic activations
+    (a few all-positive token rows, whose zero point lies below the code range) and
+    LWC weights; the code sums through omq_code_rowsum, bit for bit against numpy.
+    The kernel's integer sum is exact and rounded once, so the bound is a float32
+    rounding of the result and of the bias addition."""
+    log("code_gemm", M, N, K, abits, wbits)
+    rng = np.random.default_rng(M + N + K)
+    X = synth.normal(91, M, (M, K), 1.0)
+    X[::37] += 6.0
+    W = synth.normal(92, N, (N, K), synth.WEIGHT_STD)
+    sx, _ = quant.act_quant(X, abits)
+    ag, ab, _, _, B = _params(rng, N, K)
+    wq = quant.lwc_fakequant(W, ag, ab, wbits)
+    assert (sx.z < 0).any()
+    qa, qb = dev(sx.codes, torch.uint8), dev(wq.codes, torch.uint8)
+    sa, sb = omq.code_rowsum(qa), omq.code_rowsum(qb)
+    assert np.array_equal(host(sa), sx.codes.astype(np.int64).sum(1))
+    assert np.array_equal(host(sb), wq.codes.astype(np.int64).sum(1))
+    C = omq.code_gemm(qa, dev(sx.h), dev(sx.z), qb, dev(wq.h), dev(wq.z), sa, sb, bias=dev(B))
+    torch.cuda.synchronize()
+    want = quant.code_product(sx.codes, sx.h, sx.z, wq.codes, wq.h, wq.z, B)
+    got = host(C).astype(np.float64)
+    err = np.abs(got - want)
+    # (plus the oracle's own float64 summation error, relative to sum |terms|)
+    absa = np.abs(sx.codes - sx.z[:, None]) * sx.h[:, None]
+    absb = np.abs(wq.codes - wq.z[:, None]) * wq.h[:, None]
+    bound = 2.0 ** -23 * (np.abs(want - B[None, :]) + 2 * np.abs(B)[None, :]) + \
+        2.0 ** -40 * (absa @ absb.T) + 1e-30
+    log("max err / bound %.3f" % (err / bound).max())
+    assert (err <= bound).all()
+
+
 @pytest.mark.parametrize("c_out,c_in,nbits,let", [(77, 200, 4, True), (96, 4096, 2, True),
                                                   (64, 11008, 3, False), (4096, 4096, 4, True)])
 def test_lwc_backward(c_out, c_in, nbits, let):

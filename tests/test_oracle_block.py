@@ -171,3 +171,39 @@ def test_let_gradients_vanish_without_quantizers():
         else:
             # LET parameters: the act-side and weight-side terms cancel
             assert np.abs(v).max() < 1e-5 * max(1.0, loss), (n, np.abs(v).max())
+
+
+def test_forward_code_products_are_the_quantized_products():
+    """With the bf16 path's code-product policy (W4A4, per-channel, widths a multiple
+    of 16) each of the forward's quantized products equals the product written on
+    the integer codes (section "LWC": (q - z) h per row) plus the folded bias, and
+    the backward keeps its bf16 operands; with 8-bit codes or group-wise weights the
+    policy is off."""
+    c = _cfg(T=32, d=64, F=96, n_q=2, n_kv=2, head_dim=32, wbits=4, abits=4)
+    ops = ExactOps(bf16=True)
+    assert ops.code_product(c)
+    assert not ops.code_product(_cfg(T=32, d=64, F=96, n_q=2, n_kv=2, head_dim=32, wbits=8,
+                                     abits=4))
+    assert not ops.code_product(_cfg(T=32, d=64, F=96, n_q=2, n_kv=2, head_dim=32, wbits=4,
+                                     abits=4, group=32))
+    assert not ops.code_product(_cfg(T=32, d=64, F=40, n_q=2, n_kv=2, head_dim=32, wbits=4,
+                                     abits=4))
+    inp = synth.block_inputs(c)
+    Wd = {k: v for k, v in inp.items() if k.startswith("W_")}
+    shapes = synth.block_weight_shapes(c)
+    th = _random_theta(c, shapes, np.random.default_rng(5))
+    _, S = ob.forward(c, inp["x"], Wd, th, ops)
+    from oracle import quant
+    for name, act in (("q", "a_qkv"), ("v", "a_qkv"), ("o", "a_o"), ("up", "a_ffn"),
+                      ("down", "a_down")):
+        L = S.lin[name]
+        a = ops.states[act]
+        want = quant.code_product(a.codes, a.h, a.z, L.wst.codes, L.wst.h, L.wst.z)
+        site = {"q": "qkv", "v": "qkv", "o": "o", "up": "ffn"}.get(name)
+        if site is not None:
+            delta = th["delta_" + site] if site != "o" else ob.kv_broadcast(
+                th["delta_o"], c.n_q, c.n_kv, c.head_dim)
+            want = want + quant.bias_fold(L.W, None, delta)[None, :]
+        assert np.allclose(L.Y, want, rtol=1e-6, atol=1e-6 * np.abs(want).max()), name
+        # the backward's operand is the bf16 rounding of the same weight
+        assert np.array_equal(L.Wop, quant.bf16(L.wst.xhat.reshape(L.Wop.shape)))

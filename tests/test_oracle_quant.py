@@ -242,3 +242,38 @@ def test_group_lwc_minmax(nbits):
             assert np.all(np.abs(r.W_hat[o, k * g:(k + 1) * g] - x) <= h / 2 * (1 + 1e-5) + 1e-12)
             for c in range(0, g, 37):
                 assert r.codes[o, k * g + c] == _nearest_code(float(x[c] / h), z, Q)
+
+
+def test_code_product_brute_force_integers():
+    """The code product against exact integer arithmetic on a tiny case: every entry
+    is h_a h_b times an integer sum, formed here with Python ints, including rows
+    whose zero point lies outside the code range (all-positive / all-negative rows)."""
+    rng = np.random.default_rng(7)
+    qa = rng.integers(0, 16, size=(3, 5))
+    qb = rng.integers(0, 16, size=(4, 5))
+    z_a = np.array([3.0, -21.0, 40.0])
+    z_b = np.array([0.0, 15.0, -7.0, 8.0])
+    h_a = np.array([0.5, 0.25, 2.0 ** -6])
+    h_b = np.array([1.0, 0.125, 4.0, 2.0 ** -3])
+    bias = np.array([1.0, -2.0, 0.5, 0.0])
+    got = quant.code_product(qa, h_a, z_a, qb, h_b, z_b, bias)
+    for m in range(3):
+        for n in range(4):
+            s = sum((int(qa[m, k]) - int(z_a[m])) * (int(qb[n, k]) - int(z_b[n]))
+                    for k in range(5))
+            assert got[m, n] == s * h_a[m] * h_b[n] + bias[n]   # powers of two: exact
+
+
+def test_code_product_matches_fake_quant_product():
+    """On the quantizers' own outputs the code product is X_hat W_hat^T: the
+    fake-quantized operands are (q - z) h rounded once to float32."""
+    rng = np.random.default_rng(3)
+    X = rng.standard_normal((16, 64)).astype(np.float32)
+    X[3] += 4.0                                   # an all-positive token row: z < 0
+    W = rng.standard_normal((8, 64)).astype(np.float32)
+    sx, Xh = quant.act_quant(X, 4)
+    ref = quant.lwc_fakequant(W, np.full(8, 1.5, np.float32), np.full(8, 0.7, np.float32), 4)
+    assert sx.z[3] < 0
+    got = quant.code_product(sx.codes, sx.h, sx.z, ref.codes, ref.h, ref.z)
+    want = Xh.astype(np.float64) @ ref.W_hat.astype(np.float64).T
+    assert np.allclose(got, want, rtol=1e-6, atol=1e-6 * np.abs(want).max())
