@@ -125,3 +125,59 @@ def test_block_step(kind):
                              optim.adamw(vec[n_lwc:], gv[n_lwc:], z[n_lwc:], z[n_lwc:], 1,
                                          c.lr_let)[0]])
     assert rel(host(theta) - vec, expect - vec) < 1e-4
+
+
+def test_block_full_size_forward_and_step():
+    """The bench's workload at its full size (7B-shaped block, W4A4, T 2048, d 4096,
+    32 heads, F 11008) in the launch configuration the bench times: the
+    full-precision target and the quantized forward against the oracle's whole
+    forward (the oracle finishes it in about half a minute), the step's loss
+    against the oracle's loss on the same target, and properties of the step that
+    hold at any size: a finite gradient that is nonzero in every parameter group,
+    and AdamW's first update (-lr times the sign of the gradient wherever the
+    gradient dwarfs eps)."""
+    c = synth.BLOCK_CFG4
+    log("full-size block", c)
+    inp = synth.block_inputs(c)
+    Wd = {k: v for k, v in inp.items() if k.startswith("W_")}
+    x = inp["x"]
+    shapes = synth.block_weight_shapes(c)
+    th = random_theta(c, np.random.default_rng(11))
+    ystar = ob.reference(c, x, Wd)
+    y, _ = ob.forward(c, x, Wd, th, ExactOps(bf16=True))
+    loss = float(np.mean((y - ystar) ** 2))
+    log("oracle loss", loss)
+
+    d = desc_of(c)
+    offs, n_lwc, total = omq.block_theta_layout(d)
+    ws = torch.empty(omq.block_workspace_size(d), dtype=torch.uint8, device=DEV)
+    tx = dev(x, torch.bfloat16)
+    W = upload_weights(c, inp)
+    vec = ob.pack(c, shapes, th)
+    theta = dev(vec)
+    yfp = torch.empty(c.T, c.d, dtype=torch.float32, device=DEV)
+    omq.block_forward(d, tx, W, None, yfp, ws)
+    yq = torch.empty_like(yfp)
+    omq.block_forward(d, tx, W, theta, yq, ws)
+    torch.cuda.synchronize()
+    e_fp, e_q = rel(host(yfp), ystar), rel(host(yq), y)
+    log("y fp rel", e_fp, "y quant rel", e_q)
+    assert e_fp < TOL and e_q < TOL
+    dth = torch.zeros_like(theta)
+    m = torch.zeros_like(theta)
+    v = torch.zeros_like(theta)
+    tl = torch.zeros(1, dtype=torch.float32, device=DEV)
+    omq.block_step(d, tx, dev(ystar), W, theta, dth, m, v, 1, tl, ws)
+    torch.cuda.synchronize()
+    lg = float(host(tl)[0])
+    log("gpu loss", lg)
+    assert abs(lg - loss) <= TOL * loss
+    gv = host(dth)
+    assert np.isfinite(gv).all()
+    gg = ob.unpack(c, shapes, gv)
+    for name, _ in ob.theta_layout(c, shapes):
+        assert np.abs(gg[name]).max() > 0, name
+    lr = np.where(np.arange(total) < n_lwc, c.lr_lwc, c.lr_let)
+    big = np.abs(gv) > 1e-5
+    step = host(theta) - vec
+    assert np.allclose(step[big], -lr[big] * np.sign(gv[big]), rtol=1e-2, atol=1e-6)
