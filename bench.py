@@ -439,24 +439,44 @@ def main():
     torch.cuda.synchronize()
     loss_first = float(loss.cpu()[0]) if args.warmup else None
 
-    timer.reset()
     t0 = time.perf_counter()
     e0.record()
     for _ in range(args.steps):
         step += 1
-        omq.block_step(dt_, x, y_t, W, theta, dtheta, m, v, step, loss, ws)
+        omq.block_step(d, x, y_t, W, theta, dtheta, m, v, step, loss, ws)
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / args.steps
     loss_last = float(loss.cpu()[0])
+    # the same number of steps again with per-launch events (outside the timed
+    # region, so the event records do not weigh on `value`)
+    timer.reset()
+    for _ in range(args.steps):
+        step += 1
+        omq.block_step(dt_, x, y_t, W, theta, dtheta, m, v, step, loss, ws)
+    torch.cuda.synchronize()
     durs = timer.durations_ms()
     kinds = timer.kinds()
-    gemm_ms = sum(durs)
+    work = timer.work()
+    gemm_ms = sum(t for t, k in zip(durs, kinds) if k in (omq.TIMED_GEMM, omq.TIMED_GEMM_I8))
+    # the fake quantizers of the forward: algorithmic HBM bytes per launch over its time
+    hbm = {}
+    for name, kind in (("weight_fake_quant", omq.TIMED_WEIGHT_QUANT),
+                       ("act_quant", omq.TIMED_ACT_QUANT)):
+        d_ = [t for t, k in zip(durs, kinds) if k == kind]
+        b_ = [b for b, k in zip(work, kinds) if k == kind]
+        if d_:
+            gbs = sum(b_) / (sum(d_) * 1e-3) / 1e9
+            hbm[name] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "launches": len(d_), "avg_launch_us": round(sum(d_) / len(d_) * 1e3, 2),
+                         "bytes_per_launch": round(sum(b_) / len(b_)),
+                         "share_of_step": round(sum(d_) / (ms * args.steps), 4)}
     # the bf16 matrix-core GEMMs (every backward product; the forward's too unless
     # it runs on integer codes) and the int8 code products, each against its peak
-    bf_d = [t for t, k in zip(durs, kinds) if k == 0]
-    i8_d = [t for t, k in zip(durs, kinds) if k == 1]
+    bf_d = [t for t, k in zip(durs, kinds) if k == omq.TIMED_GEMM]
+    i8_d = [t for t, k in zip(durs, kinds) if k == omq.TIMED_GEMM_I8]
     n_l = len(bf_d)
     avg_dur_s = sum(bf_d) / n_l / 1e3
     flops_per_launch = (timer.struct.flops - timer.struct.flops_codes) / n_l
@@ -516,6 +536,7 @@ def main():
             "gemm_share_of_step": round(gemm_ms / (ms * args.steps), 4),
         },
         "roofline_codes": codes_roof,
+        "roofline_hbm": hbm or None,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -322,16 +322,21 @@ int omq_adamw(float* theta, const float* grad, float* m, float* v, int64_t n, in
               float weight_decay, int64_t step, void* stream);
 
 /*
- * Optional timing of the matrix-core contractions of a block step (benchmarks).
- * The caller creates 2 * capacity hipEvent_t handles in `events`; while
- * count < capacity the library records events[2*count] before and
- * events[2*count+1] after each GEMM launch it issues on the call's stream,
- * increments count, and adds the launch's algorithmic FLOPs to flops (2 M N K per
- * batch entry; the causal attention products count their causal half).
- * kinds (int[capacity] or NULL) receives each recorded launch's operand kind:
- * 0 bf16 (or float32) operands, 1 int8 codes (the forward's products on integer
- * codes, see omq_code_gemm); flops_codes sums the latter's share of flops.
+ * Optional timing of a block step's launches (benchmarks).  The caller creates
+ * 2 * capacity hipEvent_t handles in `events`; while count < capacity the library
+ * records events[2*count] before and events[2*count+1] after each timed launch it
+ * issues on the call's stream and increments count.  Timed launches: every GEMM
+ * (its algorithmic FLOPs, 2 M N K per batch entry, are added to flops), and the
+ * quantized forward's fake quantizers (weights and activations).
+ * kinds (int[capacity] or NULL) receives each launch's kind (OMQ_TIMED_*), work
+ * (double[capacity] or NULL) its algorithmic work: FLOPs for the GEMMs, HBM bytes
+ * for the quantizers (read x, write x_hat, and the codes when written).
+ * flops_codes sums the int8 code products' share of flops.
  */
+#define OMQ_TIMED_GEMM 0          /* bf16 (or float32) operands */
+#define OMQ_TIMED_GEMM_I8 1       /* int8 codes (the forward's products, omq_code_gemm) */
+#define OMQ_TIMED_WEIGHT_QUANT 2  /* LWC fake quantizer of a weight */
+#define OMQ_TIMED_ACT_QUANT 3     /* per-token activation quantizer */
 typedef struct omq_timer {
   void** events;
   int capacity;
@@ -339,6 +344,7 @@ typedef struct omq_timer {
   double flops;
   int* kinds;
   double flops_codes;
+  double* work;
 } omq_timer;
 
 /*

@@ -51,10 +51,14 @@ class QLinearDesc(ctypes.Structure):
                          int(use_let), path, group)
 
 
+TIMED_GEMM, TIMED_GEMM_I8, TIMED_WEIGHT_QUANT, TIMED_ACT_QUANT = 0, 1, 2, 3
+
+
 class OmqTimer(ctypes.Structure):
     _fields_ = [("events", ctypes.POINTER(ctypes.c_void_p)), ("capacity", _int),
                 ("count", _int), ("flops", ctypes.c_double),
-                ("kinds", ctypes.POINTER(ctypes.c_int)), ("flops_codes", ctypes.c_double)]
+                ("kinds", ctypes.POINTER(ctypes.c_int)), ("flops_codes", ctypes.c_double),
+                ("work", ctypes.POINTER(ctypes.c_double))]
 
 
 def _hip():
@@ -79,9 +83,10 @@ class GemmTimer:
                 raise OmqError("hipEventCreate failed (%d)" % rc)
             self._ev[i] = e.value
         self._kinds = (ctypes.c_int * capacity)()
+        self._work = (ctypes.c_double * capacity)()
         self.struct = OmqTimer(ctypes.cast(self._ev, ctypes.POINTER(ctypes.c_void_p)), capacity,
                                0, 0.0, ctypes.cast(self._kinds, ctypes.POINTER(ctypes.c_int)),
-                               0.0)
+                               0.0, ctypes.cast(self._work, ctypes.POINTER(ctypes.c_double)))
 
     def reset(self):
         self.struct.count = 0
@@ -89,8 +94,13 @@ class GemmTimer:
         self.struct.flops_codes = 0.0
 
     def kinds(self):
-        """Per recorded launch: 0 bf16 / float32 operands, 1 int8 codes."""
+        """Per recorded launch: TIMED_GEMM, TIMED_GEMM_I8, TIMED_WEIGHT_QUANT or
+        TIMED_ACT_QUANT."""
         return [self._kinds[i] for i in range(self.struct.count)]
+
+    def work(self):
+        """Per recorded launch: algorithmic FLOPs (GEMMs) or HBM bytes (quantizers)."""
+        return [self._work[i] for i in range(self.struct.count)]
 
     def durations_ms(self):
         out = []

@@ -199,11 +199,32 @@ int check(const omq_block_desc* b) {
   return OMQ_OK;
 }
 
+// Optional event timing of one launch (benchmarks): kind and work (FLOPs, or
+// algorithmic HBM bytes for the quantizers) are recorded beside the event pair.
+template <typename F>
+hipError_t timed(omq_timer* tm, int kind, double work, hipStream_t st, F&& launch) {
+  const bool rec = tm && tm->events && tm->count < tm->capacity;
+  if (rec) {
+    hipError_t e = hipEventRecord(reinterpret_cast<hipEvent_t>(tm->events[2 * tm->count]), st);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = launch();
+  if (rec && e == hipSuccess) {
+    e = hipEventRecord(reinterpret_cast<hipEvent_t>(tm->events[2 * tm->count + 1]), st);
+    if (kind <= OMQ_TIMED_GEMM_I8) tm->flops += work;
+    if (kind == OMQ_TIMED_GEMM_I8) tm->flops_codes += work;
+    if (tm->kinds) tm->kinds[tm->count] = kind;
+    if (tm->work) tm->work[tm->count] = work;
+    tm->count += 1;
+  }
+  return e;
+}
+
 // one linear's weight side: LET-W (s), LWC (theta logits), bias fold (delta)
 hipError_t wfq(const void* W, int64_t rows, int64_t cols, const float* s, const float* delta,
                const float* th, const Theta& t, int l, int wbits, bool fp, uint16_t* out,
                const Stats& st, int64_t row0, float* Bt, int64_t group, uint8_t* codes,
-               hipStream_t stream) {
+               hipStream_t stream, omq_timer* tm) {
   RowQuantFwd a;
   a.x = W; a.x_dt = OMQ_BF16; a.rows = rows; a.cols = cols; a.ldx = cols;
   a.let_mode = (s && !fp) ? OMQ_LET_MUL : OMQ_LET_NONE; a.s = s;
@@ -217,7 +238,10 @@ hipError_t wfq(const void* W, int64_t rows, int64_t cols, const float* s, const 
   if (grouped) a.group = group;
   if (!fp && delta && !grouped) { a.fold_delta = delta; a.bias_out = Bt + row0; }
   if (codes && !fp) { a.codes = codes + row0 * cols; a.qsum = st.qsum + row0; }
-  hipError_t e = launch_rowquant_fwd(a, stream);
+  // algorithmic bytes: read W, write W_hat (and the codes)
+  const double bytes = (double)rows * (double)cols * (4.0 + (a.codes ? 1.0 : 0.0));
+  hipError_t e = timed(fp ? nullptr : tm, OMQ_TIMED_WEIGHT_QUANT, bytes, stream,
+                       [&] { return launch_rowquant_fwd(a, stream); });
   if (e == hipSuccess && !fp && delta && (a.nbits >= 16 || grouped))
     e = launch_bias_fold(W, OMQ_BF16, rows, cols, delta, nullptr, Bt + row0, stream);
   return e;
@@ -226,33 +250,25 @@ hipError_t wfq(const void* W, int64_t rows, int64_t cols, const float* s, const 
 // per-token quantizer with fused LET on its input
 hipError_t aq(const void* X, int x_dt, int64_t T, int64_t C, int64_t ldx, int mode,
               const float* s, const float* delta, int abits, uint16_t* out, const Stats& st,
-              hipStream_t stream, uint8_t* codes = nullptr) {
+              hipStream_t stream, omq_timer* tm, uint8_t* codes = nullptr) {
   RowQuantFwd a;
   a.x = X; a.x_dt = x_dt; a.rows = T; a.cols = C; a.ldx = ldx;
   a.let_mode = mode; a.s = s; a.delta = delta; a.nbits = abits;
   a.out = out; a.out_dt = OMQ_BF16; a.ldo = C;
   a.h = st.h; a.z = st.z; a.amax = st.amax; a.amin = st.amin;
   if (codes && abits < 16) { a.codes = codes; a.qsum = st.qsum; }
-  return launch_rowquant_fwd(a, stream);
+  // algorithmic bytes: read X, write X_hat (and the codes)
+  const double bytes =
+      (double)T * (double)C * ((x_dt == OMQ_F32 ? 4.0 : 2.0) + 2.0 + (a.codes ? 1.0 : 0.0));
+  return timed(abits < 16 ? tm : nullptr, OMQ_TIMED_ACT_QUANT, bytes, stream,
+               [&] { return launch_rowquant_fwd(a, stream); });
 }
 
 // every matrix-core launch of the step goes through here (optional event timing)
 hipError_t run_gemm(const Gemm& g, hipStream_t st, omq_timer* tm) {
-  const bool rec = tm && tm->events && tm->count < tm->capacity;
-  if (rec) {
-    hipError_t e = hipEventRecord(reinterpret_cast<hipEvent_t>(tm->events[2 * tm->count]), st);
-    if (e != hipSuccess) return e;
-  }
-  hipError_t e = launch_gemm(g, st);
-  if (rec && e == hipSuccess) {
-    e = hipEventRecord(reinterpret_cast<hipEvent_t>(tm->events[2 * tm->count + 1]), st);
-    double f = 2.0 * (double)g.M * (double)g.N * (double)g.K * (double)g.batch;
-    tm->flops += f;
-    if (tm->kinds) tm->kinds[tm->count] = g.codes ? 1 : 0;
-    if (g.codes) tm->flops_codes += f;
-    tm->count += 1;
-  }
-  return e;
+  const double f = 2.0 * (double)g.M * (double)g.N * (double)g.K * (double)g.batch;
+  return timed(tm, g.codes ? OMQ_TIMED_GEMM_I8 : OMQ_TIMED_GEMM, f, st,
+               [&] { return launch_gemm(g, st); });
 }
 
 hipError_t gemm(const void* A, int64_t lda, const void* B, int64_t ldb, float* C, int64_t ldc,
@@ -309,16 +325,16 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
     CK(launch_rope_tables(T, m.hd, bd->rope_theta, w.cos_t, w.sin_t, st));
     // weight side of q, k, v, o
     CK(wfq(W[LQ], dq, d, s_qkv, d_qkv, th, t, LQ, wb, fp, w.Wqkv, w.wq_qkv, 0, w.Bt_qkv,
-               m.group, cq ? w.Cqkv : nullptr, st));
+               m.group, cq ? w.Cqkv : nullptr, st, tm));
     CK(wfq(W[LK], dk, d, s_qkv, d_qkv, th, t, LK, wb, fp, w.Wqkv, w.wq_qkv, dq, w.Bt_qkv,
-               m.group, cq ? w.Cqkv : nullptr, st));
+               m.group, cq ? w.Cqkv : nullptr, st, tm));
     CK(wfq(W[LV], dk, d, s_qkv, d_qkv, th, t, LV, wb, fp, w.Wqkv, w.wq_qkv, dq + dk,
-               w.Bt_qkv, m.group, cq ? w.Cqkv : nullptr, st));
+               w.Bt_qkv, m.group, cq ? w.Cqkv : nullptr, st, tm));
     CK(wfq(W[LO], d, dq, s_o, d_o, th, t, LO, wb, fp, w.Wo, w.wq_o, 0, w.Bt_o, m.group,
-           cq ? w.Co : nullptr, st));
+           cq ? w.Co : nullptr, st, tm));
     // attention input
     CK(launch_rmsnorm(x, OMQ_BF16, T, d, bd->eps, w.xn, w.r1, st));
-    CK(aq(w.xn, OMQ_F32, T, d, d, mode_let, s_qkv, d_qkv, ab, w.Xqkv, w.a_qkv, st,
+    CK(aq(w.xn, OMQ_F32, T, d, d, mode_let, s_qkv, d_qkv, ab, w.Xqkv, w.a_qkv, st, tm,
           cq ? w.Cxqkv : nullptr));
     if (cq)
       CK(code_gemm(w.Cxqkv, w.a_qkv, w.Cqkv, w.wq_qkv, w.Yqkv, nqkv, T, nqkv, d, w.Bt_qkv, nullptr,
@@ -331,11 +347,11 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
     // s_a on the affinity, then Q/K/V quantized per token
     const bool sa = m.use_sa && !fp;
     CK(aq(w.Qr, OMQ_F32, T, dq, dq, sa ? OMQ_LET_DIV : OMQ_LET_NONE, w.sa_q, nullptr, ab, w.Qh,
-          w.a_q, st));
+          w.a_q, st, tm));
     CK(aq(w.Kr, OMQ_F32, T, dk, dk, sa ? OMQ_LET_MUL : OMQ_LET_NONE, th + (sa ? t.s_a : 0),
-          nullptr, ab, w.Kh, w.a_k, st));
+          nullptr, ab, w.Kh, w.a_k, st, tm));
     CK(aq(w.Yqkv + dq + dk, OMQ_F32, T, dk, nqkv, OMQ_LET_NONE, nullptr, nullptr, ab, w.Vh, w.a_v,
-          st));
+          st, tm));
     // causal attention, float32 softmax, fused
     {
       FlashFwd f;
@@ -346,7 +362,7 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
       CK(launch_flash_fwd(f, st));
     }
     // o_proj with its LET site, residual
-    CK(aq(w.O, OMQ_F32, T, dq, dq, mode_let, s_o, d_o, ab, w.Xo, w.a_o, st,
+    CK(aq(w.O, OMQ_F32, T, dq, dq, mode_let, s_o, d_o, ab, w.Xo, w.a_o, st, tm,
           cq ? w.Cxo : nullptr));
     if (cq)
       CK(code_gemm(w.Cxo, w.a_o, w.Co, w.wq_o, w.h1, d, T, d, dq, w.Bt_o, x, OMQ_BF16, d, st,
@@ -363,12 +379,13 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
   }
   // FFN
   CK(wfq(W[LG], F, d, s_ffn, d_ffn, th, t, LG, wb, fp, w.Wgu, w.wq_gu, 0, w.Bt_gu, m.group,
-         cq ? w.Cgu : nullptr, st));
+         cq ? w.Cgu : nullptr, st, tm));
   CK(wfq(W[LU], F, d, s_ffn, d_ffn, th, t, LU, wb, fp, w.Wgu, w.wq_gu, F, w.Bt_gu, m.group,
-         cq ? w.Cgu : nullptr, st));
+         cq ? w.Cgu : nullptr, st, tm));
   CK(wfq(W[LD], d, F, nullptr, nullptr, th, t, LD, wb, fp, w.Wd, w.wq_d, 0, nullptr, m.group,
-         cq ? w.Cd : nullptr, st));
-  CK(aq(xf, xf_dt, T, d, d, mode_let, s_ffn, d_ffn, ab, w.Xf, w.a_f, st, cq ? w.Cxf : nullptr));
+         cq ? w.Cd : nullptr, st, tm));
+  CK(aq(xf, xf_dt, T, d, d, mode_let, s_ffn, d_ffn, ab, w.Xf, w.a_f, st, tm,
+        cq ? w.Cxf : nullptr));
   if (cq)
     CK(code_gemm(w.Cxf, w.a_f, w.Cgu, w.wq_gu, w.GU, 2 * F, T, 2 * F, d, w.Bt_gu, nullptr, 0, 0,
                  st, tm));
@@ -376,7 +393,7 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
     CK(gemm(w.Xf, d, w.Wgu, d, w.GU, 2 * F, T, 2 * F, d, fp ? nullptr : w.Bt_gu, nullptr, 0, 0,
             st, tm));
   CK(launch_silu_gate(w.GU, T, F, w.A, st));
-  CK(aq(w.A, OMQ_F32, T, F, F, OMQ_LET_NONE, nullptr, nullptr, ab, w.Xd, w.a_d, st,
+  CK(aq(w.A, OMQ_F32, T, F, F, OMQ_LET_NONE, nullptr, nullptr, ab, w.Xd, w.a_d, st, tm,
         cq ? w.Cxd : nullptr));
   if (cq)
     CK(code_gemm(w.Cxd, w.a_d, w.Cd, w.wq_d, w.y, d, T, d, F, nullptr,
