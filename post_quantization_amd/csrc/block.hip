@@ -437,6 +437,7 @@ struct LinBwd {
   const uint16_t* Xh;
   const uint16_t* Wh;
   uint16_t* gYb;
+  bool have_gYb;         // gYb (and, with fold, its column sums) already formed
   // weight side
   const WSeg* segs;
   int nseg;
@@ -464,8 +465,9 @@ hipError_t lin_bwd_fused(const Ws& w, const LinBwd& L, int64_t T, int wbits, int
                          omq_timer* tm) {
   hipError_t e;
   const int64_t N = L.N, K = L.K;
-  if ((e = launch_cvt_bf16_colsum(L.gY, T, N, L.gYb, L.fold ? w.cs : nullptr, w.csws, st)) !=
-      hipSuccess)
+  if (!L.have_gYb &&
+      (e = launch_cvt_bf16_colsum(L.gY, T, N, L.gYb, L.fold ? w.cs : nullptr, w.csws, st)) !=
+          hipSuccess)
     return e;
   int64_t nsl, ntl;
   // weight side (skipped when no learnable parameter depends on these weights)
@@ -558,13 +560,19 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
     L.X = w.A; L.x_dt = OMQ_F32; L.a_mode = OMQ_LET_NONE; L.ast = w.a_d; L.gx_out = w.gA;
     CK(lin_bwd_fused(w, L, T, wb, ab, th, t, dth, st, tm));
   }
-  CK(launch_silu_gate_bwd(w.GU, w.gA, T, F, w.gGU, st));
+  // dL/d(gate|up) goes straight to its bf16 operand form with its column sums
+  const bool gu_bf16 = silu_gate_bwd_bf16_fits(w.GU, w.gA, T, F, w.gGUb);
+  if (gu_bf16)
+    CK(launch_silu_gate_bwd_bf16(w.GU, w.gA, T, F, w.gGUb, w.cs, w.csws, st));
+  else
+    CK(launch_silu_gate_bwd(w.GU, w.gA, T, F, w.gGU, st));
   // gate / up with the shared ffn LET site
   {
     const WSeg segs[2] = {{W[LG], F, LG}, {W[LU], F, LU}};
     LinBwd L{};
     L.group = m.group;
     L.gY = w.gGU; L.N = 2 * F; L.K = d; L.Xh = w.Xf; L.Wh = w.Wgu; L.gYb = w.gGUb;
+    L.have_gYb = gu_bf16;
     L.segs = segs; L.nseg = 2; L.wst = w.wq_gu; L.s_w = th + t.s_ffn; L.fold = true;
     L.gs_w = dth + t.s_ffn; L.gd_w = dth + t.d_ffn; L.acc_w = 1;
     L.X = m.ffn_only ? x : (const void*)w.xn2; L.x_dt = m.ffn_only ? OMQ_BF16 : OMQ_F32;

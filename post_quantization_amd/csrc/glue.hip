@@ -181,6 +181,60 @@ __global__ __launch_bounds__(kThreads) void k_silu_gate_bwd4(const float* __rest
   *reinterpret_cast<float4*>(ggu + t * 2 * F + F + f) = make_float4(ou[0], ou[1], ou[2], ou[3]);
 }
 
+// The gate/up gradient as the bf16 operand of the backward products, with the
+// column sums of each kColsumRows-row chunk (the bias-fold gradient needs the
+// column sums of dL/d(gate|up)).  A workgroup takes 256 columns of each half (4
+// per lane: the same 4 of the gate and of the up half) over one chunk; its 4 waves
+// take the chunk's rows in turn and their sums are added in LDS in a fixed order.
+__global__ __launch_bounds__(kThreads) void k_silu_gate_bwd_bf16(const float* __restrict__ gu,
+                                                                 const float* __restrict__ ga,
+                                                                 int64_t T, int64_t F,
+                                                                 uint16_t* __restrict__ ggub,
+                                                                 float* __restrict__ part) {
+  __shared__ float4 red[4][2][64];
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int64_t f = ((int64_t)blockIdx.x * 64 + lane) * 4;
+  const bool ok = f < F;
+  const int64_t r0 = (int64_t)blockIdx.y * kColsumRows;
+  const int64_t r1 = min(r0 + kColsumRows, T);
+  float sg_[4] = {0.f, 0.f, 0.f, 0.f}, su_[4] = {0.f, 0.f, 0.f, 0.f};
+  if (ok) {
+#pragma unroll 2
+    for (int64_t t = r0 + w; t < r1; t += 4) {
+      const float4 g4 = *reinterpret_cast<const float4*>(gu + t * 2 * F + f);
+      const float4 u4 = *reinterpret_cast<const float4*>(gu + t * 2 * F + F + f);
+      const float4 d4 = *reinterpret_cast<const float4*>(ga + t * F + f);
+      const float g[4] = {g4.x, g4.y, g4.z, g4.w}, u[4] = {u4.x, u4.y, u4.z, u4.w};
+      const float d[4] = {d4.x, d4.y, d4.z, d4.w};
+      float og[4], ou[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float sg = sigmoidf_(g[e]);
+        og[e] = d[e] * u[e] * sg * (1.f + g[e] * (1.f - sg));
+        ou[e] = d[e] * g[e] * sg;
+        sg_[e] += og[e];
+        su_[e] += ou[e];
+      }
+      *reinterpret_cast<uint2*>(ggub + t * 2 * F + f) =
+          make_uint2(pack_bf16(og[0], og[1]), pack_bf16(og[2], og[3]));
+      *reinterpret_cast<uint2*>(ggub + t * 2 * F + F + f) =
+          make_uint2(pack_bf16(ou[0], ou[1]), pack_bf16(ou[2], ou[3]));
+    }
+  }
+  red[w][0][lane] = make_float4(sg_[0], sg_[1], sg_[2], sg_[3]);
+  red[w][1][lane] = make_float4(su_[0], su_[1], su_[2], su_[3]);
+  __syncthreads();
+  if (w < 2 && ok) {
+    float4 acc = red[0][w][lane];
+#pragma unroll
+    for (int q = 1; q < 4; ++q) {
+      const float4 v = red[q][w][lane];
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    *reinterpret_cast<float4*>(part + (int64_t)blockIdx.y * 2 * F + w * F + f) = acc;
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void k_silu_gate(const float* gu, int64_t T, int64_t F,
                                                         float* a) {
   const int64_t n = T * F;
@@ -360,6 +414,23 @@ hipError_t launch_silu_gate_bwd(const float* gu, const float* ga, int64_t T, int
   hipLaunchKernelGGL(k_silu_gate_bwd, dim3(grid_for(T * F)), dim3(kThreads), 0, st, gu, ga, T, F,
                      ggu);
   return hipGetLastError();
+}
+
+bool silu_gate_bwd_bf16_fits(const float* gu, const float* ga, int64_t T, int64_t F,
+                             const uint16_t* ggub) {
+  return F % 4 == 0 && al16(gu) && al16(ga) && (reinterpret_cast<uintptr_t>(ggub) & 7) == 0 &&
+         T > 0 && (T + kColsumRows - 1) / kColsumRows < 65536;
+}
+
+hipError_t launch_silu_gate_bwd_bf16(const float* gu, const float* ga, int64_t T, int64_t F,
+                                     uint16_t* ggub, float* colsum, float* ws, hipStream_t st) {
+  if (!silu_gate_bwd_bf16_fits(gu, ga, T, F, ggub)) return hipErrorInvalidValue;
+  const int64_t np = (T + kColsumRows - 1) / kColsumRows;
+  hipLaunchKernelGGL(k_silu_gate_bwd_bf16, dim3((unsigned)((F / 4 + 63) / 64), (unsigned)np),
+                     dim3(kThreads), 0, st, gu, ga, T, F, ggub, ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_part_colsum(ws, (int)np, 1, 2 * F, colsum, nullptr, 0, st);
 }
 
 hipError_t launch_mse(const float* y, const float* target, int64_t n, float* loss, float* dy,

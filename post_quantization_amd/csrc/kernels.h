@@ -128,6 +128,11 @@ void gemm_ste_extents(int64_t rows, int64_t cols, int64_t* nslabs, int64_t* ntil
 // set (ws: colsum_ws_bytes(rows, cols))
 hipError_t launch_cvt_bf16_colsum(const float* in, int64_t rows, int64_t cols, uint16_t* out,
                                   float* colsum, float* ws, hipStream_t st);
+// Column sums in two deterministic stages: partial sums over chunks of kColsumRows
+// rows ([nparts][cols] per kind), then out_k[c] (+)= sum of the nparts partials.
+constexpr int kColsumRows = 64;
+hipError_t launch_part_colsum(const float* part, int nparts, int nk, int64_t cols, float* out0,
+                              float* out1, int accumulate, hipStream_t st);
 // out[c] = sum_r in[r][c]   (deterministic two-stage)
 hipError_t launch_colsum(const float* in, int64_t rows, int64_t cols, int64_t ld, float* out,
                          float* ws, hipStream_t st);
@@ -148,6 +153,13 @@ hipError_t launch_rope(const float* x, int64_t ldx, int64_t T, int64_t n_heads, 
 hipError_t launch_silu_gate(const float* gu, int64_t T, int64_t F, float* a, hipStream_t st);
 hipError_t launch_silu_gate_bwd(const float* gu, const float* ga, int64_t T, int64_t F,
                                 float* ggu, hipStream_t st);
+// The same gradient written only as the bf16 matrix-core operand [T x 2F], with its
+// column sums (colsum: float[2F]; ws: colsum_ws_bytes(T, 2F)) formed in the same
+// pass; false when the shape does not suit (F % 4, alignment): then use the above.
+bool silu_gate_bwd_bf16_fits(const float* gu, const float* ga, int64_t T, int64_t F,
+                             const uint16_t* ggub);
+hipError_t launch_silu_gate_bwd_bf16(const float* gu, const float* ga, int64_t T, int64_t F,
+                                     uint16_t* ggub, float* colsum, float* ws, hipStream_t st);
 hipError_t launch_mse(const float* y, const float* target, int64_t n, float* loss, float* dy,
                       float* ws, hipStream_t st);
 // fused causal attention, head dimension 128 (csrc/attn.hip).  lse2 is the

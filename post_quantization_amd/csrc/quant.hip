@@ -957,8 +957,6 @@ __global__ __launch_bounds__(kThreads) void k_bias_fold(const void* W, int64_t r
   if (threadIdx.x == 0) out[r] = (B ? B[r] : 0.f) + ((sd[0] + sd[1]) + (sd[2] + sd[3]));
 }
 
-constexpr int kColsumRows = 64;
-
 __global__ __launch_bounds__(kThreads) void k_colsum_part(const float* in, int64_t rows,
                                                           int64_t cols, int64_t ld, float* part) {
   const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -971,39 +969,58 @@ __global__ __launch_bounds__(kThreads) void k_colsum_part(const float* in, int64
 
 // dY in float32 -> its bf16 copy (the matrix-core operand) and, when `part` is
 // set, the column sums of each kColsumRows-row chunk, in one pass over dY.
-// VEC: 8 consecutive columns per thread (cols % 8 == 0), else one.
+// VEC 8 (cols % 8 == 0): a workgroup takes 512 columns (8 per lane) of one chunk,
+// its 4 waves take the chunk's rows in turn, and their sums are added in LDS in a
+// fixed order.  VEC 1: one column per thread over the chunk.
 template <int VEC>
 __global__ __launch_bounds__(kThreads) void k_cvt_bf16_colpart(const float* __restrict__ in,
                                                                int64_t rows, int64_t cols,
                                                                uint16_t* __restrict__ out,
                                                                float* __restrict__ part) {
-  const int64_t c = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * VEC;
-  if (c >= cols) return;
   const int64_t r0 = (int64_t)blockIdx.y * kColsumRows;
   const int64_t r1 = min(r0 + kColsumRows, rows);
-  float s[VEC];
-#pragma unroll
-  for (int j = 0; j < VEC; ++j) s[j] = 0.f;
-  // (4 rows in flight: the loads of the next rows do not wait for this row's stores)
+  if constexpr (VEC == 8) {
+    __shared__ float4 red[4][2][64];
+    const int lane = threadIdx.x & 63, w = wave_id();
+    const int64_t c = ((int64_t)blockIdx.x * 64 + lane) * 8;
+    const bool ok = c < cols;
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (ok) {
 #pragma unroll 4
-  for (int64_t r = r0; r < r1; ++r) {
-    const float* p = in + r * cols + c;
-    if constexpr (VEC == 8) {
-      const float4 a = *reinterpret_cast<const float4*>(p);
-      const float4 b = *reinterpret_cast<const float4*>(p + 4);
-      s[0] += a.x; s[1] += a.y; s[2] += a.z; s[3] += a.w;
-      s[4] += b.x; s[5] += b.y; s[6] += b.z; s[7] += b.w;
-      *reinterpret_cast<uint4*>(out + r * cols + c) =
-          make_uint4(pack_bf16(a.x, a.y), pack_bf16(a.z, a.w), pack_bf16(b.x, b.y),
-                     pack_bf16(b.z, b.w));
-    } else {
-      s[0] += p[0];
-      out[r * cols + c] = f32_to_bf16(p[0]);
+      for (int64_t r = r0 + w; r < r1; r += 4) {
+        const float* p = in + r * cols + c;
+        const float4 a = *reinterpret_cast<const float4*>(p);
+        const float4 b = *reinterpret_cast<const float4*>(p + 4);
+        s[0] += a.x; s[1] += a.y; s[2] += a.z; s[3] += a.w;
+        s[4] += b.x; s[5] += b.y; s[6] += b.z; s[7] += b.w;
+        *reinterpret_cast<uint4*>(out + r * cols + c) =
+            make_uint4(pack_bf16(a.x, a.y), pack_bf16(a.z, a.w), pack_bf16(b.x, b.y),
+                       pack_bf16(b.z, b.w));
+      }
     }
-  }
-  if (part) {
+    if (!part) return;                               // uniform over the workgroup
+    red[w][0][lane] = make_float4(s[0], s[1], s[2], s[3]);
+    red[w][1][lane] = make_float4(s[4], s[5], s[6], s[7]);
+    __syncthreads();
+    if (w < 2 && ok) {
+      float4 acc = red[0][w][lane];
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) part[(int64_t)blockIdx.y * cols + c + j] = s[j];
+      for (int q = 1; q < 4; ++q) {
+        const float4 v = red[q][w][lane];
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+      }
+      *reinterpret_cast<float4*>(part + (int64_t)blockIdx.y * cols + c + 4 * w) = acc;
+    }
+  } else {
+    const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (c >= cols) return;
+    float s0 = 0.f;
+    for (int64_t r = r0; r < r1; ++r) {
+      const float v = in[r * cols + c];
+      s0 += v;
+      out[r * cols + c] = f32_to_bf16(v);
+    }
+    if (part) part[(int64_t)blockIdx.y * cols + c] = s0;
   }
 }
 
@@ -1039,6 +1056,10 @@ __global__ __launch_bounds__(kSumWaves * 64) void k_part_colsum(const float* par
   }
 }
 
+int bwd_rows_per_tile(int64_t rows) { return rows >= 8192 ? 32 : 16; }
+
+}  // namespace
+
 hipError_t launch_part_colsum(const float* part, int nparts, int nk, int64_t cols, float* out0,
                               float* out1, int accumulate, hipStream_t st) {
   if (cols == 0 || (!out0 && !out1)) return hipSuccess;
@@ -1046,10 +1067,6 @@ hipError_t launch_part_colsum(const float* part, int nparts, int nk, int64_t col
                      st, part, nparts, nk, cols, out0, out1, accumulate);
   return hipGetLastError();
 }
-
-int bwd_rows_per_tile(int64_t rows) { return rows >= 8192 ? 32 : 16; }
-
-}  // namespace
 
 template <int XDT>
 bool launch_fwd_wave(const RowQuantFwd& a, hipStream_t st) {
@@ -1277,7 +1294,7 @@ hipError_t launch_cvt_bf16_colsum(const float* in, int64_t rows, int64_t cols, u
   if (np == 0) return colsum ? hipMemsetAsync(colsum, 0, cols * sizeof(float), st) : hipSuccess;
   float* part = colsum ? ws : nullptr;
   if (cols % 8 == 0) {
-    const unsigned cb = (unsigned)((cols / 8 + kThreads - 1) / kThreads);
+    const unsigned cb = (unsigned)((cols / 8 + 63) / 64);
     hipLaunchKernelGGL(k_cvt_bf16_colpart<8>, dim3(cb, (unsigned)np), dim3(kThreads), 0, st, in,
                        rows, cols, out, part);
   } else {
