@@ -545,7 +545,8 @@ hipError_t lin_bwd_fused(const Ws& w, const LinBwd& L, int64_t T, int wbits, int
 }
 
 int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w,
-             const void* x, const void* const* W, const float* th, float* dth, hipStream_t st) {
+             const void* x, const void* const* W, const float* th, float* dth, hipStream_t st,
+             bool dyb_ready) {
   omq_timer* tm = bd->timer;
   const int64_t T = m.T, d = m.d, F = m.F, dq = m.dq, dk = m.dk, nqkv = m.nqkv;
   const int wb = bd->wbits, ab = bd->abits;
@@ -556,6 +557,7 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
     LinBwd L{};
     L.group = m.group;
     L.gY = w.dy; L.N = d; L.K = F; L.Xh = w.Xd; L.Wh = w.Wd; L.gYb = w.dyb;
+    L.have_gYb = dyb_ready;            // no LET on down: no column sums needed
     L.segs = segs; L.nseg = 1; L.wst = w.wq_d;
     L.X = w.A; L.x_dt = OMQ_F32; L.a_mode = OMQ_LET_NONE; L.ast = w.a_d; L.gx_out = w.gA;
     CK(lin_bwd_fused(w, L, T, wb, ab, th, t, dth, st, tm));
@@ -706,8 +708,11 @@ int omq_block_step(const omq_block_desc* d, const void* x, const float* y_target
   const hipStream_t st = S(stream);
   rc = forward(d, m, t, w, x, weights, theta, false, st);
   if (rc) return rc;
-  OMQ_HIP_CHECK(launch_mse(w.y, y_target, m.T * m.d, loss, w.dy, w.msews, st));
-  rc = backward(d, m, t, w, x, weights, theta, dtheta, st);
+  // dL/dy also in bf16 (the down product's operand) when the target is 16-byte aligned
+  const bool dyb = al16(y_target);
+  OMQ_HIP_CHECK(
+      launch_mse(w.y, y_target, m.T * m.d, loss, w.dy, w.msews, st, dyb ? w.dyb : nullptr));
+  rc = backward(d, m, t, w, x, weights, theta, dtheta, st, dyb);
   if (rc) return rc;
   if (d->optimizer == OMQ_OPT_ADAMW)
     OMQ_HIP_CHECK(launch_adamw(theta, dtheta, adam_m, adam_v, t.total, t.n_lwc, d->lr_lwc,

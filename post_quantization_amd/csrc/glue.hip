@@ -277,6 +277,32 @@ __global__ __launch_bounds__(kThreads) void k_mse_part(const float* y, const flo
   if (threadIdx.x == 0) part[blockIdx.x] = s;
 }
 
+// four elements per thread (16-byte loads and stores); dyb, when set, receives dy
+// in bf16 as well (the next product's operand)
+__global__ __launch_bounds__(kThreads) void k_mse_part4(const float* __restrict__ y,
+                                                        const float* __restrict__ t, int64_t n,
+                                                        float* __restrict__ dy,
+                                                        uint16_t* __restrict__ dyb,
+                                                        float* __restrict__ part) {
+  __shared__ float sh[4];
+  float s = 0.f;
+  const float sc = 2.f / (float)n;
+  for (int64_t i = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4; i < n;
+       i += (int64_t)gridDim.x * kThreads * 4) {
+    const float4 a = *reinterpret_cast<const float4*>(y + i);
+    const float4 b = *reinterpret_cast<const float4*>(t + i);
+    const float d[4] = {a.x - b.x, a.y - b.y, a.z - b.z, a.w - b.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s = fmaf(d[j], d[j], s);
+    const float g[4] = {sc * d[0], sc * d[1], sc * d[2], sc * d[3]};
+    if (dy) *reinterpret_cast<float4*>(dy + i) = make_float4(g[0], g[1], g[2], g[3]);
+    if (dyb)
+      *reinterpret_cast<uint2*>(dyb + i) = make_uint2(pack_bf16(g[0], g[1]), pack_bf16(g[2], g[3]));
+  }
+  s = block_sum(s, sh);
+  if (threadIdx.x == 0) part[blockIdx.x] = s;
+}
+
 __global__ __launch_bounds__(kThreads) void k_mse_final(const float* part, int np, int64_t n,
                                                         float* loss) {
   __shared__ float sh[4];
@@ -434,10 +460,17 @@ hipError_t launch_silu_gate_bwd_bf16(const float* gu, const float* ga, int64_t T
 }
 
 hipError_t launch_mse(const float* y, const float* target, int64_t n, float* loss, float* dy,
-                      float* ws, hipStream_t st) {
-  const int nb = (int)std::min<int64_t>(kMseBlocks, (n + kThreads - 1) / kThreads);
+                      float* ws, hipStream_t st, uint16_t* dyb) {
+  const bool v4 = n % 4 == 0 && al16(y) && al16(target) && (!dy || al16(dy)) &&
+                  (reinterpret_cast<uintptr_t>(dyb) & 7) == 0;
+  if (dyb && !v4) return hipErrorInvalidValue;
+  const int nb = (int)std::min<int64_t>(kMseBlocks, (n + kThreads * (v4 ? 4 : 1) - 1) /
+                                                        (kThreads * (v4 ? 4 : 1)));
   if (nb == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_mse_part, dim3(nb), dim3(kThreads), 0, st, y, target, n, dy, ws);
+  if (v4)
+    hipLaunchKernelGGL(k_mse_part4, dim3(nb), dim3(kThreads), 0, st, y, target, n, dy, dyb, ws);
+  else
+    hipLaunchKernelGGL(k_mse_part, dim3(nb), dim3(kThreads), 0, st, y, target, n, dy, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !loss) return e;
   hipLaunchKernelGGL(k_mse_final, dim3(1), dim3(kThreads), 0, st, ws, nb, n, loss);

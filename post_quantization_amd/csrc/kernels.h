@@ -160,8 +160,10 @@ bool silu_gate_bwd_bf16_fits(const float* gu, const float* ga, int64_t T, int64_
                              const uint16_t* ggub);
 hipError_t launch_silu_gate_bwd_bf16(const float* gu, const float* ga, int64_t T, int64_t F,
                                      uint16_t* ggub, float* colsum, float* ws, hipStream_t st);
+// loss = mean((y - target)^2), dy = 2 (y - target) / n (NULL: not written); dyb, when
+// set, receives dy in bf16 too (needs n % 4 == 0 and 16-byte aligned y, target, dy)
 hipError_t launch_mse(const float* y, const float* target, int64_t n, float* loss, float* dy,
-                      float* ws, hipStream_t st);
+                      float* ws, hipStream_t st, uint16_t* dyb = nullptr);
 // fused causal attention, head dimension 128 (csrc/attn.hip).  lse2 is the
 // per-(head, query) log-sum-exp of the scaled scores in the exp2 domain.
 struct FlashFwd {
