@@ -300,6 +300,29 @@ hipError_t code_gemm(const uint8_t* qx, const Stats& sx, const uint8_t* qw, cons
     if (e__ != hipSuccess) return OMQ_E_HIP; \
   } while (0)
 
+// The o-input LET pair and s_a live on the KV channels; with grouped-query
+// attention they are broadcast over each group's query heads into workspace
+// copies (and their gradients reduced back), with one query head per KV head the
+// parameter vector itself serves (and the gradients go straight into dtheta,
+// which the backward clears first).
+struct KvSites {
+  const float *s_o, *d_o, *sa_q;
+  float *gs_o, *gd_o, *gsa_q;
+};
+KvSites kv_sites(const Dims& m, const Theta& t, const Ws& w, const float* th, float* dth) {
+  KvSites k{};
+  const bool bc = m.grp > 1;
+  k.s_o = bc ? w.s_o_x : th + t.s_o;
+  k.d_o = bc ? w.d_o_x : th + t.d_o;
+  k.sa_q = bc || t.s_a < 0 ? w.sa_q : th + t.s_a;
+  if (dth) {
+    k.gs_o = bc ? w.gs_full : dth + t.s_o;
+    k.gd_o = bc ? w.gd_full : dth + t.d_o;
+    k.gsa_q = bc || t.s_a < 0 ? w.gsa_full : dth + t.s_a;
+  }
+  return k;
+}
+
 // Forward.  fp: the full-precision target (no quantizers, no LET).
 int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w, const void* x,
             const void* const* W, const float* th, bool fp, hipStream_t st) {
@@ -316,12 +339,15 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
     const float* s_qkv = fp ? nullptr : th + t.s_qkv;
     const float* d_qkv = fp ? nullptr : th + t.d_qkv;
     if (!fp) {
-      CK(launch_kv_expand(th + t.s_o, m.nq, m.nkv, m.hd, w.s_o_x, st));
-      CK(launch_kv_expand(th + t.d_o, m.nq, m.nkv, m.hd, w.d_o_x, st));
-      if (m.use_sa) CK(launch_kv_expand(th + t.s_a, m.nq, m.nkv, m.hd, w.sa_q, st));
+      if (m.grp > 1) {
+        CK(launch_kv_expand(th + t.s_o, m.nq, m.nkv, m.hd, w.s_o_x, st));
+        CK(launch_kv_expand(th + t.d_o, m.nq, m.nkv, m.hd, w.d_o_x, st));
+        if (m.use_sa) CK(launch_kv_expand(th + t.s_a, m.nq, m.nkv, m.hd, w.sa_q, st));
+      }
     }
-    const float* s_o = fp ? nullptr : w.s_o_x;
-    const float* d_o = fp ? nullptr : w.d_o_x;
+    const KvSites kv = kv_sites(m, t, w, th, nullptr);
+    const float* s_o = fp ? nullptr : kv.s_o;
+    const float* d_o = fp ? nullptr : kv.d_o;
     CK(launch_rope_tables(T, m.hd, bd->rope_theta, w.cos_t, w.sin_t, st));
     // weight side of q, k, v, o
     CK(wfq(W[LQ], dq, d, s_qkv, d_qkv, th, t, LQ, wb, fp, w.Wqkv, w.wq_qkv, 0, w.Bt_qkv,
@@ -346,7 +372,7 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
     CK(launch_rope(w.Yqkv + dq, nqkv, T, m.nkv, m.hd, w.cos_t, w.sin_t, 0, w.Kr, dk, st));
     // s_a on the affinity, then Q/K/V quantized per token
     const bool sa = m.use_sa && !fp;
-    CK(aq(w.Qr, OMQ_F32, T, dq, dq, sa ? OMQ_LET_DIV : OMQ_LET_NONE, w.sa_q, nullptr, ab, w.Qh,
+    CK(aq(w.Qr, OMQ_F32, T, dq, dq, sa ? OMQ_LET_DIV : OMQ_LET_NONE, kv.sa_q, nullptr, ab, w.Qh,
           w.a_q, st, tm));
     CK(aq(w.Kr, OMQ_F32, T, dk, dk, sa ? OMQ_LET_MUL : OMQ_LET_NONE, th + (sa ? t.s_a : 0),
           nullptr, ab, w.Kh, w.a_k, st, tm));
@@ -494,30 +520,30 @@ hipError_t lin_bwd_fused(const Ws& w, const LinBwd& L, int64_t T, int wbits, int
     se.rowpart = rowpart; se.colpart = colpart;
     const bool grouped = L.group > 0 && wbits < 16;
     se.grouped = grouped;        // one 128-column tile of a row = one group
-    const int64_t qg = grouped ? K / L.group : 1;
     if ((e = run_gemm(g, st, tm)) != hipSuccess) return e;
     RowQuantBwd a;
     a.cols = K; a.col_mode = se.col_mode; a.out0 = L.gs_w; a.out1 = L.fold ? L.gd_w : nullptr;
     a.accumulate = L.acc_w;
     if ((e = launch_ste_colfinal(a, (int)ntl, colpart, st)) != hipSuccess) return e;
-    r0 = 0;
+    // one finalizer launch over the concatenated rows, each segment with its own
+    // weight rows and logits
+    RowQuantBwd b;
+    b.x = L.segs[0].W; b.x_dt = OMQ_BF16; b.rows = r0; b.cols = K; b.ldx = K;
+    b.let_mode = se.let_mode; b.s = L.s_w; b.nbits = wbits;
+    b.h = L.wst.h; b.z = L.wst.z; b.amax = L.wst.amax; b.amin = L.wst.amin;
+    b.a_gamma = th + t.ag[L.segs[0].l]; b.a_beta = th + t.ab[L.segs[0].l];
+    b.g_agamma = dth + t.ag[L.segs[0].l]; b.g_abeta = dth + t.ab[L.segs[0].l];
+    b.nseg = L.nseg;
     for (int k = 0; k < L.nseg; ++k) {
       const WSeg& sg = L.segs[k];
-      RowQuantBwd b;
-      b.x = sg.W; b.x_dt = OMQ_BF16; b.rows = sg.rows; b.cols = K; b.ldx = K;
-      b.let_mode = se.let_mode; b.s = L.s_w; b.nbits = wbits;
-      const int64_t q0 = r0 * qg;
-      b.h = L.wst.h + q0; b.z = L.wst.z + q0; b.amax = L.wst.amax + q0;
-      b.amin = L.wst.amin + q0;
-      b.a_gamma = th + t.ag[sg.l]; b.a_beta = th + t.ab[sg.l];
-      b.g_agamma = dth + t.ag[sg.l]; b.g_abeta = dth + t.ab[sg.l];
-      b.col_mode = se.col_mode; b.out0 = L.gs_w;
-      if (grouped) b.group = L.group;
-      if ((e = launch_ste_rowfinal(b, grouped ? 1 : (int)nsl, rowpart + r0 * nsl * 2, st)) !=
-          hipSuccess)
-        return e;
-      r0 += sg.rows;
+      b.seg_end[k] = se.seg_end[k];
+      b.xseg[k] = sg.W;
+      b.agseg[k] = th + t.ag[sg.l]; b.abseg[k] = th + t.ab[sg.l];
+      b.gagseg[k] = dth + t.ag[sg.l]; b.gabseg[k] = dth + t.ab[sg.l];
     }
+    b.col_mode = se.col_mode; b.out0 = L.gs_w;
+    if (grouped) b.group = L.group;
+    if ((e = launch_ste_rowfinal(b, grouped ? 1 : (int)nsl, rowpart, st)) != hipSuccess) return e;
   }
   // activation side
   gemm_ste_extents(T, K, &nsl, &ntl);
@@ -583,6 +609,7 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
     CK(lin_bwd_fused(w, L, T, wb, ab, th, t, dth, st, tm));
   }
   if (m.ffn_only) return OMQ_OK;
+  const KvSites kv = kv_sites(m, t, w, th, dth);
 
   // RMSNorm before the FFN, residual
   CK(launch_rmsnorm_bwd(w.gxn2, w.h1, w.r2, T, d, w.dy, w.dh1, st));
@@ -592,14 +619,16 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
     LinBwd L{};
     L.group = m.group;
     L.gY = w.dh1; L.N = d; L.K = dq; L.Xh = w.Xo; L.Wh = w.Wo; L.gYb = w.dh1b;
-    L.segs = segs; L.nseg = 1; L.wst = w.wq_o; L.s_w = w.s_o_x; L.fold = true;
-    L.gs_w = w.gs_full; L.gd_w = w.gd_full; L.acc_w = 0;
-    L.X = w.O; L.x_dt = OMQ_F32; L.a_mode = OMQ_LET_DIV; L.s_x = w.s_o_x; L.d_x = w.d_o_x;
-    L.ast = w.a_o; L.gx_out = w.gO; L.gs_x = w.gs_full; L.gd_x = w.gd_full;
+    L.segs = segs; L.nseg = 1; L.wst = w.wq_o; L.s_w = kv.s_o; L.fold = true;
+    L.gs_w = kv.gs_o; L.gd_w = kv.gd_o; L.acc_w = 0;
+    L.X = w.O; L.x_dt = OMQ_F32; L.a_mode = OMQ_LET_DIV; L.s_x = kv.s_o; L.d_x = kv.d_o;
+    L.ast = w.a_o; L.gx_out = w.gO; L.gs_x = kv.gs_o; L.gd_x = kv.gd_o;
     CK(lin_bwd_fused(w, L, T, wb, ab, th, t, dth, st, tm));
   }
-  CK(launch_kv_reduce_add(w.gs_full, m.nq, m.nkv, m.hd, dth + t.s_o, st));
-  CK(launch_kv_reduce_add(w.gd_full, m.nq, m.nkv, m.hd, dth + t.d_o, st));
+  if (m.grp > 1) {
+    CK(launch_kv_reduce_add(w.gs_full, m.nq, m.nkv, m.hd, dth + t.s_o, st));
+    CK(launch_kv_reduce_add(w.gd_full, m.nq, m.nkv, m.hd, dth + t.d_o, st));
+  }
   // attention backward (scores recomputed from the forward's log-sum-exp)
   CK(launch_attn_bwd_prep(w.gO, w.O, dq, T, (int)m.nq, w.Datt, w.gOb, dq, st));
   {
@@ -614,15 +643,16 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
   }
   // Q~ / K~ / V quantizers and s_a
   const bool sa = m.use_sa;
-  CK(abwd(w, w.gQh, T, dq, w.Qr, OMQ_F32, dq, sa ? OMQ_LET_DIV : OMQ_LET_NONE, w.sa_q, nullptr,
-          ab, w.a_q, w.gQr, dq, sa ? COL_ACT_DIV : COL_NONE, sa ? w.gsa_full : nullptr, nullptr, 0,
+  CK(abwd(w, w.gQh, T, dq, w.Qr, OMQ_F32, dq, sa ? OMQ_LET_DIV : OMQ_LET_NONE, kv.sa_q, nullptr,
+          ab, w.a_q, w.gQr, dq, sa ? COL_ACT_DIV : COL_NONE, sa ? kv.gsa_q : nullptr, nullptr,
+          m.grp > 1 ? 0 : 1,
           st));
   CK(abwd(w, w.gKh, T, dk, w.Kr, OMQ_F32, dk, sa ? OMQ_LET_MUL : OMQ_LET_NONE,
           sa ? th + t.s_a : nullptr, nullptr, ab, w.a_k, w.gKr, dk, sa ? COL_ACT_MUL : COL_NONE,
           sa ? dth + t.s_a : nullptr, nullptr, 1, st));
   CK(abwd(w, w.gVh, T, dk, w.Yqkv + dq + dk, OMQ_F32, nqkv, OMQ_LET_NONE, nullptr, nullptr, ab,
           w.a_v, w.gY + dq + dk, nqkv, COL_NONE, nullptr, nullptr, 0, st));
-  if (sa) CK(launch_kv_reduce_add(w.gsa_full, m.nq, m.nkv, m.hd, dth + t.s_a, st));
+  if (sa && m.grp > 1) CK(launch_kv_reduce_add(w.gsa_full, m.nq, m.nkv, m.hd, dth + t.s_a, st));
   CK(launch_rope(w.gQr, dq, T, m.nq, m.hd, w.cos_t, w.sin_t, 1, w.gY, nqkv, st));
   CK(launch_rope(w.gKr, dk, T, m.nkv, m.hd, w.cos_t, w.sin_t, 1, w.gY + dq, nqkv, st));
   // q / k / v with the shared qkv LET site

@@ -50,6 +50,17 @@ struct RowQuantBwd {
   int accumulate = 0;                               // add into out0/out1
   float* ws = nullptr;                              // partial buffers
   int64_t group = 0;                                // as in RowQuantFwd (128 or 0)
+  // Row finalizer only: nseg > 1 concatenated weights (up to 3), segment k holding
+  // rows [seg_end[k-1], seg_end[k]) with its own x rows and logits (indexed by the
+  // segment's own quantizer row); h, z, arg_max/arg_min and the row partials run
+  // over the concatenated rows.
+  int nseg = 1;
+  int64_t seg_end[3] = {0, 0, 0};
+  const void* xseg[3] = {nullptr, nullptr, nullptr};
+  const float* agseg[3] = {nullptr, nullptr, nullptr};
+  const float* abseg[3] = {nullptr, nullptr, nullptr};
+  float* gagseg[3] = {nullptr, nullptr, nullptr};
+  float* gabseg[3] = {nullptr, nullptr, nullptr};
 };
 size_t rowquant_bwd_ws_bytes(int64_t rows, int64_t cols);
 hipError_t launch_rowquant_bwd(const RowQuantBwd& a, hipStream_t st);

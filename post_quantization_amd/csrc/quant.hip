@@ -865,7 +865,20 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_bwd_rows(RowQuantBwd a, i
   }
   if (!valid || sub != 0) return;
   const int64_t r = p / ng;
-  const char* xr = reinterpret_cast<const char*>(a.x) + r * a.ldx * (XDT == OMQ_F32 ? 4 : 2);
+  // the row's segment (concatenated weights): its x rows and logits
+  const void* xb = a.x;
+  const float *lg_g = a.a_gamma, *lg_b = a.a_beta;
+  float *gg_g = a.g_agamma, *gg_b = a.g_abeta;
+  int64_t rl = r, pl = p;
+  if (a.nseg > 1) {
+    const int sg = (r >= a.seg_end[0]) + (a.nseg > 2 && r >= a.seg_end[1]);
+    const int64_t r0 = sg == 0 ? 0 : a.seg_end[sg - 1];
+    xb = a.xseg[sg];
+    lg_g = a.agseg[sg]; lg_b = a.abseg[sg]; gg_g = a.gagseg[sg]; gg_b = a.gabseg[sg];
+    rl = r - r0;
+    pl = p - r0 * ng;
+  }
+  const char* xr = reinterpret_cast<const char*>(xb) + rl * a.ldx * (XDT == OMQ_F32 ? 4 : 2);
   auto xval = [&](int64_t c) -> float {
     return XDT == OMQ_F32 ? reinterpret_cast<const float*>(xr)[c]
                           : bf16_to_f32(reinterpret_cast<const uint16_t*>(xr)[c]);
@@ -874,8 +887,8 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_bwd_rows(RowQuantBwd a, i
   const float xM = xval(iM), xm = xval(im);
   const float M = let_x(xM, a.let_mode, a.s, a.delta, iM);
   const float m = let_x(xm, a.let_mode, a.s, a.delta, im);
-  const float gamma = a.a_gamma ? sigmoid_f32(a.a_gamma[p]) : 1.f;
-  const float beta = a.a_beta ? sigmoid_f32(a.a_beta[p]) : 1.f;
+  const float gamma = lg_g ? sigmoid_f32(lg_g[pl]) : 1.f;
+  const float beta = lg_b ? sigmoid_f32(lg_b[pl]) : 1.f;
   const RowQ q = row_step(M, m, gamma, beta, a.nbits);
   const float h = q.h;
   const float gz = -h * gzs;
@@ -883,8 +896,8 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_bwd_rows(RowQuantBwd a, i
   const float gt1 = G / q.Q;
   const float gt2 = -G / q.Q - gz / h;
   const float gM = gt1 * gamma, gm = gt2 * beta;
-  if (a.g_agamma) a.g_agamma[p] = (gt1 * M) * gamma * (1.f - gamma);
-  if (a.g_abeta) a.g_abeta[p] = (gt2 * m) * beta * (1.f - beta);
+  if (gg_g) gg_g[pl] = (gt1 * M) * gamma * (1.f - gamma);
+  if (gg_b) gg_b[pl] = (gt2 * m) * beta * (1.f - beta);
   // scatter of dL/dmax and dL/dmin into the gradient of x~ at arg_max / arg_min
   const int idx[2] = {iM, im};
   const float gv[2] = {gM, gm};
