@@ -38,8 +38,13 @@ constexpr int BK = 64, LDP = BK;
 // (row & 7) ^ ((row >> 3) & 7): the matrix-core fragment reads (8 consecutive rows,
 // one chunk) and the transposed-operand stores (rows 8 apart, one k-quad) both
 // spread over distinct banks.
+// 32-wide k steps: [rows][32] with the chunk index XOR-swizzled by (row >> 1) & 3, so
+// the 8 rows one 8-lane group of a fragment read touches cover 8 distinct 16-byte
+// slots of a 256-byte bank window.
+template <int KB = 64>
 OMQ_DEV int lds_idx(int row, int k) {
-  return row * LDP + ((((k >> 3) ^ row ^ (row >> 3)) & 7) << 3) + (k & 7);
+  if constexpr (KB == 32) return row * 32 + ((((k >> 3) ^ (row >> 1)) & 3) << 3) + (k & 7);
+  else return row * LDP + ((((k >> 3) ^ row ^ (row >> 3)) & 7) << 3) + (k & 7);
 }
 constexpr int kGroupM = 8;
 
@@ -157,19 +162,21 @@ struct Stage {
 // one wave instruction fills 8 swizzled LDS rows (1 KB, lane l at byte 16 l), so
 // lane l fetches the k-chunk that the swizzle places at its slot.  Completion is
 // tracked by vmcnt like any vector load.
-template <int R, int NW>
+template <int R, int NW, int KB = 64>
 OMQ_DEV void dma_tile(const uint16_t* P, int64_t ld, int64_t row0, int64_t k0, uint16_t* S,
                       int wid, int lane) {
-  constexpr int NB = R / 8;
-  static_assert(NB % NW == 0, "8-row blocks must divide over the waves");
+  constexpr int RPI = 512 / KB;                    // rows per 1 KB wave instruction
+  constexpr int CPR = KB / 8;                      // 16-byte chunks per row
+  constexpr int NB = R / RPI;
+  static_assert(NB % NW == 0, "row blocks must divide over the waves");
 #pragma unroll
   for (int i = 0; i < NB / NW; ++i) {
     const int b = wid + NW * i;
-    const int r = b * 8 + (lane >> 3);
-    const int c = ((lane & 7) ^ r ^ (r >> 3)) & 7;
+    const int r = b * RPI + lane / CPR;
+    const int c = KB == 32 ? (((lane & 3) ^ (r >> 1)) & 3) : (((lane & 7) ^ r ^ (r >> 3)) & 7);
     __builtin_amdgcn_global_load_lds(
         (const void*)(P + (row0 + r) * ld + k0 + c * 8),
-        (__attribute__((address_space(3))) void*)(S + b * 8 * LDP), 16, 0, 0);
+        (__attribute__((address_space(3))) void*)(S + b * RPI * KB), 16, 0, 0);
   }
 }
 
@@ -187,12 +194,12 @@ OMQ_DEV int ldsT_idx(int kr, int col) {
 // Direct global -> LDS copy of a full 64 x R tile of a K-major operand ([K x rows],
 // rows contiguous): one wave instruction fills 1 KB = 1024 / (2R) k-rows, lane l at
 // byte 16 l, so lane l fetches the chunk the swizzle places at its slot.
-template <int R, int NW>
+template <int R, int NW, int KB = 64>
 OMQ_DEV void dma_tile_t(const uint16_t* P, int64_t ld, int64_t col0, int64_t k0, uint16_t* S,
                         int wid, int lane) {
   constexpr int CPR = R / 8;                       // 16-byte chunks per k-row
   constexpr int RPI = 64 / CPR;                    // k-rows per wave instruction
-  constexpr int NI = BK / RPI;                     // instructions per tile
+  constexpr int NI = KB / RPI;                     // instructions per tile
   static_assert(NI % NW == 0, "k-row blocks must divide over the waves");
 #pragma unroll
   for (int i = 0; i < NI / NW; ++i) {
@@ -205,12 +212,12 @@ OMQ_DEV void dma_tile_t(const uint16_t* P, int64_t ld, int64_t col0, int64_t k0,
   }
 }
 
-// direct copy of one operand tile: K-contiguous (R rows x 64) or K-major (64 x R)
-template <int TR, int R, int NW>
+// direct copy of one operand tile: K-contiguous (R rows x KB) or K-major (KB x R)
+template <int TR, int R, int NW, int KB = 64>
 OMQ_DEV void dma_copy(const uint16_t* P, int64_t ld, int64_t r0, int64_t k0, uint16_t* S, int wid,
                       int lane) {
-  if constexpr (TR) dma_tile_t<R, NW>(P, ld, r0, k0, S, wid, lane);
-  else dma_tile<R, NW>(P, ld, r0, k0, S, wid, lane);
+  if constexpr (TR) dma_tile_t<R, NW, KB>(P, ld, r0, k0, S, wid, lane);
+  else dma_tile<R, NW, KB>(P, ld, r0, k0, S, wid, lane);
 }
 
 typedef __attribute__((ext_vector_type(4))) short i16x4;
@@ -259,17 +266,26 @@ constexpr int epi_code(int mode, int let, int xf) { return mode | (let << 2) | (
 // tiles as bf16 pairs (a 64-wide bf16 k-step is 128 codes), and the matrix cores
 // run v_mfma_i32_32x32x32_i8, whose lane holds 16 consecutive codes where the bf16
 // form holds 8 elements: the same 16 bytes.  The epilogue dequantizes.
-template <int BM, int BN, int WM, int WN, int TA, int TB, int EPI, int DMA, int I8 = 0>
-__global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m, int tiles_n) {
+// KB: the k-step, 64, or 32 with direct copies (half the LDS per stage, so wider
+// wave tiles still fit two workgroups per compute unit).
+template <int BM, int BN, int WM, int WN, int TA, int TB, int EPI, int DMA, int I8 = 0,
+          int KB = 64>
+__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void k_gemm_bf16(Gemm g, int tiles_m, int tiles_n) {
   constexpr int NT = WM * WN * 64, NW = WM * WN;
   constexpr int FM = BM / WM / 32, FN = BN / WN / 32;   // MFMA blocks per wave
   constexpr bool kDmaA = DMA, kDmaB = DMA;
-  static_assert(EPI == 0 || (BM == 128 && BN == 128 && WM * WN == 4),
+  static_assert(EPI == 0 ||
+                    (BN == 128 && ((BM == 128 && WM == 2 && WN == 2) ||
+                                   (BM == 256 && WM == 4 && WN == 1 && (EPI & 3) == 1))),
                 "straight-through epilogue tile");
   static_assert(!I8 || (EPI == 0 && TA == 0 && TB == 0), "integer codes: plain K-contiguous");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * LDP];
-  uint16_t (*As)[BM * LDP] = reinterpret_cast<uint16_t (*)[BM * LDP]>(smem);
-  uint16_t (*Bs)[BN * LDP] = reinterpret_cast<uint16_t (*)[BN * LDP]>(smem + 2 * BM * LDP);
+  static_assert(KB == 64 || (KB == 32 && DMA), "32-wide k steps take direct copies");
+  // operand ring, and the epilogue's [128][128] float32 parking area
+  constexpr int kRing = 2 * (BM + BN) * KB, kPark = EPI ? 128 * 128 * 2 : 0;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kRing > kPark ? kRing : kPark];
+  uint16_t (*As)[BM * KB] = reinterpret_cast<uint16_t (*)[BM * KB]>(smem);
+  uint16_t (*Bs)[BN * KB] = reinterpret_cast<uint16_t (*)[BN * KB]>(smem + 2 * BM * KB);
 
   const int tid = threadIdx.x, lane = tid & 63, wid = wave_id();
   const int wm = wid / WN, wn = wid % WN;
@@ -281,7 +297,8 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
   const int64_t kb = 0, ke = I8 ? g.K >> 1 : g.K;
   const int64_t lda = I8 ? g.lda >> 1 : g.lda, ldb = I8 ? g.ldb >> 1 : g.ldb;
 
-  const uint16_t* A = reinterpret_cast<const uint16_t*>(g.A) + bz * (I8 ? g.strideA >> 1 : g.strideA);
+  const uint16_t* A =
+      reinterpret_cast<const uint16_t*>(g.A) + bz * (I8 ? g.strideA >> 1 : g.strideA);
   const uint16_t* B = reinterpret_cast<const uint16_t*>(g.B) +
                       (bz / g.b_group) * (I8 ? g.strideB >> 1 : g.strideB);
   const int64_t M = g.M, N = g.N;
@@ -304,11 +321,17 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
   constexpr bool kXF = (EPI >> 4) & 1;
   static_assert(EPI == 0 || (kMode == 1 && kLet != kLetDiv && !kXF) ||
                     (kMode == 2 && kLet != kLetMul), "epilogue variant");
-  constexpr int RW = BM / 4;                      // epilogue rows per wave
-  constexpr int RB = 8;                           // rows per batch
+  // Rows per wave and pass: 32.  With 2 x 2 waves (a wave holds 64 x 64) the tile is
+  // parked whole and each wave takes 32 rows; with 4 x 1 waves (a wave holds 64 whole
+  // rows of 128 columns) each wave parks and finishes its own rows, 32 at a time.
+  constexpr bool kOwnRows = WN == 1;
+  constexpr int NPASS = kOwnRows ? BM / WM / 32 : 1;
+  constexpr int RW = 32;
+  constexpr int RB = kOwnRows ? 4 : 8;            // rows per batch (4: registers for the
+                                                  // accumulators of the pass still to come)
   constexpr int XR = kXF ? 2 : 1;                 // 32-bit words of x per lane and row
   const int64_t gn = n0 + 2 * lane;               // the epilogue lane's two columns
-  const int64_t wr0 = m0 + wid * RW;              // first epilogue row of this wave
+  int64_t wr0 = m0 + wid * RW;                    // first epilogue row of this wave
   // direct copies imply whole tiles: no row or column bounds in the epilogue
   constexpr bool kFull = DMA;
   auto fetch_x = [&](int b, uint32_t (&xb)[RB][XR]) {
@@ -346,11 +369,11 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
   // 128 x 128 tiles read every fragment of the buffer first and then run the MFMAs;
   // 256 x 256 tiles (twice the fragments per wave) read each 16-k slice one slice
   // ahead of its MFMAs.  One barrier per step.
-  const int nk = (int)((ke - kb + BK - 1) / BK);
+  const int nk = (int)((ke - kb + KB - 1) / KB);
   if (nk > 0) {
-    if (kDmaA) dma_copy<TA, BM, NW>(A, lda, m0, kb, As[0], wid, lane);
+    if (kDmaA) dma_copy<TA, BM, NW, KB>(A, lda, m0, kb, As[0], wid, lane);
     else { sa.load(A, lda, M, m0, kb, ke, tid); sa.store(As[0], tid); }
-    if (kDmaB) dma_copy<TB, BN, NW>(B, ldb, n0, kb, Bs[0], wid, lane);
+    if (kDmaB) dma_copy<TB, BN, NW, KB>(B, ldb, n0, kb, Bs[0], wid, lane);
     else { sb.load(B, ldb, N, n0, kb, ke, tid); sb.store(Bs[0], tid); }
     if (nk > 1) {
       if (!kDmaA) sa.load(A, lda, M, m0, kb + BK, ke, tid);
@@ -375,9 +398,9 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
     // next tile into the other buffer (staged: the tile after it into registers)
     auto issue_next = [&]() {
       if (kt + 1 < nk) {
-        const int64_t k1 = kb + (int64_t)(kt + 1) * BK;
-        if (kDmaA) dma_copy<TA, BM, NW>(A, lda, m0, k1, As[buf ^ 1], wid, lane);
-        if (kDmaB) dma_copy<TB, BN, NW>(B, ldb, n0, k1, Bs[buf ^ 1], wid, lane);
+        const int64_t k1 = kb + (int64_t)(kt + 1) * KB;
+        if (kDmaA) dma_copy<TA, BM, NW, KB>(A, lda, m0, k1, As[buf ^ 1], wid, lane);
+        if (kDmaB) dma_copy<TB, BN, NW, KB>(B, ldb, n0, k1, Bs[buf ^ 1], wid, lane);
         if (!kDmaA) sa.store(As[buf ^ 1], tid);
         if (!kDmaB) sb.store(Bs[buf ^ 1], tid);
         if (kt + 2 < nk) {
@@ -390,13 +413,13 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
     // fragment i of A / j of B for the 16-k slice kk
     auto fa = [&](int i, int kk) -> bf16x8 {
       if constexpr (DMA && TA) return tr_frag<BM>(Ab, wm * (BM / WM) + i * 32, kk * 16, lane);
-      else return *reinterpret_cast<const bf16x8*>(&Ab[lds_idx(ar + i * 32, kk * 16 + fk)]);
+      else return *reinterpret_cast<const bf16x8*>(&Ab[lds_idx<KB>(ar + i * 32, kk * 16 + fk)]);
     };
     auto fb = [&](int j, int kk) -> bf16x8 {
       if constexpr (DMA && TB) return tr_frag<BN>(Bb, wn * (BN / WN) + j * 32, kk * 16, lane);
-      else return *reinterpret_cast<const bf16x8*>(&Bb[lds_idx(br + j * 32, kk * 16 + fk)]);
+      else return *reinterpret_cast<const bf16x8*>(&Bb[lds_idx<KB>(br + j * 32, kk * 16 + fk)]);
     };
-    if constexpr (DMA && BM > 128) {
+    if constexpr (DMA && BM > 128 && KB == 64) {
       issue_next();
       bf16x8 af[2][FM], bf[2][FN];
 #pragma unroll
@@ -404,9 +427,9 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
 #pragma unroll
       for (int j = 0; j < FN; ++j) bf[0][j] = fb(j, 0);
 #pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
+      for (int kk = 0; kk < KB / 16; ++kk) {
         const int cu = kk & 1;
-        if (kk + 1 < BK / 16) {
+        if (kk + 1 < KB / 16) {
 #pragma unroll
           for (int i = 0; i < FM; ++i) af[cu ^ 1][i] = fa(i, kk + 1);
 #pragma unroll
@@ -419,9 +442,9 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
             mfma(acc[i][j], af[cu][i], bf[cu][j]);
       }
     } else {
-      bf16x8 af[BK / 16][FM], bf[BK / 16][FN];
+      bf16x8 af[KB / 16][FM], bf[KB / 16][FN];
 #pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
+      for (int kk = 0; kk < KB / 16; ++kk) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) af[kk][i] = fa(i, kk);
 #pragma unroll
@@ -429,7 +452,7 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
       }
       issue_next();
 #pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk)
+      for (int kk = 0; kk < KB / 16; ++kk)
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -454,185 +477,214 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_bf16(Gemm g, int tiles_m,
     // the LET) into C.  Rows go in batches of 8: the batch's gradients are read
     // from LDS first, its 8 rows are then independent chains of arithmetic, and
     // their partials are written last.
-    float* T = reinterpret_cast<float*>(smem);     // [128][128] fp32 = the whole buffer
+    float* T = reinterpret_cast<float*>(smem);     // [128][128] fp32
     const SteEpi& e = g.ste;
     const bool pass = e.nbits >= 16;
     const float Q = pass ? 0.f : (float)((1 << e.nbits) - 1);
     const bool colv = gn < N;
-    // x of the first two batches, in flight while the accumulators are parked
-    uint32_t x0[RB][XR], x1[RB][XR], x2[RB][XR];
-    fetch_x(0, x0);
-    fetch_x(1, x1);
-    const int64_t rme = wr0 + (lane & (RW - 1));
-    const bool rmv = rme < M;
-    const int64_t hz = e.grouped ? rme * tiles_n + tn : rme;
-    const float h_l = (!pass && rmv) ? e.h[hz] : 1.f;
-    const float z_l = (!pass && rmv) ? e.z[hz] : 0.f;
-    const float v_l = (e.rowvec && rmv) ? e.rowvec[rme] : 0.f;
-    float s_c[2] = {1.f, 1.f}, d_c[2] = {0.f, 0.f};
-    if (colv && kLet != kLetNone) { s_c[0] = e.s[gn]; s_c[1] = e.s[gn + 1]; }
-    if (colv && kLet == kLetDiv && e.delta) {
-      d_c[0] = e.delta[gn];
-      d_c[1] = e.delta[gn + 1];
-    }
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = wm * (BM / WM) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          const int col = wn * (BN / WN) + j * 32 + (lane & 31);
-          T[row * BN + col] = g.alpha * acc[i][j][r];
-        }
-    __syncthreads();
-    const float r_c[2] = {1.f / s_c[0], 1.f / s_c[1]};
-    const float rh_l = 1.f / h_l;
+    // the T rows of this wave's pass
+    const int tb0 = wid * RW;
     float ca0[2] = {0.f, 0.f}, ca1[2] = {0.f, 0.f};
-    float* Cp = g.C + bz * g.strideC;
 #pragma unroll 1
-    for (int b = 0; b < RW / RB; ++b) {
-      if (wr0 + b * RB >= M) break;                // wave-uniform
-      if (b + 2 < RW / RB) fetch_x(b + 2, x2);
-      float gv[RB][2], xv[RB][2], xt[RB][2], xd[RB][2], u[RB][2], rr[RB][2];
-      float hh[RB], zz[RB], vr[RB];
-#pragma unroll
-      for (int q = 0; q < RB; ++q) {
-        const float2 t = *reinterpret_cast<const float2*>(&T[(wid * RW + b * RB + q) * BN + 2 * lane]);
-        const bool ok = kFull || (colv && wr0 + b * RB + q < M);
-        gv[q][0] = ok ? t.x : 0.f;
-        gv[q][1] = ok ? t.y : 0.f;
+    for (int hf = 0; hf < NPASS; ++hf) {
+      wr0 = kOwnRows ? m0 + wid * (BM / WM) + hf * RW : m0 + wid * RW;
+      // x of the first two batches, in flight while the accumulators are parked
+      uint32_t x0[RB][XR], x1[RB][XR], x2[RB][XR];
+      fetch_x(0, x0);
+      fetch_x(1, x1);
+      const int64_t rme = wr0 + (lane & (RW - 1));
+      const bool rmv = rme < M;
+      const int64_t hz = e.grouped ? rme * tiles_n + tn : rme;
+      const float h_l = (!pass && rmv) ? e.h[hz] : 1.f;
+      const float z_l = (!pass && rmv) ? e.z[hz] : 0.f;
+      const float v_l = (e.rowvec && rmv) ? e.rowvec[rme] : 0.f;
+      float s_c[2] = {1.f, 1.f}, d_c[2] = {0.f, 0.f};
+      if (colv && kLet != kLetNone) { s_c[0] = e.s[gn]; s_c[1] = e.s[gn + 1]; }
+      if (colv && kLet == kLetDiv && e.delta) {
+        d_c[0] = e.delta[gn];
+        d_c[1] = e.delta[gn + 1];
       }
-      // x~ and the rounding of x~ / h by the reciprocal product for every element
-      // of the batch; an element whose product lies within |u| 2^-20 of a
-      // half-integer (or is not finite) takes the exact quotient below
-      bool near = false;
+      if constexpr (kOwnRows) {
+        // this wave's 32 rows of the pass into its own T rows (read back only by
+        // itself: LDS operations of one wave complete in order)
 #pragma unroll
-      for (int q = 0; q < RB; ++q) {
-        const int rw = b * RB + q;
-        hh[q] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(h_l), rw));
-        const float rhh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rh_l), rw));
-        zz[q] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z_l), rw));
-        vr[q] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v_l), rw));
-        if constexpr (kXF) {
-          xv[q][0] = __uint_as_float(x0[q][0]);
-          xv[q][1] = __uint_as_float(x0[q][1]);
-        } else {
-          xv[q][0] = __uint_as_float(x0[q][0] << 16);
-          xv[q][1] = __uint_as_float(x0[q][0] & 0xffff0000u);
-        }
+        for (int i = 0; i < FM; ++i)
+          if (i == hf) {
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          // x~: exact for MUL / NONE; for DIV within 2 ulp (it enters sums only; the
-          // decisions follow the exact quotient)
-          xd[q][c2] = xv[q][c2] - d_c[c2];
-          if constexpr (kLet == kLetDiv) xt[q][c2] = xd[q][c2] * r_c[c2];
-          else if constexpr (kLet == kLetMul) xt[q][c2] = s_c[c2] * xv[q][c2];
-          else xt[q][c2] = xv[q][c2];
-          u[q][c2] = xt[q][c2] * rhh;
-          rr[q][c2] = rintf(u[q][c2]);
-          near |= !(fabsf(fabsf(u[q][c2] - rr[q][c2]) - 0.5f) > fabsf(u[q][c2]) * 0x1p-20f);
-        }
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int row = tb0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                T[row * BN + j * 32 + (lane & 31)] = g.alpha * acc[i][j][r];
+              }
+          }
+      } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int row = wm * (BM / WM) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+              const int col = wn * (BN / WN) + j * 32 + (lane & 31);
+              T[row * BN + col] = g.alpha * acc[i][j][r];
+            }
+        __syncthreads();
       }
-      // (wave-uniform branches: divergent ones would be flattened into a division
-      // for every element)
-      if (!pass && __builtin_amdgcn_ballot_w64(near) != 0) {
+      const float r_c[2] = {1.f / s_c[0], 1.f / s_c[1]};
+      const float rh_l = 1.f / h_l;
+      float* Cp = g.C + bz * g.strideC;
+#pragma unroll 1
+      for (int b = 0; b < RW / RB; ++b) {
+        if (wr0 + b * RB >= M) break;                // wave-uniform
+        if (b + 2 < RW / RB) fetch_x(b + 2, x2);
+        float gv[RB][2], xv[RB][2], xt[RB][2], xd[RB][2], u[RB][2], rr[RB][2];
+        float hh[RB], zz[RB], vr[RB];
+#pragma unroll
+        for (int q = 0; q < RB; ++q) {
+          const float2 t =
+              *reinterpret_cast<const float2*>(&T[(tb0 + b * RB + q) * BN + 2 * lane]);
+          const bool ok = kFull || (colv && wr0 + b * RB + q < M);
+          gv[q][0] = ok ? t.x : 0.f;
+          gv[q][1] = ok ? t.y : 0.f;
+        }
+        // x~ and the rounding of x~ / h by the reciprocal product for every element
+        // of the batch; an element whose product lies within |u| 2^-20 of a
+        // half-integer (or is not finite) takes the exact quotient below
+        bool near = false;
+#pragma unroll
+        for (int q = 0; q < RB; ++q) {
+          const int rw = b * RB + q;
+          hh[q] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(h_l), rw));
+          const float rhh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rh_l), rw));
+          zz[q] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z_l), rw));
+          vr[q] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v_l), rw));
+          if constexpr (kXF) {
+            xv[q][0] = __uint_as_float(x0[q][0]);
+            xv[q][1] = __uint_as_float(x0[q][1]);
+          } else {
+            xv[q][0] = __uint_as_float(x0[q][0] << 16);
+            xv[q][1] = __uint_as_float(x0[q][0] & 0xffff0000u);
+          }
+#pragma unroll
+          for (int c2 = 0; c2 < 2; ++c2) {
+            // x~: exact for MUL / NONE; for DIV within 2 ulp (it enters sums only; the
+            // decisions follow the exact quotient)
+            xd[q][c2] = xv[q][c2] - d_c[c2];
+            if constexpr (kLet == kLetDiv) xt[q][c2] = xd[q][c2] * r_c[c2];
+            else if constexpr (kLet == kLetMul) xt[q][c2] = s_c[c2] * xv[q][c2];
+            else xt[q][c2] = xv[q][c2];
+            u[q][c2] = xt[q][c2] * rhh;
+            rr[q][c2] = rintf(u[q][c2]);
+            near |= !(fabsf(fabsf(u[q][c2] - rr[q][c2]) - 0.5f) > fabsf(u[q][c2]) * 0x1p-20f);
+          }
+        }
+        // (wave-uniform branches: divergent ones would be flattened into a division
+        // for every element)
+        if (!pass && __builtin_amdgcn_ballot_w64(near) != 0) {
+#pragma unroll
+          for (int q = 0; q < RB; ++q)
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+              const bool ne =
+                  !(fabsf(fabsf(u[q][c2] - rr[q][c2]) - 0.5f) > fabsf(u[q][c2]) * 0x1p-20f);
+              if (__builtin_amdgcn_ballot_w64(ne) != 0) {
+                if (ne) {
+                  u[q][c2] = kLet == kLetDiv ? (xd[q][c2] / s_c[c2]) / hh[q] : xt[q][c2] / hh[q];
+                  rr[q][c2] = rintf(u[q][c2]);
+                }
+              }
+            }
+        }
+        float ph[RB], pz[RB];
+#pragma unroll
+        for (int q = 0; q < RB; ++q) {
+          ph[q] = 0.f;
+          pz[q] = 0.f;
+          float up[2];
+#pragma unroll
+          for (int c2 = 0; c2 < 2; ++c2) {
+            const float g1 = gv[q][c2];
+            float gns = g1;
+            if (!pass) {
+              const float rq = rr[q][c2] + zz[q];
+              const bool in = (rq >= 0.f) && (rq <= Q);
+              const float qmz = fminf(fmaxf(rq, 0.f), Q) - zz[q];
+              ph[q] += g1 * (qmz - (in ? u[q][c2] : 0.f));
+              pz[q] += in ? 0.f : g1;
+              gns = in ? g1 : 0.f;
+            }
+            if constexpr (kMode == 1 && kLet == kLetMul) {
+              ca0[c2] += gns * xv[q][c2];
+              ca1[c2] += vr[q] * xv[q][c2];
+            } else if constexpr (kMode == 2 && kLet == kLetDiv) {
+              ca0[c2] += gns * (-xt[q][c2] * r_c[c2]);
+              ca1[c2] += gns * (-r_c[c2]);
+            }
+            up[c2] = kLet == kLetDiv ? gns * r_c[c2] : kLet == kLetMul ? gns * s_c[c2] : gns;
+          }
+          if constexpr (kMode == 2) {
+            const int64_t gm = wr0 + b * RB + q;
+            if (kFull || (gm < M && colv))
+              *reinterpret_cast<float2*>(&Cp[gm * g.ldc + gn]) = make_float2(up[0], up[1]);
+          }
+        }
+        if (!pass) {
+          // the batch's gradients are consumed: its LDS rows now hold the lanes'
+          // partials (g_h in columns 0..63, out-of-range sum in 64..127)
+#pragma unroll
+          for (int q = 0; q < RB; ++q) {
+            float* tr = &T[(tb0 + b * RB + q) * BN];
+            tr[lane] = ph[q];
+            tr[64 + lane] = pz[q];
+          }
+        }
 #pragma unroll
         for (int q = 0; q < RB; ++q)
 #pragma unroll
-          for (int c2 = 0; c2 < 2; ++c2) {
-            const bool ne =
-                !(fabsf(fabsf(u[q][c2] - rr[q][c2]) - 0.5f) > fabsf(u[q][c2]) * 0x1p-20f);
-            if (__builtin_amdgcn_ballot_w64(ne) != 0) {
-              if (ne) {
-                u[q][c2] = kLet == kLetDiv ? (xd[q][c2] / s_c[c2]) / hh[q] : xt[q][c2] / hh[q];
-                rr[q][c2] = rintf(u[q][c2]);
-              }
-            }
+          for (int w = 0; w < XR; ++w) {
+            x0[q][w] = x1[q][w];
+            x1[q][w] = x2[q][w];
           }
-      }
-      float ph[RB], pz[RB];
-#pragma unroll
-      for (int q = 0; q < RB; ++q) {
-        ph[q] = 0.f;
-        pz[q] = 0.f;
-        float up[2];
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          const float g1 = gv[q][c2];
-          float gns = g1;
-          if (!pass) {
-            const float rq = rr[q][c2] + zz[q];
-            const bool in = (rq >= 0.f) && (rq <= Q);
-            const float qmz = fminf(fmaxf(rq, 0.f), Q) - zz[q];
-            ph[q] += g1 * (qmz - (in ? u[q][c2] : 0.f));
-            pz[q] += in ? 0.f : g1;
-            gns = in ? g1 : 0.f;
-          }
-          if constexpr (kMode == 1 && kLet == kLetMul) {
-            ca0[c2] += gns * xv[q][c2];
-            ca1[c2] += vr[q] * xv[q][c2];
-          } else if constexpr (kMode == 2 && kLet == kLetDiv) {
-            ca0[c2] += gns * (-xt[q][c2] * r_c[c2]);
-            ca1[c2] += gns * (-r_c[c2]);
-          }
-          up[c2] = kLet == kLetDiv ? gns * r_c[c2] : kLet == kLetMul ? gns * s_c[c2] : gns;
-        }
-        if constexpr (kMode == 2) {
-          const int64_t gm = wr0 + b * RB + q;
-          if (kFull || (gm < M && colv))
-            *reinterpret_cast<float2*>(&Cp[gm * g.ldc + gn]) = make_float2(up[0], up[1]);
-        }
       }
       if (!pass) {
-        // the batch's gradients are consumed: its LDS rows now hold the lanes'
-        // partials (g_h in columns 0..63, out-of-range sum in 64..127)
-#pragma unroll
-        for (int q = 0; q < RB; ++q) {
-          float* tr = &T[(wid * RW + b * RB + q) * BN];
-          tr[lane] = ph[q];
-          tr[64 + lane] = pz[q];
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < RB; ++q)
-#pragma unroll
-        for (int w = 0; w < XR; ++w) {
-          x0[q][w] = x1[q][w];
-          x1[q][w] = x2[q][w];
-        }
-    }
-    if (!pass) {
-      // lane l sums row (l & 31)'s 64 partials of kind (l >> 5), starting at a
-      // lane-dependent offset so the 64 lanes read 64 different banks
-      const int rw = lane & 31, half = lane >> 5;
-      const int64_t gm = wr0 + rw;
-      if (gm < M) {
-        const float* src = &T[(wid * RW + rw) * BN + half * 64];
-        float sum = 0.f;
+        // lane l sums row (l & 31)'s 64 partials of kind (l >> 5), starting at a
+        // lane-dependent offset so the 64 lanes read 64 different banks
+        const int rw = lane & 31, half = lane >> 5;
+        const int64_t gm = wr0 + rw;
+        if (gm < M) {
+          const float* src = &T[(tb0 + rw) * BN + half * 64];
+          float sum = 0.f;
 #pragma unroll 16
-        for (int j = 0; j < 64; ++j) sum += src[(j + lane) & 63];
-        e.rowpart[(gm * tiles_n + tn) * 2 + half] = sum;
+          for (int j = 0; j < 64; ++j) sum += src[(j + lane) & 63];
+          e.rowpart[(gm * tiles_n + tn) * 2 + half] = sum;
+        }
       }
     }
+    // column partials of each 128-row block: the four waves' sums (2 x 2 waves: one
+    // block, all four; 4 x 1 waves: waves 2b and 2b+1 make block b), added in LDS in a
+    // fixed order
     if constexpr ((kMode == 1 && kLet == kLetMul) || (kMode == 2 && kLet == kLetDiv)) {
-      __syncthreads();                             // every wave is done reading T
+      __syncthreads();                               // every wave is done reading T
       T[(wid * 2 + 0) * BN + 2 * lane] = ca0[0];
       T[(wid * 2 + 0) * BN + 2 * lane + 1] = ca0[1];
       T[(wid * 2 + 1) * BN + 2 * lane] = ca1[0];
       T[(wid * 2 + 1) * BN + 2 * lane + 1] = ca1[1];
       __syncthreads();
-      if (tid < BN) {
-        const int64_t c = n0 + tid;
+      constexpr int NB = BM / 128, WPB = 4 / NB;     // 128-row blocks, waves per block
+      if (tid < BN * NB) {
+        const int cc = tid % BN, bb = tid / BN;
+        const int64_t c = n0 + cc;
         if (c < N) {
           float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            a0 += T[(w * 2 + 0) * BN + tid];
-            a1 += T[(w * 2 + 1) * BN + tid];
+          for (int w = 0; w < WPB; ++w) {
+            a0 += T[((bb * WPB + w) * 2 + 0) * BN + cc];
+            a1 += T[((bb * WPB + w) * 2 + 1) * BN + cc];
           }
-          e.colpart[((int64_t)tm * 2 + 0) * N + c] = a0;
-          e.colpart[((int64_t)tm * 2 + 1) * N + c] = a1;
+          const int64_t tb = (int64_t)tm * NB + bb;
+          e.colpart[(tb * 2 + 0) * N + c] = a0;
+          e.colpart[(tb * 2 + 1) * N + c] = a1;
         }
       }
     }
@@ -836,9 +888,9 @@ void launch_codes(const Gemm& g, hipStream_t st) {
 
 // Direct LDS copies need whole tiles (no bounds checks), whole K steps and 16-byte
 // aligned rows.
-bool dma_fits(const Gemm& g, int BM, int BN) {
+bool dma_fits(const Gemm& g, int BM, int BN, int KB = BK) {
   auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
-  return g.M % BM == 0 && g.N % BN == 0 && g.K % BK == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 &&
+  return g.M % BM == 0 && g.N % BN == 0 && g.K % KB == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 &&
          g.strideA % 8 == 0 && g.strideB % 8 == 0 && al16(g.A) && al16(g.B);
 }
 
@@ -849,6 +901,18 @@ constexpr int kSteBM = 128, kSteBN = 128, kSteWM = 2, kSteWN = 2;
 template <int EPI>
 void launch_ste_x(const Gemm& g, hipStream_t st) {
   constexpr int TA = (EPI & 3) == 1;             // weight side: dY^T is the K-major A
+  if constexpr (TA) {
+    // weight rows (output channels) come in the thousands: 256 x 128 tiles of 4 waves
+    // (each 64 whole rows) on 32-wide k steps read fewer LDS fragments per product
+    // (both operands take the transposing read) and keep two workgroups per CU
+    if (dma_fits(g, 256, 128, 32)) {
+      const int tm = (int)(g.M / 256), tn = (int)(g.N / 128);
+      hipLaunchKernelGGL((k_gemm_bf16<256, 128, 4, 1, 1, 1, EPI, 1, 0, 32>),
+                         dim3((unsigned)(tm * tn), (unsigned)g.batch), dim3(256), 0, st, g, tm,
+                         tn);
+      return;
+    }
+  }
   const int tiles_m = (int)((g.M + kSteBM - 1) / kSteBM);
   const int tiles_n = (int)((g.N + kSteBN - 1) / kSteBN);
   const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)g.batch), block(kSteWM * kSteWN * 64);
