@@ -110,9 +110,11 @@ DECODE_WORKLOADS = {"llama7b_w4a16g128_decode": 1, "llama7b_w4a16g128_decode_t16
 
 
 def decode_main(args):
-    """Deployment form (packed 4-bit codes, g128 steps): the 7 linear products of
-    one 7B-shaped block at T tokens (single-token decode by default), timed per
-    launch with HIP events on the launching stream; tokens/s for a 32-block model."""
+    """Deployment form (packed 4-bit codes, g128 steps): the linear products of one
+    7B-shaped block at T tokens (single-token decode by default), with the products
+    that share their input stored as one weight (q|k|v and gate|up, rows
+    concatenated: 4 launches), timed per launch with HIP events on the launching
+    stream; tokens/s for a 32-block model."""
     import numpy as np
     import torch
     import post_quantization_amd as omq
@@ -125,9 +127,13 @@ def decode_main(args):
     inp = synth.block_inputs(c)
     shapes = synth.block_weight_shapes(c)
     layers = []
-    for n in synth.WEIGHT_NAMES:
-        N, K = shapes[n]
-        W = torch.from_numpy(inp["W_" + n]).to(torch.bfloat16).to(dev)
+    fused = (("qkv", ("q", "k", "v")), ("o", ("o",)), ("gate_up", ("gate", "up")),
+             ("down", ("down",)))
+    for n, parts in fused:
+        K = shapes[parts[0]][1]
+        N = sum(shapes[p][0] for p in parts)
+        W = torch.from_numpy(np.concatenate([inp["W_" + p] for p in parts], axis=0)) \
+            .to(torch.bfloat16).to(dev)
         logits = torch.full((N * K // 128,), 4.0, dtype=torch.float32, device=dev)
         r = omq.lwc_fakequant(W, logits, logits, 4, out_dtype=torch.bfloat16, want_codes=True,
                               group=128)
@@ -169,7 +175,7 @@ def decode_main(args):
         a1.record()
         torch.cuda.synchronize()
         durs.append(a0.elapsed_time(a1) / (args.steps * R))
-    # the block as a serving loop runs it: its 7 launches captured once into a HIP
+    # the block as a serving loop runs it: its launches captured once into a HIP
     # graph and replayed (no host work between the kernels)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -193,7 +199,7 @@ def decode_main(args):
     per_layer = [(N * K // 2 + N * (K // 128) * 8 + T * K * 2 + T * N * 4)
                  for _, N, K, *_ in layers]
     bytes_launch = sum(per_layer) / len(per_layer)
-    avg_s = sum(durs) / len(durs) / 1e3             # mean launch duration over the 7 products
+    avg_s = sum(durs) / len(durs) / 1e3             # mean launch duration over the products
     achieved = bytes_launch / avg_s / 1e9
     tok_s = T * 1000.0 / (ms_block * 32)
     cpu = None
@@ -207,7 +213,7 @@ def decode_main(args):
         cpu = {"value": T / (dt * 32), "unit": "tokens/s", "cores": os.cpu_count(),
                "kind": "oracle",
                "sample": "the oracle's packed product (unpack, dequant, bf16, float64 matmul) "
-                         "for the 7 linears of one block at %d token(s), %.2f s, x32 blocks"
+                         "for the linears of one block at %d token(s), %.2f s, x32 blocks"
                          % (T, dt)}
     out = {
         "metric": "W4A16g128 decode tokens/s, LLaMA-7B-shaped linears (32 blocks), 1 GPU",
@@ -215,8 +221,8 @@ def decode_main(args):
         "warmup": args.warmup, "ms_per_step": round(ms_block, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": args.workload, "tokens": T, "d": c.d, "F": c.F, "wbits": 4,
-                   "lwc_group": 128, "step": "the 7 linear products of one block, replayed "
-                                             "from a HIP graph"},
+                   "lwc_group": 128, "step": "the linear products of one block (q|k|v, o, "
+                                             "gate|up, down), replayed from a HIP graph"},
         "roofline": {"kernel": "k_w4a16_gemv (T <= 8) / k_w4a16_gemm", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
