@@ -3,8 +3,9 @@ the C ABI: the full-precision target, the quantized forward, the MSE, every
 gradient group of the straight-through backward, and the AdamW update.
 
 Cases (reduced sizes the oracle finishes in seconds, spanning several GEMM tiles
-and a ragged tail): the 7B-shaped block at W4A4 with s_a (multi-head), the
-70B-shaped grouped-query block at W4A16 and W2A16, the FFN alone at W3A16.
+and a ragged tail): the 7B-shaped block at W4A4 with s_a (multi-head, and with
+grouped-query attention), the 70B-shaped grouped-query block at W4A16 and W2A16,
+the FFN alone at W3A16.
 Tolerance: 2e-2 relative Frobenius per quantity (bf16 matrix-core path).
 """
 import numpy as np
@@ -29,6 +30,10 @@ CASES = {
                                      n_out=4),
     "gqa_w4a16": synth.reduced(synth.BLOCK_CFG5_W4, T=256, d=1024, n_q=8, n_kv=2, F=2816,
                                n_out=10),
+    # grouped-query attention with activation quantization: s_a and the o-site LET
+    # pair broadcast over each group's query heads, forward products on int8 codes
+    "gqa_w4a4": synth.reduced(synth.BLOCK_CFG4, T=256, d=1024, n_q=8, n_kv=2, F=2816,
+                              n_out=10),
     "gqa_w2a16": synth.reduced(synth.BLOCK_CFG5_W2, T=256, d=1024, n_q=8, n_kv=2, F=2816,
                                n_out=10),
     "ffn_w3a16": synth.reduced(synth.FFN_CFG3_W3, T=256, d=512, F=1376, n_out=5),
