@@ -247,6 +247,46 @@ hipError_t wfq(const void* W, int64_t rows, int64_t cols, const float* s, const 
   return e;
 }
 
+// the weight side of linears that share an input (q|k|v, gate|up): one launch over the
+// concatenated rows where the whole-row quantizer applies, else one wfq per linear
+hipError_t wfq_cat(int n, const void* const* Ws, const int64_t* rows, const int* ls,
+                   int64_t cols, const float* s, const float* delta, const float* th, const Theta& t,
+                   int wbits, bool fp, uint16_t* out, const Stats& st, float* Bt, int64_t group,
+                   uint8_t* codes, hipStream_t stream, omq_timer* tm) {
+  RowQuantFwd a;
+  a.x = Ws[0]; a.x_dt = OMQ_BF16; a.cols = cols; a.ldx = cols; a.nbits = wbits;
+  a.group = fp ? 0 : group;
+  if (fp || !rowquant_fwd_segments_ok(a)) {
+    int64_t r0 = 0;
+    for (int k = 0; k < n; ++k) {
+      hipError_t e = wfq(Ws[k], rows[k], cols, s, delta, th, t, ls[k], wbits, fp, out, st, r0,
+                         Bt, group, codes, stream, tm);
+      if (e != hipSuccess) return e;
+      r0 += rows[k];
+    }
+    return hipSuccess;
+  }
+  a.nseg = n;
+  int64_t r0 = 0;
+  for (int k = 0; k < n; ++k) {
+    a.xseg[k] = Ws[k];
+    a.agseg[k] = th + t.ag[ls[k]];
+    a.abseg[k] = th + t.ab[ls[k]];
+    r0 += rows[k];
+    a.seg_end[k] = r0;
+  }
+  a.rows = r0;
+  a.let_mode = s ? OMQ_LET_MUL : OMQ_LET_NONE; a.s = s;
+  a.out = out; a.out_dt = OMQ_BF16; a.ldo = cols;
+  a.h = st.h; a.z = st.z; a.amax = st.amax; a.amin = st.amin;
+  if (delta) { a.fold_delta = delta; a.bias_out = Bt; }
+  if (codes) { a.codes = codes; a.qsum = st.qsum; }
+  // algorithmic bytes: read W, write W_hat (and the codes)
+  const double bytes = (double)r0 * (double)cols * (4.0 + (a.codes ? 1.0 : 0.0));
+  return timed(tm, OMQ_TIMED_WEIGHT_QUANT, bytes, stream,
+               [&] { return launch_rowquant_fwd(a, stream); });
+}
+
 // per-token quantizer with fused LET on its input
 hipError_t aq(const void* X, int x_dt, int64_t T, int64_t C, int64_t ldx, int mode,
               const float* s, const float* delta, int abits, uint16_t* out, const Stats& st,
@@ -350,12 +390,13 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
     const float* d_o = fp ? nullptr : kv.d_o;
     CK(launch_rope_tables(T, m.hd, bd->rope_theta, w.cos_t, w.sin_t, st));
     // weight side of q, k, v, o
-    CK(wfq(W[LQ], dq, d, s_qkv, d_qkv, th, t, LQ, wb, fp, w.Wqkv, w.wq_qkv, 0, w.Bt_qkv,
-               m.group, cq ? w.Cqkv : nullptr, st, tm));
-    CK(wfq(W[LK], dk, d, s_qkv, d_qkv, th, t, LK, wb, fp, w.Wqkv, w.wq_qkv, dq, w.Bt_qkv,
-               m.group, cq ? w.Cqkv : nullptr, st, tm));
-    CK(wfq(W[LV], dk, d, s_qkv, d_qkv, th, t, LV, wb, fp, w.Wqkv, w.wq_qkv, dq + dk,
-               w.Bt_qkv, m.group, cq ? w.Cqkv : nullptr, st, tm));
+    {
+      const void* Wc[3] = {W[LQ], W[LK], W[LV]};
+      const int64_t rc[3] = {dq, dk, dk};
+      const int lc[3] = {LQ, LK, LV};
+      CK(wfq_cat(3, Wc, rc, lc, d, s_qkv, d_qkv, th, t, wb, fp, w.Wqkv, w.wq_qkv, w.Bt_qkv,
+                 m.group, cq ? w.Cqkv : nullptr, st, tm));
+    }
     CK(wfq(W[LO], d, dq, s_o, d_o, th, t, LO, wb, fp, w.Wo, w.wq_o, 0, w.Bt_o, m.group,
            cq ? w.Co : nullptr, st, tm));
     // attention input
@@ -404,10 +445,13 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
     xf_dt = OMQ_BF16;
   }
   // FFN
-  CK(wfq(W[LG], F, d, s_ffn, d_ffn, th, t, LG, wb, fp, w.Wgu, w.wq_gu, 0, w.Bt_gu, m.group,
-         cq ? w.Cgu : nullptr, st, tm));
-  CK(wfq(W[LU], F, d, s_ffn, d_ffn, th, t, LU, wb, fp, w.Wgu, w.wq_gu, F, w.Bt_gu, m.group,
-         cq ? w.Cgu : nullptr, st, tm));
+  {
+    const void* Wc[2] = {W[LG], W[LU]};
+    const int64_t rc[2] = {F, F};
+    const int lc[2] = {LG, LU};
+    CK(wfq_cat(2, Wc, rc, lc, d, s_ffn, d_ffn, th, t, wb, fp, w.Wgu, w.wq_gu, w.Bt_gu, m.group,
+               cq ? w.Cgu : nullptr, st, tm));
+  }
   CK(wfq(W[LD], d, F, nullptr, nullptr, th, t, LD, wb, fp, w.Wd, w.wq_d, 0, nullptr, m.group,
          cq ? w.Cd : nullptr, st, tm));
   CK(aq(xf, xf_dt, T, d, d, mode_let, s_ffn, d_ffn, ab, w.Xf, w.a_f, st, tm,

@@ -26,8 +26,19 @@ struct RowQuantFwd {
   // (row, group), index row * cols/128 + group.  0: one quantizer per row.
   // Grouped rows take no fold_delta (the bias fold runs on its own).
   int64_t group = 0;
+  // nseg > 1 (whole rows of 512 n columns, group 0): concatenated weights (up to 3)
+  // sharing s and fold_delta, segment k holding rows [seg_end[k-1], seg_end[k]) with
+  // its own x rows and logits (indexed by the segment's own row); every output runs
+  // over the concatenated rows.
+  int nseg = 1;
+  int64_t seg_end[3] = {0, 0, 0};
+  const void* xseg[3] = {nullptr, nullptr, nullptr};
+  const float* agseg[3] = {nullptr, nullptr, nullptr};
+  const float* abseg[3] = {nullptr, nullptr, nullptr};
 };
 hipError_t launch_rowquant_fwd(const RowQuantFwd& a, hipStream_t st);
+// whether launch_rowquant_fwd takes a.nseg > 1 (the whole-row LDS kernel applies)
+bool rowquant_fwd_segments_ok(const RowQuantFwd& a);
 
 enum ColMode { COL_NONE = 0, COL_WEIGHT = 1, COL_ACT_DIV = 2, COL_ACT_MUL = 3 };
 

@@ -427,10 +427,23 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_lds(RowQuantFwd a) {
   const int lane = threadIdx.x & 63, w = wave_id();
   const int64_t r = (int64_t)blockIdx.x * 4 + w;
   if (r >= a.rows) return;
+  // the row's segment (concatenated weights): its x rows and logits
+  const void* xb = a.x;
+  const float *lg_g = a.a_gamma, *lg_b = a.a_beta;
+  int64_t rl = r;
+  if (a.nseg > 1) {
+    // selects, not a run-time index into the argument arrays (that would copy the
+    // argument block to scratch memory)
+    const bool s1 = r >= a.seg_end[0], s2 = a.nseg > 2 && r >= a.seg_end[1];
+    xb = s2 ? a.xseg[2] : s1 ? a.xseg[1] : a.xseg[0];
+    lg_g = s2 ? a.agseg[2] : s1 ? a.agseg[1] : a.agseg[0];
+    lg_b = s2 ? a.abseg[2] : s1 ? a.abseg[1] : a.abseg[0];
+    rl = r - (s2 ? a.seg_end[1] : s1 ? a.seg_end[0] : 0);
+  }
   uint4* my = slot[w];
   {
     // lane l's 16-byte piece h of chunk k lands at my[(k NH + h) 64 + l]
-    const char* xr = reinterpret_cast<const char*>(a.x) + r * a.ldx * ESZ;
+    const char* xr = reinterpret_cast<const char*>(xb) + rl * a.ldx * ESZ;
 #pragma unroll
     for (int k = 0; k < NC; ++k)
 #pragma unroll
@@ -526,8 +539,8 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_lds(RowQuantFwd a) {
   wave_argmax(vmax, imax);
   wave_argmin(vmin, imin);
   dot = wave_sum(dot);
-  const float gamma = a.a_gamma ? sigmoid_f32(a.a_gamma[r]) : 1.f;
-  const float beta = a.a_beta ? sigmoid_f32(a.a_beta[r]) : 1.f;
+  const float gamma = lg_g ? sigmoid_f32(lg_g[rl]) : 1.f;
+  const float beta = lg_b ? sigmoid_f32(lg_b[rl]) : 1.f;
   const RowQ q = row_step(vmax, vmin, gamma, beta, a.nbits);
   if (lane == 0) {
     if (a.h) a.h[r] = q.h;
@@ -1138,8 +1151,16 @@ bool launch_fwd_reg(const RowQuantFwd& a, hipStream_t st) {
   return false;
 }
 
+bool rowquant_fwd_segments_ok(const RowQuantFwd& a) {
+  // the whole-row LDS kernel: rows of 512 n columns (n <= 8), 16-byte rows
+  return a.group == 0 && a.nbits < 16 &&
+         (a.cols == 512 || a.cols == 1024 || a.cols == 2048 || a.cols == 4096) &&
+         (a.x_dt == OMQ_F32 || a.ldx % 8 == 0);
+}
+
 hipError_t launch_rowquant_fwd(const RowQuantFwd& a, hipStream_t st) {
   if (a.rows == 0 || a.cols == 0) return hipSuccess;
+  if (a.nseg > 1 && (!rowquant_fwd_segments_ok(a) || a.nseg > 3)) return hipErrorInvalidValue;
   // code sums come with the codes, per whole row
   if (a.qsum && (!a.codes || a.group > 0 || a.nbits >= 16)) return hipErrorInvalidValue;
   if (a.group > 0) {           // groups of 128 (the caller checked cols % 128 == 0)
