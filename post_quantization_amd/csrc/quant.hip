@@ -246,6 +246,131 @@ OMQ_DEV void load8f(const float* p, int64_t c, int n, float v[8]) {
   }
 }
 
+// Long rows (up to NC * 2048 elements, columns a multiple of 8), one 4-wave block per
+// row: each thread keeps NC chunks of 8 consecutive elements in registers (16-byte
+// bf16 loads, 2 x 16-byte float32 loads), so HBM sees one read of x and one write of
+// x_hat; the LET mode is fixed at compile time and the quotient takes the reciprocal
+// product with the exact quotient behind a wave-uniform branch, as in the
+// whole-row LDS kernel.  Same results as k_rowquant_fwd_reg.
+template <int XDT, int NC, int LET>
+__global__ __launch_bounds__(kThreads) void k_rowquant_fwd_blk8(RowQuantFwd a) {
+  const int64_t r = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wid = wave_id();
+  const char* xr = reinterpret_cast<const char*>(a.x) + r * a.ldx * (XDT == OMQ_F32 ? 4 : 2);
+  const int64_t cols = a.cols;
+  float xt[NC][8];
+  float vmax = -FLT_MAX, vmin = FLT_MAX, dot = 0.f;
+  int imax = 0x7fffffff, imin = 0x7fffffff;
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const int64_t c = ((int64_t)k * kThreads + tid) * 8;
+    if (c < cols) {
+      float v[8];
+      load8(xr, XDT, c, v);
+      if constexpr (LET == OMQ_LET_DIV) {
+        float sv[8], dv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        load8f(a.s, c, 8, sv);
+        if (a.delta) load8f(a.delta, c, 8, dv);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xt[k][j] = (v[j] - dv[j]) / sv[j];
+      } else if constexpr (LET == OMQ_LET_MUL) {
+        float sv[8];
+        load8f(a.s, c, 8, sv);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xt[k][j] = sv[j] * v[j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xt[k][j] = v[j];
+      }
+      if (a.fold_delta) {
+        float fv[8];
+        load8f(a.fold_delta, c, 8, fv);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dot = fmaf(fv[j], v[j], dot);
+      }
+    }
+  }
+  // per-thread scan in increasing column order keeps the first index on ties
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const int64_t c = ((int64_t)k * kThreads + tid) * 8;
+    if (c < cols) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (xt[k][j] > vmax || imax == 0x7fffffff) { vmax = xt[k][j]; imax = (int)(c + j); }
+        if (xt[k][j] < vmin || imin == 0x7fffffff) { vmin = xt[k][j]; imin = (int)(c + j); }
+      }
+    }
+  }
+  wave_argmax(vmax, imax);
+  wave_argmin(vmin, imin);
+  dot = wave_sum(dot);
+  __shared__ float s_max[4], s_min[4], s_dot[4];
+  __shared__ int s_imax[4], s_imin[4];
+  if (lane == 0) {
+    s_max[wid] = vmax; s_imax[wid] = imax;
+    s_min[wid] = vmin; s_imin[wid] = imin;
+    s_dot[wid] = dot;
+  }
+  __syncthreads();
+  float M = s_max[0], m = s_min[0], D = s_dot[0];
+  int iM = s_imax[0], im = s_imin[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) {
+    argmax_merge(M, iM, s_max[w], s_imax[w]);
+    argmin_merge(m, im, s_min[w], s_imin[w]);
+    D += s_dot[w];
+  }
+  const float gamma = a.a_gamma ? sigmoid_f32(a.a_gamma[r]) : 1.f;
+  const float beta = a.a_beta ? sigmoid_f32(a.a_beta[r]) : 1.f;
+  const RowQ q = row_step(M, m, gamma, beta, a.nbits);
+  if (tid == 0) {
+    if (a.h) a.h[r] = q.h;
+    if (a.z) a.z[r] = q.z;
+    if (a.amax) a.amax[r] = iM;
+    if (a.amin) a.amin[r] = im;
+    if (a.bias_out) a.bias_out[r] = (a.bias ? a.bias[r] : 0.f) + D;
+  }
+  // rint(x~ / h) as in the whole-row LDS kernel: reciprocal product, exact quotient
+  // for the chunks with an element within the row's bound of a half-integer
+  const float rh = 1.f / q.h;
+  const float thr = fmaxf(fabsf(M), fabsf(m)) * rh * 0x1p-20f;
+  int qs = 0;
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const int64_t c = ((int64_t)k * kThreads + tid) * 8;
+    const bool in = c < cols;
+    float rr[8];
+    bool near = false;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float u = xt[k][j] * rh;
+      rr[j] = rintf(u);
+      near |= in && !(fabsf(fabsf(u - rr[j]) - 0.5f) > thr);
+    }
+    if (__builtin_amdgcn_ballot_w64(near) != 0) {
+      if (near) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) rr[j] = rintf(xt[k][j] / q.h);
+      }
+    }
+    if (in) {
+      float o[8], qq[8];
+      uint32_t cw[2] = {0u, 0u};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        qq[j] = __builtin_amdgcn_fmed3f(rr[j] + q.z, 0.f, q.Q);
+        o[j] = (qq[j] - q.z) * q.h;
+        cw[j >> 2] |= ((uint32_t)qq[j]) << (8 * (j & 3));
+        qs += (int)qq[j];
+      }
+      store8(a.out, a.out_dt, r * a.ldo + c, o);
+      if (a.codes) *reinterpret_cast<uint2*>(a.codes + r * cols + c) = make_uint2(cw[0], cw[1]);
+    }
+  }
+  if (a.qsum) block_qsum(qs, a.qsum + r);
+}
+
 // FULL: every 512-column chunk of the row is whole (cols is a multiple of 512), so
 // no column bounds are checked.
 template <int XDT, int NC, int LET, bool FULL>
@@ -1136,6 +1261,33 @@ bool launch_fwd_wave(const RowQuantFwd& a, hipStream_t st) {
   return false;
 }
 
+// rows of 4097 .. 32768 columns, a multiple of 8, with 16-byte aligned rows and
+// outputs (the 16-byte loads and stores)
+template <int XDT>
+bool launch_fwd_blk8(const RowQuantFwd& a, hipStream_t st) {
+  if (a.cols % 8 || a.ldx % (XDT == OMQ_F32 ? 4 : 8) || a.ldo % (a.out_dt == OMQ_F32 ? 4 : 8))
+    return false;
+  const int64_t nch = (a.cols + 8 * kThreads - 1) / (8 * kThreads);
+  if (nch <= 2 || nch > 16) return false;
+  dim3 grid((unsigned)a.rows);
+#define OMQ_FWD_BLK8(N)                                                                     \
+  if (nch <= N) {                                                                           \
+    if (a.let_mode == OMQ_LET_DIV)                                                          \
+      hipLaunchKernelGGL((k_rowquant_fwd_blk8<XDT, N, OMQ_LET_DIV>), grid, dim3(kThreads), 0, \
+                         st, a);                                                            \
+    else if (a.let_mode == OMQ_LET_MUL)                                                     \
+      hipLaunchKernelGGL((k_rowquant_fwd_blk8<XDT, N, OMQ_LET_MUL>), grid, dim3(kThreads), 0, \
+                         st, a);                                                            \
+    else                                                                                    \
+      hipLaunchKernelGGL((k_rowquant_fwd_blk8<XDT, N, OMQ_LET_NONE>), grid, dim3(kThreads), 0,\
+                         st, a);                                                            \
+    return true;                                                                            \
+  }
+  OMQ_FWD_BLK8(4) OMQ_FWD_BLK8(6) OMQ_FWD_BLK8(8) OMQ_FWD_BLK8(12) OMQ_FWD_BLK8(16)
+#undef OMQ_FWD_BLK8
+  return false;
+}
+
 template <int XDT>
 bool launch_fwd_reg(const RowQuantFwd& a, hipStream_t st) {
   const int64_t nch = (a.cols + 4 * kThreads - 1) / (4 * kThreads);
@@ -1178,6 +1330,8 @@ hipError_t launch_rowquant_fwd(const RowQuantFwd& a, hipStream_t st) {
   if (a.nbits < 16) {
     bool done = a.x_dt == OMQ_F32 ? launch_fwd_wave<OMQ_F32>(a, st)
                                   : launch_fwd_wave<OMQ_BF16>(a, st);
+    if (!done)
+      done = a.x_dt == OMQ_F32 ? launch_fwd_blk8<OMQ_F32>(a, st) : launch_fwd_blk8<OMQ_BF16>(a, st);
     if (!done)
       done = a.x_dt == OMQ_F32 ? launch_fwd_reg<OMQ_F32>(a, st) : launch_fwd_reg<OMQ_BF16>(a, st);
     if (done) return hipGetLastError();

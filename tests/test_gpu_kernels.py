@@ -32,7 +32,8 @@ def _params(rng, c_out, c_in):
 
 @pytest.mark.parametrize("c_out,c_in,nbits,let,out", [
     (77, 200, 4, True, "f32"), (64, 4096, 3, True, "bf16"), (16, 11008, 2, False, "bf16"),
-    (130, 1028, 8, True, "f32"), (4096, 4096, 4, True, "bf16")])
+    (130, 1028, 8, True, "f32"), (4096, 4096, 4, True, "bf16"), (24, 8200, 4, True, "f32"),
+    (40, 28672, 2, True, "bf16")])
 def test_lwc_fakequant_bitexact(c_out, c_in, nbits, let, out):
     log("lwc_fakequant", c_out, c_in, nbits, let, out)
     rng = np.random.default_rng(c_out + c_in)
@@ -104,7 +105,8 @@ def test_lwc_group128_bitexact(c_out, c_in, nbits, let, wdt):
 
 @pytest.mark.parametrize("T,C,nbits,mode,xdt", [
     (48, 200, 4, "div", "f32"), (33, 4096, 4, "div", "bf16"), (64, 4096, 8, "mul", "f32"),
-    (40, 11008, 4, "none", "f32"), (2048, 4096, 4, "div", "bf16")])
+    (40, 11008, 4, "none", "f32"), (2048, 4096, 4, "div", "bf16"), (24, 6000, 4, "div", "f32"),
+    (16, 11008, 3, "mul", "bf16")])
 def test_act_quant_bitexact(T, C, nbits, mode, xdt):
     log("act_quant", T, C, nbits, mode, xdt)
     rng = np.random.default_rng(T * 7 + C)
@@ -158,11 +160,12 @@ def _near_tie_rows(rng, rows, cols, nbits):
     return out
 
 
-@pytest.mark.parametrize("nbits,mode", [(4, "none"), (2, "mul"), (4, "div"), (8, "div")])
-def test_act_quant_near_ties(nbits, mode):
-    log("act_quant_near_ties", nbits, mode)
+@pytest.mark.parametrize("nbits,mode,C", [(4, "none", 520), (2, "mul", 520), (4, "div", 520),
+                                          (8, "div", 520), (4, "div", 6000), (3, "mul", 11008)])
+def test_act_quant_near_ties(nbits, mode, C):
+    log("act_quant_near_ties", nbits, mode, C)
     rng = np.random.default_rng(40 + nbits)
-    T, C = 64, 520
+    T = 64
     Xt0 = _near_tie_rows(rng, T, C, nbits)
     s = rng.uniform(0.5, 2.0, C).astype(F32)
     d = (rng.standard_normal(C) * 0.3).astype(F32)
@@ -196,14 +199,14 @@ def test_act_quant_near_ties(nbits, mode):
     assert np.all(err <= 1e-5 * (np.abs(expect) + 1.0))
 
 
-@pytest.mark.parametrize("nbits", [2, 3, 4])
-def test_lwc_near_ties(nbits):
+@pytest.mark.parametrize("nbits,c_in", [(2, 1032), (3, 1032), (4, 1032), (4, 8200)])
+def test_lwc_near_ties(nbits, c_in):
     """Weight side at gamma = beta = 1 (logits 30 give sigmoid exactly 1 in float32),
     LET scale s on the columns, float32 weights built so that s * W / h lands on
     or next to half-integers."""
-    log("lwc_near_ties", nbits)
+    log("lwc_near_ties", nbits, c_in)
     rng = np.random.default_rng(50 + nbits)
-    c_out, c_in = 48, 1032
+    c_out = 48
     Wt0 = _near_tie_rows(rng, c_out, c_in, nbits)
     s = rng.uniform(0.5, 2.0, c_in).astype(F32)
     W = (Wt0 / s).astype(F32)
