@@ -161,7 +161,9 @@ __global__ __launch_bounds__(kT) void k_flash_fwd(FlashFwd a, int pair) {
 
     const int64_t kend = min(q0 + 128, T);
     const int nkb = (int)((kend + 63) / 64);
-    // scaled, masked scores of key block kb for this lane's query
+    // unscaled scores of key block kb for this lane's query, masked to -inf (the
+    // mask runs only on the blocks that cross the diagonal or the end, one
+    // wave-uniform branch per block)
     auto scores = [&](const uint16_t* Kb, int kb, f32x16 (&sc)[2]) {
   #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -170,19 +172,17 @@ __global__ __launch_bounds__(kT) void k_flash_fwd(FlashFwd a, int pair) {
   #pragma unroll
         for (int s = 0; s < 8; ++s) sc[kk] = mfma(rt_frag(Kb, 32 * kk + l32, s, h), qf[s], sc[kk]);
       }
-      const int64_t k0 = (int64_t)kb * 64;
-      const bool edge = k0 + 63 > q0 + 32 * w || k0 + 64 > T;   // wave-uniform
+      const int k0 = kb * 64;
+      if (k0 + 63 > (int)q0 + 32 * w || k0 + 64 > (int)T) {   // wave-uniform
+        const int qi = (int)q, Ti = (int)T;
   #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
+        for (int kk = 0; kk < 2; ++kk)
   #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = sc[kk][r] * a.scale2;
-          if (edge) {
-            const int64_t key = k0 + 32 * kk + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (key > q || key >= T) v = kNegInf;
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + 32 * kk + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (key > qi || key >= Ti) sc[kk][r] = kNegInf;
           }
-          sc[kk][r] = v;
-        }
+      }
     };
 
     // pass 1: log-sum-exp
@@ -200,19 +200,21 @@ __global__ __launch_bounds__(kT) void k_flash_fwd(FlashFwd a, int pair) {
         uk.store_rows(Ks[buf ^ 1], tid);
         if (kb + 2 < nkb) uk.load(a.K, a.ldk, hk * HD, (int64_t)(kb + 2) * 64, T, tid);
       }
+      // the running max in the scaled (exp2) domain: the largest scaled score is the
+      // largest unscaled one times c (rounding is monotonic)
       float mx = kNegInf;
   #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
   #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kk][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * a.scale2;
       const float mn = fmaxf(m2, mx);
       const float ms = mn == kNegInf ? 0.f : mn;
       float add = 0.f;
   #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
   #pragma unroll
-        for (int r = 0; r < 16; ++r) add += fast_exp2(sc[kk][r] - ms);
+        for (int r = 0; r < 16; ++r) add += fast_exp2(fmaf(sc[kk][r], a.scale2, -ms));
       l = l * fast_exp2(m2 - ms) + add;
       m2 = mn;
       __syncthreads();
@@ -250,7 +252,7 @@ __global__ __launch_bounds__(kT) void k_flash_fwd(FlashFwd a, int pair) {
   #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
   #pragma unroll
-        for (int r = 0; r < 16; ++r) sc[kk][r] = fast_exp2(sc[kk][r] - lse2);
+        for (int r = 0; r < 16; ++r) sc[kk][r] = fast_exp2(fmaf(sc[kk][r], a.scale2, -lse2));
       bf16x8 pf[4];
   #pragma unroll
       for (int s = 0; s < 4; ++s) pf[s] = c_frag(sc[s >> 1], 8 * (s & 1));
@@ -402,26 +404,40 @@ __global__ __launch_bounds__(kT) void k_flash_bwd_dkdv(FlashBwd a, int pair) {
         store(buf ^ 1);
         if (it + 2 < nit) load(it + 2);
       }
-      const bool edge = q0 < k0 + 127 || q0 + 64 > T;        // block-uniform
+      // P from the forward's log-sum-exp (the forward's own formula), masked on the
+      // blocks that cross the diagonal or the end (one block-uniform branch)
   #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
   #pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
           const int row0 = 32 * mb + 8 * gg + 4 * h;
           const float4 L4 = *reinterpret_cast<const float4*>(&Ls[buf][row0]);
-          const float4 D4 = *reinterpret_cast<const float4*>(&Ds[buf][row0]);
           const float Lr[4] = {L4.x, L4.y, L4.z, L4.w};
+  #pragma unroll
+          for (int c = 0; c < 4; ++c)
+            sc[mb][4 * gg + c] = fast_exp2(fmaf(sc[mb][4 * gg + c], a.scale2, -Lr[c]));
+        }
+      if ((int)q0 < (int)k0 + 127 || (int)q0 + 64 > (int)T) {
+        const int ki = (int)key, Ti = (int)T;
+  #pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int qr = (int)q0 + 32 * mb + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (ki > qr || qr >= Ti) sc[mb][r] = 0.f;
+          }
+      }
+  #pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+  #pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          const int row0 = 32 * mb + 8 * gg + 4 * h;
+          const float4 D4 = *reinterpret_cast<const float4*>(&Ds[buf][row0]);
           const float Dr[4] = {D4.x, D4.y, D4.z, D4.w};
   #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const int r = 4 * gg + c;
-            float p = fast_exp2(sc[mb][r] * a.scale2 - Lr[c]);
-            if (edge) {
-              const int64_t qr = q0 + row0 + c;
-              if (key > qr || qr >= T) p = 0.f;
-            }
-            sc[mb][r] = p;
-            dp[mb][r] = p * (dp[mb][r] - Dr[c]) * a.scale;
+            dp[mb][r] = sc[mb][r] * (dp[mb][r] - Dr[c]) * a.scale;
           }
         }
       bf16x8 pf[4], sf[4];
@@ -534,19 +550,25 @@ __global__ __launch_bounds__(kT) void k_flash_bwd_dq(FlashBwd a, int pair) {
           uv.load(a.V, a.ldk, hk * HD, (int64_t)(kb + 2) * 64, T, tid);
         }
       }
-      const int64_t k0 = (int64_t)kb * 64;
-      const bool edge = k0 + 63 > q0 + 32 * w || k0 + 64 > T;
   #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
   #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(sc[kk][r] * a.scale2 - lse);
-          if (edge) {
-            const int64_t kr = k0 + 32 * kk + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (kr > q || kr >= T) p = 0.f;
+        for (int r = 0; r < 16; ++r) sc[kk][r] = fast_exp2(fmaf(sc[kk][r], a.scale2, -lse));
+      const int k0 = kb * 64;
+      if (k0 + 63 > (int)q0 + 32 * w || k0 + 64 > (int)T) {   // wave-uniform
+        const int qi = (int)q, Ti = (int)T;
+  #pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kr = k0 + 32 * kk + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (kr > qi || kr >= Ti) sc[kk][r] = 0.f;
           }
-          dp[kk][r] = p * (dp[kk][r] - Dq) * a.scale;
-        }
+      }
+  #pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) dp[kk][r] = sc[kk][r] * (dp[kk][r] - Dq) * a.scale;
       bf16x8 sf[4];
   #pragma unroll
       for (int s = 0; s < 4; ++s) sf[s] = c_frag(dp[s >> 1], 8 * (s & 1));
@@ -572,6 +594,7 @@ __global__ __launch_bounds__(kT) void k_flash_bwd_dq(FlashBwd a, int pair) {
 
 hipError_t launch_flash_fwd(const FlashFwd& a, hipStream_t st) {
   if (a.T == 0 || a.n_q == 0) return hipSuccess;
+  if (a.T > (int64_t)1 << 30) return hipErrorInvalidValue;    // positions are 32-bit
   const int nqb = (int)((a.T + 127) / 128);
   // pair the causal query blocks when that still leaves a block per compute unit
   const int pair = (int64_t)((nqb + 1) / 2) * a.n_q >= kPairMinBlocks;
@@ -590,6 +613,7 @@ hipError_t launch_attn_bwd_prep(const float* gO, const float* O, int64_t ld, int
 
 hipError_t launch_flash_bwd(const FlashBwd& a, hipStream_t st) {
   if (a.T == 0 || a.n_q == 0) return hipSuccess;
+  if (a.T > (int64_t)1 << 30) return hipErrorInvalidValue;    // positions are 32-bit
   const int nkb = (int)((a.T + 127) / 128);
   const int npb = (nkb + 1) / 2;
   const int n_kv = a.n_q / a.grp;
