@@ -15,7 +15,9 @@
 // between lanes: a C tile whose columns are indexed by lane is re-read as B with
 // its rows as k.  Those rows come in the order 16s + {0..3, 8..11} + 4*(lane/32)
 // within a 16-wide k slice s, so the A operand of that product is read from LDS in
-// the same order (transposed tiles below).
+// the same order: from a transposed copy (tt_frag, the forward's V) or by transposing
+// reads of the row tile itself (rt_tr_frag, the backward's Q, dO and K, whose row
+// tiles the backward reads as well).
 #include "common.h"
 #include "kernels.h"
 
@@ -63,6 +65,27 @@ OMQ_DEV bf16x8 tt_frag(const uint16_t* t, int r, int s, int h) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// A-operand fragment of the transposed view of a row tile, in C-row order: fragment
+// row rb + (lane & 31) is tile column rb + (lane & 31), its k positions are tile rows
+// 16s + 4h + {0..3} and 16s + 8 + 4h + {0..3}.  Two transposing LDS reads
+// (ds_read_b64_tr_b16): in each 16-lane group, lane 4j + q addresses tile row
+// k + j, columns 4q .. 4q+3 of the group's 16 columns, and lane i receives the 4
+// rows k .. k+3 of column i.  (The 272-byte rows put the 4 rows of one read 16 bytes
+// apart modulo 256, a 2-way bank overlap the fragment reads along rows avoid.)
+template <int STRIDE = RS>
+OMQ_DEV bf16x8 rt_tr_frag(const uint16_t* t, int rb, int s, int lane) {
+  const int G = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
+  const int col = rb + 16 * (G & 1) + 4 * q;
+  const int k = 16 * s + 4 * (G >> 1) + j;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(t + k * STRIDE + col));
+  const i16x4 hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(t + (k + 8) * STRIDE + col));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // 8 consecutive C values r0..r0+7 of one tile as a B-operand fragment
 OMQ_DEV bf16x8 c_frag(const f32x16& c, int r0) {
   const u32x4 v = {pack_bf16(c[r0 + 0], c[r0 + 1]), pack_bf16(c[r0 + 2], c[r0 + 3]),
@@ -85,12 +108,13 @@ struct Unit {
     v2 = *reinterpret_cast<const u32x4*>(b + min(r + 2, rows - 1) * ld);
     v3 = *reinterpret_cast<const u32x4*>(b + min(r + 3, rows - 1) * ld);
   }
+  template <int STRIDE = RS>
   OMQ_DEV void store_rows(uint16_t* t, int tid) const {
     const int kq = tid >> 4, c = tid & 15;
-    *reinterpret_cast<u32x4*>(&t[rt_idx(4 * kq + 0, c)]) = v0;
-    *reinterpret_cast<u32x4*>(&t[rt_idx(4 * kq + 1, c)]) = v1;
-    *reinterpret_cast<u32x4*>(&t[rt_idx(4 * kq + 2, c)]) = v2;
-    *reinterpret_cast<u32x4*>(&t[rt_idx(4 * kq + 3, c)]) = v3;
+    *reinterpret_cast<u32x4*>(&t[(4 * kq + 0) * STRIDE + 8 * c]) = v0;
+    *reinterpret_cast<u32x4*>(&t[(4 * kq + 1) * STRIDE + 8 * c]) = v1;
+    *reinterpret_cast<u32x4*>(&t[(4 * kq + 2) * STRIDE + 8 * c]) = v2;
+    *reinterpret_cast<u32x4*>(&t[(4 * kq + 3) * STRIDE + 8 * c]) = v3;
   }
   // the same 4 x 8 block written transposed: 8 rows (columns 8c + j) of 4 positions
   OMQ_DEV void store_transposed(uint16_t* t, int tid) const {
@@ -309,8 +333,6 @@ __global__ __launch_bounds__(kT) void k_attn_bwd_prep(const float* gO, const flo
 __global__ __launch_bounds__(kT) void k_flash_bwd_dkdv(FlashBwd a, int pair) {
   __shared__ __attribute__((aligned(16))) uint16_t Qs[2][64 * RS];
   __shared__ __attribute__((aligned(16))) uint16_t Gs[2][64 * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[2][HD * 64];
-  __shared__ __attribute__((aligned(16))) uint16_t Gt[2][HD * 64];
   __shared__ __attribute__((aligned(16))) float Ls[2][64];
   __shared__ __attribute__((aligned(16))) float Ds[2][64];
   const int64_t T = a.T;
@@ -359,9 +381,7 @@ __global__ __launch_bounds__(kT) void k_flash_bwd_dkdv(FlashBwd a, int pair) {
     };
     auto store = [&](int buf) {
       uq.store_rows(Qs[buf], tid);
-      uq.store_transposed(Qt[buf], tid);
       ug.store_rows(Gs[buf], tid);
-      ug.store_transposed(Gt[buf], tid);
       if (tid < 64) {
         Ls[buf][tid] = lv;
         Ds[buf][tid] = dv;
@@ -450,8 +470,8 @@ __global__ __launch_bounds__(kT) void k_flash_bwd_dkdv(FlashBwd a, int pair) {
       for (int hb = 0; hb < 4; ++hb)
   #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          dvt[hb] = mfma(tt_frag(Gt[buf], 32 * hb + l32, s, h), pf[s], dvt[hb]);
-          dk[hb] = mfma(tt_frag(Qt[buf], 32 * hb + l32, s, h), sf[s], dk[hb]);
+          dvt[hb] = mfma(rt_tr_frag(Gs[buf], 32 * hb, s, lane), pf[s], dvt[hb]);
+          dk[hb] = mfma(rt_tr_frag(Qs[buf], 32 * hb, s, lane), sf[s], dk[hb]);
         }
       __syncthreads();
     }
@@ -480,7 +500,6 @@ __global__ __launch_bounds__(kT) void k_flash_bwd_dkdv(FlashBwd a, int pair) {
 __global__ __launch_bounds__(kT) void k_flash_bwd_dq(FlashBwd a, int pair) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * RS];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][64 * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][HD * 64];
   const int64_t T = a.T;
   const int nqb = (int)((T + 127) / 128);
   // pair: query blocks nqb-1-p and then p (equal causal work per block)
@@ -512,7 +531,6 @@ __global__ __launch_bounds__(kT) void k_flash_bwd_dq(FlashBwd a, int pair) {
     uk.load(a.K, a.ldk, hk * HD, 0, T, tid);
     uv.load(a.V, a.ldk, hk * HD, 0, T, tid);
     uk.store_rows(Ks[0], tid);
-    uk.store_transposed(Kt[0], tid);
     uv.store_rows(Vs[0], tid);
     if (nkb > 1) {
       uk.load(a.K, a.ldk, hk * HD, 64, T, tid);
@@ -543,7 +561,6 @@ __global__ __launch_bounds__(kT) void k_flash_bwd_dq(FlashBwd a, int pair) {
       }
       if (kb + 1 < nkb) {
         uk.store_rows(Ks[buf ^ 1], tid);
-        uk.store_transposed(Kt[buf ^ 1], tid);
         uv.store_rows(Vs[buf ^ 1], tid);
         if (kb + 2 < nkb) {
           uk.load(a.K, a.ldk, hk * HD, (int64_t)(kb + 2) * 64, T, tid);
@@ -575,7 +592,7 @@ __global__ __launch_bounds__(kT) void k_flash_bwd_dq(FlashBwd a, int pair) {
   #pragma unroll
       for (int hb = 0; hb < 4; ++hb)
   #pragma unroll
-        for (int s = 0; s < 4; ++s) dq[hb] = mfma(tt_frag(Kt[buf], 32 * hb + l32, s, h), sf[s], dq[hb]);
+        for (int s = 0; s < 4; ++s) dq[hb] = mfma(rt_tr_frag(Ks[buf], 32 * hb, s, lane), sf[s], dq[hb]);
       __syncthreads();
     }
     if (q < T) {
