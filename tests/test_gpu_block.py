@@ -5,7 +5,8 @@ gradient group of the straight-through backward, and the AdamW update.
 Cases (reduced sizes the oracle finishes in seconds, spanning several GEMM tiles
 and a ragged tail): the 7B-shaped block at W4A4 with s_a (multi-head, and with
 grouped-query attention), the 70B-shaped grouped-query block at W4A16 and W2A16,
-the FFN alone at W3A16.
+the FFN alone at W3A16; and two at full widths: the FFN workload whole (W2A16) and
+the 70B-shaped block on 256 tokens (W4A16).
 Tolerance: 2e-2 relative Frobenius per quantity (bf16 matrix-core path).
 """
 import numpy as np
@@ -42,7 +43,14 @@ CASES = {
                                    F=1408, n_out=5),
     "gqa_w2a16g128": synth.reduced(synth.BLOCK_CFG4_W2G128, T=256, d=1024, n_q=8, n_kv=2,
                                    F=2816, n_out=10),
+    # the FFN workload at its full size (T 2048, d 4096, F 11008, W2A16)
+    "ffn_w2a16_full": synth.FFN_CFG3_W2,
+    # the 70B-shaped block at its full widths (d 8192, 64 / 8 heads, F 28672, W4A16) on
+    # 256 tokens: the oracle's step takes about a minute
+    "gqa70b_w4a16_t256": synth.reduced(synth.BLOCK_CFG5_W4, T=256),
 }
+# the full-width cases take the oracle tens of seconds
+SLOW = {"ffn_w2a16_full": 300, "gqa70b_w4a16_t256": 600}
 
 
 def desc_of(c):
@@ -73,7 +81,8 @@ def upload_weights(c, inp):
     return out
 
 
-@pytest.mark.parametrize("kind", list(CASES))
+@pytest.mark.parametrize("kind", [pytest.param(k, marks=pytest.mark.timeout(SLOW[k])) if k in SLOW
+                                  else k for k in CASES])
 def test_block_step(kind):
     c = CASES[kind]
     log("block step", kind, c)
