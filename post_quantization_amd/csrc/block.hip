@@ -105,7 +105,7 @@ struct Ws {
   uint16_t *Xqkv, *Qh, *Kh, *Vh, *Xo, *Xf, *Xd;
   Stats a_qkv, a_q, a_k, a_v, a_o, a_f, a_d;
   // backward
-  float *dy, *gX, *gA, *gGU, *gxn2, *dh1, *gO, *Datt, *gQh, *gKh, *gVh, *gQr, *gKr, *gY;
+  float *dy, *gA, *gGU, *gxn2, *dh1, *gO, *Datt, *gQh, *gKh, *gVh, *gQr, *gKr, *gY;
   uint16_t *dyb, *gGUb, *dh1b, *gOb, *gYb;
   float *cs, *gs_full, *gd_full, *gsa_full;
   float *rq, *csws, *msews;
@@ -119,7 +119,6 @@ Ws layout(const Dims& m, void* base) {
   Ws w{};
   const int64_t T = m.T, d = m.d, F = m.F, dq = m.dq, dk = m.dk, nqkv = m.nqkv;
   const bool att = !m.ffn_only;
-  const int64_t maxc = std::max({d, att ? dq : 0, F});
   if (att) {
     w.s_o_x = b.take<float>(dq); w.d_o_x = b.take<float>(dq); w.sa_q = b.take<float>(dq);
     w.Wqkv = b.take<uint16_t>(nqkv * d); w.Wo = b.take<uint16_t>(d * dq);
@@ -144,7 +143,6 @@ Ws layout(const Dims& m, void* base) {
   w.a_f = take_stats(b, T); w.a_d = take_stats(b, T);
   // backward
   w.dy = b.take<float>(T * d);
-  w.gX = b.take<float>(T * maxc);
   w.gA = b.take<float>(T * F); w.gGU = b.take<float>(T * 2 * F);
   w.dyb = b.take<uint16_t>(T * d);
   w.gGUb = b.take<uint16_t>(T * 2 * F);
@@ -649,7 +647,7 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
     L.gs_w = dth + t.s_ffn; L.gd_w = dth + t.d_ffn; L.acc_w = 1;
     L.X = m.ffn_only ? x : (const void*)w.xn2; L.x_dt = m.ffn_only ? OMQ_BF16 : OMQ_F32;
     L.a_mode = OMQ_LET_DIV; L.s_x = th + t.s_ffn; L.d_x = th + t.d_ffn; L.ast = w.a_f;
-    L.gx_out = m.ffn_only ? w.gX : w.gxn2; L.gs_x = dth + t.s_ffn; L.gd_x = dth + t.d_ffn;
+    L.gx_out = m.ffn_only ? nullptr : w.gxn2; L.gs_x = dth + t.s_ffn; L.gd_x = dth + t.d_ffn;
     CK(lin_bwd_fused(w, L, T, wb, ab, th, t, dth, st, tm));
   }
   if (m.ffn_only) return OMQ_OK;
@@ -708,7 +706,8 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
     L.segs = segs; L.nseg = 3; L.wst = w.wq_qkv; L.s_w = th + t.s_qkv; L.fold = true;
     L.gs_w = dth + t.s_qkv; L.gd_w = dth + t.d_qkv; L.acc_w = 1;
     L.X = w.xn; L.x_dt = OMQ_F32; L.a_mode = OMQ_LET_DIV; L.s_x = th + t.s_qkv;
-    L.d_x = th + t.d_qkv; L.ast = w.a_qkv; L.gx_out = w.gX;
+    // dL/dx of the block input is not needed (x is no parameter): not written
+    L.d_x = th + t.d_qkv; L.ast = w.a_qkv; L.gx_out = nullptr;
     L.gs_x = dth + t.s_qkv; L.gd_x = dth + t.d_qkv;
     CK(lin_bwd_fused(w, L, T, wb, ab, th, t, dth, st, tm));
   }

@@ -533,7 +533,8 @@ void k_gemm_bf16(Gemm g, int tiles_m, int tiles_n) {
       }
       const float r_c[2] = {1.f / s_c[0], 1.f / s_c[1]};
       const float rh_l = 1.f / h_l;
-      float* Cp = g.C + bz * g.strideC;
+      // activation side: dL/dx is written unless the caller has no use for it (C null)
+      float* Cp = g.C ? g.C + bz * g.strideC : nullptr;
 #pragma unroll 1
       for (int b = 0; b < RW / RB; ++b) {
         if (wr0 + b * RB >= M) break;                // wave-uniform
@@ -625,7 +626,7 @@ void k_gemm_bf16(Gemm g, int tiles_m, int tiles_n) {
           }
           if constexpr (kMode == 2) {
             const int64_t gm = wr0 + b * RB + q;
-            if (kFull || (gm < M && colv))
+            if (Cp && (kFull || (gm < M && colv)))
               *reinterpret_cast<float2*>(&Cp[gm * g.ldc + gn]) = make_float2(up[0], up[1]);
           }
         }
