@@ -512,9 +512,8 @@ struct LinBwd {
   Stats wst;
   const float* s_w;      // LET scale on W (NULL: none)
   bool fold;             // bias fold with delta (needs column sums of dY)
-  float* gs_w;
+  float* gs_w;           // gradients of the LET pair: added to (running totals)
   float* gd_w;
-  int acc_w;             // accumulate into gs_w / gd_w
   int64_t group;         // LWC group along K (0 or 128)
   // activation side
   const void* X;
@@ -565,8 +564,6 @@ hipError_t lin_bwd_fused(const Ws& w, const LinBwd& L, int64_t T, int wbits, int
     if ((e = run_gemm(g, st, tm)) != hipSuccess) return e;
     RowQuantBwd a;
     a.cols = K; a.col_mode = se.col_mode; a.out0 = L.gs_w; a.out1 = L.fold ? L.gd_w : nullptr;
-    a.accumulate = L.acc_w;
-    if ((e = launch_ste_colfinal(a, (int)ntl, colpart, st)) != hipSuccess) return e;
     // one finalizer launch over the concatenated rows, each segment with its own
     // weight rows and logits
     RowQuantBwd b;
@@ -585,7 +582,10 @@ hipError_t lin_bwd_fused(const Ws& w, const LinBwd& L, int64_t T, int wbits, int
     }
     b.col_mode = se.col_mode; b.out0 = L.gs_w;
     if (grouped) b.group = L.group;
-    if ((e = launch_ste_rowfinal(b, grouped ? 1 : (int)nsl, rowpart, st)) != hipSuccess) return e;
+    // the column sums and the row finalizers in one launch (both add into gs_w)
+    if ((e = launch_ste_final(a, (int)ntl, colpart, b, grouped ? 1 : (int)nsl, rowpart, st)) !=
+        hipSuccess)
+      return e;
   }
   // activation side
   gemm_ste_extents(T, K, &nsl, &ntl);
@@ -608,8 +608,7 @@ hipError_t lin_bwd_fused(const Ws& w, const LinBwd& L, int64_t T, int wbits, int
   a.h = L.ast.h; a.z = L.ast.z; a.amax = L.ast.amax; a.amin = L.ast.amin;
   a.col_mode = acol; a.gx = L.gx_out; a.ldgx = K;
   a.out0 = L.gs_x; a.out1 = L.gd_x; a.accumulate = 1;
-  if ((e = launch_ste_colfinal(a, (int)ntl, colpart, st)) != hipSuccess) return e;
-  return launch_ste_rowfinal(a, (int)nsl, rowpart, st);
+  return launch_ste_final(a, (int)ntl, colpart, a, (int)nsl, rowpart, st);
 }
 
 int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w,
@@ -619,6 +618,12 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
   const int64_t T = m.T, d = m.d, F = m.F, dq = m.dq, dk = m.dk, nqkv = m.nqkv;
   const int wb = bd->wbits, ab = bd->abits;
   CK(hipMemsetAsync(dth, 0, t.total * sizeof(float), st));
+  // the column sums add into their destinations: the o-site LET gradients of grouped
+  // heads are formed per query channel first
+  if (!m.ffn_only && m.grp > 1) {
+    CK(hipMemsetAsync(w.gs_full, 0, m.dq * sizeof(float), st));
+    CK(hipMemsetAsync(w.gd_full, 0, m.dq * sizeof(float), st));
+  }
   // FFN second linear (no LET): its input is A = SiLU(G) * U
   {
     const WSeg segs[1] = {{W[LD], d, LD}};
@@ -644,7 +649,7 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
     L.gY = w.gGU; L.N = 2 * F; L.K = d; L.Xh = w.Xf; L.Wh = w.Wgu; L.gYb = w.gGUb;
     L.have_gYb = gu_bf16;
     L.segs = segs; L.nseg = 2; L.wst = w.wq_gu; L.s_w = th + t.s_ffn; L.fold = true;
-    L.gs_w = dth + t.s_ffn; L.gd_w = dth + t.d_ffn; L.acc_w = 1;
+    L.gs_w = dth + t.s_ffn; L.gd_w = dth + t.d_ffn;
     L.X = m.ffn_only ? x : (const void*)w.xn2; L.x_dt = m.ffn_only ? OMQ_BF16 : OMQ_F32;
     L.a_mode = OMQ_LET_DIV; L.s_x = th + t.s_ffn; L.d_x = th + t.d_ffn; L.ast = w.a_f;
     L.gx_out = m.ffn_only ? nullptr : w.gxn2; L.gs_x = dth + t.s_ffn; L.gd_x = dth + t.d_ffn;
@@ -662,7 +667,7 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
     L.group = m.group;
     L.gY = w.dh1; L.N = d; L.K = dq; L.Xh = w.Xo; L.Wh = w.Wo; L.gYb = w.dh1b;
     L.segs = segs; L.nseg = 1; L.wst = w.wq_o; L.s_w = kv.s_o; L.fold = true;
-    L.gs_w = kv.gs_o; L.gd_w = kv.gd_o; L.acc_w = 0;
+    L.gs_w = kv.gs_o; L.gd_w = kv.gd_o;
     L.X = w.O; L.x_dt = OMQ_F32; L.a_mode = OMQ_LET_DIV; L.s_x = kv.s_o; L.d_x = kv.d_o;
     L.ast = w.a_o; L.gx_out = w.gO; L.gs_x = kv.gs_o; L.gd_x = kv.gd_o;
     CK(lin_bwd_fused(w, L, T, wb, ab, th, t, dth, st, tm));
@@ -704,7 +709,7 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
     L.group = m.group;
     L.gY = w.gY; L.N = nqkv; L.K = d; L.Xh = w.Xqkv; L.Wh = w.Wqkv; L.gYb = w.gYb;
     L.segs = segs; L.nseg = 3; L.wst = w.wq_qkv; L.s_w = th + t.s_qkv; L.fold = true;
-    L.gs_w = dth + t.s_qkv; L.gd_w = dth + t.d_qkv; L.acc_w = 1;
+    L.gs_w = dth + t.s_qkv; L.gd_w = dth + t.d_qkv;
     L.X = w.xn; L.x_dt = OMQ_F32; L.a_mode = OMQ_LET_DIV; L.s_x = th + t.s_qkv;
     // dL/dx of the block input is not needed (x is no parameter): not written
     L.d_x = th + t.d_qkv; L.ast = w.a_qkv; L.gx_out = nullptr;

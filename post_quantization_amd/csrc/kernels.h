@@ -81,6 +81,12 @@ hipError_t launch_rowquant_bwd(const RowQuantBwd& a, hipStream_t st);
 // rowfinal turns row partials into LWC-logit gradients and adds the max/min scatter.
 size_t ste_partials_floats(int64_t rows, int64_t cols, int64_t nslabs, int64_t ntiles);
 hipError_t launch_ste_colfinal(const RowQuantBwd& a, int ntiles, float* colpart, hipStream_t st);
+// both in one launch: the column sums of cf (added to cf.out0 / cf.out1 atomically,
+// whatever cf.accumulate says: the destinations hold their running totals) and the
+// row finalizers of rf
+hipError_t launch_ste_final(const RowQuantBwd& cf, int ntiles, const float* colpart,
+                           const RowQuantBwd& rf, int nslabs, const float* rowpart,
+                           hipStream_t st);
 hipError_t launch_ste_rowfinal(const RowQuantBwd& a, int nslabs, const float* rowpart,
                                hipStream_t st);
 

@@ -981,11 +981,10 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_bwd_tile(RowQuantBwd a, i
 // reads, then a shuffle reduction), one of them finishes the row: LWC-logit
 // gradients and the max/min scatter.
 template <int XDT, int LPR>
-__global__ __launch_bounds__(kThreads) void k_rowquant_bwd_rows(RowQuantBwd a, int nslabs,
-                                                                const float* rowpart) {
+OMQ_DEV void rows_final(const RowQuantBwd& a, int nslabs, const float* rowpart, int64_t blk) {
   // quantizer rows: rows, or (row, group) pairs p = row * ng + group
   const int64_t ng = a.group > 0 ? a.cols / 128 : 1;
-  const int64_t p = ((int64_t)blockIdx.x * kThreads + threadIdx.x) / LPR;
+  const int64_t p = (blk * kThreads + threadIdx.x) / LPR;
   const int sub = (int)(threadIdx.x % LPR);
   const bool valid = p < a.rows * ng;
   float gh = 0.f, gzs = 0.f;
@@ -1065,6 +1064,46 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_bwd_rows(RowQuantBwd a, i
       default:
         break;
     }
+  }
+}
+
+template <int XDT, int LPR>
+__global__ __launch_bounds__(kThreads) void k_rowquant_bwd_rows(RowQuantBwd a, int nslabs,
+                                                                const float* rowpart) {
+  rows_final<XDT, LPR>(a, nslabs, rowpart, blockIdx.x);
+}
+
+// Both second stages of a straight-through GEMM epilogue in one launch: workgroups
+// [0, ncb) sum the column partials of 64 columns each (4 waves over the partial
+// rows, the wave sums added in LDS in a fixed order) and add the totals to out0 /
+// out1 atomically, since the row finalizers of the other workgroups scatter into the
+// same vectors meanwhile; the rest finish the quantizer rows as k_rowquant_bwd_rows.
+template <int XDT, int LPR>
+__global__ __launch_bounds__(kThreads) void k_ste_final(RowQuantBwd cf, int ntiles,
+                                                        const float* colpart, int ncb,
+                                                        RowQuantBwd rf, int nslabs,
+                                                        const float* rowpart) {
+  __shared__ float red[2][4][64];
+  if ((int)blockIdx.x >= ncb) {
+    rows_final<XDT, LPR>(rf, nslabs, rowpart, (int64_t)blockIdx.x - ncb);
+    return;
+  }
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int64_t cols = cf.cols, c = (int64_t)blockIdx.x * 64 + lane;
+  float s0 = 0.f, s1 = 0.f;
+  if (c < cols) {
+#pragma unroll 4
+    for (int t = w; t < ntiles; t += 4) {
+      s0 += colpart[((int64_t)t * 2 + 0) * cols + c];
+      s1 += colpart[((int64_t)t * 2 + 1) * cols + c];
+    }
+  }
+  red[0][w][lane] = s0;
+  red[1][w][lane] = s1;
+  __syncthreads();
+  if (w < 2 && c < cols) {
+    float* o = w == 0 ? cf.out0 : cf.out1;
+    if (o) atomicAdd(o + c, ((red[w][0][lane] + red[w][1][lane]) + red[w][2][lane]) + red[w][3][lane]);
   }
 }
 
@@ -1413,6 +1452,36 @@ hipError_t launch_ste_colfinal(const RowQuantBwd& a, int ntiles, float* colpart,
                                hipStream_t st) {
   if (a.col_mode == COL_NONE || !(a.out0 || a.out1)) return hipSuccess;
   return launch_part_colsum(colpart, ntiles, 2, a.cols, a.out0, a.out1, a.accumulate, st);
+}
+
+hipError_t launch_ste_final(const RowQuantBwd& cf, int ntiles, const float* colpart,
+                           const RowQuantBwd& rf, int nslabs, const float* rowpart,
+                           hipStream_t st) {
+  const int ncb = (cf.col_mode != COL_NONE && (cf.out0 || cf.out1) && cf.cols > 0)
+                      ? (int)((cf.cols + 63) / 64) : 0;
+  const int lpr = nslabs == 1 ? 1 : 16;
+  const int64_t n = (rf.nbits < 16 && rf.rows > 0) ? rf.rows * (rf.group > 0 ? rf.cols / 128 : 1)
+                                                   : 0;
+  const int64_t nrb = (n * lpr + kThreads - 1) / kThreads;
+  if (ncb + nrb == 0) return hipSuccess;
+  const dim3 grid((unsigned)(ncb + nrb));
+  const bool f32 = rf.x_dt == OMQ_F32;
+  if (lpr == 1) {
+    if (f32)
+      hipLaunchKernelGGL((k_ste_final<OMQ_F32, 1>), grid, dim3(kThreads), 0, st, cf, ntiles,
+                         colpart, ncb, rf, nslabs, rowpart);
+    else
+      hipLaunchKernelGGL((k_ste_final<OMQ_BF16, 1>), grid, dim3(kThreads), 0, st, cf, ntiles,
+                         colpart, ncb, rf, nslabs, rowpart);
+  } else {
+    if (f32)
+      hipLaunchKernelGGL((k_ste_final<OMQ_F32, 16>), grid, dim3(kThreads), 0, st, cf, ntiles,
+                         colpart, ncb, rf, nslabs, rowpart);
+    else
+      hipLaunchKernelGGL((k_ste_final<OMQ_BF16, 16>), grid, dim3(kThreads), 0, st, cf, ntiles,
+                         colpart, ncb, rf, nslabs, rowpart);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_ste_rowfinal(const RowQuantBwd& a, int nslabs, const float* rowpart,
