@@ -407,8 +407,8 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
     else
       CK(gemm(w.Xqkv, d, w.Wqkv, d, w.Yqkv, nqkv, T, nqkv, d, fp ? nullptr : w.Bt_qkv, nullptr,
               0, 0, st, tm));
-    CK(launch_rope(w.Yqkv, nqkv, T, m.nq, m.hd, w.cos_t, w.sin_t, 0, w.Qr, dq, st));
-    CK(launch_rope(w.Yqkv + dq, nqkv, T, m.nkv, m.hd, w.cos_t, w.sin_t, 0, w.Kr, dk, st));
+    CK(launch_rope2(w.Yqkv, nqkv, w.Qr, dq, m.nq, w.Yqkv + dq, nqkv, w.Kr, dk, m.nkv, T, m.hd,
+                    w.cos_t, w.sin_t, 0, st));
     // s_a on the affinity, then Q/K/V quantized per token
     const bool sa = m.use_sa && !fp;
     CK(aq(w.Qr, OMQ_F32, T, dq, dq, sa ? OMQ_LET_DIV : OMQ_LET_NONE, kv.sa_q, nullptr, ab, w.Qh,
@@ -700,8 +700,8 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
   CK(abwd(w, w.gVh, T, dk, w.Yqkv + dq + dk, OMQ_F32, nqkv, OMQ_LET_NONE, nullptr, nullptr, ab,
           w.a_v, w.gY + dq + dk, nqkv, COL_NONE, nullptr, nullptr, 0, st));
   if (sa && m.grp > 1) CK(launch_kv_reduce_add(w.gsa_full, m.nq, m.nkv, m.hd, dth + t.s_a, st));
-  CK(launch_rope(w.gQr, dq, T, m.nq, m.hd, w.cos_t, w.sin_t, 1, w.gY, nqkv, st));
-  CK(launch_rope(w.gKr, dk, T, m.nkv, m.hd, w.cos_t, w.sin_t, 1, w.gY + dq, nqkv, st));
+  CK(launch_rope2(w.gQr, dq, w.gY, nqkv, m.nq, w.gKr, dk, w.gY + dq, nqkv, m.nkv, T, m.hd,
+                  w.cos_t, w.sin_t, 1, st));
   // q / k / v with the shared qkv LET site
   {
     const WSeg segs[3] = {{W[LQ], dq, LQ}, {W[LK], dk, LK}, {W[LV], dk, LV}};

@@ -147,6 +147,48 @@ __global__ __launch_bounds__(kThreads) void k_rope4(const float* __restrict__ x,
   *reinterpret_cast<float4*>(yr + half) = yb;
 }
 
+// Two RoPE operands in one launch (Q and K heads of one token row): heads [0, n0) of
+// the first, then n1 heads of the second; the per-element arithmetic is k_rope4's.
+struct RopeSeg {
+  const float* x; int64_t ldx; float* y; int64_t ldy; int n;
+};
+__global__ __launch_bounds__(kThreads) void k_rope4x2(RopeSeg s0, RopeSeg s1, int hd,
+                                                      const float* __restrict__ cos_t,
+                                                      const float* __restrict__ sin_t,
+                                                      int inverse) {
+  const int half = hd / 2;
+  const int j = (blockIdx.x * kThreads + threadIdx.x) * 4;   // over (n0 + n1) * half
+  if (j >= (s0.n + s1.n) * half) return;
+  const int64_t t = blockIdx.y;
+  const int hg = j / half, k = j % half;
+  const bool second = hg >= s0.n;
+  const int hh = second ? hg - s0.n : hg;
+  const float* x = second ? s1.x : s0.x;
+  const int64_t ldx = second ? s1.ldx : s0.ldx;
+  float* y = second ? s1.y : s0.y;
+  const int64_t ldy = second ? s1.ldy : s0.ldy;
+  const float4 c = *reinterpret_cast<const float4*>(cos_t + t * half + k);
+  const float4 s = *reinterpret_cast<const float4*>(sin_t + t * half + k);
+  const float* xr = x + t * ldx + (int64_t)hh * hd + k;
+  const float4 a = *reinterpret_cast<const float4*>(xr);
+  const float4 b = *reinterpret_cast<const float4*>(xr + half);
+  float4 ya, yb;
+  if (!inverse) {
+    ya = make_float4(a.x * c.x - b.x * s.x, a.y * c.y - b.y * s.y, a.z * c.z - b.z * s.z,
+                     a.w * c.w - b.w * s.w);
+    yb = make_float4(b.x * c.x + a.x * s.x, b.y * c.y + a.y * s.y, b.z * c.z + a.z * s.z,
+                     b.w * c.w + a.w * s.w);
+  } else {
+    ya = make_float4(a.x * c.x + b.x * s.x, a.y * c.y + b.y * s.y, a.z * c.z + b.z * s.z,
+                     a.w * c.w + b.w * s.w);
+    yb = make_float4(b.x * c.x - a.x * s.x, b.y * c.y - a.y * s.y, b.z * c.z - a.z * s.z,
+                     b.w * c.w - a.w * s.w);
+  }
+  float* yr = y + t * ldy + (int64_t)hh * hd + k;
+  *reinterpret_cast<float4*>(yr) = ya;
+  *reinterpret_cast<float4*>(yr + half) = yb;
+}
+
 __global__ __launch_bounds__(kThreads) void k_silu_gate4(const float* __restrict__ gu, int64_t F,
                                                          float* __restrict__ a) {
   const int64_t f = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4;
@@ -414,6 +456,26 @@ hipError_t launch_rope(const float* x, int64_t ldx, int64_t T, int64_t n_heads, 
   }
   hipLaunchKernelGGL(k_rope, dim3(grid_for(n)), dim3(kThreads), 0, st, x, ldx, T, n_heads, hd,
                      cos_t, sin_t, inverse, y, ldy);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope2(const float* x0, int64_t ldx0, float* y0, int64_t ldy0, int64_t n0,
+                        const float* x1, int64_t ldx1, float* y1, int64_t ldy1, int64_t n1,
+                        int64_t T, int64_t hd, const float* cos_t, const float* sin_t,
+                        int inverse, hipStream_t st) {
+  const bool vec = (hd / 2) % 4 == 0 && ldx0 % 4 == 0 && ldy0 % 4 == 0 && ldx1 % 4 == 0 &&
+                   ldy1 % 4 == 0 && al16(x0) && al16(y0) && al16(x1) && al16(y1) &&
+                   al16(cos_t) && al16(sin_t) && T < 65536 && (n0 + n1) * hd < (1 << 30);
+  if (!vec) {
+    hipError_t e = launch_rope(x0, ldx0, T, n0, hd, cos_t, sin_t, inverse, y0, ldy0, st);
+    if (e != hipSuccess) return e;
+    return launch_rope(x1, ldx1, T, n1, hd, cos_t, sin_t, inverse, y1, ldy1, st);
+  }
+  if (T == 0 || n0 + n1 == 0) return hipSuccess;
+  const RopeSeg s0{x0, ldx0, y0, ldy0, (int)n0}, s1{x1, ldx1, y1, ldy1, (int)n1};
+  const int64_t w = (n0 + n1) * (hd / 2) / 4;
+  hipLaunchKernelGGL(k_rope4x2, dim3((unsigned)((w + kThreads - 1) / kThreads), (unsigned)T),
+                     dim3(kThreads), 0, st, s0, s1, (int)hd, cos_t, sin_t, inverse);
   return hipGetLastError();
 }
 

@@ -1439,9 +1439,12 @@ hipError_t launch_rowquant_bwd(const RowQuantBwd& a, hipStream_t st) {
 #undef OMQ_TILE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const int rs = a.group > 0 ? 1 : (int)nslabs;
+  // column sums added to running totals: one launch with the row finalizers
+  if (a.accumulate) return launch_ste_final(a, (int)ntiles, colpart, a, rs, rowpart, st);
   e = launch_ste_colfinal(a, (int)ntiles, colpart, st);
   if (e != hipSuccess) return e;
-  return launch_ste_rowfinal(a, a.group > 0 ? 1 : (int)nslabs, rowpart, st);
+  return launch_ste_rowfinal(a, rs, rowpart, st);
 }
 
 size_t ste_partials_floats(int64_t rows, int64_t cols, int64_t nslabs, int64_t ntiles) {
