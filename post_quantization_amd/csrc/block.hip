@@ -285,19 +285,29 @@ hipError_t wfq_cat(int n, const void* const* Ws, const int64_t* rows, const int*
                [&] { return launch_rowquant_fwd(a, stream); });
 }
 
+// whether the per-token quantizer of a d-wide input can take its RMSNorm along
+bool rms_fused(int x_dt, int64_t d, int abits, int mode) {
+  RowQuantFwd p;
+  p.x_dt = x_dt; p.cols = d; p.ldx = d; p.nbits = abits; p.let_mode = mode;
+  return rowquant_fwd_rms_ok(p);
+}
+
 // per-token quantizer with fused LET on its input
 hipError_t aq(const void* X, int x_dt, int64_t T, int64_t C, int64_t ldx, int mode,
               const float* s, const float* delta, int abits, uint16_t* out, const Stats& st,
-              hipStream_t stream, omq_timer* tm, uint8_t* codes = nullptr) {
+              hipStream_t stream, omq_timer* tm, uint8_t* codes = nullptr,
+              float* rms_out = nullptr, float* rstd = nullptr, float eps = 0.f) {
   RowQuantFwd a;
   a.x = X; a.x_dt = x_dt; a.rows = T; a.cols = C; a.ldx = ldx;
+  a.rms_out = rms_out; a.rstd = rstd; a.eps = eps;
   a.let_mode = mode; a.s = s; a.delta = delta; a.nbits = abits;
   a.out = out; a.out_dt = OMQ_BF16; a.ldo = C;
   a.h = st.h; a.z = st.z; a.amax = st.amax; a.amin = st.amin;
   if (codes && abits < 16) { a.codes = codes; a.qsum = st.qsum; }
-  // algorithmic bytes: read X, write X_hat (and the codes)
-  const double bytes =
-      (double)T * (double)C * ((x_dt == OMQ_F32 ? 4.0 : 2.0) + 2.0 + (a.codes ? 1.0 : 0.0));
+  // algorithmic bytes: read X, write X_hat (and the codes, and the normalized rows)
+  const double bytes = (double)T * (double)C *
+                       ((x_dt == OMQ_F32 ? 4.0 : 2.0) + 2.0 + (a.codes ? 1.0 : 0.0) +
+                        (rms_out ? 4.0 : 0.0));
   return timed(abits < 16 ? tm : nullptr, OMQ_TIMED_ACT_QUANT, bytes, stream,
                [&] { return launch_rowquant_fwd(a, stream); });
 }
@@ -397,10 +407,15 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
     }
     CK(wfq(W[LO], d, dq, s_o, d_o, th, t, LO, wb, fp, w.Wo, w.wq_o, 0, w.Bt_o, m.group,
            cq ? w.Co : nullptr, st, tm));
-    // attention input
-    CK(launch_rmsnorm(x, OMQ_BF16, T, d, bd->eps, w.xn, w.r1, st));
-    CK(aq(w.xn, OMQ_F32, T, d, d, mode_let, s_qkv, d_qkv, ab, w.Xqkv, w.a_qkv, st, tm,
-          cq ? w.Cxqkv : nullptr));
+    // attention input: the RMSNorm runs inside the quantizer where that applies
+    if (rms_fused(OMQ_BF16, d, ab, mode_let)) {
+      CK(aq(x, OMQ_BF16, T, d, d, mode_let, s_qkv, d_qkv, ab, w.Xqkv, w.a_qkv, st, tm,
+            cq ? w.Cxqkv : nullptr, w.xn, w.r1, bd->eps));
+    } else {
+      CK(launch_rmsnorm(x, OMQ_BF16, T, d, bd->eps, w.xn, w.r1, st));
+      CK(aq(w.xn, OMQ_F32, T, d, d, mode_let, s_qkv, d_qkv, ab, w.Xqkv, w.a_qkv, st, tm,
+            cq ? w.Cxqkv : nullptr));
+    }
     if (cq)
       CK(code_gemm(w.Cxqkv, w.a_qkv, w.Cqkv, w.wq_qkv, w.Yqkv, nqkv, T, nqkv, d, w.Bt_qkv, nullptr,
                    0, 0, st, tm));
@@ -435,7 +450,9 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
     else
       CK(gemm(w.Xo, dq, w.Wo, dq, w.h1, d, T, d, dq, fp ? nullptr : w.Bt_o, x, OMQ_BF16, d, st,
               tm));
-    CK(launch_rmsnorm(w.h1, OMQ_F32, T, d, bd->eps, w.xn2, w.r2, st));
+    // the FFN input's RMSNorm runs inside its quantizer where that applies
+    if (!rms_fused(OMQ_F32, d, ab, mode_let))
+      CK(launch_rmsnorm(w.h1, OMQ_F32, T, d, bd->eps, w.xn2, w.r2, st));
     xf = w.xn2;
     xf_dt = OMQ_F32;
   } else {
@@ -452,8 +469,12 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
   }
   CK(wfq(W[LD], d, F, nullptr, nullptr, th, t, LD, wb, fp, w.Wd, w.wq_d, 0, nullptr, m.group,
          cq ? w.Cd : nullptr, st, tm));
-  CK(aq(xf, xf_dt, T, d, d, mode_let, s_ffn, d_ffn, ab, w.Xf, w.a_f, st, tm,
-        cq ? w.Cxf : nullptr));
+  if (!m.ffn_only && rms_fused(OMQ_F32, d, ab, mode_let))
+    CK(aq(w.h1, OMQ_F32, T, d, d, mode_let, s_ffn, d_ffn, ab, w.Xf, w.a_f, st, tm,
+          cq ? w.Cxf : nullptr, w.xn2, w.r2, bd->eps));
+  else
+    CK(aq(xf, xf_dt, T, d, d, mode_let, s_ffn, d_ffn, ab, w.Xf, w.a_f, st, tm,
+          cq ? w.Cxf : nullptr));
   if (cq)
     CK(code_gemm(w.Cxf, w.a_f, w.Cgu, w.wq_gu, w.GU, 2 * F, T, 2 * F, d, w.Bt_gu, nullptr, 0, 0,
                  st, tm));

@@ -35,10 +35,18 @@ struct RowQuantFwd {
   const void* xseg[3] = {nullptr, nullptr, nullptr};
   const float* agseg[3] = {nullptr, nullptr, nullptr};
   const float* abseg[3] = {nullptr, nullptr, nullptr};
+  // rms_out set (whole-row LDS kernel, activations): x is first divided by its row's
+  // root mean square, sqrt(mean(x^2) + eps); the normalized rows go to rms_out
+  // ([rows x cols] float32) and 1/rms to rstd[rows]
+  float* rms_out = nullptr;
+  float* rstd = nullptr;
+  float eps = 0.f;
 };
 hipError_t launch_rowquant_fwd(const RowQuantFwd& a, hipStream_t st);
 // whether launch_rowquant_fwd takes a.nseg > 1 (the whole-row LDS kernel applies)
 bool rowquant_fwd_segments_ok(const RowQuantFwd& a);
+// whether launch_rowquant_fwd takes a.rms_out
+bool rowquant_fwd_rms_ok(const RowQuantFwd& a);
 
 enum ColMode { COL_NONE = 0, COL_WEIGHT = 1, COL_ACT_DIV = 2, COL_ACT_MUL = 3 };
 

@@ -544,7 +544,9 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_wave(RowQuantFwd a) {
 // copies are in flight per compute unit.  For fp32 input pass 1 writes x~ back
 // over the raw value (the LET division happens once per element).  Same results as
 // k_rowquant_fwd_wave.
-template <int XDT, int NC, int LET>
+// RMS: x is first normalized by its row's root mean square (the RMSNorm before the
+// linear, unit gain), the normalized row written to rms_out and 1/rms to rstd.
+template <int XDT, int NC, int LET, bool RMS = false>
 __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_lds(RowQuantFwd a) {
   constexpr int ESZ = XDT == OMQ_F32 ? 4 : 2;
   constexpr int NH = ESZ / 2;                      // 1 KB copies per 8-element chunk
@@ -578,6 +580,32 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_lds(RowQuantFwd a) {
             (__attribute__((address_space(3))) void*)(my + (k * NH + h) * 64), 16, 0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
+  // the row's 1 / rms: sum of squares over the staged row
+  float rs = 1.f;
+  if constexpr (RMS) {
+    float ss = 0.f;
+#pragma unroll 2
+    for (int k = 0; k < NC; ++k) {
+      if constexpr (XDT == OMQ_F32) {
+        const uint4 t0 = my[(2 * k) * 64 + lane], t1 = my[(2 * k + 1) * 64 + lane];
+        const uint32_t wv[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss = fmaf(__uint_as_float(wv[j]), __uint_as_float(wv[j]), ss);
+      } else {
+        const uint4 t0 = my[k * 64 + lane];
+        const uint32_t wv[4] = {t0.x, t0.y, t0.z, t0.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float lo = __uint_as_float(wv[q] << 16), hi = __uint_as_float(wv[q] & 0xffff0000u);
+          ss = fmaf(lo, lo, ss);
+          ss = fmaf(hi, hi, ss);
+        }
+      }
+    }
+    ss = wave_sum(ss);
+    rs = 1.f / sqrtf(ss / (float)a.cols + a.eps);
+    if (lane == 0 && a.rstd) a.rstd[r] = rs;
+  }
   // x~ of chunk k for this lane (8 consecutive columns c .. c+7)
   auto chunk = [&](int k, float (&xt)[8], float& dot, bool first) {
     const int64_t c = ((int64_t)k * 64 + lane) * 8;
@@ -600,6 +628,11 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_lds(RowQuantFwd a) {
         v[2 * q] = __uint_as_float(wv[q] << 16);
         v[2 * q + 1] = __uint_as_float(wv[q] & 0xffff0000u);
       }
+    }
+    if constexpr (RMS) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = v[j] * rs;
+      if (first) store8(a.rms_out, OMQ_F32, r * a.cols + c, v);
     }
     if constexpr (LET == OMQ_LET_DIV) {
       float sv[8], dv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -1284,9 +1317,18 @@ bool launch_fwd_wave(const RowQuantFwd& a, hipStream_t st) {
   else                                                                                        \
     hipLaunchKernelGGL((k_rowquant_fwd_lds<XDT, N, OMQ_LET_NONE>), grid, dim3(kThreads), 0, st,\
                        a);
+#define OMQ_FWD_RMS(N)                                                                        \
+  if (a.let_mode == OMQ_LET_DIV)                                                              \
+    hipLaunchKernelGGL((k_rowquant_fwd_lds<XDT, N, OMQ_LET_DIV, true>), grid, dim3(kThreads), \
+                       0, st, a);                                                             \
+  else                                                                                        \
+    hipLaunchKernelGGL((k_rowquant_fwd_lds<XDT, N, OMQ_LET_NONE, true>), grid, dim3(kThreads),\
+                       0, st, a);
 #define OMQ_FWD_WAVE(N)                                                                       \
   if (nc <= N) {                                                                              \
-    if (a.cols == N * 512) {                                                                  \
+    if (a.rms_out && a.cols == N * 512) {                                                     \
+      OMQ_FWD_RMS(N)                                                                          \
+    } else if (a.cols == N * 512) {                                                           \
       OMQ_FWD_LDS(N)                                                                          \
     } else {                                                                                  \
       OMQ_FWD_WAVE_L(N, false)                                                                \
@@ -1295,6 +1337,7 @@ bool launch_fwd_wave(const RowQuantFwd& a, hipStream_t st) {
   }
   OMQ_FWD_WAVE(1) OMQ_FWD_WAVE(2) OMQ_FWD_WAVE(4) OMQ_FWD_WAVE(8)
 #undef OMQ_FWD_LDS
+#undef OMQ_FWD_RMS
 #undef OMQ_FWD_WAVE_L
 #undef OMQ_FWD_WAVE
   return false;
@@ -1342,6 +1385,14 @@ bool launch_fwd_reg(const RowQuantFwd& a, hipStream_t st) {
   return false;
 }
 
+bool rowquant_fwd_rms_ok(const RowQuantFwd& a) {
+  // the whole-row LDS kernel, activations (no logits, no fold), LET divide or none
+  return a.group == 0 && a.nbits < 16 && a.nseg == 1 && !a.fold_delta && !a.a_gamma &&
+         (a.let_mode == OMQ_LET_DIV || a.let_mode == OMQ_LET_NONE) && a.ldx == a.cols &&
+         (a.cols == 512 || a.cols == 1024 || a.cols == 2048 || a.cols == 4096) &&
+         (a.x_dt == OMQ_F32 || a.ldx % 8 == 0);
+}
+
 bool rowquant_fwd_segments_ok(const RowQuantFwd& a) {
   // the whole-row LDS kernel: rows of 512 n columns (n <= 8), 16-byte rows
   return a.group == 0 && a.nbits < 16 &&
@@ -1352,6 +1403,7 @@ bool rowquant_fwd_segments_ok(const RowQuantFwd& a) {
 hipError_t launch_rowquant_fwd(const RowQuantFwd& a, hipStream_t st) {
   if (a.rows == 0 || a.cols == 0) return hipSuccess;
   if (a.nseg > 1 && (!rowquant_fwd_segments_ok(a) || a.nseg > 3)) return hipErrorInvalidValue;
+  if (a.rms_out && !rowquant_fwd_rms_ok(a)) return hipErrorInvalidValue;
   // code sums come with the codes, per whole row
   if (a.qsum && (!a.codes || a.group > 0 || a.nbits >= 16)) return hipErrorInvalidValue;
   if (a.group > 0) {           // groups of 128 (the caller checked cols % 128 == 0)
