@@ -66,7 +66,7 @@ int omq_lwc_fakequant(const void* W, int w_dt, int64_t c_out, int64_t c_in, int6
   if (B_tilde && !delta) {
     // no shift: B~ = B
     if (B) OMQ_HIP_CHECK(hipMemcpyAsync(B_tilde, B, c_out * 4, hipMemcpyDeviceToDevice, S(stream)));
-    else OMQ_HIP_CHECK(hipMemsetAsync(B_tilde, 0, c_out * 4, S(stream)));
+    else OMQ_HIP_CHECK(launch_fill_f32(B_tilde, c_out, 0.f, S(stream)));
     a.bias_out = nullptr;
   }
   if (grp) {
@@ -110,7 +110,7 @@ int omq_let_apply(const void* X, int x_dt, int64_t T, int64_t c_in, const float*
     else if (B)
       OMQ_HIP_CHECK(hipMemcpyAsync(B_tilde, B, c_out * 4, hipMemcpyDeviceToDevice, S(stream)));
     else
-      OMQ_HIP_CHECK(hipMemsetAsync(B_tilde, 0, c_out * 4, S(stream)));
+      OMQ_HIP_CHECK(launch_fill_f32(B_tilde, c_out, 0.f, S(stream)));
   }
   return OMQ_OK;
 }
@@ -380,7 +380,7 @@ int omq_qlinear_bwd(const omq_qlinear_desc* d, const void* X, const void* W, con
   float* g_d = d->use_let ? dtheta + 2 * rq + ci : nullptr;
   // dW = dY^T X_hat and dX_hat = dY W_hat, with dY^T, X_hat and W_hat read K-major
   if (dl && !bf) OMQ_HIP_CHECK(launch_colsum(dY, T, co, co, w.colsum, w.cs, st));
-  if (d->wbits >= 16) OMQ_HIP_CHECK(hipMemsetAsync(dtheta, 0, 2 * rq * sizeof(float), st));
+  if (d->wbits >= 16) OMQ_HIP_CHECK(launch_fill_f32(dtheta, 2 * rq, 0.f, st));
   if (bf) {
     // bf16 path: dY's bf16 copy and column sums in one pass; both straight-through
     // passes run in the GEMM epilogues

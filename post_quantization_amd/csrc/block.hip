@@ -638,12 +638,12 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
   omq_timer* tm = bd->timer;
   const int64_t T = m.T, d = m.d, F = m.F, dq = m.dq, dk = m.dk, nqkv = m.nqkv;
   const int wb = bd->wbits, ab = bd->abits;
-  CK(hipMemsetAsync(dth, 0, t.total * sizeof(float), st));
+  CK(launch_fill_f32(dth, t.total, 0.f, st));
   // the column sums add into their destinations: the o-site LET gradients of grouped
   // heads are formed per query channel first
   if (!m.ffn_only && m.grp > 1) {
-    CK(hipMemsetAsync(w.gs_full, 0, m.dq * sizeof(float), st));
-    CK(hipMemsetAsync(w.gd_full, 0, m.dq * sizeof(float), st));
+    CK(launch_fill_f32(w.gs_full, m.dq, 0.f, st));
+    CK(launch_fill_f32(w.gd_full, m.dq, 0.f, st));
   }
   // FFN second linear (no LET): its input is A = SiLU(G) * U
   {

@@ -459,6 +459,22 @@ hipError_t launch_rope(const float* x, int64_t ldx, int64_t T, int64_t n_heads, 
   return hipGetLastError();
 }
 
+// a float32 buffer set to one value: a kernel rather than a memset, so the
+// calls stay valid inside a captured graph
+__global__ __launch_bounds__(kThreads) void k_fill_f32(float* __restrict__ p, int64_t n, float v) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * kThreads)
+    p[i] = v;
+}
+
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + kThreads - 1) / kThreads;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_fill_f32, dim3((unsigned)blocks), dim3(kThreads), 0, st, p, n, v);
+  return hipGetLastError();
+}
+
 hipError_t launch_rope2(const float* x0, int64_t ldx0, float* y0, int64_t ldy0, int64_t n0,
                         const float* x1, int64_t ldx1, float* y1, int64_t ldy1, int64_t n1,
                         int64_t T, int64_t hd, const float* cos_t, const float* sin_t,

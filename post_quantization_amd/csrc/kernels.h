@@ -186,6 +186,8 @@ hipError_t launch_rope_tables(int64_t T, int64_t hd, float theta, float* cos_t, 
 hipError_t launch_rope(const float* x, int64_t ldx, int64_t T, int64_t n_heads, int64_t hd,
                        const float* cos_t, const float* sin_t, int inverse, float* y,
                        int64_t ldy, hipStream_t st);
+// p[0 .. n) = v (a kernel, also inside captured graphs)
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t st);
 // RoPE of two operands (the Q and K heads) in one launch
 hipError_t launch_rope2(const float* x0, int64_t ldx0, float* y0, int64_t ldy0, int64_t n0,
                         const float* x1, int64_t ldx1, float* y1, int64_t ldy1, int64_t n1,

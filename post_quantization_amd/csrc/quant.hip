@@ -1603,7 +1603,7 @@ hipError_t launch_cvt_bf16_colsum(const float* in, int64_t rows, int64_t cols, u
                                   float* colsum, float* ws, hipStream_t st) {
   if (cols == 0) return hipSuccess;
   const int64_t np = (rows + kColsumRows - 1) / kColsumRows;
-  if (np == 0) return colsum ? hipMemsetAsync(colsum, 0, cols * sizeof(float), st) : hipSuccess;
+  if (np == 0) return colsum ? launch_fill_f32(colsum, cols, 0.f, st) : hipSuccess;
   float* part = colsum ? ws : nullptr;
   if (cols % 8 == 0) {
     const unsigned cb = (unsigned)((cols / 8 + 63) / 64);
@@ -1625,7 +1625,7 @@ hipError_t launch_colsum(const float* in, int64_t rows, int64_t cols, int64_t ld
   const int64_t np = (rows + kColsumRows - 1) / kColsumRows;
   const unsigned cb = (unsigned)((cols + kThreads - 1) / kThreads);
   if (np == 0) {
-    return hipMemsetAsync(out, 0, cols * sizeof(float), st);
+    return launch_fill_f32(out, cols, 0.f, st);
   }
   hipLaunchKernelGGL(k_colsum_part, dim3(cb, (unsigned)np), dim3(kThreads), 0, st, in, rows, cols,
                      ld, ws);
