@@ -375,8 +375,8 @@ def main():
                          "FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py: this build measures one GPU only (the block-calibration step does not "
-              "shard across GPUs here); run with --gpus 1", file=sys.stderr)
+        print("bench.py: the block-calibration step runs on one GPU (blocks are sequential "
+              "and the step is not sharded across GPUs); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

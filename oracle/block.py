@@ -10,7 +10,7 @@ Follows the paper reading "OmniQuant ..." (onecrewdev.com):
   the attention affinity Softmax(Q K^T) = Softmax((Q / s_a)(s_a * K)^T); Q, K, V
   quantized (low-bit KV cache); the softmax output kept in full precision.
 
-Readings of what the pages leave open (all listed in the design doc):
+Readings of what the pages leave open:
 * the norm of the objective is the mean squared error over tokens x hidden;
 * RMSNorm with eps 1e-6 and unit gain; RoPE (rotate-half, theta 10000,
   positions 0..T-1); SiLU gating; no biases (B = 0, so B~ = delta W);

@@ -12,7 +12,7 @@ Follows the paper reading "OmniQuant: ..." (onecrewdev.com):
   AdamW with zero weight decay, learning rate 5e-3 for the LWC logits and 1e-2 for
   the LET parameters.
 
-Readings (listed in DESIGN.md):
+Readings of points the pages leave open:
 * "the same input X" is the quantized chain's input (there is no separate
   full-precision chain): the target of block k is F(W_k, X_k) with X_k the output of
   the calibrated blocks 1..k-1;

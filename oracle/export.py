@@ -12,7 +12,7 @@ Follows the paper reading "OmniQuant: ..." (onecrewdev.com):
 * section "LWC": the deployed weight is the integer code q with its step h and zero
   point z, dequantized as (q - z) h.
 
-Readings (the pages print no layout; each is listed in the design doc):
+Readings (the pages print no layout):
 * codes are packed along the input-channel axis into 32-bit words, floor(32 / N)
   codes per word, code j of a word in bits [j N, (j + 1) N), the word's lowest
   column first; a row is ceil(C_in / per_word) words; unused high bits are 0;

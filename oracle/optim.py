@@ -5,10 +5,10 @@ TEST INFRASTRUCTURE ONLY (see the package header).
 Follows the paper reading "OmniQuant ..." (onecrewdev.com), section "实验证据":
 AdamW with zero weight decay, learning rate 5e-3 for the LWC logits and 1e-2 for
 the LET parameters, batch size 1.  Adam's beta1 = 0.9, beta2 = 0.999 and
-eps = 1e-8 are not on the pages (standard defaults; a reading listed in
-the design doc).  The single-layer fp32 workload uses plain SGD (lr 5e-3).
+eps = 1e-8 are not on the pages (standard defaults, a reading of a point the
+pages leave open).  The single-layer fp32 workload uses plain SGD (lr 5e-3).
 
-Parity: pinned by tests/test_oracle_optim.py (first Adam step is lr * sign(g)
+Parity: pinned by tests/test_oracle_linear.py (first Adam step is lr * sign(g)
 for |g| >> eps; SGD is theta - lr g; bias correction makes the k-th step of a
 constant gradient equal to the first).
 """

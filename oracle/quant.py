@@ -15,7 +15,7 @@ for LLMs" (onecrewdev.com):
   (s scales W's input channels), B~ = B + delta W; Y = Q_a(X~) Q_w(W~) + B~.
 * section "实验证据": weights per output channel, activations per token.
 
-Readings of points the pages leave open (each is listed in the design doc):
+Readings of points the pages leave open:
 * rounding ties go to even (IEEE rint);
 * h is floored at 1e-8 (a constant row would otherwise divide by zero);
 * only the rounding is straight-through (the blog on LWC, section 2.2, states the
