@@ -1350,7 +1350,7 @@ bool launch_fwd_blk8(const RowQuantFwd& a, hipStream_t st) {
   if (a.cols % 8 || a.ldx % (XDT == OMQ_F32 ? 4 : 8) || a.ldo % (a.out_dt == OMQ_F32 ? 4 : 8))
     return false;
   const int64_t nch = (a.cols + 8 * kThreads - 1) / (8 * kThreads);
-  if (nch <= 2 || nch > 16) return false;
+  if (nch > 16) return false;
   dim3 grid((unsigned)a.rows);
 #define OMQ_FWD_BLK8(N)                                                                     \
   if (nch <= N) {                                                                           \
@@ -1365,7 +1365,8 @@ bool launch_fwd_blk8(const RowQuantFwd& a, hipStream_t st) {
                          st, a);                                                            \
     return true;                                                                            \
   }
-  OMQ_FWD_BLK8(4) OMQ_FWD_BLK8(6) OMQ_FWD_BLK8(8) OMQ_FWD_BLK8(12) OMQ_FWD_BLK8(16)
+  OMQ_FWD_BLK8(1) OMQ_FWD_BLK8(2) OMQ_FWD_BLK8(4) OMQ_FWD_BLK8(6) OMQ_FWD_BLK8(8)
+  OMQ_FWD_BLK8(12) OMQ_FWD_BLK8(16)
 #undef OMQ_FWD_BLK8
   return false;
 }
@@ -1419,8 +1420,13 @@ hipError_t launch_rowquant_fwd(const RowQuantFwd& a, hipStream_t st) {
   }
   dim3 grid((unsigned)a.rows);
   if (a.nbits < 16) {
-    bool done = a.x_dt == OMQ_F32 ? launch_fwd_wave<OMQ_F32>(a, st)
-                                  : launch_fwd_wave<OMQ_BF16>(a, st);
+    // float32 rows of 2048 .. 4096 columns (activations): a block per row in registers
+    // keeps more rows in flight than staging each in LDS (16 KB a row)
+    bool done = a.x_dt == OMQ_F32 && !a.rms_out && a.nseg == 1 && a.cols >= 2048 &&
+                a.cols <= 4096 && launch_fwd_blk8<OMQ_F32>(a, st);
+    if (!done)
+      done = a.x_dt == OMQ_F32 ? launch_fwd_wave<OMQ_F32>(a, st)
+                               : launch_fwd_wave<OMQ_BF16>(a, st);
     if (!done)
       done = a.x_dt == OMQ_F32 ? launch_fwd_blk8<OMQ_F32>(a, st) : launch_fwd_blk8<OMQ_BF16>(a, st);
     if (!done)

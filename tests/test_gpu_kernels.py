@@ -161,7 +161,8 @@ def _near_tie_rows(rng, rows, cols, nbits):
 
 
 @pytest.mark.parametrize("nbits,mode,C", [(4, "none", 520), (2, "mul", 520), (4, "div", 520),
-                                          (8, "div", 520), (4, "div", 6000), (3, "mul", 11008)])
+                                          (8, "div", 520), (4, "div", 4096), (4, "div", 6000),
+                                          (3, "mul", 11008)])
 def test_act_quant_near_ties(nbits, mode, C):
     log("act_quant_near_ties", nbits, mode, C)
     rng = np.random.default_rng(40 + nbits)
