@@ -252,7 +252,8 @@ OMQ_DEV void load8f(const float* p, int64_t c, int n, float v[8]) {
 // x_hat; the LET mode is fixed at compile time and the quotient takes the reciprocal
 // product with the exact quotient behind a wave-uniform branch, as in the
 // whole-row LDS kernel.  Same results as k_rowquant_fwd_reg.
-template <int XDT, int NC, int LET>
+// RMS: the row is first divided by its root mean square (as the whole-row LDS kernel).
+template <int XDT, int NC, int LET, bool RMS = false>
 __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_blk8(RowQuantFwd a) {
   const int64_t r = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wid = wave_id();
@@ -267,7 +268,10 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_blk8(RowQuantFwd a) {
     if (c < cols) {
       float v[8];
       load8(xr, XDT, c, v);
-      if constexpr (LET == OMQ_LET_DIV) {
+      if constexpr (RMS) {                         // LET after the normalization below
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xt[k][j] = v[j];
+      } else if constexpr (LET == OMQ_LET_DIV) {
         float sv[8], dv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         load8f(a.s, c, 8, sv);
         if (a.delta) load8f(a.delta, c, 8, dv);
@@ -282,11 +286,50 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_blk8(RowQuantFwd a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) xt[k][j] = v[j];
       }
-      if (a.fold_delta) {
+      if (!RMS && a.fold_delta) {
         float fv[8];
         load8f(a.fold_delta, c, 8, fv);
 #pragma unroll
         for (int j = 0; j < 8; ++j) dot = fmaf(fv[j], v[j], dot);
+      }
+    }
+  }
+  if constexpr (RMS) {
+    // 1 / rms of the row (block sum of squares), the normalized row stored, then LET
+    __shared__ float s_ss[4];
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      const int64_t c = ((int64_t)k * kThreads + tid) * 8;
+      if (c < cols) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss = fmaf(xt[k][j], xt[k][j], ss);
+      }
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) s_ss[wid] = ss;
+    __syncthreads();
+    ss = (s_ss[0] + s_ss[1]) + (s_ss[2] + s_ss[3]);
+    const float rs = 1.f / sqrtf(ss / (float)cols + a.eps);
+    if (tid == 0 && a.rstd) a.rstd[r] = rs;
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      const int64_t c = ((int64_t)k * kThreads + tid) * 8;
+      if (c < cols) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = xt[k][j] * rs;
+        store8(a.rms_out, OMQ_F32, r * cols + c, v);
+        if constexpr (LET == OMQ_LET_DIV) {
+          float sv[8], dv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+          load8f(a.s, c, 8, sv);
+          if (a.delta) load8f(a.delta, c, 8, dv);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) xt[k][j] = (v[j] - dv[j]) / sv[j];
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) xt[k][j] = v[j];
+        }
       }
     }
   }
@@ -1365,6 +1408,21 @@ bool launch_fwd_blk8(const RowQuantFwd& a, hipStream_t st) {
                          st, a);                                                            \
     return true;                                                                            \
   }
+  if (a.rms_out) {
+#define OMQ_FWD_BLK8R(N)                                                                    \
+  if (nch <= N) {                                                                           \
+    if (a.let_mode == OMQ_LET_DIV)                                                          \
+      hipLaunchKernelGGL((k_rowquant_fwd_blk8<XDT, N, OMQ_LET_DIV, true>), grid,            \
+                         dim3(kThreads), 0, st, a);                                         \
+    else                                                                                    \
+      hipLaunchKernelGGL((k_rowquant_fwd_blk8<XDT, N, OMQ_LET_NONE, true>), grid,           \
+                         dim3(kThreads), 0, st, a);                                         \
+    return true;                                                                            \
+  }
+    OMQ_FWD_BLK8R(1) OMQ_FWD_BLK8R(2) OMQ_FWD_BLK8R(4) OMQ_FWD_BLK8R(8) OMQ_FWD_BLK8R(16)
+#undef OMQ_FWD_BLK8R
+    return false;
+  }
   OMQ_FWD_BLK8(1) OMQ_FWD_BLK8(2) OMQ_FWD_BLK8(4) OMQ_FWD_BLK8(6) OMQ_FWD_BLK8(8)
   OMQ_FWD_BLK8(12) OMQ_FWD_BLK8(16)
 #undef OMQ_FWD_BLK8
@@ -1387,10 +1445,11 @@ bool launch_fwd_reg(const RowQuantFwd& a, hipStream_t st) {
 }
 
 bool rowquant_fwd_rms_ok(const RowQuantFwd& a) {
-  // the whole-row LDS kernel, activations (no logits, no fold), LET divide or none
+  // activations (no logits, no fold), LET divide or none: the whole-row LDS kernel
+  // (512 or 1024 columns) or the block-per-row kernel (2048 .. 32768, multiples of 8)
   return a.group == 0 && a.nbits < 16 && a.nseg == 1 && !a.fold_delta && !a.a_gamma &&
          (a.let_mode == OMQ_LET_DIV || a.let_mode == OMQ_LET_NONE) && a.ldx == a.cols &&
-         (a.cols == 512 || a.cols == 1024 || a.cols == 2048 || a.cols == 4096) &&
+         (a.cols == 512 || a.cols == 1024 || (a.cols >= 2048 && a.cols <= 32768 && a.cols % 8 == 0)) &&
          (a.x_dt == OMQ_F32 || a.ldx % 8 == 0);
 }
 
@@ -1422,8 +1481,10 @@ hipError_t launch_rowquant_fwd(const RowQuantFwd& a, hipStream_t st) {
   if (a.nbits < 16) {
     // float32 rows of 2048 .. 4096 columns (activations): a block per row in registers
     // keeps more rows in flight than staging each in LDS (16 KB a row)
-    bool done = a.x_dt == OMQ_F32 && !a.rms_out && a.nseg == 1 && a.cols >= 2048 &&
-                a.cols <= 4096 && launch_fwd_blk8<OMQ_F32>(a, st);
+    bool done = (a.x_dt == OMQ_F32 || a.rms_out) && a.nseg == 1 && a.cols >= 2048 &&
+                (a.cols <= 4096 || a.rms_out) &&
+                (a.x_dt == OMQ_F32 ? launch_fwd_blk8<OMQ_F32>(a, st)
+                                   : launch_fwd_blk8<OMQ_BF16>(a, st));
     if (!done)
       done = a.x_dt == OMQ_F32 ? launch_fwd_wave<OMQ_F32>(a, st)
                                : launch_fwd_wave<OMQ_BF16>(a, st);

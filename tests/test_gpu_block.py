@@ -48,9 +48,13 @@ CASES = {
     # the 70B-shaped block at its full widths (d 8192, 64 / 8 heads, F 28672, W4A16) on
     # 256 tokens: the oracle's step takes about a minute
     "gqa70b_w4a16_t256": synth.reduced(synth.BLOCK_CFG5_W4, T=256),
+    # the bench's 7B-shaped W4A4 block at its full widths on 128 tokens (every
+    # gradient group; the whole 2048-token step is checked below by its forward, loss
+    # and update)
+    "mha_w4a4_full_widths_t128": synth.reduced(synth.BLOCK_CFG4, T=128),
 }
 # the full-width cases take the oracle tens of seconds
-SLOW = {"ffn_w2a16_full": 300, "gqa70b_w4a16_t256": 600}
+SLOW = {"ffn_w2a16_full": 300, "gqa70b_w4a16_t256": 600, "mha_w4a4_full_widths_t128": 300}
 
 
 def desc_of(c):
