@@ -23,6 +23,9 @@
  *    OMQ_OK (0) or a negative OMQ_E_* status; on error nothing is launched.
  *  - Row lengths must be multiples of 4 elements (OMQ_E_ALIGN), and of 8 for the
  *    bf16 operands of omq_gemm; pointers must be 16-byte aligned (OMQ_E_ALIGN).
+ *  - Empty outputs: omq_lwc_fakequant with c_out = 0, omq_act_quant with T = 0, and
+ *    omq_gemm / omq_code_gemm with M = 0 or N = 0 return OMQ_OK at once, reading
+ *    and writing nothing (their pointers may then be NULL).
  *  - Bit widths: 2..8, or 16 meaning "this quantizer is off".
  *  - Quantizer arithmetic is IEEE float32, one rounding per operation, no fused
  *    multiply-add, rint = round half to even, gamma = sigmoid(a) computed in

@@ -46,6 +46,7 @@ int omq_lwc_fakequant(const void* W, int w_dt, int64_t c_out, int64_t c_in, int6
                       const float* delta, const float* B, void* W_hat, int what_dt, float* h,
                       float* z, int32_t* arg_max, int32_t* arg_min, float* B_tilde,
                       uint8_t* codes, void* stream) {
+  if (c_out == 0) return OMQ_OK;                   // no rows: nothing read or written
   if (!W || !a_gamma || !a_beta || !W_hat || !h || !z || !arg_max || !arg_min)
     return OMQ_E_INVALID_ARG;
   if (n_bits < 2 || n_bits > 8) return OMQ_E_INVALID_ARG;
@@ -118,6 +119,7 @@ int omq_let_apply(const void* X, int x_dt, int64_t T, int64_t c_in, const float*
 int omq_act_quant(const void* X, int x_dt, int64_t T, int64_t C, int n_bits, int let_mode,
                   const float* s, const float* delta, void* X_hat, int xh_dt, float* h, float* z,
                   int32_t* arg_max, int32_t* arg_min, uint8_t* codes, void* stream) {
+  if (T == 0) return OMQ_OK;                       // no rows: nothing read or written
   if (!X || !X_hat) return OMQ_E_INVALID_ARG;
   if (!bits_ok(n_bits)) return OMQ_E_INVALID_ARG;
   if (n_bits < 16 && (!h || !z || !arg_max || !arg_min)) return OMQ_E_INVALID_ARG;
@@ -138,6 +140,7 @@ int omq_act_quant(const void* X, int x_dt, int64_t T, int64_t C, int n_bits, int
 int omq_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int trans_a,
              const void* B, int64_t ldb, int trans_b, int dt, const float* bias, float alpha,
              float* C, int64_t ldc, int accumulate, void* stream) {
+  if (M == 0 || N == 0) return OMQ_OK;             // empty C: nothing read or written
   if (!A || !B || !C) return OMQ_E_INVALID_ARG;
   if (!dt_ok(dt)) return OMQ_E_DTYPE;
   if (M < 0 || N < 0 || K < 0 || ldc < N) return OMQ_E_SHAPE;
@@ -165,6 +168,7 @@ int omq_code_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* qa, int64_t ld
                   const float* h_a, const float* z_a, const int32_t* sum_a, const uint8_t* qb,
                   int64_t ldb, const float* h_b, const float* z_b, const int32_t* sum_b,
                   const float* bias, float* C, int64_t ldc, void* stream) {
+  if (M == 0 || N == 0) return OMQ_OK;             // empty C: nothing read or written
   if (!qa || !qb || !C || !h_a || !z_a || !sum_a || !h_b || !z_b || !sum_b)
     return OMQ_E_INVALID_ARG;
   if (M < 0 || N < 0 || K < 0 || ldc < N || lda < K || ldb < K || K > (1 << 17))

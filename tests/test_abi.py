@@ -117,3 +117,20 @@ def test_block_theta_layout_matches_oracle(kind):
     assert offs == list(np.cumsum([0] + sizes[:-1]))
     assert n_lwc == sum(n for name, n in lay if name.startswith("a_"))
     assert omq.block_workspace_size(d) > 0
+
+
+def test_empty_outputs_return_ok_without_touching_pointers():
+    """Calls whose outputs have no rows return OMQ_OK before any pointer is read, so
+    they run here, where there is no GPU (NULL pointers: nothing is dereferenced)."""
+    L = omq.lib()
+    assert L.omq_act_quant(None, 1, 0, 8, 4, 0, None, None, None, 1, None, None, None, None,
+                           None, None) == 0
+    assert L.omq_lwc_fakequant(None, 1, 0, 8, 0, 4, None, None, None, None, None, None, 1,
+                               None, None, None, None, None, None, None) == 0
+    assert L.omq_gemm(0, 4, 16, None, 16, 0, None, 16, 0, 1, None, 1.0, None, 4, 0, None) == 0
+    assert L.omq_gemm(4, 0, 16, None, 16, 0, None, 16, 0, 1, None, 1.0, None, 0, 0, None) == 0
+    assert L.omq_code_gemm(0, 4, 16, None, 16, None, None, None, None, 16, None, None, None,
+                           None, None, 4, None) == 0
+    # negative sizes stay errors
+    assert L.omq_act_quant(None, 1, -1, 8, 4, 0, None, None, None, 1, None, None, None, None,
+                           None, None) != 0
