@@ -406,3 +406,38 @@ def test_optimizers():
     expect = np.concatenate([optim.sgd(th[:n_lwc], g[:n_lwc], 5e-3),
                              optim.sgd(th[n_lwc:], g[n_lwc:], 1e-2)])
     assert np.all(np.abs(host(tt) - expect) <= 2 * np.spacing(np.abs(expect)) + 1e-5 * lr * 1e-2)
+
+
+@pytest.mark.parametrize("C,xdt", [(520, "f32"), (4096, "f32"), (6000, "f32"), (4096, "bf16")])
+def test_act_quant_degenerate_rows(C, xdt):
+    """Rows the quantizer treats specially: constant rows (max = min, the step floored
+    at 1e-8), all-zero rows, a single spike, ties for the max and min (first index
+    wins), a row whose range is one float32 ulp; bit-exact against the oracle on every
+    kernel that row width takes."""
+    log("act_quant_degenerate", C, xdt)
+    rng = np.random.default_rng(C)
+    T = 12
+    X = np.zeros((T, C), F32)
+    X[0] = 3.25
+    X[1] = -0.5
+    X[3, C // 3] = 7.0
+    X[4] = rng.standard_normal(C).astype(F32)
+    X[4, [5, C - 7]] = 9.0
+    X[4, [2, C - 3]] = -9.0
+    X[5] = np.float32(1.0)
+    X[5, C // 2] = np.nextafter(F32(1.0), F32(2.0))
+    X[6] = rng.standard_normal(C).astype(F32) * F32(1e-30)
+    X[7:] = rng.standard_normal((T - 7, C)).astype(F32)
+    if xdt == "bf16":
+        X = bf16_np(X).astype(F32)
+    for nbits in (2, 4, 8):
+        st = quant.quantize_rows(X, F32(1), F32(1), nbits)
+        r = omq.act_quant(dev(X, torch.float32 if xdt == "f32" else torch.bfloat16), nbits,
+                          omq.LET_NONE, None, None, out_dtype=torch.float32, want_codes=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(r["h"]), st.h), nbits
+        assert np.array_equal(host(r["z"]), st.z), nbits
+        assert np.array_equal(host(r["arg_max"]), st.iM), nbits
+        assert np.array_equal(host(r["arg_min"]), st.im), nbits
+        assert np.array_equal(host(r["codes"]), st.codes), nbits
+        assert np.array_equal(host(r["X_hat"]), st.xhat), nbits
