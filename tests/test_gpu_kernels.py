@@ -441,3 +441,37 @@ def test_act_quant_degenerate_rows(C, xdt):
         assert np.array_equal(host(r["arg_min"]), st.im), nbits
         assert np.array_equal(host(r["codes"]), st.codes), nbits
         assert np.array_equal(host(r["X_hat"]), st.xhat), nbits
+
+
+@pytest.mark.parametrize("c_in", [520, 4096, 11008])
+def test_lwc_degenerate_rows(c_in):
+    """Weight rows the quantizer treats specially (constant, all-zero, a single spike,
+    tied extremes, a one-ulp range), with gamma = beta (a constant row then has a zero
+    range, the step floored at 1e-8) and with gamma != beta; bit-exact against the
+    oracle on every row kernel that width takes."""
+    log("lwc_degenerate", c_in)
+    rng = np.random.default_rng(c_in + 1)
+    c_out = 8
+    W = np.zeros((c_out, c_in), F32)
+    W[0] = 0.25
+    W[1] = -0.125
+    W[3, c_in // 3] = 0.5
+    W[4] = (rng.standard_normal(c_in) * 0.02).astype(F32)
+    W[4, [5, c_in - 7]] = 0.3
+    W[4, [2, c_in - 3]] = -0.3
+    W[5] = 1.0
+    W[5, c_in // 2] = np.nextafter(F32(1.0), F32(2.0))
+    W[6:] = (rng.standard_normal((c_out - 6, c_in)) * 0.02).astype(F32)
+    W = bf16_np(W).astype(F32)
+    for same in (True, False):
+        ag = np.full(c_out, 4.0, F32)
+        ab = ag.copy() if same else rng.uniform(0.0, 6.0, c_out).astype(F32)
+        for nbits in (2, 4):
+            ref = quant.lwc_fakequant(W, ag, ab, nbits, None, None, None)
+            r = omq.lwc_fakequant(dev(W, torch.bfloat16), dev(ag), dev(ab), nbits,
+                                  out_dtype=torch.float32, want_codes=True)
+            torch.cuda.synchronize()
+            assert np.array_equal(host(r["h"]), ref.h), (same, nbits)
+            assert np.array_equal(host(r["z"]), ref.z), (same, nbits)
+            assert np.array_equal(host(r["codes"]), ref.codes), (same, nbits)
+            assert np.array_equal(host(r["W_hat"]), ref.W_hat), (same, nbits)
