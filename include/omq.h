@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define OMQ_ABI_VERSION 3
+#define OMQ_ABI_VERSION 4
 
 /* status codes */
 #define OMQ_OK 0
@@ -169,6 +169,44 @@ int omq_code_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* qa, int64_t ld
                   const float* h_a, const float* z_a, const int32_t* sum_a, const uint8_t* qb,
                   int64_t ldb, const float* h_b, const float* z_b, const int32_t* sum_b,
                   const float* bias, float* C, int64_t ldc, void* stream);
+
+/*
+ * omq_attention_fwd -- the block's causal attention on its quantized operands
+ * (paper reading, section "LET": the affinity of Q~ = Q / s_a and K~ = s_a K, and
+ * the softmax output kept in full precision).  Per query head h, with KV head
+ * g = h / (n_q / n_kv) (grouped-query attention):
+ *   S = Q_h K_g^T / sqrt(head_dim) with the causal mask (key position <= query),
+ *   P = softmax(S) in float32, O_h = P V_g with P rounded to bf16 as the matrix-core
+ *   operand (the probabilities themselves are never quantized).
+ * Q: bf16 [T x n_q*128], row stride ldq; K, V: bf16 [T x n_kv*128], row stride ldk
+ * (e.g. the X_hat outputs of omq_act_quant for Q~, K~, V).  O: float [T x n_q*128],
+ * row stride ldo.  lse2: float [n_q x T], the base-2 log-sum-exp of each query's
+ * scaled scores, which omq_attention_bwd takes.  head_dim must be 128 (OMQ_E_SHAPE);
+ * ldq, ldk multiples of 8 and ldo of 4, pointers 16-byte aligned (OMQ_E_ALIGN);
+ * n_q a multiple of n_kv; T up to 2^30; T = 0 returns OMQ_OK at once.
+ */
+int omq_attention_fwd(const void* Q, int64_t ldq, const void* K, const void* V, int64_t ldk,
+                      int64_t T, int64_t n_q, int64_t n_kv, int64_t head_dim, float* O,
+                      int64_t ldo, float* lse2, void* stream);
+
+/*
+ * omq_attention_bwd -- backward of omq_attention_fwd given dO = dL/dO:
+ *   dV_g = sum over the group's heads of P^T dO_h;  dP = dO_h V_g^T;
+ *   dS = P (dP - rowsum(dO_h O_h)) / sqrt(head_dim);  dQ_h = dS K_g;
+ *   dK_g = sum over the group's heads of dS^T Q_h
+ * with the scores recomputed from lse2 (no score matrix is stored); dO, P and dS
+ * enter the matrix cores in bf16, every sum is float32.
+ * O, dO: float [T x n_q*128], row stride ldo; lse2 as the forward wrote it.
+ * dQ: float [T x n_q*128], row stride lddq; dK, dV: float [T x n_kv*128], row
+ * stride lddk (multiples of 4); all overwritten.  ws: device workspace of at least
+ * omq_attention_bwd_workspace_size(T, n_q, ldq) bytes (dO in bf16, rowsum(dO O)).
+ */
+size_t omq_attention_bwd_workspace_size(int64_t T, int64_t n_q, int64_t ldq);
+int omq_attention_bwd(const void* Q, int64_t ldq, const void* K, const void* V, int64_t ldk,
+                      int64_t T, int64_t n_q, int64_t n_kv, int64_t head_dim, const float* O,
+                      const float* dO, int64_t ldo, const float* lse2, float* dQ, int64_t lddq,
+                      float* dK, float* dV, int64_t lddk, void* ws, size_t ws_bytes,
+                      void* stream);
 
 /*
  * omq_code_rowsum -- sums[r] = sum over c < cols of codes[r * ld + c] (int32), the
@@ -361,6 +399,13 @@ typedef struct omq_timer {
  * abits < 16.  Q~, K~, V and every linear input are quantized per token at abits;
  * softmax is never quantized.  ffn_only: y = down(SiLU(gate(x~)) * up(x~)) with the
  * ffn LET site, no norm and no residual.
+ * With both quantizers on, the forward's four quantized products are formed exactly
+ * on the integer codes (h_x h_w sum (q_x - z_x)(q_w - z_w), rounded once to float).
+ * Limits (checked by every block entry point; omq_block_workspace_size returns 0):
+ * head_dim must be 128 and n_q a multiple of n_kv (OMQ_E_SHAPE); T, d, F multiples
+ * of 8 (OMQ_E_ALIGN); group 128 needs d and F multiples of 128 (OMQ_E_SHAPE); group
+ * 128 with abits < 16 and wbits < 16 (group-wise clipping with quantized
+ * activations) is not implemented (OMQ_E_UNIMPLEMENTED).
  */
 typedef struct omq_block_desc {
   size_t struct_size; /* sizeof(omq_block_desc) */

@@ -22,10 +22,9 @@ Readings of what the pages leave open:
   one on the o_proj input; with grouped-query attention s_o, delta_o and s_a live
   on the KV channels and are broadcast over the query heads of each group;
 * the block's quantized input is the same x as the full-precision target;
-* operand precision of the bf16 path (ops.ExactOps): every product takes bf16
-  operands, except the forward's four quantized products with per-row quantizers
-  on both sides below 8 bits (and input widths a multiple of 16), which the GPU
-  forms exactly on the integer codes.
+* operand precision of the bf16 path (ops.ExactOps): the forward product of
+  every layer with both quantizers on takes the exact dequantized operands (the
+  method's Y = Q_a(X~) Q_w(W~) + B~); every other product takes bf16 operands.
 
 Parity: pinned by tests/test_oracle_block.py (full-precision block vs torch's
 rms_norm / scaled_dot_product_attention / silu; RoPE invariants; LET identity of
@@ -51,10 +50,20 @@ LINEARS = ("q", "k", "v", "o", "gate", "up", "down")
 # smooth pieces (float64)
 # ---------------------------------------------------------------------------
 
-def rmsnorm(x, eps):
+def rmsnorm(x, eps, code=True):
+    """RMSNorm with unit gain, y = x / sqrt(mean(x^2) + eps), and the scale r.
+
+    code: the output enters a quantizer, so its rounding is fixed like the
+    quantizer's (reading R29): r is formed in float64 (eps as the float32 the GPU
+    takes) and rounded once to float32, the normalized row is x r rounded once to
+    float32 per element.  code=False: everything in float64 (the full-precision
+    target, which feeds no quantizer)."""
     x = np.asarray(x, F64)
-    r = 1.0 / np.sqrt(np.mean(x * x, axis=1) + eps)
-    return x * r[:, None], r
+    if not code:
+        r = 1.0 / np.sqrt(np.mean(x * x, axis=1) + eps)
+        return x * r[:, None], r
+    r = (1.0 / np.sqrt(np.mean(x * x, axis=1) + float(F32(eps)))).astype(F32).astype(F64)
+    return (x * r[:, None]).astype(F32).astype(F64), r
 
 
 def rmsnorm_bwd(dy, x, r):
@@ -121,7 +130,11 @@ def attention(Q, K, V, n_q, n_kv, hd, cast=None):
     return O, P
 
 
-def attention_bwd(dO, Q, K, V, P, n_q, n_kv, hd):
+def attention_bwd(dO, Q, K, V, P, n_q, n_kv, hd, cast=None):
+    """Backward of attention(); cast: how dO and dS enter their matrix products (the
+    bf16 path feeds them to the matrix cores in bf16).  The softmax term
+    rowsum(dP P) is formed from the uncast dO as rowsum(dO O)."""
+    cast = (lambda a: a) if cast is None else cast
     T = Q.shape[0]
     grp = n_q // n_kv
     c = 1.0 / np.sqrt(hd)
@@ -133,12 +146,16 @@ def attention_bwd(dO, Q, K, V, P, n_q, n_kv, hd):
         sl_q = slice(h * hd, (h + 1) * hd)
         sl_k = slice(g * hd, (g + 1) * hd)
         do = dO[:, sl_q]
+        doc = cast(do)
         Ph, Pop = P[h]
-        dV[:, sl_k] += Pop.T @ do
-        dP = do @ V[:, sl_k].T
-        dS = Ph * (dP - np.sum(dP * Ph, axis=1, keepdims=True))
-        dQ[:, sl_q] = c * (dS @ K[:, sl_k])
-        dK[:, sl_k] += c * (dS.T @ Q[:, sl_q])
+        dV[:, sl_k] += Pop.T @ doc
+        dP = doc @ V[:, sl_k].T
+        # rowsum(dP P) written as rowsum(dO O) with O = P V, the product the forward
+        # formed (its P operand the cast one)
+        Dr = np.sum((do @ V[:, sl_k].T) * Pop, axis=1, keepdims=True)
+        dS = cast(c * (Ph * (dP - Dr)))
+        dQ[:, sl_q] = dS @ K[:, sl_k]
+        dK[:, sl_k] += dS.T @ Q[:, sl_q]
     return dQ, dK, dV
 
 
@@ -230,7 +247,7 @@ def unpack(c, shapes, flat):
 def _qlin(ops, S, name, Xop, W, th, c, s=None, delta=None, Xfw=None):
     """One quantized linear on an already-quantized operand Xop (the backward's
     operand); Xfw, when given, is the exact quantized input the forward product
-    takes instead, with the exact quantized weight (the product on integer codes)."""
+    takes instead, with the exact quantized weight."""
     gamma = ops.sigmoid(th["a_gamma_" + name])
     beta = ops.sigmoid(th["a_beta_" + name])
     Wt = ops.let_weight(W, s) if s is not None else ops.to_code(W)
@@ -258,9 +275,9 @@ def forward(c, x, Wd, th, ops=None):
         ops = ExactOps(bf16=True)
     S = SimpleNamespace(c=c, ops=ops, th=th)
     S.lin = {}
-    # the forward's quantized products on integer codes (exact operands)
-    cp = getattr(ops, "code_product", None)
-    exact = cp is not None and cp(c)
+    # weight-activation quantized products on their exact operands (method level)
+    ep = getattr(ops, "exact_product", None)
+    exact = ep is not None and ep(c.wbits, c.abits)
 
     def fw(Xh):
         return Xh if exact else None
@@ -268,7 +285,8 @@ def forward(c, x, Wd, th, ops=None):
     hd, n_q, n_kv = c.head_dim, c.n_q, c.n_kv
     sv = {}
     if not c.ffn_only:
-        xn, r1 = rmsnorm(x64, c.eps)
+        rr = getattr(ops, "rms_rounding", False)
+        xn, r1 = rmsnorm(x64, c.eps, code=rr)
         s_qkv, d_qkv = th["s_qkv"], th["delta_qkv"]
         Xt_qkv = ops.let_act(xn, s_qkv, d_qkv)
         a_qkv, Xh = ops.act(Xt_qkv, c.abits, "a_qkv")
@@ -291,14 +309,14 @@ def forward(c, x, Wd, th, ops=None):
         aK, Kh = ops.act(Kt, c.abits, "a_k")
         aV, Vh = ops.act(Yv, c.abits, "a_v")
         Qo, Ko, Vo = ops.operand(Qh), ops.operand(Kh), ops.operand(Vh)
-        O, P = attention(Qo, Ko, Vo, n_q, n_kv, hd, cast=ops.operand)
+        O, P = attention(Qo, Ko, Vo, n_q, n_kv, hd, cast=getattr(ops, "prob", ops.operand))
         s_o = kv_broadcast(th["s_o"], n_q, n_kv, hd)
         d_o = kv_broadcast(th["delta_o"], n_q, n_kv, hd)
         Xt_o = ops.let_act(O, s_o, d_o)
         a_o, Xh_o = ops.act(Xt_o, c.abits, "a_o")
         Xop_o = ops.operand(Xh_o)
         h1 = x64 + _qlin(ops, sv, "o", Xop_o, Wd["W_o"], th, c, s_o, d_o, fw(Xh_o))
-        xn2, r2 = rmsnorm(h1, c.eps)
+        xn2, r2 = rmsnorm(h1, c.eps, code=rr)
         S.__dict__.update(xn=xn, r1=r1, Xt_qkv=Xt_qkv, a_qkv=a_qkv, Xop_qkv=Xop_qkv,
                           cos=cos, sin=sin, Qr=Qr, Kr=Kr, Qt=Qt, Kt=Kt, Yv=Yv, sa_q=sa_q,
                           sa_k=sa_k, aQ=aQ, aK=aK, aV=aV, Qo=Qo, Ko=Ko, Vo=Vo, O=O, P=P,
@@ -332,14 +350,14 @@ def reference(c, x, Wd):
         xn2 = x64
         h1 = None
     else:
-        xn, _ = rmsnorm(x64, c.eps)
+        xn, _ = rmsnorm(x64, c.eps, code=False)
         cos, sin = rope_tables(c.T, hd, c.rope_theta)
         Q = rope(xn @ W["W_q"].T, n_q, hd, cos, sin)
         K = rope(xn @ W["W_k"].T, n_kv, hd, cos, sin)
         V = xn @ W["W_v"].T
         O, _ = attention(Q, K, V, n_q, n_kv, hd)
         h1 = x64 + O @ W["W_o"].T
-        xn2, _ = rmsnorm(h1, c.eps)
+        xn2, _ = rmsnorm(h1, c.eps, code=False)
     A = silu(xn2 @ W["W_gate"].T) * (xn2 @ W["W_up"].T)
     D = A @ W["W_down"].T
     return D if c.ffn_only else h1 + D
@@ -358,8 +376,9 @@ def _qlin_bwd(S, name, gY, Xop, g, gs=None):
     """Backward of one quantized linear: returns dL/dXop; fills the LWC logit
     grads and accumulates the weight-side s grad into gs."""
     L = S.lin[name]
-    gXop = gY @ L.Wop
-    gWop = gY.T @ Xop
+    gYo = S.ops.grad_operand(gY) if hasattr(S.ops, "grad_operand") else gY
+    gXop = gYo @ L.Wop
+    gWop = gYo.T @ Xop
     if L.wst is None:
         rows = lwc_rows(S.c, gWop.shape)
         gWt, g_gamma, g_beta = gWop, np.zeros(rows), np.zeros(rows)
@@ -417,7 +436,8 @@ def backward(S, dy):
     g["s_o"] = kv_reduce(gs_o + gs_o2, n_q, n_kv, hd)
     g["delta_o"] = kv_reduce(gd_o, n_q, n_kv, hd)
     # attention
-    gQo, gKo, gVo = attention_bwd(gO, S.Qo, S.Ko, S.Vo, S.P, n_q, n_kv, hd)
+    gQo, gKo, gVo = attention_bwd(gO, S.Qo, S.Ko, S.Vo, S.P, n_q, n_kv, hd,
+                                  cast=getattr(S.ops, "grad_operand", None))
     gQt = quant.act_quant_bwd(gQo, S.aQ)
     gKt = quant.act_quant_bwd(gKo, S.aK)
     gYv = quant.act_quant_bwd(gVo, S.aV)

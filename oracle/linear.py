@@ -8,6 +8,9 @@ linear-layer equation with the quantizers applied to X~ and W~) and section
 "LWC" (the weight quantizer).  Weights are stored [C_out x C_in] (Y = X W^T + B),
 so the page's s * W scales W's columns.
 
+Operand precision: as ops.ExactOps states (the forward product of a layer with
+both quantizers on is exact; other products take the bf16 path's operand casts).
+
 Parity: pinned by tests/test_oracle_linear.py (LET identity with quantizers off,
 finite differences of the frozen-decision surrogate, SGD trajectory invariants).
 """
@@ -43,17 +46,24 @@ def forward(X, W, B, theta, wbits, abits, let, ops, group=0):
     ast, Xh = ops.act(Xt, abits, "a")
     Xop = ops.operand(Xh)
     Wop = ops.operand(np.reshape(wst.xhat, np.shape(Wt)) if wst is not None else Wt)
-    Y = Xop @ Wop.T + Bt[None, :]
+    ep = getattr(ops, "exact_product", None)
+    if ep is not None and ep(wbits, abits):
+        # both sides quantized: the product of the exact dequantized operands
+        Y = np.asarray(Xh, F64) @ np.reshape(wst.xhat, np.shape(Wt)).astype(F64).T
+    else:
+        Y = Xop @ Wop.T
+    Y = Y + Bt[None, :]
     return Y, SimpleNamespace(X=X, W=W, Wt=Wt, Xt=Xt, wst=wst, ast=ast, Xop=Xop, Wop=Wop,
-                              gamma=gamma, beta=beta, theta=theta, let=let)
+                              gamma=gamma, beta=beta, theta=theta, let=let, ops=ops)
 
 
 def backward(dY, sv):
     """Gradients of the loss w.r.t. X and theta, given dL/dY."""
     dY = np.asarray(dY, dtype=F64)
     g = {}
-    gXop = dY @ sv.Wop
-    gWop = dY.T @ sv.Xop
+    dYo = sv.ops.grad_operand(dY) if hasattr(sv.ops, "grad_operand") else dY
+    gXop = dYo @ sv.Wop
+    gWop = dYo.T @ sv.Xop
     if sv.wst is None:
         n = np.asarray(sv.theta["a_gamma"]).size
         gWt, g_gamma, g_beta = gWop, np.zeros(n), np.zeros(n)

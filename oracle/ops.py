@@ -8,6 +8,13 @@ proper: the quantizer code path in exact float32 and, for the bf16 path, bf16
 GEMM operands.  The tests plug in a float64 surrogate with frozen rounding /
 clamping / argmax decisions to pin the hand-written backward by finite
 differences.
+
+Operand precision (``ExactOps(bf16=True)``, the bf16 path of reading R17): the
+forward product of a layer whose weights and activations are both quantized is
+the exact product of the dequantized values (``exact_product``); every other
+matrix product -- a weight-only layer's forward, every backward product, and
+the attention products -- takes its operands rounded to bf16 as the matrix
+cores take them, with float64 accumulation.
 """
 from __future__ import annotations
 
@@ -20,6 +27,9 @@ F64 = np.float64
 
 
 class ExactOps:
+    # the RMSNorm rows entering a quantizer take the code path's rounding (R29)
+    rms_rounding = True
+
     def __init__(self, bf16: bool):
         self.bf16 = bf16
         self.states = {}
@@ -63,13 +73,27 @@ class ExactOps:
             return quant.bf16(a)
         return np.asarray(a, dtype=F64)
 
-    def code_product(self, c):
-        """Whether the bf16 path forms the block forward's four quantized products
-        (quantized activations times LWC weights) on the integer codes: exactly
-        (q_x - z_x) h_x times (q_w - z_w) h_w, no operand rounding.  It does so for
-        per-row quantizers with codes below 128 on both sides and every input width
-        a multiple of 16; otherwise the operands enter as bf16 like any other.  The
-        backward's products take the bf16 operands either way."""
-        widths = [c.d, c.F] + ([] if c.ffn_only else [c.n_q * c.head_dim])
-        return (self.bf16 and c.wbits <= 7 and c.abits <= 7 and not c.group
-                and all(w % 16 == 0 for w in widths))
+    def grad_operand(self, g):
+        """An upstream gradient as a backward product takes it (dL/dY of a linear
+        layer, dL/dO and dL/dS of the attention): in bf16 on the bf16 path, like
+        every other matrix-core operand (reading R17)."""
+        return self.operand(g)
+
+    def prob(self, P):
+        """The softmax output as the P V product takes it: the bf16 path feeds the
+        normalized probabilities to the matrix cores rounded to bf16 (reading R20);
+        the softmax itself is never quantized."""
+        return self.operand(P)
+
+    def exact_product(self, wbits, abits):
+        """Whether a linear layer's forward product takes the exact quantized operands.
+
+        The method's quantized layer computes Y = Q_a(X~) Q_w(W~) + B~ (paper reading,
+        section "LET"), each quantized operand being (q - z) h per quantizer row
+        (section "LWC").  When both quantizers are on, that product is formed from
+        the exact dequantized values (float32, products and sums in float64): the
+        definition written out, whatever the widths, bit widths or LWC grouping.
+        When one side is unquantized its operand is a plain float tensor, which the
+        bf16 path feeds to the matrix cores in bf16 (reading R17), so the product
+        takes the operand() casts.  The backward's products always take operand()."""
+        return wbits < 16 and abits < 16

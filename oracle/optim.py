@@ -8,9 +8,11 @@ the LET parameters, batch size 1.  Adam's beta1 = 0.9, beta2 = 0.999 and
 eps = 1e-8 are not on the pages (standard defaults, a reading of a point the
 pages leave open).  The single-layer fp32 workload uses plain SGD (lr 5e-3).
 
-Parity: pinned by tests/test_oracle_linear.py (first Adam step is lr * sign(g)
-for |g| >> eps; SGD is theta - lr g; bias correction makes the k-th step of a
-constant gradient equal to the first).
+Parity: the update rule is pinned by tests/test_oracle_linear.py (first Adam step
+is lr * sign(g) for |g| >> eps; Adam's closed form on a +g, -g gradient sequence;
+decoupled weight decay; SGD is theta - lr g).  The constants BETA1, BETA2 and EPS
+are parity unpinned: the pages give no values, and a different choice would pass
+every pin above that does not name them.
 """
 from __future__ import annotations
 

@@ -20,6 +20,7 @@ __all__ = [
     "block_theta_layout", "block_workspace_size", "block_forward", "block_step",
     "F32", "BF16", "LET_NONE", "LET_DIV", "LET_MUL", "PATH_FP32", "PATH_BF16",
     "OPT_ADAMW", "OPT_SGD", "GemmTimer", "pack_codes", "fold_linear", "w4a16_gemm",
+    "attention_fwd", "attention_bwd",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -146,6 +147,11 @@ _SIGS = {
     "omq_code_gemm": (_int, [_i64, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp,
                              _vp, _vp, _vp, _i64, _vp]),
     "omq_code_rowsum": (_int, [_vp, _i64, _i64, _i64, _vp, _vp]),
+    "omq_attention_fwd": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64,
+                                 _vp, _vp]),
+    "omq_attention_bwd_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "omq_attention_bwd": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp, _vp,
+                                 _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _sz, _vp]),
     "omq_lwc_backward_workspace_size": (_sz, [_i64, _i64]),
     "omq_lwc_backward": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -322,6 +328,33 @@ def code_gemm(qa, h_a, z_a, qb, h_b, z_b, sum_a=None, sum_b=None, bias=None, C=N
         M, N, K, _p(qa), K, _p(h_a), _p(z_a), _p(sum_a), _p(qb), K, _p(h_b), _p(z_b), _p(sum_b),
         _p(bias), _p(C), N, _stream()))
     return C
+
+
+def attention_fwd(Q, K, V, n_q, n_kv, head_dim=128):
+    """Causal attention of bf16 Q [T x n_q*hd], K, V [T x n_kv*hd]: returns O (float32
+    [T x n_q*hd]) and the base-2 log-sum-exp per (head, query) [n_q x T]."""
+    T = Q.shape[0]
+    O = torch.empty(T, n_q * head_dim, dtype=torch.float32, device=Q.device)
+    lse2 = torch.empty(n_q, T, dtype=torch.float32, device=Q.device)
+    _check("omq_attention_fwd", lib().omq_attention_fwd(
+        _p(Q), Q.shape[1], _p(K), _p(V), K.shape[1], T, n_q, n_kv, head_dim, _p(O), O.shape[1],
+        _p(lse2), _stream()))
+    return O, lse2
+
+
+def attention_bwd(Q, K, V, O, lse2, dO, n_q, n_kv, head_dim=128):
+    """Backward of attention_fwd given dO (float32 like O): (dQ, dK, dV) float32."""
+    T = Q.shape[0]
+    dQ = torch.empty(T, n_q * head_dim, dtype=torch.float32, device=Q.device)
+    dK = torch.empty(T, n_kv * head_dim, dtype=torch.float32, device=Q.device)
+    dV = torch.empty_like(dK)
+    nbytes = lib().omq_attention_bwd_workspace_size(T, n_q, Q.shape[1])
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=Q.device)
+    _check("omq_attention_bwd", lib().omq_attention_bwd(
+        _p(Q), Q.shape[1], _p(K), _p(V), K.shape[1], T, n_q, n_kv, head_dim, _p(O), _p(dO),
+        O.shape[1], _p(lse2), _p(dQ), dQ.shape[1], _p(dK), _p(dV), dK.shape[1], _p(ws), nbytes,
+        _stream()))
+    return dQ, dK, dV
 
 
 def lwc_backward(gW_hat, W, n_bits, a_gamma, a_beta, h, z, arg_max, arg_min, s=None,

@@ -2,6 +2,8 @@
 // layout, and the composition of kernels into the layer-level operations.
 #include "api_util.h"
 
+#include <math.h>
+
 using namespace omq;
 
 extern "C" {
@@ -184,6 +186,80 @@ int omq_code_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* qa, int64_t ld
   return OMQ_OK;
 }
 
+// ---------------------------------------------------------------------------
+// causal attention of the block on its quantized operands
+// ---------------------------------------------------------------------------
+
+namespace {
+int attn_check(const void* Q, int64_t ldq, const void* K, const void* V, int64_t ldk, int64_t T,
+               int64_t n_q, int64_t n_kv, int64_t head_dim, const void* O, int64_t ldo) {
+  if (!Q || !K || !V || !O) return OMQ_E_INVALID_ARG;
+  if (T < 0 || T > ((int64_t)1 << 30) || n_q <= 0 || n_kv <= 0 || n_q % n_kv) return OMQ_E_SHAPE;
+  if (head_dim != 128) return OMQ_E_SHAPE;
+  if (ldq < n_q * 128 || ldk < n_kv * 128 || ldo < n_q * 128) return OMQ_E_SHAPE;
+  if (ldq % 8 || ldk % 8 || ldo % 4 || !al16(Q) || !al16(K) || !al16(V) || !al16(O))
+    return OMQ_E_ALIGN;
+  return OMQ_OK;
+}
+}  // namespace
+
+int omq_attention_fwd(const void* Q, int64_t ldq, const void* K, const void* V, int64_t ldk,
+                      int64_t T, int64_t n_q, int64_t n_kv, int64_t head_dim, float* O,
+                      int64_t ldo, float* lse2, void* stream) {
+  int rc = attn_check(Q, ldq, K, V, ldk, T, n_q, n_kv, head_dim, O, ldo);
+  if (rc) return rc;
+  if (!lse2) return OMQ_E_INVALID_ARG;
+  if (T == 0) return OMQ_OK;
+  FlashFwd f;
+  f.Q = reinterpret_cast<const uint16_t*>(Q);
+  f.K = reinterpret_cast<const uint16_t*>(K);
+  f.V = reinterpret_cast<const uint16_t*>(V);
+  f.ldq = ldq; f.ldk = ldk; f.T = T; f.n_q = (int)n_q; f.grp = (int)(n_q / n_kv);
+  f.scale2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
+  f.O = O; f.ldo = ldo; f.lse2 = lse2;
+  OMQ_HIP_CHECK(launch_flash_fwd(f, S(stream)));
+  return OMQ_OK;
+}
+
+size_t omq_attention_bwd_workspace_size(int64_t T, int64_t n_q, int64_t ldq) {
+  if (T < 0 || n_q < 0 || ldq < 0) return 0;
+  Bump b(nullptr);
+  b.take<float>(n_q * T);       // D = rowsum(dO * O) per (head, query)
+  b.take<uint16_t>(T * ldq);    // dO in bf16, rows like Q's
+  return b.off;
+}
+
+int omq_attention_bwd(const void* Q, int64_t ldq, const void* K, const void* V, int64_t ldk,
+                      int64_t T, int64_t n_q, int64_t n_kv, int64_t head_dim, const float* O,
+                      const float* dO, int64_t ldo, const float* lse2, float* dQ, int64_t lddq,
+                      float* dK, float* dV, int64_t lddk, void* ws, size_t ws_bytes,
+                      void* stream) {
+  int rc = attn_check(Q, ldq, K, V, ldk, T, n_q, n_kv, head_dim, O, ldo);
+  if (rc) return rc;
+  if (!dO || !lse2 || !dQ || !dK || !dV) return OMQ_E_INVALID_ARG;
+  if (lddq < n_q * 128 || lddk < n_kv * 128) return OMQ_E_SHAPE;
+  if (lddq % 4 || lddk % 4 || !al16(dO) || !al16(dQ) || !al16(dK) || !al16(dV))
+    return OMQ_E_ALIGN;
+  if (T == 0) return OMQ_OK;
+  if (!ws || ws_bytes < omq_attention_bwd_workspace_size(T, n_q, ldq)) return OMQ_E_WORKSPACE;
+  Bump b(ws);
+  float* D = b.take<float>(n_q * T);
+  uint16_t* dOb = b.take<uint16_t>(T * ldq);
+  const hipStream_t st = S(stream);
+  OMQ_HIP_CHECK(launch_attn_bwd_prep(dO, O, ldo, T, (int)n_q, D, dOb, ldq, st));
+  FlashBwd f;
+  f.Q = reinterpret_cast<const uint16_t*>(Q);
+  f.K = reinterpret_cast<const uint16_t*>(K);
+  f.V = reinterpret_cast<const uint16_t*>(V);
+  f.dO = dOb; f.ldq = ldq; f.ldk = ldk; f.T = T; f.n_q = (int)n_q; f.grp = (int)(n_q / n_kv);
+  f.scale = (float)(1.0 / sqrt((double)head_dim));
+  f.scale2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
+  f.lse2 = lse2; f.D = D;
+  f.dQ = dQ; f.lddq = lddq; f.dK = dK; f.dV = dV; f.lddk = lddk;
+  OMQ_HIP_CHECK(launch_flash_bwd(f, st));
+  return OMQ_OK;
+}
+
 size_t omq_lwc_backward_workspace_size(int64_t c_out, int64_t c_in) {
   return rowquant_bwd_ws_bytes(c_out, c_in);
 }
@@ -264,11 +340,21 @@ namespace {
 struct QLinWs {
   void* What; float *wh, *wz; int32_t *wamax, *wamin; float* Bt;
   void* Xhat; float *ah, *az; int32_t *aamax, *aamin;
+  // the forward product on integer codes (bf16 path, both sides quantized per row):
+  // code rows padded with zero codes to cip columns, and the rows' code sums
+  uint8_t *Wq, *Xq; int32_t *wqs, *aqs; int64_t cip;
   float *gW, *gXh, *colsum;
   uint16_t* dYb;
   float *rq, *cs;
   size_t total;
 };
+
+// whether the forward product runs exactly on the integer codes: the bf16 path with
+// both quantizers on, per output channel (8-bit codes stored shifted by 128)
+bool qlin_codes(const omq_qlinear_desc* d) {
+  return d->path == OMQ_PATH_BF16 && d->wbits <= 8 && d->abits <= 8 &&
+         lwc_group(d->group, d->c_in) == 0;
+}
 
 QLinWs qlin_layout(const omq_qlinear_desc* d, void* base) {
   Bump b(base);
@@ -288,6 +374,12 @@ QLinWs qlin_layout(const omq_qlinear_desc* d, void* base) {
   w.gXh = b.take<float>(T * ci);
   w.colsum = b.take<float>(co);
   w.dYb = bf ? b.take<uint16_t>(T * co) : nullptr;
+  w.cip = (ci + 15) / 16 * 16;
+  w.Wq = w.Xq = nullptr; w.wqs = w.aqs = nullptr;
+  if (qlin_codes(d)) {
+    w.Wq = b.take<uint8_t>(co * w.cip); w.Xq = b.take<uint8_t>(T * w.cip);
+    w.wqs = b.take<int32_t>(co); w.aqs = b.take<int32_t>(T);
+  }
   int64_t n1, t1, n2, t2;
   gemm_ste_extents(co, ci, &n1, &t1);
   gemm_ste_extents(T, ci, &n2, &t2);
@@ -344,6 +436,15 @@ int omq_qlinear_fwd(const omq_qlinear_desc* d, const void* X, const void* W, con
   if (grp && d->wbits < 16) {     // grouped rows: the bias fold runs on its own
     a.group = grp; a.fold_delta = nullptr; a.bias_out = nullptr;
   }
+  const bool cq = qlin_codes(d);
+  const int woff = d->wbits == 8 ? 128 : 0, aoff = d->abits == 8 ? 128 : 0;
+  if (cq) {
+    if (w.cip != ci) {           // padded code rows: zero codes past the row end
+      OMQ_HIP_CHECK(launch_fill_f32(reinterpret_cast<float*>(w.Wq), co * w.cip / 4, 0.f, st));
+      OMQ_HIP_CHECK(launch_fill_f32(reinterpret_cast<float*>(w.Xq), T * w.cip / 4, 0.f, st));
+    }
+    a.codes = w.Wq; a.ldq = w.cip; a.code_off = woff; a.qsum = w.wqs;
+  }
   OMQ_HIP_CHECK(launch_rowquant_fwd(a, st));
   if (dl && (d->wbits >= 16 || grp))
     OMQ_HIP_CHECK(launch_bias_fold(W, dt, co, ci, dl, B, w.Bt, st));
@@ -354,10 +455,19 @@ int omq_qlinear_fwd(const omq_qlinear_desc* d, const void* X, const void* W, con
   x.let_mode = s ? OMQ_LET_DIV : OMQ_LET_NONE; x.s = s; x.delta = dl;
   x.nbits = d->abits; x.out = w.Xhat; x.out_dt = dt; x.ldo = ci;
   x.h = w.ah; x.z = w.az; x.amax = w.aamax; x.amin = w.aamin;
+  if (cq) { x.codes = w.Xq; x.ldq = w.cip; x.code_off = aoff; x.qsum = w.aqs; }
   OMQ_HIP_CHECK(launch_rowquant_fwd(x, st));
   Gemm g;
-  g.A = w.Xhat; g.lda = ci; g.B = w.What; g.ldb = ci; g.C = Y; g.ldc = co; g.bias = bias;
-  g.M = T; g.N = co; g.K = ci; g.dt = dt;
+  if (cq) {
+    // Q_a(X~) Q_w(W~)^T exactly: h_x h_w sum (q_x - z_x)(q_w - z_w), rounded once
+    g.codes = 1;
+    g.A = w.Xq; g.lda = w.cip; g.B = w.Wq; g.ldb = w.cip; g.K = w.cip; g.kz = ci;
+    g.ha = w.ah; g.za = w.az; g.sa = w.aqs; g.hb = w.wh; g.zb = w.wz; g.sb = w.wqs;
+    g.zoa = (float)aoff; g.zob = (float)woff;
+  } else {
+    g.A = w.Xhat; g.lda = ci; g.B = w.What; g.ldb = ci; g.K = ci; g.dt = dt;
+  }
+  g.C = Y; g.ldc = co; g.bias = bias; g.M = T; g.N = co;
   OMQ_HIP_CHECK(launch_gemm(g, st));
   return OMQ_OK;
 }
@@ -410,8 +520,8 @@ int omq_qlinear_bwd(const omq_qlinear_desc* d, const void* X, const void* W, con
       a.h = w.wh; a.z = w.wz; a.amax = w.wamax; a.amin = w.wamin;
       a.a_gamma = theta; a.a_beta = theta + rq; a.g_agamma = g_ag; a.g_abeta = g_ab;
       a.col_mode = se.col_mode; a.out0 = g_s; a.out1 = g_d; a.group = grp;
-      OMQ_HIP_CHECK(launch_ste_colfinal(a, (int)ntl, colpart, st));
-      OMQ_HIP_CHECK(launch_ste_rowfinal(a, grp ? 1 : (int)nsl, rowpart, st));
+      OMQ_HIP_CHECK(launch_ste_finish(a, (int)ntl, colpart, a, grp ? 1 : (int)nsl, rowpart,
+                                      w.rq + ste_records_offset(co, ci, nsl, ntl), st));
     }
     if (dX || s) {
       gemm_ste_extents(T, ci, &nsl, &ntl);
@@ -432,8 +542,8 @@ int omq_qlinear_bwd(const omq_qlinear_desc* d, const void* X, const void* W, con
       x.h = w.ah; x.z = w.az; x.amax = w.aamax; x.amin = w.aamin;
       x.col_mode = se.col_mode; x.gx = g.C; x.ldgx = ci; x.out0 = g_s; x.out1 = g_d;
       x.accumulate = 1;
-      OMQ_HIP_CHECK(launch_ste_colfinal(x, (int)ntl, colpart, st));
-      OMQ_HIP_CHECK(launch_ste_rowfinal(x, (int)nsl, rowpart, st));
+      OMQ_HIP_CHECK(launch_ste_finish(x, (int)ntl, colpart, x, (int)nsl, rowpart,
+                                      w.rq + ste_records_offset(T, ci, nsl, ntl), st));
     }
     return OMQ_OK;
   }

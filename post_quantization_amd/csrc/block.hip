@@ -23,8 +23,11 @@ struct Dims {
   int grp;
   bool ffn_only, use_sa;
   // the forward's four products on integer codes (int8 matrix cores): weights and
-  // activations quantized per row with codes below 128, every C_in a multiple of 16
+  // activations both quantized, per row (8-bit codes stored shifted by 128 into
+  // signed bytes); code rows padded with zero codes to a multiple of 16 columns
   bool codes;
+  int64_t dp, dqp, Fp;     // padded code-row lengths of the d-, dq- and F-wide inputs
+  int woff, aoff;          // stored code offsets (128 for 8-bit codes)
   // LWC quantizer rows per output channel of a weight with C_in = cin
   int64_t g_of(int64_t cin) const { return group ? cin / group : 1; }
 };
@@ -37,8 +40,11 @@ Dims dims_of(const omq_block_desc* b) {
   m.ffn_only = b->ffn_only != 0;
   m.use_sa = !m.ffn_only && b->abits < 16;
   m.group = b->group;
-  m.codes = b->wbits <= 7 && b->abits <= 7 && m.group == 0 && m.d % 16 == 0 && m.F % 16 == 0 &&
-            (m.ffn_only || m.dq % 16 == 0);
+  m.codes = b->wbits <= 8 && b->abits <= 8 && m.group == 0;
+  auto up16 = [](int64_t v) { return (v + 15) / 16 * 16; };
+  m.dp = up16(m.d); m.dqp = up16(m.dq); m.Fp = up16(m.F);
+  m.woff = b->wbits == 8 ? 128 : 0;
+  m.aoff = b->abits == 8 ? 128 : 0;
   return m;
 }
 
@@ -171,11 +177,11 @@ Ws layout(const Dims& m, void* base) {
   w.msews = b.take<float>(2048);
   if (m.codes) {
     if (att) {
-      w.Cqkv = b.take<uint8_t>(nqkv * d); w.Co = b.take<uint8_t>(d * dq);
-      w.Cxqkv = b.take<uint8_t>(T * d); w.Cxo = b.take<uint8_t>(T * dq);
+      w.Cqkv = b.take<uint8_t>(nqkv * m.dp); w.Co = b.take<uint8_t>(d * m.dqp);
+      w.Cxqkv = b.take<uint8_t>(T * m.dp); w.Cxo = b.take<uint8_t>(T * m.dqp);
     }
-    w.Cgu = b.take<uint8_t>(2 * F * d); w.Cd = b.take<uint8_t>(d * F);
-    w.Cxf = b.take<uint8_t>(T * d); w.Cxd = b.take<uint8_t>(T * F);
+    w.Cgu = b.take<uint8_t>(2 * F * m.dp); w.Cd = b.take<uint8_t>(d * m.Fp);
+    w.Cxf = b.take<uint8_t>(T * m.dp); w.Cxd = b.take<uint8_t>(T * m.Fp);
   }
   w.total = b.off;
   return w;
@@ -194,6 +200,10 @@ int check(const omq_block_desc* b) {
   // group-wise LWC in groups of 128 input channels: every C_in (d, F, and the
   // attention width) a multiple of 128
   if (b->group != 0 && (b->group != 128 || b->d % 128 || b->F % 128)) return OMQ_E_SHAPE;
+  // weight-activation quantization runs its forward products exactly on integer codes
+  // of per-row quantizers: group-wise clipping with quantized activations has no such
+  // product here
+  if (b->group != 0 && b->wbits < 16 && b->abits < 16) return OMQ_E_UNIMPLEMENTED;
   return OMQ_OK;
 }
 
@@ -222,7 +232,7 @@ hipError_t timed(omq_timer* tm, int kind, double work, hipStream_t st, F&& launc
 hipError_t wfq(const void* W, int64_t rows, int64_t cols, const float* s, const float* delta,
                const float* th, const Theta& t, int l, int wbits, bool fp, uint16_t* out,
                const Stats& st, int64_t row0, float* Bt, int64_t group, uint8_t* codes,
-               hipStream_t stream, omq_timer* tm) {
+               int64_t ldq, int code_off, hipStream_t stream, omq_timer* tm) {
   RowQuantFwd a;
   a.x = W; a.x_dt = OMQ_BF16; a.rows = rows; a.cols = cols; a.ldx = cols;
   a.let_mode = (s && !fp) ? OMQ_LET_MUL : OMQ_LET_NONE; a.s = s;
@@ -235,7 +245,9 @@ hipError_t wfq(const void* W, int64_t rows, int64_t cols, const float* s, const 
   const bool grouped = group && a.nbits < 16;
   if (grouped) a.group = group;
   if (!fp && delta && !grouped) { a.fold_delta = delta; a.bias_out = Bt + row0; }
-  if (codes && !fp) { a.codes = codes + row0 * cols; a.qsum = st.qsum + row0; }
+  if (codes && !fp) {
+    a.codes = codes + row0 * ldq; a.ldq = ldq; a.code_off = code_off; a.qsum = st.qsum + row0;
+  }
   // algorithmic bytes: read W, write W_hat (and the codes)
   const double bytes = (double)rows * (double)cols * (4.0 + (a.codes ? 1.0 : 0.0));
   hipError_t e = timed(fp ? nullptr : tm, OMQ_TIMED_WEIGHT_QUANT, bytes, stream,
@@ -250,7 +262,8 @@ hipError_t wfq(const void* W, int64_t rows, int64_t cols, const float* s, const 
 hipError_t wfq_cat(int n, const void* const* Ws, const int64_t* rows, const int* ls,
                    int64_t cols, const float* s, const float* delta, const float* th, const Theta& t,
                    int wbits, bool fp, uint16_t* out, const Stats& st, float* Bt, int64_t group,
-                   uint8_t* codes, hipStream_t stream, omq_timer* tm) {
+                   uint8_t* codes, int64_t ldq, int code_off, hipStream_t stream,
+                   omq_timer* tm) {
   RowQuantFwd a;
   a.x = Ws[0]; a.x_dt = OMQ_BF16; a.cols = cols; a.ldx = cols; a.nbits = wbits;
   a.group = fp ? 0 : group;
@@ -258,7 +271,7 @@ hipError_t wfq_cat(int n, const void* const* Ws, const int64_t* rows, const int*
     int64_t r0 = 0;
     for (int k = 0; k < n; ++k) {
       hipError_t e = wfq(Ws[k], rows[k], cols, s, delta, th, t, ls[k], wbits, fp, out, st, r0,
-                         Bt, group, codes, stream, tm);
+                         Bt, group, codes, ldq, code_off, stream, tm);
       if (e != hipSuccess) return e;
       r0 += rows[k];
     }
@@ -278,7 +291,7 @@ hipError_t wfq_cat(int n, const void* const* Ws, const int64_t* rows, const int*
   a.out = out; a.out_dt = OMQ_BF16; a.ldo = cols;
   a.h = st.h; a.z = st.z; a.amax = st.amax; a.amin = st.amin;
   if (delta) { a.fold_delta = delta; a.bias_out = Bt; }
-  if (codes) { a.codes = codes; a.qsum = st.qsum; }
+  if (codes) { a.codes = codes; a.ldq = ldq; a.code_off = code_off; a.qsum = st.qsum; }
   // algorithmic bytes: read W, write W_hat (and the codes)
   const double bytes = (double)r0 * (double)cols * (4.0 + (a.codes ? 1.0 : 0.0));
   return timed(tm, OMQ_TIMED_WEIGHT_QUANT, bytes, stream,
@@ -295,21 +308,27 @@ bool rms_fused(int x_dt, int64_t d, int abits, int mode) {
 // per-token quantizer with fused LET on its input
 hipError_t aq(const void* X, int x_dt, int64_t T, int64_t C, int64_t ldx, int mode,
               const float* s, const float* delta, int abits, uint16_t* out, const Stats& st,
-              hipStream_t stream, omq_timer* tm, uint8_t* codes = nullptr,
-              float* rms_out = nullptr, float* rstd = nullptr, float eps = 0.f) {
+              hipStream_t stream, omq_timer* tm, uint8_t* codes = nullptr, int64_t ldq = 0,
+              int code_off = 0, float* rms_out = nullptr, float* rstd = nullptr,
+              float eps = 0.f) {
   RowQuantFwd a;
   a.x = X; a.x_dt = x_dt; a.rows = T; a.cols = C; a.ldx = ldx;
   a.rms_out = rms_out; a.rstd = rstd; a.eps = eps;
   a.let_mode = mode; a.s = s; a.delta = delta; a.nbits = abits;
   a.out = out; a.out_dt = OMQ_BF16; a.ldo = C;
   a.h = st.h; a.z = st.z; a.amax = st.amax; a.amin = st.amin;
-  if (codes && abits < 16) { a.codes = codes; a.qsum = st.qsum; }
+  if (codes && abits < 16) { a.codes = codes; a.ldq = ldq; a.code_off = code_off; a.qsum = st.qsum; }
   // algorithmic bytes: read X, write X_hat (and the codes, and the normalized rows)
   const double bytes = (double)T * (double)C *
                        ((x_dt == OMQ_F32 ? 4.0 : 2.0) + 2.0 + (a.codes ? 1.0 : 0.0) +
                         (rms_out ? 4.0 : 0.0));
   return timed(abits < 16 ? tm : nullptr, OMQ_TIMED_ACT_QUANT, bytes, stream,
                [&] { return launch_rowquant_fwd(a, stream); });
+}
+
+// n bytes (a multiple of 4, 4-byte aligned) set to zero by a fill kernel
+hipError_t zero_bytes(void* p, int64_t n, hipStream_t st) {
+  return launch_fill_f32(reinterpret_cast<float*>(p), n / 4, 0.f, st);
 }
 
 // every matrix-core launch of the step goes through here (optional event timing)
@@ -330,16 +349,21 @@ hipError_t gemm(const void* A, int64_t lda, const void* B, int64_t ldb, float* C
 
 // the forward product Y = X_hat W_hat^T (+ bias) (+ resid) on the operands' integer
 // codes: X [T x K] per-token, W [N x K] per-output-channel quantizer rows
+// (code rows Kp long: K codes, then zero codes; stored codes shifted by the offsets)
 hipError_t code_gemm(const uint8_t* qx, const Stats& sx, const uint8_t* qw, const Stats& sw,
-                     float* C, int64_t ldc, int64_t T, int64_t N, int64_t K, const float* bias,
-                     const void* resid, int resid_dt, int64_t ldr, hipStream_t st,
-                     omq_timer* tm) {
+                     float* C, int64_t ldc, int64_t T, int64_t N, int64_t K, int64_t Kp,
+                     const Dims& m, const float* bias, const void* resid, int resid_dt,
+                     int64_t ldr, hipStream_t st, omq_timer* tm) {
   Gemm g;
   g.codes = 1;
-  g.A = qx; g.lda = K; g.B = qw; g.ldb = K; g.C = C; g.ldc = ldc;
-  g.M = T; g.N = N; g.K = K; g.bias = bias; g.resid = resid; g.resid_dt = resid_dt; g.ldr = ldr;
+  g.A = qx; g.lda = Kp; g.B = qw; g.ldb = Kp; g.C = C; g.ldc = ldc;
+  g.M = T; g.N = N; g.K = Kp; g.kz = K; g.bias = bias; g.resid = resid; g.resid_dt = resid_dt;
+  g.ldr = ldr;
   g.ha = sx.h; g.za = sx.z; g.sa = sx.qsum; g.hb = sw.h; g.zb = sw.z; g.sb = sw.qsum;
-  return run_gemm(g, st, tm);
+  g.zoa = (float)m.aoff; g.zob = (float)m.woff;
+  // timed with the algorithmic K
+  const double f = 2.0 * (double)T * (double)N * (double)K;
+  return timed(tm, OMQ_TIMED_GEMM_I8, f, st, [&] { return launch_gemm(g, st); });
 }
 
 #define CK(x)                               \
@@ -395,6 +419,13 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
     }
     const KvSites kv = kv_sites(m, t, w, th, nullptr);
     const float* s_o = fp ? nullptr : kv.s_o;
+    if (cq && (m.dp != d || m.dqp != dq)) {
+      // padded code rows: the columns past the row end must hold zero codes
+      CK(zero_bytes(w.Cqkv, nqkv * m.dp, st));
+      CK(zero_bytes(w.Co, d * m.dqp, st));
+      CK(zero_bytes(w.Cxqkv, T * m.dp, st));
+      CK(zero_bytes(w.Cxo, T * m.dqp, st));
+    }
     const float* d_o = fp ? nullptr : kv.d_o;
     CK(launch_rope_tables(T, m.hd, bd->rope_theta, w.cos_t, w.sin_t, st));
     // weight side of q, k, v, o
@@ -403,22 +434,22 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
       const int64_t rc[3] = {dq, dk, dk};
       const int lc[3] = {LQ, LK, LV};
       CK(wfq_cat(3, Wc, rc, lc, d, s_qkv, d_qkv, th, t, wb, fp, w.Wqkv, w.wq_qkv, w.Bt_qkv,
-                 m.group, cq ? w.Cqkv : nullptr, st, tm));
+                 m.group, cq ? w.Cqkv : nullptr, m.dp, m.woff, st, tm));
     }
     CK(wfq(W[LO], d, dq, s_o, d_o, th, t, LO, wb, fp, w.Wo, w.wq_o, 0, w.Bt_o, m.group,
-           cq ? w.Co : nullptr, st, tm));
+           cq ? w.Co : nullptr, m.dqp, m.woff, st, tm));
     // attention input: the RMSNorm runs inside the quantizer where that applies
     if (rms_fused(OMQ_BF16, d, ab, mode_let)) {
       CK(aq(x, OMQ_BF16, T, d, d, mode_let, s_qkv, d_qkv, ab, w.Xqkv, w.a_qkv, st, tm,
-            cq ? w.Cxqkv : nullptr, w.xn, w.r1, bd->eps));
+            cq ? w.Cxqkv : nullptr, m.dp, m.aoff, w.xn, w.r1, bd->eps));
     } else {
       CK(launch_rmsnorm(x, OMQ_BF16, T, d, bd->eps, w.xn, w.r1, st));
       CK(aq(w.xn, OMQ_F32, T, d, d, mode_let, s_qkv, d_qkv, ab, w.Xqkv, w.a_qkv, st, tm,
-            cq ? w.Cxqkv : nullptr));
+            cq ? w.Cxqkv : nullptr, m.dp, m.aoff));
     }
     if (cq)
-      CK(code_gemm(w.Cxqkv, w.a_qkv, w.Cqkv, w.wq_qkv, w.Yqkv, nqkv, T, nqkv, d, w.Bt_qkv, nullptr,
-                   0, 0, st, tm));
+      CK(code_gemm(w.Cxqkv, w.a_qkv, w.Cqkv, w.wq_qkv, w.Yqkv, nqkv, T, nqkv, d, m.dp, m,
+                   w.Bt_qkv, nullptr, 0, 0, st, tm));
     else
       CK(gemm(w.Xqkv, d, w.Wqkv, d, w.Yqkv, nqkv, T, nqkv, d, fp ? nullptr : w.Bt_qkv, nullptr,
               0, 0, st, tm));
@@ -443,10 +474,10 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
     }
     // o_proj with its LET site, residual
     CK(aq(w.O, OMQ_F32, T, dq, dq, mode_let, s_o, d_o, ab, w.Xo, w.a_o, st, tm,
-          cq ? w.Cxo : nullptr));
+          cq ? w.Cxo : nullptr, m.dqp, m.aoff));
     if (cq)
-      CK(code_gemm(w.Cxo, w.a_o, w.Co, w.wq_o, w.h1, d, T, d, dq, w.Bt_o, x, OMQ_BF16, d, st,
-                   tm));
+      CK(code_gemm(w.Cxo, w.a_o, w.Co, w.wq_o, w.h1, d, T, d, dq, m.dqp, m, w.Bt_o, x, OMQ_BF16,
+                   d, st, tm));
     else
       CK(gemm(w.Xo, dq, w.Wo, dq, w.h1, d, T, d, dq, fp ? nullptr : w.Bt_o, x, OMQ_BF16, d, st,
               tm));
@@ -460,32 +491,38 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
     xf_dt = OMQ_BF16;
   }
   // FFN
+  if (cq && (m.dp != d || m.Fp != F)) {
+    CK(zero_bytes(w.Cgu, 2 * F * m.dp, st));
+    CK(zero_bytes(w.Cd, d * m.Fp, st));
+    CK(zero_bytes(w.Cxf, T * m.dp, st));
+    CK(zero_bytes(w.Cxd, T * m.Fp, st));
+  }
   {
     const void* Wc[2] = {W[LG], W[LU]};
     const int64_t rc[2] = {F, F};
     const int lc[2] = {LG, LU};
     CK(wfq_cat(2, Wc, rc, lc, d, s_ffn, d_ffn, th, t, wb, fp, w.Wgu, w.wq_gu, w.Bt_gu, m.group,
-               cq ? w.Cgu : nullptr, st, tm));
+               cq ? w.Cgu : nullptr, m.dp, m.woff, st, tm));
   }
   CK(wfq(W[LD], d, F, nullptr, nullptr, th, t, LD, wb, fp, w.Wd, w.wq_d, 0, nullptr, m.group,
-         cq ? w.Cd : nullptr, st, tm));
+         cq ? w.Cd : nullptr, m.Fp, m.woff, st, tm));
   if (!m.ffn_only && rms_fused(OMQ_F32, d, ab, mode_let))
     CK(aq(w.h1, OMQ_F32, T, d, d, mode_let, s_ffn, d_ffn, ab, w.Xf, w.a_f, st, tm,
-          cq ? w.Cxf : nullptr, w.xn2, w.r2, bd->eps));
+          cq ? w.Cxf : nullptr, m.dp, m.aoff, w.xn2, w.r2, bd->eps));
   else
     CK(aq(xf, xf_dt, T, d, d, mode_let, s_ffn, d_ffn, ab, w.Xf, w.a_f, st, tm,
-          cq ? w.Cxf : nullptr));
+          cq ? w.Cxf : nullptr, m.dp, m.aoff));
   if (cq)
-    CK(code_gemm(w.Cxf, w.a_f, w.Cgu, w.wq_gu, w.GU, 2 * F, T, 2 * F, d, w.Bt_gu, nullptr, 0, 0,
-                 st, tm));
+    CK(code_gemm(w.Cxf, w.a_f, w.Cgu, w.wq_gu, w.GU, 2 * F, T, 2 * F, d, m.dp, m, w.Bt_gu,
+                 nullptr, 0, 0, st, tm));
   else
     CK(gemm(w.Xf, d, w.Wgu, d, w.GU, 2 * F, T, 2 * F, d, fp ? nullptr : w.Bt_gu, nullptr, 0, 0,
             st, tm));
   CK(launch_silu_gate(w.GU, T, F, w.A, st));
   CK(aq(w.A, OMQ_F32, T, F, F, OMQ_LET_NONE, nullptr, nullptr, ab, w.Xd, w.a_d, st, tm,
-        cq ? w.Cxd : nullptr));
+        cq ? w.Cxd : nullptr, m.Fp, m.aoff));
   if (cq)
-    CK(code_gemm(w.Cxd, w.a_d, w.Cd, w.wq_d, w.y, d, T, d, F, nullptr,
+    CK(code_gemm(w.Cxd, w.a_d, w.Cd, w.wq_d, w.y, d, T, d, F, m.Fp, m, nullptr,
                  m.ffn_only ? nullptr : w.h1, OMQ_F32, d, st, tm));
   else
     CK(gemm(w.Xd, F, w.Wd, F, w.y, d, T, d, F, nullptr, m.ffn_only ? nullptr : w.h1, OMQ_F32, d,
@@ -585,6 +622,7 @@ hipError_t lin_bwd_fused(const Ws& w, const LinBwd& L, int64_t T, int wbits, int
     if ((e = run_gemm(g, st, tm)) != hipSuccess) return e;
     RowQuantBwd a;
     a.cols = K; a.col_mode = se.col_mode; a.out0 = L.gs_w; a.out1 = L.fold ? L.gd_w : nullptr;
+    a.accumulate = 1;     // running totals of the LET pair's gradients
     // one finalizer launch over the concatenated rows, each segment with its own
     // weight rows and logits
     RowQuantBwd b;
@@ -603,9 +641,9 @@ hipError_t lin_bwd_fused(const Ws& w, const LinBwd& L, int64_t T, int wbits, int
     }
     b.col_mode = se.col_mode; b.out0 = L.gs_w;
     if (grouped) b.group = L.group;
-    // the column sums and the row finalizers in one launch (both add into gs_w)
-    if ((e = launch_ste_final(a, (int)ntl, colpart, b, grouped ? 1 : (int)nsl, rowpart, st)) !=
-        hipSuccess)
+    // the row finalizers, then the column sums with their scatter terms (both into gs_w)
+    if ((e = launch_ste_finish(a, (int)ntl, colpart, b, grouped ? 1 : (int)nsl, rowpart,
+                               w.rq + ste_records_offset(N, K, nsl, ntl), st)) != hipSuccess)
       return e;
   }
   // activation side
@@ -629,7 +667,8 @@ hipError_t lin_bwd_fused(const Ws& w, const LinBwd& L, int64_t T, int wbits, int
   a.h = L.ast.h; a.z = L.ast.z; a.amax = L.ast.amax; a.amin = L.ast.amin;
   a.col_mode = acol; a.gx = L.gx_out; a.ldgx = K;
   a.out0 = L.gs_x; a.out1 = L.gd_x; a.accumulate = 1;
-  return launch_ste_final(a, (int)ntl, colpart, a, (int)nsl, rowpart, st);
+  return launch_ste_finish(a, (int)ntl, colpart, a, (int)nsl, rowpart,
+                           w.rq + ste_records_offset(T, K, nsl, ntl), st);
 }
 
 int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w,

@@ -84,6 +84,13 @@ OMQ_DEV T wave_sum(T v) {
   return v;
 }
 
+// The RMSNorm scale of a row from its sum of squares (accumulated in double):
+// 1 / sqrt(ss / n + eps) in double, rounded once to float; the normalized row is
+// then x * scale in float (one rounding per element).
+OMQ_DEV float rms_scale(double ss, int64_t n, float eps) {
+  return (float)(1.0 / sqrt(ss / (double)n + (double)eps));
+}
+
 // (value, index) reductions; ties go to the lower index.
 OMQ_DEV void argmax_merge(float& v, int& i, float v2, int i2) {
   if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }

@@ -706,6 +706,8 @@ void k_gemm_bf16(Gemm g, int tiles_m, int tiles_n) {
   const int64_t row0 = m0 + lr0;
   // Integer codes: C = ha hb (S - zb Ra - za (Rb - K zb)) with S the integer sum of
   // code products and Ra, Rb the rows' code sums, i.e. sum_k (qa - za)(qb - zb)
+  // (codes and zero points both shifted by the stored offsets; zero-code padding
+  // adds nothing to S, Ra, Rb, and K is the unpadded length)
   // without rounding (every term an integer below 2^53), then one rounding to
   // float.  The rows' and columns' (h, z, code sum) go through LDS (the K loop
   // ended on a barrier, so the operand buffers are free).
@@ -716,18 +718,18 @@ void k_gemm_bf16(Gemm g, int tiles_m, int tiles_n) {
       const int64_t gm = m0 + t;
       const bool ok = gm < M;
       qs[t] = ok ? g.ha[gm] : 0.f;
-      qs[BM + t] = ok ? g.za[gm] : 0.f;
+      qs[BM + t] = ok ? g.za[gm] - g.zoa : 0.f;
       qs[2 * BM + t] = ok ? (float)g.sa[gm] : 0.f;
     }
     for (int t = tid; t < BN; t += NT) {
       const int64_t gn = n0 + t;
       const bool ok = gn < N;
       qs[3 * BM + t] = ok ? g.hb[gn] : 0.f;
-      qs[3 * BM + BN + t] = ok ? g.zb[gn] : 0.f;
+      qs[3 * BM + BN + t] = ok ? g.zb[gn] - g.zob : 0.f;
       qs[3 * BM + 2 * BN + t] = ok ? (float)g.sb[gn] : 0.f;
     }
     __syncthreads();
-    const double Kd = (double)g.K;
+    const double Kd = (double)(g.kz ? g.kz : g.K);
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int col = wn * (BN / WN) + j * 32 + (lane & 31);

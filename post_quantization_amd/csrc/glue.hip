@@ -14,7 +14,8 @@ namespace {
 
 constexpr int kThreads = 256;
 
-OMQ_DEV float block_sum(float v, float* sh) {
+template <typename T>
+OMQ_DEV T block_sum(T v, T* sh) {
   v = wave_sum(v);
   const int lane = threadIdx.x & 63, wid = wave_id();
   __syncthreads();
@@ -28,16 +29,16 @@ __global__ __launch_bounds__(kThreads) void k_rmsnorm(const void* x, int64_t d, 
                                                       float* y, float* rstd) {
   const int64_t r = blockIdx.x;
   const char* xr = reinterpret_cast<const char*>(x) + r * d * (XDT == OMQ_F32 ? 4 : 2);
-  __shared__ float sh[4];
-  float ss = 0.f;
+  __shared__ double sh[4];
+  double ss = 0.0;
   for (int64_t c = (int64_t)threadIdx.x * 4; c < d; c += 4 * kThreads) {
     float v[4];
     load4(xr, XDT, c, v);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ss = fmaf(v[j], v[j], ss);
+    for (int j = 0; j < 4; ++j) ss = fma((double)v[j], (double)v[j], ss);
   }
   ss = block_sum(ss, sh);
-  const float rs = 1.f / sqrtf(ss / (float)d + eps);
+  const float rs = rms_scale(ss, d, eps);
   if (threadIdx.x == 0 && rstd) rstd[r] = rs;
   for (int64_t c = (int64_t)threadIdx.x * 4; c < d; c += 4 * kThreads) {
     float v[4];

@@ -17,8 +17,10 @@ struct RowQuantFwd {
   const float* a_gamma = nullptr;  const float* a_beta = nullptr;  // NULL: 1
   void* out = nullptr;  int out_dt = 0;  int64_t ldo = 0;
   float* h = nullptr;  float* z = nullptr;  int32_t* amax = nullptr;  int32_t* amin = nullptr;
-  uint8_t* codes = nullptr;                         // [rows x cols], ld = cols
-  int32_t* qsum = nullptr;                          // per-row sum of the codes (group 0)
+  uint8_t* codes = nullptr;                         // [rows x cols], row stride ldq
+  int64_t ldq = 0;                                  // 0: cols (multiple of 4 otherwise)
+  int code_off = 0;                                 // codes stored as q - code_off (a byte)
+  int32_t* qsum = nullptr;                          // per-row sum of the stored codes (group 0)
   const float* fold_delta = nullptr;                // bias fold: sum_i fold_delta_i x_ri
   const float* bias = nullptr;  float* bias_out = nullptr;
   // 128: each run of 128 columns of a row is its own quantizer (group-wise LWC);
@@ -85,18 +87,17 @@ size_t rowquant_bwd_ws_bytes(int64_t rows, int64_t cols);
 hipError_t launch_rowquant_bwd(const RowQuantBwd& a, hipStream_t st);
 // Finalizers of the straight-through backward, shared by the tile pass and the
 // GEMM-epilogue form.  Partials: rowpart [rows][nslabs][2] (g_h, sum g (1 - in)),
-// colpart [ntiles][2][cols].  colfinal reduces the column partials into out0/out1;
-// rowfinal turns row partials into LWC-logit gradients and adds the max/min scatter.
+// colpart [ntiles][2][cols], then the row finalizers' scatter records (offset
+// ste_records_offset).  launch_ste_finish runs the row finalizers of rf (LWC-logit
+// gradients, the max/min scatter into rf.gx, one scatter record per row and
+// extreme) and then the column pass of cf: out0 / out1 = (cf.accumulate ? their
+// contents : 0) + the column partials + the records, every sum in a fixed order
+// (no atomics: a step is bitwise reproducible).
 size_t ste_partials_floats(int64_t rows, int64_t cols, int64_t nslabs, int64_t ntiles);
-hipError_t launch_ste_colfinal(const RowQuantBwd& a, int ntiles, float* colpart, hipStream_t st);
-// both in one launch: the column sums of cf (added to cf.out0 / cf.out1 atomically,
-// whatever cf.accumulate says: the destinations hold their running totals) and the
-// row finalizers of rf
-hipError_t launch_ste_final(const RowQuantBwd& cf, int ntiles, const float* colpart,
-                           const RowQuantBwd& rf, int nslabs, const float* rowpart,
-                           hipStream_t st);
-hipError_t launch_ste_rowfinal(const RowQuantBwd& a, int nslabs, const float* rowpart,
-                               hipStream_t st);
+int64_t ste_records_offset(int64_t rows, int64_t cols, int64_t nslabs, int64_t ntiles);
+hipError_t launch_ste_finish(const RowQuantBwd& cf, int ntiles, const float* colpart,
+                             const RowQuantBwd& rf, int nslabs, const float* rowpart,
+                             float* records, hipStream_t st);
 
 // LET alone: y = (x - delta) / s  or  y = s * x, elementwise over [rows x cols].
 hipError_t launch_let_elementwise(const void* x, int x_dt, int64_t rows, int64_t cols,
@@ -148,6 +149,11 @@ struct Gemm {
   int codes = 0;
   const float *ha = nullptr, *za = nullptr, *hb = nullptr, *zb = nullptr;
   const int32_t *sa = nullptr, *sb = nullptr;
+  // codes stored as q - zoa / q - zob (signed bytes: 8-bit codes shift by 128), so the
+  // zero points enter as za - zoa, zb - zob; kz: the K of the zero-point term when
+  // the code rows are padded with zero codes up to K (0: K)
+  float zoa = 0.f, zob = 0.f;
+  int64_t kz = 0;
   int ta = 0, tb = 0;                               // A is [K x M] / B is [K x N]
   SteEpi ste;                                       // bf16 only; mode 2 writes dL/dx into C
 };

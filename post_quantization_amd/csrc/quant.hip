@@ -29,6 +29,9 @@ OMQ_DEV float let_x(float x, int mode, const float* s, const float* delta, int64
   return x;
 }
 
+// row stride of the codes output
+OMQ_DEV int64_t code_ld(const RowQuantFwd& a) { return a.ldq ? a.ldq : a.cols; }
+
 // the block's code sum into *out (every thread of the 4-wave block calls it)
 OMQ_DEV void block_qsum(int qs, int32_t* out) {
   __shared__ int s_qs[4];
@@ -115,11 +118,12 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd(RowQuantFwd a) {
       float rr = rint_quot(xt, q.h, rh, u) + q.z;
       float qq = fminf(fmaxf(rr, 0.f), q.Q);
       o[j] = (qq - q.z) * q.h;
-      cw |= ((uint32_t)qq) << (8 * j);
-      qs += (int)qq;
+      const int qi = (int)qq - a.code_off;
+      cw |= ((uint32_t)qi & 0xffu) << (8 * j);
+      qs += qi;
     }
     store4(a.out, a.out_dt, r * a.ldo + c, o);
-    if (a.codes) *reinterpret_cast<uint32_t*>(a.codes + r * cols + c) = cw;
+    if (a.codes) *reinterpret_cast<uint32_t*>(a.codes + r * code_ld(a) + c) = cw;
   }
   if (a.qsum) block_qsum(qs, a.qsum + r);
 }
@@ -205,11 +209,12 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_reg(RowQuantFwd a) {
         const float rr = rint_quot(xt[k][j], q.h, rh, u) + q.z;
         const float qq = fminf(fmaxf(rr, 0.f), q.Q);
         o[j] = (qq - q.z) * q.h;
-        cw |= ((uint32_t)qq) << (8 * j);
-        qs += (int)qq;
+        const int qi = (int)qq - a.code_off;
+        cw |= ((uint32_t)qi & 0xffu) << (8 * j);
+        qs += qi;
       }
       store4(a.out, a.out_dt, r * a.ldo + c, o);
-      if (a.codes) *reinterpret_cast<uint32_t*>(a.codes + r * cols + c) = cw;
+      if (a.codes) *reinterpret_cast<uint32_t*>(a.codes + r * code_ld(a) + c) = cw;
     }
   }
   if (a.qsum) block_qsum(qs, a.qsum + r);
@@ -295,22 +300,23 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_blk8(RowQuantFwd a) {
     }
   }
   if constexpr (RMS) {
-    // 1 / rms of the row (block sum of squares), the normalized row stored, then LET
-    __shared__ float s_ss[4];
-    float ss = 0.f;
+    // 1 / rms of the row (block sum of squares in double), the normalized row stored,
+    // then LET
+    __shared__ double s_ss[4];
+    double ss = 0.0;
 #pragma unroll
     for (int k = 0; k < NC; ++k) {
       const int64_t c = ((int64_t)k * kThreads + tid) * 8;
       if (c < cols) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) ss = fmaf(xt[k][j], xt[k][j], ss);
+        for (int j = 0; j < 8; ++j) ss = fma((double)xt[k][j], (double)xt[k][j], ss);
       }
     }
     ss = wave_sum(ss);
     if (lane == 0) s_ss[wid] = ss;
     __syncthreads();
     ss = (s_ss[0] + s_ss[1]) + (s_ss[2] + s_ss[3]);
-    const float rs = 1.f / sqrtf(ss / (float)cols + a.eps);
+    const float rs = rms_scale(ss, cols, a.eps);
     if (tid == 0 && a.rstd) a.rstd[r] = rs;
 #pragma unroll
     for (int k = 0; k < NC; ++k) {
@@ -404,11 +410,12 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_blk8(RowQuantFwd a) {
       for (int j = 0; j < 8; ++j) {
         qq[j] = __builtin_amdgcn_fmed3f(rr[j] + q.z, 0.f, q.Q);
         o[j] = (qq[j] - q.z) * q.h;
-        cw[j >> 2] |= ((uint32_t)qq[j]) << (8 * (j & 3));
-        qs += (int)qq[j];
+        const int qi = (int)qq[j] - a.code_off;
+        cw[j >> 2] |= ((uint32_t)qi & 0xffu) << (8 * (j & 3));
+        qs += qi;
       }
       store8(a.out, a.out_dt, r * a.ldo + c, o);
-      if (a.codes) *reinterpret_cast<uint2*>(a.codes + r * cols + c) = make_uint2(cw[0], cw[1]);
+      if (a.codes) *reinterpret_cast<uint2*>(a.codes + r * code_ld(a) + c) = make_uint2(cw[0], cw[1]);
     }
   }
   if (a.qsum) block_qsum(qs, a.qsum + r);
@@ -563,14 +570,15 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_wave(RowQuantFwd a) {
         const float rr = xt[k][j] + q.z;
         const float qq = fminf(fmaxf(rr, 0.f), q.Q);
         o[j] = (qq - q.z) * q.h;
-        cw[j >> 2] |= ((uint32_t)qq) << (8 * (j & 3));
-        if (j < n) qs += (int)qq;
+        const int qi = (int)qq - a.code_off;
+        cw[j >> 2] |= ((uint32_t)qi & 0xffu) << (8 * (j & 3));
+        if (j < n) qs += qi;
       }
       store4(a.out, a.out_dt, r * a.ldo + c, o);
-      if (a.codes) *reinterpret_cast<uint32_t*>(a.codes + r * cols + c) = cw[0];
+      if (a.codes) *reinterpret_cast<uint32_t*>(a.codes + r * code_ld(a) + c) = cw[0];
       if (FULL || c + 8 <= cols) {
         store4(a.out, a.out_dt, r * a.ldo + c + 4, o + 4);
-        if (a.codes) *reinterpret_cast<uint32_t*>(a.codes + r * cols + c + 4) = cw[1];
+        if (a.codes) *reinterpret_cast<uint32_t*>(a.codes + r * code_ld(a) + c + 4) = cw[1];
       }
     }
   }
@@ -626,27 +634,31 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_lds(RowQuantFwd a) {
   // the row's 1 / rms: sum of squares over the staged row
   float rs = 1.f;
   if constexpr (RMS) {
-    float ss = 0.f;
+    double ss = 0.0;
 #pragma unroll 2
     for (int k = 0; k < NC; ++k) {
       if constexpr (XDT == OMQ_F32) {
         const uint4 t0 = my[(2 * k) * 64 + lane], t1 = my[(2 * k + 1) * 64 + lane];
         const uint32_t wv[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) ss = fmaf(__uint_as_float(wv[j]), __uint_as_float(wv[j]), ss);
+        for (int j = 0; j < 8; ++j) {
+          const double v = (double)__uint_as_float(wv[j]);
+          ss = fma(v, v, ss);
+        }
       } else {
         const uint4 t0 = my[k * 64 + lane];
         const uint32_t wv[4] = {t0.x, t0.y, t0.z, t0.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float lo = __uint_as_float(wv[q] << 16), hi = __uint_as_float(wv[q] & 0xffff0000u);
-          ss = fmaf(lo, lo, ss);
-          ss = fmaf(hi, hi, ss);
+          const double lo = (double)__uint_as_float(wv[q] << 16);
+          const double hi = (double)__uint_as_float(wv[q] & 0xffff0000u);
+          ss = fma(lo, lo, ss);
+          ss = fma(hi, hi, ss);
         }
       }
     }
     ss = wave_sum(ss);
-    rs = 1.f / sqrtf(ss / (float)a.cols + a.eps);
+    rs = rms_scale(ss, a.cols, a.eps);
     if (lane == 0 && a.rstd) a.rstd[r] = rs;
   }
   // x~ of chunk k for this lane (8 consecutive columns c .. c+7)
@@ -789,10 +801,11 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_lds(RowQuantFwd a) {
       uint32_t cw[2] = {0u, 0u};
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        cw[j >> 2] |= ((uint32_t)qq[j]) << (8 * (j & 3));
-        qs += (int)qq[j];
+        const int qi = (int)qq[j] - a.code_off;
+        cw[j >> 2] |= ((uint32_t)qi & 0xffu) << (8 * (j & 3));
+        qs += qi;
       }
-      *reinterpret_cast<uint2*>(a.codes + r * a.cols + c) = make_uint2(cw[0], cw[1]);
+      *reinterpret_cast<uint2*>(a.codes + r * code_ld(a) + c) = make_uint2(cw[0], cw[1]);
     }
   }
   if (a.qsum) {
@@ -867,13 +880,13 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_g128(RowQuantFwd a) {
     const float rr = rint_quot(xt[j], q.h, rh, u) + q.z;
     const float qq = fminf(fmaxf(rr, 0.f), q.Q);
     o[j] = (qq - q.z) * q.h;
-    cw[j >> 2] |= ((uint32_t)qq) << (8 * (j & 3));
+    cw[j >> 2] |= ((uint32_t)((int)qq - a.code_off) & 0xffu) << (8 * (j & 3));
   }
   store4(a.out, a.out_dt, r * a.ldo + c, o);
   store4(a.out, a.out_dt, r * a.ldo + c + 4, o + 4);
   if (a.codes) {
-    *reinterpret_cast<uint32_t*>(a.codes + r * a.cols + c) = cw[0];
-    *reinterpret_cast<uint32_t*>(a.codes + r * a.cols + c + 4) = cw[1];
+    *reinterpret_cast<uint32_t*>(a.codes + r * code_ld(a) + c) = cw[0];
+    *reinterpret_cast<uint32_t*>(a.codes + r * code_ld(a) + c + 4) = cw[1];
   }
 }
 
@@ -1053,11 +1066,32 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_bwd_tile(RowQuantBwd a, i
   }
 }
 
+// Scatter records of the row finalizers: for quantizer row p, entry 2p (its
+// argmax) and 2p + 1 (its argmin) give the column and the terms the column outputs
+// take there (v0 for out0, v1 for out1); the column pass adds them in row order.
+struct SteRec {
+  int32_t* col = nullptr;
+  float* v0 = nullptr;
+  float* v1 = nullptr;
+};
+
+inline SteRec ste_rec(float* base, int64_t nq) {
+  SteRec r;
+  if (base) {
+    r.col = reinterpret_cast<int32_t*>(base);
+    r.v0 = base + 2 * nq;
+    r.v1 = base + 4 * nq;
+  }
+  return r;
+}
+
 // row finalize: LPR lanes per quantizer row sum its per-slab partials (coalesced
 // reads, then a shuffle reduction), one of them finishes the row: LWC-logit
-// gradients and the max/min scatter.
+// gradients, the max/min scatter into the upstream gradient (one writer per row),
+// and the scatter records of the column outputs (no atomics).
 template <int XDT, int LPR>
-OMQ_DEV void rows_final(const RowQuantBwd& a, int nslabs, const float* rowpart, int64_t blk) {
+OMQ_DEV void rows_final(const RowQuantBwd& a, int nslabs, const float* rowpart, int64_t blk,
+                        SteRec rec) {
   // quantizer rows: rows, or (row, group) pairs p = row * ng + group
   const int64_t ng = a.group > 0 ? a.cols / 128 : 1;
   const int64_t p = (blk * kThreads + threadIdx.x) / LPR;
@@ -1126,46 +1160,48 @@ OMQ_DEV void rows_final(const RowQuantBwd& a, int nslabs, const float* rowpart, 
       else if (a.let_mode == OMQ_LET_MUL) up = gsc * a.s[c];
       a.gx[r * a.ldgx + c] += up;
     }
-    switch (a.col_mode) {
-      case COL_WEIGHT:
-        if (a.out0) atomicAdd(a.out0 + c, gsc * xo[e]);
-        break;
-      case COL_ACT_DIV:
-        if (a.out0) atomicAdd(a.out0 + c, gsc * (-xtl[e] / a.s[c]));
-        if (a.out1) atomicAdd(a.out1 + c, gsc * (-1.f / a.s[c]));
-        break;
-      case COL_ACT_MUL:
-        if (a.out0) atomicAdd(a.out0 + c, gsc * xo[e]);
-        break;
-      default:
-        break;
+    if (rec.col) {
+      float v0 = 0.f, v1 = 0.f;
+      switch (a.col_mode) {
+        case COL_WEIGHT:
+        case COL_ACT_MUL:
+          v0 = gsc * xo[e];
+          break;
+        case COL_ACT_DIV:
+          v0 = gsc * (-xtl[e] / a.s[c]);
+          v1 = gsc * (-1.f / a.s[c]);
+          break;
+        default:
+          break;
+      }
+      rec.col[2 * p + e] = c;
+      rec.v0[2 * p + e] = v0;
+      rec.v1[2 * p + e] = v1;
     }
   }
 }
 
 template <int XDT, int LPR>
-__global__ __launch_bounds__(kThreads) void k_rowquant_bwd_rows(RowQuantBwd a, int nslabs,
-                                                                const float* rowpart) {
-  rows_final<XDT, LPR>(a, nslabs, rowpart, blockIdx.x);
+__global__ __launch_bounds__(kThreads) void k_ste_rows(RowQuantBwd a, int nslabs,
+                                                       const float* rowpart, SteRec rec) {
+  rows_final<XDT, LPR>(a, nslabs, rowpart, blockIdx.x, rec);
 }
 
-// Both second stages of a straight-through GEMM epilogue in one launch: workgroups
-// [0, ncb) sum the column partials of 64 columns each (4 waves over the partial
-// rows, the wave sums added in LDS in a fixed order) and add the totals to out0 /
-// out1 atomically, since the row finalizers of the other workgroups scatter into the
-// same vectors meanwhile; the rest finish the quantizer rows as k_rowquant_bwd_rows.
-template <int XDT, int LPR>
-__global__ __launch_bounds__(kThreads) void k_ste_final(RowQuantBwd cf, int ntiles,
-                                                        const float* colpart, int ncb,
-                                                        RowQuantBwd rf, int nslabs,
-                                                        const float* rowpart) {
-  __shared__ float red[2][4][64];
-  if ((int)blockIdx.x >= ncb) {
-    rows_final<XDT, LPR>(rf, nslabs, rowpart, (int64_t)blockIdx.x - ncb);
-    return;
-  }
+// Column pass of a straight-through backward, after the row finalizers: per column c
+// (64 per workgroup, 4 waves)
+//   out_k[c] = (accumulate ? out_k[c] : 0) + sum_t colpart_k[t][c] + sum of the
+//              scatter records whose column is c
+// with every sum in a fixed order: the waves take the partial rows t = w, w + 4, ...
+// and contiguous quarters of the records (for group-wise rows only those of the
+// block's 128-column group), a batch's matches in lane order; the wave totals are
+// added in LDS in wave order.  Deterministic: no atomics anywhere.
+__global__ __launch_bounds__(kThreads) void k_ste_cols(const float* colpart, int ntiles,
+                                                       int64_t cols, float* out0, float* out1,
+                                                       int accumulate, SteRec rec,
+                                                       int64_t nrows, int64_t ng) {
+  __shared__ float red[4][4][64];
   const int lane = threadIdx.x & 63, w = wave_id();
-  const int64_t cols = cf.cols, c = (int64_t)blockIdx.x * 64 + lane;
+  const int64_t c0 = (int64_t)blockIdx.x * 64, c = c0 + lane;
   float s0 = 0.f, s1 = 0.f;
   if (c < cols) {
 #pragma unroll 4
@@ -1174,12 +1210,49 @@ __global__ __launch_bounds__(kThreads) void k_ste_final(RowQuantBwd cf, int ntil
       s1 += colpart[((int64_t)t * 2 + 1) * cols + c];
     }
   }
+  float a0 = 0.f, a1 = 0.f;
+  if (rec.col && nrows > 0) {
+    const int64_t g = c0 / 128;                       // the group of these columns
+    const int64_t n = 2 * nrows;                      // entries: max and min per row
+    const int64_t per = (n + 3) / 4;
+    const int64_t j0 = (int64_t)w * per, j1 = min(n, j0 + per);
+    for (int64_t jb = j0; jb < j1; jb += 64) {
+      const int64_t j = jb + lane;
+      const int64_t idx = ng > 1 ? 2 * ((j >> 1) * ng + g) + (j & 1) : j;
+      const int cj = j < j1 ? rec.col[idx] : -1;
+      const bool hit = cj >= c0 && cj < c0 + 64;
+      float v0 = 0.f, v1 = 0.f;
+      if (hit) {
+        v0 = rec.v0[idx];
+        v1 = rec.v1[idx];
+      }
+      uint64_t msk = __builtin_amdgcn_ballot_w64(hit);
+      while (msk) {
+        const int k = __builtin_ctzll(msk);
+        msk &= msk - 1;
+        const int ck = __builtin_amdgcn_readlane(cj, k) - (int)c0;
+        const float b0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v0), k));
+        const float b1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v1), k));
+        if (lane == ck) {
+          a0 += b0;
+          a1 += b1;
+        }
+      }
+    }
+  }
   red[0][w][lane] = s0;
   red[1][w][lane] = s1;
+  red[2][w][lane] = a0;
+  red[3][w][lane] = a1;
   __syncthreads();
   if (w < 2 && c < cols) {
-    float* o = w == 0 ? cf.out0 : cf.out1;
-    if (o) atomicAdd(o + c, ((red[w][0][lane] + red[w][1][lane]) + red[w][2][lane]) + red[w][3][lane]);
+    float* o = w == 0 ? out0 : out1;
+    if (o) {
+      const float cs = ((red[w][0][lane] + red[w][1][lane]) + red[w][2][lane]) + red[w][3][lane];
+      const float sc =
+          ((red[2 + w][0][lane] + red[2 + w][1][lane]) + red[2 + w][2][lane]) + red[2 + w][3][lane];
+      o[c] = (accumulate ? o[c] : 0.f) + (cs + sc);
+    }
   }
 }
 
@@ -1559,79 +1632,58 @@ hipError_t launch_rowquant_bwd(const RowQuantBwd& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rs = a.group > 0 ? 1 : (int)nslabs;
-  // column sums added to running totals: one launch with the row finalizers
-  if (a.accumulate) return launch_ste_final(a, (int)ntiles, colpart, a, rs, rowpart, st);
-  e = launch_ste_colfinal(a, (int)ntiles, colpart, st);
-  if (e != hipSuccess) return e;
-  return launch_ste_rowfinal(a, rs, rowpart, st);
+  float* records = a.ws + ste_records_offset(a.rows, a.cols, (a.cols + 127) / 128, ntiles);
+  return launch_ste_finish(a, (int)ntiles, colpart, a, rs, rowpart, records, st);
 }
 
 size_t ste_partials_floats(int64_t rows, int64_t cols, int64_t nslabs, int64_t ntiles) {
-  return (size_t)(nslabs * rows * 2 + ntiles * 2 * cols) + 64;
+  // row partials, column partials, then the scatter records (room for one quantizer
+  // row per 128 columns of a row: group-wise rows)
+  return (size_t)(ste_records_offset(rows, cols, nslabs, ntiles) +
+                  6 * rows * ((cols + 127) / 128)) + 64;
 }
 
-hipError_t launch_ste_colfinal(const RowQuantBwd& a, int ntiles, float* colpart,
-                               hipStream_t st) {
-  if (a.col_mode == COL_NONE || !(a.out0 || a.out1)) return hipSuccess;
-  return launch_part_colsum(colpart, ntiles, 2, a.cols, a.out0, a.out1, a.accumulate, st);
+int64_t ste_records_offset(int64_t rows, int64_t cols, int64_t nslabs, int64_t ntiles) {
+  return ((nslabs * rows * 2 + ntiles * 2 * cols) + 63) & ~int64_t(63);
 }
 
-hipError_t launch_ste_final(const RowQuantBwd& cf, int ntiles, const float* colpart,
-                           const RowQuantBwd& rf, int nslabs, const float* rowpart,
-                           hipStream_t st) {
-  const int ncb = (cf.col_mode != COL_NONE && (cf.out0 || cf.out1) && cf.cols > 0)
-                      ? (int)((cf.cols + 63) / 64) : 0;
-  const int lpr = nslabs == 1 ? 1 : 16;
-  const int64_t n = (rf.nbits < 16 && rf.rows > 0) ? rf.rows * (rf.group > 0 ? rf.cols / 128 : 1)
-                                                   : 0;
-  const int64_t nrb = (n * lpr + kThreads - 1) / kThreads;
-  if (ncb + nrb == 0) return hipSuccess;
-  const dim3 grid((unsigned)(ncb + nrb));
-  const bool f32 = rf.x_dt == OMQ_F32;
-  if (lpr == 1) {
-    if (f32)
-      hipLaunchKernelGGL((k_ste_final<OMQ_F32, 1>), grid, dim3(kThreads), 0, st, cf, ntiles,
-                         colpart, ncb, rf, nslabs, rowpart);
-    else
-      hipLaunchKernelGGL((k_ste_final<OMQ_BF16, 1>), grid, dim3(kThreads), 0, st, cf, ntiles,
-                         colpart, ncb, rf, nslabs, rowpart);
-  } else {
-    if (f32)
-      hipLaunchKernelGGL((k_ste_final<OMQ_F32, 16>), grid, dim3(kThreads), 0, st, cf, ntiles,
-                         colpart, ncb, rf, nslabs, rowpart);
-    else
-      hipLaunchKernelGGL((k_ste_final<OMQ_BF16, 16>), grid, dim3(kThreads), 0, st, cf, ntiles,
-                         colpart, ncb, rf, nslabs, rowpart);
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_ste_rowfinal(const RowQuantBwd& a, int nslabs, const float* rowpart,
-                               hipStream_t st) {
-  hipError_t e = hipSuccess;
-  if (a.nbits < 16 && a.rows > 0) {
-    const int64_t n = a.rows * (a.group > 0 ? a.cols / 128 : 1);
-    // one slab per row: a lane per row; else 16 lanes share a row's slabs
-    if (nslabs == 1) {
-      dim3 g2((unsigned)((n + kThreads - 1) / kThreads));
-      if (a.x_dt == OMQ_F32)
-        hipLaunchKernelGGL((k_rowquant_bwd_rows<OMQ_F32, 1>), g2, dim3(kThreads), 0, st, a,
-                           (int)nslabs, rowpart);
+hipError_t launch_ste_finish(const RowQuantBwd& cf, int ntiles, const float* colpart,
+                             const RowQuantBwd& rf, int nslabs, const float* rowpart,
+                             float* records, hipStream_t st) {
+  const bool cols_out = cf.col_mode != COL_NONE && (cf.out0 || cf.out1) && cf.cols > 0;
+  const int64_t ng = rf.group > 0 ? rf.cols / 128 : 1;
+  const int64_t nq = (rf.nbits < 16 && rf.rows > 0) ? rf.rows * ng : 0;
+  const bool recs = cols_out && nq > 0 && rf.col_mode != COL_NONE;
+  if (recs && !records) return hipErrorInvalidValue;
+  const SteRec rec = ste_rec(recs ? records : nullptr, nq);
+  if (nq > 0) {
+    // one lane per row when it has one slab, else 16 lanes share a row's slabs
+    const int lpr = nslabs == 1 ? 1 : 16;
+    const dim3 grid((unsigned)((nq * lpr + kThreads - 1) / kThreads));
+    const bool f32 = rf.x_dt == OMQ_F32;
+    if (lpr == 1) {
+      if (f32)
+        hipLaunchKernelGGL((k_ste_rows<OMQ_F32, 1>), grid, dim3(kThreads), 0, st, rf, nslabs,
+                           rowpart, rec);
       else
-        hipLaunchKernelGGL((k_rowquant_bwd_rows<OMQ_BF16, 1>), g2, dim3(kThreads), 0, st, a,
-                           (int)nslabs, rowpart);
+        hipLaunchKernelGGL((k_ste_rows<OMQ_BF16, 1>), grid, dim3(kThreads), 0, st, rf, nslabs,
+                           rowpart, rec);
     } else {
-      dim3 g2((unsigned)((n * 16 + kThreads - 1) / kThreads));
-      if (a.x_dt == OMQ_F32)
-        hipLaunchKernelGGL((k_rowquant_bwd_rows<OMQ_F32, 16>), g2, dim3(kThreads), 0, st, a,
-                           (int)nslabs, rowpart);
+      if (f32)
+        hipLaunchKernelGGL((k_ste_rows<OMQ_F32, 16>), grid, dim3(kThreads), 0, st, rf, nslabs,
+                           rowpart, rec);
       else
-        hipLaunchKernelGGL((k_rowquant_bwd_rows<OMQ_BF16, 16>), g2, dim3(kThreads), 0, st, a,
-                           (int)nslabs, rowpart);
+        hipLaunchKernelGGL((k_ste_rows<OMQ_BF16, 16>), grid, dim3(kThreads), 0, st, rf, nslabs,
+                           rowpart, rec);
     }
-    e = hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return e;
+  if (!cols_out) return hipSuccess;
+  hipLaunchKernelGGL(k_ste_cols, dim3((unsigned)((cf.cols + 63) / 64)), dim3(kThreads), 0, st,
+                     colpart, ntiles, cf.cols, cf.out0, cf.out1, cf.accumulate, rec,
+                     recs ? rf.rows : (int64_t)0, ng);
+  return hipGetLastError();
 }
 
 hipError_t launch_let_elementwise(const void* x, int x_dt, int64_t rows, int64_t cols, int mode,

@@ -209,3 +209,14 @@ def stack_samples_device(c: BlockCfg, n_samples: int, device, seed: int = 0):
 def reduced(c, **kw):
     """The same workload at other sizes (parity cases the oracle finishes fast)."""
     return replace(c, **kw)
+
+
+def attention_inputs(cfg: int, T: int, n_q: int, n_kv: int, hd: int = 128,
+                     q_scale: float = 2.0) -> Dict[str, np.ndarray]:
+    """bf16 Q [T x n_q hd], K, V [T x n_kv hd] ~ N(0, 1) (Q times q_scale, for a
+    softmax with some sharp rows) and an upstream gradient dO [T x n_q hd] ~ N(0, 1),
+    all bf16-exact float32 arrays (tensor ids 20-23 of workload cfg)."""
+    return {"Q": to_bf16(normal(cfg, 20, (T, n_q * hd), bf16=False) * np.float32(q_scale)),
+            "K": normal(cfg, 21, (T, n_kv * hd)),
+            "V": normal(cfg, 22, (T, n_kv * hd)),
+            "dO": normal(cfg, 23, (T, n_q * hd))}

@@ -27,7 +27,7 @@ def test_every_declared_symbol_is_exported():
     assert len(names) >= 20
     for n in names:
         assert hasattr(L, n), n
-    assert omq.abi_version() == 3
+    assert omq.abi_version() == 4
 
 
 def test_status_strings():
@@ -98,6 +98,33 @@ def test_validation_before_launch():
     assert omq.block_workspace_size(b) == 0            # the attention kernels take head_dim 128
     b = omq.BlockDesc(T=64, d=256, n_q=2, n_kv=2, head_dim=128, F=64, wbits=4, abits=4)
     assert omq.block_workspace_size(b) > 0
+    # group-wise clipping with quantized activations: not implemented
+    b = omq.BlockDesc(T=64, d=256, n_q=2, n_kv=2, head_dim=128, F=256, wbits=4, abits=4,
+                      group=128)
+    assert omq.block_workspace_size(b) == 0
+    assert L.omq_block_theta_layout(ctypes.byref(b), None, None, None, None) == -7
+    b = omq.BlockDesc(T=64, d=256, n_q=2, n_kv=2, head_dim=128, F=256, wbits=4, abits=16,
+                      group=128)
+    assert omq.block_workspace_size(b) > 0
+    # 8-bit codes and widths that are not multiples of 16 run the exact code product
+    b = omq.BlockDesc(T=64, d=264, n_q=2, n_kv=2, head_dim=128, F=200, wbits=8, abits=8)
+    assert omq.block_workspace_size(b) > 0
+    # attention on quantized operands: head_dim 128 only, strides and alignment
+    assert L.omq_attention_fwd(FAKE, 512, FAKE, FAKE, 256, 64, 4, 2, 64, FAKE, 512, FAKE,
+                               None) == -2
+    assert L.omq_attention_fwd(FAKE, 512, FAKE, FAKE, 256, 64, 4, 3, 128, FAKE, 512, FAKE,
+                               None) == -2
+    assert L.omq_attention_fwd(FAKE, 500, FAKE, FAKE, 256, 64, 4, 2, 128, FAKE, 512, FAKE,
+                               None) == -2
+    assert L.omq_attention_fwd(FAKE, 516, FAKE, FAKE, 256, 64, 4, 2, 128, FAKE, 512, FAKE,
+                               None) == -4
+    assert L.omq_attention_fwd(FAKE, 512, FAKE, FAKE, 256, 64, 4, 2, 128, FAKE, 512, None,
+                               None) == -1
+    assert L.omq_attention_fwd(FAKE, 512, FAKE, FAKE, 256, 0, 4, 2, 128, FAKE, 512, FAKE,
+                               None) == 0
+    assert L.omq_attention_bwd(FAKE, 512, FAKE, FAKE, 256, 64, 4, 2, 128, FAKE, FAKE, 512, FAKE,
+                               FAKE, 512, FAKE, FAKE, 256, FAKE, 16, None) == -5
+    assert omq.lib().omq_attention_bwd_workspace_size(64, 4, 512) >= 64 * 4 * 4 + 64 * 512 * 2
     b = omq.BlockDesc(T=64, d=64, n_q=4, n_kv=2, head_dim=16, F=64, wbits=4, abits=4,
                       optimizer=5)
     assert L.omq_block_step(ctypes.byref(b), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None,

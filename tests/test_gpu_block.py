@@ -48,13 +48,20 @@ CASES = {
     # the 70B-shaped block at its full widths (d 8192, 64 / 8 heads, F 28672, W4A16) on
     # 256 tokens: the oracle's step takes about a minute
     "gqa70b_w4a16_t256": synth.reduced(synth.BLOCK_CFG5_W4, T=256),
-    # the bench's 7B-shaped W4A4 block at its full widths on 128 tokens (every
-    # gradient group; the whole 2048-token step is checked below by its forward, loss
-    # and update)
+    # the bench's 7B-shaped W4A4 block at its full widths on 128 tokens
     "mha_w4a4_full_widths_t128": synth.reduced(synth.BLOCK_CFG4, T=128),
+    # the FFN workload at W3A16 whole, and the 70B-shaped block at W2A16 on its full
+    # widths (256 tokens)
+    "ffn_w3a16_full": synth.FFN_CFG3_W3,
+    "gqa70b_w2a16_t256": synth.reduced(synth.BLOCK_CFG5_W2, T=256),
+    # the 70B-shaped block whole (T 2048, d 8192, 64 / 8 heads, F 28672, W4A16): its
+    # attention forward and dQ run paired causal blocks, dK/dV unpaired; the oracle's
+    # step needs ~70 GB of host memory and a few minutes
+    "gqa70b_w4a16_full": synth.BLOCK_CFG5_W4,
 }
-# the full-width cases take the oracle tens of seconds
-SLOW = {"ffn_w2a16_full": 300, "gqa70b_w4a16_t256": 600, "mha_w4a4_full_widths_t128": 300}
+# the full-width cases take the oracle tens of seconds (the whole 70B block minutes)
+SLOW = {"ffn_w2a16_full": 300, "gqa70b_w4a16_t256": 600, "mha_w4a4_full_widths_t128": 300,
+        "ffn_w3a16_full": 300, "gqa70b_w2a16_t256": 600, "gqa70b_w4a16_full": 1100}
 
 
 def desc_of(c):
@@ -83,6 +90,38 @@ def upload_weights(c, inp):
         w = inp.get("W_" + n)
         out.append(dev(w, torch.bfloat16) if w is not None else None)
     return out
+
+
+def _per_head(v, ref, hd=128):
+    """Largest relative error over the head-sized slices of a per-channel vector."""
+    n = ref.size // hd
+    return max(rel(v[h * hd:(h + 1) * hd], ref[h * hd:(h + 1) * hd]) for h in range(n))
+
+
+def _full_size_setup(c, th):
+    inp = synth.block_inputs(c)
+    Wd = {k: v for k, v in inp.items() if k.startswith("W_")}
+    x = inp["x"]
+    ystar = ob.reference(c, x, Wd)
+    d = desc_of(c)
+    ws = torch.empty(omq.block_workspace_size(d), dtype=torch.uint8, device=DEV)
+    return inp, Wd, x, ystar, d, ws, dev(x, torch.bfloat16), upload_weights(c, inp)
+
+
+def _compare_grads(c, shapes, gpu_vec, g, tol=TOL, heads=True):
+    gg = ob.unpack(c, shapes, gpu_vec)
+    for name, _ in ob.theta_layout(c, shapes):
+        e = rel(gg[name], g[name])
+        msg = "grad %-12s %.2e" % (name, e)
+        # per-head slices of the per-channel attention vectors: a fault confined to
+        # some heads or query blocks shows there even when the whole vector passes
+        if heads and not c.ffn_only and (name in ("s_a", "s_o", "delta_o") or
+                                         name.endswith(("_q", "_k", "_v"))):
+            eh = _per_head(gg[name], np.asarray(g[name], np.float64))
+            msg += "  worst head %.2e" % eh
+            assert eh < 5 * tol, name
+        log(msg)
+        assert e < tol, name
 
 
 @pytest.mark.parametrize("kind", [pytest.param(k, marks=pytest.mark.timeout(SLOW[k])) if k in SLOW
@@ -114,8 +153,10 @@ def test_block_step(kind):
     yq = torch.empty_like(yfp)
     omq.block_forward(d, tx, W, theta, yq, ws)
     torch.cuda.synchronize()
-    e_fp, e_q = rel(host(yfp), ystar), rel(host(yq), y)
-    log("y fp rel", e_fp, "y quant rel", e_q)
+    # the block's update y - x (the residual x would dominate y itself)
+    x0 = 0.0 if c.ffn_only else np.asarray(x, np.float64)
+    e_fp, e_q = rel(host(yfp) - x0, ystar - x0), rel(host(yq) - x0, y - x0)
+    log("y - x fp rel", e_fp, "quant rel", e_q)
     assert e_fp < TOL and e_q < TOL
     # one calibration step (AdamW, step 1) against the oracle's target
     dth = torch.zeros_like(theta)
@@ -127,13 +168,7 @@ def test_block_step(kind):
     lg = float(host(tl)[0])
     log("gpu loss", lg)
     assert abs(lg - loss) <= TOL * loss
-    gg = ob.unpack(c, shapes, host(dth))
-    worst = 0.0
-    for name, _ in ob.theta_layout(c, shapes):
-        e = rel(gg[name], g[name])
-        worst = max(worst, e)
-        log("grad", name, "%.2e" % e, "norm %.3e" % np.linalg.norm(g[name]))
-        assert e < TOL, name
+    _compare_grads(c, shapes, host(dth), g)
     # the update applied by the step is AdamW (step 1) on the step's own gradient
     lrs = np.where(np.arange(total) < n_lwc, c.lr_lwc, c.lr_let)
     gv = host(dth)
@@ -145,32 +180,23 @@ def test_block_step(kind):
     assert rel(host(theta) - vec, expect - vec) < 1e-4
 
 
-def test_block_full_size_forward_and_step():
-    """The bench's workload at its full size (7B-shaped block, W4A4, T 2048, d 4096,
-    32 heads, F 11008) in the launch configuration the bench times: the
-    full-precision target and the quantized forward against the oracle's whole
-    forward (the oracle finishes it in about half a minute), the step's loss
-    against the oracle's loss on the same target, and properties of the step that
-    hold at any size: a finite gradient that is nonzero in every parameter group,
-    and AdamW's first update (-lr times the sign of the gradient wherever the
-    gradient dwarfs eps)."""
+@pytest.mark.timeout(900)
+def test_block_full_size_step_gradients():
+    """The bench's workload at its full size and launch configuration (7B-shaped
+    block, W4A4 with s_a, T 2048, d 4096, 32 heads, F 11008: every attention kernel
+    on its paired causal blocks) against the oracle's whole step: the
+    full-precision target, the block's update y - x of the quantized forward (the
+    residual x, with its outlier channels, would dominate y itself), the loss, every
+    gradient group (and per head for the attention's per-channel vectors and the
+    q/k/v clipping logits), and the AdamW update."""
     c = synth.BLOCK_CFG4
     log("full-size block", c)
-    inp = synth.block_inputs(c)
-    Wd = {k: v for k, v in inp.items() if k.startswith("W_")}
-    x = inp["x"]
     shapes = synth.block_weight_shapes(c)
     th = random_theta(c, np.random.default_rng(11))
-    ystar = ob.reference(c, x, Wd)
-    y, _ = ob.forward(c, x, Wd, th, ExactOps(bf16=True))
-    loss = float(np.mean((y - ystar) ** 2))
+    inp, Wd, x, ystar, d, ws, tx, W = _full_size_setup(c, th)
+    loss, g, y, _ = ob.calib_step(c, x, Wd, ystar, th, ExactOps(bf16=True))
     log("oracle loss", loss)
-
-    d = desc_of(c)
     offs, n_lwc, total = omq.block_theta_layout(d)
-    ws = torch.empty(omq.block_workspace_size(d), dtype=torch.uint8, device=DEV)
-    tx = dev(x, torch.bfloat16)
-    W = upload_weights(c, inp)
     vec = ob.pack(c, shapes, th)
     theta = dev(vec)
     yfp = torch.empty(c.T, c.d, dtype=torch.float32, device=DEV)
@@ -178,8 +204,10 @@ def test_block_full_size_forward_and_step():
     yq = torch.empty_like(yfp)
     omq.block_forward(d, tx, W, theta, yq, ws)
     torch.cuda.synchronize()
-    e_fp, e_q = rel(host(yfp), ystar), rel(host(yq), y)
-    log("y fp rel", e_fp, "y quant rel", e_q)
+    x64 = np.asarray(x, np.float64)
+    e_fp = rel(host(yfp) - x64, ystar - x64)
+    e_q = rel(host(yq) - x64, y - x64)
+    log("block update y - x: fp rel %.2e, quantized rel %.2e" % (e_fp, e_q))
     assert e_fp < TOL and e_q < TOL
     dth = torch.zeros_like(theta)
     m = torch.zeros_like(theta)
@@ -188,14 +216,97 @@ def test_block_full_size_forward_and_step():
     omq.block_step(d, tx, dev(ystar), W, theta, dth, m, v, 1, tl, ws)
     torch.cuda.synchronize()
     lg = float(host(tl)[0])
-    log("gpu loss", lg)
+    log("gpu loss %.6e oracle %.6e" % (lg, loss))
     assert abs(lg - loss) <= TOL * loss
     gv = host(dth)
     assert np.isfinite(gv).all()
-    gg = ob.unpack(c, shapes, gv)
-    for name, _ in ob.theta_layout(c, shapes):
-        assert np.abs(gg[name]).max() > 0, name
+    _compare_grads(c, shapes, gv, g)
     lr = np.where(np.arange(total) < n_lwc, c.lr_lwc, c.lr_let)
-    big = np.abs(gv) > 1e-5
-    step = host(theta) - vec
-    assert np.allclose(step[big], -lr[big] * np.sign(gv[big]), rtol=1e-2, atol=1e-6)
+    z = np.zeros(total, F32)
+    expect = np.concatenate([optim.adamw(vec[:n_lwc], gv[:n_lwc], z[:n_lwc], z[:n_lwc], 1,
+                                         c.lr_lwc)[0],
+                             optim.adamw(vec[n_lwc:], gv[n_lwc:], z[n_lwc:], z[n_lwc:], 1,
+                                         c.lr_let)[0]])
+    assert rel(host(theta) - vec, expect - vec) < 1e-4
+
+
+@pytest.mark.timeout(900)
+def test_block_full_size_trajectory():
+    """Three AdamW steps of the bench's workload at full size from the bench's
+    initialization (logits 4, s = 1, delta = 0, s_a = 1), each step recomputed by the
+    oracle from the GPU's own parameters: the loss and every gradient group of each
+    step, and each update against AdamW applied to the GPU's gradient and moments.
+    (AdamW turns sub-tolerance gradient differences into full-size updates, so two
+    free-running trajectories drift apart for reasons unrelated to correctness.)"""
+    c = synth.BLOCK_CFG4
+    shapes = synth.block_weight_shapes(c)
+    th0 = ob.init_theta(c, shapes)
+    inp, Wd, x, ystar, d, ws, tx, W = _full_size_setup(c, th0)
+    offs, n_lwc, total = omq.block_theta_layout(d)
+    theta = dev(ob.pack(c, shapes, th0))
+    dth = torch.zeros_like(theta)
+    m = torch.zeros_like(theta)
+    v = torch.zeros_like(theta)
+    tl = torch.zeros(1, dtype=torch.float32, device=DEV)
+    yt = dev(ystar)
+    losses = []
+    for step in (1, 2, 3):
+        vec, mv, vv = host(theta), host(m), host(v)
+        omq.block_step(d, tx, yt, W, theta, dth, m, v, step, tl, ws)
+        torch.cuda.synchronize()
+        lg = float(host(tl)[0])
+        loss, g, _, _ = ob.calib_step(c, x, Wd, ystar, ob.unpack(c, shapes, vec),
+                                      ExactOps(bf16=True))
+        log("step %d: gpu loss %.6e oracle %.6e" % (step, lg, loss))
+        losses.append((lg, loss))
+        assert abs(lg - loss) <= TOL * loss
+        gv = host(dth)
+        _compare_grads(c, shapes, gv, g, heads=False)
+        a = optim.adamw(vec[:n_lwc], gv[:n_lwc], mv[:n_lwc], vv[:n_lwc], step, c.lr_lwc)
+        b = optim.adamw(vec[n_lwc:], gv[n_lwc:], mv[n_lwc:], vv[n_lwc:], step, c.lr_let)
+        expect = np.concatenate([a[0], b[0]])
+        assert rel(host(theta) - vec, expect - vec) < 1e-4
+        assert rel(host(m), np.concatenate([a[1], b[1]])) < 1e-5
+    # the loss falls over the first steps, on both sides alike
+    assert losses[2][0] < losses[0][0] and losses[2][1] < losses[0][1]
+
+
+REPEAT_CASES = {
+    "mha_w4a4_full": synth.BLOCK_CFG4,
+    "gqa_w4a4": CASES["gqa_w4a4"],
+    "mha_w3a16g128": CASES["mha_w3a16g128"],
+    "ffn_w3a16": CASES["ffn_w3a16"],
+}
+
+
+@pytest.mark.parametrize("kind", list(REPEAT_CASES))
+def test_block_step_bitwise_repeatable(kind):
+    """Run-twice check: three calibration steps from the same state, twice, give
+    bit-identical loss, gradients, parameters and Adam moments (every reduction of
+    the step runs in a fixed order; a race or an order-dependent sum would show
+    here)."""
+    c = REPEAT_CASES[kind]
+    inp = synth.block_inputs(c)
+    shapes = synth.block_weight_shapes(c)
+    th = random_theta(c, np.random.default_rng(3))
+    d = desc_of(c)
+    ws = torch.empty(omq.block_workspace_size(d), dtype=torch.uint8, device=DEV)
+    tx = dev(inp["x"], torch.bfloat16)
+    W = upload_weights(c, inp)
+    yt = torch.empty(c.T, c.d, dtype=torch.float32, device=DEV)
+    omq.block_forward(d, tx, W, None, yt, ws)
+    vec = ob.pack(c, shapes, th)
+    runs = []
+    for _ in range(2):
+        theta = dev(vec)
+        dth = torch.zeros_like(theta)
+        m = torch.zeros_like(theta)
+        v = torch.zeros_like(theta)
+        tl = torch.zeros(3, dtype=torch.float32, device=DEV)
+        for step in (1, 2, 3):
+            omq.block_step(d, tx, yt, W, theta, dth, m, v, step, tl[step - 1:step], ws)
+        torch.cuda.synchronize()
+        runs.append([host(t).copy() for t in (tl, dth, theta, m, v)])
+    for name, a, b in zip(("loss", "dtheta", "theta", "m", "v"), *runs):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), name
+    log(kind, "losses", runs[0][0])

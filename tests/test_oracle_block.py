@@ -112,7 +112,7 @@ def test_attention_and_rmsnorm_bwd_vs_autograd():
         assert np.allclose(a, b.grad.numpy(), atol=1e-10)
     x = rng.standard_normal((T, 16)) * 3
     dy = rng.standard_normal((T, 16))
-    y, r = ob.rmsnorm(x, 1e-6)
+    y, r = ob.rmsnorm(x, 1e-6, code=False)
     tx = torch.tensor(x, requires_grad=True)
     Fn.rms_norm(tx, (16,), eps=1e-6).backward(torch.tensor(dy))
     assert np.allclose(ob.rmsnorm_bwd(dy, x, r), tx.grad.numpy(), atol=1e-10)
@@ -173,21 +173,20 @@ def test_let_gradients_vanish_without_quantizers():
             assert np.abs(v).max() < 1e-5 * max(1.0, loss), (n, np.abs(v).max())
 
 
-def test_forward_code_products_are_the_quantized_products():
-    """With the bf16 path's code-product policy (W4A4, per-channel, widths a multiple
-    of 16) each of the forward's quantized products equals the product written on
-    the integer codes (section "LWC": (q - z) h per row) plus the folded bias, and
-    the backward keeps its bf16 operands; with 8-bit codes or group-wise weights the
-    policy is off."""
-    c = _cfg(T=32, d=64, F=96, n_q=2, n_kv=2, head_dim=32, wbits=4, abits=4)
+@pytest.mark.parametrize("kw", [dict(wbits=4, abits=4, F=96), dict(wbits=8, abits=8, F=96),
+                                dict(wbits=4, abits=4, F=40),
+                                dict(wbits=3, abits=6, F=96, group=32)],
+                         ids=["w4a4", "w8a8", "w4a4_width40", "w3a6_g32"])
+def test_forward_quantized_products_are_exact(kw):
+    """The quantized layer is Y = Q_a(X~) Q_w(W~) + B~ (section "LET") with each
+    quantized operand (q - z) h per quantizer row (section "LWC").  With both
+    quantizers on, the oracle's forward products equal that definition written on
+    the integer codes (plus the folded bias), whatever the bit widths, the input
+    widths or the LWC grouping; the backward keeps the bf16 path's operands."""
+    c = _cfg(T=32, d=64, n_q=2, n_kv=2, head_dim=32, **kw)
     ops = ExactOps(bf16=True)
-    assert ops.code_product(c)
-    assert not ops.code_product(_cfg(T=32, d=64, F=96, n_q=2, n_kv=2, head_dim=32, wbits=8,
-                                     abits=4))
-    assert not ops.code_product(_cfg(T=32, d=64, F=96, n_q=2, n_kv=2, head_dim=32, wbits=4,
-                                     abits=4, group=32))
-    assert not ops.code_product(_cfg(T=32, d=64, F=40, n_q=2, n_kv=2, head_dim=32, wbits=4,
-                                     abits=4))
+    assert ops.exact_product(c.wbits, c.abits)
+    assert not ops.exact_product(16, c.abits) and not ops.exact_product(c.wbits, 16)
     inp = synth.block_inputs(c)
     Wd = {k: v for k, v in inp.items() if k.startswith("W_")}
     shapes = synth.block_weight_shapes(c)
@@ -198,7 +197,18 @@ def test_forward_code_products_are_the_quantized_products():
                       ("down", "a_down")):
         L = S.lin[name]
         a = ops.states[act]
-        want = quant.code_product(a.codes, a.h, a.z, L.wst.codes, L.wst.h, L.wst.z)
+        C_out, C_in = L.Wop.shape
+        if c.group:
+            # integer codes of each (row, group) with its own step and zero point
+            g = C_in // c.group
+            qw = (L.wst.codes.reshape(C_out, g, c.group).astype(np.int64)
+                  - L.wst.z.reshape(C_out, g, 1).astype(np.int64))
+            wdq = (qw * L.wst.h.reshape(C_out, g, 1).astype(F64)).reshape(C_out, C_in)
+            xdq = (a.codes.astype(np.int64) - a.z[:, None].astype(np.int64)) * \
+                a.h[:, None].astype(F64)
+            want = xdq @ wdq.T
+        else:
+            want = quant.code_product(a.codes, a.h, a.z, L.wst.codes, L.wst.h, L.wst.z)
         site = {"q": "qkv", "v": "qkv", "o": "o", "up": "ffn"}.get(name)
         if site is not None:
             delta = th["delta_" + site] if site != "o" else ob.kv_broadcast(
@@ -207,3 +217,73 @@ def test_forward_code_products_are_the_quantized_products():
         assert np.allclose(L.Y, want, rtol=1e-6, atol=1e-6 * np.abs(want).max()), name
         # the backward's operand is the bf16 rounding of the same weight
         assert np.array_equal(L.Wop, quant.bf16(L.wst.xhat.reshape(L.Wop.shape)))
+
+
+class _UnroundedP(ExactOps):
+    """The bf16 path with the softmax output fed to P V unrounded."""
+
+    def prob(self, P):
+        return np.asarray(P, F64)
+
+
+# gradient groups whose value moves by more than the bf16 tolerance (2e-2) when the
+# bf16 path's operand roundings are removed: the attention side's
+_ROUNDING_SENSITIVE = {"a_gamma_q", "a_beta_q", "a_gamma_k", "a_beta_k", "a_gamma_v", "a_beta_v",
+                       "a_gamma_o", "a_beta_o", "s_o", "delta_o", "s_a", "delta_qkv",
+                       "delta_ffn"}
+
+
+@pytest.mark.parametrize("theta_kind", ["init", "random"])
+def test_rounding_point_sensitivity(theta_kind):
+    """How much of the bf16 path's 2e-2 gradient tolerance its rounding points use.
+
+    The oracle's bf16 path (reading R17) rounds every matrix-core operand to bf16
+    where the GPU does (weights and activations of the backward products, Q~, K~, V,
+    and the softmax output P, reading R20); the exact path rounds nothing.  On the
+    7B-shaped W4A4 block at reduced size the loss and the block's update y - x move
+    little between the two, the FFN-side gradients (gate/up/down logits, s_ffn) and
+    s_qkv by less than the tolerance, but several attention-side groups by more:
+    parity at 2e-2 for those (the set _ROUNDING_SENSITIVE) rests on the oracle
+    rounding where the kernels round.  P's rounding alone moves s_o by several
+    percent."""
+    c = synth.reduced(synth.BLOCK_CFG4, T=256, d=512, n_q=4, n_kv=4, F=1376, n_out=5)
+    inp = synth.block_inputs(c)
+    Wd = {k: v for k, v in inp.items() if k.startswith("W_")}
+    shapes = synth.block_weight_shapes(c)
+    if theta_kind == "init":
+        th = ob.init_theta(c, shapes)
+    else:
+        rng = np.random.default_rng(7)
+        th = ob.init_theta(c, shapes)
+        for k in th:
+            n = th[k].size
+            if k.startswith("a_"):
+                th[k] = rng.uniform(2.0, 5.0, n).astype(F32)
+            elif k.startswith("delta"):
+                th[k] = (rng.standard_normal(n) * 0.05).astype(F32)
+            else:
+                th[k] = rng.uniform(0.7, 1.4, n).astype(F32)
+    x = inp["x"]
+    ystar = ob.reference(c, x, Wd)
+    lb, gb, yb, _ = ob.calib_step(c, x, Wd, ystar, th, ExactOps(bf16=True))
+    le, ge, ye, _ = ob.calib_step(c, x, Wd, ystar, th, ExactOps(bf16=False))
+    _, gp, _, _ = ob.calib_step(c, x, Wd, ystar, th, _UnroundedP(bf16=True))
+
+    def rel(a, b):
+        a, b = np.asarray(a, F64), np.asarray(b, F64)
+        return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+    assert abs(le - lb) < 1e-3 * lb
+    assert rel(ye - x, yb - x) < 2.5e-2
+    over = set()
+    for name, _ in ob.theta_layout(c, shapes):
+        gap = rel(ge[name], gb[name])
+        print("%-12s exact vs bf16 %.2e, unrounded P vs bf16 %.2e"
+              % (name, gap, rel(gp[name], gb[name])))
+        assert gap < 1e-1, name
+        if gap > 2e-2:
+            over.add(name)
+    assert over <= _ROUNDING_SENSITIVE, over - _ROUNDING_SENSITIVE
+    assert over, "no group exceeds the tolerance: the documented sensitivity is stale"
+    # P's bf16 rounding (reading R20) on its own moves the o-site scale by > 1e-2
+    assert rel(gp["s_o"], gb["s_o"]) > 1e-2

@@ -2,6 +2,12 @@
 
 * AdamW's first step with |g| >> eps moves each parameter by lr * sign(g); with
   bias correction a constant gradient gives the same step every time.
+* AdamW against Adam's closed form on a gradient sequence +g, -g: the second step
+  is lr (1 - beta1) / (1 + beta1) in the direction of +g (bias-corrected moments:
+  m^ = -(1 - beta1) g / (1 + beta1), v^ = g^2), and weight decay scales theta by
+  (1 - lr wd) first.  This pins the update rule for the constants the oracle uses;
+  the constants themselves (beta1 0.9, beta2 0.999, eps 1e-8) are not on the pages:
+  parity unpinned, a reading (standard defaults).
 * SGD is theta - lr g.
 * The single-layer fp32 workload (W4A16, LWC only, SGD at lr 5e-3): its logit
   gradients are ~1e-4, so lr * g is about one float32 spacing of the logits at
@@ -28,6 +34,24 @@ def test_adamw_first_step_and_bias_correction():
     assert np.allclose(t1 - th, -1e-2 * np.sign(g), rtol=1e-4, atol=1e-7)
     t2, m, v = optim.adamw(t1, g, m, v, 2, 1e-2)
     assert np.allclose(t2 - t1, t1 - th, rtol=1e-3, atol=1e-7)
+
+
+def test_adamw_closed_form_two_steps():
+    g = np.array([0.3, -2.0, 5e-2], F32)
+    th = np.array([1.0, 0.5, -0.25], F32)
+    z = np.zeros(3, F32)
+    lr = 1e-2
+    t1, m, v = optim.adamw(th, g, z, z, 1, lr)
+    t2, m, v = optim.adamw(t1, -g, m, v, 2, lr)
+    b1, b2, eps = optim.BETA1, optim.BETA2, optim.EPS
+    # m^_2 = -(1 - b1) g / (1 + b1) and v^_2 = g^2 exactly; step = -lr m^ / (|g| + eps)
+    want = lr * (1 - b1) / (1 + b1) * np.abs(g) / (np.abs(g) + eps) * np.sign(g)
+    assert np.allclose(t2.astype(np.float64) - t1, want, rtol=1e-4, atol=2e-8)
+    assert np.allclose(m, -(1 - b1) ** 2 * g, rtol=1e-5)
+    assert np.allclose(v, (1 - b2) * (1 + b2) * g.astype(np.float64) ** 2, rtol=1e-5)
+    # decoupled weight decay: theta (1 - lr wd) - lr m^ / (sqrt(v^) + eps)
+    t3, _, _ = optim.adamw(th, g, z, z, 1, lr, weight_decay=0.1)
+    assert np.allclose(t3, th * (1 - lr * 0.1) - lr * np.sign(g), rtol=1e-5, atol=1e-7)
 
 
 def test_sgd():
