@@ -304,6 +304,29 @@ int omq_lwc_backward(const float* gW_hat, const void* W, int w_dt, int64_t c_out
  * gX: float[T x C] or NULL; g_s, g_delta: float[C] or NULL (written, not accumulated).
  * ws: at least omq_act_quant_backward_workspace_size(T, C) bytes.
  */
+/*
+ * omq_lwc_backward_noalloc -- omq_lwc_backward for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments without ws / ws_bytes, the same results.
+ * The partial buffers live in a fixed device array of omq_noalloc_scratch_bytes()
+ * (64 MiB) that each GPU the library runs on holds until the process ends; the
+ * call allocates and frees nothing.  Shapes whose workspace query
+ * (omq_lwc_backward_workspace_size) exceeds that size return OMQ_E_WORKSPACE
+ * before any launch (every 7B-shaped weight, and the 70B-shaped q, k, v, o
+ * weights, fit).  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (two streams, two threads) race and must be serialized by
+ * the caller.  Nothing in the array needs clearing between calls.  The first call
+ * on a device looks up the array's device address (an exception to "no global
+ * mutable state": the per-device address is cached, under a lock).
+ */
+size_t omq_noalloc_scratch_bytes(void);
+int omq_lwc_backward_noalloc(const float* gW_hat, const void* W, int w_dt, int64_t c_out,
+                             int64_t c_in, int64_t group, int n_bits, const float* a_gamma,
+                             const float* a_beta, const float* s, const float* h, const float* z,
+                             const int32_t* arg_max, const int32_t* arg_min,
+                             const float* dy_colsum, float* g_a_gamma, float* g_a_beta,
+                             float* g_s, float* g_delta, void* stream);
+
 size_t omq_act_quant_backward_workspace_size(int64_t T, int64_t C);
 int omq_act_quant_backward(const float* gX_hat, int64_t T, int64_t C, const void* X, int x_dt,
                            int n_bits, int let_mode, const float* s, const float* delta,

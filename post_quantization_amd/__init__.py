@@ -20,7 +20,7 @@ __all__ = [
     "block_theta_layout", "block_workspace_size", "block_forward", "block_step",
     "F32", "BF16", "LET_NONE", "LET_DIV", "LET_MUL", "PATH_FP32", "PATH_BF16",
     "OPT_ADAMW", "OPT_SGD", "GemmTimer", "pack_codes", "fold_linear", "w4a16_gemm",
-    "attention_fwd", "attention_bwd",
+    "attention_fwd", "attention_bwd", "lwc_backward_noalloc", "noalloc_scratch_bytes",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -155,6 +155,9 @@ _SIGS = {
     "omq_lwc_backward_workspace_size": (_sz, [_i64, _i64]),
     "omq_lwc_backward": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "omq_noalloc_scratch_bytes": (_sz, []),
+    "omq_lwc_backward_noalloc": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _int, _vp, _vp, _vp,
+                                        _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "omq_act_quant_backward_workspace_size": (_sz, [_i64, _i64]),
     "omq_act_quant_backward": (_int, [_vp, _i64, _i64, _vp, _int, _int, _int, _vp, _vp, _vp,
                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -373,6 +376,31 @@ def lwc_backward(gW_hat, W, n_bits, a_gamma, a_beta, h, z, arg_max, arg_min, s=N
         _p(h),
         _p(z), _p(arg_max), _p(arg_min), _p(dy_colsum), _p(ga), _p(gb), _p(gs), _p(gd), _p(ws),
         nbytes, _stream()))
+    return ga, gb, gs, gd
+
+
+def noalloc_scratch_bytes() -> int:
+    return lib().omq_noalloc_scratch_bytes()
+
+
+def lwc_backward_noalloc(gW_hat, W, n_bits, a_gamma, a_beta, h, z, arg_max, arg_min, s=None,
+                         dy_colsum=None, want_s=False, want_delta=False, group=0, out=None):
+    """lwc_backward with the library's fixed device scratch (no workspace allocation
+    inside the library).  out: optional (ga, gb, gs, gd) tensors to write into."""
+    c_out, c_in = W.shape
+    dev = W.device
+    rows = _lwc_rows(c_out, c_in, group)
+    if out is None:
+        ga = torch.empty(rows, dtype=torch.float32, device=dev)
+        gb = torch.empty(rows, dtype=torch.float32, device=dev)
+        gs = torch.empty(c_in, dtype=torch.float32, device=dev) if want_s else None
+        gd = torch.empty(c_in, dtype=torch.float32, device=dev) if want_delta else None
+    else:
+        ga, gb, gs, gd = out
+    _check("omq_lwc_backward_noalloc", lib().omq_lwc_backward_noalloc(
+        _p(gW_hat), _p(W), _dt(W), c_out, c_in, group, n_bits, _p(a_gamma), _p(a_beta), _p(s),
+        _p(h), _p(z), _p(arg_max), _p(arg_min), _p(dy_colsum), _p(ga), _p(gb), _p(gs), _p(gd),
+        _stream()))
     return ga, gb, gs, gd
 
 

@@ -85,6 +85,12 @@ def test_validation_before_launch():
     # workspace too small
     assert L.omq_lwc_backward(FAKE, FAKE, 1, 8, 8, 0, 4, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
                               None, FAKE, FAKE, None, None, FAKE, 16, None) == -5
+    # the fixed-scratch form: shapes whose partials exceed the array are refused
+    assert omq.noalloc_scratch_bytes() == 64 << 20
+    assert L.omq_lwc_backward_noalloc(FAKE, FAKE, 1, 28672, 8192, 0, 4, FAKE, FAKE, None, FAKE,
+                                      FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None, None) == -5
+    assert L.omq_lwc_backward_noalloc(FAKE, FAKE, 1, 8, 0, 0, 4, FAKE, FAKE, None, FAKE, FAKE,
+                                      FAKE, FAKE, None, FAKE, FAKE, None, None, None) == -2
     assert L.omq_adamw(FAKE, FAKE, FAKE, FAKE, 10, 4, 1e-3, 1e-3, 0.9, 0.999, 1e-8, 0.0, 0,
                        None) == -1
     d = omq.QLinearDesc(T=12, c_in=16, c_out=8, wbits=4, abits=4, use_let=1, path=omq.PATH_BF16)
