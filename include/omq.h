@@ -95,13 +95,18 @@ int omq_abi_version(void);
  * = c_out or c_out * c_in / 128.  a_gamma, a_beta: float[rows].
  * B_tilde: float[c_out] or NULL.  codes: uint8[c_out x c_in] or NULL.
  * n_bits 2..8.
+ * nonfinite: int32 device flag or NULL; set to 1 when any element of W~ is NaN or
+ * infinite (never cleared: the caller zeroes it).  A non-finite element never
+ * wins the max / min comparisons, so such a row's h, z and codes are meaningless
+ * (its arg_max / arg_min still name columns of the row); the other rows are
+ * unaffected.
  */
 int omq_lwc_fakequant(const void* W, int w_dt, int64_t c_out, int64_t c_in, int64_t group,
                       int n_bits,
                       const float* a_gamma, const float* a_beta, const float* s,
                       const float* delta, const float* B, void* W_hat, int what_dt, float* h,
                       float* z, int32_t* arg_max, int32_t* arg_min, float* B_tilde,
-                      uint8_t* codes, void* stream);
+                      uint8_t* codes, int32_t* nonfinite, void* stream);
 
 /*
  * omq_let_apply -- the LET transforms alone (paper reading, section "LET",
@@ -127,10 +132,13 @@ int omq_let_apply(const void* X, int x_dt, int64_t T, int64_t c_in, const float*
  * n_bits 2..8, or 16: X_hat = x~ and h, z, arg_max, arg_min are not written.
  * X: [T x C] of x_dt; X_hat: [T x C] of xh_dt; h, z: float[T]; arg_max,
  * arg_min: int32[T]; codes: uint8[T x C] or NULL.
+ * nonfinite: int32 device flag or NULL; set to 1 when any element of x~ is NaN or
+ * infinite (n_bits < 16 only; never cleared), as for omq_lwc_fakequant.
  */
 int omq_act_quant(const void* X, int x_dt, int64_t T, int64_t C, int n_bits, int let_mode,
                   const float* s, const float* delta, void* X_hat, int xh_dt, float* h, float* z,
-                  int32_t* arg_max, int32_t* arg_min, uint8_t* codes, void* stream);
+                  int32_t* arg_max, int32_t* arg_min, uint8_t* codes, int32_t* nonfinite,
+                  void* stream);
 
 /*
  * omq_gemm -- the quantized layer's contraction (paper reading, section "LET":
@@ -443,6 +451,9 @@ typedef struct omq_block_desc {
   omq_timer* timer;   /* NULL, or per-launch GEMM timing (host struct, caller-owned) */
   int64_t group;      /* LWC group along C_in: 0 = per output channel, or 128 (every
                          C_in of the block a multiple of 128) */
+  int32_t* nonfinite; /* NULL, or an int32 device flag that every quantizer of the
+                         quantized forward sets to 1 when its input holds a NaN or an
+                         infinity (never cleared by the library) */
 } omq_block_desc;
 
 /*

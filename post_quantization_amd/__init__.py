@@ -121,27 +121,28 @@ class BlockDesc(ctypes.Structure):
                 ("abits", _int), ("ffn_only", _int), ("eps", _f), ("rope_theta", _f),
                 ("optimizer", _int), ("lr_lwc", _f), ("lr_let", _f), ("beta1", _f),
                 ("beta2", _f), ("adam_eps", _f), ("weight_decay", _f),
-                ("timer", ctypes.POINTER(OmqTimer)), ("group", _i64)]
+                ("timer", ctypes.POINTER(OmqTimer)), ("group", _i64), ("nonfinite", _vp)]
 
     def __init__(self, T, d, n_q, n_kv, head_dim, F, wbits, abits, ffn_only=False, eps=1e-6,
                  rope_theta=10000.0, optimizer=OPT_ADAMW, lr_lwc=5e-3, lr_let=1e-2,
                  beta1=0.9, beta2=0.999, adam_eps=1e-8, weight_decay=0.0, timer=None,
-                 group=0):
+                 group=0, nonfinite=None):
         super().__init__(ctypes.sizeof(BlockDesc), T, d, n_q, n_kv, head_dim, F, wbits, abits,
                          int(ffn_only), eps, rope_theta, optimizer, lr_lwc, lr_let, beta1,
                          beta2, adam_eps, weight_decay,
-                         ctypes.pointer(timer.struct) if timer is not None else None, group)
+                         ctypes.pointer(timer.struct) if timer is not None else None, group,
+                         nonfinite.data_ptr() if nonfinite is not None else None)
 
 
 _SIGS = {
     "omq_status_str": (ctypes.c_char_p, [_int]),
     "omq_abi_version": (_int, []),
     "omq_lwc_fakequant": (_int, [_vp, _int, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp,
-                                 _vp, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+                                 _vp, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "omq_let_apply": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _vp, _int, _vp, _int, _i64, _vp,
                              _vp, _int, _vp, _vp]),
     "omq_act_quant": (_int, [_vp, _int, _i64, _i64, _int, _int, _vp, _vp, _vp, _int, _vp, _vp,
-                             _vp, _vp, _vp, _vp]),
+                             _vp, _vp, _vp, _vp, _vp]),
     "omq_gemm": (_int, [_i64, _i64, _i64, _vp, _i64, _int, _vp, _i64, _int, _int, _vp, _f, _vp,
                         _i64, _int, _vp]),
     "omq_code_gemm": (_int, [_i64, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp,
@@ -240,7 +241,10 @@ def _lwc_rows(c_out, c_in, group):
 
 
 def lwc_fakequant(W, a_gamma, a_beta, n_bits, s=None, delta=None, B=None, out_dtype=None,
-                  want_bias=False, want_codes=False, group=0) -> Dict[str, torch.Tensor]:
+                  want_bias=False, want_codes=False, group=0,
+                  nonfinite=None) -> Dict[str, torch.Tensor]:
+    """nonfinite: optional int32 device tensor of one element, set to 1 when any
+    element of the LET-transformed weight is NaN or infinite."""
     c_out, c_in = W.shape
     dev = W.device
     out_dtype = W.dtype if out_dtype is None else out_dtype
@@ -256,7 +260,7 @@ def lwc_fakequant(W, a_gamma, a_beta, n_bits, s=None, delta=None, B=None, out_dt
         _p(W), _dt(W), c_out, c_in, group, n_bits, _p(a_gamma), _p(a_beta), _p(s), _p(delta),
         _p(B),
         _p(r["W_hat"]), _dt(r["W_hat"]), _p(r["h"]), _p(r["z"]), _p(r["arg_max"]),
-        _p(r["arg_min"]), _p(r["B_tilde"]), _p(r["codes"]), _stream()))
+        _p(r["arg_min"]), _p(r["B_tilde"]), _p(r["codes"]), _p(nonfinite), _stream()))
     return r
 
 
@@ -277,7 +281,7 @@ def let_apply(s, delta=None, X=None, W=None, B=None, x_out_dtype=torch.float32,
 
 
 def act_quant(X, n_bits, let_mode=LET_NONE, s=None, delta=None, out_dtype=torch.bfloat16,
-              want_codes=False) -> Dict[str, torch.Tensor]:
+              want_codes=False, nonfinite=None) -> Dict[str, torch.Tensor]:
     T, C = X.shape
     dev = X.device
     r = {"X_hat": torch.empty(T, C, dtype=out_dtype, device=dev),
@@ -289,7 +293,7 @@ def act_quant(X, n_bits, let_mode=LET_NONE, s=None, delta=None, out_dtype=torch.
     _check("omq_act_quant", lib().omq_act_quant(
         _p(X), _dt(X), T, C, n_bits, let_mode, _p(s), _p(delta), _p(r["X_hat"]),
         _dt(r["X_hat"]), _p(r["h"]), _p(r["z"]), _p(r["arg_max"]), _p(r["arg_min"]),
-        _p(r["codes"]), _stream()))
+        _p(r["codes"]), _p(nonfinite), _stream()))
     return r
 
 

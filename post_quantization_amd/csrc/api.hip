@@ -47,7 +47,7 @@ int omq_lwc_fakequant(const void* W, int w_dt, int64_t c_out, int64_t c_in, int6
                       int n_bits, const float* a_gamma, const float* a_beta, const float* s,
                       const float* delta, const float* B, void* W_hat, int what_dt, float* h,
                       float* z, int32_t* arg_max, int32_t* arg_min, float* B_tilde,
-                      uint8_t* codes, void* stream) {
+                      uint8_t* codes, int32_t* nonfinite, void* stream) {
   if (c_out == 0) return OMQ_OK;                   // no rows: nothing read or written
   if (!W || !a_gamma || !a_beta || !W_hat || !h || !z || !arg_max || !arg_min)
     return OMQ_E_INVALID_ARG;
@@ -57,7 +57,8 @@ int omq_lwc_fakequant(const void* W, int w_dt, int64_t c_out, int64_t c_in, int6
   if (c_in % 4) return OMQ_E_ALIGN;
   const int64_t grp = lwc_group(group, c_in);
   if (grp < 0) return OMQ_E_SHAPE;
-  if (!al16(W) || !al16(W_hat) || !al16(s) || !al16(delta) || !al4(codes)) return OMQ_E_ALIGN;
+  if (!al16(W) || !al16(W_hat) || !al16(s) || !al16(delta) || !al4(codes) || !al4(nonfinite))
+    return OMQ_E_ALIGN;
   RowQuantFwd a;
   a.x = W; a.x_dt = w_dt; a.rows = c_out; a.cols = c_in; a.ldx = c_in;
   a.let_mode = s ? OMQ_LET_MUL : OMQ_LET_NONE; a.s = s;
@@ -65,7 +66,7 @@ int omq_lwc_fakequant(const void* W, int w_dt, int64_t c_out, int64_t c_in, int6
   a.out = W_hat; a.out_dt = what_dt; a.ldo = c_in;
   a.h = h; a.z = z; a.amax = arg_max; a.amin = arg_min; a.codes = codes;
   a.fold_delta = delta; a.bias = B; a.bias_out = B_tilde;
-  a.group = grp;
+  a.group = grp; a.nonfinite = nonfinite;
   if (B_tilde && !delta) {
     // no shift: B~ = B
     if (B) OMQ_HIP_CHECK(hipMemcpyAsync(B_tilde, B, c_out * 4, hipMemcpyDeviceToDevice, S(stream)));
@@ -120,7 +121,8 @@ int omq_let_apply(const void* X, int x_dt, int64_t T, int64_t c_in, const float*
 
 int omq_act_quant(const void* X, int x_dt, int64_t T, int64_t C, int n_bits, int let_mode,
                   const float* s, const float* delta, void* X_hat, int xh_dt, float* h, float* z,
-                  int32_t* arg_max, int32_t* arg_min, uint8_t* codes, void* stream) {
+                  int32_t* arg_max, int32_t* arg_min, uint8_t* codes, int32_t* nonfinite,
+                  void* stream) {
   if (T == 0) return OMQ_OK;                       // no rows: nothing read or written
   if (!X || !X_hat) return OMQ_E_INVALID_ARG;
   if (!bits_ok(n_bits)) return OMQ_E_INVALID_ARG;
@@ -129,12 +131,14 @@ int omq_act_quant(const void* X, int x_dt, int64_t T, int64_t C, int n_bits, int
   if (!dt_ok(x_dt) || !dt_ok(xh_dt)) return OMQ_E_DTYPE;
   if (T < 0 || C <= 0) return OMQ_E_SHAPE;
   if (C % 4) return OMQ_E_ALIGN;
-  if (!al16(X) || !al16(X_hat) || !al4(codes) || !al16(s) || !al16(delta)) return OMQ_E_ALIGN;
+  if (!al16(X) || !al16(X_hat) || !al4(codes) || !al16(s) || !al16(delta) || !al4(nonfinite))
+    return OMQ_E_ALIGN;
   RowQuantFwd a;
   a.x = X; a.x_dt = x_dt; a.rows = T; a.cols = C; a.ldx = C;
   a.let_mode = let_mode; a.s = s; a.delta = delta; a.nbits = n_bits;
   a.out = X_hat; a.out_dt = xh_dt; a.ldo = C;
   a.h = h; a.z = z; a.amax = arg_max; a.amin = arg_min; a.codes = codes;
+  a.nonfinite = nonfinite;
   OMQ_HIP_CHECK(launch_rowquant_fwd(a, S(stream)));
   return OMQ_OK;
 }

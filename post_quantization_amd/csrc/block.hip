@@ -232,7 +232,7 @@ hipError_t timed(omq_timer* tm, int kind, double work, hipStream_t st, F&& launc
 hipError_t wfq(const void* W, int64_t rows, int64_t cols, const float* s, const float* delta,
                const float* th, const Theta& t, int l, int wbits, bool fp, uint16_t* out,
                const Stats& st, int64_t row0, float* Bt, int64_t group, uint8_t* codes,
-               int64_t ldq, int code_off, hipStream_t stream, omq_timer* tm) {
+               int64_t ldq, int code_off, hipStream_t stream, omq_timer* tm, int32_t* nf) {
   RowQuantFwd a;
   a.x = W; a.x_dt = OMQ_BF16; a.rows = rows; a.cols = cols; a.ldx = cols;
   a.let_mode = (s && !fp) ? OMQ_LET_MUL : OMQ_LET_NONE; a.s = s;
@@ -248,6 +248,7 @@ hipError_t wfq(const void* W, int64_t rows, int64_t cols, const float* s, const 
   if (codes && !fp) {
     a.codes = codes + row0 * ldq; a.ldq = ldq; a.code_off = code_off; a.qsum = st.qsum + row0;
   }
+  if (!fp) a.nonfinite = nf;
   // algorithmic bytes: read W, write W_hat (and the codes)
   const double bytes = (double)rows * (double)cols * (4.0 + (a.codes ? 1.0 : 0.0));
   hipError_t e = timed(fp ? nullptr : tm, OMQ_TIMED_WEIGHT_QUANT, bytes, stream,
@@ -263,7 +264,7 @@ hipError_t wfq_cat(int n, const void* const* Ws, const int64_t* rows, const int*
                    int64_t cols, const float* s, const float* delta, const float* th, const Theta& t,
                    int wbits, bool fp, uint16_t* out, const Stats& st, float* Bt, int64_t group,
                    uint8_t* codes, int64_t ldq, int code_off, hipStream_t stream,
-                   omq_timer* tm) {
+                   omq_timer* tm, int32_t* nf) {
   RowQuantFwd a;
   a.x = Ws[0]; a.x_dt = OMQ_BF16; a.cols = cols; a.ldx = cols; a.nbits = wbits;
   a.group = fp ? 0 : group;
@@ -271,7 +272,7 @@ hipError_t wfq_cat(int n, const void* const* Ws, const int64_t* rows, const int*
     int64_t r0 = 0;
     for (int k = 0; k < n; ++k) {
       hipError_t e = wfq(Ws[k], rows[k], cols, s, delta, th, t, ls[k], wbits, fp, out, st, r0,
-                         Bt, group, codes, ldq, code_off, stream, tm);
+                         Bt, group, codes, ldq, code_off, stream, tm, nf);
       if (e != hipSuccess) return e;
       r0 += rows[k];
     }
@@ -292,6 +293,7 @@ hipError_t wfq_cat(int n, const void* const* Ws, const int64_t* rows, const int*
   a.h = st.h; a.z = st.z; a.amax = st.amax; a.amin = st.amin;
   if (delta) { a.fold_delta = delta; a.bias_out = Bt; }
   if (codes) { a.codes = codes; a.ldq = ldq; a.code_off = code_off; a.qsum = st.qsum; }
+  a.nonfinite = nf;
   // algorithmic bytes: read W, write W_hat (and the codes)
   const double bytes = (double)r0 * (double)cols * (4.0 + (a.codes ? 1.0 : 0.0));
   return timed(tm, OMQ_TIMED_WEIGHT_QUANT, bytes, stream,
@@ -308,7 +310,8 @@ bool rms_fused(int x_dt, int64_t d, int abits, int mode) {
 // per-token quantizer with fused LET on its input
 hipError_t aq(const void* X, int x_dt, int64_t T, int64_t C, int64_t ldx, int mode,
               const float* s, const float* delta, int abits, uint16_t* out, const Stats& st,
-              hipStream_t stream, omq_timer* tm, uint8_t* codes = nullptr, int64_t ldq = 0,
+              hipStream_t stream, omq_timer* tm, int32_t* nf, uint8_t* codes = nullptr,
+              int64_t ldq = 0,
               int code_off = 0, float* rms_out = nullptr, float* rstd = nullptr,
               float eps = 0.f) {
   RowQuantFwd a;
@@ -318,6 +321,7 @@ hipError_t aq(const void* X, int x_dt, int64_t T, int64_t C, int64_t ldx, int mo
   a.out = out; a.out_dt = OMQ_BF16; a.ldo = C;
   a.h = st.h; a.z = st.z; a.amax = st.amax; a.amin = st.amin;
   if (codes && abits < 16) { a.codes = codes; a.ldq = ldq; a.code_off = code_off; a.qsum = st.qsum; }
+  if (abits < 16) a.nonfinite = nf;
   // algorithmic bytes: read X, write X_hat (and the codes, and the normalized rows)
   const double bytes = (double)T * (double)C *
                        ((x_dt == OMQ_F32 ? 4.0 : 2.0) + 2.0 + (a.codes ? 1.0 : 0.0) +
@@ -399,6 +403,7 @@ KvSites kv_sites(const Dims& m, const Theta& t, const Ws& w, const float* th, fl
 int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w, const void* x,
             const void* const* W, const float* th, bool fp, hipStream_t st) {
   omq_timer* tm = bd->timer;
+  int32_t* const nf = fp ? nullptr : bd->nonfinite;   // the input-health flag
   const int64_t T = m.T, d = m.d, F = m.F, dq = m.dq, dk = m.dk, nqkv = m.nqkv;
   const int wb = fp ? 16 : bd->wbits, ab = fp ? 16 : bd->abits;
   const float* s_ffn = fp ? nullptr : th + t.s_ffn;
@@ -434,17 +439,17 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
       const int64_t rc[3] = {dq, dk, dk};
       const int lc[3] = {LQ, LK, LV};
       CK(wfq_cat(3, Wc, rc, lc, d, s_qkv, d_qkv, th, t, wb, fp, w.Wqkv, w.wq_qkv, w.Bt_qkv,
-                 m.group, cq ? w.Cqkv : nullptr, m.dp, m.woff, st, tm));
+                 m.group, cq ? w.Cqkv : nullptr, m.dp, m.woff, st, tm, nf));
     }
     CK(wfq(W[LO], d, dq, s_o, d_o, th, t, LO, wb, fp, w.Wo, w.wq_o, 0, w.Bt_o, m.group,
-           cq ? w.Co : nullptr, m.dqp, m.woff, st, tm));
+           cq ? w.Co : nullptr, m.dqp, m.woff, st, tm, nf));
     // attention input: the RMSNorm runs inside the quantizer where that applies
     if (rms_fused(OMQ_BF16, d, ab, mode_let)) {
-      CK(aq(x, OMQ_BF16, T, d, d, mode_let, s_qkv, d_qkv, ab, w.Xqkv, w.a_qkv, st, tm,
+      CK(aq(x, OMQ_BF16, T, d, d, mode_let, s_qkv, d_qkv, ab, w.Xqkv, w.a_qkv, st, tm, nf,
             cq ? w.Cxqkv : nullptr, m.dp, m.aoff, w.xn, w.r1, bd->eps));
     } else {
       CK(launch_rmsnorm(x, OMQ_BF16, T, d, bd->eps, w.xn, w.r1, st));
-      CK(aq(w.xn, OMQ_F32, T, d, d, mode_let, s_qkv, d_qkv, ab, w.Xqkv, w.a_qkv, st, tm,
+      CK(aq(w.xn, OMQ_F32, T, d, d, mode_let, s_qkv, d_qkv, ab, w.Xqkv, w.a_qkv, st, tm, nf,
             cq ? w.Cxqkv : nullptr, m.dp, m.aoff));
     }
     if (cq)
@@ -458,11 +463,11 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
     // s_a on the affinity, then Q/K/V quantized per token
     const bool sa = m.use_sa && !fp;
     CK(aq(w.Qr, OMQ_F32, T, dq, dq, sa ? OMQ_LET_DIV : OMQ_LET_NONE, kv.sa_q, nullptr, ab, w.Qh,
-          w.a_q, st, tm));
+          w.a_q, st, tm, nf));
     CK(aq(w.Kr, OMQ_F32, T, dk, dk, sa ? OMQ_LET_MUL : OMQ_LET_NONE, th + (sa ? t.s_a : 0),
-          nullptr, ab, w.Kh, w.a_k, st, tm));
+          nullptr, ab, w.Kh, w.a_k, st, tm, nf));
     CK(aq(w.Yqkv + dq + dk, OMQ_F32, T, dk, nqkv, OMQ_LET_NONE, nullptr, nullptr, ab, w.Vh, w.a_v,
-          st, tm));
+          st, tm, nf));
     // causal attention, float32 softmax, fused
     {
       FlashFwd f;
@@ -473,7 +478,7 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
       CK(launch_flash_fwd(f, st));
     }
     // o_proj with its LET site, residual
-    CK(aq(w.O, OMQ_F32, T, dq, dq, mode_let, s_o, d_o, ab, w.Xo, w.a_o, st, tm,
+    CK(aq(w.O, OMQ_F32, T, dq, dq, mode_let, s_o, d_o, ab, w.Xo, w.a_o, st, tm, nf,
           cq ? w.Cxo : nullptr, m.dqp, m.aoff));
     if (cq)
       CK(code_gemm(w.Cxo, w.a_o, w.Co, w.wq_o, w.h1, d, T, d, dq, m.dqp, m, w.Bt_o, x, OMQ_BF16,
@@ -502,15 +507,15 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
     const int64_t rc[2] = {F, F};
     const int lc[2] = {LG, LU};
     CK(wfq_cat(2, Wc, rc, lc, d, s_ffn, d_ffn, th, t, wb, fp, w.Wgu, w.wq_gu, w.Bt_gu, m.group,
-               cq ? w.Cgu : nullptr, m.dp, m.woff, st, tm));
+               cq ? w.Cgu : nullptr, m.dp, m.woff, st, tm, nf));
   }
   CK(wfq(W[LD], d, F, nullptr, nullptr, th, t, LD, wb, fp, w.Wd, w.wq_d, 0, nullptr, m.group,
-         cq ? w.Cd : nullptr, m.Fp, m.woff, st, tm));
+         cq ? w.Cd : nullptr, m.Fp, m.woff, st, tm, nf));
   if (!m.ffn_only && rms_fused(OMQ_F32, d, ab, mode_let))
-    CK(aq(w.h1, OMQ_F32, T, d, d, mode_let, s_ffn, d_ffn, ab, w.Xf, w.a_f, st, tm,
+    CK(aq(w.h1, OMQ_F32, T, d, d, mode_let, s_ffn, d_ffn, ab, w.Xf, w.a_f, st, tm, nf,
           cq ? w.Cxf : nullptr, m.dp, m.aoff, w.xn2, w.r2, bd->eps));
   else
-    CK(aq(xf, xf_dt, T, d, d, mode_let, s_ffn, d_ffn, ab, w.Xf, w.a_f, st, tm,
+    CK(aq(xf, xf_dt, T, d, d, mode_let, s_ffn, d_ffn, ab, w.Xf, w.a_f, st, tm, nf,
           cq ? w.Cxf : nullptr, m.dp, m.aoff));
   if (cq)
     CK(code_gemm(w.Cxf, w.a_f, w.Cgu, w.wq_gu, w.GU, 2 * F, T, 2 * F, d, m.dp, m, w.Bt_gu,
@@ -519,7 +524,7 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
     CK(gemm(w.Xf, d, w.Wgu, d, w.GU, 2 * F, T, 2 * F, d, fp ? nullptr : w.Bt_gu, nullptr, 0, 0,
             st, tm));
   CK(launch_silu_gate(w.GU, T, F, w.A, st));
-  CK(aq(w.A, OMQ_F32, T, F, F, OMQ_LET_NONE, nullptr, nullptr, ab, w.Xd, w.a_d, st, tm,
+  CK(aq(w.A, OMQ_F32, T, F, F, OMQ_LET_NONE, nullptr, nullptr, ab, w.Xd, w.a_d, st, tm, nf,
         cq ? w.Cxd : nullptr, m.Fp, m.aoff));
   if (cq)
     CK(code_gemm(w.Cxd, w.a_d, w.Cd, w.wq_d, w.y, d, T, d, F, m.Fp, m, nullptr,

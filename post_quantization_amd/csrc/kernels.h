@@ -21,6 +21,7 @@ struct RowQuantFwd {
   int64_t ldq = 0;                                  // 0: cols (multiple of 4 otherwise)
   int code_off = 0;                                 // codes stored as q - code_off (a byte)
   int32_t* qsum = nullptr;                          // per-row sum of the stored codes (group 0)
+  int32_t* nonfinite = nullptr;                     // set to 1 when any x~ is NaN or infinite
   const float* fold_delta = nullptr;                // bias fold: sum_i fold_delta_i x_ri
   const float* bias = nullptr;  float* bias_out = nullptr;
   // 128: each run of 128 columns of a row is its own quantizer (group-wise LWC);

@@ -32,6 +32,17 @@ OMQ_DEV float let_x(float x, int mode, const float* s, const float* delta, int64
 // row stride of the codes output
 OMQ_DEV int64_t code_ld(const RowQuantFwd& a) { return a.ldq ? a.ldq : a.cols; }
 
+// a row's extreme-value column, kept inside the row: with a NaN in the row the
+// comparisons of the reductions never pick it, and lanes that held no column could
+// leave their sentinel index
+OMQ_DEV int col_in(int i, int64_t cols) { return (i >= 0 && (int64_t)i < cols) ? i : 0; }
+
+// the input flag: set when any lane of the wave saw a NaN or infinite x~ (every
+// lane of the wave calls it; the flag is only ever set, never cleared)
+OMQ_DEV void flag_nonfinite(int32_t* flag, bool nf) {
+  if (__builtin_amdgcn_ballot_w64(nf) != 0 && (threadIdx.x & 63) == 0) *flag = 1;
+}
+
 // the block's code sum into *out (every thread of the 4-wave block calls it)
 OMQ_DEV void block_qsum(int qs, int32_t* out) {
   __shared__ int s_qs[4];
@@ -65,6 +76,7 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd(RowQuantFwd a) {
 
   float vmax = -FLT_MAX, vmin = FLT_MAX, dot = 0.f;
   int imax = 0x7fffffff, imin = 0x7fffffff;
+  bool nf = false;
   for (int64_t c = (int64_t)tid * 4; c < cols; c += 4 * kThreads) {
     float v[4];
     load4(xr, XDT, c, v);
@@ -73,9 +85,11 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd(RowQuantFwd a) {
       float xt = let_x(v[j], a.let_mode, a.s, a.delta, c + j);
       if (xt > vmax || imax == 0x7fffffff) { vmax = xt; imax = (int)(c + j); }
       if (xt < vmin || imin == 0x7fffffff) { vmin = xt; imin = (int)(c + j); }
+      nf |= !__builtin_isfinite(xt);
       if (a.fold_delta) dot = fmaf(a.fold_delta[c + j], v[j], dot);
     }
   }
+  if (a.nonfinite) flag_nonfinite(a.nonfinite, nf);
   wave_argmax(vmax, imax);
   wave_argmin(vmin, imin);
   dot = wave_sum(dot);
@@ -101,8 +115,8 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd(RowQuantFwd a) {
   if (tid == 0) {
     if (a.h) a.h[r] = q.h;
     if (a.z) a.z[r] = q.z;
-    if (a.amax) a.amax[r] = iM;
-    if (a.amin) a.amin[r] = im;
+    if (a.amax) a.amax[r] = col_in(iM, cols);
+    if (a.amin) a.amin[r] = col_in(im, cols);
     if (a.bias_out) a.bias_out[r] = (a.bias ? a.bias[r] : 0.f) + D;
   }
   const float rh = 1.f / q.h;
@@ -166,6 +180,17 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_reg(RowQuantFwd a) {
       }
     }
   }
+  if (a.nonfinite) {
+    bool nf = false;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int64_t c = ((int64_t)k * kThreads + tid) * 4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (c + j < cols) nf |= !__builtin_isfinite(xt[k][j]);
+    }
+    flag_nonfinite(a.nonfinite, nf);
+  }
   wave_argmax(vmax, imax);
   wave_argmin(vmin, imin);
   dot = wave_sum(dot);
@@ -191,8 +216,8 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_reg(RowQuantFwd a) {
   if (tid == 0) {
     if (a.h) a.h[r] = q.h;
     if (a.z) a.z[r] = q.z;
-    if (a.amax) a.amax[r] = iM;
-    if (a.amin) a.amin[r] = im;
+    if (a.amax) a.amax[r] = col_in(iM, cols);
+    if (a.amin) a.amin[r] = col_in(im, cols);
     if (a.bias_out) a.bias_out[r] = (a.bias ? a.bias[r] : 0.f) + D;
   }
   const float rh = 1.f / q.h;
@@ -351,6 +376,17 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_blk8(RowQuantFwd a) {
       }
     }
   }
+  if (a.nonfinite) {
+    bool nf = false;
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      const int64_t c = ((int64_t)k * kThreads + tid) * 8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (c + j < cols) nf |= !__builtin_isfinite(xt[k][j]);
+    }
+    flag_nonfinite(a.nonfinite, nf);
+  }
   wave_argmax(vmax, imax);
   wave_argmin(vmin, imin);
   dot = wave_sum(dot);
@@ -376,8 +412,8 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_blk8(RowQuantFwd a) {
   if (tid == 0) {
     if (a.h) a.h[r] = q.h;
     if (a.z) a.z[r] = q.z;
-    if (a.amax) a.amax[r] = iM;
-    if (a.amin) a.amin[r] = im;
+    if (a.amax) a.amax[r] = col_in(iM, cols);
+    if (a.amin) a.amin[r] = col_in(im, cols);
     if (a.bias_out) a.bias_out[r] = (a.bias ? a.bias[r] : 0.f) + D;
   }
   // rint(x~ / h) as in the whole-row LDS kernel: reciprocal product, exact quotient
@@ -490,6 +526,17 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_wave(RowQuantFwd a) {
       }
     }
   }
+  if (a.nonfinite) {
+    bool nf = false;
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      const int64_t c = ((int64_t)k * 64 + lane) * 8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (FULL || c + j < cols) nf |= !__builtin_isfinite(xt[k][j]);
+    }
+    flag_nonfinite(a.nonfinite, nf);
+  }
   wave_argmax(vmax, imax);
   wave_argmin(vmin, imin);
   dot = wave_sum(dot);
@@ -499,8 +546,8 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_wave(RowQuantFwd a) {
   if (lane == 0) {
     if (a.h) a.h[r] = q.h;
     if (a.z) a.z[r] = q.z;
-    if (a.amax) a.amax[r] = imax;
-    if (a.amin) a.amin[r] = imin;
+    if (a.amax) a.amax[r] = col_in(imax, a.cols);
+    if (a.amin) a.amin[r] = col_in(imin, a.cols);
     if (a.bias_out) a.bias_out[r] = (a.bias ? a.bias[r] : 0.f) + dot;
   }
   // rint(x~ / h) for every element by the reciprocal product, then the exact
@@ -725,6 +772,7 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_lds(RowQuantFwd a) {
   // visited in increasing order; chunk 0 seeds the lane's values)
   float vmax, vmin, dot = 0.f;
   int imax, imin;
+  bool nf = false;
   {
     float xt[8];
     chunk(0, xt, dot, true);
@@ -734,6 +782,10 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_lds(RowQuantFwd a) {
     for (int j = 1; j < 8; ++j) {
       if (xt[j] > vmax) { vmax = xt[j]; imax = lane * 8 + j; }
       if (xt[j] < vmin) { vmin = xt[j]; imin = lane * 8 + j; }
+    }
+    if (a.nonfinite) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) nf |= !__builtin_isfinite(xt[j]);
     }
   }
   // (two chunks per iteration: unrolling all of them would hoist every chunk's loads
@@ -748,7 +800,12 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_lds(RowQuantFwd a) {
       if (xt[j] > vmax) { vmax = xt[j]; imax = c + j; }
       if (xt[j] < vmin) { vmin = xt[j]; imin = c + j; }
     }
+    if (a.nonfinite) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) nf |= !__builtin_isfinite(xt[j]);
+    }
   }
+  if (a.nonfinite) flag_nonfinite(a.nonfinite, nf);
   wave_argmax(vmax, imax);
   wave_argmin(vmin, imin);
   dot = wave_sum(dot);
@@ -758,8 +815,8 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_lds(RowQuantFwd a) {
   if (lane == 0) {
     if (a.h) a.h[r] = q.h;
     if (a.z) a.z[r] = q.z;
-    if (a.amax) a.amax[r] = imax;
-    if (a.amin) a.amin[r] = imin;
+    if (a.amax) a.amax[r] = col_in(imax, a.cols);
+    if (a.amin) a.amin[r] = col_in(imin, a.cols);
     if (a.bias_out) a.bias_out[r] = (a.bias ? a.bias[r] : 0.f) + dot;
   }
   // pass 2: rint(x~ / h) by the reciprocal product.  u = x~ rh lies within 3 ulp of
@@ -828,6 +885,7 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_g128(RowQuantFwd a) {
   float xt[8];
   float vmax = -FLT_MAX, vmin = FLT_MAX;
   int imax = 0x7fffffff, imin = 0x7fffffff;
+  bool nf = false;
   if (pv) {
     float v[8];
     load8(xr, XDT, c, v);
@@ -850,8 +908,10 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_g128(RowQuantFwd a) {
     for (int j = 0; j < 8; ++j) {
       if (xt[j] > vmax || imax == 0x7fffffff) { vmax = xt[j]; imax = (int)(c + j); }
       if (xt[j] < vmin || imin == 0x7fffffff) { vmin = xt[j]; imin = (int)(c + j); }
+      nf |= !__builtin_isfinite(xt[j]);
     }
   }
+  if (a.nonfinite) flag_nonfinite(a.nonfinite, nf);
 #pragma unroll
   for (int o = 8; o > 0; o >>= 1) {
     const float v2 = __shfl_xor(vmax, o, kWave);
@@ -868,8 +928,8 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_g128(RowQuantFwd a) {
   if ((lane & 15) == 0) {
     if (a.h) a.h[p] = q.h;
     if (a.z) a.z[p] = q.z;
-    if (a.amax) a.amax[p] = imax;
-    if (a.amin) a.amin[p] = imin;
+    if (a.amax) a.amax[p] = col_in(imax, a.cols);
+    if (a.amin) a.amin[p] = col_in(imin, a.cols);
   }
   const float rh = 1.f / q.h;
   float o[8];

@@ -44,24 +44,27 @@ def test_validation_before_launch():
     L = omq.lib()
     # missing required pointer
     assert L.omq_lwc_fakequant(None, 1, 4, 8, 0, 4, FAKE, FAKE, None, None, None, FAKE, 1, FAKE,
-                               FAKE, FAKE, FAKE, None, None, None) == -1
+                               FAKE, FAKE, FAKE, None, None, None, None) == -1
     # bit width out of range
     assert L.omq_lwc_fakequant(FAKE, 1, 4, 8, 0, 9, FAKE, FAKE, None, None, None, FAKE, 1, FAKE,
-                               FAKE, FAKE, FAKE, None, None, None) == -1
+                               FAKE, FAKE, FAKE, None, None, None, None) == -1
     assert L.omq_act_quant(FAKE, 1, 4, 8, 1, 0, None, None, FAKE, 1, FAKE, FAKE, FAKE, FAKE,
-                           None, None) == -1
+                           None, None, None) == -1
     # bad dtype
     assert L.omq_act_quant(FAKE, 7, 4, 8, 4, 0, None, None, FAKE, 1, FAKE, FAKE, FAKE, FAKE,
-                           None, None) == -3
+                           None, None, None) == -3
     # LET mode without s
     assert L.omq_act_quant(FAKE, 1, 4, 8, 4, 1, None, None, FAKE, 1, FAKE, FAKE, FAKE, FAKE,
-                           None, None) == -1
+                           None, None, None) == -1
     # row length not a multiple of 4
     assert L.omq_act_quant(FAKE, 1, 4, 10, 4, 0, None, None, FAKE, 1, FAKE, FAKE, FAKE, FAKE,
-                           None, None) == -4
+                           None, None, None) == -4
+    # misaligned input-health flag
+    assert L.omq_act_quant(FAKE, 1, 4, 8, 4, 0, None, None, FAKE, 1, FAKE, FAKE, FAKE, FAKE,
+                           None, FAKE + 2, None) == -4
     # misaligned pointer
     assert L.omq_act_quant(FAKE + 2, 1, 4, 8, 4, 0, None, None, FAKE, 1, FAKE, FAKE, FAKE, FAKE,
-                           None, None) == -4
+                           None, None, None) == -4
     # bf16 GEMM needs K % 8 == 0
     assert L.omq_gemm(4, 4, 12, FAKE, 12, 0, FAKE, 12, 0, 1, None, 1.0, FAKE, 4, 0, None) == -4
     assert L.omq_gemm(4, 4, 16, FAKE, 8, 0, FAKE, 16, 0, 1, None, 1.0, FAKE, 4, 0, None) == -2
@@ -79,9 +82,9 @@ def test_validation_before_launch():
     assert L.omq_code_rowsum(FAKE, 4, 32, 16, FAKE, None) == -2
     # unsupported LWC group (only per channel or 128 input channels)
     assert L.omq_lwc_fakequant(FAKE, 1, 4, 256, 64, 4, FAKE, FAKE, None, None, None, FAKE, 1,
-                               FAKE, FAKE, FAKE, FAKE, None, None, None) == -2
+                               FAKE, FAKE, FAKE, FAKE, None, None, None, None) == -2
     assert L.omq_lwc_fakequant(FAKE, 1, 4, 200, 128, 4, FAKE, FAKE, None, None, None, FAKE, 1,
-                               FAKE, FAKE, FAKE, FAKE, None, None, None) == -2
+                               FAKE, FAKE, FAKE, FAKE, None, None, None, None) == -2
     # workspace too small
     assert L.omq_lwc_backward(FAKE, FAKE, 1, 8, 8, 0, 4, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
                               None, FAKE, FAKE, None, None, FAKE, 16, None) == -5
@@ -157,13 +160,13 @@ def test_empty_outputs_return_ok_without_touching_pointers():
     they run here, where there is no GPU (NULL pointers: nothing is dereferenced)."""
     L = omq.lib()
     assert L.omq_act_quant(None, 1, 0, 8, 4, 0, None, None, None, 1, None, None, None, None,
-                           None, None) == 0
+                           None, None, None) == 0
     assert L.omq_lwc_fakequant(None, 1, 0, 8, 0, 4, None, None, None, None, None, None, 1,
-                               None, None, None, None, None, None, None) == 0
+                               None, None, None, None, None, None, None, None) == 0
     assert L.omq_gemm(0, 4, 16, None, 16, 0, None, 16, 0, 1, None, 1.0, None, 4, 0, None) == 0
     assert L.omq_gemm(4, 0, 16, None, 16, 0, None, 16, 0, 1, None, 1.0, None, 0, 0, None) == 0
     assert L.omq_code_gemm(0, 4, 16, None, 16, None, None, None, None, 16, None, None, None,
                            None, None, 4, None) == 0
     # negative sizes stay errors
     assert L.omq_act_quant(None, 1, -1, 8, 4, 0, None, None, None, 1, None, None, None, None,
-                           None, None) != 0
+                           None, None, None) != 0

@@ -475,3 +475,55 @@ def test_lwc_degenerate_rows(c_in):
             assert np.array_equal(host(r["z"]), ref.z), (same, nbits)
             assert np.array_equal(host(r["codes"]), ref.codes), (same, nbits)
             assert np.array_equal(host(r["W_hat"]), ref.W_hat), (same, nbits)
+
+
+@pytest.mark.parametrize("kind,rows,cols,dt", [
+    ("act", 64, 200, "f32"), ("act", 64, 1024, "bf16"), ("act", 40, 4096, "f32"),
+    ("act", 24, 11008, "bf16"), ("act", 16, 6000, "f32"),
+    ("lwc", 48, 4096, "bf16"), ("lwc", 33, 1032, "bf16"), ("lwc_g128", 40, 1024, "bf16")])
+def test_nonfinite_flag(kind, rows, cols, dt):
+    """The input-health flag: a row holding one NaN and a row holding one infinity set
+    it (every quantizer kernel variant: the widths pick them); every other row's
+    codes, dequantized values, h, z and extreme-value columns are bit-identical to
+    those of the same input with the two rows made finite, which leaves the flag at
+    zero; the bad rows' extreme-value columns still name columns of their row."""
+    log("nonfinite", kind, rows, cols, dt)
+    rng = np.random.default_rng(rows + cols)
+    X = (rng.standard_normal((rows, cols)) * 0.5).astype(F32)
+    if dt == "bf16":
+        X = synth.to_bf16(X)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    bad = X.copy()
+    bad[3, cols // 3] = np.nan
+    bad[7, cols - 1] = np.inf
+    group = 128 if kind == "lwc_g128" else 0
+    nrows = rows * (cols // 128 if group else 1)
+    ag = dev(rng.uniform(2.0, 5.0, nrows).astype(F32))
+    ab = dev(rng.uniform(2.0, 5.0, nrows).astype(F32))
+    s = dev(rng.uniform(0.7, 1.4, cols).astype(F32))
+
+    def run(A):
+        flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+        if kind == "act":
+            r = omq.act_quant(dev(A, tdt), 4, omq.LET_DIV, s, None, want_codes=True,
+                              nonfinite=flag)
+            out = (r["X_hat"], r["h"], r["z"], r["arg_max"], r["arg_min"], r["codes"])
+        else:
+            r = omq.lwc_fakequant(dev(A, tdt), ag, ab, 3, s, out_dtype=torch.bfloat16,
+                                  want_codes=True, group=group, nonfinite=flag)
+            out = (r["W_hat"], r["h"], r["z"], r["arg_max"], r["arg_min"], r["codes"])
+        torch.cuda.synchronize()
+        return int(host(flag)[0]), [host(t) for t in out]
+
+    f_good, good = run(X)
+    f_bad, badr = run(bad)
+    assert f_good == 0 and f_bad == 1
+    ok = np.ones(rows, bool)
+    ok[[3, 7]] = False
+    per = cols // 128 if group else 1
+    okq = np.repeat(ok, per)
+    for name, a, b in zip(("x_hat", "h", "z", "arg_max", "arg_min", "codes"), good, badr):
+        sel = okq if a.ndim == 1 else ok
+        assert np.array_equal(np.asarray(a)[sel], np.asarray(b)[sel]), name
+    for am in (badr[3], badr[4]):
+        assert ((am >= 0) & (am < cols)).all()
