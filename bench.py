@@ -20,7 +20,13 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-METRIC = "LWC+LET block fwd+bwd calib steps/s & TFLOP/s, LLaMA-7B-shaped, W4A4, 1 GPU"
+def metric_of(c):
+    """The metric string of a block workload, from its own shape and bit widths (the
+    7B-shaped W4A4 block's is the headline metric above)."""
+    shape = "LLaMA-2-70B-shaped" if c.d == 8192 else "LLaMA-7B-shaped"
+    bits = "W%dA%d" % (c.wbits, c.abits) + ("g%d" % c.group if c.group else "")
+    part = "FFN" if c.ffn_only else "block"
+    return "LWC+LET %s fwd+bwd calib steps/s & TFLOP/s, %s, %s, 1 GPU" % (part, shape, bits)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 matrix-core peak
 PEAK_HBM_GBS = 8000.0
@@ -69,11 +75,13 @@ def measured_traffic(workload):
 
 
 def cpu_baseline(c, inp, tokens):
-    """The oracle (never tuned for speed) on a bounded sample of the workload:
-    the same block with only `tokens` of the 2048 tokens, one full step
-    (forward, MSE, backward, AdamW); steps/s scaled linearly to the full token
-    count (the weight-side quantizer work does not shrink with tokens, so this
-    understates the oracle's full-size time per token only mildly)."""
+    """The oracle (never tuned for speed) on a bounded sample of the workload: one
+    full step (forward, MSE, backward, AdamW) of the same block on `tokens` tokens
+    (by default all of them: the workload's own step, about 20 s on 16 cores).  With
+    fewer tokens the rate is scaled linearly to the full count, which is only an
+    estimate: the weight-side quantizer work does not shrink with the tokens (the
+    scaled rate then understates the full-size one) while attention grows with their
+    square (it then overstates it)."""
     import numpy as np
     import synth
     from oracle import block as ob
@@ -99,11 +107,16 @@ def cpu_baseline(c, inp, tokens):
     optim.adamw(vec, gv, z, z, 1, c.lr_let)
     dt = time.perf_counter() - t0
     sec_full = dt * (c.T / tokens)
+    if tokens == c.T:
+        sample = ("one oracle step (fwd+MSE+bwd+AdamW) of the whole workload (%d tokens, "
+                  "all weights full size): %.1f s measured" % (c.T, dt))
+    else:
+        sample = ("one oracle step (fwd+MSE+bwd+AdamW) on %d of %d tokens, all weights full "
+                  "size; %.1f s measured, scaled x%.2f to the full token count (an estimate: "
+                  "weight-side work does not scale with tokens, attention scales with their "
+                  "square)" % (tokens, c.T, dt, c.T / tokens))
     return {"value": 1.0 / sec_full, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
-            "sample": "one oracle step (fwd+MSE+bwd+AdamW) on %d of %d tokens, all weights "
-                      "full size; %.1f s measured, scaled x%d to the full token count"
-                      % (tokens, c.T, dt, c.T // tokens),
-            "host": platform.processor() or platform.machine()}
+            "sample": sample, "host": platform.processor() or platform.machine()}
 
 
 DECODE_WORKLOADS = {"llama7b_w4a16g128_decode": 1, "llama7b_w4a16g128_decode_t16": 16}
@@ -369,7 +382,8 @@ def main():
                     help="blocks timed by the whole-model calibration workload")
     ap.add_argument("--calib-samples", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="tokens of the oracle's timed step (0: the workload's own count)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (known bytes) to calibrate the "
                          "FETCH_SIZE / WRITE_SIZE counters")
@@ -425,7 +439,9 @@ def main():
     dtheta = torch.zeros_like(theta)
     m = torch.zeros_like(theta)
     v = torch.zeros_like(theta)
-    loss = torch.zeros(1, dtype=torch.float32, device=dev)
+    # the loss of every step (warm-up and timed) lands in its own slot: no host sync
+    losses = torch.zeros(args.warmup + 2 * args.steps + 1, dtype=torch.float32, device=dev)
+    slots = [losses[i:i + 1] for i in range(losses.numel())]
     ws = torch.empty(omq.block_workspace_size(d), dtype=torch.uint8, device=dev)
     y_t = torch.empty(c.T, c.d, dtype=torch.float32, device=dev)
 
@@ -441,26 +457,25 @@ def main():
     step = 0
     for _ in range(args.warmup):
         step += 1
-        omq.block_step(d, x, y_t, W, theta, dtheta, m, v, step, loss, ws)
+        omq.block_step(d, x, y_t, W, theta, dtheta, m, v, step, slots[step - 1], ws)
     torch.cuda.synchronize()
-    loss_first = float(loss.cpu()[0]) if args.warmup else None
 
     t0 = time.perf_counter()
     e0.record()
     for _ in range(args.steps):
         step += 1
-        omq.block_step(d, x, y_t, W, theta, dtheta, m, v, step, loss, ws)
+        omq.block_step(d, x, y_t, W, theta, dtheta, m, v, step, slots[step - 1], ws)
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / args.steps
-    loss_last = float(loss.cpu()[0])
+    loss_curve = [round(float(l), 6) for l in losses[:step].cpu()]
     # the same number of steps again with per-launch events (outside the timed
     # region, so the event records do not weigh on `value`)
     timer.reset()
     for _ in range(args.steps):
         step += 1
-        omq.block_step(dt_, x, y_t, W, theta, dtheta, m, v, step, loss, ws)
+        omq.block_step(dt_, x, y_t, W, theta, dtheta, m, v, step, slots[step - 1], ws)
     torch.cuda.synchronize()
     durs = timer.durations_ms()
     kinds = timer.kinds()
@@ -503,10 +518,10 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(c, inp, min(args.cpu_tokens, c.T))
+        cpu = cpu_baseline(c, inp, min(args.cpu_tokens or c.T, c.T))
 
     out = {
-        "metric": METRIC,
+        "metric": metric_of(c),
         "value": round(sps, 4),
         "unit": "steps/s",
         "n_gpus": 1,
@@ -526,8 +541,10 @@ def main():
         "step_tflop": round(step_flops(c) / 1e12, 4),
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
         "fp_target_ms": round(fp_ms, 3),
-        "loss_first_warmup": loss_first,
-        "loss_last": loss_last,
+        "loss_per_step": loss_curve,
+        "loss_note": "the loss before each step's update, warm-up steps first, from the "
+                     "initialization (logits 4, s 1, delta 0, s_a 1) on one repeated sample; "
+                     "the oracle's own trajectory rises the same way after a few steps",
         "roofline": {
             "kernel": "k_gemm_bf16 (the bf16 matrix-core GEMM launches of the timed steps)",
             "bound": "mfma",
