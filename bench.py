@@ -302,6 +302,90 @@ def export_main(args):
     print(json.dumps(out), flush=True)
 
 
+GEMM_WORKLOADS = {"llama7b_step_gemms": "BLOCK_CFG4"}
+
+
+def gemm_main(args):
+    """The matrix products of one 7B-shaped W4A4 calibration step, each alone: the
+    backward's eight bf16 products through omq_gemm (main loop only, no fused
+    straight-through epilogue) beside torch.matmul (hipBLASLt) on the same operand
+    layouts, and the forward's four products on int8 codes through omq_code_gemm.
+    Per shape: the mean of `steps` launches after `warmup`, on HIP events."""
+    import torch
+    import post_quantization_amd as omq
+    import synth
+
+    c = getattr(synth, GEMM_WORKLOADS[args.workload])
+    T, d, F = c.T, c.d, c.F
+    nqkv = (c.n_q + 2 * c.n_kv) * c.head_dim
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    # (name, M, N, K, trans_a, trans_b): C[M x N] = op(A) op(B)^T; backward dX = dY W_hat
+    # (rows = tokens), dW = dY^T X_hat (rows = output channels, both operands K-major)
+    bwd = [("dX_down", T, F, d, 0, 1), ("dX_gate_up", T, d, 2 * F, 0, 1),
+           ("dX_o", T, d, d, 0, 1), ("dX_qkv", T, d, nqkv, 0, 1),
+           ("dW_down", d, F, T, 1, 1), ("dW_gate_up", 2 * F, d, T, 1, 1),
+           ("dW_o", d, d, T, 1, 1), ("dW_qkv", nqkv, d, T, 1, 1)]
+    fwd = [("Y_qkv", T, nqkv, d), ("Y_o", T, d, d), ("Y_gate_up", T, 2 * F, d), ("Y_down", T, d, F)]
+
+    def timeit(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    rows, tot_o, tot_t, flops = [], 0.0, 0.0, 0.0
+    for name, M, N, K, ta, tb in bwd:
+        A = torch.randn((K, M) if ta else (M, K), generator=g, device=dev).to(torch.bfloat16)
+        B = torch.randn((K, N) if tb else (N, K), generator=g, device=dev).to(torch.bfloat16)
+        C = torch.empty(M, N, dtype=torch.float32, device=dev)
+        f = 2.0 * M * N * K
+        t_o = timeit(lambda: omq.gemm(A, B, C=C, trans_a=bool(ta), trans_b=bool(tb)))
+        At, Bt = (A.t() if ta else A), (B if tb else B.t())
+        t_t = timeit(lambda: torch.matmul(At, Bt))
+        tot_o += t_o
+        tot_t += t_t
+        flops += f
+        rows.append({"product": name, "M": M, "N": N, "K": K, "omq_us": round(t_o * 1e3, 1),
+                     "omq_tflops": round(f / t_o / 1e9, 1), "hipblaslt_us": round(t_t * 1e3, 1),
+                     "hipblaslt_tflops": round(f / t_t / 1e9, 1)})
+    codes = []
+    for name, M, N, K in fwd:
+        qa = torch.randint(0, 16, (M, K), generator=g, dtype=torch.uint8, device=dev)
+        qb = torch.randint(0, 16, (N, K), generator=g, dtype=torch.uint8, device=dev)
+        ha, hb = torch.rand(M, device=dev), torch.rand(N, device=dev)
+        za, zb = torch.full((M,), 7.0, device=dev), torch.full((N,), 8.0, device=dev)
+        sa, sb = omq.code_rowsum(qa), omq.code_rowsum(qb)
+        C = torch.empty(M, N, dtype=torch.float32, device=dev)
+        t = timeit(lambda: omq.code_gemm(qa, ha, za, qb, hb, zb, sa, sb, C=C))
+        codes.append({"product": name, "M": M, "N": N, "K": K, "omq_us": round(t * 1e3, 1),
+                      "omq_tops": round(2.0 * M * N * K / t / 1e9, 1)})
+    tf = flops / tot_o / 1e9
+    out = {
+        "metric": "bf16 matrix-core TFLOP/s of the backward products of one LLaMA-7B-shaped W4A4 "
+                  "calibration step (main loops alone), 1 GPU",
+        "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(tot_o, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "T": T, "d": d, "F": F},
+        "roofline": {"kernel": "k_gemm_bf16 main loop (omq_gemm)", "bound": "mfma",
+                     "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "hipblaslt_ms": round(tot_t, 4),
+        "hipblaslt_tflops": round(flops / tot_t / 1e9, 2),
+        "products": rows, "code_products": codes, "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 CALIB_WORKLOADS = {"llama7b_w4a4_model_calib": ("BLOCK_CFG4", 32, 20)}
 
 
@@ -377,7 +461,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama7b_block_w4a4",
                     choices=list(workloads()) + list(DECODE_WORKLOADS) +
-                    list(EXPORT_WORKLOADS) + list(CALIB_WORKLOADS))
+                    list(EXPORT_WORKLOADS) + list(CALIB_WORKLOADS) + list(GEMM_WORKLOADS))
     ap.add_argument("--calib-blocks", type=int, default=2,
                     help="blocks timed by the whole-model calibration workload")
     ap.add_argument("--calib-samples", type=int, default=128)
@@ -406,6 +490,9 @@ def main():
         return
     if args.workload in CALIB_WORKLOADS:
         calib_main(args)
+        return
+    if args.workload in GEMM_WORKLOADS:
+        gemm_main(args)
         return
 
     if args.copy_calibration:

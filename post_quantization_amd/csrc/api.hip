@@ -525,7 +525,7 @@ int omq_qlinear_bwd(const omq_qlinear_desc* d, const void* X, const void* W, con
       a.a_gamma = theta; a.a_beta = theta + rq; a.g_agamma = g_ag; a.g_abeta = g_ab;
       a.col_mode = se.col_mode; a.out0 = g_s; a.out1 = g_d; a.group = grp;
       OMQ_HIP_CHECK(launch_ste_finish(a, (int)ntl, colpart, a, grp ? 1 : (int)nsl, rowpart,
-                                      w.rq + ste_records_offset(co, ci, nsl, ntl), st));
+                                      kSteTileRows, st));
     }
     if (dX || s) {
       gemm_ste_extents(T, ci, &nsl, &ntl);
@@ -547,7 +547,7 @@ int omq_qlinear_bwd(const omq_qlinear_desc* d, const void* X, const void* W, con
       x.col_mode = se.col_mode; x.gx = g.C; x.ldgx = ci; x.out0 = g_s; x.out1 = g_d;
       x.accumulate = 1;
       OMQ_HIP_CHECK(launch_ste_finish(x, (int)ntl, colpart, x, (int)nsl, rowpart,
-                                      w.rq + ste_records_offset(T, ci, nsl, ntl), st));
+                                      kSteTileRows, st));
     }
     return OMQ_OK;
   }

@@ -648,7 +648,7 @@ hipError_t lin_bwd_fused(const Ws& w, const LinBwd& L, int64_t T, int wbits, int
     if (grouped) b.group = L.group;
     // the row finalizers, then the column sums with their scatter terms (both into gs_w)
     if ((e = launch_ste_finish(a, (int)ntl, colpart, b, grouped ? 1 : (int)nsl, rowpart,
-                               w.rq + ste_records_offset(N, K, nsl, ntl), st)) != hipSuccess)
+                               kSteTileRows, st)) != hipSuccess)
       return e;
   }
   // activation side
@@ -672,8 +672,7 @@ hipError_t lin_bwd_fused(const Ws& w, const LinBwd& L, int64_t T, int wbits, int
   a.h = L.ast.h; a.z = L.ast.z; a.amax = L.ast.amax; a.amin = L.ast.amin;
   a.col_mode = acol; a.gx = L.gx_out; a.ldgx = K;
   a.out0 = L.gs_x; a.out1 = L.gd_x; a.accumulate = 1;
-  return launch_ste_finish(a, (int)ntl, colpart, a, (int)nsl, rowpart,
-                           w.rq + ste_records_offset(T, K, nsl, ntl), st);
+  return launch_ste_finish(a, (int)ntl, colpart, a, (int)nsl, rowpart, kSteTileRows, st);
 }
 
 int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w,

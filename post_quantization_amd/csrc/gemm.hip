@@ -899,7 +899,7 @@ bool dma_fits(const Gemm& g, int BM, int BN, int KB = BK) {
 
 // the straight-through epilogue runs on 128 x 128 tiles of 4 waves (64-row blocks,
 // 64-column slabs), for the two layouts the backward uses
-constexpr int kSteBM = 128, kSteBN = 128, kSteWM = 2, kSteWN = 2;
+constexpr int kSteBM = kSteTileRows, kSteBN = 128, kSteWM = 2, kSteWN = 2;
 
 template <int EPI>
 void launch_ste_x(const Gemm& g, hipStream_t st) {

@@ -88,17 +88,17 @@ size_t rowquant_bwd_ws_bytes(int64_t rows, int64_t cols);
 hipError_t launch_rowquant_bwd(const RowQuantBwd& a, hipStream_t st);
 // Finalizers of the straight-through backward, shared by the tile pass and the
 // GEMM-epilogue form.  Partials: rowpart [rows][nslabs][2] (g_h, sum g (1 - in)),
-// colpart [ntiles][2][cols], then the row finalizers' scatter records (offset
-// ste_records_offset).  launch_ste_finish runs the row finalizers of rf (LWC-logit
-// gradients, the max/min scatter into rf.gx, one scatter record per row and
-// extreme) and then the column pass of cf: out0 / out1 = (cf.accumulate ? their
-// contents : 0) + the column partials + the records, every sum in a fixed order
-// (no atomics: a step is bitwise reproducible).
+// colpart [ntiles][2][cols], one column-partial row per tile of tile_rows rows.
+// launch_ste_finish runs the row finalizers of rf (LWC-logit gradients, the max/min
+// scatter into rf.gx, and the scatter terms of the column outputs, which each tile
+// adds to its own column partials in row order) and then the column pass of cf:
+// out0 / out1 = (cf.accumulate ? their contents : 0) + the column partials, every
+// sum in a fixed order (no atomics: a step is bitwise reproducible).
+constexpr int kSteTileRows = 128;   // rows per column-partial tile of the GEMM epilogues
 size_t ste_partials_floats(int64_t rows, int64_t cols, int64_t nslabs, int64_t ntiles);
-int64_t ste_records_offset(int64_t rows, int64_t cols, int64_t nslabs, int64_t ntiles);
-hipError_t launch_ste_finish(const RowQuantBwd& cf, int ntiles, const float* colpart,
+hipError_t launch_ste_finish(const RowQuantBwd& cf, int ntiles, float* colpart,
                              const RowQuantBwd& rf, int nslabs, const float* rowpart,
-                             float* records, hipStream_t st);
+                             int tile_rows, hipStream_t st);
 
 // LET alone: y = (x - delta) / s  or  y = s * x, elementwise over [rows x cols].
 hipError_t launch_let_elementwise(const void* x, int x_dt, int64_t rows, int64_t cols,

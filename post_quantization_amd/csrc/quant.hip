@@ -11,6 +11,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <algorithm>
+
 #include <float.h>
 
 namespace omq {
@@ -1126,51 +1128,14 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_bwd_tile(RowQuantBwd a, i
   }
 }
 
-// Scatter records of the row finalizers: for quantizer row p, entry 2p (its
-// argmax) and 2p + 1 (its argmin) give the column and the terms the column outputs
-// take there (v0 for out0, v1 for out1); the column pass adds them in row order.
-struct SteRec {
-  int32_t* col = nullptr;
-  float* v0 = nullptr;
-  float* v1 = nullptr;
-};
-
-inline SteRec ste_rec(float* base, int64_t nq) {
-  SteRec r;
-  if (base) {
-    r.col = reinterpret_cast<int32_t*>(base);
-    r.v0 = base + 2 * nq;
-    r.v1 = base + 4 * nq;
-  }
-  return r;
-}
-
-// row finalize: LPR lanes per quantizer row sum its per-slab partials (coalesced
-// reads, then a shuffle reduction), one of them finishes the row: LWC-logit
-// gradients, the max/min scatter into the upstream gradient (one writer per row),
-// and the scatter records of the column outputs (no atomics).
-template <int XDT, int LPR>
-OMQ_DEV void rows_final(const RowQuantBwd& a, int nslabs, const float* rowpart, int64_t blk,
-                        SteRec rec) {
-  // quantizer rows: rows, or (row, group) pairs p = row * ng + group
+// One quantizer row's finalizer: the LWC-logit gradients, the max / min scatter into
+// the upstream gradient (one writer per row), and the row's two scatter terms of the
+// column outputs (column, term for out0, term for out1: argmax first, then argmin).
+// gh, gzs: the row's summed partials.
+template <int XDT>
+OMQ_DEV void row_finish(const RowQuantBwd& a, int64_t p, float gh, float gzs, int (&cs)[2],
+                        float (&v0)[2], float (&v1)[2]) {
   const int64_t ng = a.group > 0 ? a.cols / 128 : 1;
-  const int64_t p = (blk * kThreads + threadIdx.x) / LPR;
-  const int sub = (int)(threadIdx.x % LPR);
-  const bool valid = p < a.rows * ng;
-  float gh = 0.f, gzs = 0.f;
-  if (valid) {
-    for (int s = sub; s < nslabs; s += LPR) {
-      const float2 v = *reinterpret_cast<const float2*>(&rowpart[(p * nslabs + s) * 2]);
-      gh += v.x;
-      gzs += v.y;
-    }
-  }
-#pragma unroll
-  for (int o = LPR / 2; o > 0; o >>= 1) {
-    gh += __shfl_xor(gh, o);
-    gzs += __shfl_xor(gzs, o);
-  }
-  if (!valid || sub != 0) return;
   const int64_t r = p / ng;
   // the row's segment (concatenated weights): its x rows and logits
   const void* xb = a.x;
@@ -1220,48 +1185,147 @@ OMQ_DEV void rows_final(const RowQuantBwd& a, int nslabs, const float* rowpart, 
       else if (a.let_mode == OMQ_LET_MUL) up = gsc * a.s[c];
       a.gx[r * a.ldgx + c] += up;
     }
-    if (rec.col) {
-      float v0 = 0.f, v1 = 0.f;
-      switch (a.col_mode) {
-        case COL_WEIGHT:
-        case COL_ACT_MUL:
-          v0 = gsc * xo[e];
-          break;
-        case COL_ACT_DIV:
-          v0 = gsc * (-xtl[e] / a.s[c]);
-          v1 = gsc * (-1.f / a.s[c]);
-          break;
-        default:
-          break;
-      }
-      rec.col[2 * p + e] = c;
-      rec.v0[2 * p + e] = v0;
-      rec.v1[2 * p + e] = v1;
+    cs[e] = c;
+    v0[e] = 0.f;
+    v1[e] = 0.f;
+    switch (a.col_mode) {
+      case COL_WEIGHT:
+      case COL_ACT_MUL:
+        v0[e] = gsc * xo[e];
+        break;
+      case COL_ACT_DIV:
+        v0[e] = gsc * (-xtl[e] / a.s[c]);
+        v1[e] = gsc * (-1.f / a.s[c]);
+        break;
+      default:
+        break;
     }
   }
 }
 
+// Row finalizers, one workgroup per (column-partial tile, column group): the tile's
+// tile_rows rows (for group-wise rows, their quantizer rows of one 128-column group)
+// in one pass, LPR lanes per row summing its per-slab partials; then the rows'
+// scatter terms of the column outputs are merged in LDS and added to the tile's
+// column partials in row order: the first of the tile's terms on a column adds, in
+// row order, every term on that column.  The tile's partials of those columns have
+// this workgroup as their only writer, so the column pass that follows sums
+// everything in a fixed order.
+constexpr int kFinThreads = 1024;
+
 template <int XDT, int LPR>
-__global__ __launch_bounds__(kThreads) void k_ste_rows(RowQuantBwd a, int nslabs,
-                                                       const float* rowpart, SteRec rec) {
-  rows_final<XDT, LPR>(a, nslabs, rowpart, blockIdx.x, rec);
+__global__ __launch_bounds__(kFinThreads) void k_ste_rows(RowQuantBwd a, int nslabs,
+                                                          const float* rowpart, int tile_rows,
+                                                          float* colpart, int merge) {
+  __shared__ int e_col[256];
+  __shared__ float e_v0[256], e_v1[256];
+  const int64_t ng = a.group > 0 ? a.cols / 128 : 1;
+  const int64_t t = blockIdx.x / ng, g = blockIdx.x % ng;
+  const int64_t r0 = t * tile_rows;
+  const int nr = (int)min((int64_t)tile_rows, a.rows - r0);
+  const int sub = (int)(threadIdx.x % LPR);
+  const int i = (int)(threadIdx.x / LPR);               // row of the tile
+  const bool valid = i < nr;
+  const int64_t p = (r0 + i) * ng + g;                  // its quantizer row
+  float gh = 0.f, gzs = 0.f;
+  if (valid) {
+    for (int s = sub; s < nslabs; s += LPR) {
+      const float2 v = *reinterpret_cast<const float2*>(&rowpart[(p * nslabs + s) * 2]);
+      gh += v.x;
+      gzs += v.y;
+    }
+  }
+#pragma unroll
+  for (int o = LPR / 2; o > 0; o >>= 1) {
+    gh += __shfl_xor(gh, o);
+    gzs += __shfl_xor(gzs, o);
+  }
+  if (valid && sub == 0) {
+    int cs[2];
+    float v0[2], v1[2];
+    row_finish<XDT>(a, p, gh, gzs, cs, v0, v1);
+    if (merge) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        e_col[2 * i + e] = cs[e];
+        e_v0[2 * i + e] = v0[e];
+        e_v1[2 * i + e] = v1[e];
+      }
+    }
+  }
+  if (!merge) return;                                   // uniform over the workgroup
+  // every row's terms are in LDS before any thread reads another thread's
+  __syncthreads();
+  // sort the terms by (column, term index): a bitonic sort of 256 keys in LDS, one per
+  // thread (the workgroup has at least 256), the unused slots keyed past every column
+  __shared__ int key[256];
+  __shared__ float sv0[256], sv1[256];
+  __shared__ int head[256];
+  const int ne = 2 * nr;
+  const int e = threadIdx.x;
+  if (e < 256) key[e] = e < ne ? (e_col[e] << 8) | e : 0x7fffffff;
+  __syncthreads();
+  for (int k = 2; k <= 256; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const int o = e ^ j;
+      if (e < 256 && o > e) {
+        const int a0 = key[e], b0 = key[o];
+        if ((a0 > b0) == ((e & k) == 0)) {
+          key[e] = b0;
+          key[o] = a0;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // a segmented inclusive scan of each column's run (fixed tree order), then the last
+  // term of each run adds the run's total to the tile's partial of that column
+  int c = -1;
+  if (e < 256) {
+    const int kv = key[e];
+    c = kv >> 8;
+    const bool real = e < ne;
+    sv0[e] = real ? e_v0[kv & 255] : 0.f;
+    sv1[e] = real ? e_v1[kv & 255] : 0.f;
+    head[e] = e == 0 || (key[e - 1] >> 8) != c;
+  }
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    float a0 = 0.f, a1 = 0.f;
+    int hd = 1;
+    if (e < 256) {
+      hd = head[e];
+      if (!hd && e >= off) {
+        a0 = sv0[e - off];
+        a1 = sv1[e - off];
+        hd = head[e - off];
+      }
+    }
+    __syncthreads();
+    if (e < 256 && !head[e] && e >= off) {
+      sv0[e] += a0;
+      sv1[e] += a1;
+      head[e] = hd;
+    }
+    __syncthreads();
+  }
+  if (e < ne && (e == ne - 1 || (key[e + 1] >> 8) != c)) {
+    colpart[(t * 2 + 0) * a.cols + c] += sv0[e];
+    colpart[(t * 2 + 1) * a.cols + c] += sv1[e];
+  }
 }
 
 // Column pass of a straight-through backward, after the row finalizers: per column c
 // (64 per workgroup, 4 waves)
-//   out_k[c] = (accumulate ? out_k[c] : 0) + sum_t colpart_k[t][c] + sum of the
-//              scatter records whose column is c
-// with every sum in a fixed order: the waves take the partial rows t = w, w + 4, ...
-// and contiguous quarters of the records (for group-wise rows only those of the
-// block's 128-column group), a batch's matches in lane order; the wave totals are
-// added in LDS in wave order.  Deterministic: no atomics anywhere.
+//   out_k[c] = (accumulate ? out_k[c] : 0) + sum_t colpart_k[t][c]
+// the waves taking the partial rows t = w, w + 4, ..., their sums added in LDS in
+// wave order.  Deterministic: no atomics anywhere.
 __global__ __launch_bounds__(kThreads) void k_ste_cols(const float* colpart, int ntiles,
                                                        int64_t cols, float* out0, float* out1,
-                                                       int accumulate, SteRec rec,
-                                                       int64_t nrows, int64_t ng) {
-  __shared__ float red[4][4][64];
+                                                       int accumulate) {
+  __shared__ float red[2][4][64];
   const int lane = threadIdx.x & 63, w = wave_id();
-  const int64_t c0 = (int64_t)blockIdx.x * 64, c = c0 + lane;
+  const int64_t c = (int64_t)blockIdx.x * 64 + lane;
   float s0 = 0.f, s1 = 0.f;
   if (c < cols) {
 #pragma unroll 4
@@ -1270,48 +1334,14 @@ __global__ __launch_bounds__(kThreads) void k_ste_cols(const float* colpart, int
       s1 += colpart[((int64_t)t * 2 + 1) * cols + c];
     }
   }
-  float a0 = 0.f, a1 = 0.f;
-  if (rec.col && nrows > 0) {
-    const int64_t g = c0 / 128;                       // the group of these columns
-    const int64_t n = 2 * nrows;                      // entries: max and min per row
-    const int64_t per = (n + 3) / 4;
-    const int64_t j0 = (int64_t)w * per, j1 = min(n, j0 + per);
-    for (int64_t jb = j0; jb < j1; jb += 64) {
-      const int64_t j = jb + lane;
-      const int64_t idx = ng > 1 ? 2 * ((j >> 1) * ng + g) + (j & 1) : j;
-      const int cj = j < j1 ? rec.col[idx] : -1;
-      const bool hit = cj >= c0 && cj < c0 + 64;
-      float v0 = 0.f, v1 = 0.f;
-      if (hit) {
-        v0 = rec.v0[idx];
-        v1 = rec.v1[idx];
-      }
-      uint64_t msk = __builtin_amdgcn_ballot_w64(hit);
-      while (msk) {
-        const int k = __builtin_ctzll(msk);
-        msk &= msk - 1;
-        const int ck = __builtin_amdgcn_readlane(cj, k) - (int)c0;
-        const float b0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v0), k));
-        const float b1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v1), k));
-        if (lane == ck) {
-          a0 += b0;
-          a1 += b1;
-        }
-      }
-    }
-  }
   red[0][w][lane] = s0;
   red[1][w][lane] = s1;
-  red[2][w][lane] = a0;
-  red[3][w][lane] = a1;
   __syncthreads();
   if (w < 2 && c < cols) {
     float* o = w == 0 ? out0 : out1;
     if (o) {
       const float cs = ((red[w][0][lane] + red[w][1][lane]) + red[w][2][lane]) + red[w][3][lane];
-      const float sc =
-          ((red[2 + w][0][lane] + red[2 + w][1][lane]) + red[2 + w][2][lane]) + red[2 + w][3][lane];
-      o[c] = (accumulate ? o[c] : 0.f) + (cs + sc);
+      o[c] = (accumulate ? o[c] : 0.f) + cs;
     }
   }
 }
@@ -1692,57 +1722,46 @@ hipError_t launch_rowquant_bwd(const RowQuantBwd& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rs = a.group > 0 ? 1 : (int)nslabs;
-  float* records = a.ws + ste_records_offset(a.rows, a.cols, (a.cols + 127) / 128, ntiles);
-  return launch_ste_finish(a, (int)ntiles, colpart, a, rs, rowpart, records, st);
+  return launch_ste_finish(a, (int)ntiles, colpart, a, rs, rowpart, R, st);
 }
 
 size_t ste_partials_floats(int64_t rows, int64_t cols, int64_t nslabs, int64_t ntiles) {
-  // row partials, column partials, then the scatter records (room for one quantizer
-  // row per 128 columns of a row: group-wise rows)
-  return (size_t)(ste_records_offset(rows, cols, nslabs, ntiles) +
-                  6 * rows * ((cols + 127) / 128)) + 64;
+  return (size_t)(nslabs * rows * 2 + ntiles * 2 * cols) + 64;
 }
 
-int64_t ste_records_offset(int64_t rows, int64_t cols, int64_t nslabs, int64_t ntiles) {
-  return ((nslabs * rows * 2 + ntiles * 2 * cols) + 63) & ~int64_t(63);
-}
-
-hipError_t launch_ste_finish(const RowQuantBwd& cf, int ntiles, const float* colpart,
+hipError_t launch_ste_finish(const RowQuantBwd& cf, int ntiles, float* colpart,
                              const RowQuantBwd& rf, int nslabs, const float* rowpart,
-                             float* records, hipStream_t st) {
+                             int tile_rows, hipStream_t st) {
   const bool cols_out = cf.col_mode != COL_NONE && (cf.out0 || cf.out1) && cf.cols > 0;
   const int64_t ng = rf.group > 0 ? rf.cols / 128 : 1;
-  const int64_t nq = (rf.nbits < 16 && rf.rows > 0) ? rf.rows * ng : 0;
-  const bool recs = cols_out && nq > 0 && rf.col_mode != COL_NONE;
-  if (recs && !records) return hipErrorInvalidValue;
-  const SteRec rec = ste_rec(recs ? records : nullptr, nq);
-  if (nq > 0) {
-    // one lane per row when it has one slab, else 16 lanes share a row's slabs
-    const int lpr = nslabs == 1 ? 1 : 16;
-    const dim3 grid((unsigned)((nq * lpr + kThreads - 1) / kThreads));
+  const bool rows = rf.nbits < 16 && rf.rows > 0;
+  if (tile_rows < 1 || tile_rows > 128) return hipErrorInvalidValue;   // 256 LDS terms
+  if (rows) {
+    const int merge = cols_out && rf.col_mode != COL_NONE;
+    // the tile's rows in one pass: one lane per row when it has one slab, else 8 lanes
+    // per row for 128-row tiles, 16 for shorter ones
+    const int lpr = nslabs == 1 ? 1 : tile_rows > 64 ? 8 : 16;
+    const int nt = std::max(256, (tile_rows * lpr + 63) / 64 * 64);
+    const int64_t units = ((rf.rows + tile_rows - 1) / tile_rows) * ng;
+    const dim3 grid((unsigned)units), block((unsigned)nt);
     const bool f32 = rf.x_dt == OMQ_F32;
-    if (lpr == 1) {
-      if (f32)
-        hipLaunchKernelGGL((k_ste_rows<OMQ_F32, 1>), grid, dim3(kThreads), 0, st, rf, nslabs,
-                           rowpart, rec);
-      else
-        hipLaunchKernelGGL((k_ste_rows<OMQ_BF16, 1>), grid, dim3(kThreads), 0, st, rf, nslabs,
-                           rowpart, rec);
-    } else {
-      if (f32)
-        hipLaunchKernelGGL((k_ste_rows<OMQ_F32, 16>), grid, dim3(kThreads), 0, st, rf, nslabs,
-                           rowpart, rec);
-      else
-        hipLaunchKernelGGL((k_ste_rows<OMQ_BF16, 16>), grid, dim3(kThreads), 0, st, rf, nslabs,
-                           rowpart, rec);
-    }
+#define OMQ_ROWS(L)                                                                          \
+  if (lpr == L) {                                                                            \
+    if (f32)                                                                                 \
+      hipLaunchKernelGGL((k_ste_rows<OMQ_F32, L>), grid, block, 0, st, rf, nslabs, rowpart,  \
+                         tile_rows, colpart, merge);                                         \
+    else                                                                                     \
+      hipLaunchKernelGGL((k_ste_rows<OMQ_BF16, L>), grid, block, 0, st, rf, nslabs, rowpart, \
+                         tile_rows, colpart, merge);                                         \
+  }
+    OMQ_ROWS(1) OMQ_ROWS(8) OMQ_ROWS(16)
+#undef OMQ_ROWS
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (!cols_out) return hipSuccess;
   hipLaunchKernelGGL(k_ste_cols, dim3((unsigned)((cf.cols + 63) / 64)), dim3(kThreads), 0, st,
-                     colpart, ntiles, cf.cols, cf.out0, cf.out1, cf.accumulate, rec,
-                     recs ? rf.rows : (int64_t)0, ng);
+                     colpart, ntiles, cf.cols, cf.out0, cf.out1, cf.accumulate);
   return hipGetLastError();
 }
 
