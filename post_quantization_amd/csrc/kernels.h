@@ -19,7 +19,8 @@ struct RowQuantFwd {
   float* h = nullptr;  float* z = nullptr;  int32_t* amax = nullptr;  int32_t* amin = nullptr;
   uint8_t* codes = nullptr;                         // [rows x cols], row stride ldq
   int64_t ldq = 0;                                  // 0: cols (multiple of 4 otherwise)
-  int code_off = 0;                                 // codes stored as q - code_off (a byte)
+  int code_off = 0;                                 // codes stored as q - code_off (a byte);
+                                                    // 0 or 128
   int32_t* qsum = nullptr;                          // per-row sum of the stored codes (group 0)
   int32_t* nonfinite = nullptr;                     // set to 1 when any x~ is NaN or infinite
   const float* fold_delta = nullptr;                // bias fold: sum_i fold_delta_i x_ri

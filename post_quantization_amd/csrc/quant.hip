@@ -55,6 +55,100 @@ OMQ_DEV void block_qsum(int qs, int32_t* out) {
 }
 
 // ---------------------------------------------------------------------------
+// chunk helpers of the whole-row forward kernels: a lane holds 8 consecutive
+// elements of x~ at a time
+// ---------------------------------------------------------------------------
+// largest and smallest of 8 values (three-operand max / min; a NaN operand is
+// passed over, as the comparisons of an element-wise scan pass it over)
+OMQ_DEV float max8(const float (&v)[8]) {
+  return fmaxf(fmaxf(fmaxf(fmaxf(v[0], v[1]), v[2]), fmaxf(fmaxf(v[3], v[4]), v[5])),
+               fmaxf(v[6], v[7]));
+}
+OMQ_DEV float min8(const float (&v)[8]) {
+  return fminf(fminf(fminf(fminf(v[0], v[1]), v[2]), fminf(fminf(v[3], v[4]), v[5])),
+               fminf(v[6], v[7]));
+}
+OMQ_DEV float wave_maxf(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+OMQ_DEV float wave_minf(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+// the first of 8 values equal to v (float comparison, so -0 == +0): its position
+// in j (8 when none is) and its own value in x
+OMQ_DEV void first_eq8(const float (&t)[8], float v, int& j, float& x) {
+  j = 8;
+#pragma unroll
+  for (int q = 7; q >= 0; --q)
+    if (t[q] == v) { j = q; x = t[q]; }
+}
+// finiteness accumulator: x * 0 is 0 for a finite x and NaN for an infinite or NaN
+// one, so acc stays finite exactly while every element is finite
+OMQ_DEV float nf_acc8(const float (&v)[8], float acc) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc = fmaf(v[j], 0.f, acc);
+  return acc;
+}
+// the codes of 8 elements: q (integer-valued floats in [0, 255]) as the bytes
+// q - off (off 0 or 128: then the byte is q xor 0x80), their sum of q added to qsum
+OMQ_DEV uint2 codes8(const float (&q)[8], bool off128, uint32_t& qsum) {
+  uint32_t lo = 0u, hi = 0u;
+  lo = __builtin_amdgcn_cvt_pk_u8_f32(q[0], 0, lo);
+  lo = __builtin_amdgcn_cvt_pk_u8_f32(q[1], 1, lo);
+  lo = __builtin_amdgcn_cvt_pk_u8_f32(q[2], 2, lo);
+  lo = __builtin_amdgcn_cvt_pk_u8_f32(q[3], 3, lo);
+  hi = __builtin_amdgcn_cvt_pk_u8_f32(q[4], 0, hi);
+  hi = __builtin_amdgcn_cvt_pk_u8_f32(q[5], 1, hi);
+  hi = __builtin_amdgcn_cvt_pk_u8_f32(q[6], 2, hi);
+  hi = __builtin_amdgcn_cvt_pk_u8_f32(q[7], 3, hi);
+  qsum = __builtin_amdgcn_udot4(lo, 0x01010101u, qsum, false);
+  qsum = __builtin_amdgcn_udot4(hi, 0x01010101u, qsum, false);
+  if (off128) {
+    lo ^= 0x80808080u;
+    hi ^= 0x80808080u;
+  }
+  return make_uint2(lo, hi);
+}
+// rint(x~ / h) of a chunk by the reciprocal product u = x~ rh, which lies within 3
+// ulp of the exact quotient: the two can round apart only within |u| 2^-20 of a
+// half-integer, and thr (the row's bound max|x~| rh 2^-20) covers every element, so a
+// chunk whose smallest distance | |u - rint u| - 1/2 | is not above thr takes the
+// exact quotient, behind a wave-uniform branch (a divergent one would be flattened
+// into a division for every element).  f = u - rint u is exact and |f| <= 1/2, so
+// that smallest distance is 1/2 - max |f| (rounding is monotone: the same float as
+// the smallest of the rounded distances).  A NaN f (u infinite or NaN) is passed
+// over: both quotients then clamp to the same code.
+OMQ_DEV void rint_quot8(const float (&xt)[8], float h, float rh, float thr, bool in,
+                        float (&rr)[8]) {
+  float fm = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float u = xt[j] * rh;
+    rr[j] = rintf(u);
+    fm = fmaxf(fm, fabsf(u - rr[j]));
+  }
+  const bool near = in && !(0.5f - fm > thr);
+  if (__builtin_amdgcn_ballot_w64(near) != 0) {
+    if (near) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) rr[j] = rintf(xt[j] / h);
+    }
+  }
+}
+// code and dequantized value of a chunk: q = clamp(r + z, 0, Q), (q - z) h
+OMQ_DEV void dequant8(const float (&rr)[8], const RowQ& q, float (&qq)[8], float (&o)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    qq[j] = __builtin_amdgcn_fmed3f(rr[j] + q.z, 0.f, q.Q);
+    o[j] = (qq[j] - q.z) * q.h;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // forward: one 256-thread block per row
 // ---------------------------------------------------------------------------
 template <int XDT>
@@ -292,8 +386,7 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_blk8(RowQuantFwd a) {
   const char* xr = reinterpret_cast<const char*>(a.x) + r * a.ldx * (XDT == OMQ_F32 ? 4 : 2);
   const int64_t cols = a.cols;
   float xt[NC][8];
-  float vmax = -FLT_MAX, vmin = FLT_MAX, dot = 0.f;
-  int imax = 0x7fffffff, imin = 0x7fffffff;
+  float dot = 0.f;
 #pragma unroll
   for (int k = 0; k < NC; ++k) {
     const int64_t c = ((int64_t)k * kThreads + tid) * 8;
@@ -366,41 +459,76 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_blk8(RowQuantFwd a) {
       }
     }
   }
-  // per-thread scan in increasing column order keeps the first index on ties
+  // per chunk its max / min; the thread keeps the first chunk holding its extreme
+  // (chunks run in increasing column order)
+  float lmax = -FLT_MAX, lmin = FLT_MAX, nfa = 0.f;
+  int kmx = -1, kmn = -1;
 #pragma unroll
   for (int k = 0; k < NC; ++k) {
     const int64_t c = ((int64_t)k * kThreads + tid) * 8;
     if (c < cols) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (xt[k][j] > vmax || imax == 0x7fffffff) { vmax = xt[k][j]; imax = (int)(c + j); }
-        if (xt[k][j] < vmin || imin == 0x7fffffff) { vmin = xt[k][j]; imin = (int)(c + j); }
-      }
+      const float cM = max8(xt[k]), cm = min8(xt[k]);
+      if (kmx < 0 || cM > lmax) { lmax = cM; kmx = k; }
+      if (kmn < 0 || cm < lmin) { lmin = cm; kmn = k; }
+      if (a.nonfinite) nfa = nf_acc8(xt[k], nfa);
     }
   }
-  if (a.nonfinite) {
-    bool nf = false;
-#pragma unroll
-    for (int k = 0; k < NC; ++k) {
-      const int64_t c = ((int64_t)k * kThreads + tid) * 8;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (c + j < cols) nf |= !__builtin_isfinite(xt[k][j]);
-    }
-    flag_nonfinite(a.nonfinite, nf);
+  if (a.nonfinite) flag_nonfinite(a.nonfinite, nfa != nfa);
+  // the row's extreme values over the block
+  __shared__ float s_ext[2][4];
+  {
+    const float wM = wave_maxf(lmax), wm = wave_minf(lmin);
+    if (lane == 0) { s_ext[0][wid] = wM; s_ext[1][wid] = wm; }
   }
-  wave_argmax(vmax, imax);
-  wave_argmin(vmin, imin);
   dot = wave_sum(dot);
+  __syncthreads();
+  float M = fmaxf(fmaxf(s_ext[0][0], s_ext[0][1]), fmaxf(s_ext[0][2], s_ext[0][3]));
+  float m = fminf(fminf(s_ext[1][0], s_ext[1][1]), fminf(s_ext[1][2], s_ext[1][3]));
+  // their first columns: the threads holding an extreme take the first equal element
+  // of their chunk (only waves with such a thread search); the others offer (the
+  // extreme, no column), so the lowest column wins and its value is kept
+  int imax = 0x7fffffff, imin = 0x7fffffff;
+  const bool hM = kmx >= 0 && lmax == M, hm = kmn >= 0 && lmin == m;
+  if (__builtin_amdgcn_ballot_w64(hM) != 0) {
+    if (hM) {
+      float t[8];
+#pragma unroll
+      for (int k = 0; k < NC; ++k)
+        if (k == kmx) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) t[j] = xt[k][j];
+        }
+      int j;
+      first_eq8(t, M, j, M);
+      if (j < 8) imax = (int)(((int64_t)kmx * kThreads + tid) * 8 + j);
+    }
+  }
+  if (__builtin_amdgcn_ballot_w64(hm) != 0) {
+    if (hm) {
+      float t[8];
+#pragma unroll
+      for (int k = 0; k < NC; ++k)
+        if (k == kmn) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) t[j] = xt[k][j];
+        }
+      int j;
+      first_eq8(t, m, j, m);
+      if (j < 8) imin = (int)(((int64_t)kmn * kThreads + tid) * 8 + j);
+    }
+  }
+  wave_argmax(M, imax);
+  wave_argmin(m, imin);
   __shared__ float s_max[4], s_min[4], s_dot[4];
   __shared__ int s_imax[4], s_imin[4];
   if (lane == 0) {
-    s_max[wid] = vmax; s_imax[wid] = imax;
-    s_min[wid] = vmin; s_imin[wid] = imin;
+    s_max[wid] = M; s_imax[wid] = imax;
+    s_min[wid] = m; s_imin[wid] = imin;
     s_dot[wid] = dot;
   }
   __syncthreads();
-  float M = s_max[0], m = s_min[0], D = s_dot[0];
+  M = s_max[0]; m = s_min[0];
+  float D = s_dot[0];
   int iM = s_imax[0], im = s_imin[0];
 #pragma unroll
   for (int w = 1; w < 4; ++w) {
@@ -418,45 +546,29 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_blk8(RowQuantFwd a) {
     if (a.amin) a.amin[r] = col_in(im, cols);
     if (a.bias_out) a.bias_out[r] = (a.bias ? a.bias[r] : 0.f) + D;
   }
-  // rint(x~ / h) as in the whole-row LDS kernel: reciprocal product, exact quotient
-  // for the chunks with an element within the row's bound of a half-integer
+  // round, clamp, dequantize and store from the registers
   const float rh = 1.f / q.h;
   const float thr = fmaxf(fabsf(M), fabsf(m)) * rh * 0x1p-20f;
-  int qs = 0;
+  const bool off128 = a.code_off != 0;
+  uint32_t qsum = 0u;
 #pragma unroll
   for (int k = 0; k < NC; ++k) {
     const int64_t c = ((int64_t)k * kThreads + tid) * 8;
     const bool in = c < cols;
     float rr[8];
-    bool near = false;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float u = xt[k][j] * rh;
-      rr[j] = rintf(u);
-      near |= in && !(fabsf(fabsf(u - rr[j]) - 0.5f) > thr);
-    }
-    if (__builtin_amdgcn_ballot_w64(near) != 0) {
-      if (near) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) rr[j] = rintf(xt[k][j] / q.h);
-      }
-    }
+    rint_quot8(xt[k], q.h, rh, thr, in, rr);
     if (in) {
       float o[8], qq[8];
-      uint32_t cw[2] = {0u, 0u};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        qq[j] = __builtin_amdgcn_fmed3f(rr[j] + q.z, 0.f, q.Q);
-        o[j] = (qq[j] - q.z) * q.h;
-        const int qi = (int)qq[j] - a.code_off;
-        cw[j >> 2] |= ((uint32_t)qi & 0xffu) << (8 * (j & 3));
-        qs += qi;
-      }
+      dequant8(rr, q, qq, o);
       store8(a.out, a.out_dt, r * a.ldo + c, o);
-      if (a.codes) *reinterpret_cast<uint2*>(a.codes + r * code_ld(a) + c) = make_uint2(cw[0], cw[1]);
+      if (a.codes) {
+        const uint2 cw = codes8(qq, off128, qsum);
+        *reinterpret_cast<uint2*>(a.codes + r * code_ld(a) + c) = cw;
+      }
     }
   }
-  if (a.qsum) block_qsum(qs, a.qsum + r);
+  // sum of the stored codes q - off over the row's columns
+  if (a.qsum) block_qsum((int)qsum - (tid == 0 ? a.code_off * (int)cols : 0), a.qsum + r);
 }
 
 // FULL: every 512-column chunk of the row is whole (cols is a multiple of 512), so
@@ -638,12 +750,16 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_wave(RowQuantFwd a) {
 }
 
 // Whole rows (cols = 512 NC), one wave per row, the row staged in LDS: the wave
-// copies its row straight from HBM into its own LDS slot, then reads it twice:
-// pass 1 forms x~ and its max / min (lowest column among equal values), pass 2
-// rounds and stores.  Registers hold one 8-element chunk at a time, so many rows'
-// copies are in flight per compute unit.  For fp32 input pass 1 writes x~ back
-// over the raw value (the LET division happens once per element).  Same results as
-// k_rowquant_fwd_wave.
+// copies its row straight from HBM into its own LDS slot, then forms x~ chunk by
+// chunk into registers (pass 1: the chunk's max / min, the bias fold, finiteness),
+// and rounds and stores from those registers (pass 2).  The extreme values take the
+// three-operand max / min per chunk and the lane remembers the first chunk holding
+// its extreme; only the lanes holding the row's extreme look for its first column
+// inside that chunk (re-forming it from LDS), so the column is the lowest one among
+// equal values, as an element-wise scan in column order gives.  Same results as
+// k_rowquant_fwd_wave.  (One row per wave: a wave that kept taking rows would have to
+// wait for its previous row's stores before reading the next copy from LDS, where a
+// finished wave lets them drain.)
 // RMS: x is first normalized by its row's root mean square (the RMSNorm before the
 // linear, unit gain), the normalized row written to rms_out and 1/rms to rstd.
 template <int XDT, int NC, int LET, bool RMS = false>
@@ -680,50 +796,13 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_lds(RowQuantFwd a) {
             (__attribute__((address_space(3))) void*)(my + (k * NH + h) * 64), 16, 0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
-  // the row's 1 / rms: sum of squares over the staged row
-  float rs = 1.f;
-  if constexpr (RMS) {
-    double ss = 0.0;
-#pragma unroll 2
-    for (int k = 0; k < NC; ++k) {
-      if constexpr (XDT == OMQ_F32) {
-        const uint4 t0 = my[(2 * k) * 64 + lane], t1 = my[(2 * k + 1) * 64 + lane];
-        const uint32_t wv[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const double v = (double)__uint_as_float(wv[j]);
-          ss = fma(v, v, ss);
-        }
-      } else {
-        const uint4 t0 = my[k * 64 + lane];
-        const uint32_t wv[4] = {t0.x, t0.y, t0.z, t0.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const double lo = (double)__uint_as_float(wv[q] << 16);
-          const double hi = (double)__uint_as_float(wv[q] & 0xffff0000u);
-          ss = fma(lo, lo, ss);
-          ss = fma(hi, hi, ss);
-        }
-      }
-    }
-    ss = wave_sum(ss);
-    rs = rms_scale(ss, a.cols, a.eps);
-    if (lane == 0 && a.rstd) a.rstd[r] = rs;
-  }
-  // x~ of chunk k for this lane (8 consecutive columns c .. c+7)
-  auto chunk = [&](int k, float (&xt)[8], float& dot, bool first) {
-    const int64_t c = ((int64_t)k * 64 + lane) * 8;
-    float v[8];
+  // the raw elements of chunk k
+  auto raw = [&](int k, float (&v)[8]) {
     if constexpr (XDT == OMQ_F32) {
       const uint4 t0 = my[(2 * k) * 64 + lane], t1 = my[(2 * k + 1) * 64 + lane];
       const uint32_t wv[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[j] = __uint_as_float(wv[j]);
-      if (!first) {                                // pass 1 stored x~ itself
-#pragma unroll
-        for (int j = 0; j < 8; ++j) xt[j] = v[j];
-        return;
-      }
     } else {
       const uint4 t0 = my[k * 64 + lane];
       const uint32_t wv[4] = {t0.x, t0.y, t0.z, t0.w};
@@ -733,11 +812,26 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_lds(RowQuantFwd a) {
         v[2 * q + 1] = __uint_as_float(wv[q] & 0xffff0000u);
       }
     }
-    if constexpr (RMS) {
+  };
+  // the row's 1 / rms: sum of squares over the staged row
+  float rs = 1.f;
+  if constexpr (RMS) {
+    double ss = 0.0;
+#pragma unroll 2
+    for (int k = 0; k < NC; ++k) {
+      float v[8];
+      raw(k, v);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = v[j] * rs;
-      if (first) store8(a.rms_out, OMQ_F32, r * a.cols + c, v);
+      for (int j = 0; j < 8; ++j) ss = fma((double)v[j], (double)v[j], ss);
     }
+    ss = wave_sum(ss);
+    rs = rms_scale(ss, a.cols, a.eps);
+    if (lane == 0 && a.rstd) a.rstd[r] = rs;
+  }
+  // x~ of chunk k (columns c .. c+7, c = (64 k + lane) 8) from the raw elements v
+  // (normalized when RMS)
+  auto let = [&](int k, const float (&v)[8], float (&xt)[8]) {
+    const int64_t c = ((int64_t)k * 64 + lane) * 8;
     if constexpr (LET == OMQ_LET_DIV) {
       float sv[8], dv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
       load8f(a.s, c, 8, sv);
@@ -753,67 +847,74 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_lds(RowQuantFwd a) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) xt[j] = v[j];
     }
-    if (first && a.fold_delta) {
+  };
+  auto xtilde = [&](int k, float (&xt)[8]) {
+    float v[8];
+    raw(k, v);
+    if constexpr (RMS) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = v[j] * rs;
+    }
+    let(k, v, xt);
+  };
+  // pass 1: x~ into registers; per chunk its max / min (the lane keeps the first
+  // chunk holding its extreme), the bias fold and the finiteness accumulator
+  float xs[NC][8];
+  float lmax = 0.f, lmin = 0.f, dot = 0.f, nfa = 0.f;
+  int kmx = 0, kmn = 0;
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const int64_t c = ((int64_t)k * 64 + lane) * 8;
+    float v[8];
+    raw(k, v);
+    if constexpr (RMS) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = v[j] * rs;
+      store8(a.rms_out, OMQ_F32, r * a.cols + c, v);
+    }
+    if (a.fold_delta) {
       float fv[8];
       load8f(a.fold_delta, c, 8, fv);
 #pragma unroll
       for (int j = 0; j < 8; ++j) dot = fmaf(fv[j], v[j], dot);
     }
-    if constexpr (XDT == OMQ_F32) {
-      if (first) {
-        my[(2 * k) * 64 + lane] =
-            make_uint4(__float_as_uint(xt[0]), __float_as_uint(xt[1]), __float_as_uint(xt[2]),
-                       __float_as_uint(xt[3]));
-        my[(2 * k + 1) * 64 + lane] =
-            make_uint4(__float_as_uint(xt[4]), __float_as_uint(xt[5]), __float_as_uint(xt[6]),
-                       __float_as_uint(xt[7]));
-      }
+    let(k, v, xs[k]);
+    const float cM = max8(xs[k]), cm = min8(xs[k]);
+    if (k == 0) {
+      lmax = cM;
+      lmin = cm;
+    } else {
+      if (cM > lmax) { lmax = cM; kmx = k; }
+      if (cm < lmin) { lmin = cm; kmn = k; }
     }
-  };
-  // pass 1: max / min with the lowest column among equal values (columns are
-  // visited in increasing order; chunk 0 seeds the lane's values)
-  float vmax, vmin, dot = 0.f;
-  int imax, imin;
-  bool nf = false;
+    if (a.nonfinite) nfa = nf_acc8(xs[k], nfa);
+  }
+  if (a.nonfinite) flag_nonfinite(a.nonfinite, nfa != nfa);
+  // the row's extremes, then their first columns: the lanes holding an extreme
+  // re-form their chunk from LDS and take its first equal element; the others offer
+  // (the extreme, no column), so the lowest column wins and its value is kept
+  float M = wave_maxf(lmax), m = wave_minf(lmin);
+  int imax = 0x7fffffff, imin = 0x7fffffff;
   {
-    float xt[8];
-    chunk(0, xt, dot, true);
-    vmax = vmin = xt[0];
-    imax = imin = lane * 8;
-#pragma unroll
-    for (int j = 1; j < 8; ++j) {
-      if (xt[j] > vmax) { vmax = xt[j]; imax = lane * 8 + j; }
-      if (xt[j] < vmin) { vmin = xt[j]; imin = lane * 8 + j; }
+    float t[8];
+    int j;
+    if (lmax == M) {
+      xtilde(kmx, t);
+      first_eq8(t, M, j, M);
+      if (j < 8) imax = (kmx * 64 + lane) * 8 + j;
     }
-    if (a.nonfinite) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) nf |= !__builtin_isfinite(xt[j]);
-    }
-  }
-  // (two chunks per iteration: unrolling all of them would hoist every chunk's loads
-  // and take the registers the occupancy needs)
-#pragma unroll 2
-  for (int k = 1; k < NC; ++k) {
-    float xt[8];
-    chunk(k, xt, dot, true);
-    const int c = (k * 64 + lane) * 8;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (xt[j] > vmax) { vmax = xt[j]; imax = c + j; }
-      if (xt[j] < vmin) { vmin = xt[j]; imin = c + j; }
-    }
-    if (a.nonfinite) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) nf |= !__builtin_isfinite(xt[j]);
+    if (lmin == m) {
+      xtilde(kmn, t);
+      first_eq8(t, m, j, m);
+      if (j < 8) imin = (kmn * 64 + lane) * 8 + j;
     }
   }
-  if (a.nonfinite) flag_nonfinite(a.nonfinite, nf);
-  wave_argmax(vmax, imax);
-  wave_argmin(vmin, imin);
+  wave_argmax(M, imax);
+  wave_argmin(m, imin);
   dot = wave_sum(dot);
   const float gamma = lg_g ? sigmoid_f32(lg_g[rl]) : 1.f;
   const float beta = lg_b ? sigmoid_f32(lg_b[rl]) : 1.f;
-  const RowQ q = row_step(vmax, vmin, gamma, beta, a.nbits);
+  const RowQ q = row_step(M, m, gamma, beta, a.nbits);
   if (lane == 0) {
     if (a.h) a.h[r] = q.h;
     if (a.z) a.z[r] = q.z;
@@ -821,54 +922,25 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_lds(RowQuantFwd a) {
     if (a.amin) a.amin[r] = col_in(imin, a.cols);
     if (a.bias_out) a.bias_out[r] = (a.bias ? a.bias[r] : 0.f) + dot;
   }
-  // pass 2: rint(x~ / h) by the reciprocal product.  u = x~ rh lies within 3 ulp of
-  // the exact quotient, so they can round apart only within |u| 2^-20 of a
-  // half-integer; the test uses the row's bound max|x~| rh 2^-20 >= |u| 2^-20 (a few
-  // more elements take the exact path, none fewer).  A chunk with such an element (or
-  // a non-finite u) takes the exact quotient behind a wave-uniform branch (a
-  // divergent one would be flattened into a division for every element).
+  // pass 2: round, clamp, dequantize and store from the registers
   const float rh = 1.f / q.h;
-  const float thr = fmaxf(fabsf(vmax), fabsf(vmin)) * rh * 0x1p-20f;
-  const bool want_codes = a.codes != nullptr;
-  int qs = 0;
-#pragma unroll 2
+  const float thr = fmaxf(fabsf(M), fabsf(m)) * rh * 0x1p-20f;
+  const bool off128 = a.code_off != 0;
+  uint32_t qsum = 0u;
+#pragma unroll
   for (int k = 0; k < NC; ++k) {
     const int64_t c = ((int64_t)k * 64 + lane) * 8;
-    float xt[8], rr[8];
-    chunk(k, xt, dot, false);
-    bool near = false;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float u = xt[j] * rh;
-      rr[j] = rintf(u);
-      near |= !(fabsf(fabsf(u - rr[j]) - 0.5f) > thr);
-    }
-    if (__builtin_amdgcn_ballot_w64(near) != 0) {
-      if (near) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) rr[j] = rintf(xt[j] / q.h);
-      }
-    }
-    float o[8], qq[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      qq[j] = __builtin_amdgcn_fmed3f(rr[j] + q.z, 0.f, q.Q);
-      o[j] = (qq[j] - q.z) * q.h;
-    }
+    float rr[8], o[8], qq[8];
+    rint_quot8(xs[k], q.h, rh, thr, true, rr);
+    dequant8(rr, q, qq, o);
     store8(a.out, a.out_dt, r * a.ldo + c, o);
-    if (want_codes) {
-      uint32_t cw[2] = {0u, 0u};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int qi = (int)qq[j] - a.code_off;
-        cw[j >> 2] |= ((uint32_t)qi & 0xffu) << (8 * (j & 3));
-        qs += qi;
-      }
-      *reinterpret_cast<uint2*>(a.codes + r * code_ld(a) + c) = make_uint2(cw[0], cw[1]);
+    if (a.codes) {
+      const uint2 cw = codes8(qq, off128, qsum);
+      *reinterpret_cast<uint2*>(a.codes + r * code_ld(a) + c) = cw;
     }
   }
   if (a.qsum) {
-    qs = wave_sum(qs);
+    const int qs = (int)wave_sum(qsum) - a.code_off * (int)a.cols;
     if (lane == 0) a.qsum[r] = qs;
   }
 }
@@ -1513,23 +1585,23 @@ bool launch_fwd_wave(const RowQuantFwd& a, hipStream_t st) {
   else                                                                                        \
     hipLaunchKernelGGL((k_rowquant_fwd_wave<XDT, N, OMQ_LET_NONE, F>), grid, dim3(kThreads), 0,\
                        st, a);
-#define OMQ_FWD_LDS(N)                                                                        \
-  if (a.let_mode == OMQ_LET_DIV)                                                              \
-    hipLaunchKernelGGL((k_rowquant_fwd_lds<XDT, N, OMQ_LET_DIV>), grid, dim3(kThreads), 0, st, \
-                       a);                                                                    \
-  else if (a.let_mode == OMQ_LET_MUL)                                                         \
-    hipLaunchKernelGGL((k_rowquant_fwd_lds<XDT, N, OMQ_LET_MUL>), grid, dim3(kThreads), 0, st, \
-                       a);                                                                    \
-  else                                                                                        \
-    hipLaunchKernelGGL((k_rowquant_fwd_lds<XDT, N, OMQ_LET_NONE>), grid, dim3(kThreads), 0, st,\
-                       a);
-#define OMQ_FWD_RMS(N)                                                                        \
-  if (a.let_mode == OMQ_LET_DIV)                                                              \
-    hipLaunchKernelGGL((k_rowquant_fwd_lds<XDT, N, OMQ_LET_DIV, true>), grid, dim3(kThreads), \
-                       0, st, a);                                                             \
-  else                                                                                        \
-    hipLaunchKernelGGL((k_rowquant_fwd_lds<XDT, N, OMQ_LET_NONE, true>), grid, dim3(kThreads),\
-                       0, st, a);
+#define OMQ_FWD_LDS(N)                                                                      \
+  if (a.let_mode == OMQ_LET_DIV)                                                            \
+    hipLaunchKernelGGL((k_rowquant_fwd_lds<XDT, N, OMQ_LET_DIV>), grid, dim3(kThreads), 0,   \
+                       st, a);                                                              \
+  else if (a.let_mode == OMQ_LET_MUL)                                                       \
+    hipLaunchKernelGGL((k_rowquant_fwd_lds<XDT, N, OMQ_LET_MUL>), grid, dim3(kThreads), 0,   \
+                       st, a);                                                              \
+  else                                                                                      \
+    hipLaunchKernelGGL((k_rowquant_fwd_lds<XDT, N, OMQ_LET_NONE>), grid, dim3(kThreads), 0,  \
+                       st, a);
+#define OMQ_FWD_RMS(N)                                                                      \
+  if (a.let_mode == OMQ_LET_DIV)                                                            \
+    hipLaunchKernelGGL((k_rowquant_fwd_lds<XDT, N, OMQ_LET_DIV, true>), grid,               \
+                       dim3(kThreads), 0, st, a);                                           \
+  else                                                                                      \
+    hipLaunchKernelGGL((k_rowquant_fwd_lds<XDT, N, OMQ_LET_NONE, true>), grid,              \
+                       dim3(kThreads), 0, st, a);
 #define OMQ_FWD_WAVE(N)                                                                       \
   if (nc <= N) {                                                                              \
     if (a.rms_out && a.cols == N * 512) {                                                     \
@@ -1629,6 +1701,8 @@ hipError_t launch_rowquant_fwd(const RowQuantFwd& a, hipStream_t st) {
   if (a.rms_out && !rowquant_fwd_rms_ok(a)) return hipErrorInvalidValue;
   // code sums come with the codes, per whole row
   if (a.qsum && (!a.codes || a.group > 0 || a.nbits >= 16)) return hipErrorInvalidValue;
+  // stored codes are q itself or q - 128 (8-bit codes as signed bytes)
+  if (a.codes && a.code_off != 0 && a.code_off != 128) return hipErrorInvalidValue;
   if (a.group > 0) {           // groups of 128 (the caller checked cols % 128 == 0)
     if (a.group != 128 || a.cols % 128 || a.nbits >= 16 || a.fold_delta)
       return hipErrorInvalidValue;
