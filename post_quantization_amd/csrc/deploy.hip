@@ -32,10 +32,23 @@ __global__ __launch_bounds__(256) void k_pack_codes(const uint8_t* codes, int64_
   words[i] = w;
 }
 
+// The 4-bit codes of one word as two words of bytes: the even columns' codes in
+// lo, the odd columns' in hi.  Formed in one ALU block the compiler cannot see
+// into, so that each byte of lo / hi then converts with one v_cvt_f32_ubyteN (it
+// would otherwise fold the masks into a bit-field extract per code, two
+// instructions per column).
+OMQ_DEV void nibble_bytes(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  asm("v_and_b32 %0, 0x0f0f0f0f, %2\n\tv_lshrrev_b32 %1, 4, %2\n\t"
+      "v_and_b32 %1, 0x0f0f0f0f, %1"
+      : "=&v"(lo), "=&v"(hi)
+      : "v"(w));
+}
+
 // W_hat of 8 consecutive columns from one word of 4-bit codes: (q - z) h rounded
 // once to float32, the same values the calibration's fake quantizer produced
 OMQ_DEV void dequant8(uint32_t w, float h, float z, float out[8]) {
-  const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
+  uint32_t lo, hi;
+  nibble_bytes(w, lo, hi);
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     out[2 * b] = ((float)((lo >> (8 * b)) & 0xffu) - z) * h;
@@ -61,7 +74,7 @@ __global__ __launch_bounds__(256) void k_fold_linear(DeployFold a) {
       for (int p = 0; p < P; ++p) {
         const int64_t k = j * P + p;
         if (k >= a.K) break;
-        const int64_t gi = n * G + (a.group ? k / a.group : 0);
+        const int64_t gi = a.group ? n * G + (k >> 7) : n;   // group 128 or the row
         const float wh = ((float)((w >> (p * a.nbits)) & mask) - a.z[gi]) * a.h[gi];
         acc += wh * (a.delta[k] / a.s[k]);
       }
@@ -119,7 +132,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_w4a16_gemm(DeployGemm a) {
       zz[j] = 0.f;
       if (nv && kb < nkb) {
         cw[j] = *reinterpret_cast<const u32x4*>(a.words + n * nw + k0 / 8);
-        const int64_t gi = n * G + (a.group ? k0 / a.group : 0);
+        const int64_t gi = a.group ? n * G + (k0 >> 7) : n;  // group 128 or the row
         hh[j] = a.h[gi];
         zz[j] = a.z[gi];
       }
@@ -184,14 +197,15 @@ __global__ __launch_bounds__(256) void k_w4a16_gemv(DeployGemm a) {
   // one 16-byte chunk (32 columns) of codes into the accumulators
   auto chunk = [&](const u32x4 cw, int64_t j) {
     const int64_t col0 = j * 8;
-    const int64_t gi = n * G + (a.group ? col0 / a.group : 0);
+    const int64_t gi = a.group ? n * G + (col0 >> 7) : n;  // group 128 or the row
     const float hh = a.h[gi], zz = a.z[gi];
     // W_hat pairs (columns col0 + 2p, col0 + 2p + 1), p = 0..15
     uint32_t wp[16];
     const uint32_t ws[4] = {cw.x, cw.y, cw.z, cw.w};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const uint32_t lo = ws[s] & 0x0f0f0f0fu, hi = (ws[s] >> 4) & 0x0f0f0f0fu;
+      uint32_t lo, hi;
+      nibble_bytes(ws[s], lo, hi);
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const float f0 = ((float)((lo >> (8 * b)) & 0xffu) - zz) * hh;

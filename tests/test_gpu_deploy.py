@@ -72,7 +72,12 @@ def test_fold_linear(N, K, group):
 
 @pytest.mark.parametrize("T,N,K,group", [(1, 4096, 4096, 128), (7, 300, 4096, 128),
                                          (32, 1024, 11008, 128), (100, 512, 1024, 0),
-                                         (16, 22016, 4096, 128)])
+                                         (16, 22016, 4096, 128),
+                                         # the vector-unit kernel at 1 to 3 tokens with
+                                         # ragged N, per-channel steps and a tail
+                                         # column position (K 11008)
+                                         (1, 1000, 11008, 128), (2, 300, 1024, 0),
+                                         (3, 1030, 4096, 128)])
 def test_w4a16_gemm(T, N, K, group):
     log("w4a16", T, N, K, group)
     rng = np.random.default_rng(T * 7 + N + K)
