@@ -139,9 +139,23 @@ struct Unit {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
-// paired causal blocks (a long and a short query or key block per workgroup) are
+// paired causal blocks (a long and a short key block per workgroup, dK/dV) are
 // used when that still leaves at least one workgroup per compute unit
 constexpr int64_t kPairMinBlocks = 256;
+
+// The query-stationary kernels (forward, dQ) take one 128-query unit per workgroup
+// and fit two waves per SIMD (two workgroups per compute unit).  Under the causal
+// mask a unit's work grows with its position, so the grid is ordered by unit size:
+// workgroup b < half takes query block nqb-1-v (v = b / heads) and workgroup
+// b + half takes block v of the same head, where half = ceil(nqb/2) * heads.  The
+// dispatcher fills the second slot of each compute unit in the same order as the
+// first, so a long and a short unit share a compute unit (equal work per unit in
+// one round on the 7B and 70B shapes); with more rounds the longest run first.
+OMQ_DEV void query_unit(int heads, int nqb, int& hq, int& qb) {
+  const int v = blockIdx.x / heads, half = (nqb + 1) / 2;
+  hq = blockIdx.x % heads;
+  qb = v < half ? nqb - 1 - v : v - half;
+}
 
 // 2^x on the transcendental unit (no denormal rescaling: results below 2^-126 are
 // probabilities that vanish against the row sum anyway)
@@ -158,22 +172,17 @@ OMQ_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 //      two-step softmax, and as the backward's recomputation), O^T += V^T P^T
 //      (A = V^T from LDS, B = P from registers).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kT) void k_flash_fwd(FlashFwd a, int pair) {
+__global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(2)))
+void k_flash_fwd(FlashFwd a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * RS];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[2][HD * 64];
   const int64_t T = a.T;
   const int nqb = (int)((T + 127) / 128);
-  // pair: the block takes query blocks nqb-1-p and then p (equal work per block
-  // under the causal mask); else query block nqb-1-p alone (longest rows first)
-  const int npb = pair ? (nqb + 1) / 2 : nqb;
-  const int hq = blockIdx.x / npb;
-  const int p = (int)(blockIdx.x % npb);
-  const int nunits = (pair && p != nqb - 1 - p) ? 2 : 1;
+  int hq, qb;
+  query_unit(a.n_q, nqb, hq, qb);
   const int hk = hq / a.grp;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), h = lane >> 5, l32 = lane & 31;
-  for (int u = 0; u < nunits; ++u) {
-    const int qb = u == 0 ? nqb - 1 - p : p;
-    if (u > 0) __syncthreads();                          // LDS of the previous unit
+  {
     const int64_t q0 = (int64_t)qb * 128;
     const int64_t q = q0 + 32 * w + l32;
     const int64_t qc = min(q, T - 1);
@@ -497,21 +506,17 @@ __global__ __launch_bounds__(kT) void k_flash_bwd_dkdv(FlashBwd a, int pair) {
 // S^T = K Q^T and dP^T = V dO^T (A = K / V rows from LDS, B = Q / dO from
 // registers), dS^T as above, dQ^T += K^T dS^T (A = transposed K from LDS).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kT) void k_flash_bwd_dq(FlashBwd a, int pair) {
+__global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(2)))
+void k_flash_bwd_dq(FlashBwd a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * RS];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][64 * RS];
   const int64_t T = a.T;
   const int nqb = (int)((T + 127) / 128);
-  // pair: query blocks nqb-1-p and then p (equal causal work per block)
-  const int npb = pair ? (nqb + 1) / 2 : nqb;
-  const int hq = blockIdx.x / npb;
-  const int p = (int)(blockIdx.x % npb);
-  const int nunits = (pair && p != nqb - 1 - p) ? 2 : 1;
+  int hq, qb;
+  query_unit(a.n_q, nqb, hq, qb);
   const int hk = hq / a.grp;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), h = lane >> 5, l32 = lane & 31;
-  for (int u = 0; u < nunits; ++u) {
-    const int qb = u == 0 ? nqb - 1 - p : p;
-    if (u > 0) __syncthreads();                          // LDS of the previous unit
+  {
     const int64_t q0 = (int64_t)qb * 128;
     const int64_t q = q0 + 32 * w + l32;
     const int64_t qc = min(q, T - 1);
@@ -613,10 +618,7 @@ hipError_t launch_flash_fwd(const FlashFwd& a, hipStream_t st) {
   if (a.T == 0 || a.n_q == 0) return hipSuccess;
   if (a.T > (int64_t)1 << 30) return hipErrorInvalidValue;    // positions are 32-bit
   const int nqb = (int)((a.T + 127) / 128);
-  // pair the causal query blocks when that still leaves a block per compute unit
-  const int pair = (int64_t)((nqb + 1) / 2) * a.n_q >= kPairMinBlocks;
-  const int npb = pair ? (nqb + 1) / 2 : nqb;
-  hipLaunchKernelGGL(k_flash_fwd, dim3((unsigned)(npb * a.n_q)), dim3(kT), 0, st, a, pair);
+  hipLaunchKernelGGL(k_flash_fwd, dim3((unsigned)(nqb * a.n_q)), dim3(kT), 0, st, a);
   return hipGetLastError();
 }
 
@@ -639,9 +641,7 @@ hipError_t launch_flash_bwd(const FlashBwd& a, hipStream_t st) {
                      st, a, pair_kv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int pair_q = (int64_t)npb * a.n_q >= kPairMinBlocks;
-  hipLaunchKernelGGL(k_flash_bwd_dq, dim3((unsigned)((pair_q ? npb : nkb) * a.n_q)), dim3(kT), 0,
-                     st, a, pair_q);
+  hipLaunchKernelGGL(k_flash_bwd_dq, dim3((unsigned)(nkb * a.n_q)), dim3(kT), 0, st, a);
   return hipGetLastError();
 }
 
