@@ -5,8 +5,9 @@ gradient group of the straight-through backward, and the AdamW update.
 Cases (reduced sizes the oracle finishes in seconds, spanning several GEMM tiles
 and a ragged tail): the 7B-shaped block at W4A4 with s_a (multi-head, and with
 grouped-query attention), the 70B-shaped grouped-query block at W4A16 and W2A16,
-the FFN alone at W3A16; and two at full widths: the FFN workload whole (W2A16) and
-the 70B-shaped block on 256 tokens (W4A16).
+the FFN alone at W3A16; at full widths: the FFN workload whole (W2A16, W3A16), the
+70B-shaped block on 256 tokens (W4A16, W2A16) and whole (W4A16, W2A16), and the 7B
+block on 128 tokens.
 Tolerance: 2e-2 relative Frobenius per quantity (bf16 matrix-core path).
 """
 import numpy as np
@@ -58,10 +59,13 @@ CASES = {
     # attention forward and dQ run paired causal blocks, dK/dV unpaired; the oracle's
     # step needs ~70 GB of host memory and a few minutes
     "gqa70b_w4a16_full": synth.BLOCK_CFG5_W4,
+    # and at W2A16
+    "gqa70b_w2a16_full": synth.BLOCK_CFG5_W2,
 }
 # the full-width cases take the oracle tens of seconds (the whole 70B block minutes)
 SLOW = {"ffn_w2a16_full": 300, "gqa70b_w4a16_t256": 600, "mha_w4a4_full_widths_t128": 300,
-        "ffn_w3a16_full": 300, "gqa70b_w2a16_t256": 600, "gqa70b_w4a16_full": 1100}
+        "ffn_w3a16_full": 300, "gqa70b_w2a16_t256": 600, "gqa70b_w4a16_full": 1100,
+        "gqa70b_w2a16_full": 1100}
 
 
 def desc_of(c):
