@@ -366,6 +366,9 @@ size_t omq_qlinear_workspace_size(const omq_qlinear_desc* d);
  * X: [T x c_in], W: [c_out x c_in] (path dtype), B: float[c_out] or NULL.
  * The state the backward needs (dequantized operands, step sizes, indices) is
  * kept in ws, which must be passed unchanged to omq_qlinear_bwd.
+ * c_in must be a multiple of 4, and on the bf16 path T, c_in and c_out multiples of
+ * 8 (OMQ_E_ALIGN: the 16-byte operand rows of the matrix-core products); with
+ * group 128, c_in a multiple of 128 (OMQ_E_SHAPE).
  */
 int omq_qlinear_fwd(const omq_qlinear_desc* d, const void* X, const void* W, const float* B,
                     const float* theta, float* Y, void* ws, size_t ws_bytes, void* stream);
