@@ -551,8 +551,13 @@ void k_gemm_bf16(Gemm g, int tiles_m, int tiles_n) {
         }
         // x~ and the rounding of x~ / h by the reciprocal product for every element
         // of the batch; an element whose product lies within |u| 2^-20 of a
-        // half-integer (or is not finite) takes the exact quotient below
-        bool near = false;
+        // half-integer takes the exact quotient below.  The batch test uses the
+        // batch's bound: with f = u - rint u (exact, |f| <= 1/2), an element that
+        // needs the exact quotient has 1/2 - |f| <= |u| 2^-20, so 1/2 - max|f| <=
+        // max|u| 2^-20 too; the flagged batches then test each element.  (An
+        // infinite u flags its batch through max|u|; a NaN u is passed over, its
+        // exact quotient being NaN as well.)
+        float fmx = 0.f, umx = 0.f;
 #pragma unroll
         for (int q = 0; q < RB; ++q) {
           const int rw = b * RB + q;
@@ -577,9 +582,11 @@ void k_gemm_bf16(Gemm g, int tiles_m, int tiles_n) {
             else xt[q][c2] = xv[q][c2];
             u[q][c2] = xt[q][c2] * rhh;
             rr[q][c2] = rintf(u[q][c2]);
-            near |= !(fabsf(fabsf(u[q][c2] - rr[q][c2]) - 0.5f) > fabsf(u[q][c2]) * 0x1p-20f);
+            fmx = fmaxf(fmx, fabsf(u[q][c2] - rr[q][c2]));
+            umx = fmaxf(umx, fabsf(u[q][c2]));
           }
         }
+        const bool near = !(0.5f - fmx > umx * 0x1p-20f);
         // (wave-uniform branches: divergent ones would be flattened into a division
         // for every element)
         if (!pass && __builtin_amdgcn_ballot_w64(near) != 0) {
