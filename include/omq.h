@@ -207,7 +207,10 @@ int omq_attention_fwd(const void* Q, int64_t ldq, const void* K, const void* V, 
  * O, dO: float [T x n_q*128], row stride ldo; lse2 as the forward wrote it.
  * dQ: float [T x n_q*128], row stride lddq; dK, dV: float [T x n_kv*128], row
  * stride lddk (multiples of 4); all overwritten.  ws: device workspace of at least
- * omq_attention_bwd_workspace_size(T, n_q, ldq) bytes (dO in bf16, rowsum(dO O)).
+ * omq_attention_bwd_workspace_size(T, n_q, ldq) bytes (dO in bf16, rowsum(dO O),
+ * and, where the K/V heads are too few to occupy the device, float32 partial dK, dV
+ * of query-head subsets, added in a fixed order; the size covers any n_kv dividing
+ * n_q).  The result is bitwise repeatable: no float atomics.
  */
 size_t omq_attention_bwd_workspace_size(int64_t T, int64_t n_q, int64_t ldq);
 int omq_attention_bwd(const void* Q, int64_t ldq, const void* K, const void* V, int64_t ldk,

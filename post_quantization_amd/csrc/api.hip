@@ -230,6 +230,11 @@ size_t omq_attention_bwd_workspace_size(int64_t T, int64_t n_q, int64_t ldq) {
   Bump b(nullptr);
   b.take<float>(n_q * T);       // D = rowsum(dO * O) per (head, query)
   b.take<uint16_t>(T * ldq);    // dO in bf16, rows like Q's
+  // partial dK, dV of the query-head splits, for the largest need of any n_kv
+  int64_t part = 0;
+  for (int64_t kv = 1; kv <= n_q; ++kv)
+    if (n_q % kv == 0) part = std::max(part, flash_bwd_part_floats(T, (int)n_q, (int)kv));
+  b.take<float>(part);
   return b.off;
 }
 
@@ -249,6 +254,7 @@ int omq_attention_bwd(const void* Q, int64_t ldq, const void* K, const void* V, 
   Bump b(ws);
   float* D = b.take<float>(n_q * T);
   uint16_t* dOb = b.take<uint16_t>(T * ldq);
+  float* part = b.take<float>(flash_bwd_part_floats(T, (int)n_q, (int)n_kv));
   const hipStream_t st = S(stream);
   OMQ_HIP_CHECK(launch_attn_bwd_prep(dO, O, ldo, T, (int)n_q, D, dOb, ldq, st));
   FlashBwd f;
@@ -259,7 +265,7 @@ int omq_attention_bwd(const void* Q, int64_t ldq, const void* K, const void* V, 
   f.scale = (float)(1.0 / sqrt((double)head_dim));
   f.scale2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
   f.lse2 = lse2; f.D = D;
-  f.dQ = dQ; f.lddq = lddq; f.dK = dK; f.dV = dV; f.lddk = lddk;
+  f.dQ = dQ; f.lddq = lddq; f.dK = dK; f.dV = dV; f.lddk = lddk; f.part = part;
   OMQ_HIP_CHECK(launch_flash_bwd(f, st));
   return OMQ_OK;
 }

@@ -21,6 +21,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace omq {
 
 namespace {
@@ -339,7 +341,7 @@ __global__ __launch_bounds__(kT) void k_attn_bwd_prep(const float* gO, const flo
 // from LDS, B = K / V from registers), P = exp2(S c - lse2), dS = P (dP - D) / sqrt(hd),
 // dV^T += dO^T P and dK^T += Q^T dS (A = transposed Q / dO from LDS, B = P / dS).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kT) void k_flash_bwd_dkdv(FlashBwd a, int pair) {
+__global__ __launch_bounds__(kT) void k_flash_bwd_dkdv(FlashBwd a, int pair, int nsplit) {
   __shared__ __attribute__((aligned(16))) uint16_t Qs[2][64 * RS];
   __shared__ __attribute__((aligned(16))) uint16_t Gs[2][64 * RS];
   __shared__ __attribute__((aligned(16))) float Ls[2][64];
@@ -347,10 +349,18 @@ __global__ __launch_bounds__(kT) void k_flash_bwd_dkdv(FlashBwd a, int pair) {
   const int64_t T = a.T;
   const int nkb = (int)((T + 127) / 128);
   // pair: key blocks p and then nkb-1-p (equal causal work per block); else key
-  // block p alone (kb = 0, the longest, first)
+  // block p alone (kb = 0, the longest, first).  Workgroup (g, sp, p) covers query
+  // heads sp*gh .. sp*gh + gh-1 of K/V head g's group; split 0 writes dK, dV, the
+  // others their own partial slices, added in split order afterwards.
   const int npb = pair ? (nkb + 1) / 2 : nkb;
-  const int g = blockIdx.x / npb;
   const int p = (int)(blockIdx.x % npb);
+  const int g = (int)(blockIdx.x / npb) / nsplit;
+  const int sp = (int)(blockIdx.x / npb) % nsplit;
+  const int gh = a.grp / nsplit;
+  const int64_t ldp = (int64_t)(a.n_q / a.grp) * HD;
+  float* const oK = sp == 0 ? a.dK : a.part + (int64_t)(sp - 1) * 2 * T * ldp;
+  float* const oV = sp == 0 ? a.dV : oK + T * ldp;
+  const int64_t ldo = sp == 0 ? a.lddk : ldp;
   const int nunits = (pair && p != nkb - 1 - p) ? 2 : 1;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), h = lane >> 5, l32 = lane & 31;
   for (int u = 0; u < nunits; ++u) {
@@ -369,9 +379,9 @@ __global__ __launch_bounds__(kT) void k_flash_bwd_dkdv(FlashBwd a, int pair) {
     const int nqb = (int)((T + 63) / 64);
     const int qb0 = (int)(k0 / 64);
     const int per = nqb - qb0;                              // query blocks per head
-    const int nit = per * a.grp;
+    const int nit = per * gh;
     auto qbase = [&](int it, int& hq) -> int64_t {
-      hq = g * a.grp + it / per;
+      hq = g * a.grp + sp * gh + it / per;
       return (int64_t)(qb0 + it % per) * 64;
     };
 
@@ -485,8 +495,8 @@ __global__ __launch_bounds__(kT) void k_flash_bwd_dkdv(FlashBwd a, int pair) {
       __syncthreads();
     }
     if (key < T) {
-      float* krow = a.dK + key * a.lddk + g * HD;
-      float* vrow = a.dV + key * a.lddk + g * HD;
+      float* krow = oK + key * ldo + g * HD;
+      float* vrow = oV + key * ldo + g * HD;
   #pragma unroll
       for (int hb = 0; hb < 4; ++hb)
   #pragma unroll
@@ -612,7 +622,44 @@ void k_flash_bwd_dq(FlashBwd a) {
   }
 }
 
+// dK, dV += the partial slices of splits 1 .. nsplit-1, added in that order (float4
+// units; ldp, a multiple of 128, is the row length of every slice)
+__global__ __launch_bounds__(kT) void k_kv_part_add(float* dK, float* dV, int64_t lddk,
+                                                    const float* part, int64_t T, int64_t ldp,
+                                                    int nsplit) {
+  const int64_t n4 = T * ldp / 4;
+  for (int64_t i = (int64_t)blockIdx.x * kT + threadIdx.x; i < 2 * n4;
+       i += (int64_t)gridDim.x * kT) {
+    const int which = i >= n4;                   // 0: dK, 1: dV
+    const int64_t j = i - which * n4, t = j / (ldp / 4), c = 4 * (j % (ldp / 4));
+    float* o = (which ? dV : dK) + t * lddk + c;
+    float4 acc = *reinterpret_cast<const float4*>(o);
+    for (int sp = 1; sp < nsplit; ++sp) {
+      const float4 v = *reinterpret_cast<const float4*>(
+          part + ((int64_t)(sp - 1) * 2 + which) * T * ldp + t * ldp + c);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    *reinterpret_cast<float4*>(o) = acc;
+  }
+}
+
 }  // namespace
+
+// The dK/dV grid has npb workgroups per K/V head (paired key blocks).  When the K/V
+// heads alone leave compute units without a workgroup, each group's query heads
+// are split over the smallest divisor of the group size that fills the device.
+int flash_bwd_splits(int64_t T, int n_q, int n_kv) {
+  if (T <= 0 || n_q <= 0 || n_kv <= 0 || n_q % n_kv) return 1;
+  const int64_t npb = ((T + 127) / 128 + 1) / 2;
+  const int grp = n_q / n_kv;
+  for (int s = 1; s < grp; ++s)
+    if (grp % s == 0 && npb * n_kv * s >= kPairMinBlocks) return s;
+  return grp;
+}
+
+int64_t flash_bwd_part_floats(int64_t T, int n_q, int n_kv) {
+  return (int64_t)(flash_bwd_splits(T, n_q, n_kv) - 1) * 2 * T * n_kv * HD;
+}
 
 hipError_t launch_flash_fwd(const FlashFwd& a, hipStream_t st) {
   if (a.T == 0 || a.n_q == 0) return hipSuccess;
@@ -636,11 +683,22 @@ hipError_t launch_flash_bwd(const FlashBwd& a, hipStream_t st) {
   const int nkb = (int)((a.T + 127) / 128);
   const int npb = (nkb + 1) / 2;
   const int n_kv = a.n_q / a.grp;
-  const int pair_kv = (int64_t)npb * n_kv >= kPairMinBlocks;
-  hipLaunchKernelGGL(k_flash_bwd_dkdv, dim3((unsigned)((pair_kv ? npb : nkb) * n_kv)), dim3(kT), 0,
-                     st, a, pair_kv);
+  const int ns = flash_bwd_splits(a.T, a.n_q, n_kv);
+  if (ns > 1 && !a.part) return hipErrorInvalidValue;
+  const int pair_kv = (int64_t)npb * n_kv * ns >= kPairMinBlocks;
+  hipLaunchKernelGGL(k_flash_bwd_dkdv, dim3((unsigned)((pair_kv ? npb : nkb) * n_kv * ns)),
+                     dim3(kT), 0, st, a, pair_kv, ns);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (ns > 1) {
+    const int64_t ldp = (int64_t)n_kv * HD;
+    const int64_t n4 = 2 * a.T * ldp / 4;
+    const unsigned nb = (unsigned)std::min<int64_t>((n4 + kT - 1) / kT, 2048);
+    hipLaunchKernelGGL(k_kv_part_add, dim3(nb), dim3(kT), 0, st, a.dK, a.dV, a.lddk, a.part, a.T,
+                       ldp, ns);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(k_flash_bwd_dq, dim3((unsigned)(nkb * a.n_q)), dim3(kT), 0, st, a);
   return hipGetLastError();
 }

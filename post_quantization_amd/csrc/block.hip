@@ -112,6 +112,7 @@ struct Ws {
   Stats a_qkv, a_q, a_k, a_v, a_o, a_f, a_d;
   // backward
   float *dy, *gA, *gGU, *gxn2, *dh1, *gO, *Datt, *gQh, *gKh, *gVh, *gQr, *gKr, *gY;
+  float* attn_part;   // partial dK, dV of the attention backward's query-head splits
   uint16_t *dyb, *gGUb, *dh1b, *gOb, *gYb;
   float *cs, *gs_full, *gd_full, *gsa_full;
   float *rq, *csws, *msews;
@@ -158,6 +159,7 @@ Ws layout(const Dims& m, void* base) {
     w.gO = b.take<float>(T * dq); w.gOb = b.take<uint16_t>(T * dq);
     w.Datt = b.take<float>(m.nq * T);
     w.gQh = b.take<float>(T * dq); w.gKh = b.take<float>(T * dk); w.gVh = b.take<float>(T * dk);
+    w.attn_part = b.take<float>(flash_bwd_part_floats(T, (int)m.nq, (int)m.nkv));
     w.gQr = b.take<float>(T * dq); w.gKr = b.take<float>(T * dk);
     w.gY = b.take<float>(T * nqkv);
     w.gYb = b.take<uint16_t>(T * nqkv);
@@ -750,6 +752,7 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
     f.scale2 = (float)(1.4426950408889634 / sqrt((double)m.hd));
     f.lse2 = w.lse2; f.D = w.Datt;
     f.dQ = w.gQh; f.lddq = dq; f.dK = w.gKh; f.dV = w.gVh; f.lddk = dk;
+    f.part = w.attn_part;
     CK(launch_flash_bwd(f, st));
   }
   // Q~ / K~ / V quantizers and s_a

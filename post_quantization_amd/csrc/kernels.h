@@ -240,7 +240,14 @@ struct FlashBwd {
   int64_t lddq;
   float *dK, *dV;           // [T x n_kv*128] fp32, row stride lddk
   int64_t lddk;
+  // flash_bwd_part_floats(T, n_q, n_kv) floats of scratch for the partial dK, dV of
+  // the query-head splits beyond the first (nullptr when that count is 0)
+  float* part;
 };
+// Query-head splits of the dK/dV pass: a grouped K/V head's query heads are shared
+// over this many workgroups when the K/V heads alone leave compute units idle.
+int flash_bwd_splits(int64_t T, int n_q, int n_kv);
+int64_t flash_bwd_part_floats(int64_t T, int n_q, int n_kv);
 hipError_t launch_flash_fwd(const FlashFwd& a, hipStream_t st);
 hipError_t launch_attn_bwd_prep(const float* gO, const float* O, int64_t ld, int64_t T, int n_q,
                                 float* D, uint16_t* gOb, int64_t ldb, hipStream_t st);

@@ -6,8 +6,10 @@ of Q~ and K~, the softmax output kept in full precision) at the block workloads'
 own sizes: T 2048 with 32 query heads on 32 KV heads (the 7B-shaped block: the
 forward, the key-stationary dK/dV kernel and the query-stationary dQ kernel all run
 their paired causal blocks) and with 64 query heads on 8 KV heads (the 70B-shaped
-block: forward and dQ paired, dK/dV unpaired); plus a ragged paired case (T 2000),
-small unpaired ones with ragged tails, and a single query.
+block: every kernel paired, the dK/dV kernel's query heads split four ways, with
+the partial dK, dV added afterwards); plus a ragged paired case (T 2000), small
+unpaired ones with ragged tails (the grouped ones with split query heads), and a
+single query.
 
 The oracle (float64) rounds P to bf16 for the P V product, as the kernel's operand
 is (reading R20).  Inputs are bf16-exact, so the kernel's bf16 copy of dO is
