@@ -315,21 +315,34 @@ hipError_t aq(const void* X, int x_dt, int64_t T, int64_t C, int64_t ldx, int mo
               hipStream_t stream, omq_timer* tm, int32_t* nf, uint8_t* codes = nullptr,
               int64_t ldq = 0,
               int code_off = 0, float* rms_out = nullptr, float* rstd = nullptr,
-              float eps = 0.f) {
+              float eps = 0.f, const float* rope_cos = nullptr, const float* rope_sin = nullptr,
+              float* rope_out = nullptr) {
   RowQuantFwd a;
   a.x = X; a.x_dt = x_dt; a.rows = T; a.cols = C; a.ldx = ldx;
   a.rms_out = rms_out; a.rstd = rstd; a.eps = eps;
+  a.rope_cos = rope_cos; a.rope_sin = rope_sin; a.rope_out = rope_out;
   a.let_mode = mode; a.s = s; a.delta = delta; a.nbits = abits;
   a.out = out; a.out_dt = OMQ_BF16; a.ldo = C;
   a.h = st.h; a.z = st.z; a.amax = st.amax; a.amin = st.amin;
   if (codes && abits < 16) { a.codes = codes; a.ldq = ldq; a.code_off = code_off; a.qsum = st.qsum; }
   if (abits < 16) a.nonfinite = nf;
-  // algorithmic bytes: read X, write X_hat (and the codes, and the normalized rows)
+  // algorithmic bytes: read X, write X_hat (and the codes, and the normalized or
+  // rotated rows)
   const double bytes = (double)T * (double)C *
                        ((x_dt == OMQ_F32 ? 4.0 : 2.0) + 2.0 + (a.codes ? 1.0 : 0.0) +
-                        (rms_out ? 4.0 : 0.0));
+                        (rms_out || rope_out ? 4.0 : 0.0));
   return timed(abits < 16 ? tm : nullptr, OMQ_TIMED_ACT_QUANT, bytes, stream,
                [&] { return launch_rowquant_fwd(a, stream); });
+}
+
+// whether aq can rotate float32 rows of C columns (row stride ldx) itself (RoPE)
+bool aq_rope_ok(int64_t T, int64_t C, int64_t ldx, int abits) {
+  RowQuantFwd a;
+  a.x_dt = OMQ_F32; a.rows = T; a.cols = C; a.ldx = ldx; a.nbits = abits;
+  a.out_dt = OMQ_BF16; a.ldo = C;
+  static const float one = 1.f;
+  a.rope_cos = a.rope_sin = &one;            // presence only
+  return rowquant_fwd_rope_ok(a);
 }
 
 // n bytes (a multiple of 4, 4-byte aligned) set to zero by a fill kernel
@@ -460,14 +473,24 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
     else
       CK(gemm(w.Xqkv, d, w.Wqkv, d, w.Yqkv, nqkv, T, nqkv, d, fp ? nullptr : w.Bt_qkv, nullptr,
               0, 0, st, tm));
-    CK(launch_rope2(w.Yqkv, nqkv, w.Qr, dq, m.nq, w.Yqkv + dq, nqkv, w.Kr, dk, m.nkv, T, m.hd,
-                    w.cos_t, w.sin_t, 0, st));
-    // s_a on the affinity, then Q/K/V quantized per token
+    // RoPE, s_a on the affinity, then Q/K/V quantized per token; the per-token
+    // quantizers of Q and K rotate their rows themselves where they can
     const bool sa = m.use_sa && !fp;
-    CK(aq(w.Qr, OMQ_F32, T, dq, dq, sa ? OMQ_LET_DIV : OMQ_LET_NONE, kv.sa_q, nullptr, ab, w.Qh,
-          w.a_q, st, tm, nf));
-    CK(aq(w.Kr, OMQ_F32, T, dk, dk, sa ? OMQ_LET_MUL : OMQ_LET_NONE, th + (sa ? t.s_a : 0),
-          nullptr, ab, w.Kh, w.a_k, st, tm, nf));
+    if (aq_rope_ok(T, dq, nqkv, ab) && aq_rope_ok(T, dk, nqkv, ab)) {
+      CK(aq(w.Yqkv, OMQ_F32, T, dq, nqkv, sa ? OMQ_LET_DIV : OMQ_LET_NONE, kv.sa_q, nullptr, ab,
+            w.Qh, w.a_q, st, tm, nf, nullptr, 0, 0, nullptr, nullptr, 0.f, w.cos_t, w.sin_t,
+            w.Qr));
+      CK(aq(w.Yqkv + dq, OMQ_F32, T, dk, nqkv, sa ? OMQ_LET_MUL : OMQ_LET_NONE,
+            th + (sa ? t.s_a : 0), nullptr, ab, w.Kh, w.a_k, st, tm, nf, nullptr, 0, 0, nullptr,
+            nullptr, 0.f, w.cos_t, w.sin_t, w.Kr));
+    } else {
+      CK(launch_rope2(w.Yqkv, nqkv, w.Qr, dq, m.nq, w.Yqkv + dq, nqkv, w.Kr, dk, m.nkv, T, m.hd,
+                      w.cos_t, w.sin_t, 0, st));
+      CK(aq(w.Qr, OMQ_F32, T, dq, dq, sa ? OMQ_LET_DIV : OMQ_LET_NONE, kv.sa_q, nullptr, ab, w.Qh,
+            w.a_q, st, tm, nf));
+      CK(aq(w.Kr, OMQ_F32, T, dk, dk, sa ? OMQ_LET_MUL : OMQ_LET_NONE, th + (sa ? t.s_a : 0),
+            nullptr, ab, w.Kh, w.a_k, st, tm, nf));
+    }
     CK(aq(w.Yqkv + dq + dk, OMQ_F32, T, dk, nqkv, OMQ_LET_NONE, nullptr, nullptr, ab, w.Vh, w.a_v,
           st, tm, nf));
     // causal attention, float32 softmax, fused
@@ -590,6 +613,9 @@ struct LinBwd {
   float* gx_out;         // dL/dX [T x K]
   float* gs_x;
   float* gd_x;
+  // q|k|v: the Q and K columns of gY come from their rotated gradients (inverse RoPE
+  // on the way to the bf16 copy); NULL otherwise
+  const RopeIn* rope;
 };
 
 hipError_t lin_bwd_fused(const Ws& w, const LinBwd& L, int64_t T, int wbits, int abits,
@@ -597,10 +623,12 @@ hipError_t lin_bwd_fused(const Ws& w, const LinBwd& L, int64_t T, int wbits, int
                          omq_timer* tm) {
   hipError_t e;
   const int64_t N = L.N, K = L.K;
-  if (!L.have_gYb &&
-      (e = launch_cvt_bf16_colsum(L.gY, T, N, L.gYb, L.fold ? w.cs : nullptr, w.csws, st)) !=
-          hipSuccess)
-    return e;
+  if (!L.have_gYb) {
+    e = L.rope ? launch_cvt_bf16_colsum_rope(L.gY, T, N, *L.rope, L.gYb,
+                                             L.fold ? w.cs : nullptr, w.csws, st)
+               : launch_cvt_bf16_colsum(L.gY, T, N, L.gYb, L.fold ? w.cs : nullptr, w.csws, st);
+    if (e != hipSuccess) return e;
+  }
   int64_t nsl, ntl;
   // weight side (skipped when no learnable parameter depends on these weights)
   if (wbits < 16 || L.s_w) {
@@ -767,10 +795,10 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
   CK(abwd(w, w.gVh, T, dk, w.Yqkv + dq + dk, OMQ_F32, nqkv, OMQ_LET_NONE, nullptr, nullptr, ab,
           w.a_v, w.gY + dq + dk, nqkv, COL_NONE, nullptr, nullptr, 0, st));
   if (sa && m.grp > 1) CK(launch_kv_reduce_add(w.gsa_full, m.nq, m.nkv, m.hd, dth + t.s_a, st));
-  CK(launch_rope2(w.gQr, dq, w.gY, nqkv, m.nq, w.gKr, dk, w.gY + dq, nqkv, m.nkv, T, m.hd,
-                  w.cos_t, w.sin_t, 1, st));
-  // q / k / v with the shared qkv LET site
+  // q / k / v with the shared qkv LET site; the inverse RoPE of the Q and K gradients
+  // runs inside the bf16 conversion of dL/dY
   {
+    const RopeIn rp{w.gQr, dq, dq, w.gKr, dk, dk, w.cos_t, w.sin_t};
     const WSeg segs[3] = {{W[LQ], dq, LQ}, {W[LK], dk, LK}, {W[LV], dk, LV}};
     LinBwd L{};
     L.group = m.group;
@@ -781,6 +809,7 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
     // dL/dx of the block input is not needed (x is no parameter): not written
     L.d_x = th + t.d_qkv; L.ast = w.a_qkv; L.gx_out = nullptr;
     L.gs_x = dth + t.s_qkv; L.gd_x = dth + t.d_qkv;
+    L.rope = &rp;
     CK(lin_bwd_fused(w, L, T, wb, ab, th, t, dth, st, tm));
   }
   return OMQ_OK;

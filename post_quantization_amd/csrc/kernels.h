@@ -45,12 +45,21 @@ struct RowQuantFwd {
   float* rms_out = nullptr;
   float* rstd = nullptr;
   float eps = 0.f;
+  // rope_out set (float32 activations in heads of 128 columns, rowquant_fwd_rope_ok):
+  // each row is first rotated, RoPE with position = the row and tables rope_cos,
+  // rope_sin [rows x 64] (rotate-half: column k of a head pairs with k + 64); the
+  // rotated rows go to rope_out ([rows x cols] float32) and are then quantized
+  const float* rope_cos = nullptr;
+  const float* rope_sin = nullptr;
+  float* rope_out = nullptr;
 };
 hipError_t launch_rowquant_fwd(const RowQuantFwd& a, hipStream_t st);
 // whether launch_rowquant_fwd takes a.nseg > 1 (the whole-row LDS kernel applies)
 bool rowquant_fwd_segments_ok(const RowQuantFwd& a);
 // whether launch_rowquant_fwd takes a.rms_out
 bool rowquant_fwd_rms_ok(const RowQuantFwd& a);
+// whether launch_rowquant_fwd takes a.rope_out
+bool rowquant_fwd_rope_ok(const RowQuantFwd& a);
 
 enum ColMode { COL_NONE = 0, COL_WEIGHT = 1, COL_ACT_DIV = 2, COL_ACT_MUL = 3 };
 
@@ -172,6 +181,18 @@ void gemm_ste_extents(int64_t rows, int64_t cols, int64_t* nslabs, int64_t* ntil
 // set (ws: colsum_ws_bytes(rows, cols))
 hipError_t launch_cvt_bf16_colsum(const float* in, int64_t rows, int64_t cols, uint16_t* out,
                                   float* colsum, float* ws, hipStream_t st);
+// The same for a q|k|v gradient whose Q and K heads (head dimension 128) arrive as
+// gradients of the rotated values: columns [0, qcols) are read from q and
+// [qcols, qcols + kcols) from k, each through the inverse RoPE (cos/sin tables
+// [rows x 64]) with the rotation kernel's arithmetic; the other columns from `in`.
+struct RopeIn {
+  const float* q; int64_t ldq, qcols;
+  const float* k; int64_t ldk, kcols;
+  const float *cos_t, *sin_t;
+};
+hipError_t launch_cvt_bf16_colsum_rope(const float* in, int64_t rows, int64_t cols,
+                                       const RopeIn& rp, uint16_t* out, float* colsum, float* ws,
+                                       hipStream_t st);
 // Column sums in two deterministic stages: partial sums over chunks of kColsumRows
 // rows ([nparts][cols] per kind), then out_k[c] (+)= sum of the nparts partials.
 constexpr int kColsumRows = 64;

@@ -372,6 +372,30 @@ OMQ_DEV void load8f(const float* p, int64_t c, int n, float v[8]) {
   }
 }
 
+// RoPE of the 8 consecutive columns c .. c+7 of row r, in heads of 128 columns with
+// the row as the position: column k < 64 of a head becomes x_k cos - x_(k+64) sin and
+// column k + 64 becomes x_(k+64) cos + x_k sin (cos, sin of table column k; products
+// rounded before the sum).  In the block-per-row kernel the partner columns are 64
+// columns, 8 lanes, away in the same wave, and a head's 16 lanes are all in range
+// or all out.  The rotated values are also written to rope_out.
+OMQ_DEV void rope8(const RowQuantFwd& a, int64_t r, int64_t c, float (&v)[8]) {
+  float p[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) p[j] = __shfl_xor(v[j], 8);
+  const int kh = (int)(c & 127);
+  float cs[8], sn[8];
+  load8f(a.rope_cos + r * 64, kh & 63, 8, cs);
+  load8f(a.rope_sin + r * 64, kh & 63, 8, sn);
+  if (kh < 64) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = v[j] * cs[j] - p[j] * sn[j];
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = v[j] * cs[j] + p[j] * sn[j];
+  }
+  store8(a.rope_out, OMQ_F32, r * a.cols + c, v);
+}
+
 // Long rows (up to NC * 2048 elements, columns a multiple of 8), one 4-wave block per
 // row: each thread keeps NC chunks of 8 consecutive elements in registers (16-byte
 // bf16 loads, 2 x 16-byte float32 loads), so HBM sees one read of x and one write of
@@ -379,7 +403,8 @@ OMQ_DEV void load8f(const float* p, int64_t c, int n, float v[8]) {
 // product with the exact quotient behind a wave-uniform branch, as in the
 // whole-row LDS kernel.  Same results as k_rowquant_fwd_reg.
 // RMS: the row is first divided by its root mean square (as the whole-row LDS kernel).
-template <int XDT, int NC, int LET, bool RMS = false>
+// ROPE: the row is first rotated (rope8; float32 rows, heads of 128 columns).
+template <int XDT, int NC, int LET, bool RMS = false, bool ROPE = false>
 __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_blk8(RowQuantFwd a) {
   const int64_t r = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wid = wave_id();
@@ -393,6 +418,7 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_blk8(RowQuantFwd a) {
     if (c < cols) {
       float v[8];
       load8(xr, XDT, c, v);
+      if constexpr (ROPE) rope8(a, r, c, v);
       if constexpr (RMS) {                         // LET after the normalization below
 #pragma unroll
         for (int j = 0; j < 8; ++j) xt[k][j] = v[j];
@@ -1472,12 +1498,17 @@ __global__ __launch_bounds__(kThreads) void k_colsum_part(const float* in, int64
 // set, the column sums of each kColsumRows-row chunk, in one pass over dY.
 // VEC 8 (cols % 8 == 0): a workgroup takes 512 columns (8 per lane) of one chunk,
 // its 4 waves take the chunk's rows in turn, and their sums are added in LDS in a
-// fixed order.  VEC 1: one column per thread over the chunk.
-template <int VEC>
+// fixed order.  VEC 1: one column per thread over the chunk.  ROPE (VEC 8 only):
+// the columns of the Q and K heads come from rp.q / rp.k through the inverse RoPE,
+// x c + x' s in the first half of a head and x c - x' s in the second, x' the
+// element 64 positions away and c, s the row's table entries (products rounded
+// before the sum, as in the rotation kernel).
+template <int VEC, bool ROPE = false>
 __global__ __launch_bounds__(kThreads) void k_cvt_bf16_colpart(const float* __restrict__ in,
                                                                int64_t rows, int64_t cols,
                                                                uint16_t* __restrict__ out,
-                                                               float* __restrict__ part) {
+                                                               float* __restrict__ part,
+                                                               RopeIn rp = {}) {
   const int64_t r0 = (int64_t)blockIdx.y * kColsumRows;
   const int64_t r1 = min(r0 + kColsumRows, rows);
   if constexpr (VEC == 8) {
@@ -1485,13 +1516,41 @@ __global__ __launch_bounds__(kThreads) void k_cvt_bf16_colpart(const float* __re
     const int lane = threadIdx.x & 63, w = wave_id();
     const int64_t c = ((int64_t)blockIdx.x * 64 + lane) * 8;
     const bool ok = c < cols;
+    // (ROPE) this thread's 8 columns: their source, the partner offset, the sign
+    const bool rot = ROPE && c < rp.qcols + rp.kcols;
+    const bool isq = c < rp.qcols;
+    const float* src = !rot ? nullptr : isq ? rp.q + c : rp.k + (c - rp.qcols);
+    const int64_t lds = isq ? rp.ldq : rp.ldk;
+    const int kh = (int)(c & 127);                 // position in the head (qcols % 128 == 0)
+    const int pofs = kh < 64 ? 64 : -64;
+    const float sg = kh < 64 ? 1.f : -1.f;
     float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (ok) {
 #pragma unroll 4
       for (int64_t r = r0 + w; r < r1; r += 4) {
-        const float* p = in + r * cols + c;
-        const float4 a = *reinterpret_cast<const float4*>(p);
-        const float4 b = *reinterpret_cast<const float4*>(p + 4);
+        float4 a, b;
+        if (rot) {
+          const float* x = src + r * lds;
+          const float* cs = rp.cos_t + r * 64 + (kh & 63);
+          const float* sn = rp.sin_t + r * 64 + (kh & 63);
+          const float4 x0 = *reinterpret_cast<const float4*>(x);
+          const float4 x1 = *reinterpret_cast<const float4*>(x + 4);
+          const float4 p0 = *reinterpret_cast<const float4*>(x + pofs);
+          const float4 p1 = *reinterpret_cast<const float4*>(x + pofs + 4);
+          const float4 c0 = *reinterpret_cast<const float4*>(cs);
+          const float4 c1 = *reinterpret_cast<const float4*>(cs + 4);
+          const float4 s0 = *reinterpret_cast<const float4*>(sn);
+          const float4 s1 = *reinterpret_cast<const float4*>(sn + 4);
+          // sg * (p s) is exact: the sum is the rotation kernel's a c + b s or b c - a s
+          a = make_float4(x0.x * c0.x + sg * (p0.x * s0.x), x0.y * c0.y + sg * (p0.y * s0.y),
+                          x0.z * c0.z + sg * (p0.z * s0.z), x0.w * c0.w + sg * (p0.w * s0.w));
+          b = make_float4(x1.x * c1.x + sg * (p1.x * s1.x), x1.y * c1.y + sg * (p1.y * s1.y),
+                          x1.z * c1.z + sg * (p1.z * s1.z), x1.w * c1.w + sg * (p1.w * s1.w));
+        } else {
+          const float* p = in + r * cols + c;
+          a = *reinterpret_cast<const float4*>(p);
+          b = *reinterpret_cast<const float4*>(p + 4);
+        }
         s[0] += a.x; s[1] += a.y; s[2] += a.z; s[3] += a.w;
         s[4] += b.x; s[5] += b.y; s[6] += b.z; s[7] += b.w;
         *reinterpret_cast<uint4*>(out + r * cols + c) =
@@ -1643,6 +1702,26 @@ bool launch_fwd_blk8(const RowQuantFwd& a, hipStream_t st) {
                          st, a);                                                            \
     return true;                                                                            \
   }
+  if (a.rope_out) {
+    if constexpr (XDT == OMQ_F32) {
+#define OMQ_FWD_BLK8P(N)                                                                    \
+  if (nch <= N) {                                                                           \
+    if (a.let_mode == OMQ_LET_DIV)                                                          \
+      hipLaunchKernelGGL((k_rowquant_fwd_blk8<XDT, N, OMQ_LET_DIV, false, true>), grid,     \
+                         dim3(kThreads), 0, st, a);                                         \
+    else if (a.let_mode == OMQ_LET_MUL)                                                     \
+      hipLaunchKernelGGL((k_rowquant_fwd_blk8<XDT, N, OMQ_LET_MUL, false, true>), grid,     \
+                         dim3(kThreads), 0, st, a);                                         \
+    else                                                                                    \
+      hipLaunchKernelGGL((k_rowquant_fwd_blk8<XDT, N, OMQ_LET_NONE, false, true>), grid,    \
+                         dim3(kThreads), 0, st, a);                                         \
+    return true;                                                                            \
+  }
+      OMQ_FWD_BLK8P(1) OMQ_FWD_BLK8P(2) OMQ_FWD_BLK8P(4) OMQ_FWD_BLK8P(8) OMQ_FWD_BLK8P(16)
+#undef OMQ_FWD_BLK8P
+    }
+    return false;
+  }
   if (a.rms_out) {
 #define OMQ_FWD_BLK8R(N)                                                                    \
   if (nch <= N) {                                                                           \
@@ -1688,6 +1767,15 @@ bool rowquant_fwd_rms_ok(const RowQuantFwd& a) {
          (a.x_dt == OMQ_F32 || a.ldx % 8 == 0);
 }
 
+bool rowquant_fwd_rope_ok(const RowQuantFwd& a) {
+  // float32 activations in heads of 128 columns (no logits, fold or normalization):
+  // the block-per-row kernel, rows of 2048 .. 32768 columns
+  return a.group == 0 && a.nbits < 16 && a.nseg == 1 && !a.fold_delta && !a.a_gamma &&
+         !a.rms_out && a.x_dt == OMQ_F32 && a.cols % 128 == 0 && a.cols >= 2048 &&
+         a.cols <= 32768 && a.ldx % 4 == 0 && a.ldo % (a.out_dt == OMQ_F32 ? 4 : 8) == 0 &&
+         a.rope_cos && a.rope_sin;
+}
+
 bool rowquant_fwd_segments_ok(const RowQuantFwd& a) {
   // the whole-row LDS kernel: rows of 512 n columns (n <= 8), 16-byte rows
   return a.group == 0 && a.nbits < 16 &&
@@ -1699,6 +1787,12 @@ hipError_t launch_rowquant_fwd(const RowQuantFwd& a, hipStream_t st) {
   if (a.rows == 0 || a.cols == 0) return hipSuccess;
   if (a.nseg > 1 && (!rowquant_fwd_segments_ok(a) || a.nseg > 3)) return hipErrorInvalidValue;
   if (a.rms_out && !rowquant_fwd_rms_ok(a)) return hipErrorInvalidValue;
+  if (a.rope_out) {
+    if (!rowquant_fwd_rope_ok(a) || (a.qsum && !a.codes)) return hipErrorInvalidValue;
+    if (a.codes && a.code_off != 0 && a.code_off != 128) return hipErrorInvalidValue;
+    if (!launch_fwd_blk8<OMQ_F32>(a, st)) return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   // code sums come with the codes, per whole row
   if (a.qsum && (!a.codes || a.group > 0 || a.nbits >= 16)) return hipErrorInvalidValue;
   // stored codes are q itself or q - 128 (8-bit codes as signed bytes)
@@ -1869,6 +1963,24 @@ hipError_t launch_bias_fold(const void* W, int w_dt, int64_t rows, int64_t cols,
 
 size_t colsum_ws_bytes(int64_t rows, int64_t cols) {
   return (size_t)(((rows + kColsumRows - 1) / kColsumRows) * cols) * sizeof(float) + 256;
+}
+
+hipError_t launch_cvt_bf16_colsum_rope(const float* in, int64_t rows, int64_t cols,
+                                       const RopeIn& rp, uint16_t* out, float* colsum, float* ws,
+                                       hipStream_t st) {
+  if (cols % 8 || rp.qcols % 128 || rp.kcols % 128 || rp.qcols + rp.kcols > cols ||
+      rp.ldq % 4 || rp.ldk % 4 || !rp.q || !rp.k || !rp.cos_t || !rp.sin_t)
+    return hipErrorInvalidValue;
+  if (cols == 0) return hipSuccess;
+  const int64_t np = (rows + kColsumRows - 1) / kColsumRows;
+  if (np == 0) return colsum ? launch_fill_f32(colsum, cols, 0.f, st) : hipSuccess;
+  float* part = colsum ? ws : nullptr;
+  const unsigned cb = (unsigned)((cols / 8 + 63) / 64);
+  hipLaunchKernelGGL((k_cvt_bf16_colpart<8, true>), dim3(cb, (unsigned)np), dim3(kThreads), 0, st,
+                     in, rows, cols, out, part, rp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !colsum) return e;
+  return launch_part_colsum(ws, (int)np, 1, cols, colsum, nullptr, 0, st);
 }
 
 hipError_t launch_cvt_bf16_colsum(const float* in, int64_t rows, int64_t cols, uint16_t* out,
