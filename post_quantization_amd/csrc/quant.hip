@@ -1226,39 +1226,58 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_bwd_tile(RowQuantBwd a, i
   }
 }
 
-// One quantizer row's finalizer: the LWC-logit gradients, the max / min scatter into
-// the upstream gradient (one writer per row), and the row's two scatter terms of the
-// column outputs (column, term for out0, term for out1: argmax first, then argmin).
-// gh, gzs: the row's summed partials.
+// One quantizer row's finalizer, in two parts.  row_fetch: the row's segment
+// (concatenated weights: its x rows and logits), its extreme columns, their x and
+// x~ values and the clipping strengths (issued before the row's partial sums are
+// read, so the dependent loads overlap them).  row_finish: the LWC-logit gradients,
+// the max / min scatter into the upstream gradient (one writer per row), and the
+// row's two scatter terms of the column outputs (column, term for out0, term for
+// out1: argmax first, then argmin).  gh, gzs: the row's summed partials.
+struct RowFetch {
+  int64_t r, pl;
+  float *gg_g, *gg_b;
+  int iM, im;
+  float xM, xm, M, m, gamma, beta;
+};
+
 template <int XDT>
-OMQ_DEV void row_finish(const RowQuantBwd& a, int64_t p, float gh, float gzs, int (&cs)[2],
-                        float (&v0)[2], float (&v1)[2]) {
+OMQ_DEV RowFetch row_fetch(const RowQuantBwd& a, int64_t p) {
+  RowFetch f;
   const int64_t ng = a.group > 0 ? a.cols / 128 : 1;
-  const int64_t r = p / ng;
-  // the row's segment (concatenated weights): its x rows and logits
+  f.r = p / ng;
   const void* xb = a.x;
   const float *lg_g = a.a_gamma, *lg_b = a.a_beta;
-  float *gg_g = a.g_agamma, *gg_b = a.g_abeta;
-  int64_t rl = r, pl = p;
+  f.gg_g = a.g_agamma;
+  f.gg_b = a.g_abeta;
+  int64_t rl = f.r;
+  f.pl = p;
   if (a.nseg > 1) {
-    const int sg = (r >= a.seg_end[0]) + (a.nseg > 2 && r >= a.seg_end[1]);
+    const int sg = (f.r >= a.seg_end[0]) + (a.nseg > 2 && f.r >= a.seg_end[1]);
     const int64_t r0 = sg == 0 ? 0 : a.seg_end[sg - 1];
     xb = a.xseg[sg];
-    lg_g = a.agseg[sg]; lg_b = a.abseg[sg]; gg_g = a.gagseg[sg]; gg_b = a.gabseg[sg];
-    rl = r - r0;
-    pl = p - r0 * ng;
+    lg_g = a.agseg[sg]; lg_b = a.abseg[sg]; f.gg_g = a.gagseg[sg]; f.gg_b = a.gabseg[sg];
+    rl = f.r - r0;
+    f.pl = p - r0 * ng;
   }
   const char* xr = reinterpret_cast<const char*>(xb) + rl * a.ldx * (XDT == OMQ_F32 ? 4 : 2);
   auto xval = [&](int64_t c) -> float {
     return XDT == OMQ_F32 ? reinterpret_cast<const float*>(xr)[c]
                           : bf16_to_f32(reinterpret_cast<const uint16_t*>(xr)[c]);
   };
-  const int iM = a.amax[p], im = a.amin[p];
-  const float xM = xval(iM), xm = xval(im);
-  const float M = let_x(xM, a.let_mode, a.s, a.delta, iM);
-  const float m = let_x(xm, a.let_mode, a.s, a.delta, im);
-  const float gamma = lg_g ? sigmoid_f32(lg_g[pl]) : 1.f;
-  const float beta = lg_b ? sigmoid_f32(lg_b[pl]) : 1.f;
+  f.iM = a.amax[p];
+  f.im = a.amin[p];
+  f.xM = xval(f.iM);
+  f.xm = xval(f.im);
+  f.M = let_x(f.xM, a.let_mode, a.s, a.delta, f.iM);
+  f.m = let_x(f.xm, a.let_mode, a.s, a.delta, f.im);
+  f.gamma = lg_g ? sigmoid_f32(lg_g[f.pl]) : 1.f;
+  f.beta = lg_b ? sigmoid_f32(lg_b[f.pl]) : 1.f;
+  return f;
+}
+
+OMQ_DEV void row_finish(const RowQuantBwd& a, const RowFetch& f, float gh, float gzs,
+                        int (&cs)[2], float (&v0)[2], float (&v1)[2]) {
+  const float M = f.M, m = f.m, gamma = f.gamma, beta = f.beta;
   const RowQ q = row_step(M, m, gamma, beta, a.nbits);
   const float h = q.h;
   const float gz = -h * gzs;
@@ -1266,12 +1285,12 @@ OMQ_DEV void row_finish(const RowQuantBwd& a, int64_t p, float gh, float gzs, in
   const float gt1 = G / q.Q;
   const float gt2 = -G / q.Q - gz / h;
   const float gM = gt1 * gamma, gm = gt2 * beta;
-  if (gg_g) gg_g[pl] = (gt1 * M) * gamma * (1.f - gamma);
-  if (gg_b) gg_b[pl] = (gt2 * m) * beta * (1.f - beta);
+  if (f.gg_g) f.gg_g[f.pl] = (gt1 * M) * gamma * (1.f - gamma);
+  if (f.gg_b) f.gg_b[f.pl] = (gt2 * m) * beta * (1.f - beta);
   // scatter of dL/dmax and dL/dmin into the gradient of x~ at arg_max / arg_min
-  const int idx[2] = {iM, im};
+  const int idx[2] = {f.iM, f.im};
   const float gv[2] = {gM, gm};
-  const float xo[2] = {xM, xm};
+  const float xo[2] = {f.xM, f.xm};
   const float xtl[2] = {M, m};
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
@@ -1281,7 +1300,7 @@ OMQ_DEV void row_finish(const RowQuantBwd& a, int64_t p, float gh, float gzs, in
       float up = gsc;
       if (a.let_mode == OMQ_LET_DIV) up = gsc / a.s[c];
       else if (a.let_mode == OMQ_LET_MUL) up = gsc * a.s[c];
-      a.gx[r * a.ldgx + c] += up;
+      a.gx[f.r * a.ldgx + c] += up;
     }
     cs[e] = c;
     v0[e] = 0.f;
@@ -1325,6 +1344,8 @@ __global__ __launch_bounds__(kFinThreads) void k_ste_rows(RowQuantBwd a, int nsl
   const int i = (int)(threadIdx.x / LPR);               // row of the tile
   const bool valid = i < nr;
   const int64_t p = (r0 + i) * ng + g;                  // its quantizer row
+  RowFetch rf;
+  if (valid && sub == 0) rf = row_fetch<XDT>(a, p);
   float gh = 0.f, gzs = 0.f;
   if (valid) {
     for (int s = sub; s < nslabs; s += LPR) {
@@ -1341,7 +1362,7 @@ __global__ __launch_bounds__(kFinThreads) void k_ste_rows(RowQuantBwd a, int nsl
   if (valid && sub == 0) {
     int cs[2];
     float v0[2], v1[2];
-    row_finish<XDT>(a, p, gh, gzs, cs, v0, v1);
+    row_finish(a, rf, gh, gzs, cs, v0, v1);
     if (merge) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
