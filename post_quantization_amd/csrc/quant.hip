@@ -149,6 +149,46 @@ OMQ_DEV void dequant8(const float (&rr)[8], const RowQ& q, float (&qq)[8], float
 }
 
 // ---------------------------------------------------------------------------
+// forward, pass-through (16 bits and more: x~ only, no rounding): 8 consecutive
+// columns per thread and step, 16-byte accesses, the LET mode fixed at compile time;
+// the same arithmetic as the per-row kernel's pass-through below
+// ---------------------------------------------------------------------------
+OMQ_DEV void load8x(const char* xr, int dt, int64_t c, float (&v)[8]);
+template <int XDT, int LET>
+__global__ __launch_bounds__(kThreads) void k_rowquant_pass8(RowQuantFwd a) {
+  const int64_t per_row = a.cols / 8, n = a.rows * per_row;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * kThreads) {
+    const int64_t r = i / per_row, c = (i - r * per_row) * 8;
+    const char* xr = reinterpret_cast<const char*>(a.x) + r * a.ldx * (XDT == OMQ_F32 ? 4 : 2);
+    float v[8];
+    load8x(xr, XDT, c, v);
+    if constexpr (LET == OMQ_LET_DIV) {
+      float sv[8], dv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      const float4 s0 = *reinterpret_cast<const float4*>(a.s + c);
+      const float4 s1 = *reinterpret_cast<const float4*>(a.s + c + 4);
+      sv[0] = s0.x; sv[1] = s0.y; sv[2] = s0.z; sv[3] = s0.w;
+      sv[4] = s1.x; sv[5] = s1.y; sv[6] = s1.z; sv[7] = s1.w;
+      if (a.delta) {
+        const float4 d0 = *reinterpret_cast<const float4*>(a.delta + c);
+        const float4 d1 = *reinterpret_cast<const float4*>(a.delta + c + 4);
+        dv[0] = d0.x; dv[1] = d0.y; dv[2] = d0.z; dv[3] = d0.w;
+        dv[4] = d1.x; dv[5] = d1.y; dv[6] = d1.z; dv[7] = d1.w;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = (v[j] - dv[j]) / sv[j];
+    } else if constexpr (LET == OMQ_LET_MUL) {
+      const float4 s0 = *reinterpret_cast<const float4*>(a.s + c);
+      const float4 s1 = *reinterpret_cast<const float4*>(a.s + c + 4);
+      const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = sv[j] * v[j];
+    }
+    store8(a.out, a.out_dt, r * a.ldo + c, v);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // forward: one 256-thread block per row
 // ---------------------------------------------------------------------------
 template <int XDT>
@@ -359,6 +399,8 @@ OMQ_DEV void load8(const char* xr, int dt, int64_t c, float v[8]) {
     }
   }
 }
+
+OMQ_DEV void load8x(const char* xr, int dt, int64_t c, float (&v)[8]) { load8(xr, dt, c, v); }
 
 // 8 consecutive float32 parameters (s, delta) starting at c; n = 8 or 4 valid
 OMQ_DEV void load8f(const float* p, int64_t c, int n, float v[8]) {
@@ -1830,6 +1872,28 @@ hipError_t launch_rowquant_fwd(const RowQuantFwd& a, hipStream_t st) {
     return hipGetLastError();
   }
   dim3 grid((unsigned)a.rows);
+  if (a.nbits >= 16 && a.cols % 8 == 0 && a.ldx % 8 == 0 && a.ldo % 8 == 0 &&
+      (reinterpret_cast<uintptr_t>(a.x) & 15) == 0 && (reinterpret_cast<uintptr_t>(a.out) & 15) == 0 &&
+      (a.let_mode == OMQ_LET_NONE ||
+       ((reinterpret_cast<uintptr_t>(a.s) & 15) == 0 &&
+        (reinterpret_cast<uintptr_t>(a.delta) & 15) == 0))) {
+    const int64_t n8 = a.rows * (a.cols / 8);
+    const unsigned nb = (unsigned)std::min<int64_t>((n8 + kThreads - 1) / kThreads, 8192);
+#define OMQ_PASS8(XD)                                                                        \
+  if (a.let_mode == OMQ_LET_DIV)                                                             \
+    hipLaunchKernelGGL((k_rowquant_pass8<XD, OMQ_LET_DIV>), dim3(nb), dim3(kThreads), 0, st, a); \
+  else if (a.let_mode == OMQ_LET_MUL)                                                        \
+    hipLaunchKernelGGL((k_rowquant_pass8<XD, OMQ_LET_MUL>), dim3(nb), dim3(kThreads), 0, st, a); \
+  else                                                                                       \
+    hipLaunchKernelGGL((k_rowquant_pass8<XD, OMQ_LET_NONE>), dim3(nb), dim3(kThreads), 0, st, a);
+    if (a.x_dt == OMQ_F32) {
+      OMQ_PASS8(OMQ_F32)
+    } else {
+      OMQ_PASS8(OMQ_BF16)
+    }
+#undef OMQ_PASS8
+    return hipGetLastError();
+  }
   if (a.nbits < 16) {
     // float32 rows of 2048 .. 4096 columns (activations): a block per row in registers
     // keeps more rows in flight than staging each in LDS (16 KB a row)
