@@ -231,9 +231,14 @@ size_t omq_attention_bwd_workspace_size(int64_t T, int64_t n_q, int64_t ldq) {
   b.take<float>(n_q * T);       // D = rowsum(dO * O) per (head, query)
   b.take<uint16_t>(T * ldq);    // dO in bf16, rows like Q's
   // partial dK, dV of the query-head splits, for the largest need of any n_kv
+  // dividing n_q (the divisors in pairs i, n_q / i)
+  if (n_q > (int64_t)1 << 30) return 0;
   int64_t part = 0;
-  for (int64_t kv = 1; kv <= n_q; ++kv)
-    if (n_q % kv == 0) part = std::max(part, flash_bwd_part_floats(T, (int)n_q, (int)kv));
+  for (int64_t i = 1; i * i <= n_q; ++i)
+    if (n_q % i == 0) {
+      part = std::max(part, flash_bwd_part_floats(T, (int)n_q, (int)i));
+      part = std::max(part, flash_bwd_part_floats(T, (int)n_q, (int)(n_q / i)));
+    }
   b.take<float>(part);
   return b.off;
 }
