@@ -179,6 +179,20 @@ int omq_code_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* qa, int64_t ld
                   const float* bias, float* C, int64_t ldc, void* stream);
 
 /*
+ * omq_code_gemm4 -- omq_code_gemm on 4-bit codes (n_bits up to 4) stored two to a
+ * byte, the packed form of omq_pack_codes with n_bits = 4: code k of a row in byte
+ * k / 2, the low nibble for even k.  lda, ldb: row strides in bytes (at least K / 2,
+ * multiples of 16); sum_a, sum_b as for omq_code_gemm (sums of the code values).
+ * The same exact product and rounding; half the operand bytes through memory and
+ * the local data share.  M, N and K multiples of 128 (OMQ_E_SHAPE), qa, qb 16-byte
+ * aligned (OMQ_E_ALIGN).
+ */
+int omq_code_gemm4(int64_t M, int64_t N, int64_t K, const uint8_t* qa, int64_t lda,
+                   const float* h_a, const float* z_a, const int32_t* sum_a, const uint8_t* qb,
+                   int64_t ldb, const float* h_b, const float* z_b, const int32_t* sum_b,
+                   const float* bias, float* C, int64_t ldc, void* stream);
+
+/*
  * omq_attention_fwd -- the block's causal attention on its quantized operands
  * (paper reading, section "LET": the affinity of Q~ = Q / s_a and K~ = s_a K, and
  * the softmax output kept in full precision).  Per query head h, with KV head

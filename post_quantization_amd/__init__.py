@@ -147,6 +147,8 @@ _SIGS = {
                         _i64, _int, _vp]),
     "omq_code_gemm": (_int, [_i64, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp,
                              _vp, _vp, _vp, _i64, _vp]),
+    "omq_code_gemm4": (_int, [_i64, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp,
+                             _vp, _vp, _vp, _i64, _vp]),
     "omq_code_rowsum": (_int, [_vp, _i64, _i64, _i64, _vp, _vp]),
     "omq_attention_fwd": (_int, [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64,
                                  _vp, _vp]),
@@ -334,6 +336,18 @@ def code_gemm(qa, h_a, z_a, qb, h_b, z_b, sum_a=None, sum_b=None, bias=None, C=N
     _check("omq_code_gemm", lib().omq_code_gemm(
         M, N, K, _p(qa), K, _p(h_a), _p(z_a), _p(sum_a), _p(qb), K, _p(h_b), _p(z_b), _p(sum_b),
         _p(bias), _p(C), N, _stream()))
+    return C
+
+
+def code_gemm4(qa, h_a, z_a, qb, h_b, z_b, K, sum_a, sum_b, bias=None, C=None):
+    """code_gemm on 4-bit codes packed two to a byte (uint8 [M x K/2], [N x K/2], the
+    low nibble first); K is the number of codes per row, sum_a / sum_b their sums."""
+    M, N = qa.shape[0], qb.shape[0]
+    if C is None:
+        C = torch.empty(M, N, dtype=torch.float32, device=qa.device)
+    _check("omq_code_gemm4", lib().omq_code_gemm4(
+        M, N, K, _p(qa), qa.shape[1], _p(h_a), _p(z_a), _p(sum_a), _p(qb), qb.shape[1], _p(h_b),
+        _p(z_b), _p(sum_b), _p(bias), _p(C), N, _stream()))
     return C
 
 

@@ -190,6 +190,27 @@ int omq_code_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* qa, int64_t ld
   return OMQ_OK;
 }
 
+int omq_code_gemm4(int64_t M, int64_t N, int64_t K, const uint8_t* qa, int64_t lda,
+                   const float* h_a, const float* z_a, const int32_t* sum_a, const uint8_t* qb,
+                   int64_t ldb, const float* h_b, const float* z_b, const int32_t* sum_b,
+                   const float* bias, float* C, int64_t ldc, void* stream) {
+  if (M == 0 || N == 0) return OMQ_OK;             // empty C: nothing read or written
+  if (!qa || !qb || !C || !h_a || !z_a || !sum_a || !h_b || !z_b || !sum_b)
+    return OMQ_E_INVALID_ARG;
+  if (M < 0 || N < 0 || K < 0 || ldc < N || 2 * lda < K || 2 * ldb < K || K > (1 << 17) ||
+      M % 128 || N % 128 || K % 128)
+    return OMQ_E_SHAPE;
+  if (lda % 16 || ldb % 16 || !al16(qa) || !al16(qb)) return OMQ_E_ALIGN;
+  Gemm g;
+  g.codes = 1;
+  g.pack4 = 1;
+  g.A = qa; g.lda = lda; g.B = qb; g.ldb = ldb; g.C = C; g.ldc = ldc; g.bias = bias;
+  g.M = M; g.N = N; g.K = K;
+  g.ha = h_a; g.za = z_a; g.sa = sum_a; g.hb = h_b; g.zb = z_b; g.sb = sum_b;
+  OMQ_HIP_CHECK(launch_gemm(g, S(stream)));
+  return OMQ_OK;
+}
+
 // ---------------------------------------------------------------------------
 // causal attention of the block on its quantized operands
 // ---------------------------------------------------------------------------

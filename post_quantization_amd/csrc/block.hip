@@ -26,7 +26,10 @@ struct Dims {
   // activations both quantized, per row (8-bit codes stored shifted by 128 into
   // signed bytes); code rows padded with zero codes to a multiple of 16 columns
   bool codes;
-  int64_t dp, dqp, Fp;     // padded code-row lengths of the d-, dq- and F-wide inputs
+  // ... and with 4-bit codes on both sides and whole 128 x 128 tiles, the codes two to
+  // a byte (half the bytes the quantizers write and the products read)
+  bool pk;
+  int64_t dp, dqp, Fp;     // code-row strides (bytes) of the d-, dq- and F-wide inputs
   int woff, aoff;          // stored code offsets (128 for 8-bit codes)
   // LWC quantizer rows per output channel of a weight with C_in = cin
   int64_t g_of(int64_t cin) const { return group ? cin / group : 1; }
@@ -42,7 +45,13 @@ Dims dims_of(const omq_block_desc* b) {
   m.group = b->group;
   m.codes = b->wbits <= 8 && b->abits <= 8 && m.group == 0;
   auto up16 = [](int64_t v) { return (v + 15) / 16 * 16; };
-  m.dp = up16(m.d); m.dqp = up16(m.dq); m.Fp = up16(m.F);
+  m.pk = m.codes && b->wbits <= 4 && b->abits <= 4 && m.T % 128 == 0 && m.d % 128 == 0 &&
+         m.F % 128 == 0 && (m.ffn_only || (m.dq % 128 == 0 && m.nqkv % 128 == 0));
+  if (m.pk) {
+    m.dp = m.d / 2; m.dqp = m.dq / 2; m.Fp = m.F / 2;
+  } else {
+    m.dp = up16(m.d); m.dqp = up16(m.dq); m.Fp = up16(m.F);
+  }
   m.woff = b->wbits == 8 ? 128 : 0;
   m.aoff = b->abits == 8 ? 128 : 0;
   return m;
@@ -234,7 +243,8 @@ hipError_t timed(omq_timer* tm, int kind, double work, hipStream_t st, F&& launc
 hipError_t wfq(const void* W, int64_t rows, int64_t cols, const float* s, const float* delta,
                const float* th, const Theta& t, int l, int wbits, bool fp, uint16_t* out,
                const Stats& st, int64_t row0, float* Bt, int64_t group, uint8_t* codes,
-               int64_t ldq, int code_off, hipStream_t stream, omq_timer* tm, int32_t* nf) {
+               int64_t ldq, int code_off, int code_pack, hipStream_t stream, omq_timer* tm,
+               int32_t* nf) {
   RowQuantFwd a;
   a.x = W; a.x_dt = OMQ_BF16; a.rows = rows; a.cols = cols; a.ldx = cols;
   a.let_mode = (s && !fp) ? OMQ_LET_MUL : OMQ_LET_NONE; a.s = s;
@@ -249,10 +259,12 @@ hipError_t wfq(const void* W, int64_t rows, int64_t cols, const float* s, const 
   if (!fp && delta && !grouped) { a.fold_delta = delta; a.bias_out = Bt + row0; }
   if (codes && !fp) {
     a.codes = codes + row0 * ldq; a.ldq = ldq; a.code_off = code_off; a.qsum = st.qsum + row0;
+    a.code_pack = code_pack;
   }
   if (!fp) a.nonfinite = nf;
   // algorithmic bytes: read W, write W_hat (and the codes)
-  const double bytes = (double)rows * (double)cols * (4.0 + (a.codes ? 1.0 : 0.0));
+  const double bytes =
+      (double)rows * (double)cols * (4.0 + (a.codes ? (code_pack ? 0.5 : 1.0) : 0.0));
   hipError_t e = timed(fp ? nullptr : tm, OMQ_TIMED_WEIGHT_QUANT, bytes, stream,
                        [&] { return launch_rowquant_fwd(a, stream); });
   if (e == hipSuccess && !fp && delta && (a.nbits >= 16 || grouped))
@@ -265,7 +277,7 @@ hipError_t wfq(const void* W, int64_t rows, int64_t cols, const float* s, const 
 hipError_t wfq_cat(int n, const void* const* Ws, const int64_t* rows, const int* ls,
                    int64_t cols, const float* s, const float* delta, const float* th, const Theta& t,
                    int wbits, bool fp, uint16_t* out, const Stats& st, float* Bt, int64_t group,
-                   uint8_t* codes, int64_t ldq, int code_off, hipStream_t stream,
+                   uint8_t* codes, int64_t ldq, int code_off, int code_pack, hipStream_t stream,
                    omq_timer* tm, int32_t* nf) {
   RowQuantFwd a;
   a.x = Ws[0]; a.x_dt = OMQ_BF16; a.cols = cols; a.ldx = cols; a.nbits = wbits;
@@ -274,7 +286,7 @@ hipError_t wfq_cat(int n, const void* const* Ws, const int64_t* rows, const int*
     int64_t r0 = 0;
     for (int k = 0; k < n; ++k) {
       hipError_t e = wfq(Ws[k], rows[k], cols, s, delta, th, t, ls[k], wbits, fp, out, st, r0,
-                         Bt, group, codes, ldq, code_off, stream, tm, nf);
+                         Bt, group, codes, ldq, code_off, code_pack, stream, tm, nf);
       if (e != hipSuccess) return e;
       r0 += rows[k];
     }
@@ -294,10 +306,14 @@ hipError_t wfq_cat(int n, const void* const* Ws, const int64_t* rows, const int*
   a.out = out; a.out_dt = OMQ_BF16; a.ldo = cols;
   a.h = st.h; a.z = st.z; a.amax = st.amax; a.amin = st.amin;
   if (delta) { a.fold_delta = delta; a.bias_out = Bt; }
-  if (codes) { a.codes = codes; a.ldq = ldq; a.code_off = code_off; a.qsum = st.qsum; }
+  if (codes) {
+    a.codes = codes; a.ldq = ldq; a.code_off = code_off; a.qsum = st.qsum;
+    a.code_pack = code_pack;
+  }
   a.nonfinite = nf;
   // algorithmic bytes: read W, write W_hat (and the codes)
-  const double bytes = (double)r0 * (double)cols * (4.0 + (a.codes ? 1.0 : 0.0));
+  const double bytes =
+      (double)r0 * (double)cols * (4.0 + (a.codes ? (code_pack ? 0.5 : 1.0) : 0.0));
   return timed(tm, OMQ_TIMED_WEIGHT_QUANT, bytes, stream,
                [&] { return launch_rowquant_fwd(a, stream); });
 }
@@ -314,7 +330,8 @@ hipError_t aq(const void* X, int x_dt, int64_t T, int64_t C, int64_t ldx, int mo
               const float* s, const float* delta, int abits, uint16_t* out, const Stats& st,
               hipStream_t stream, omq_timer* tm, int32_t* nf, uint8_t* codes = nullptr,
               int64_t ldq = 0,
-              int code_off = 0, float* rms_out = nullptr, float* rstd = nullptr,
+              int code_off = 0, int code_pack = 0, float* rms_out = nullptr,
+              float* rstd = nullptr,
               float eps = 0.f, const float* rope_cos = nullptr, const float* rope_sin = nullptr,
               float* rope_out = nullptr) {
   RowQuantFwd a;
@@ -324,12 +341,15 @@ hipError_t aq(const void* X, int x_dt, int64_t T, int64_t C, int64_t ldx, int mo
   a.let_mode = mode; a.s = s; a.delta = delta; a.nbits = abits;
   a.out = out; a.out_dt = OMQ_BF16; a.ldo = C;
   a.h = st.h; a.z = st.z; a.amax = st.amax; a.amin = st.amin;
-  if (codes && abits < 16) { a.codes = codes; a.ldq = ldq; a.code_off = code_off; a.qsum = st.qsum; }
+  if (codes && abits < 16) {
+    a.codes = codes; a.ldq = ldq; a.code_off = code_off; a.qsum = st.qsum; a.code_pack = code_pack;
+  }
   if (abits < 16) a.nonfinite = nf;
   // algorithmic bytes: read X, write X_hat (and the codes, and the normalized or
   // rotated rows)
   const double bytes = (double)T * (double)C *
-                       ((x_dt == OMQ_F32 ? 4.0 : 2.0) + 2.0 + (a.codes ? 1.0 : 0.0) +
+                       ((x_dt == OMQ_F32 ? 4.0 : 2.0) + 2.0 +
+                        (a.codes ? (code_pack ? 0.5 : 1.0) : 0.0) +
                         (rms_out || rope_out ? 4.0 : 0.0));
   return timed(abits < 16 ? tm : nullptr, OMQ_TIMED_ACT_QUANT, bytes, stream,
                [&] { return launch_rowquant_fwd(a, stream); });
@@ -375,8 +395,11 @@ hipError_t code_gemm(const uint8_t* qx, const Stats& sx, const uint8_t* qw, cons
                      int64_t ldr, hipStream_t st, omq_timer* tm) {
   Gemm g;
   g.codes = 1;
+  // byte codes: rows of Kp (padded) codes; packed: rows of K / 2 bytes (Kp)
+  g.pack4 = m.pk;
   g.A = qx; g.lda = Kp; g.B = qw; g.ldb = Kp; g.C = C; g.ldc = ldc;
-  g.M = T; g.N = N; g.K = Kp; g.kz = K; g.bias = bias; g.resid = resid; g.resid_dt = resid_dt;
+  g.M = T; g.N = N; g.K = m.pk ? K : Kp; g.kz = K; g.bias = bias; g.resid = resid;
+  g.resid_dt = resid_dt;
   g.ldr = ldr;
   g.ha = sx.h; g.za = sx.z; g.sa = sx.qsum; g.hb = sw.h; g.zb = sw.z; g.sb = sw.qsum;
   g.zoa = (float)m.aoff; g.zob = (float)m.woff;
@@ -439,7 +462,7 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
     }
     const KvSites kv = kv_sites(m, t, w, th, nullptr);
     const float* s_o = fp ? nullptr : kv.s_o;
-    if (cq && (m.dp != d || m.dqp != dq)) {
+    if (cq && !m.pk && (m.dp != d || m.dqp != dq)) {
       // padded code rows: the columns past the row end must hold zero codes
       CK(zero_bytes(w.Cqkv, nqkv * m.dp, st));
       CK(zero_bytes(w.Co, d * m.dqp, st));
@@ -454,18 +477,18 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
       const int64_t rc[3] = {dq, dk, dk};
       const int lc[3] = {LQ, LK, LV};
       CK(wfq_cat(3, Wc, rc, lc, d, s_qkv, d_qkv, th, t, wb, fp, w.Wqkv, w.wq_qkv, w.Bt_qkv,
-                 m.group, cq ? w.Cqkv : nullptr, m.dp, m.woff, st, tm, nf));
+                 m.group, cq ? w.Cqkv : nullptr, m.dp, m.woff, m.pk, st, tm, nf));
     }
     CK(wfq(W[LO], d, dq, s_o, d_o, th, t, LO, wb, fp, w.Wo, w.wq_o, 0, w.Bt_o, m.group,
-           cq ? w.Co : nullptr, m.dqp, m.woff, st, tm, nf));
+           cq ? w.Co : nullptr, m.dqp, m.woff, m.pk, st, tm, nf));
     // attention input: the RMSNorm runs inside the quantizer where that applies
     if (rms_fused(OMQ_BF16, d, ab, mode_let)) {
       CK(aq(x, OMQ_BF16, T, d, d, mode_let, s_qkv, d_qkv, ab, w.Xqkv, w.a_qkv, st, tm, nf,
-            cq ? w.Cxqkv : nullptr, m.dp, m.aoff, w.xn, w.r1, bd->eps));
+            cq ? w.Cxqkv : nullptr, m.dp, m.aoff, m.pk, w.xn, w.r1, bd->eps));
     } else {
       CK(launch_rmsnorm(x, OMQ_BF16, T, d, bd->eps, w.xn, w.r1, st));
       CK(aq(w.xn, OMQ_F32, T, d, d, mode_let, s_qkv, d_qkv, ab, w.Xqkv, w.a_qkv, st, tm, nf,
-            cq ? w.Cxqkv : nullptr, m.dp, m.aoff));
+            cq ? w.Cxqkv : nullptr, m.dp, m.aoff, m.pk));
     }
     if (cq)
       CK(code_gemm(w.Cxqkv, w.a_qkv, w.Cqkv, w.wq_qkv, w.Yqkv, nqkv, T, nqkv, d, m.dp, m,
@@ -478,10 +501,10 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
     const bool sa = m.use_sa && !fp;
     if (aq_rope_ok(T, dq, nqkv, ab) && aq_rope_ok(T, dk, nqkv, ab)) {
       CK(aq(w.Yqkv, OMQ_F32, T, dq, nqkv, sa ? OMQ_LET_DIV : OMQ_LET_NONE, kv.sa_q, nullptr, ab,
-            w.Qh, w.a_q, st, tm, nf, nullptr, 0, 0, nullptr, nullptr, 0.f, w.cos_t, w.sin_t,
+            w.Qh, w.a_q, st, tm, nf, nullptr, 0, 0, 0, nullptr, nullptr, 0.f, w.cos_t, w.sin_t,
             w.Qr));
       CK(aq(w.Yqkv + dq, OMQ_F32, T, dk, nqkv, sa ? OMQ_LET_MUL : OMQ_LET_NONE,
-            th + (sa ? t.s_a : 0), nullptr, ab, w.Kh, w.a_k, st, tm, nf, nullptr, 0, 0, nullptr,
+            th + (sa ? t.s_a : 0), nullptr, ab, w.Kh, w.a_k, st, tm, nf, nullptr, 0, 0, 0, nullptr,
             nullptr, 0.f, w.cos_t, w.sin_t, w.Kr));
     } else {
       CK(launch_rope2(w.Yqkv, nqkv, w.Qr, dq, m.nq, w.Yqkv + dq, nqkv, w.Kr, dk, m.nkv, T, m.hd,
@@ -504,7 +527,7 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
     }
     // o_proj with its LET site, residual
     CK(aq(w.O, OMQ_F32, T, dq, dq, mode_let, s_o, d_o, ab, w.Xo, w.a_o, st, tm, nf,
-          cq ? w.Cxo : nullptr, m.dqp, m.aoff));
+          cq ? w.Cxo : nullptr, m.dqp, m.aoff, m.pk));
     if (cq)
       CK(code_gemm(w.Cxo, w.a_o, w.Co, w.wq_o, w.h1, d, T, d, dq, m.dqp, m, w.Bt_o, x, OMQ_BF16,
                    d, st, tm));
@@ -521,7 +544,7 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
     xf_dt = OMQ_BF16;
   }
   // FFN
-  if (cq && (m.dp != d || m.Fp != F)) {
+  if (cq && !m.pk && (m.dp != d || m.Fp != F)) {
     CK(zero_bytes(w.Cgu, 2 * F * m.dp, st));
     CK(zero_bytes(w.Cd, d * m.Fp, st));
     CK(zero_bytes(w.Cxf, T * m.dp, st));
@@ -532,16 +555,16 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
     const int64_t rc[2] = {F, F};
     const int lc[2] = {LG, LU};
     CK(wfq_cat(2, Wc, rc, lc, d, s_ffn, d_ffn, th, t, wb, fp, w.Wgu, w.wq_gu, w.Bt_gu, m.group,
-               cq ? w.Cgu : nullptr, m.dp, m.woff, st, tm, nf));
+               cq ? w.Cgu : nullptr, m.dp, m.woff, m.pk, st, tm, nf));
   }
   CK(wfq(W[LD], d, F, nullptr, nullptr, th, t, LD, wb, fp, w.Wd, w.wq_d, 0, nullptr, m.group,
-         cq ? w.Cd : nullptr, m.Fp, m.woff, st, tm, nf));
+         cq ? w.Cd : nullptr, m.Fp, m.woff, m.pk, st, tm, nf));
   if (!m.ffn_only && rms_fused(OMQ_F32, d, ab, mode_let))
     CK(aq(w.h1, OMQ_F32, T, d, d, mode_let, s_ffn, d_ffn, ab, w.Xf, w.a_f, st, tm, nf,
-          cq ? w.Cxf : nullptr, m.dp, m.aoff, w.xn2, w.r2, bd->eps));
+          cq ? w.Cxf : nullptr, m.dp, m.aoff, m.pk, w.xn2, w.r2, bd->eps));
   else
     CK(aq(xf, xf_dt, T, d, d, mode_let, s_ffn, d_ffn, ab, w.Xf, w.a_f, st, tm, nf,
-          cq ? w.Cxf : nullptr, m.dp, m.aoff));
+          cq ? w.Cxf : nullptr, m.dp, m.aoff, m.pk));
   if (cq)
     CK(code_gemm(w.Cxf, w.a_f, w.Cgu, w.wq_gu, w.GU, 2 * F, T, 2 * F, d, m.dp, m, w.Bt_gu,
                  nullptr, 0, 0, st, tm));
@@ -550,7 +573,7 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
             st, tm));
   CK(launch_silu_gate(w.GU, T, F, w.A, st));
   CK(aq(w.A, OMQ_F32, T, F, F, OMQ_LET_NONE, nullptr, nullptr, ab, w.Xd, w.a_d, st, tm, nf,
-        cq ? w.Cxd : nullptr, m.Fp, m.aoff));
+        cq ? w.Cxd : nullptr, m.Fp, m.aoff, m.pk));
   if (cq)
     CK(code_gemm(w.Cxd, w.a_d, w.Cd, w.wq_d, w.y, d, T, d, F, m.Fp, m, nullptr,
                  m.ffn_only ? nullptr : w.h1, OMQ_F32, d, st, tm));

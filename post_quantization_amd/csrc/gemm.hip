@@ -31,6 +31,8 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 typedef __attribute__((ext_vector_type(16))) int i32x16;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
 constexpr int BK = 64, LDP = BK;
 
@@ -268,8 +270,13 @@ constexpr int epi_code(int mode, int let, int xf) { return mode | (let << 2) | (
 // form holds 8 elements: the same 16 bytes.  The epilogue dequantizes.
 // KB: the k-step, 64, or 32 with direct copies (half the LDS per stage, so wider
 // wave tiles still fit two workgroups per compute unit).
+// PK (with I8, direct copies and KB = 32): 4-bit codes two to a byte; a k-step of 64
+// bytes is 128 codes, and each fragment read of 8 bytes is unpacked into the 16
+// bytes of the int8 operand (the low nibbles of a word, then its high nibbles: codes
+// 0 2 4 6 1 3 5 7 of each 8).  Both operands take the same order, so the sum over k
+// is the same.
 template <int BM, int BN, int WM, int WN, int TA, int TB, int EPI, int DMA, int I8 = 0,
-          int KB = 64>
+          int KB = 64, int PK = 0>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void k_gemm_bf16(Gemm g, int tiles_m, int tiles_n) {
   constexpr int NT = WM * WN * 64, NW = WM * WN;
@@ -281,6 +288,7 @@ void k_gemm_bf16(Gemm g, int tiles_m, int tiles_n) {
                 "straight-through epilogue tile");
   static_assert(!I8 || (EPI == 0 && TA == 0 && TB == 0), "integer codes: plain K-contiguous");
   static_assert(KB == 64 || (KB == 32 && DMA), "32-wide k steps take direct copies");
+  static_assert(!PK || (I8 && DMA && KB == 32 && BM == 128 && BN == 128), "packed codes");
   // operand ring, and the epilogue's [128][128] float32 parking area
   constexpr int kRing = 2 * (BM + BN) * KB, kPark = EPI ? 128 * 128 * 2 : 0;
   __shared__ __attribute__((aligned(16))) uint16_t smem[kRing > kPark ? kRing : kPark];
@@ -294,7 +302,7 @@ void k_gemm_bf16(Gemm g, int tiles_m, int tiles_n) {
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int bz = blockIdx.y;
   // K extent and leading dimensions in 16-bit units (codes: pairs of bytes)
-  const int64_t kb = 0, ke = I8 ? g.K >> 1 : g.K;
+  const int64_t kb = 0, ke = I8 ? (PK ? g.K >> 2 : g.K >> 1) : g.K;
   const int64_t lda = I8 ? g.lda >> 1 : g.lda, ldb = I8 ? g.ldb >> 1 : g.ldb;
 
   const uint16_t* A =
@@ -441,6 +449,32 @@ void k_gemm_bf16(Gemm g, int tiles_m, int tiles_n) {
           for (int j = 0; j < FN; ++j)
             mfma(acc[i][j], af[cu][i], bf[cu][j]);
       }
+    } else if constexpr (PK) {
+      // 4 slices of 32 codes per k-step; lane half h reads the slice's 8 bytes of
+      // codes 16h .. 16h+15
+      const int f4 = (lane >> 5) * 4;
+      auto unpack = [](const uint16_t* p) -> bf16x8 {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+        const u32x4 v = {w.x & 0x0f0f0f0fu, (w.x >> 4) & 0x0f0f0f0fu, w.y & 0x0f0f0f0fu,
+                         (w.y >> 4) & 0x0f0f0f0fu};
+        return __builtin_bit_cast(bf16x8, v);
+      };
+      bf16x8 af[4][FM], bf[4][FN];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af[kk][i] = unpack(&Ab[lds_idx<32>(ar + i * 32, kk * 8 + f4)]);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bf[kk][j] = unpack(&Bb[lds_idx<32>(br + j * 32, kk * 8 + f4)]);
+      }
+      issue_next();
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            mfma(acc[i][j], af[kk][i], bf[kk][j]);
     } else {
       bf16x8 af[KB / 16][FM], bf[KB / 16][FN];
 #pragma unroll
@@ -1040,6 +1074,18 @@ hipError_t launch_gemm_codes(const Gemm& g, hipStream_t st) {
   v.K = g.K / 2;
   v.lda = g.lda / 2;
   v.ldb = g.ldb / 2;
+  if (g.pack4) {
+    // two codes to a byte: whole 128 x 128 tiles and 128-code k-steps, direct copies
+    v.K = g.K / 4;
+    if (g.K % 128 || g.M % 128 || g.N % 128 || g.zoa != 0.f || g.zob != 0.f ||
+        g.lda * 2 < g.K || g.ldb * 2 < g.K || !dma_fits(v, 128, 128, 32))
+      return hipErrorInvalidValue;
+    const int tiles_m = (int)(g.M / 128), tiles_n = (int)(g.N / 128);
+    hipLaunchKernelGGL((k_gemm_bf16<128, 128, 2, 2, 0, 0, 0, 1, 1, 32, 1>),
+                       dim3((unsigned)(tiles_m * tiles_n), (unsigned)g.batch), dim3(256), 0, st, g,
+                       tiles_m, tiles_n);
+    return hipGetLastError();
+  }
   const int64_t big_tiles = (g.M / 256) * (g.N / 256);
   if (big_tiles >= 512 && dma_fits(v, 256, 256))
     launch_codes<256, 256, 2, 4, 1>(g, st);

@@ -21,6 +21,9 @@ struct RowQuantFwd {
   int64_t ldq = 0;                                  // 0: cols (multiple of 4 otherwise)
   int code_off = 0;                                 // codes stored as q - code_off (a byte);
                                                     // 0 or 128
+  int code_pack = 0;                                // 1: 4-bit codes two to a byte (code c in
+                                                    // byte c / 2, low nibble for even c;
+                                                    // ldq in bytes), n_bits <= 4, cols % 8 == 0
   int32_t* qsum = nullptr;                          // per-row sum of the stored codes (group 0)
   int32_t* nonfinite = nullptr;                     // set to 1 when any x~ is NaN or infinite
   const float* fold_delta = nullptr;                // bias fold: sum_i fold_delta_i x_ri
@@ -165,6 +168,9 @@ struct Gemm {
   // the code rows are padded with zero codes up to K (0: K)
   float zoa = 0.f, zob = 0.f;
   int64_t kz = 0;
+  // 4-bit codes two to a byte (code k of a row in byte k / 2, the low nibble for even
+  // k; lda/ldb in bytes): M, N and K multiples of 128, zoa = zob = 0
+  int pack4 = 0;
   int ta = 0, tb = 0;                               // A is [K x M] / B is [K x N]
   SteEpi ste;                                       // bf16 only; mode 2 writes dL/dx into C
 };

@@ -31,8 +31,31 @@ OMQ_DEV float let_x(float x, int mode, const float* s, const float* delta, int64
   return x;
 }
 
-// row stride of the codes output
-OMQ_DEV int64_t code_ld(const RowQuantFwd& a) { return a.ldq ? a.ldq : a.cols; }
+// row stride of the codes output, in bytes
+OMQ_DEV int64_t code_ld(const RowQuantFwd& a) {
+  return a.ldq ? a.ldq : a.code_pack ? a.cols / 2 : a.cols;
+}
+
+// Code stores: 4 or 8 consecutive codes (one per byte of cw) of row r from column c,
+// as bytes, or two to a byte when code_pack is set (byte c / 2 holds codes c, c + 1 in
+// its low and high nibble).
+OMQ_DEV uint32_t nibble_pack4(uint32_t w) {   // bytes b0..b3 (each < 16) -> b0|b1<<4|b2<<8|b3<<12
+  const uint32_t t = w | (w >> 4);
+  return (t & 0xffu) | ((t >> 8) & 0xff00u);
+}
+OMQ_DEV void store_codes4(const RowQuantFwd& a, int64_t r, int64_t c, uint32_t cw) {
+  if (a.code_pack)
+    *reinterpret_cast<uint16_t*>(a.codes + r * code_ld(a) + (c >> 1)) = (uint16_t)nibble_pack4(cw);
+  else
+    *reinterpret_cast<uint32_t*>(a.codes + r * code_ld(a) + c) = cw;
+}
+OMQ_DEV void store_codes8(const RowQuantFwd& a, int64_t r, int64_t c, uint32_t lo, uint32_t hi) {
+  if (a.code_pack)
+    *reinterpret_cast<uint32_t*>(a.codes + r * code_ld(a) + (c >> 1)) =
+        nibble_pack4(lo) | (nibble_pack4(hi) << 16);
+  else
+    *reinterpret_cast<uint2*>(a.codes + r * code_ld(a) + c) = make_uint2(lo, hi);
+}
 
 // a row's extreme-value column, kept inside the row: with a NaN in the row the
 // comparisons of the reductions never pick it, and lanes that held no column could
@@ -273,7 +296,7 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd(RowQuantFwd a) {
       qs += qi;
     }
     store4(a.out, a.out_dt, r * a.ldo + c, o);
-    if (a.codes) *reinterpret_cast<uint32_t*>(a.codes + r * code_ld(a) + c) = cw;
+    if (a.codes) store_codes4(a, r, c, cw);
   }
   if (a.qsum) block_qsum(qs, a.qsum + r);
 }
@@ -375,7 +398,7 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_reg(RowQuantFwd a) {
         qs += qi;
       }
       store4(a.out, a.out_dt, r * a.ldo + c, o);
-      if (a.codes) *reinterpret_cast<uint32_t*>(a.codes + r * code_ld(a) + c) = cw;
+      if (a.codes) store_codes4(a, r, c, cw);
     }
   }
   if (a.qsum) block_qsum(qs, a.qsum + r);
@@ -631,7 +654,7 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_blk8(RowQuantFwd a) {
       store8(a.out, a.out_dt, r * a.ldo + c, o);
       if (a.codes) {
         const uint2 cw = codes8(qq, off128, qsum);
-        *reinterpret_cast<uint2*>(a.codes + r * code_ld(a) + c) = cw;
+        store_codes8(a, r, c, cw.x, cw.y);
       }
     }
   }
@@ -804,10 +827,10 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_wave(RowQuantFwd a) {
         if (j < n) qs += qi;
       }
       store4(a.out, a.out_dt, r * a.ldo + c, o);
-      if (a.codes) *reinterpret_cast<uint32_t*>(a.codes + r * code_ld(a) + c) = cw[0];
+      if (a.codes) store_codes4(a, r, c, cw[0]);
       if (FULL || c + 8 <= cols) {
         store4(a.out, a.out_dt, r * a.ldo + c + 4, o + 4);
-        if (a.codes) *reinterpret_cast<uint32_t*>(a.codes + r * code_ld(a) + c + 4) = cw[1];
+        if (a.codes) store_codes4(a, r, c + 4, cw[1]);
       }
     }
   }
@@ -1004,7 +1027,7 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_lds(RowQuantFwd a) {
     store8(a.out, a.out_dt, r * a.ldo + c, o);
     if (a.codes) {
       const uint2 cw = codes8(qq, off128, qsum);
-      *reinterpret_cast<uint2*>(a.codes + r * code_ld(a) + c) = cw;
+      store_codes8(a, r, c, cw.x, cw.y);
     }
   }
   if (a.qsum) {
@@ -1086,10 +1109,7 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_fwd_g128(RowQuantFwd a) {
   }
   store4(a.out, a.out_dt, r * a.ldo + c, o);
   store4(a.out, a.out_dt, r * a.ldo + c + 4, o + 4);
-  if (a.codes) {
-    *reinterpret_cast<uint32_t*>(a.codes + r * code_ld(a) + c) = cw[0];
-    *reinterpret_cast<uint32_t*>(a.codes + r * code_ld(a) + c + 4) = cw[1];
-  }
+  if (a.codes) store_codes8(a, r, c, cw[0], cw[1]);
 }
 
 // ---------------------------------------------------------------------------
@@ -1850,6 +1870,10 @@ hipError_t launch_rowquant_fwd(const RowQuantFwd& a, hipStream_t st) {
   if (a.rows == 0 || a.cols == 0) return hipSuccess;
   if (a.nseg > 1 && (!rowquant_fwd_segments_ok(a) || a.nseg > 3)) return hipErrorInvalidValue;
   if (a.rms_out && !rowquant_fwd_rms_ok(a)) return hipErrorInvalidValue;
+  // two 4-bit codes to a byte: 4-bit codes at most, stored as q, whole 8-column chunks
+  if (a.codes && a.code_pack &&
+      (a.nbits > 4 || a.code_off != 0 || a.cols % 8 || (a.ldq && a.ldq % 4)))
+    return hipErrorInvalidValue;
   if (a.rope_out) {
     if (!rowquant_fwd_rope_ok(a) || (a.qsum && !a.codes)) return hipErrorInvalidValue;
     if (a.codes && a.code_off != 0 && a.code_off != 128) return hipErrorInvalidValue;

@@ -311,6 +311,43 @@ def test_code_gemm(M, N, K, abits, wbits):
     assert (err <= bound).all()
 
 
+def _pack4(codes):
+    """Two 4-bit codes to a byte, code k of a row in byte k // 2, the low nibble for even
+    k (numpy, from the definition)."""
+    c = codes.astype(np.uint8)
+    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+
+
+@pytest.mark.parametrize("M,N,K,abits,wbits", [
+    (256, 384, 4096, 4, 4),       # the 7B widths
+    (128, 256, 11008, 4, 3),      # the FFN down width
+    (2048, 1024, 512, 4, 2)])
+def test_code_gemm4_packed(M, N, K, abits, wbits):
+    """The product on 4-bit codes stored two to a byte equals the product on byte codes
+    bit for bit (the same integer sums, unpacked inside the kernel, and the same single
+    rounding), and the oracle's code product within a float32 rounding."""
+    log("code_gemm4", M, N, K, abits, wbits)
+    rng = np.random.default_rng(M + N + K + 4)
+    X = synth.normal(94, M, (M, K), 1.0)
+    X[::37] += 6.0
+    W = synth.normal(95, N, (N, K), synth.WEIGHT_STD)
+    sx, _ = quant.act_quant(X, abits)
+    ag, ab, _, _, B = _params(rng, N, K)
+    wq = quant.lwc_fakequant(W, ag, ab, wbits)
+    assert sx.codes.max() < 16 and wq.codes.max() < 16
+    qa, qb = dev(sx.codes, torch.uint8), dev(wq.codes, torch.uint8)
+    sa, sb = omq.code_rowsum(qa), omq.code_rowsum(qb)
+    pa, pb = dev(_pack4(sx.codes), torch.uint8), dev(_pack4(wq.codes), torch.uint8)
+    C1 = omq.code_gemm(qa, dev(sx.h), dev(sx.z), qb, dev(wq.h), dev(wq.z), sa, sb, bias=dev(B))
+    C4 = omq.code_gemm4(pa, dev(sx.h), dev(sx.z), pb, dev(wq.h), dev(wq.z), K, sa, sb,
+                        bias=dev(B))
+    torch.cuda.synchronize()
+    got1, got4 = host(C1), host(C4)
+    assert np.array_equal(got4.view(np.uint32), got1.view(np.uint32))
+    want = quant.code_product(sx.codes, sx.h, sx.z, wq.codes, wq.h, wq.z, B)
+    assert rel(got4.astype(np.float64), want) < 1e-6
+
+
 @pytest.mark.parametrize("c_out,c_in,nbits,let", [(77, 200, 4, True), (96, 4096, 2, True),
                                                   (64, 11008, 3, False), (4096, 4096, 4, True)])
 def test_lwc_backward(c_out, c_in, nbits, let):
