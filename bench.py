@@ -309,7 +309,8 @@ def gemm_main(args):
     """The matrix products of one 7B-shaped W4A4 calibration step, each alone: the
     backward's eight bf16 products through omq_gemm (main loop only, no fused
     straight-through epilogue) beside torch.matmul (hipBLASLt) on the same operand
-    layouts, and the forward's four products on int8 codes through omq_code_gemm.
+    layouts, and the forward's four products on int8 codes through omq_code_gemm (and,
+    for 4-bit codes, on codes two to a byte through omq_code_gemm4, the step's form).
     Per shape: the mean of `steps` launches after `warmup`, on HIP events."""
     import torch
     import post_quantization_amd as omq
@@ -366,8 +367,16 @@ def gemm_main(args):
         sa, sb = omq.code_rowsum(qa), omq.code_rowsum(qb)
         C = torch.empty(M, N, dtype=torch.float32, device=dev)
         t = timeit(lambda: omq.code_gemm(qa, ha, za, qb, hb, zb, sa, sb, C=C))
-        codes.append({"product": name, "M": M, "N": N, "K": K, "omq_us": round(t * 1e3, 1),
-                      "omq_tops": round(2.0 * M * N * K / t / 1e9, 1)})
+        row = {"product": name, "M": M, "N": N, "K": K, "omq_us": round(t * 1e3, 1),
+               "omq_tops": round(2.0 * M * N * K / t / 1e9, 1)}
+        if c.wbits <= 4 and c.abits <= 4:
+            # the step's form: 4-bit codes two to a byte (omq_code_gemm4)
+            pa = (qa[:, 0::2] | (qa[:, 1::2] << 4)).contiguous()
+            pb = (qb[:, 0::2] | (qb[:, 1::2] << 4)).contiguous()
+            t4 = timeit(lambda: omq.code_gemm4(pa, ha, za, pb, hb, zb, K, sa, sb, C=C))
+            row.update({"packed_us": round(t4 * 1e3, 1),
+                        "packed_tops": round(2.0 * M * N * K / t4 / 1e9, 1)})
+        codes.append(row)
     tf = flops / tot_o / 1e9
     out = {
         "metric": "bf16 matrix-core TFLOP/s of the backward products of one LLaMA-7B-shaped W4A4 "
