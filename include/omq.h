@@ -216,15 +216,18 @@ int omq_attention_fwd(const void* Q, int64_t ldq, const void* K, const void* V, 
  *   dV_g = sum over the group's heads of P^T dO_h;  dP = dO_h V_g^T;
  *   dS = P (dP - rowsum(dO_h O_h)) / sqrt(head_dim);  dQ_h = dS K_g;
  *   dK_g = sum over the group's heads of dS^T Q_h
- * with the scores recomputed from lse2 (no score matrix is stored); dO, P and dS
- * enter the matrix cores in bf16, every sum is float32.
+ * with the scores recomputed from lse2; dO, P and dS enter the matrix cores in
+ * bf16, every sum is float32.  The dK/dV pass writes the bf16 dS it forms to the
+ * workspace and dQ is formed from that same dS (the probabilities are never stored).
  * O, dO: float [T x n_q*128], row stride ldo; lse2 as the forward wrote it.
  * dQ: float [T x n_q*128], row stride lddq; dK, dV: float [T x n_kv*128], row
  * stride lddk (multiples of 4); all overwritten.  ws: device workspace of at least
- * omq_attention_bwd_workspace_size(T, n_q, ldq) bytes (dO in bf16, rowsum(dO O),
- * and, where the K/V heads are too few to occupy the device, float32 partial dK, dV
- * of query-head subsets, added in a fixed order; the size covers any n_kv dividing
- * n_q).  The result is bitwise repeatable: no float atomics.
+ * omq_attention_bwd_workspace_size(T, n_q, ldq) bytes: dO in bf16, rowsum(dO O);
+ * where the K/V heads are too few to occupy the device, float32 partial dK, dV of
+ * query-head subsets, added in a fixed order (the size covers any n_kv dividing
+ * n_q); and dS, n_q * Tp * Tp bf16 with Tp = T rounded up to 128 (268 MB at T 2048
+ * with 32 heads).  The size is 0, and the call returns OMQ_E_SHAPE, when that dS
+ * would exceed 2^50 elements.  The result is bitwise repeatable: no float atomics.
  */
 size_t omq_attention_bwd_workspace_size(int64_t T, int64_t n_q, int64_t ldq);
 int omq_attention_bwd(const void* Q, int64_t ldq, const void* K, const void* V, int64_t ldk,
@@ -453,8 +456,9 @@ typedef struct omq_timer {
  * With both quantizers on, the forward's four quantized products are formed exactly
  * on the integer codes (h_x h_w sum (q_x - z_x)(q_w - z_w), rounded once to float).
  * Limits (checked by every block entry point; omq_block_workspace_size returns 0):
- * head_dim must be 128 and n_q a multiple of n_kv (OMQ_E_SHAPE); T, d, F multiples
- * of 8 (OMQ_E_ALIGN); group 128 needs d and F multiples of 128 (OMQ_E_SHAPE); group
+ * head_dim must be 128 and n_q a multiple of n_kv (OMQ_E_SHAPE), and the attention
+ * backward's dS (n_q * Tp * Tp bf16, Tp = T rounded up to 128) at most 2^50 elements
+ * (OMQ_E_SHAPE); T, d, F multiples of 8 (OMQ_E_ALIGN); group 128 needs d and F multiples of 128 (OMQ_E_SHAPE); group
  * 128 with abits < 16 and wbits < 16 (group-wise clipping with quantized
  * activations) is not implemented (OMQ_E_UNIMPLEMENTED).
  */

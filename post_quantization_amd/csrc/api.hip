@@ -261,6 +261,10 @@ size_t omq_attention_bwd_workspace_size(int64_t T, int64_t n_q, int64_t ldq) {
       part = std::max(part, flash_bwd_part_floats(T, (int)n_q, (int)(n_q / i)));
     }
   b.take<float>(part);
+  // bf16 dS of every head, [Tp][Tp] each (Tp = T rounded up to 128)
+  const int64_t ds = flash_bwd_ds_elems(T, n_q);
+  if (ds < 0) return 0;
+  b.take<uint16_t>(ds);
   return b.off;
 }
 
@@ -276,11 +280,14 @@ int omq_attention_bwd(const void* Q, int64_t ldq, const void* K, const void* V, 
   if (lddq % 4 || lddk % 4 || !al16(dO) || !al16(dQ) || !al16(dK) || !al16(dV))
     return OMQ_E_ALIGN;
   if (T == 0) return OMQ_OK;
-  if (!ws || ws_bytes < omq_attention_bwd_workspace_size(T, n_q, ldq)) return OMQ_E_WORKSPACE;
+  const size_t need = omq_attention_bwd_workspace_size(T, n_q, ldq);
+  if (need == 0) return OMQ_E_SHAPE;
+  if (!ws || ws_bytes < need) return OMQ_E_WORKSPACE;
   Bump b(ws);
   float* D = b.take<float>(n_q * T);
   uint16_t* dOb = b.take<uint16_t>(T * ldq);
   float* part = b.take<float>(flash_bwd_part_floats(T, (int)n_q, (int)n_kv));
+  uint16_t* ds = b.take<uint16_t>(flash_bwd_ds_elems(T, n_q));
   const hipStream_t st = S(stream);
   OMQ_HIP_CHECK(launch_attn_bwd_prep(dO, O, ldo, T, (int)n_q, D, dOb, ldq, st));
   FlashBwd f;
@@ -291,7 +298,7 @@ int omq_attention_bwd(const void* Q, int64_t ldq, const void* K, const void* V, 
   f.scale = (float)(1.0 / sqrt((double)head_dim));
   f.scale2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
   f.lse2 = lse2; f.D = D;
-  f.dQ = dQ; f.lddq = lddq; f.dK = dK; f.dV = dV; f.lddk = lddk; f.part = part;
+  f.dQ = dQ; f.lddq = lddq; f.dK = dK; f.dV = dV; f.lddk = lddk; f.part = part; f.ds = ds;
   OMQ_HIP_CHECK(launch_flash_bwd(f, st));
   return OMQ_OK;
 }

@@ -4,9 +4,10 @@
 // its bf16 rounding as a matrix-core operand).
 //
 // Head dimension 128, causal mask, grouped K/V heads (query head h reads K/V head
-// h / grp).  Scores never reach HBM: the forward keeps a running max and sum per
-// query (exp2 domain) and writes O and the row's log-sum-exp; the backward
-// recomputes the scores from that log-sum-exp.
+// h / grp).  Scores and probabilities never reach HBM: the forward keeps a running
+// max and sum per query (exp2 domain) and writes O and the row's log-sum-exp; the
+// backward's dK/dV pass recomputes the scores from that log-sum-exp and writes the
+// bf16 dS it forms, which the dQ pass reads back.
 //
 // MFMA 32x32x16 bf16 layouts.  A lane of the instruction supplies 8 consecutive k
 // of one row (A) or one column (B) and receives a column of C: col = lane & 31,
@@ -77,15 +78,30 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 // k + j, columns 4q .. 4q+3 of the group's 16 columns, and lane i receives the 4
 // rows k .. k+3 of column i.  (The 272-byte rows put the 4 rows of one read 16 bytes
 // apart modulo 256, a 2-way bank overlap the fragment reads along rows avoid.)
+// The same read with the lane's 4-column group given by its LDS column `col` (a tile
+// whose groups of 4 columns are stored in another order).
 template <int STRIDE = RS>
-OMQ_DEV bf16x8 rt_tr_frag(const uint16_t* t, int rb, int s, int lane) {
-  const int G = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
-  const int col = rb + 16 * (G & 1) + 4 * q;
+OMQ_DEV bf16x8 rt_tr_frag_at(const uint16_t* t, int col, int s, int lane) {
+  const int G = lane >> 4, j = (lane >> 2) & 3;
   const int k = 16 * s + 4 * (G >> 1) + j;
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(t + k * STRIDE + col));
   const i16x4 hi =
       __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(t + (k + 8) * STRIDE + col));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+template <int STRIDE = RS>
+OMQ_DEV bf16x8 rt_tr_frag(const uint16_t* t, int rb, int s, int lane) {
+  const int G = lane >> 4, q = lane & 3;
+  return rt_tr_frag_at<STRIDE>(t, rb + 16 * (G & 1) + 4 * q, s, lane);
+}
+
+// Stored dS rows (one key, the queries of 64-query blocks): query 16s + 8b + 4h + i of
+// a block sits at 32h + 8s + 4b + i, so that the dK/dV pass's lane (key, h) writes its
+// 32 values (C-row order) as 64 contiguous bytes.  Position of the 4-query group
+// starting at query n (a multiple of 4) of a row:
+OMQ_DEV int ds_pos(int n) {
+  const int m = n & 63;
+  return (n & ~63) + 32 * ((m >> 2) & 1) + 8 * (m >> 4) + 4 * ((m >> 3) & 1);
 }
 
 // 8 consecutive C values r0..r0+7 of one tile as a B-operand fragment
@@ -340,13 +356,14 @@ __global__ __launch_bounds__(kT) void k_attn_bwd_prep(const float* gO, const flo
 // 64-query block at or after the keys: S = Q K^T and dP = dO V^T (A = Q / dO rows
 // from LDS, B = K / V from registers), P = exp2(S c - lse2), dS = P (dP - D) / sqrt(hd),
 // dV^T += dO^T P and dK^T += Q^T dS (A = transposed Q / dO from LDS, B = P / dS).
+// The bf16 dS of every (query, key) it forms goes to a.ds for the dQ pass.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kT) void k_flash_bwd_dkdv(FlashBwd a, int pair, int nsplit) {
   __shared__ __attribute__((aligned(16))) uint16_t Qs[2][64 * RS];
   __shared__ __attribute__((aligned(16))) uint16_t Gs[2][64 * RS];
   __shared__ __attribute__((aligned(16))) float Ls[2][64];
   __shared__ __attribute__((aligned(16))) float Ds[2][64];
-  const int64_t T = a.T;
+  const int64_t T = a.T, Tp = (T + 127) / 128 * 128;
   const int nkb = (int)((T + 127) / 128);
   // pair: key blocks p and then nkb-1-p (equal causal work per block); else key
   // block p alone (kb = 0, the longest, first).  Workgroup (g, sp, p) covers query
@@ -485,6 +502,15 @@ __global__ __launch_bounds__(kT) void k_flash_bwd_dkdv(FlashBwd a, int pair, int
         pf[s] = c_frag(sc[s >> 1], 8 * (s & 1));
         sf[s] = c_frag(dp[s >> 1], 8 * (s & 1));
       }
+      // dS as rounded here, kept for the dQ pass: the lane's key row, queries
+      // q0 + 16s + 4h + {0..3} and q0 + 16s + 8 + 4h + {0..3} (zero where masked), at
+      // q0 + 32h + 8s + {0..7} (ds_pos)
+      {
+        uint16_t* drow = a.ds + ((int64_t)hq * Tp + key) * Tp + q0 + 32 * h;
+  #pragma unroll
+        for (int s = 0; s < 4; ++s)
+          *reinterpret_cast<u32x4*>(drow + 8 * s) = __builtin_bit_cast(u32x4, sf[s]);
+      }
   #pragma unroll
       for (int hb = 0; hb < 4; ++hb)
   #pragma unroll
@@ -513,112 +539,72 @@ __global__ __launch_bounds__(kT) void k_flash_bwd_dkdv(FlashBwd a, int pair, int
 
 // ---------------------------------------------------------------------------
 // backward, queries stationary: block = (query head, 128 queries); per 64-key block
-// S^T = K Q^T and dP^T = V dO^T (A = K / V rows from LDS, B = Q / dO from
-// registers), dS^T as above, dQ^T += K^T dS^T (A = transposed K from LDS).
+// dQ^T += K^T dS^T (A = transposed K rows from LDS, B = the stored dS read
+// transposed from LDS, each lane at its query group's stored position: lane = query,
+// k = keys), so the scores are not formed again.
+// The dS tile [64 keys][128 queries] of every key block at or before the queries was
+// written by the dK/dV pass (zeros where the mask applies); its columns past T, and
+// K rows clamped to T - 1, meet only zeros or outputs that are not stored.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(2)))
 void k_flash_bwd_dq(FlashBwd a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][64 * RS];
-  const int64_t T = a.T;
+  __shared__ __attribute__((aligned(16))) uint16_t Ss[2][64 * RS];
+  const int64_t T = a.T, Tp = (T + 127) / 128 * 128;
   const int nqb = (int)((T + 127) / 128);
   int hq, qb;
   query_unit(a.n_q, nqb, hq, qb);
   const int hk = hq / a.grp;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), h = lane >> 5, l32 = lane & 31;
-  {
-    const int64_t q0 = (int64_t)qb * 128;
-    const int64_t q = q0 + 32 * w + l32;
-    const int64_t qc = min(q, T - 1);
+  const int64_t q0 = (int64_t)qb * 128;
+  const int64_t q = q0 + 32 * w + l32;
+  const uint16_t* Sh = a.ds + (int64_t)hq * Tp * Tp;
+  const int nkb = (int)((min(q0 + 128, T) + 63) / 64);
+  // the lane's 4-query group of the stored dS rows (B operand: lane = query)
+  const int pc = ds_pos(32 * w + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+  Unit uk, us;
+  uk.load(a.K, a.ldk, hk * HD, 0, T, tid);
+  us.load(Sh, Tp, q0, 0, Tp, tid);
+  uk.store_rows(Ks[0], tid);
+  us.store_rows(Ss[0], tid);
+  if (nkb > 1) {
+    uk.load(a.K, a.ldk, hk * HD, 64, T, tid);
+    us.load(Sh, Tp, q0, 64, Tp, tid);
+  }
+  __syncthreads();
 
-    bf16x8 qf[8], gf[8];
-  #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      qf[s] = *reinterpret_cast<const bf16x8*>(a.Q + qc * a.ldq + hq * HD + 16 * s + 8 * h);
-      gf[s] = *reinterpret_cast<const bf16x8*>(a.dO + qc * a.ldq + hq * HD + 16 * s + 8 * h);
-    }
-    const float lse = a.lse2[(int64_t)hq * T + qc];
-    const float Dq = a.D[(int64_t)hq * T + qc];
-
-    const int64_t kend = min(q0 + 128, T);
-    const int nkb = (int)((kend + 63) / 64);
-    Unit uk, uv;
-    uk.load(a.K, a.ldk, hk * HD, 0, T, tid);
-    uv.load(a.V, a.ldk, hk * HD, 0, T, tid);
-    uk.store_rows(Ks[0], tid);
-    uv.store_rows(Vs[0], tid);
-    if (nkb > 1) {
-      uk.load(a.K, a.ldk, hk * HD, 64, T, tid);
-      uv.load(a.V, a.ldk, hk * HD, 64, T, tid);
+  f32x16 dq[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[i][r] = 0.f;
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int buf = kb & 1;
+    bf16x8 sf[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) sf[s] = rt_tr_frag_at(Ss[buf], pc, s, lane);
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) dq[hb] = mfma(rt_tr_frag(Ks[buf], 32 * hb, s, lane), sf[s], dq[hb]);
+    if (kb + 1 < nkb) {
+      uk.store_rows(Ks[buf ^ 1], tid);
+      us.store_rows(Ss[buf ^ 1], tid);
+      if (kb + 2 < nkb) {
+        uk.load(a.K, a.ldk, hk * HD, (int64_t)(kb + 2) * 64, T, tid);
+        us.load(Sh, Tp, q0, (int64_t)(kb + 2) * 64, Tp, tid);
+      }
     }
     __syncthreads();
-
-    f32x16 dq[4];
-  #pragma unroll
-    for (int i = 0; i < 4; ++i)
-  #pragma unroll
-      for (int r = 0; r < 16; ++r) dq[i][r] = 0.f;
-    for (int kb = 0; kb < nkb; ++kb) {
-      const int buf = kb & 1;
-      f32x16 sc[2], dp[2];
-  #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-  #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          sc[kk][r] = 0.f;
-          dp[kk][r] = 0.f;
-        }
-  #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          sc[kk] = mfma(rt_frag(Ks[buf], 32 * kk + l32, s, h), qf[s], sc[kk]);
-          dp[kk] = mfma(rt_frag(Vs[buf], 32 * kk + l32, s, h), gf[s], dp[kk]);
-        }
-      }
-      if (kb + 1 < nkb) {
-        uk.store_rows(Ks[buf ^ 1], tid);
-        uv.store_rows(Vs[buf ^ 1], tid);
-        if (kb + 2 < nkb) {
-          uk.load(a.K, a.ldk, hk * HD, (int64_t)(kb + 2) * 64, T, tid);
-          uv.load(a.V, a.ldk, hk * HD, (int64_t)(kb + 2) * 64, T, tid);
-        }
-      }
-  #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-  #pragma unroll
-        for (int r = 0; r < 16; ++r) sc[kk][r] = fast_exp2(fmaf(sc[kk][r], a.scale2, -lse));
-      const int k0 = kb * 64;
-      if (k0 + 63 > (int)q0 + 32 * w || k0 + 64 > (int)T) {   // wave-uniform
-        const int qi = (int)q, Ti = (int)T;
-  #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-  #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kr = k0 + 32 * kk + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (kr > qi || kr >= Ti) sc[kk][r] = 0.f;
-          }
-      }
-  #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-  #pragma unroll
-        for (int r = 0; r < 16; ++r) dp[kk][r] = sc[kk][r] * (dp[kk][r] - Dq) * a.scale;
-      bf16x8 sf[4];
-  #pragma unroll
-      for (int s = 0; s < 4; ++s) sf[s] = c_frag(dp[s >> 1], 8 * (s & 1));
-  #pragma unroll
-      for (int hb = 0; hb < 4; ++hb)
-  #pragma unroll
-        for (int s = 0; s < 4; ++s) dq[hb] = mfma(rt_tr_frag(Ks[buf], 32 * hb, s, lane), sf[s], dq[hb]);
-      __syncthreads();
-    }
-    if (q < T) {
-      float* qrow = a.dQ + q * a.lddq + hq * HD;
-  #pragma unroll
-      for (int hb = 0; hb < 4; ++hb)
-  #pragma unroll
-        for (int gg = 0; gg < 4; ++gg)
-          *reinterpret_cast<float4*>(qrow + 32 * hb + 8 * gg + 4 * h) =
-              make_float4(dq[hb][4 * gg], dq[hb][4 * gg + 1], dq[hb][4 * gg + 2], dq[hb][4 * gg + 3]);
-    }
+  }
+  if (q < T) {
+    float* qrow = a.dQ + q * a.lddq + hq * HD;
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg)
+        *reinterpret_cast<float4*>(qrow + 32 * hb + 8 * gg + 4 * h) =
+            make_float4(dq[hb][4 * gg], dq[hb][4 * gg + 1], dq[hb][4 * gg + 2], dq[hb][4 * gg + 3]);
   }
 }
 
@@ -661,6 +647,13 @@ int64_t flash_bwd_part_floats(int64_t T, int n_q, int n_kv) {
   return (int64_t)(flash_bwd_splits(T, n_q, n_kv) - 1) * 2 * T * n_kv * HD;
 }
 
+int64_t flash_bwd_ds_elems(int64_t T, int64_t n_q) {
+  if (T < 0 || n_q < 0) return -1;
+  const int64_t Tp = (T + 127) / 128 * 128;
+  if (Tp > ((int64_t)1 << 25) || (Tp && n_q > ((int64_t)1 << 50) / Tp / Tp)) return -1;
+  return n_q * Tp * Tp;
+}
+
 hipError_t launch_flash_fwd(const FlashFwd& a, hipStream_t st) {
   if (a.T == 0 || a.n_q == 0) return hipSuccess;
   if (a.T > (int64_t)1 << 30) return hipErrorInvalidValue;    // positions are 32-bit
@@ -684,7 +677,7 @@ hipError_t launch_flash_bwd(const FlashBwd& a, hipStream_t st) {
   const int npb = (nkb + 1) / 2;
   const int n_kv = a.n_q / a.grp;
   const int ns = flash_bwd_splits(a.T, a.n_q, n_kv);
-  if (ns > 1 && !a.part) return hipErrorInvalidValue;
+  if ((ns > 1 && !a.part) || !a.ds) return hipErrorInvalidValue;
   const int pair_kv = (int64_t)npb * n_kv * ns >= kPairMinBlocks;
   hipLaunchKernelGGL(k_flash_bwd_dkdv, dim3((unsigned)((pair_kv ? npb : nkb) * n_kv * ns)),
                      dim3(kT), 0, st, a, pair_kv, ns);

@@ -122,6 +122,7 @@ struct Ws {
   // backward
   float *dy, *gA, *gGU, *gxn2, *dh1, *gO, *Datt, *gQh, *gKh, *gVh, *gQr, *gKr, *gY;
   float* attn_part;   // partial dK, dV of the attention backward's query-head splits
+  uint16_t* attn_ds;  // the attention backward's bf16 dS, [n_q][Tp][Tp]
   uint16_t *dyb, *gGUb, *dh1b, *gOb, *gYb;
   float *cs, *gs_full, *gd_full, *gsa_full;
   float *rq, *csws, *msews;
@@ -169,6 +170,7 @@ Ws layout(const Dims& m, void* base) {
     w.Datt = b.take<float>(m.nq * T);
     w.gQh = b.take<float>(T * dq); w.gKh = b.take<float>(T * dk); w.gVh = b.take<float>(T * dk);
     w.attn_part = b.take<float>(flash_bwd_part_floats(T, (int)m.nq, (int)m.nkv));
+    w.attn_ds = b.take<uint16_t>(flash_bwd_ds_elems(T, m.nq));
     w.gQr = b.take<float>(T * dq); w.gKr = b.take<float>(T * dk);
     w.gY = b.take<float>(T * nqkv);
     w.gYb = b.take<uint16_t>(T * nqkv);
@@ -206,6 +208,7 @@ int check(const omq_block_desc* b) {
   if (!b->ffn_only) {
     if (b->n_q <= 0 || b->n_kv <= 0 || b->head_dim <= 0 || b->n_q % b->n_kv) return OMQ_E_SHAPE;
     if (b->head_dim != 128) return OMQ_E_SHAPE;   // the fused attention kernels
+    if (flash_bwd_ds_elems(b->T, b->n_q) < 0) return OMQ_E_SHAPE;   // dS scratch size
   }
   if (b->T % 8 || b->d % 8 || b->F % 8) return OMQ_E_ALIGN;
   // group-wise LWC in groups of 128 input channels: every C_in (d, F, and the
@@ -793,7 +796,8 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
     CK(launch_kv_reduce_add(w.gs_full, m.nq, m.nkv, m.hd, dth + t.s_o, st));
     CK(launch_kv_reduce_add(w.gd_full, m.nq, m.nkv, m.hd, dth + t.d_o, st));
   }
-  // attention backward (scores recomputed from the forward's log-sum-exp)
+  // attention backward (scores recomputed from the forward's log-sum-exp; dQ from the
+  // dS the dK/dV pass writes)
   CK(launch_attn_bwd_prep(w.gO, w.O, dq, T, (int)m.nq, w.Datt, w.gOb, dq, st));
   {
     FlashBwd f;
@@ -803,7 +807,7 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
     f.scale2 = (float)(1.4426950408889634 / sqrt((double)m.hd));
     f.lse2 = w.lse2; f.D = w.Datt;
     f.dQ = w.gQh; f.lddq = dq; f.dK = w.gKh; f.dV = w.gVh; f.lddk = dk;
-    f.part = w.attn_part;
+    f.part = w.attn_part; f.ds = w.attn_ds;
     CK(launch_flash_bwd(f, st));
   }
   // Q~ / K~ / V quantizers and s_a

@@ -270,11 +270,16 @@ struct FlashBwd {
   // flash_bwd_part_floats(T, n_q, n_kv) floats of scratch for the partial dK, dV of
   // the query-head splits beyond the first (nullptr when that count is 0)
   float* part;
+  // flash_bwd_ds_elems(T, n_q) bf16 of scratch: dS as the dK/dV pass rounds it, per
+  // query head [Tp keys][Tp queries] (Tp = T rounded up to 128), read back by dQ
+  uint16_t* ds;
 };
 // Query-head splits of the dK/dV pass: a grouped K/V head's query heads are shared
 // over this many workgroups when the K/V heads alone leave compute units idle.
 int flash_bwd_splits(int64_t T, int n_q, int n_kv);
 int64_t flash_bwd_part_floats(int64_t T, int n_q, int n_kv);
+// n_q * Tp * Tp, or -1 when that exceeds 2^50 elements
+int64_t flash_bwd_ds_elems(int64_t T, int64_t n_q);
 hipError_t launch_flash_fwd(const FlashFwd& a, hipStream_t st);
 hipError_t launch_attn_bwd_prep(const float* gO, const float* O, int64_t ld, int64_t T, int n_q,
                                 float* D, uint16_t* gOb, int64_t ldb, hipStream_t st);

@@ -137,10 +137,16 @@ def test_validation_before_launch():
     # grouped K/V heads too few to fill the device: the dK/dV pass splits a group's query
     # heads and keeps float32 partial dK, dV of all splits but the first; the size covers
     # the largest need over every n_kv dividing n_q (64 query heads at 2048 tokens: one
-    # K/V head, 8 paired key blocks, 32 splits)
-    need = 64 * 2048 * 4 + 2048 * 8192 * 2 + 31 * 2 * 2048 * 1 * 128 * 4
+    # K/V head, 8 paired key blocks, 32 splits); then the bf16 dS of every head,
+    # [2048 keys x 2048 queries] each
+    need = (64 * 2048 * 4 + 2048 * 8192 * 2 + 31 * 2 * 2048 * 1 * 128 * 4
+            + 64 * 2048 * 2048 * 2)
     assert omq.lib().omq_attention_bwd_workspace_size(2048, 64, 8192) >= need
     assert omq.lib().omq_attention_bwd_workspace_size(2048, 64, 8192) < need + 4096
+    # a dS scratch beyond 2^50 elements: no size, and the call is refused as a shape error
+    assert omq.lib().omq_attention_bwd_workspace_size(1 << 26, 4, 512) == 0
+    assert L.omq_attention_bwd(FAKE, 512, FAKE, FAKE, 256, 1 << 26, 4, 2, 128, FAKE, FAKE, 512,
+                               FAKE, FAKE, 512, FAKE, FAKE, 256, FAKE, 1 << 62, None) == -2
     b = omq.BlockDesc(T=64, d=64, n_q=4, n_kv=2, head_dim=16, F=64, wbits=4, abits=4,
                       optimizer=5)
     assert L.omq_block_step(ctypes.byref(b), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None,
