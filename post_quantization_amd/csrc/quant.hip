@@ -1289,21 +1289,28 @@ __global__ __launch_bounds__(kThreads) void k_rowquant_bwd_tile(RowQuantBwd a, i
 }
 
 // One quantizer row's finalizer, in two parts.  row_fetch: the row's segment
-// (concatenated weights: its x rows and logits), its extreme columns, their x and
-// x~ values and the clipping strengths (issued before the row's partial sums are
-// read, so the dependent loads overlap them).  row_finish: the LWC-logit gradients,
-// the max / min scatter into the upstream gradient (one writer per row), and the
-// row's two scatter terms of the column outputs (column, term for out0, term for
-// out1: argmax first, then argmin).  gh, gzs: the row's summed partials.
+// (concatenated weights: its x rows and logits), its extreme columns, and every
+// value that depends on them alone (x and x~ there, the LET scale and shift there,
+// the upstream gradient there, the tile's column partials there when the terms
+// are merged) and the clipping strengths, all issued in one round once the extreme
+// columns have arrived and before the row's partial sums are read, so the
+// dependent loads overlap them.  row_finish: the LWC-logit gradients, the max / min
+// scatter into the upstream gradient (one writer per row), and the row's two
+// scatter terms of the column outputs (column, term for out0, term for out1:
+// argmax first, then argmin).  gh, gzs: the row's summed partials.
 struct RowFetch {
   int64_t r, pl;
   float *gg_g, *gg_b;
   int iM, im;
   float xM, xm, M, m, gamma, beta;
+  float sv[2];          // LET scale at arg_max, arg_min (1 without LET)
+  float gxo[2];         // upstream gradient there before the scatter (with gx)
+  float cp0[2], cp1[2]; // the tile's two column partials there (merged terms)
 };
 
 template <int XDT>
-OMQ_DEV RowFetch row_fetch(const RowQuantBwd& a, int64_t p) {
+OMQ_DEV RowFetch row_fetch(const RowQuantBwd& a, int64_t p, const float* colpart, int64_t t,
+                           bool merge) {
   RowFetch f;
   const int64_t ng = a.group > 0 ? a.cols / 128 : 1;
   f.r = p / ng;
@@ -1328,10 +1335,28 @@ OMQ_DEV RowFetch row_fetch(const RowQuantBwd& a, int64_t p) {
   };
   f.iM = a.amax[p];
   f.im = a.amin[p];
-  f.xM = xval(f.iM);
-  f.xm = xval(f.im);
-  f.M = let_x(f.xM, a.let_mode, a.s, a.delta, f.iM);
-  f.m = let_x(f.xm, a.let_mode, a.s, a.delta, f.im);
+  const int idx[2] = {f.iM, f.im};
+  float xo[2], dl[2] = {0.f, 0.f};
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int c = idx[e];
+    xo[e] = xval(c);
+    f.sv[e] = a.let_mode != OMQ_LET_NONE ? a.s[c] : 1.f;
+    if (a.let_mode == OMQ_LET_DIV && a.delta) dl[e] = a.delta[c];
+    f.gxo[e] = a.gx ? a.gx[f.r * a.ldgx + c] : 0.f;
+    f.cp0[e] = merge ? colpart[(t * 2 + 0) * a.cols + c] : 0.f;
+    f.cp1[e] = merge ? colpart[(t * 2 + 1) * a.cols + c] : 0.f;
+  }
+  f.xM = xo[0];
+  f.xm = xo[1];
+  // x~ exactly as the forward formed it (the LET of the quantizer's input)
+  auto let = [&](float x, int e) {
+    if (a.let_mode == OMQ_LET_DIV) return (x - dl[e]) / f.sv[e];
+    if (a.let_mode == OMQ_LET_MUL) return f.sv[e] * x;
+    return x;
+  };
+  f.M = let(f.xM, 0);
+  f.m = let(f.xm, 1);
   f.gamma = lg_g ? sigmoid_f32(lg_g[f.pl]) : 1.f;
   f.beta = lg_b ? sigmoid_f32(lg_b[f.pl]) : 1.f;
   return f;
@@ -1354,30 +1379,28 @@ OMQ_DEV void row_finish(const RowQuantBwd& a, const RowFetch& f, float gh, float
   const float gv[2] = {gM, gm};
   const float xo[2] = {f.xM, f.xm};
   const float xtl[2] = {M, m};
+  float up[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int c = idx[e];
     const float gsc = gv[e];
-    if (a.gx) {
-      float up = gsc;
-      if (a.let_mode == OMQ_LET_DIV) up = gsc / a.s[c];
-      else if (a.let_mode == OMQ_LET_MUL) up = gsc * a.s[c];
-      a.gx[f.r * a.ldgx + c] += up;
-    }
+    up[e] = gsc;
+    if (a.let_mode == OMQ_LET_DIV) up[e] = gsc / f.sv[e];
+    else if (a.let_mode == OMQ_LET_MUL) up[e] = gsc * f.sv[e];
     cs[e] = c;
-    v0[e] = 0.f;
-    v1[e] = 0.f;
-    switch (a.col_mode) {
-      case COL_WEIGHT:
-      case COL_ACT_MUL:
-        v0[e] = gsc * xo[e];
-        break;
-      case COL_ACT_DIV:
-        v0[e] = gsc * (-xtl[e] / a.s[c]);
-        v1[e] = gsc * (-1.f / a.s[c]);
-        break;
-      default:
-        break;
+    const bool div = a.col_mode == COL_ACT_DIV;
+    const bool mul = a.col_mode == COL_WEIGHT || a.col_mode == COL_ACT_MUL;
+    v0[e] = div ? gsc * (-xtl[e] / f.sv[e]) : mul ? gsc * xo[e] : 0.f;
+    v1[e] = div ? gsc * (-1.f / f.sv[e]) : 0.f;
+  }
+  // the argmax term first, then the argmin term, on the value read before either
+  if (a.gx) {
+    float* gr = a.gx + f.r * a.ldgx;
+    if (f.iM == f.im) {
+      gr[f.iM] = (f.gxo[0] + up[0]) + up[1];
+    } else {
+      gr[f.iM] = f.gxo[0] + up[0];
+      gr[f.im] = f.gxo[1] + up[1];
     }
   }
 }
@@ -1385,11 +1408,11 @@ OMQ_DEV void row_finish(const RowQuantBwd& a, const RowFetch& f, float gh, float
 // Row finalizers, one workgroup per (column-partial tile, column group): the tile's
 // tile_rows rows (for group-wise rows, their quantizer rows of one 128-column group)
 // in one pass, LPR lanes per row summing its per-slab partials; then the rows'
-// scatter terms of the column outputs are merged in LDS and added to the tile's
-// column partials in row order: the first of the tile's terms on a column adds, in
-// row order, every term on that column.  The tile's partials of those columns have
-// this workgroup as their only writer, so the column pass that follows sums
-// everything in a fixed order.
+// scatter terms of the column outputs are merged by the first wave alone and added
+// to the tile's column partials in row order: the first of the tile's terms on a
+// column adds, in row order, every term on that column.  The tile's partials of
+// those columns have this workgroup as their only writer, so the column pass that
+// follows sums everything in a fixed order.
 constexpr int kFinThreads = 1024;
 
 template <int XDT, int LPR>
@@ -1397,7 +1420,7 @@ __global__ __launch_bounds__(kFinThreads) void k_ste_rows(RowQuantBwd a, int nsl
                                                           const float* rowpart, int tile_rows,
                                                           float* colpart, int merge) {
   __shared__ int e_col[256];
-  __shared__ float e_v0[256], e_v1[256];
+  __shared__ float e_v0[256], e_v1[256], e_c0[256], e_c1[256];
   const int64_t ng = a.group > 0 ? a.cols / 128 : 1;
   const int64_t t = blockIdx.x / ng, g = blockIdx.x % ng;
   const int64_t r0 = t * tile_rows;
@@ -1407,7 +1430,7 @@ __global__ __launch_bounds__(kFinThreads) void k_ste_rows(RowQuantBwd a, int nsl
   const bool valid = i < nr;
   const int64_t p = (r0 + i) * ng + g;                  // its quantizer row
   RowFetch rf;
-  if (valid && sub == 0) rf = row_fetch<XDT>(a, p);
+  if (valid && sub == 0) rf = row_fetch<XDT>(a, p, colpart, t, merge != 0);
   float gh = 0.f, gzs = 0.f;
   if (valid) {
     for (int s = sub; s < nslabs; s += LPR) {
@@ -1431,68 +1454,102 @@ __global__ __launch_bounds__(kFinThreads) void k_ste_rows(RowQuantBwd a, int nsl
         e_col[2 * i + e] = cs[e];
         e_v0[2 * i + e] = v0[e];
         e_v1[2 * i + e] = v1[e];
+        e_c0[2 * i + e] = rf.cp0[e];
+        e_c1[2 * i + e] = rf.cp1[e];
       }
     }
   }
   if (!merge) return;                                   // uniform over the workgroup
-  // every row's terms are in LDS before any thread reads another thread's
+  // every row's terms are in LDS before the first wave reads them
   __syncthreads();
-  // sort the terms by (column, term index): a bitonic sort of 256 keys in LDS, one per
-  // thread (the workgroup has at least 256), the unused slots keyed past every column
-  __shared__ int key[256];
-  __shared__ float sv0[256], sv1[256];
-  __shared__ int head[256];
+  if (threadIdx.x >= 64) return;
+  // The first wave merges the (at most 256) terms in registers, 4 per lane: term
+  // slot e = 4 lane + k.  Sort by (column, term index), a bitonic network whose
+  // partners are in the lane (distance 1, 2) or 4 slots per lane apart (a lane
+  // exchange); the unused slots are keyed past every column.
+  const int ln = (int)threadIdx.x;
   const int ne = 2 * nr;
-  const int e = threadIdx.x;
-  if (e < 256) key[e] = e < ne ? (e_col[e] << 8) | e : 0x7fffffff;
-  __syncthreads();
-  for (int k = 2; k <= 256; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const int o = e ^ j;
-      if (e < 256 && o > e) {
-        const int a0 = key[e], b0 = key[o];
-        if ((a0 > b0) == ((e & k) == 0)) {
-          key[e] = b0;
-          key[o] = a0;
-        }
+  int key[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int e = 4 * ln + k;
+    key[k] = e < ne ? (e_col[e] << 8) | e : 0x7fffffff;
+  }
+#pragma unroll
+  for (int kb = 2; kb <= 256; kb <<= 1) {
+#pragma unroll
+    for (int j = kb >> 1; j > 0; j >>= 1) {
+      int pk[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) pk[k] = j >= 4 ? __shfl_xor(key[k], j >> 2, 64) : key[k ^ j];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int e = 4 * ln + k, o = e ^ j;
+        const bool asc = (e & kb) == 0;
+        key[k] = (asc == (e < o)) ? min(key[k], pk[k]) : max(key[k], pk[k]);
       }
-      __syncthreads();
     }
   }
-  // a segmented inclusive scan of each column's run (fixed tree order), then the last
-  // term of each run adds the run's total to the tile's partial of that column
-  int c = -1;
-  if (e < 256) {
-    const int kv = key[e];
-    c = kv >> 8;
-    const bool real = e < ne;
-    sv0[e] = real ? e_v0[kv & 255] : 0.f;
-    sv1[e] = real ? e_v1[kv & 255] : 0.f;
-    head[e] = e == 0 || (key[e - 1] >> 8) != c;
+  // a segmented inclusive scan of each column's run (the tree of offsets 1, 2, 4,
+  // ..., 128), then the last term of each run adds the run's total to the tile's
+  // partial of that column (read before any term was added)
+  int col[4], hd[4];
+  float s0[4], s1[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int e = 4 * ln + k;
+    col[k] = key[k] >> 8;
+    s0[k] = e < ne ? e_v0[key[k] & 255] : 0.f;
+    s1[k] = e < ne ? e_v1[key[k] & 255] : 0.f;
   }
-  __syncthreads();
+  {
+    const int pc = __shfl_up(col[3], 1, 64);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = 4 * ln + k;
+      hd[k] = e == 0 || (k > 0 ? col[k - 1] : pc) != col[k];
+    }
+  }
+#pragma unroll
   for (int off = 1; off < 256; off <<= 1) {
-    float a0 = 0.f, a1 = 0.f;
-    int hd = 1;
-    if (e < 256) {
-      hd = head[e];
-      if (!hd && e >= off) {
-        a0 = sv0[e - off];
-        a1 = sv1[e - off];
-        hd = head[e - off];
+    float a0[4], a1[4];
+    int ah[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (off >= 4) {
+        a0[k] = __shfl_up(s0[k], off >> 2, 64);
+        a1[k] = __shfl_up(s1[k], off >> 2, 64);
+        ah[k] = __shfl_up(hd[k], off >> 2, 64);
+      } else if (k >= off) {
+        a0[k] = s0[k - off];
+        a1[k] = s1[k - off];
+        ah[k] = hd[k - off];
+      } else {
+        a0[k] = __shfl_up(s0[(k - off + 4) & 3], 1, 64);
+        a1[k] = __shfl_up(s1[(k - off + 4) & 3], 1, 64);
+        ah[k] = __shfl_up(hd[(k - off + 4) & 3], 1, 64);
       }
     }
-    __syncthreads();
-    if (e < 256 && !head[e] && e >= off) {
-      sv0[e] += a0;
-      sv1[e] += a1;
-      head[e] = hd;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = 4 * ln + k;
+      if (!hd[k] && e >= off) {
+        s0[k] += a0[k];
+        s1[k] += a1[k];
+        hd[k] = ah[k];
+      }
     }
-    __syncthreads();
   }
-  if (e < ne && (e == ne - 1 || (key[e + 1] >> 8) != c)) {
-    colpart[(t * 2 + 0) * a.cols + c] += sv0[e];
-    colpart[(t * 2 + 1) * a.cols + c] += sv1[e];
+  const int nc = __shfl_down(col[0], 1, 64);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int e = 4 * ln + k;
+    const int cn = k < 3 ? col[k + 1] : nc;
+    if (e < ne && (e == ne - 1 || cn != col[k])) {
+      const int te = key[k] & 255;
+      colpart[(t * 2 + 0) * a.cols + col[k]] = e_c0[te] + s0[k];
+      colpart[(t * 2 + 1) * a.cols + col[k]] = e_c1[te] + s1[k];
+    }
   }
 }
 
