@@ -126,6 +126,11 @@ struct Ws {
   uint16_t *dyb, *gGUb, *dh1b, *gOb, *gYb;
   float *cs, *gs_full, *gd_full, *gsa_full;
   float *rq, *csws, *msews;
+  // the weight side's straight-through partials of q|k|v, o, gate|up, down (kept until
+  // their finalizers run together at the end of the backward)
+  float* wpart[4];
+  // the Q~, K~, V quantizers' straight-through partials (their finalizers run together)
+  float* apart[3];
   // integer codes of the forward's product operands (weights, activations)
   uint8_t *Cqkv, *Co, *Cgu, *Cd, *Cxqkv, *Cxo, *Cxf, *Cxd;
   size_t total;
@@ -186,6 +191,20 @@ Ws layout(const Dims& m, void* base) {
     rq = std::max(rq, ste_partials_floats(r[0], r[1], nsl, ntl) * sizeof(float));
   }
   w.rq = b.take<float>(rq / 4);
+  {
+    const int64_t wsh[4][2] = {{nqkv, d}, {d, dq}, {2 * F, d}, {d, F}};
+    for (int i = 0; i < 4; ++i) {
+      if (!att && i < 2) continue;
+      int64_t nsl, ntl;
+      gemm_ste_extents(wsh[i][0], wsh[i][1], &nsl, &ntl);
+      w.wpart[i] = b.take<float>((int64_t)ste_partials_floats(wsh[i][0], wsh[i][1], nsl, ntl));
+    }
+    if (att) {
+      w.apart[0] = b.take<float>((int64_t)(rowquant_bwd_ws_bytes(T, dq) / 4));
+      w.apart[1] = b.take<float>((int64_t)(rowquant_bwd_ws_bytes(T, dk) / 4));
+      w.apart[2] = b.take<float>((int64_t)(rowquant_bwd_ws_bytes(T, dk) / 4));
+    }
+  }
   w.csws = b.take<float>(colsum_ws_bytes(T, std::max(nqkv, 2 * F)) / 4);
   w.msews = b.take<float>(2048);
   if (m.codes) {
@@ -590,14 +609,15 @@ int forward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& w
 hipError_t abwd(const Ws& w, const float* g, int64_t T, int64_t C, const void* X, int x_dt,
                 int64_t ldx, int mode, const float* s, const float* delta, int abits,
                 const Stats& st, float* gx, int64_t ldgx, int col_mode, float* out0, float* out1,
-                int accumulate, hipStream_t stream) {
+                int accumulate, hipStream_t stream, float* part = nullptr,
+                SteFinJob* job = nullptr) {
   RowQuantBwd a;
   a.g = g; a.ldg = C; a.x = X; a.x_dt = x_dt; a.rows = T; a.cols = C; a.ldx = ldx;
   a.let_mode = mode; a.s = s; a.delta = delta; a.nbits = abits;
   a.h = st.h; a.z = st.z; a.amax = st.amax; a.amin = st.amin;
   a.col_mode = col_mode; a.gx = gx; a.ldgx = ldgx;
-  a.out0 = out0; a.out1 = out1; a.accumulate = accumulate; a.ws = w.rq;
-  return launch_rowquant_bwd(a, stream);
+  a.out0 = out0; a.out1 = out1; a.accumulate = accumulate; a.ws = part ? part : w.rq;
+  return launch_rowquant_bwd_tiles(a, stream, job);
 }
 
 // The backward of one (possibly concatenated) quantized linear with both
@@ -642,6 +662,23 @@ struct LinBwd {
   // q|k|v: the Q and K columns of gY come from their rotated gradients (inverse RoPE
   // on the way to the bf16 copy); NULL otherwise
   const RopeIn* rope;
+  // the weight side's partials in a buffer of their own (else the shared w.rq), and
+  // its finalizers queued there instead of launched (else launched at once)
+  float* wpart;
+  struct FinQueue* defer;
+};
+
+// Weight-side finalizers queued by the layers' backward passes: nothing reads their
+// outputs (the logit gradients, the LET scales' column totals) before the update, so
+// they run together, two launches for the whole block, once every GEMM is done.
+struct FinQueue {
+  SteFinJob job[kMaxFinJobs];
+  int n = 0;
+  hipError_t flush(hipStream_t st) {
+    const hipError_t e = launch_ste_finish_multi(job, n, st);
+    n = 0;
+    return e;
+  }
 };
 
 hipError_t lin_bwd_fused(const Ws& w, const LinBwd& L, int64_t T, int wbits, int abits,
@@ -659,8 +696,9 @@ hipError_t lin_bwd_fused(const Ws& w, const LinBwd& L, int64_t T, int wbits, int
   // weight side (skipped when no learnable parameter depends on these weights)
   if (wbits < 16 || L.s_w) {
     gemm_ste_extents(N, K, &nsl, &ntl);
-    float* rowpart = w.rq;
-    float* colpart = w.rq + nsl * N * 2;
+    float* const base = L.wpart ? L.wpart : w.rq;
+    float* rowpart = base;
+    float* colpart = base + nsl * N * 2;
     Gemm g;
     g.A = L.gYb; g.lda = N; g.ta = 1; g.B = L.Xh; g.ldb = K; g.tb = 1;
     g.C = nullptr; g.ldc = K; g.M = N; g.N = K; g.K = T;
@@ -703,9 +741,16 @@ hipError_t lin_bwd_fused(const Ws& w, const LinBwd& L, int64_t T, int wbits, int
     b.col_mode = se.col_mode; b.out0 = L.gs_w;
     if (grouped) b.group = L.group;
     // the row finalizers, then the column sums with their scatter terms (both into gs_w)
-    if ((e = launch_ste_finish(a, (int)ntl, colpart, b, grouped ? 1 : (int)nsl, rowpart,
-                               kSteTileRows, st)) != hipSuccess)
+    if (L.defer && L.wpart && L.defer->n < kMaxFinJobs) {
+      SteFinJob& j = L.defer->job[L.defer->n++];
+      j.rf = b; j.nslabs = grouped ? 1 : (int)nsl; j.tile_rows = kSteTileRows;
+      j.ntiles = (int)ntl; j.rowpart = rowpart; j.colpart = colpart;
+      j.cols = a.cols; j.col_mode = a.col_mode; j.out0 = a.out0; j.out1 = a.out1;
+      j.accumulate = a.accumulate;
+    } else if ((e = launch_ste_finish(a, (int)ntl, colpart, b, grouped ? 1 : (int)nsl, rowpart,
+                                      kSteTileRows, st)) != hipSuccess) {
       return e;
+    }
   }
   // activation side
   gemm_ste_extents(T, K, &nsl, &ntl);
@@ -738,6 +783,7 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
   const int64_t T = m.T, d = m.d, F = m.F, dq = m.dq, dk = m.dk, nqkv = m.nqkv;
   const int wb = bd->wbits, ab = bd->abits;
   CK(launch_fill_f32(dth, t.total, 0.f, st));
+  FinQueue fq;          // the weight side's finalizers, run after the last GEMM
   // the column sums add into their destinations: the o-site LET gradients of grouped
   // heads are formed per query channel first
   if (!m.ffn_only && m.grp > 1) {
@@ -753,6 +799,7 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
     L.have_gYb = dyb_ready;            // no LET on down: no column sums needed
     L.segs = segs; L.nseg = 1; L.wst = w.wq_d;
     L.X = w.A; L.x_dt = OMQ_F32; L.a_mode = OMQ_LET_NONE; L.ast = w.a_d; L.gx_out = w.gA;
+    L.wpart = w.wpart[3]; L.defer = &fq;
     CK(lin_bwd_fused(w, L, T, wb, ab, th, t, dth, st, tm));
   }
   // dL/d(gate|up) goes straight to its bf16 operand form with its column sums
@@ -773,9 +820,13 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
     L.X = m.ffn_only ? x : (const void*)w.xn2; L.x_dt = m.ffn_only ? OMQ_BF16 : OMQ_F32;
     L.a_mode = OMQ_LET_DIV; L.s_x = th + t.s_ffn; L.d_x = th + t.d_ffn; L.ast = w.a_f;
     L.gx_out = m.ffn_only ? nullptr : w.gxn2; L.gs_x = dth + t.s_ffn; L.gd_x = dth + t.d_ffn;
+    L.wpart = w.wpart[2]; L.defer = &fq;
     CK(lin_bwd_fused(w, L, T, wb, ab, th, t, dth, st, tm));
   }
-  if (m.ffn_only) return OMQ_OK;
+  if (m.ffn_only) {
+    CK(fq.flush(st));
+    return OMQ_OK;
+  }
   const KvSites kv = kv_sites(m, t, w, th, dth);
 
   // RMSNorm before the FFN, residual
@@ -790,11 +841,8 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
     L.gs_w = kv.gs_o; L.gd_w = kv.gd_o;
     L.X = w.O; L.x_dt = OMQ_F32; L.a_mode = OMQ_LET_DIV; L.s_x = kv.s_o; L.d_x = kv.d_o;
     L.ast = w.a_o; L.gx_out = w.gO; L.gs_x = kv.gs_o; L.gd_x = kv.gd_o;
+    L.wpart = w.wpart[1]; L.defer = &fq;
     CK(lin_bwd_fused(w, L, T, wb, ab, th, t, dth, st, tm));
-  }
-  if (m.grp > 1) {
-    CK(launch_kv_reduce_add(w.gs_full, m.nq, m.nkv, m.hd, dth + t.s_o, st));
-    CK(launch_kv_reduce_add(w.gd_full, m.nq, m.nkv, m.hd, dth + t.d_o, st));
   }
   // attention backward (scores recomputed from the forward's log-sum-exp; dQ from the
   // dS the dK/dV pass writes)
@@ -811,16 +859,21 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
     CK(launch_flash_bwd(f, st));
   }
   // Q~ / K~ / V quantizers and s_a
+  // (the three tile passes, then their finalizers together: each has partial buffers
+  // of its own; the Q and K column passes, both into s_a without grouped heads, keep
+  // their order)
   const bool sa = m.use_sa;
+  SteFinJob qkvj[3];
   CK(abwd(w, w.gQh, T, dq, w.Qr, OMQ_F32, dq, sa ? OMQ_LET_DIV : OMQ_LET_NONE, kv.sa_q, nullptr,
           ab, w.a_q, w.gQr, dq, sa ? COL_ACT_DIV : COL_NONE, sa ? kv.gsa_q : nullptr, nullptr,
           m.grp > 1 ? 0 : 1,
-          st));
+          st, w.apart[0], &qkvj[0]));
   CK(abwd(w, w.gKh, T, dk, w.Kr, OMQ_F32, dk, sa ? OMQ_LET_MUL : OMQ_LET_NONE,
           sa ? th + t.s_a : nullptr, nullptr, ab, w.a_k, w.gKr, dk, sa ? COL_ACT_MUL : COL_NONE,
-          sa ? dth + t.s_a : nullptr, nullptr, 1, st));
+          sa ? dth + t.s_a : nullptr, nullptr, 1, st, w.apart[1], &qkvj[1]));
   CK(abwd(w, w.gVh, T, dk, w.Yqkv + dq + dk, OMQ_F32, nqkv, OMQ_LET_NONE, nullptr, nullptr, ab,
-          w.a_v, w.gY + dq + dk, nqkv, COL_NONE, nullptr, nullptr, 0, st));
+          w.a_v, w.gY + dq + dk, nqkv, COL_NONE, nullptr, nullptr, 0, st, w.apart[2], &qkvj[2]));
+  CK(launch_ste_finish_multi(qkvj, 3, st));
   if (sa && m.grp > 1) CK(launch_kv_reduce_add(w.gsa_full, m.nq, m.nkv, m.hd, dth + t.s_a, st));
   // q / k / v with the shared qkv LET site; the inverse RoPE of the Q and K gradients
   // runs inside the bf16 conversion of dL/dY
@@ -837,7 +890,15 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
     L.d_x = th + t.d_qkv; L.ast = w.a_qkv; L.gx_out = nullptr;
     L.gs_x = dth + t.s_qkv; L.gd_x = dth + t.d_qkv;
     L.rope = &rp;
+    L.wpart = w.wpart[0]; L.defer = &fq;
     CK(lin_bwd_fused(w, L, T, wb, ab, th, t, dth, st, tm));
+  }
+  CK(fq.flush(st));
+  // the o-site LET gradients of grouped heads, per query channel until here (the
+  // activation side's terms, then the weight side's), summed over each group
+  if (m.grp > 1) {
+    CK(launch_kv_reduce_add(w.gs_full, m.nq, m.nkv, m.hd, dth + t.s_o, st));
+    CK(launch_kv_reduce_add(w.gd_full, m.nq, m.nkv, m.hd, dth + t.d_o, st));
   }
   return OMQ_OK;
 }

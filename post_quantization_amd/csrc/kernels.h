@@ -112,6 +112,25 @@ size_t ste_partials_floats(int64_t rows, int64_t cols, int64_t nslabs, int64_t n
 hipError_t launch_ste_finish(const RowQuantBwd& cf, int ntiles, float* colpart,
                              const RowQuantBwd& rf, int nslabs, const float* rowpart,
                              int tile_rows, hipStream_t st);
+// Independent finalizer jobs (each one launch_ste_finish's arguments, with cf's
+// column-pass fields inline) in two launches in all: every job's row finalizers,
+// then every job's column pass.  Jobs share no partial buffers and no outputs, so
+// each output gets the same sums in the same order as from its own launches.
+constexpr int kMaxFinJobs = 4;
+struct SteFinJob {
+  RowQuantBwd rf;
+  int nslabs = 0, tile_rows = 0, ntiles = 0;
+  const float* rowpart = nullptr;
+  float* colpart = nullptr;
+  int64_t cols = 0;
+  int col_mode = COL_NONE;
+  float *out0 = nullptr, *out1 = nullptr;
+  int accumulate = 0;
+};
+hipError_t launch_ste_finish_multi(const SteFinJob* jobs, int n, hipStream_t st);
+// launch_rowquant_bwd's tile pass alone, its finalizers left in *job for
+// launch_ste_finish_multi (job->rf.rows 0: nothing to finish)
+hipError_t launch_rowquant_bwd_tiles(const RowQuantBwd& a, hipStream_t st, SteFinJob* job);
 
 // LET alone: y = (x - delta) / s  or  y = s * x, elementwise over [rows x cols].
 hipError_t launch_let_elementwise(const void* x, int x_dt, int64_t rows, int64_t cols,

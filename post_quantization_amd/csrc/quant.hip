@@ -1415,14 +1415,14 @@ OMQ_DEV void row_finish(const RowQuantBwd& a, const RowFetch& f, float gh, float
 // follows sums everything in a fixed order.
 constexpr int kFinThreads = 1024;
 
+// The finalizers of one unit (bid: the workgroup's index within its job).
 template <int XDT, int LPR>
-__global__ __launch_bounds__(kFinThreads) void k_ste_rows(RowQuantBwd a, int nslabs,
-                                                          const float* rowpart, int tile_rows,
-                                                          float* colpart, int merge) {
+OMQ_DEV void ste_rows_unit(const RowQuantBwd& a, int nslabs, const float* rowpart,
+                           int tile_rows, float* colpart, int merge, int64_t bid) {
   __shared__ int e_col[256];
   __shared__ float e_v0[256], e_v1[256], e_c0[256], e_c1[256];
   const int64_t ng = a.group > 0 ? a.cols / 128 : 1;
-  const int64_t t = blockIdx.x / ng, g = blockIdx.x % ng;
+  const int64_t t = bid / ng, g = bid % ng;
   const int64_t r0 = t * tile_rows;
   const int nr = (int)min((int64_t)tile_rows, a.rows - r0);
   const int sub = (int)(threadIdx.x % LPR);
@@ -1553,17 +1553,57 @@ __global__ __launch_bounds__(kFinThreads) void k_ste_rows(RowQuantBwd a, int nsl
   }
 }
 
+template <int XDT, int LPR>
+__global__ __launch_bounds__(kFinThreads) void k_ste_rows(RowQuantBwd a, int nslabs,
+                                                          const float* rowpart, int tile_rows,
+                                                          float* colpart, int merge) {
+  ste_rows_unit<XDT, LPR>(a, nslabs, rowpart, tile_rows, colpart, merge, blockIdx.x);
+}
+
+// Up to kMaxFinJobs independent finalizer jobs in one launch: job j takes the
+// workgroups [sum of the earlier jobs' units, + its own units).  Each job is read
+// through a constant index (a run-time index into the argument block would copy it
+// to scratch memory).
+struct SteRowsJob {
+  RowQuantBwd a;
+  const float* rowpart;
+  float* colpart;
+  int nslabs, tile_rows, merge, units;
+};
+struct SteRowsJobs {
+  SteRowsJob j[kMaxFinJobs];
+  int n;
+};
+
+// (at most 64 registers, so two workgroups of 16 waves fit on a compute unit)
+template <int XDT, int LPR>
+__global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(8)))
+void k_ste_rows_multi(SteRowsJobs m) {
+  int64_t bid = blockIdx.x;
+#pragma unroll
+  for (int q = 0; q < kMaxFinJobs; ++q) {
+    if (q < m.n) {
+      const SteRowsJob& jb = m.j[q];
+      if (bid < jb.units) {
+        ste_rows_unit<XDT, LPR>(jb.a, jb.nslabs, jb.rowpart, jb.tile_rows, jb.colpart,
+                                jb.merge, bid);
+        return;
+      }
+      bid -= jb.units;
+    }
+  }
+}
+
 // Column pass of a straight-through backward, after the row finalizers: per column c
 // (64 per workgroup, 4 waves)
 //   out_k[c] = (accumulate ? out_k[c] : 0) + sum_t colpart_k[t][c]
 // the waves taking the partial rows t = w, w + 4, ..., their sums added in LDS in
 // wave order.  Deterministic: no atomics anywhere.
-__global__ __launch_bounds__(kThreads) void k_ste_cols(const float* colpart, int ntiles,
-                                                       int64_t cols, float* out0, float* out1,
-                                                       int accumulate) {
+OMQ_DEV void ste_cols_unit(const float* colpart, int ntiles, int64_t cols, float* out0,
+                           float* out1, int accumulate, int64_t bid) {
   __shared__ float red[2][4][64];
   const int lane = threadIdx.x & 63, w = wave_id();
-  const int64_t c = (int64_t)blockIdx.x * 64 + lane;
+  const int64_t c = bid * 64 + lane;
   float s0 = 0.f, s1 = 0.f;
   if (c < cols) {
 #pragma unroll 4
@@ -1580,6 +1620,38 @@ __global__ __launch_bounds__(kThreads) void k_ste_cols(const float* colpart, int
     if (o) {
       const float cs = ((red[w][0][lane] + red[w][1][lane]) + red[w][2][lane]) + red[w][3][lane];
       o[c] = (accumulate ? o[c] : 0.f) + cs;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void k_ste_cols(const float* colpart, int ntiles,
+                                                       int64_t cols, float* out0, float* out1,
+                                                       int accumulate) {
+  ste_cols_unit(colpart, ntiles, cols, out0, out1, accumulate, blockIdx.x);
+}
+
+struct SteColsJob {
+  const float* colpart;
+  float *out0, *out1;
+  int64_t cols;
+  int ntiles, accumulate, units;
+};
+struct SteColsJobs {
+  SteColsJob j[kMaxFinJobs];
+  int n;
+};
+
+__global__ __launch_bounds__(kThreads) void k_ste_cols_multi(SteColsJobs m) {
+  int64_t bid = blockIdx.x;
+#pragma unroll
+  for (int q = 0; q < kMaxFinJobs; ++q) {
+    if (q < m.n) {
+      const SteColsJob& jb = m.j[q];
+      if (bid < jb.units) {
+        ste_cols_unit(jb.colpart, jb.ntiles, jb.cols, jb.out0, jb.out1, jb.accumulate, bid);
+        return;
+      }
+      bid -= jb.units;
     }
   }
 }
@@ -2029,6 +2101,11 @@ size_t rowquant_bwd_ws_bytes(int64_t rows, int64_t cols) {
 }
 
 hipError_t launch_rowquant_bwd(const RowQuantBwd& a, hipStream_t st) {
+  return launch_rowquant_bwd_tiles(a, st, nullptr);
+}
+
+hipError_t launch_rowquant_bwd_tiles(const RowQuantBwd& a, hipStream_t st, SteFinJob* job) {
+  if (job) *job = SteFinJob{};        // nothing to finish unless filled in below
   if (a.rows == 0 || a.cols == 0) return hipSuccess;
   if (a.group > 0 && (a.group != 128 || a.cols % 128)) return hipErrorInvalidValue;
   const int64_t nslabs = (a.cols + kSlab - 1) / kSlab;
@@ -2056,6 +2133,13 @@ hipError_t launch_rowquant_bwd(const RowQuantBwd& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rs = a.group > 0 ? 1 : (int)nslabs;
+  if (job) {
+    job->rf = a; job->nslabs = rs; job->tile_rows = R; job->ntiles = (int)ntiles;
+    job->rowpart = rowpart; job->colpart = colpart;
+    job->cols = a.cols; job->col_mode = a.col_mode; job->out0 = a.out0; job->out1 = a.out1;
+    job->accumulate = a.accumulate;
+    return hipSuccess;
+  }
   return launch_ste_finish(a, (int)ntiles, colpart, a, rs, rowpart, R, st);
 }
 
@@ -2097,6 +2181,91 @@ hipError_t launch_ste_finish(const RowQuantBwd& cf, int ntiles, float* colpart,
   hipLaunchKernelGGL(k_ste_cols, dim3((unsigned)((cf.cols + 63) / 64)), dim3(kThreads), 0, st,
                      colpart, ntiles, cf.cols, cf.out0, cf.out1, cf.accumulate);
   return hipGetLastError();
+}
+
+hipError_t launch_ste_finish_multi(const SteFinJob* jobs, int n, hipStream_t st) {
+  if (n < 0 || n > kMaxFinJobs) return hipErrorInvalidValue;
+  SteRowsJobs rj{};
+  SteColsJobs cj{};
+  int lpr0 = -1, xdt0 = -1, nt0 = -1;
+  bool rows_one = true;              // every job's row finalizers take one kernel instance
+  int64_t rows_units = 0, cols_units = 0;
+  for (int i = 0; i < n; ++i) {
+    const SteFinJob& J = jobs[i];
+    const RowQuantBwd& rf = J.rf;
+    if (J.tile_rows < 1 || J.tile_rows > 128) return hipErrorInvalidValue;
+    const bool cols_out = J.col_mode != COL_NONE && (J.out0 || J.out1) && J.cols > 0;
+    if (rf.nbits < 16 && rf.rows > 0) {
+      const int64_t ng = rf.group > 0 ? rf.cols / 128 : 1;
+      const int lpr = J.nslabs == 1 ? 1 : J.tile_rows > 64 ? 8 : 16;
+      const int nt = std::max(256, (J.tile_rows * lpr + 63) / 64 * 64);
+      rows_one = rows_one && (nt0 < 0 || nt == nt0) && (lpr0 < 0 || lpr == lpr0) &&
+                 (xdt0 < 0 || rf.x_dt == xdt0);
+      nt0 = nt;
+      lpr0 = lpr;
+      xdt0 = rf.x_dt;
+      SteRowsJob& r = rj.j[rj.n++];
+      r.a = rf; r.rowpart = J.rowpart; r.colpart = J.colpart; r.nslabs = J.nslabs;
+      r.tile_rows = J.tile_rows; r.merge = cols_out && rf.col_mode != COL_NONE;
+      r.units = (int)(((rf.rows + J.tile_rows - 1) / J.tile_rows) * ng);
+      rows_units += r.units;
+    }
+    if (cols_out) {
+      SteColsJob& c = cj.j[cj.n++];
+      c.colpart = J.colpart; c.out0 = J.out0; c.out1 = J.out1; c.cols = J.cols;
+      c.ntiles = J.ntiles; c.accumulate = J.accumulate; c.units = (int)((J.cols + 63) / 64);
+      cols_units += c.units;
+    }
+  }
+  // two column passes adding into one output must not run side by side
+  bool cols_disjoint = true;
+  for (int a0 = 0; a0 < cj.n; ++a0)
+    for (int b0 = a0 + 1; b0 < cj.n; ++b0) {
+      const float* oa[2] = {cj.j[a0].out0, cj.j[a0].out1};
+      const float* ob[2] = {cj.j[b0].out0, cj.j[b0].out1};
+      for (const float* x : oa)
+        for (const float* y : ob) cols_disjoint = cols_disjoint && !(x && x == y);
+    }
+  if (!rows_one) {
+    // jobs that need different kernel instances: one launch_ste_finish each, in order
+    for (int i = 0; i < n; ++i) {
+      const SteFinJob& J = jobs[i];
+      RowQuantBwd cf;
+      cf.cols = J.cols; cf.col_mode = J.col_mode; cf.out0 = J.out0; cf.out1 = J.out1;
+      cf.accumulate = J.accumulate;
+      const hipError_t e = launch_ste_finish(cf, J.ntiles, J.colpart, J.rf, J.nslabs, J.rowpart,
+                                             J.tile_rows, st);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  if (rj.n > 0) {
+    const dim3 grid((unsigned)rows_units), block((unsigned)nt0);
+    const bool f32 = xdt0 == OMQ_F32;
+#define OMQ_ROWS_M(L)                                                                        \
+  if (lpr0 == L) {                                                                           \
+    if (f32) hipLaunchKernelGGL((k_ste_rows_multi<OMQ_F32, L>), grid, block, 0, st, rj);     \
+    else hipLaunchKernelGGL((k_ste_rows_multi<OMQ_BF16, L>), grid, block, 0, st, rj);        \
+  }
+    OMQ_ROWS_M(1) OMQ_ROWS_M(8) OMQ_ROWS_M(16)
+#undef OMQ_ROWS_M
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (cj.n == 0) return hipSuccess;
+  if (cols_disjoint) {
+    hipLaunchKernelGGL(k_ste_cols_multi, dim3((unsigned)cols_units), dim3(kThreads), 0, st, cj);
+    return hipGetLastError();
+  }
+  // column passes that share an output, in job order
+  for (int i = 0; i < cj.n; ++i) {
+    const SteColsJob& c = cj.j[i];
+    hipLaunchKernelGGL(k_ste_cols, dim3((unsigned)c.units), dim3(kThreads), 0, st, c.colpart,
+                       c.ntiles, c.cols, c.out0, c.out1, c.accumulate);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_let_elementwise(const void* x, int x_dt, int64_t rows, int64_t cols, int mode,
