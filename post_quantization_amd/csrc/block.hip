@@ -131,6 +131,8 @@ struct Ws {
   float* wpart[4];
   // the Q~, K~, V quantizers' straight-through partials (their finalizers run together)
   float* apart[3];
+  // the activation side's partials of gate|up, o and q|k|v (column passes at the end)
+  float* xpart[3];
   // integer codes of the forward's product operands (weights, activations)
   uint8_t *Cqkv, *Co, *Cgu, *Cd, *Cxqkv, *Cxo, *Cxf, *Cxd;
   size_t total;
@@ -198,6 +200,13 @@ Ws layout(const Dims& m, void* base) {
       int64_t nsl, ntl;
       gemm_ste_extents(wsh[i][0], wsh[i][1], &nsl, &ntl);
       w.wpart[i] = b.take<float>((int64_t)ste_partials_floats(wsh[i][0], wsh[i][1], nsl, ntl));
+    }
+    const int64_t xk[3] = {d, dq, d};
+    for (int i = 0; i < 3; ++i) {
+      if (!att && i > 0) continue;
+      int64_t nsl, ntl;
+      gemm_ste_extents(T, xk[i], &nsl, &ntl);
+      w.xpart[i] = b.take<float>((int64_t)ste_partials_floats(T, xk[i], nsl, ntl));
     }
     if (att) {
       w.apart[0] = b.take<float>((int64_t)(rowquant_bwd_ws_bytes(T, dq) / 4));
@@ -666,6 +675,9 @@ struct LinBwd {
   // its finalizers queued there instead of launched (else launched at once)
   float* wpart;
   struct FinQueue* defer;
+  // the activation side's partials in a buffer of their own (else w.rq): its column
+  // pass queued (its row finalizers too when dL/dX is not written)
+  float* xpart;
 };
 
 // Weight-side finalizers queued by the layers' backward passes: nothing reads their
@@ -674,6 +686,8 @@ struct LinBwd {
 struct FinQueue {
   SteFinJob job[kMaxFinJobs];
   int n = 0;
+  bool room() const { return n < kMaxFinJobs; }
+  void push(const SteFinJob& j) { job[n++] = j; }
   hipError_t flush(hipStream_t st) {
     const hipError_t e = launch_ste_finish_multi(job, n, st);
     n = 0;
@@ -741,12 +755,13 @@ hipError_t lin_bwd_fused(const Ws& w, const LinBwd& L, int64_t T, int wbits, int
     b.col_mode = se.col_mode; b.out0 = L.gs_w;
     if (grouped) b.group = L.group;
     // the row finalizers, then the column sums with their scatter terms (both into gs_w)
-    if (L.defer && L.wpart && L.defer->n < kMaxFinJobs) {
-      SteFinJob& j = L.defer->job[L.defer->n++];
+    if (L.defer && L.wpart && L.defer->room()) {
+      SteFinJob j;
       j.rf = b; j.nslabs = grouped ? 1 : (int)nsl; j.tile_rows = kSteTileRows;
       j.ntiles = (int)ntl; j.rowpart = rowpart; j.colpart = colpart;
       j.cols = a.cols; j.col_mode = a.col_mode; j.out0 = a.out0; j.out1 = a.out1;
       j.accumulate = a.accumulate;
+      L.defer->push(j);
     } else if ((e = launch_ste_finish(a, (int)ntl, colpart, b, grouped ? 1 : (int)nsl, rowpart,
                                       kSteTileRows, st)) != hipSuccess) {
       return e;
@@ -754,8 +769,9 @@ hipError_t lin_bwd_fused(const Ws& w, const LinBwd& L, int64_t T, int wbits, int
   }
   // activation side
   gemm_ste_extents(T, K, &nsl, &ntl);
-  float* rowpart = w.rq;
-  float* colpart = w.rq + nsl * T * 2;
+  float* const xbase = L.xpart ? L.xpart : w.rq;
+  float* rowpart = xbase;
+  float* colpart = xbase + nsl * T * 2;
   Gemm g;
   g.A = L.gYb; g.lda = N; g.B = L.Wh; g.ldb = K; g.tb = 1;
   g.C = L.gx_out; g.ldc = K; g.M = T; g.N = K; g.K = N;
@@ -773,6 +789,23 @@ hipError_t lin_bwd_fused(const Ws& w, const LinBwd& L, int64_t T, int wbits, int
   a.h = L.ast.h; a.z = L.ast.z; a.amax = L.ast.amax; a.amin = L.ast.amin;
   a.col_mode = acol; a.gx = L.gx_out; a.ldgx = K;
   a.out0 = L.gs_x; a.out1 = L.gd_x; a.accumulate = 1;
+  const bool cols_out = acol != COL_NONE && (a.out0 || a.out1) && K > 0;
+  if (L.defer && L.xpart && cols_out && L.defer->room()) {
+    SteFinJob j;
+    j.rf = a; j.nslabs = (int)nsl; j.tile_rows = kSteTileRows; j.ntiles = (int)ntl;
+    j.rowpart = rowpart; j.colpart = colpart;
+    j.cols = K; j.col_mode = acol; j.out0 = a.out0; j.out1 = a.out1; j.accumulate = 1;
+    if (L.gx_out) {
+      // the row finalizers now (their scatter completes dL/dX for the next stage),
+      // merging into this layer's own column partials; the column pass queued
+      if ((e = launch_ste_finish_rows(a, colpart, a, (int)nsl, rowpart, kSteTileRows, st)) !=
+          hipSuccess)
+        return e;
+      j.rf.rows = 0;
+    }
+    L.defer->push(j);
+    return hipSuccess;
+  }
   return launch_ste_finish(a, (int)ntl, colpart, a, (int)nsl, rowpart, kSteTileRows, st);
 }
 
@@ -820,7 +853,7 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
     L.X = m.ffn_only ? x : (const void*)w.xn2; L.x_dt = m.ffn_only ? OMQ_BF16 : OMQ_F32;
     L.a_mode = OMQ_LET_DIV; L.s_x = th + t.s_ffn; L.d_x = th + t.d_ffn; L.ast = w.a_f;
     L.gx_out = m.ffn_only ? nullptr : w.gxn2; L.gs_x = dth + t.s_ffn; L.gd_x = dth + t.d_ffn;
-    L.wpart = w.wpart[2]; L.defer = &fq;
+    L.wpart = w.wpart[2]; L.xpart = w.xpart[0]; L.defer = &fq;
     CK(lin_bwd_fused(w, L, T, wb, ab, th, t, dth, st, tm));
   }
   if (m.ffn_only) {
@@ -841,7 +874,7 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
     L.gs_w = kv.gs_o; L.gd_w = kv.gd_o;
     L.X = w.O; L.x_dt = OMQ_F32; L.a_mode = OMQ_LET_DIV; L.s_x = kv.s_o; L.d_x = kv.d_o;
     L.ast = w.a_o; L.gx_out = w.gO; L.gs_x = kv.gs_o; L.gd_x = kv.gd_o;
-    L.wpart = w.wpart[1]; L.defer = &fq;
+    L.wpart = w.wpart[1]; L.xpart = w.xpart[1]; L.defer = &fq;
     CK(lin_bwd_fused(w, L, T, wb, ab, th, t, dth, st, tm));
   }
   // attention backward (scores recomputed from the forward's log-sum-exp; dQ from the
@@ -873,8 +906,21 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
           sa ? dth + t.s_a : nullptr, nullptr, 1, st, w.apart[1], &qkvj[1]));
   CK(abwd(w, w.gVh, T, dk, w.Yqkv + dq + dk, OMQ_F32, nqkv, OMQ_LET_NONE, nullptr, nullptr, ab,
           w.a_v, w.gY + dq + dk, nqkv, COL_NONE, nullptr, nullptr, 0, st, w.apart[2], &qkvj[2]));
+  // their row finalizers now (the scatter completes the gradients the q|k|v backward
+  // reads), their column passes (s_a) queued
+  for (SteFinJob& j : qkvj) j.skip_cols = true;
   CK(launch_ste_finish_multi(qkvj, 3, st));
-  if (sa && m.grp > 1) CK(launch_kv_reduce_add(w.gsa_full, m.nq, m.nkv, m.hd, dth + t.s_a, st));
+  for (SteFinJob& j : qkvj) {
+    if (j.col_mode == COL_NONE || !(j.out0 || j.out1) || j.cols == 0) continue;
+    SteFinJob c = j;
+    c.rf.rows = 0;
+    c.skip_cols = false;
+    if (fq.room()) {
+      fq.push(c);
+    } else {
+      CK(launch_ste_finish_multi(&c, 1, st));
+    }
+  }
   // q / k / v with the shared qkv LET site; the inverse RoPE of the Q and K gradients
   // runs inside the bf16 conversion of dL/dY
   {
@@ -890,15 +936,16 @@ int backward(const omq_block_desc* bd, const Dims& m, const Theta& t, const Ws& 
     L.d_x = th + t.d_qkv; L.ast = w.a_qkv; L.gx_out = nullptr;
     L.gs_x = dth + t.s_qkv; L.gd_x = dth + t.d_qkv;
     L.rope = &rp;
-    L.wpart = w.wpart[0]; L.defer = &fq;
+    L.wpart = w.wpart[0]; L.xpart = w.xpart[2]; L.defer = &fq;
     CK(lin_bwd_fused(w, L, T, wb, ab, th, t, dth, st, tm));
   }
   CK(fq.flush(st));
-  // the o-site LET gradients of grouped heads, per query channel until here (the
-  // activation side's terms, then the weight side's), summed over each group
+  // the o-site LET and s_a gradients of grouped heads, per query channel until here,
+  // summed over each group
   if (m.grp > 1) {
     CK(launch_kv_reduce_add(w.gs_full, m.nq, m.nkv, m.hd, dth + t.s_o, st));
     CK(launch_kv_reduce_add(w.gd_full, m.nq, m.nkv, m.hd, dth + t.d_o, st));
+    if (sa) CK(launch_kv_reduce_add(w.gsa_full, m.nq, m.nkv, m.hd, dth + t.s_a, st));
   }
   return OMQ_OK;
 }

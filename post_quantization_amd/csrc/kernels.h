@@ -112,11 +112,15 @@ size_t ste_partials_floats(int64_t rows, int64_t cols, int64_t nslabs, int64_t n
 hipError_t launch_ste_finish(const RowQuantBwd& cf, int ntiles, float* colpart,
                              const RowQuantBwd& rf, int nslabs, const float* rowpart,
                              int tile_rows, hipStream_t st);
-// Independent finalizer jobs (each one launch_ste_finish's arguments, with cf's
-// column-pass fields inline) in two launches in all: every job's row finalizers,
-// then every job's column pass.  Jobs share no partial buffers and no outputs, so
-// each output gets the same sums in the same order as from its own launches.
-constexpr int kMaxFinJobs = 4;
+// Finalizer jobs (each one launch_ste_finish's arguments, with cf's column-pass
+// fields inline) in few launches: every job's row finalizers in one (up to
+// kMaxRowJobs jobs of one kernel instance; otherwise one per job), then the column
+// passes in rounds of one launch each, a pass going to the round after the last
+// earlier job that adds into one of its outputs, so each output receives its jobs'
+// sums in job order.  A job with rf.rows 0 has no row finalizers; skip_cols: the
+// row finalizers still merge their scatter terms into the column partials, but the
+// column pass is left to a later column-only job.
+constexpr int kMaxFinJobs = 10, kMaxRowJobs = 4;
 struct SteFinJob {
   RowQuantBwd rf;
   int nslabs = 0, tile_rows = 0, ntiles = 0;
@@ -126,8 +130,14 @@ struct SteFinJob {
   int col_mode = COL_NONE;
   float *out0 = nullptr, *out1 = nullptr;
   int accumulate = 0;
+  bool skip_cols = false;
 };
 hipError_t launch_ste_finish_multi(const SteFinJob* jobs, int n, hipStream_t st);
+// the row finalizers of launch_ste_finish alone (merging into colpart when cf names
+// column outputs); its column pass is left to the caller
+hipError_t launch_ste_finish_rows(const RowQuantBwd& cf, float* colpart, const RowQuantBwd& rf,
+                                  int nslabs, const float* rowpart, int tile_rows,
+                                  hipStream_t st);
 // launch_rowquant_bwd's tile pass alone, its finalizers left in *job for
 // launch_ste_finish_multi (job->rf.rows 0: nothing to finish)
 hipError_t launch_rowquant_bwd_tiles(const RowQuantBwd& a, hipStream_t st, SteFinJob* job);

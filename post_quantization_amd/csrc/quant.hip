@@ -1560,7 +1560,7 @@ __global__ __launch_bounds__(kFinThreads) void k_ste_rows(RowQuantBwd a, int nsl
   ste_rows_unit<XDT, LPR>(a, nslabs, rowpart, tile_rows, colpart, merge, blockIdx.x);
 }
 
-// Up to kMaxFinJobs independent finalizer jobs in one launch: job j takes the
+// Up to kMaxRowJobs independent finalizer jobs in one launch: job j takes the
 // workgroups [sum of the earlier jobs' units, + its own units).  Each job is read
 // through a constant index (a run-time index into the argument block would copy it
 // to scratch memory).
@@ -1571,7 +1571,7 @@ struct SteRowsJob {
   int nslabs, tile_rows, merge, units;
 };
 struct SteRowsJobs {
-  SteRowsJob j[kMaxFinJobs];
+  SteRowsJob j[kMaxRowJobs];
   int n;
 };
 
@@ -1581,7 +1581,7 @@ __global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(8))
 void k_ste_rows_multi(SteRowsJobs m) {
   int64_t bid = blockIdx.x;
 #pragma unroll
-  for (int q = 0; q < kMaxFinJobs; ++q) {
+  for (int q = 0; q < kMaxRowJobs; ++q) {
     if (q < m.n) {
       const SteRowsJob& jb = m.j[q];
       if (bid < jb.units) {
@@ -2150,6 +2150,18 @@ size_t ste_partials_floats(int64_t rows, int64_t cols, int64_t nslabs, int64_t n
 hipError_t launch_ste_finish(const RowQuantBwd& cf, int ntiles, float* colpart,
                              const RowQuantBwd& rf, int nslabs, const float* rowpart,
                              int tile_rows, hipStream_t st) {
+  const hipError_t e = launch_ste_finish_rows(cf, colpart, rf, nslabs, rowpart, tile_rows, st);
+  if (e != hipSuccess) return e;
+  const bool cols_out = cf.col_mode != COL_NONE && (cf.out0 || cf.out1) && cf.cols > 0;
+  if (!cols_out) return hipSuccess;
+  hipLaunchKernelGGL(k_ste_cols, dim3((unsigned)((cf.cols + 63) / 64)), dim3(kThreads), 0, st,
+                     colpart, ntiles, cf.cols, cf.out0, cf.out1, cf.accumulate);
+  return hipGetLastError();
+}
+
+hipError_t launch_ste_finish_rows(const RowQuantBwd& cf, float* colpart, const RowQuantBwd& rf,
+                                  int nslabs, const float* rowpart, int tile_rows,
+                                  hipStream_t st) {
   const bool cols_out = cf.col_mode != COL_NONE && (cf.out0 || cf.out1) && cf.cols > 0;
   const int64_t ng = rf.group > 0 ? rf.cols / 128 : 1;
   const bool rows = rf.nbits < 16 && rf.rows > 0;
@@ -2174,76 +2186,51 @@ hipError_t launch_ste_finish(const RowQuantBwd& cf, int ntiles, float* colpart,
   }
     OMQ_ROWS(1) OMQ_ROWS(8) OMQ_ROWS(16)
 #undef OMQ_ROWS
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    return hipGetLastError();
   }
-  if (!cols_out) return hipSuccess;
-  hipLaunchKernelGGL(k_ste_cols, dim3((unsigned)((cf.cols + 63) / 64)), dim3(kThreads), 0, st,
-                     colpart, ntiles, cf.cols, cf.out0, cf.out1, cf.accumulate);
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 hipError_t launch_ste_finish_multi(const SteFinJob* jobs, int n, hipStream_t st) {
   if (n < 0 || n > kMaxFinJobs) return hipErrorInvalidValue;
-  SteRowsJobs rj{};
-  SteColsJobs cj{};
-  int lpr0 = -1, xdt0 = -1, nt0 = -1;
-  bool rows_one = true;              // every job's row finalizers take one kernel instance
-  int64_t rows_units = 0, cols_units = 0;
+  // row finalizers: the jobs that take one kernel instance (x type, lanes per row)
+  // share a launch, up to kMaxRowJobs at a time; jobs are independent, so the
+  // launches' order does not matter
+  bool done[kMaxFinJobs] = {};
   for (int i = 0; i < n; ++i) {
     const SteFinJob& J = jobs[i];
-    const RowQuantBwd& rf = J.rf;
-    if (J.tile_rows < 1 || J.tile_rows > 128) return hipErrorInvalidValue;
-    const bool cols_out = J.col_mode != COL_NONE && (J.out0 || J.out1) && J.cols > 0;
-    if (rf.nbits < 16 && rf.rows > 0) {
+    if (J.tile_rows < 0 || J.tile_rows > 128) return hipErrorInvalidValue;
+    if (!(J.rf.nbits < 16 && J.rf.rows > 0)) done[i] = true;
+    else if (J.tile_rows < 1) return hipErrorInvalidValue;
+  }
+  auto lpr_of = [](const SteFinJob& J) {
+    return J.nslabs == 1 ? 1 : J.tile_rows > 64 ? 8 : 16;
+  };
+  for (int i = 0; i < n; ++i) {
+    if (done[i]) continue;
+    const int lpr = lpr_of(jobs[i]), xdt = jobs[i].rf.x_dt;
+    const int nt = std::max(256, (jobs[i].tile_rows * lpr + 63) / 64 * 64);
+    SteRowsJobs rj{};
+    int64_t units = 0;
+    for (int k = i; k < n && rj.n < kMaxRowJobs; ++k) {
+      const SteFinJob& J = jobs[k];
+      if (done[k] || lpr_of(J) != lpr || J.rf.x_dt != xdt ||
+          std::max(256, (J.tile_rows * lpr + 63) / 64 * 64) != nt)
+        continue;
+      done[k] = true;
+      const RowQuantBwd& rf = J.rf;
+      const bool cols_out = J.col_mode != COL_NONE && (J.out0 || J.out1) && J.cols > 0;
       const int64_t ng = rf.group > 0 ? rf.cols / 128 : 1;
-      const int lpr = J.nslabs == 1 ? 1 : J.tile_rows > 64 ? 8 : 16;
-      const int nt = std::max(256, (J.tile_rows * lpr + 63) / 64 * 64);
-      rows_one = rows_one && (nt0 < 0 || nt == nt0) && (lpr0 < 0 || lpr == lpr0) &&
-                 (xdt0 < 0 || rf.x_dt == xdt0);
-      nt0 = nt;
-      lpr0 = lpr;
-      xdt0 = rf.x_dt;
       SteRowsJob& r = rj.j[rj.n++];
       r.a = rf; r.rowpart = J.rowpart; r.colpart = J.colpart; r.nslabs = J.nslabs;
       r.tile_rows = J.tile_rows; r.merge = cols_out && rf.col_mode != COL_NONE;
       r.units = (int)(((rf.rows + J.tile_rows - 1) / J.tile_rows) * ng);
-      rows_units += r.units;
+      units += r.units;
     }
-    if (cols_out) {
-      SteColsJob& c = cj.j[cj.n++];
-      c.colpart = J.colpart; c.out0 = J.out0; c.out1 = J.out1; c.cols = J.cols;
-      c.ntiles = J.ntiles; c.accumulate = J.accumulate; c.units = (int)((J.cols + 63) / 64);
-      cols_units += c.units;
-    }
-  }
-  // two column passes adding into one output must not run side by side
-  bool cols_disjoint = true;
-  for (int a0 = 0; a0 < cj.n; ++a0)
-    for (int b0 = a0 + 1; b0 < cj.n; ++b0) {
-      const float* oa[2] = {cj.j[a0].out0, cj.j[a0].out1};
-      const float* ob[2] = {cj.j[b0].out0, cj.j[b0].out1};
-      for (const float* x : oa)
-        for (const float* y : ob) cols_disjoint = cols_disjoint && !(x && x == y);
-    }
-  if (!rows_one) {
-    // jobs that need different kernel instances: one launch_ste_finish each, in order
-    for (int i = 0; i < n; ++i) {
-      const SteFinJob& J = jobs[i];
-      RowQuantBwd cf;
-      cf.cols = J.cols; cf.col_mode = J.col_mode; cf.out0 = J.out0; cf.out1 = J.out1;
-      cf.accumulate = J.accumulate;
-      const hipError_t e = launch_ste_finish(cf, J.ntiles, J.colpart, J.rf, J.nslabs, J.rowpart,
-                                             J.tile_rows, st);
-      if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
-  }
-  if (rj.n > 0) {
-    const dim3 grid((unsigned)rows_units), block((unsigned)nt0);
-    const bool f32 = xdt0 == OMQ_F32;
+    const dim3 grid((unsigned)units), block((unsigned)nt);
+    const bool f32 = xdt == OMQ_F32;
 #define OMQ_ROWS_M(L)                                                                        \
-  if (lpr0 == L) {                                                                           \
+  if (lpr == L) {                                                                            \
     if (f32) hipLaunchKernelGGL((k_ste_rows_multi<OMQ_F32, L>), grid, block, 0, st, rj);     \
     else hipLaunchKernelGGL((k_ste_rows_multi<OMQ_BF16, L>), grid, block, 0, st, rj);        \
   }
@@ -2252,16 +2239,40 @@ hipError_t launch_ste_finish_multi(const SteFinJob* jobs, int n, hipStream_t st)
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (cj.n == 0) return hipSuccess;
-  if (cols_disjoint) {
-    hipLaunchKernelGGL(k_ste_cols_multi, dim3((unsigned)cols_units), dim3(kThreads), 0, st, cj);
-    return hipGetLastError();
+  // column passes, in rounds: a pass goes to the round after the last earlier pass
+  // that shares one of its outputs
+  int round[kMaxFinJobs];
+  int nround = 0;
+  for (int i = 0; i < n; ++i) {
+    const SteFinJob& J = jobs[i];
+    round[i] = -1;
+    const bool cols_out = J.col_mode != COL_NONE && (J.out0 || J.out1) && J.cols > 0;
+    if (!cols_out || J.skip_cols) continue;
+    int rd = 0;
+    for (int k = 0; k < i; ++k) {
+      if (round[k] < 0) continue;
+      const float* oa[2] = {jobs[k].out0, jobs[k].out1};
+      const float* ob[2] = {J.out0, J.out1};
+      bool share = false;
+      for (const float* x : oa)
+        for (const float* y : ob) share = share || (x && x == y);
+      if (share) rd = std::max(rd, round[k] + 1);
+    }
+    round[i] = rd;
+    nround = std::max(nround, rd + 1);
   }
-  // column passes that share an output, in job order
-  for (int i = 0; i < cj.n; ++i) {
-    const SteColsJob& c = cj.j[i];
-    hipLaunchKernelGGL(k_ste_cols, dim3((unsigned)c.units), dim3(kThreads), 0, st, c.colpart,
-                       c.ntiles, c.cols, c.out0, c.out1, c.accumulate);
+  for (int rd = 0; rd < nround; ++rd) {
+    SteColsJobs cj{};
+    int64_t units = 0;
+    for (int i = 0; i < n; ++i) {
+      if (round[i] != rd) continue;
+      const SteFinJob& J = jobs[i];
+      SteColsJob& c = cj.j[cj.n++];
+      c.colpart = J.colpart; c.out0 = J.out0; c.out1 = J.out1; c.cols = J.cols;
+      c.ntiles = J.ntiles; c.accumulate = J.accumulate; c.units = (int)((J.cols + 63) / 64);
+      units += c.units;
+    }
+    hipLaunchKernelGGL(k_ste_cols_multi, dim3((unsigned)units), dim3(kThreads), 0, st, cj);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
