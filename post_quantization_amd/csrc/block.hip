@@ -680,9 +680,11 @@ struct LinBwd {
   float* xpart;
 };
 
-// Weight-side finalizers queued by the layers' backward passes: nothing reads their
-// outputs (the logit gradients, the LET scales' column totals) before the update, so
-// they run together, two launches for the whole block, once every GEMM is done.
+// Straight-through work queued by the layers' backward passes: the weight sides'
+// finalizers, the q|k|v input's (no dL/dx written there) and every column pass.
+// Nothing reads their outputs (the logit gradients, the LET and s_a column totals)
+// before the update, so they run together once every GEMM is done: one row-finalizer
+// launch per kernel instance and two rounds of column passes for the whole block.
 struct FinQueue {
   SteFinJob job[kMaxFinJobs];
   int n = 0;
